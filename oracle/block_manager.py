@@ -1,0 +1,233 @@
+"""Reference block manager (oracle): free list, reference counts, block tables.
+
+Passages followed:
+
+* "KV Cache Management", section "The PagedAttention virtual memory model": a
+  token at offset o != 0 goes into the already allocated block T[l]; at o == 0
+  a free block id is popped and appended to the table.
+* Same page, Table 3 / section "Asynchronous paged swapping": free ids are kept
+  in a FIFO queue. The reading taken: pop from the front, return freed ids at
+  the back, and start from an order the caller gives.
+* Same page, section "Zero-copy deliberation via copy-on-write branching":
+  fork = duplicate the table, increment every listed block's count, give the
+  child the parent's length; a write into a block whose count is above one
+  first takes a new block, copies the shared one into it, decrements the old
+  count and remaps the table entry; release decrements every block of the table
+  and returns those reaching zero to the free list.
+* "PagedAttention" (Inference book), sections "Paging", "It is the same
+  function" and "Inference Lab increment": out-of-blocks and double-free are
+  errors, and a reservation that cannot be met leaks nothing.
+* "KV Cache Management", section "Asynchronous paged swapping": swapping out
+  releases a sequence's frames to the free queue and marks the table entries as
+  not resident; swapping in takes fresh frames and remaps the entries.
+
+Every operation checks all of its preconditions before it changes anything, so a
+failed call leaves the manager exactly as it was.
+"""
+
+from __future__ import annotations
+
+from collections import deque
+
+
+class BlockManagerError(Exception):
+    pass
+
+
+class OutOfBlocks(BlockManagerError):
+    pass
+
+
+class DoubleFree(BlockManagerError):
+    pass
+
+
+class InvalidArgument(BlockManagerError):
+    pass
+
+
+NOT_RESIDENT = -1
+
+
+class BlockManager:
+    def __init__(self, num_blocks, block_size, free_order=None):
+        if num_blocks < 1 or block_size < 1:
+            raise InvalidArgument("num_blocks and block_size must be positive")
+        order = list(range(num_blocks)) if free_order is None else [int(x) for x in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise InvalidArgument("free_order must be a permutation of 0..N-1")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+        self.tables = {}
+        self.lengths = {}
+        self._next_seq = 0
+
+    # ---- raw allocator -------------------------------------------------------
+    def num_free(self):
+        return len(self.free)
+
+    def refcount(self, block):
+        return self.ref[block]
+
+    def alloc(self, n):
+        """Take n blocks (count 1 each), all or none."""
+        if n < 0:
+            raise InvalidArgument("negative count")
+        if n > len(self.free):
+            raise OutOfBlocks(f"need {n}, have {len(self.free)}")
+        out = [self.free.popleft() for _ in range(n)]
+        for b in out:
+            self.ref[b] = 1
+        return out
+
+    def incref(self, ids):
+        for b in ids:
+            if not 0 <= b < self.num_blocks or self.ref[b] == 0:
+                raise InvalidArgument(f"block {b} is not allocated")
+        for b in ids:
+            self.ref[b] += 1
+
+    def free_blocks(self, ids):
+        """Drop one reference from each id; ids reaching zero go back to the queue."""
+        pending = {}
+        for b in ids:
+            if not 0 <= b < self.num_blocks:
+                raise InvalidArgument(f"block {b} out of range")
+            pending[b] = pending.get(b, 0) + 1
+            if pending[b] > self.ref[b]:
+                raise DoubleFree(f"block {b} has no reference left to drop")
+        for b in ids:
+            self._decref(b)
+
+    def _decref(self, b):
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(b)
+
+    # ---- sequences -----------------------------------------------------------
+    def _check_seq(self, sid):
+        if sid not in self.tables:
+            raise InvalidArgument(f"unknown sequence {sid}")
+
+    def seq_new(self):
+        sid = self._next_seq
+        self._next_seq += 1
+        self.tables[sid] = []
+        self.lengths[sid] = 0
+        return sid
+
+    def fork(self, parent):
+        self._check_seq(parent)
+        table = self.tables[parent]
+        if any(p == NOT_RESIDENT for p in table):
+            raise InvalidArgument("cannot fork a sequence with blocks swapped out")
+        child = self._next_seq
+        self._next_seq += 1
+        self.tables[child] = list(table)            # 1. duplicate the table
+        for p in table:                             # 2. one more reference each
+            self.ref[p] += 1
+        self.lengths[child] = self.lengths[parent]  # 3. same starting length
+        return child
+
+    def blocks_needed(self, sid, n):
+        """(copy-on-write blocks, fresh blocks) an append of n tokens would take."""
+        table, S, B = self.tables[sid], self.lengths[sid], self.block_size
+        cow = 0
+        if n > 0 and S % B != 0:
+            tail = table[S // B]
+            if tail == NOT_RESIDENT:
+                raise InvalidArgument("tail block is swapped out")
+            if self.ref[tail] > 1:
+                cow = 1
+        fresh = sum(1 for t in range(S, S + n) if t % B == 0)
+        return cow, fresh
+
+    def append(self, sid, n):
+        """Reserve room for n more tokens; returns (slots, copy_pairs).
+
+        slots[k] is the flat slot (block * B + offset) of token S + k, and
+        copy_pairs lists (src, dst) block copies that must run before the write.
+        """
+        self._check_seq(sid)
+        if n < 0:
+            raise InvalidArgument("negative token count")
+        cow, fresh = self.blocks_needed(sid, n)
+        if cow + fresh > len(self.free):
+            raise OutOfBlocks(f"need {cow + fresh}, have {len(self.free)}")
+        table, S, B = self.tables[sid], self.lengths[sid], self.block_size
+        pairs = []
+        if cow:
+            lb = S // B
+            old = table[lb]
+            new = self.free.popleft()
+            self.ref[new] = 1
+            self.ref[old] -= 1          # still >= 1: another owner keeps it
+            table[lb] = new
+            pairs.append((old, new))
+        slots = []
+        for t in range(S, S + n):
+            lb, off = t // B, t % B
+            if off == 0:
+                new = self.free.popleft()
+                self.ref[new] = 1
+                table.append(new)
+            slots.append(table[lb] * B + off)
+        self.lengths[sid] = S + n
+        return slots, pairs
+
+    def release(self, sid):
+        """Decrement every block of the table; blocks reaching zero are freed."""
+        self._check_seq(sid)
+        for p in self.tables[sid]:
+            if p != NOT_RESIDENT:
+                self._decref(p)
+        del self.tables[sid]
+        del self.lengths[sid]
+
+    def swap_out(self, sid, logical):
+        """Drop the sequence's reference to the listed logical blocks; returns
+        the physical ids they had (in list order)."""
+        self._check_seq(sid)
+        table = self.tables[sid]
+        if len(set(logical)) != len(logical):
+            raise InvalidArgument("repeated logical block")
+        for lb in logical:
+            if not 0 <= lb < len(table) or table[lb] == NOT_RESIDENT:
+                raise InvalidArgument(f"logical block {lb} is not resident")
+        phys = [table[lb] for lb in logical]
+        for lb in logical:
+            self._decref(table[lb])
+            table[lb] = NOT_RESIDENT
+        return phys
+
+    def swap_in(self, sid, logical):
+        """Give the listed non-resident logical blocks fresh physical blocks."""
+        self._check_seq(sid)
+        table = self.tables[sid]
+        if len(set(logical)) != len(logical):
+            raise InvalidArgument("repeated logical block")
+        for lb in logical:
+            if not 0 <= lb < len(table) or table[lb] != NOT_RESIDENT:
+                raise InvalidArgument(f"logical block {lb} is resident")
+        if len(logical) > len(self.free):
+            raise OutOfBlocks(f"need {len(logical)}, have {len(self.free)}")
+        out = []
+        for lb in logical:
+            p = self.free.popleft()
+            self.ref[p] = 1
+            table[lb] = p
+            out.append(p)
+        return out
+
+    def table(self, sid):
+        self._check_seq(sid)
+        return list(self.tables[sid])
+
+    def length(self, sid):
+        self._check_seq(sid)
+        return self.lengths[sid]
+
+    def blocks_in_use(self):
+        return self.num_blocks - len(self.free)

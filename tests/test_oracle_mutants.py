@@ -1,0 +1,132 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that its pins catch
+each one. Each mutant replaces one oracle function for the duration of a test."""
+import math
+from collections import deque
+
+import numpy as np
+import pytest
+
+import oracle.attention as att
+import oracle.block_manager as obm
+import oracle.footprint as fp
+import oracle.layout as layout
+from tests import test_oracle_attention as TA
+from tests import test_oracle_block_manager as TB
+from tests import test_oracle_footprint as TF
+from tests import test_oracle_kv_ops as TK
+
+
+def _attend_mod_groups(q, K, V, scale):
+    Hq, d = q.shape
+    S, Hkv, _ = K.shape
+    out = np.zeros((Hq, d))
+    for h in range(Hq):
+        g = h % Hkv                                   # wrong: strided instead of contiguous groups
+        s = scale * (K[:, g, :] @ q[h])
+        p = np.exp(s - s.max())
+        out[h] = (p @ V[:, g, :]) / p.sum()
+    return out
+
+
+def _attend_no_scale(q, K, V, scale):
+    return att_orig_attend(q, K, V, 1.0)
+
+
+def _v_tile_untransposed(v_pool, layer, phys, head):
+    return v_pool[layer, phys, head, :, :]
+
+
+def _rebuild_short(k_pool, v_pool, layer, table, length, block_size, dtype):
+    K, V = rebuild_orig(k_pool, v_pool, layer, table, length, block_size, dtype)
+    if length > 1:
+        K[-1] = K[-2]                                 # wrong: last token replaced by its neighbour
+    return K, V
+
+
+def _merge_wrong_sign(m_prev, l_prev, O_prev, m_blk, l_blk, O_blk):
+    m_new = max(m_prev, m_blk)
+    a = math.exp(m_new - m_prev) if m_prev != -math.inf else 0.0   # wrong sign
+    b = math.exp(m_blk - m_new)
+    return m_new, l_prev * a + l_blk * b, O_prev * a + O_blk * b
+
+
+def _bytes_per_token_no_kv_factor(L, H, d, b, tp=1):
+    return L * max(1, -(-H // tp)) * d * b
+
+
+att_orig_attend = att.attend
+rebuild_orig = att.rebuild_sequence
+
+
+class _LifoDeque(deque):
+    def popleft(self):
+        return self.pop()
+
+
+def _append_without_cow(self, sid, n):
+    saved = self.ref[:]
+    try:
+        self.ref = [min(r, 1) for r in self.ref]     # wrong: never sees a shared tail
+        return orig_append(self, sid, n)
+    finally:
+        for i, r in enumerate(saved):
+            if r > 1:
+                self.ref[i] = r
+
+
+orig_append = obm.BlockManager.append
+
+
+def _raises(fn, *args):
+    """The pin must fail: by a failed assertion, or by the mutant's shapes not fitting."""
+    with pytest.raises((AssertionError, ValueError)):
+        fn(*args)
+
+
+def test_mutant_gqa_mapping(monkeypatch):
+    monkeypatch.setattr(att, "attend", _attend_mod_groups)
+    _raises(TA.test_gqa_groups_are_contiguous)
+
+
+def test_mutant_missing_scale(monkeypatch):
+    monkeypatch.setattr(att, "attend", _attend_no_scale)
+    _raises(TA.test_two_keys_weights_one_to_three_pin_the_scale)
+    _raises(TA.test_brute_force_tiny, 16)
+
+
+def test_mutant_v_layout(monkeypatch):
+    monkeypatch.setattr(layout, "read_v_tile", _v_tile_untransposed)
+    _raises(TK.test_tiny_rebuild)
+    _raises(TA.test_brute_force_tiny, 4)
+
+
+def test_mutant_dropped_token(monkeypatch):
+    monkeypatch.setattr(att, "rebuild_sequence", _rebuild_short)
+    _raises(TA.test_brute_force_tiny, 16)
+    _raises(TK.test_appended_history_reads_back_exactly)
+
+
+def test_mutant_online_merge_sign(monkeypatch):
+    monkeypatch.setattr(att, "_merge", _merge_wrong_sign)
+    _raises(TA.test_online_split_equals_direct, 100)
+
+
+def test_mutant_footprint_factor(monkeypatch):
+    monkeypatch.setattr(fp, "bytes_per_token", _bytes_per_token_no_kv_factor)
+    _raises(TF.test_bytes_per_token, TF.GOLD["bytes_per_token"][0])
+
+
+def test_mutant_lifo_free_list(monkeypatch):
+    orig_init = obm.BlockManager.__init__
+
+    def init(self, *a, **k):
+        orig_init(self, *a, **k)
+        self.free = _LifoDeque(self.free)
+    monkeypatch.setattr(obm.BlockManager, "__init__", init)
+    _raises(TB.test_figure5, "figure5_boundary")
+
+
+def test_mutant_no_copy_on_write(monkeypatch):
+    monkeypatch.setattr(obm.BlockManager, "append", _append_without_cow)
+    _raises(TB.test_p3_fork_example)
+    _raises(TB.test_figure5, "figure5_cow")
