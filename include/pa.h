@@ -1,0 +1,240 @@
+/*
+ * pa.h -- C interface of libpa, paged-KV attention decode for AMD MI355X (gfx950).
+ *
+ * What the library computes, and where the pages define it:
+ *   - KV footprint: "KV Cache Management", section "From Context Tokens to KV
+ *     State", Eq. (1), and section "The PagedAttention virtual memory model"
+ *     (block bytes, blocks per prompt); per-rank form with tensor parallelism:
+ *     "EfficientAgent: What Makes KV Cache Offloading Work for Concurrent
+ *     Agents?", section "KV footprint and hardware balance", Eq. (1).
+ *   - Block tables and slot-mapped writes: "KV Cache Management", section "The
+ *     PagedAttention virtual memory model" (l = floor(t/B), o = t mod B, T[l] = p).
+ *   - Paged decode attention: same page, same section (the kernel takes the
+ *     block table as an input and walks logical blocks 0..floor((S-1)/B)), with
+ *     the online softmax of section "Chunked prefill mechanics".
+ *   - Reference counts, fork, copy-on-write, release: same page, section
+ *     "Zero-copy deliberation via copy-on-write branching"; error behaviour from
+ *     "PagedAttention" (Inference book, ch. 14), sections "It is the same
+ *     function" and "Inference Lab increment".
+ *   - Block gather/scatter and the host copy: "KV Cache Management", section
+ *     "Asynchronous paged swapping".
+ *
+ * ---------------------------------------------------------------------------
+ * Memory layout (fixed by this interface)
+ * ---------------------------------------------------------------------------
+ * A pool is two device arrays of the geometry's element type (fp32 or bf16):
+ *   K pool [L][N][H_kv][B][d]   element (layer, block, head, slot offset, dim)
+ *   V pool [L][N][H_kv][d][B]   element (layer, block, head, dim, slot offset)
+ * Each (layer, block, head) is one contiguous run of B*d elements in both.
+ * A slot is block * B + offset. A block table is int32 [n_seqs][max_blocks]
+ * (row-major); entry j of row i is the physical block of sequence i's logical
+ * block j. context_lens[i] is the number of tokens sequence i attends to.
+ * Staging (gather/scatter): for the i-th listed block, bytes_per_block bytes
+ * laid out [L][2][run]: that layer's K run of the block, then its V run, each
+ * exactly as stored in the pool.
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions
+ * ---------------------------------------------------------------------------
+ * Ownership: the caller allocates and owns every device and host buffer; the
+ *   device entry points never allocate device memory. Decode split partials live
+ *   in a caller-provided workspace (size from pa_decode_workspace_bytes).
+ * Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   Device entry points only enqueue work and return; results are visible after
+ *   the caller synchronises the stream.
+ * Errors: every entry point returns pa_status. Arguments and geometry are
+ *   checked on the host before anything is launched; a launch failure returns
+ *   PA_ERR_HIP. Block manager calls that fail leave the manager unchanged.
+ * Device-side preconditions (not checked on the host): block ids in tables and
+ *   id lists lie in [0, N); slots lie in [0, N*B) or are negative (skip);
+ *   context_lens[i] <= max_context_len <= max_blocks_per_seq * B. Kernels guard
+ *   their own memory accesses against out-of-range ids and lengths (an
+ *   out-of-range slot is skipped, an out-of-range block id is read as block 0,
+ *   a length is clamped), so bad indices give wrong numbers, never a fault.
+ * Dtypes: q, out and both pools share one dtype; arithmetic is fp32.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = -1,   /* bad pointer, size, index or geometry           */
+  PA_ERR_OUT_OF_BLOCKS = -2, /* the free list cannot satisfy the request        */
+  PA_ERR_DOUBLE_FREE = -3,   /* dropping a reference that does not exist        */
+  PA_ERR_NOT_FOUND = -4,     /* unknown sequence id                             */
+  PA_ERR_HIP = -5,           /* a HIP runtime call or launch failed             */
+  PA_ERR_WORKSPACE = -6,     /* decode workspace too small                      */
+  PA_ERR_UNSUPPORTED = -7    /* geometry outside what the kernels implement     */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Pool geometry: L layers, H_kv KV heads of dimension d, blocks of B slots,
+ * N physical blocks, element type dtype (a pa_dtype value). */
+typedef struct {
+  int32_t num_layers;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t num_blocks;
+  int32_t dtype;
+} pa_geom;
+
+const char* pa_status_str(int32_t status);
+int32_t pa_version(void);
+
+/* ---------------------------------------------------------------- footprint */
+
+/* Bytes of K and V one token occupies on one rank: 2*L*d*b*max(1, ceil(H_kv/tp)).
+ * tp == 1 gives Eq. (1) of "KV Cache Management". Returns -1 on bad input. */
+int64_t pa_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t elem_bytes, int32_t tp);
+/* M_block = 2*L*H_kv*B*d*b ("The PagedAttention virtual memory model"); -1 on bad geometry. */
+int64_t pa_bytes_per_block(const pa_geom* g);
+/* ceil(tokens / block_size); -1 on bad input. */
+int64_t pa_blocks_for_tokens(int64_t tokens, int32_t block_size);
+/* Bytes of one pool array (K or V): L*N*H_kv*B*d*b; -1 on bad geometry. */
+int64_t pa_pool_bytes(const pa_geom* g);
+
+/* ------------------------------------------------------------ device entry points */
+
+/* Slot-mapped write of new keys and values into one layer.
+ * k_new, v_new: [n_tokens][H_kv][d] device arrays. slot_mapping: int64 [n_tokens]
+ * device array; token j goes to block slot/B, offset slot%B; a negative slot
+ * skips the token. Source: "KV Cache Management", "The PagedAttention virtual
+ * memory model" (write into T[l] at offset o); "PagedAttention", "The real cache". */
+pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer,
+                       const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                       int32_t n_tokens, void* stream);
+
+/* Decode tuning; pass NULL for the defaults. */
+typedef struct {
+  int32_t blocks_per_split; /* logical blocks per split-K work item (0 = choose; rounded up to even) */
+  int32_t kernel;           /* 0 = choose, 1 = generic VALU kernel, 2 = MFMA kernel (bf16, B=16) */
+} pa_decode_opts;
+
+/* Workspace bytes pa_decode needs for these sizes and options (0 when the
+ * chosen plan writes the output directly). Returns 0 also for invalid input;
+ * pa_decode reports the error. */
+size_t pa_decode_workspace_bytes(const pa_geom* g, int32_t n_seqs, int32_t n_q_heads,
+                                 int32_t max_context_len, const pa_decode_opts* opts);
+
+/* Ragged-batch GQA decode over block tables, one layer.
+ * q, out: [n_seqs][n_q_heads][d] device arrays (pool dtype). Query head h reads
+ * KV head h / (n_q_heads / H_kv). For sequence i, out[i][h] =
+ * sum_t softmax_t(scale * q[i][h] . K_t) V_t over its first context_lens[i]
+ * tokens, read through block_tables row i. scale <= 0 means 1/sqrt(d).
+ * context_lens[i] == 0 writes zeros. max_context_len bounds every
+ * context_lens[i] (lengths above it are clamped) and sizes the launch. Splits
+ * the keys into runs of blocks_per_split blocks processed in parallel and merges
+ * them with the online-softmax rule of "Chunked prefill mechanics". Results do
+ * not depend on which physical blocks hold the data. */
+pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, int32_t layer,
+                    const void* q, void* out, int32_t n_seqs, int32_t n_q_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, float scale,
+                    const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Copy-on-write block copy: for each k, block dst[k] <- block src[k] in every
+ * layer, K and V, all B slots. src, dst: int32 [n_pairs] device arrays; no dst
+ * may appear as a src or twice. Source: "KV Cache Management", "Zero-copy
+ * deliberation via copy-on-write branching". */
+pa_status pa_copy_blocks(const pa_geom* g, void* k_pool, void* v_pool, const int32_t* src,
+                         const int32_t* dst, int32_t n_pairs, void* stream);
+
+/* staging[i] <- block block_ids[i] (the staging layout above; n * bytes_per_block
+ * bytes). block_ids: int32 [n] device array. Source: "Asynchronous paged swapping". */
+pa_status pa_gather_blocks(const pa_geom* g, const void* k_pool, const void* v_pool,
+                           const int32_t* block_ids, int32_t n, void* staging, void* stream);
+
+/* block block_ids[i] <- staging[i]; the inverse of pa_gather_blocks. Ids must be distinct. */
+pa_status pa_scatter_blocks(const pa_geom* g, void* k_pool, void* v_pool, const void* staging,
+                            const int32_t* block_ids, int32_t n, void* stream);
+
+/* Asynchronous copies over the host link (hipMemcpyAsync). host buffers should
+ * be pinned (page-locked) for the copy to be asynchronous and run at link speed. */
+pa_status pa_copy_to_host(void* host_dst, const void* device_src, size_t bytes, void* stream);
+pa_status pa_copy_to_device(void* device_dst, const void* host_src, size_t bytes, void* stream);
+
+/* ---------------------------------------------------------------- timing */
+
+/* When enabled, the library records a hipEvent pair on the launch stream around
+ * each kernel it launches and accumulates per-kernel durations. Kernel names:
+ * "append", "decode_partial", "decode_combine", "copy_blocks", "gather", "scatter".
+ * pa_prof_read synchronises the recorded events. */
+pa_status pa_prof_enable(int32_t on);
+pa_status pa_prof_reset(void);
+pa_status pa_prof_read(const char* kernel, int64_t* launches, double* total_ms);
+
+/* ---------------------------------------------------------------- block manager */
+/* Host-only state: a FIFO free list of block ids (initial order given by the
+ * caller, NULL = 0..N-1), a reference count per block and a block table and
+ * length per sequence. Appends allocate at block boundaries; a write into a
+ * partly filled block whose count is above 1 first takes a fresh block and
+ * reports a (src, dst) copy for pa_copy_blocks. Every call checks its
+ * preconditions before changing anything. Not thread-safe. */
+typedef struct pa_bm pa_bm;
+
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       pa_bm** out);
+void pa_bm_destroy(pa_bm* bm);
+int32_t pa_bm_num_free(const pa_bm* bm);
+/* Reference count of a block, -1 if the id is out of range. */
+int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
+
+/* Raw allocator: take n blocks (count 1), all or none. */
+pa_status pa_bm_alloc(pa_bm* bm, int32_t n, int32_t* ids_out);
+/* One more reference to each listed (allocated) block. */
+pa_status pa_bm_incref(pa_bm* bm, const int32_t* ids, int32_t n);
+/* Drop one reference from each listed block; a block reaching 0 returns to the
+ * back of the free list. PA_ERR_DOUBLE_FREE if a block has no reference left. */
+pa_status pa_bm_free_blocks(pa_bm* bm, const int32_t* ids, int32_t n);
+
+pa_status pa_bm_seq_new(pa_bm* bm, int32_t* seq_out);
+/* Child gets a copy of the parent's table and length; every block gains a reference. */
+pa_status pa_bm_seq_fork(pa_bm* bm, int32_t parent, int32_t* child_out);
+/* Reserve n_tokens more positions. slots_out (may be NULL) receives n_tokens
+ * int64 slots; *n_cow_out is 0 or 1 and, when 1, cow_src_out[0]/cow_dst_out[0]
+ * name the block copy that must precede the write. */
+pa_status pa_bm_seq_append(pa_bm* bm, int32_t seq, int32_t n_tokens, int64_t* slots_out,
+                           int32_t* cow_src_out, int32_t* cow_dst_out, int32_t* n_cow_out);
+/* Append counts[k] tokens to seqs[k] for every k, all or nothing. slots_out
+ * receives sum(counts) slots in order; cow arrays need room for n entries. */
+pa_status pa_bm_append_batch(pa_bm* bm, const int32_t* seqs, const int32_t* counts, int32_t n,
+                             int64_t* slots_out, int32_t* cow_src_out, int32_t* cow_dst_out,
+                             int32_t* n_cow_out);
+/* Drop a reference to every block of the table; blocks reaching 0 are freed. */
+pa_status pa_bm_seq_release(pa_bm* bm, int32_t seq);
+/* Swap-out: drop the sequence's reference to the listed logical blocks and mark
+ * them not resident (-1 in the table); phys_out receives their physical ids. */
+pa_status pa_bm_seq_swap_out(pa_bm* bm, int32_t seq, const int32_t* logical, int32_t n,
+                             int32_t* phys_out);
+/* Swap-in: give the listed non-resident logical blocks fresh physical blocks. */
+pa_status pa_bm_seq_swap_in(pa_bm* bm, int32_t seq, const int32_t* logical, int32_t n,
+                            int32_t* phys_out);
+pa_status pa_bm_seq_info(const pa_bm* bm, int32_t seq, int64_t* n_tokens, int32_t* n_blocks);
+/* Copy the table (up to cap entries) into table_out; *n_blocks gets its length. */
+pa_status pa_bm_seq_table(const pa_bm* bm, int32_t seq, int32_t* table_out, int32_t cap,
+                          int32_t* n_blocks);
+/* Decode-step tables for a batch: row k of tables_out ([n][max_blocks]) holds
+ * seqs[k]'s table padded with `pad`; lens_out[k] its length. */
+pa_status pa_bm_build_tables(const pa_bm* bm, const int32_t* seqs, int32_t n, int32_t max_blocks,
+                             int32_t pad, int32_t* tables_out, int32_t* lens_out);
+/* Check internal invariants: every count covers the table references to its
+ * block, the free list holds each zero-count block exactly once and nothing
+ * else, and every table has ceil(length / B) entries. PA_OK if consistent. */
+pa_status pa_bm_validate(const pa_bm* bm);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

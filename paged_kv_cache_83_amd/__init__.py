@@ -1,0 +1,16 @@
+"""paged_kv_cache_83_amd: paged-KV attention decode for AMD MI355X (gfx950).
+
+The computation lives in libpa.so (HIP kernels for gfx950 plus a host block
+manager, C interface in include/pa.h). This package is its Python binding.
+Importing it loads the library and fails if it has not been built: there is no
+fallback implementation.
+"""
+
+from ._lib import (DoubleFreeError, OutOfBlocksError, PagedKVError, LIB_PATH,  # noqa: F401
+                   load as _load)
+from .api import (BlockManager, Geometry, Profiler, alloc_pools, append_kv,  # noqa: F401
+                  blocks_for_tokens, bytes_per_block, bytes_per_token, copy_blocks,
+                  copy_to_device, copy_to_host, decode, decode_workspace_bytes, gather_blocks,
+                  pool_bytes, scatter_blocks)
+
+_load()

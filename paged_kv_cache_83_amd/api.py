@@ -1,0 +1,392 @@
+"""Python binding of libpa: argument marshalling only.
+
+Every function here checks that tensors are where and what the C interface
+expects (device, dtype, contiguity, size) -- the C side only sees raw pointers
+and cannot -- and then calls the library. No arithmetic of the method happens
+here; torch is used for device memory and streams only.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import check
+
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
+_CODE = {"f32": _lib.PA_F32, "bf16": _lib.PA_BF16}
+
+
+@dataclass(frozen=True)
+class Geometry:
+    num_layers: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    dtype: str  # "f32" or "bf16"
+
+    def c(self) -> _lib.pa_geom:
+        return _lib.pa_geom(self.num_layers, self.num_kv_heads, self.head_dim, self.block_size,
+                            self.num_blocks, _CODE[self.dtype])
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH[self.dtype]
+
+    @property
+    def elem_bytes(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def k_pool_shape(self):
+        return (self.num_layers, self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim)
+
+    @property
+    def v_pool_shape(self):
+        return (self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size)
+
+    @property
+    def pool_numel(self) -> int:
+        return (self.num_layers * self.num_blocks * self.num_kv_heads * self.block_size
+                * self.head_dim)
+
+
+def _L():
+    return _lib.load()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream, device) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _dev(t: torch.Tensor, what: str, dtype=None, numel=None) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{what} must be a CUDA (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{what} must have {numel} elements, got {t.numel()}")
+
+
+# --------------------------------------------------------------------- footprint
+def bytes_per_token(num_layers, num_kv_heads, head_dim, elem_bytes, tp=1) -> int:
+    return int(_L().pa_bytes_per_token(num_layers, num_kv_heads, head_dim, elem_bytes, tp))
+
+
+def bytes_per_block(geom: Geometry) -> int:
+    g = geom.c()
+    return int(_L().pa_bytes_per_block(C.byref(g)))
+
+
+def blocks_for_tokens(tokens: int, block_size: int) -> int:
+    return int(_L().pa_blocks_for_tokens(tokens, block_size))
+
+
+def pool_bytes(geom: Geometry) -> int:
+    g = geom.c()
+    return int(_L().pa_pool_bytes(C.byref(g)))
+
+
+def alloc_pools(geom: Geometry, device="cuda"):
+    """Uninitialised K and V pools of the documented shapes (torch owns them)."""
+    k = torch.empty(geom.k_pool_shape, dtype=geom.torch_dtype, device=device)
+    v = torch.empty(geom.v_pool_shape, dtype=geom.torch_dtype, device=device)
+    return k, v
+
+
+# --------------------------------------------------------------------- device ops
+def append_kv(geom: Geometry, k_pool, v_pool, layer: int, k_new, v_new, slot_mapping, stream=None):
+    n = slot_mapping.numel()
+    _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
+    _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
+    per = geom.num_kv_heads * geom.head_dim
+    _dev(k_new, "k_new", geom.torch_dtype, n * per)
+    _dev(v_new, "v_new", geom.torch_dtype, n * per)
+    _dev(slot_mapping, "slot_mapping", torch.int64)
+    g = geom.c()
+    check(_L().pa_append_kv(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(k_new),
+                            _ptr(v_new), _ptr(slot_mapping), n, _stream(stream, k_pool.device)),
+          "pa_append_kv")
+
+
+def _opts(blocks_per_split: int, kernel: int) -> _lib.pa_decode_opts:
+    return _lib.pa_decode_opts(int(blocks_per_split), int(kernel))
+
+
+KERNELS = {"auto": 0, "generic": 1, "mfma": 2}
+
+
+def decode_workspace_bytes(geom: Geometry, n_seqs: int, n_q_heads: int, max_context_len: int,
+                           blocks_per_split: int = 0, kernel: str = "auto") -> int:
+    g = geom.c()
+    o = _opts(blocks_per_split, KERNELS[kernel])
+    return int(_L().pa_decode_workspace_bytes(C.byref(g), n_seqs, n_q_heads, max_context_len,
+                                              C.byref(o)))
+
+
+def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, context_lens,
+           max_context_len: int, scale: float = 0.0, workspace=None, blocks_per_split: int = 0,
+           kernel: str = "auto", stream=None):
+    """out[i, h] = softmax attention of q[i, h] over sequence i's first
+    context_lens[i] tokens, read through block_tables[i]."""
+    _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
+    _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
+    if q.dim() != 3 or q.shape[2] != geom.head_dim:
+        raise ValueError("q must be [n_seqs, n_q_heads, head_dim]")
+    n, hq = int(q.shape[0]), int(q.shape[1])
+    _dev(q, "q", geom.torch_dtype)
+    _dev(out, "out", geom.torch_dtype, q.numel())
+    if block_tables.dim() != 2 or block_tables.shape[0] != n:
+        raise ValueError("block_tables must be [n_seqs, max_blocks]")
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(context_lens, "context_lens", torch.int32, n)
+    g = geom.c()
+    o = _opts(blocks_per_split, KERNELS[kernel])
+    need = int(_L().pa_decode_workspace_bytes(C.byref(g), n, hq, max_context_len, C.byref(o)))
+    ws_ptr, ws_bytes = None, 0
+    if need:
+        if workspace is None:
+            raise ValueError(f"decode needs a workspace of {need} bytes")
+        _dev(workspace, "workspace")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    check(_L().pa_decode(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(q), _ptr(out), n, hq,
+                         _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
+                         int(max_context_len), float(scale), C.byref(o), ws_ptr, ws_bytes,
+                         _stream(stream, q.device)),
+          "pa_decode")
+
+
+def _ids(t, what, n=None):
+    _dev(t, what, torch.int32, n)
+
+
+def copy_blocks(geom: Geometry, k_pool, v_pool, src, dst, stream=None):
+    _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
+    _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
+    n = src.numel()
+    _ids(src, "src")
+    _ids(dst, "dst", n)
+    g = geom.c()
+    check(_L().pa_copy_blocks(C.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(src), _ptr(dst), n,
+                              _stream(stream, k_pool.device)), "pa_copy_blocks")
+
+
+def gather_blocks(geom: Geometry, k_pool, v_pool, block_ids, staging, stream=None):
+    _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
+    _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
+    n = block_ids.numel()
+    _ids(block_ids, "block_ids")
+    _dev(staging, "staging")
+    if staging.numel() * staging.element_size() < n * bytes_per_block(geom):
+        raise ValueError("staging buffer too small")
+    g = geom.c()
+    check(_L().pa_gather_blocks(C.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(block_ids), n,
+                                _ptr(staging), _stream(stream, k_pool.device)), "pa_gather_blocks")
+
+
+def scatter_blocks(geom: Geometry, k_pool, v_pool, staging, block_ids, stream=None):
+    _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
+    _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
+    n = block_ids.numel()
+    _ids(block_ids, "block_ids")
+    _dev(staging, "staging")
+    if staging.numel() * staging.element_size() < n * bytes_per_block(geom):
+        raise ValueError("staging buffer too small")
+    g = geom.c()
+    check(_L().pa_scatter_blocks(C.byref(g), _ptr(k_pool), _ptr(v_pool), _ptr(staging),
+                                 _ptr(block_ids), n, _stream(stream, k_pool.device)),
+          "pa_scatter_blocks")
+
+
+def copy_to_host(host_dst: torch.Tensor, device_src: torch.Tensor, nbytes: Optional[int] = None,
+                 stream=None):
+    if host_dst.is_cuda or not device_src.is_cuda:
+        raise ValueError("copy_to_host: host_dst on the host, device_src on the device")
+    if not host_dst.is_contiguous() or not device_src.is_contiguous():
+        raise ValueError("copy_to_host: contiguous tensors only")
+    cap = min(host_dst.numel() * host_dst.element_size(), device_src.numel() * device_src.element_size())
+    nbytes = cap if nbytes is None else int(nbytes)
+    if nbytes > cap:
+        raise ValueError("copy_to_host: nbytes exceeds a buffer")
+    check(_L().pa_copy_to_host(_ptr(host_dst), _ptr(device_src), nbytes,
+                               _stream(stream, device_src.device)), "pa_copy_to_host")
+
+
+def copy_to_device(device_dst: torch.Tensor, host_src: torch.Tensor, nbytes: Optional[int] = None,
+                   stream=None):
+    if host_src.is_cuda or not device_dst.is_cuda:
+        raise ValueError("copy_to_device: host_src on the host, device_dst on the device")
+    if not host_src.is_contiguous() or not device_dst.is_contiguous():
+        raise ValueError("copy_to_device: contiguous tensors only")
+    cap = min(host_src.numel() * host_src.element_size(), device_dst.numel() * device_dst.element_size())
+    nbytes = cap if nbytes is None else int(nbytes)
+    if nbytes > cap:
+        raise ValueError("copy_to_device: nbytes exceeds a buffer")
+    check(_L().pa_copy_to_device(_ptr(device_dst), _ptr(host_src), nbytes,
+                                 _stream(stream, device_dst.device)), "pa_copy_to_device")
+
+
+# --------------------------------------------------------------------- timing
+class Profiler:
+    """Per-kernel launch timing recorded by the library with hipEvents."""
+
+    @staticmethod
+    def enable(on: bool = True):
+        check(_L().pa_prof_enable(1 if on else 0), "pa_prof_enable")
+
+    @staticmethod
+    def reset():
+        check(_L().pa_prof_reset(), "pa_prof_reset")
+
+    @staticmethod
+    def read(kernel: str):
+        n, ms = C.c_int64(0), C.c_double(0.0)
+        check(_L().pa_prof_read(kernel.encode(), C.byref(n), C.byref(ms)), "pa_prof_read")
+        return int(n.value), float(ms.value)
+
+
+# --------------------------------------------------------------------- block manager
+def _i32arr(values) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+
+
+def _p32(a: np.ndarray):
+    return a.ctypes.data_as(C.POINTER(C.c_int32))
+
+
+def _p64(a: np.ndarray):
+    return a.ctypes.data_as(C.POINTER(C.c_int64))
+
+
+class BlockManager:
+    """Host block manager of libpa (free list, reference counts, block tables)."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        self._lib = _L()
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        h = C.c_void_p()
+        fo = None if free_order is None else _i32arr(free_order)
+        if fo is not None and fo.size != num_blocks:
+            raise ValueError("free_order must list every block once")
+        check(self._lib.pa_bm_create(num_blocks, block_size, None if fo is None else _p32(fo),
+                                     C.byref(h)), "pa_bm_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def num_free(self) -> int:
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pa_bm_refcount(self._h, block))
+
+    def alloc(self, n: int):
+        out = np.empty(max(n, 1), np.int32)
+        check(self._lib.pa_bm_alloc(self._h, n, _p32(out)), "pa_bm_alloc")
+        return out[:n].tolist()
+
+    def incref(self, ids):
+        a = _i32arr(ids)
+        check(self._lib.pa_bm_incref(self._h, _p32(a), a.size), "pa_bm_incref")
+
+    def free_blocks(self, ids):
+        a = _i32arr(ids)
+        check(self._lib.pa_bm_free_blocks(self._h, _p32(a), a.size), "pa_bm_free_blocks")
+
+    def seq_new(self) -> int:
+        s = C.c_int32()
+        check(self._lib.pa_bm_seq_new(self._h, C.byref(s)), "pa_bm_seq_new")
+        return s.value
+
+    def fork(self, parent: int) -> int:
+        s = C.c_int32()
+        check(self._lib.pa_bm_seq_fork(self._h, parent, C.byref(s)), "pa_bm_seq_fork")
+        return s.value
+
+    def append(self, seq: int, n_tokens: int):
+        """Returns (slots as int64 numpy array, list of (src, dst) copy pairs)."""
+        slots = np.empty(max(n_tokens, 1), np.int64)
+        src, dst, nc = C.c_int32(), C.c_int32(), C.c_int32()
+        check(self._lib.pa_bm_seq_append(self._h, seq, n_tokens, _p64(slots), C.byref(src),
+                                         C.byref(dst), C.byref(nc)), "pa_bm_seq_append")
+        pairs = [(src.value, dst.value)] if nc.value else []
+        return slots[:n_tokens], pairs
+
+    def append_batch(self, seqs, counts):
+        s, c = _i32arr(seqs), _i32arr(counts)
+        total = int(c.sum()) if c.size else 0
+        slots = np.empty(max(total, 1), np.int64)
+        cs, cd = np.empty(max(s.size, 1), np.int32), np.empty(max(s.size, 1), np.int32)
+        nc = C.c_int32()
+        check(self._lib.pa_bm_append_batch(self._h, _p32(s), _p32(c), s.size, _p64(slots),
+                                           _p32(cs), _p32(cd), C.byref(nc)), "pa_bm_append_batch")
+        return slots[:total], list(zip(cs[:nc.value].tolist(), cd[:nc.value].tolist()))
+
+    def release(self, seq: int):
+        check(self._lib.pa_bm_seq_release(self._h, seq), "pa_bm_seq_release")
+
+    def swap_out(self, seq: int, logical):
+        a = _i32arr(logical)
+        out = np.empty(max(a.size, 1), np.int32)
+        check(self._lib.pa_bm_seq_swap_out(self._h, seq, _p32(a), a.size, _p32(out)),
+              "pa_bm_seq_swap_out")
+        return out[:a.size].tolist()
+
+    def swap_in(self, seq: int, logical):
+        a = _i32arr(logical)
+        out = np.empty(max(a.size, 1), np.int32)
+        check(self._lib.pa_bm_seq_swap_in(self._h, seq, _p32(a), a.size, _p32(out)),
+              "pa_bm_seq_swap_in")
+        return out[:a.size].tolist()
+
+    def info(self, seq: int):
+        n, b = C.c_int64(), C.c_int32()
+        check(self._lib.pa_bm_seq_info(self._h, seq, C.byref(n), C.byref(b)), "pa_bm_seq_info")
+        return n.value, b.value
+
+    def length(self, seq: int) -> int:
+        return self.info(seq)[0]
+
+    def table(self, seq: int):
+        _, nb = self.info(seq)
+        out = np.empty(max(nb, 1), np.int32)
+        m = C.c_int32()
+        check(self._lib.pa_bm_seq_table(self._h, seq, _p32(out), nb, C.byref(m)), "pa_bm_seq_table")
+        return out[:nb].tolist()
+
+    def build_tables(self, seqs, max_blocks: int, pad: int = 0):
+        """(tables int32 [n, max_blocks], lens int32 [n]) as numpy arrays."""
+        s = _i32arr(seqs)
+        tables = np.empty((max(s.size, 1), max(max_blocks, 1)), np.int32)
+        lens = np.empty(max(s.size, 1), np.int32)
+        check(self._lib.pa_bm_build_tables(self._h, _p32(s), s.size, max_blocks, pad, _p32(tables),
+                                           _p32(lens)), "pa_bm_build_tables")
+        return tables[:s.size, :max_blocks], lens[:s.size]
+
+    def validate(self):
+        check(self._lib.pa_bm_validate(self._h), "pa_bm_validate")

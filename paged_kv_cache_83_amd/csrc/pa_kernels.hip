@@ -1,0 +1,908 @@
+// Device side of libpa for gfx950 (CDNA4, wave64): slot-mapped KV append,
+// split-K paged decode (MFMA kernel for bf16 with 16-slot blocks, generic VALU
+// kernel for every other supported shape), the cross-split combine, and the
+// whole-block copy / gather / scatter kernels.
+//
+// Sources on the pages:
+//   "KV Cache Management", section "The PagedAttention virtual memory model":
+//     token t of a sequence lives in logical block l = t / B at offset t mod B;
+//     the decode kernel takes the block table as an input, loads the physical
+//     block ids on chip and walks the logical blocks 0..floor((S-1)/B).
+//   Same page, section "Chunked prefill mechanics": the running maximum m and
+//     normaliser l, with the accumulator rescaled by exp(m_prev - m_new) as each
+//     tile of keys arrives; the same rule merges the split partials.
+//   Same page, sections "Zero-copy deliberation via copy-on-write branching"
+//     (copy a shared block into a fresh one) and "Asynchronous paged swapping"
+//     (move frames of bytes_per_block between the pool and a staging buffer).
+//
+// Pool layout (the interface fixes it): K [L][N][H_kv][B][d], V [L][N][H_kv][d][B].
+// Keeping V dimension-major inside a block means a 16-byte load of V gives 8
+// consecutive slots of one dimension, which is exactly the operand fragment the
+// PV matrix-core instruction wants; K is slot-major, which is what QK^T wants.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/pa.h"
+
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even; NaN stays a quiet NaN of the same sign.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Attended length of sequence i, clamped into [0, max_ctx].
+__device__ __forceinline__ int clamp_len(const int32_t* lens, int i, int max_ctx) {
+  int len = lens[i];
+  return len < 0 ? 0 : (len > max_ctx ? max_ctx : len);
+}
+
+__device__ __forceinline__ int guard_block(int p, int N) { return (p >= 0 && p < N) ? p : 0; }
+
+// =============================================================================
+// Append: token j's K/V go to slot slot_mapping[j] of one layer.
+// One thread moves VEC consecutive elements of one (token, head).
+// =============================================================================
+template <typename T, int VEC>
+__global__ void append_kv_kernel(T* __restrict__ kpool, T* __restrict__ vpool,
+                                 const T* __restrict__ knew, const T* __restrict__ vnew,
+                                 const int64_t* __restrict__ slots, int n_tok, int Hkv, int D,
+                                 int B, int64_t nslots, int64_t layer_off) {
+  const int chunks = D / VEC;
+  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)n_tok * Hkv * chunks;
+  if (tid >= total) return;
+  const int c = (int)(tid % chunks);
+  const int64_t th = tid / chunks;
+  const int h = (int)(th % Hkv);
+  const int64_t j = th / Hkv;
+  const int64_t slot = slots[j];
+  if (slot < 0 || slot >= nslots) return;
+  const int64_t p = slot / B;
+  const int o = (int)(slot % B);
+  const int64_t src = (j * Hkv + h) * D + (int64_t)c * VEC;
+  const int64_t tile = layer_off + (p * Hkv + h) * (int64_t)B * D;
+  T kv[VEC], vv[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    kv[e] = knew[src + e];
+    vv[e] = vnew[src + e];
+  }
+  T* kd = kpool + tile + (int64_t)o * D + (int64_t)c * VEC;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) kd[e] = kv[e];
+  T* vd = vpool + tile + (int64_t)c * VEC * B + o;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) vd[(int64_t)e * B] = vv[e];
+}
+
+// =============================================================================
+// Whole-block moves. A "run" is one (layer, block, K-or-V) stretch of
+// H_kv*B*d elements, contiguous in the pool. MODE 0: pool -> pool (copy-on-write
+// copy, ids_a = src, ids_b = dst). MODE 1: pool -> staging (gather). MODE 2:
+// staging -> pool (scatter). One work-group moves one run.
+// =============================================================================
+template <int MODE, typename V>
+__global__ __launch_bounds__(256) void block_move_kernel(char* __restrict__ kpool,
+                                                         char* __restrict__ vpool,
+                                                         char* __restrict__ staging,
+                                                         const int32_t* __restrict__ ids_a,
+                                                         const int32_t* __restrict__ ids_b,
+                                                         int L, int N, int64_t run_bytes) {
+  const int64_t r = blockIdx.x;
+  const int kv = (int)(r & 1);
+  const int layer = (int)((r >> 1) % L);
+  const int64_t i = (r >> 1) / L;
+  char* pool = kv ? vpool : kpool;
+  const char* src;
+  char* dst;
+  if (MODE == 0) {
+    int a = ids_a[i], b = ids_b[i];
+    if (a < 0 || a >= N || b < 0 || b >= N) return;
+    src = pool + ((int64_t)layer * N + a) * run_bytes;
+    dst = pool + ((int64_t)layer * N + b) * run_bytes;
+  } else {
+    int a = ids_a[i];
+    if (a < 0 || a >= N) return;
+    char* p = pool + ((int64_t)layer * N + a) * run_bytes;
+    char* s = staging + (((i * L) + layer) * 2 + kv) * run_bytes;
+    src = (MODE == 1) ? p : s;
+    dst = (MODE == 1) ? s : p;
+  }
+  const V* sv = reinterpret_cast<const V*>(src);
+  V* dv = reinterpret_cast<V*>(dst);
+  const int64_t n = run_bytes / (int64_t)sizeof(V);
+  constexpr int U = 4;
+  for (int64_t base = threadIdx.x; base < n; base += (int64_t)blockDim.x * U) {
+    V tmp[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t k = base + (int64_t)u * blockDim.x;
+      if (k < n) tmp[u] = __builtin_nontemporal_load(sv + k);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int64_t k = base + (int64_t)u * blockDim.x;
+      if (k < n) __builtin_nontemporal_store(tmp[u], dv + k);
+    }
+  }
+}
+
+// =============================================================================
+// Decode, MFMA kernel: bf16 pool, B = 16, d in {64, 128, 256}, up to 16 query
+// heads per KV head. One wave = one work item (sequence i, KV head g, split s)
+// covering logical blocks [s*bps, min((s+1)*bps, nblk)), bps even.
+//
+// Per pair of blocks (32 keys) it issues two 16x16x32 bf16 MFMA chains:
+//   S^T[32 keys][16 q] = K[keys][d] . Q^T[d][q]     (d/32 steps, two row tiles)
+//   O^T[d][16 q]      += V^T[d][keys] . P^T[keys][q] (d/16 row tiles)
+// Lane l = (c = l%16, gq = l/16). MFMA operand layout on gfx950 (checked on
+// the device): A[row = c][k = 8*gq + j], B[k = 8*gq + j][col = c],
+// C[row = 4*gq + i][col = c]. Rows of the score tiles are assigned to keys so
+// that lane l ends up holding the 8 scores of keys 8*gq .. 8*gq+7 (pair-local)
+// for query c -- which is exactly the B-operand fragment of the PV product, so
+// probabilities never leave registers. K rows and V^T rows are each fetched
+// with 16-byte loads straight from the pool.
+// =============================================================================
+template <int D>
+struct MfmaCfg {
+  static constexpr int KC = D / 32;  // QK k-steps
+  static constexpr int DT = D / 16;  // PV row tiles
+};
+
+template <int D, bool DIRECT>
+__global__ __launch_bounds__(64) void decode_mfma_bf16_kernel(
+    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ out, float* __restrict__ part_o,
+    float* __restrict__ part_ml, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lens, int64_t layer_off, int N, int Hkv, int Hq, int G,
+    int max_blocks, int max_ctx, int bps, int S_max, float qk_scale) {
+  constexpr int KC = MfmaCfg<D>::KC;
+  constexpr int DT = MfmaCfg<D>::DT;
+  constexpr int TILE = 16 * D;  // elements of one (block, head) run
+
+  const int w = blockIdx.x;
+  const int s = w % S_max;
+  const int gi = w / S_max;
+  const int g = gi % Hkv;
+  const int i = gi / Hkv;
+  const int lane = threadIdx.x;
+  const int c = lane & 15;
+  const int gq = lane >> 4;
+
+  const int len = clamp_len(lens, i, max_ctx);
+  const int nblk = (len + 15) >> 4;
+  const int b0 = s * bps;
+  const int h = g * G + c;
+  const bool qvalid = c < G;
+  if (b0 >= nblk) {
+    if (DIRECT && len == 0 && qvalid) {
+      uint16_t* o = out + ((int64_t)i * Hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[16 * dt + 4 * gq + e] = 0;
+      }
+    }
+    return;
+  }
+  const int b1 = min(b0 + bps, nblk);
+
+  // Q fragments (B operand of QK): Q[h][32*kc + 8*gq .. +8]; zero for padded columns.
+  bf16x8 qf[KC];
+  {
+    const uint16_t* qrow = q + ((int64_t)i * Hq + (qvalid ? h : 0)) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qvalid) v = *reinterpret_cast<const uint4*>(qrow + 32 * kc + 8 * gq);
+      qf[kc] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const int32_t* trow = tables + (int64_t)i * max_blocks;
+  const uint16_t* kl = kpool + layer_off;
+  const uint16_t* vl = vpool + layer_off;
+  // Row r = c of each score tile holds pair-local key 8*(c>>2) + 4*t + (c&3):
+  // block (c >> 3) of the pair, offset 8*((c>>2)&1) + 4*t + (c&3).
+  const int k_blk_sel = c >> 3;
+  const int k_off0 = 8 * ((c >> 2) & 1) + (c & 3);
+  // V^T fragment of lane: block (gq >> 1), dims 16*dt + c, slots 8*(gq&1) .. +8.
+  const int v_blk_sel = gq >> 1;
+  const int v_off = 16 * c + 8 * (gq & 1);
+
+  for (int base = b0; base < b1; base += 64) {
+    // The split's block ids, one per lane, read once ("load the physical block
+    // pointers on chip"); each pair below takes its two ids from lanes.
+    const int cnt = min(64, b1 - base);
+    int tb = 0;
+    if (lane < cnt) tb = guard_block(trow[base + lane], N);
+    for (int j = 0; j < cnt; j += 2) {
+      const int p0 = __builtin_amdgcn_readlane(tb, j);
+      const int p1 = (j + 1 < cnt) ? __builtin_amdgcn_readlane(tb, j + 1) : p0;
+      const int blk = base + j;
+
+      const uint16_t* krow = kl + ((int64_t)(k_blk_sel ? p1 : p0) * Hkv + g) * TILE;
+      const uint16_t* vrow = vl + ((int64_t)(v_blk_sel ? p1 : p0) * Hkv + g) * TILE;
+      uint4 kf[2][KC];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          kf[t][kc] = *reinterpret_cast<const uint4*>(krow + (k_off0 + 4 * t) * D + 32 * kc + 8 * gq);
+      }
+      uint4 vf[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        vf[dt] = *reinterpret_cast<const uint4*>(vrow + dt * 256 + v_off);
+
+      f32x4 sc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[t][kc]),
+                                                          qf[kc], sc[t], 0, 0, 0);
+      }
+      // Lane holds scores of pair-local keys 8*gq + 4*t + e for query c.
+      const int pos0 = blk * 16 + 8 * gq;
+      float sv[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sv[4 * t + e] = (pos0 + 4 * t + e < len) ? sc[t][e] * qk_scale : -INFINITY;
+      }
+      float mb = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mb = fmaxf(mb, sv[e]);
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float m_new = fmaxf(m_run, mb);  // finite: the pair's first key is attended
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.f;
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float pa = exp2f(sv[e] - m_new);
+        const float pb = exp2f(sv[e + 1] - m_new);
+        psum += pa + pb;
+        pw[e >> 1] = (uint32_t)f32_to_bf16(pa) | ((uint32_t)f32_to_bf16(pb) << 16);
+      }
+      l_run = l_run * alpha + psum;
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+
+      // Slots at or past the length hold unspecified data (possibly NaN): their
+      // probability is 0, and their V elements are zeroed so 0 * V stays 0.
+      if (blk * 16 + 32 > len) {
+        uint32_t keep[4];
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) {
+          const int p = pos0 + 2 * wv;
+          keep[wv] = (p < len ? 0x0000ffffu : 0u) | (p + 1 < len ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          vf[dt].x &= keep[0];
+          vf[dt].y &= keep[1];
+          vf[dt].z &= keep[2];
+          vf[dt].w &= keep[3];
+        }
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        acc[dt] = acc[dt] * alpha;
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), pf,
+                                                          acc[dt], 0, 0, 0);
+      }
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (!qvalid) return;
+  // acc[dt][e] = O^T[d = 16*dt + 4*gq + e][q = c]
+  if (DIRECT) {
+    const float inv = 1.f / l_run;
+    uint16_t* o = out + ((int64_t)i * Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16(acc[dt][0] * inv) | ((uint32_t)f32_to_bf16(acc[dt][1] * inv) << 16);
+      pk.y = (uint32_t)f32_to_bf16(acc[dt][2] * inv) | ((uint32_t)f32_to_bf16(acc[dt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) = pk;
+    }
+  } else {
+    const int64_t row = ((int64_t)i * Hq + h) * S_max + s;
+    float* po = part_o + row * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * gq) =
+          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (gq == 0) {
+      part_ml[row * 2 + 0] = m_run;
+      part_ml[row * 2 + 1] = l_run;
+    }
+  }
+}
+
+// =============================================================================
+// Decode, generic kernel (fp32 or bf16; B <= 64, d <= 256, B*d <= 4096,
+// G*d <= 4096). One wave per (sequence, KV head, split). Each block's K and V
+// tiles are staged in LDS as fp32; scores, the online-softmax update and the
+// PV accumulation run on the vector ALUs in fp32.
+// =============================================================================
+constexpr int kGenMaxAcc = 64;  // largest G*d / 64 the generic kernel accepts
+
+// R = accumulators per lane, ceil(G*d / 64) rounded up to one of 1, 4, 16, 64.
+template <typename T, bool DIRECT, int R>
+__global__ __launch_bounds__(64) void decode_generic_kernel(
+    const T* __restrict__ kpool, const T* __restrict__ vpool, const T* __restrict__ q,
+    T* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ lens, int64_t layer_off, int N,
+    int Hkv, int Hq, int G, int D, int B, int max_blocks, int max_ctx, int bps, int S_max,
+    float qk_scale) {
+  extern __shared__ float smem[];
+  float* Qs = smem;            // [G][D]
+  float* Ks = Qs + G * D;      // [B][D]
+  float* Vs = Ks + B * D;      // [D][B]
+  float* Ps = Vs + B * D;      // [G][B]
+  float* As = Ps + G * B;      // [G]
+
+  const int w = blockIdx.x;
+  const int s = w % S_max;
+  const int gi = w / S_max;
+  const int g = gi % Hkv;
+  const int i = gi / Hkv;
+  const int lane = threadIdx.x;
+  const int GD = G * D;
+
+  const int len = clamp_len(lens, i, max_ctx);
+  const int nblk = (len + B - 1) / B;
+  const int b0 = s * bps;
+  if (b0 >= nblk) {
+    if (DIRECT && len == 0) {
+      T* o = out + ((int64_t)i * Hq + (int64_t)g * G) * D;
+      for (int idx = lane; idx < GD; idx += 64) o[idx] = from_f32<T>(0.f);
+    }
+    return;
+  }
+  const int b1 = min(b0 + bps, nblk);
+
+  const T* qg = q + ((int64_t)i * Hq + (int64_t)g * G) * D;  // the group's heads are contiguous
+  for (int idx = lane; idx < GD; idx += 64) Qs[idx] = to_f32<T>(qg[idx]);
+
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;  // lane q < G owns query q's statistics
+
+  const int32_t* trow = tables + (int64_t)i * max_blocks;
+  const int BD = B * D;
+  for (int blk = b0; blk < b1; ++blk) {
+    const int p = guard_block(trow[blk], N);
+    const T* kt = kpool + layer_off + ((int64_t)p * Hkv + g) * BD;
+    const T* vt = vpool + layer_off + ((int64_t)p * Hkv + g) * BD;
+    const int valid = min(B, len - blk * B);
+    __syncthreads();
+    for (int idx = lane; idx < BD; idx += 64) {
+      Ks[idx] = to_f32<T>(kt[idx]);
+      Vs[idx] = to_f32<T>(vt[idx]);
+    }
+    __syncthreads();
+    for (int idx = lane; idx < G * B; idx += 64) {
+      const int qi = idx / B, k = idx % B;
+      float sc = -INFINITY;
+      if (k < valid) {
+        float dot = 0.f;
+        for (int dd = 0; dd < D; ++dd) dot = fmaf(Qs[qi * D + dd], Ks[k * D + dd], dot);
+        sc = dot * qk_scale;
+      }
+      Ps[idx] = sc;
+    }
+    __syncthreads();
+    if (lane < G) {
+      float mb = -INFINITY;
+      for (int k = 0; k < valid; ++k) mb = fmaxf(mb, Ps[lane * B + k]);
+      const float m_new = fmaxf(m_run, mb);
+      const float alpha = exp2f(m_run - m_new);
+      float ps = 0.f;
+      for (int k = 0; k < B; ++k) {
+        const float pk = (k < valid) ? exp2f(Ps[lane * B + k] - m_new) : 0.f;
+        Ps[lane * B + k] = pk;
+        ps += pk;
+      }
+      l_run = l_run * alpha + ps;
+      m_run = m_new;
+      As[lane] = alpha;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = lane + 64 * r;
+      if (idx < GD) {
+        const int qi = idx / D, dd = idx % D;
+        float a = acc[r] * As[qi];
+        for (int k = 0; k < valid; ++k) a = fmaf(Ps[qi * B + k], Vs[dd * B + k], a);
+        acc[r] = a;
+      }
+    }
+  }
+  __syncthreads();
+  if (lane < G) {
+    As[lane] = l_run;
+    Ps[lane] = m_run;
+  }
+  __syncthreads();
+  if (DIRECT) {
+    T* o = out + ((int64_t)i * Hq + (int64_t)g * G) * D;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = lane + 64 * r;
+      if (idx < GD) o[idx] = from_f32<T>(acc[r] / As[idx / D]);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int idx = lane + 64 * r;
+      if (idx < GD) {
+        const int qi = idx / D, dd = idx % D;
+        const int64_t row = ((int64_t)i * Hq + (int64_t)g * G + qi) * S_max + s;
+        part_o[row * D + dd] = acc[r];
+      }
+    }
+    if (lane < G) {
+      const int64_t row = ((int64_t)i * Hq + (int64_t)g * G + lane) * S_max + s;
+      part_ml[row * 2 + 0] = m_run;
+      part_ml[row * 2 + 1] = l_run;
+    }
+  }
+}
+
+// =============================================================================
+// Combine: merge the splits of one (sequence, query head) with the online-softmax
+// rule: M = max_s m_s, w_s = 2^(m_s - M), out = sum_s w_s o_s / sum_s w_s l_s.
+// (m is kept in log2 units: scores were scaled by log2(e).)
+// =============================================================================
+template <typename T>
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ part_o,
+                                                            const float* __restrict__ part_ml,
+                                                            T* __restrict__ out,
+                                                            const int32_t* __restrict__ lens,
+                                                            int Hq, int D, int B, int S_max,
+                                                            int bps, int max_ctx) {
+  const int w = blockIdx.x;
+  const int h = w % Hq;
+  const int i = w / Hq;
+  const int lane = threadIdx.x;
+  const int len = clamp_len(lens, i, max_ctx);
+  const int nblk = (len + B - 1) / B;
+  const int ns = min(S_max, (nblk + bps - 1) / bps);
+  T* o = out + ((int64_t)i * Hq + h) * D;
+  if (ns == 0) {
+    for (int d = lane; d < D; d += 64) o[d] = from_f32<T>(0.f);
+    return;
+  }
+  const int64_t row0 = ((int64_t)i * Hq + h) * S_max;
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_ml[(row0 + s) * 2]);
+  M = wave_max(M);
+  float Lsum = 0.f;
+  for (int s = lane; s < ns; s += 64)
+    Lsum += exp2f(part_ml[(row0 + s) * 2] - M) * part_ml[(row0 + s) * 2 + 1];
+  Lsum = wave_sum(Lsum);
+  const float inv = 1.f / Lsum;
+  for (int d = lane; d < D; d += 64) {
+    float a = 0.f;
+    for (int s = 0; s < ns; ++s) a = fmaf(exp2f(part_ml[(row0 + s) * 2] - M), part_o[(row0 + s) * D + d], a);
+    o[d] = from_f32<T>(a * inv);
+  }
+}
+
+// =============================================================================
+// Host-side helpers: argument checks, launch timing.
+// =============================================================================
+bool geom_ok(const pa_geom* g) {
+  return g && g->num_layers > 0 && g->num_kv_heads > 0 && g->head_dim > 0 && g->block_size > 0 &&
+         g->num_blocks > 0 && (g->dtype == PA_F32 || g->dtype == PA_BF16);
+}
+int64_t esize(const pa_geom* g) { return g->dtype == PA_F32 ? 4 : 2; }
+
+struct ProfRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+struct ProfAcc {
+  std::string name;
+  int64_t launches = 0;
+  double ms = 0.0;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_pending;
+std::vector<ProfAcc> g_prof_acc;
+
+struct ProfScope {
+  const char* name;
+  hipStream_t st;
+  hipEvent_t a = nullptr, b = nullptr;
+  bool on;
+  ProfScope(const char* n, hipStream_t s) : name(n), st(s), on(false) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) return;
+    if (hipEventCreate(&a) != hipSuccess) return;
+    if (hipEventCreate(&b) != hipSuccess) {
+      (void)hipEventDestroy(a);
+      return;
+    }
+    on = hipEventRecord(a, st) == hipSuccess;
+  }
+  ~ProfScope() {
+    if (!on) return;
+    (void)hipEventRecord(b, st);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_pending.push_back({name, a, b});
+  }
+};
+
+pa_status launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+size_t generic_lds_bytes(int G, int D, int B) {
+  return sizeof(float) * ((size_t)G * D + 2 * (size_t)B * D + (size_t)G * B + G + 64);
+}
+
+struct DecodePlan {
+  int kernel;  // 1 generic, 2 mfma
+  int bps;
+  int S_max;
+  bool direct;
+  size_t ws;
+};
+
+pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ctx,
+                    const pa_decode_opts* opts, DecodePlan* plan) {
+  if (!geom_ok(g) || n_seqs < 0 || Hq <= 0 || max_ctx < 0) return PA_ERR_INVALID_ARG;
+  if (Hq % g->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+  const int D = g->head_dim, B = g->block_size, G = Hq / g->num_kv_heads;
+  const bool mfma_ok = g->dtype == PA_BF16 && B == 16 && (D == 64 || D == 128 || D == 256) && G <= 16;
+  const size_t gen_lds = generic_lds_bytes(G, D, B);
+  const bool gen_ok = B <= 64 && D <= 256 && B * D <= 4096 && G * D <= 64 * kGenMaxAcc && G <= 64 &&
+                      gen_lds <= 65536;
+  const int want = opts ? opts->kernel : 0;
+  int k;
+  if (want == 1) {
+    if (!gen_ok) return PA_ERR_UNSUPPORTED;
+    k = 1;
+  } else if (want == 2) {
+    if (!mfma_ok) return PA_ERR_UNSUPPORTED;
+    k = 2;
+  } else if (want == 0) {
+    if (mfma_ok) k = 2;
+    else if (gen_ok) k = 1;
+    else return PA_ERR_UNSUPPORTED;
+  } else {
+    return PA_ERR_INVALID_ARG;
+  }
+  const int64_t maxb = ((int64_t)max_ctx + B - 1) / B;
+  int64_t bps;
+  if (opts && opts->blocks_per_split > 0) {
+    bps = opts->blocks_per_split;
+  } else {
+    const int64_t units = (int64_t)n_seqs * g->num_kv_heads;
+    if (units >= 1024 || units == 0) {
+      bps = maxb;
+    } else {
+      const int64_t want_splits = (4096 + units - 1) / units;
+      bps = std::max<int64_t>(16, (maxb + want_splits - 1) / want_splits);
+    }
+  }
+  bps = std::max<int64_t>(2, bps);
+  bps += bps & 1;  // pairs of blocks never straddle two splits
+  if (bps > INT32_MAX / 2) bps = INT32_MAX / 2;
+  int64_t S = maxb == 0 ? 1 : (maxb + bps - 1) / bps;
+  plan->kernel = k;
+  plan->bps = (int)bps;
+  plan->S_max = (int)S;
+  plan->direct = S == 1;
+  plan->ws = plan->direct ? 0 : (size_t)n_seqs * Hq * S * (D + 2) * sizeof(float);
+  return PA_OK;
+}
+
+}  // namespace
+
+// =============================================================================
+// C ABI
+// =============================================================================
+extern "C" {
+
+pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer,
+                       const void* k_new, const void* v_new, const int64_t* slot_mapping,
+                       int32_t n_tokens, void* stream) {
+  if (!geom_ok(g) || layer < 0 || layer >= g->num_layers || n_tokens < 0) return PA_ERR_INVALID_ARG;
+  if (n_tokens == 0) return PA_OK;
+  if (!k_pool || !v_pool || !k_new || !v_new || !slot_mapping) return PA_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const int D = g->head_dim, B = g->block_size, H = g->num_kv_heads;
+  const int64_t layer_off = (int64_t)layer * g->num_blocks * H * B * D;
+  const int64_t nslots = (int64_t)g->num_blocks * B;
+  ProfScope ps("append", st);
+  if (g->dtype == PA_BF16) {
+    const bool v8 = D % 8 == 0;
+    const int vec = v8 ? 8 : 1;
+    const int64_t total = (int64_t)n_tokens * H * (D / vec);
+    const int64_t blocks = (total + 255) / 256;
+    if (v8)
+      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 8>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_new,
+                         (const uint16_t*)v_new, slot_mapping, n_tokens, H, D, B, nslots, layer_off);
+    else
+      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 1>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_new,
+                         (const uint16_t*)v_new, slot_mapping, n_tokens, H, D, B, nslots, layer_off);
+  } else {
+    const bool v4 = D % 4 == 0;
+    const int vec = v4 ? 4 : 1;
+    const int64_t total = (int64_t)n_tokens * H * (D / vec);
+    const int64_t blocks = (total + 255) / 256;
+    if (v4)
+      hipLaunchKernelGGL((append_kv_kernel<float, 4>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         (float*)k_pool, (float*)v_pool, (const float*)k_new, (const float*)v_new,
+                         slot_mapping, n_tokens, H, D, B, nslots, layer_off);
+    else
+      hipLaunchKernelGGL((append_kv_kernel<float, 1>), dim3((unsigned)blocks), dim3(256), 0, st,
+                         (float*)k_pool, (float*)v_pool, (const float*)k_new, (const float*)v_new,
+                         slot_mapping, n_tokens, H, D, B, nslots, layer_off);
+  }
+  return launch_status();
+}
+
+size_t pa_decode_workspace_bytes(const pa_geom* g, int32_t n_seqs, int32_t n_q_heads,
+                                 int32_t max_context_len, const pa_decode_opts* opts) {
+  DecodePlan plan;
+  if (make_plan(g, n_seqs, n_q_heads, max_context_len, opts, &plan) != PA_OK) return 0;
+  return plan.ws;
+}
+
+pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, int32_t layer,
+                    const void* q, void* out, int32_t n_seqs, int32_t n_q_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, float scale,
+                    const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  DecodePlan plan;
+  pa_status st0 = make_plan(g, n_seqs, n_q_heads, max_context_len, opts, &plan);
+  if (st0 != PA_OK) return st0;
+  if (layer < 0 || layer >= g->num_layers || max_blocks_per_seq < 0) return PA_ERR_INVALID_ARG;
+  const int B = g->block_size, D = g->head_dim, Hkv = g->num_kv_heads;
+  if ((int64_t)max_blocks_per_seq * B < max_context_len) return PA_ERR_INVALID_ARG;
+  if (n_seqs == 0) return PA_OK;
+  if (!k_pool || !v_pool || !q || !out || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  if (!plan.direct && (!workspace || workspace_bytes < plan.ws)) return PA_ERR_WORKSPACE;
+  const int64_t items = (int64_t)n_seqs * Hkv * plan.S_max;
+  if (items > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+  const float qk_scale = scale * kLog2e;
+  const int G = n_q_heads / Hkv;
+  const int64_t layer_off = (int64_t)layer * g->num_blocks * Hkv * B * D;
+  float* part_o = (float*)workspace;
+  float* part_ml = plan.direct ? nullptr : part_o + (size_t)n_seqs * n_q_heads * plan.S_max * D;
+  {
+    ProfScope ps("decode_partial", st);
+    const dim3 grid((unsigned)items), block(64);
+    if (plan.kernel == 2) {
+#define PA_MFMA_LAUNCH(DD, DIR)                                                                   \
+  hipLaunchKernelGGL((decode_mfma_bf16_kernel<DD, DIR>), grid, block, 0, st,                      \
+                     (const uint16_t*)k_pool, (const uint16_t*)v_pool, (const uint16_t*)q,         \
+                     (uint16_t*)out, part_o, part_ml, block_tables, context_lens, layer_off,       \
+                     g->num_blocks, Hkv, n_q_heads, G, max_blocks_per_seq, max_context_len,        \
+                     plan.bps, plan.S_max, qk_scale)
+      if (D == 64) {
+        if (plan.direct) PA_MFMA_LAUNCH(64, true); else PA_MFMA_LAUNCH(64, false);
+      } else if (D == 128) {
+        if (plan.direct) PA_MFMA_LAUNCH(128, true); else PA_MFMA_LAUNCH(128, false);
+      } else {
+        if (plan.direct) PA_MFMA_LAUNCH(256, true); else PA_MFMA_LAUNCH(256, false);
+      }
+#undef PA_MFMA_LAUNCH
+    } else {
+      const size_t lds = generic_lds_bytes(G, D, B);
+#define PA_GEN_LAUNCH_R(T, DIR, RR)                                                               \
+  hipLaunchKernelGGL((decode_generic_kernel<T, DIR, RR>), grid, block, lds, st, (const T*)k_pool, \
+                     (const T*)v_pool, (const T*)q, (T*)out, part_o, part_ml, block_tables,        \
+                     context_lens, layer_off, g->num_blocks, Hkv, n_q_heads, G, D, B,              \
+                     max_blocks_per_seq, max_context_len, plan.bps, plan.S_max, qk_scale)
+#define PA_GEN_LAUNCH(T, DIR)                         \
+  do {                                                \
+    const int need = (G * D + 63) / 64;               \
+    if (need <= 1) PA_GEN_LAUNCH_R(T, DIR, 1);        \
+    else if (need <= 4) PA_GEN_LAUNCH_R(T, DIR, 4);   \
+    else if (need <= 16) PA_GEN_LAUNCH_R(T, DIR, 16); \
+    else PA_GEN_LAUNCH_R(T, DIR, 64);                 \
+  } while (0)
+      if (g->dtype == PA_F32) {
+        if (plan.direct) PA_GEN_LAUNCH(float, true); else PA_GEN_LAUNCH(float, false);
+      } else {
+        if (plan.direct) PA_GEN_LAUNCH(uint16_t, true); else PA_GEN_LAUNCH(uint16_t, false);
+      }
+#undef PA_GEN_LAUNCH_R
+#undef PA_GEN_LAUNCH
+    }
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  if (!plan.direct) {
+    ProfScope ps("decode_combine", st);
+    const dim3 grid((unsigned)((int64_t)n_seqs * n_q_heads)), block(64);
+    if (g->dtype == PA_F32)
+      hipLaunchKernelGGL((decode_combine_kernel<float>), grid, block, 0, st, part_o, part_ml,
+                         (float*)out, context_lens, n_q_heads, D, B, plan.S_max, plan.bps,
+                         max_context_len);
+    else
+      hipLaunchKernelGGL((decode_combine_kernel<uint16_t>), grid, block, 0, st, part_o, part_ml,
+                         (uint16_t*)out, context_lens, n_q_heads, D, B, plan.S_max, plan.bps,
+                         max_context_len);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+static pa_status block_move(int mode, const char* name, const pa_geom* g, void* k_pool,
+                            void* v_pool, void* staging, const int32_t* ids_a,
+                            const int32_t* ids_b, int32_t n, void* stream) {
+  if (!geom_ok(g) || n < 0) return PA_ERR_INVALID_ARG;
+  if (n == 0) return PA_OK;
+  if (!k_pool || !v_pool || !ids_a || (mode == 0 && !ids_b) || (mode != 0 && !staging))
+    return PA_ERR_INVALID_ARG;
+  const int64_t run = (int64_t)g->num_kv_heads * g->block_size * g->head_dim * esize(g);
+  const int64_t runs = (int64_t)n * g->num_layers * 2;
+  if (runs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  hipStream_t st = (hipStream_t)stream;
+  ProfScope ps(name, st);
+  const dim3 grid((unsigned)runs), block(256);
+#define PA_MOVE(M, V)                                                                             \
+  hipLaunchKernelGGL((block_move_kernel<M, V>), grid, block, 0, st, (char*)k_pool, (char*)v_pool, \
+                     (char*)staging, ids_a, ids_b, g->num_layers, g->num_blocks, run)
+#define PA_MOVE_MODE(M)                                            \
+  do {                                                             \
+    if (run % 16 == 0) PA_MOVE(M, u32x4);                          \
+    else if (run % 4 == 0) PA_MOVE(M, uint32_t);                   \
+    else PA_MOVE(M, uint16_t);                                     \
+  } while (0)
+  if (mode == 0) PA_MOVE_MODE(0);
+  else if (mode == 1) PA_MOVE_MODE(1);
+  else PA_MOVE_MODE(2);
+#undef PA_MOVE_MODE
+#undef PA_MOVE
+  return launch_status();
+}
+
+pa_status pa_copy_blocks(const pa_geom* g, void* k_pool, void* v_pool, const int32_t* src,
+                         const int32_t* dst, int32_t n_pairs, void* stream) {
+  return block_move(0, "copy_blocks", g, k_pool, v_pool, nullptr, src, dst, n_pairs, stream);
+}
+
+pa_status pa_gather_blocks(const pa_geom* g, const void* k_pool, const void* v_pool,
+                           const int32_t* block_ids, int32_t n, void* staging, void* stream) {
+  return block_move(1, "gather", g, const_cast<void*>(k_pool), const_cast<void*>(v_pool), staging,
+                    block_ids, nullptr, n, stream);
+}
+
+pa_status pa_scatter_blocks(const pa_geom* g, void* k_pool, void* v_pool, const void* staging,
+                            const int32_t* block_ids, int32_t n, void* stream) {
+  return block_move(2, "scatter", g, k_pool, v_pool, const_cast<void*>(staging), block_ids, nullptr,
+                    n, stream);
+}
+
+pa_status pa_copy_to_host(void* host_dst, const void* device_src, size_t bytes, void* stream) {
+  if (bytes == 0) return PA_OK;
+  if (!host_dst || !device_src) return PA_ERR_INVALID_ARG;
+  return hipMemcpyAsync(host_dst, device_src, bytes, hipMemcpyDeviceToHost, (hipStream_t)stream) ==
+                 hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+pa_status pa_copy_to_device(void* device_dst, const void* host_src, size_t bytes, void* stream) {
+  if (bytes == 0) return PA_OK;
+  if (!device_dst || !host_src) return PA_ERR_INVALID_ARG;
+  return hipMemcpyAsync(device_dst, host_src, bytes, hipMemcpyHostToDevice, (hipStream_t)stream) ==
+                 hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+pa_status pa_prof_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_on = on != 0;
+  return PA_OK;
+}
+
+static void prof_drain_locked() {
+  for (auto& r : g_prof_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      ProfAcc* acc = nullptr;
+      for (auto& x : g_prof_acc)
+        if (x.name == r.name) acc = &x;
+      if (!acc) {
+        g_prof_acc.push_back({r.name, 0, 0.0});
+        acc = &g_prof_acc.back();
+      }
+      acc->launches += 1;
+      acc->ms += ms;
+    }
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  g_prof_pending.clear();
+}
+
+pa_status pa_prof_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_drain_locked();
+  g_prof_acc.clear();
+  return PA_OK;
+}
+
+pa_status pa_prof_read(const char* kernel, int64_t* launches, double* total_ms) {
+  if (!kernel || !launches || !total_ms) return PA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  prof_drain_locked();
+  *launches = 0;
+  *total_ms = 0.0;
+  for (auto& x : g_prof_acc)
+    if (x.name == kernel) {
+      *launches = x.launches;
+      *total_ms = x.ms;
+    }
+  return PA_OK;
+}
+
+}  // extern "C"

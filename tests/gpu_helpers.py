@@ -1,0 +1,142 @@
+"""Helpers shared by the GPU tests: moving storage-form arrays between numpy and
+device tensors, and building a decode batch's inputs from the seeded generators.
+
+Both sides of every comparison start from the same numpy arrays; the library only
+ever sees device copies of them, and the oracle only ever sees host copies taken
+before any library kernel runs (or its own results).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import List
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import block_manager as obm
+from oracle import kv_ops as okv
+from oracle import layout as olayout
+from synth import gen
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch.device("cuda:0")
+
+
+def to_dev(a: np.ndarray, dtype: str) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def to_host(t: torch.Tensor, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.contiguous().cpu().numpy()
+
+
+def print_case(**kw):
+    print("CASE " + " ".join(f"{k}={v}" for k, v in kw.items()), flush=True)
+
+
+@dataclass
+class DecodeBatch:
+    """One decode step's inputs, in storage form on the host."""
+    dtype: str
+    L: int
+    N: int
+    Hq: int
+    Hkv: int
+    d: int
+    B: int
+    lengths: np.ndarray          # attended lengths (include the new token)
+    free_order: np.ndarray
+    k_pool: np.ndarray           # before the step's append
+    v_pool: np.ndarray
+    q: np.ndarray                # [n, Hq, d]
+    k_new: np.ndarray            # [n, Hkv, d]
+    v_new: np.ndarray
+    tables: List[List[int]]      # oracle block manager's tables after the step's reservation
+    slots_new: np.ndarray        # oracle slots of the new tokens
+    max_blocks: int
+
+
+def make_batch(dtype, L, N, Hq, Hkv, d, B, lengths, seed, poison=True) -> DecodeBatch:
+    """History tokens are reserved by the oracle block manager from a seeded
+    free order; pool values are standard normal; every slot no sequence uses
+    (including the slot the new token will take) is NaN when `poison`."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    n = len(lengths)
+    free_order = gen.permutation(seed, N)
+    bm = obm.BlockManager(N, B, free_order)
+    seqs = []
+    for S in lengths:
+        s = bm.seq_new()
+        bm.append(s, int(S) - 1 if S > 0 else 0)
+        seqs.append(s)
+    slots_new = []
+    for s, S in zip(seqs, lengths):
+        if S > 0:
+            sl, _ = bm.append(s, 1)
+            slots_new.append(sl[0])
+        else:
+            slots_new.append(-1)
+    tables = [bm.table(s) for s in seqs]
+    k_pool = gen.normal_values(seed + 1, olayout.k_pool_shape(L, N, Hkv, B, d), dtype)
+    v_pool = gen.normal_values(seed + 2, olayout.v_pool_shape(L, N, Hkv, B, d), dtype)
+    if poison:
+        nan = np.float32(np.nan) if dtype == "f32" else np.uint16(0x7FC0)
+        used = np.zeros((N, B), dtype=bool)
+        for t, S in zip(tables, lengths):
+            for pos in range(int(S) - 1):          # history only: the new token's slot stays NaN
+                used[t[pos // B], pos % B] = True
+        for p in range(N):
+            for o in range(B):
+                if not used[p, o]:
+                    k_pool[:, p, :, o, :] = nan
+                    v_pool[:, p, :, :, o] = nan
+    q = gen.normal_values(seed + 3, (n, Hq, d), dtype)
+    k_new = gen.normal_values(seed + 4, (n, Hkv, d), dtype)
+    v_new = gen.normal_values(seed + 5, (n, Hkv, d), dtype)
+    max_blocks = max(1, max(len(t) for t in tables))
+    return DecodeBatch(dtype, L, N, Hq, Hkv, d, B, lengths, free_order, k_pool, v_pool, q, k_new,
+                       v_new, tables, np.asarray(slots_new, np.int64), max_blocks)
+
+
+def padded_tables(tables, max_blocks, pad=0):
+    out = np.full((len(tables), max_blocks), pad, dtype=np.int32)
+    for i, t in enumerate(tables):
+        out[i, :len(t)] = t
+    return out
+
+
+def oracle_step(batch: DecodeBatch, layer: int, scale=None):
+    """The oracle's result of the step on `layer`: (k_pool, v_pool) after the
+    append and the float64 decode output."""
+    kp, vp = okv.append_kv(batch.k_pool, batch.v_pool, layer, batch.k_new, batch.v_new,
+                           batch.slots_new, batch.B)
+    from oracle import attention as oatt
+    out = oatt.paged_decode(batch.q, kp, vp, layer, batch.tables, batch.lengths, batch.B,
+                            batch.dtype, scale=scale)
+    return kp, vp, out
+
+
+def widen(a, dtype):
+    return olayout.widen(a, dtype)
+
+
+def max_abs_err(got_storage, expect_f64, dtype):
+    return float(np.max(np.abs(widen(got_storage, dtype) - expect_f64))) if expect_f64.size else 0.0
+
+
+def default_scale(d):
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,86 @@
+"""The C-ABI library loads on the host and exports every symbol include/pa.h declares."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+LIB = os.path.join(ROOT, "paged_kv_cache_83_amd", "libpa.so")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    names = declared()
+    for must in ("pa_append_kv", "pa_decode", "pa_copy_blocks", "pa_gather_blocks",
+                 "pa_scatter_blocks", "pa_bytes_per_token", "pa_decode_workspace_bytes",
+                 "pa_bm_create", "pa_bm_seq_append", "pa_bm_seq_fork", "pa_bm_seq_release"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (pa_[a-z0-9_]+)$", out, flags=re.M))
+    assert set(declared()) <= exported
+
+
+def test_binding_declares_every_symbol():
+    from paged_kv_cache_83_amd import _lib
+    assert set(declared()) == set(_lib.SIGNATURES)
+
+
+def test_library_is_for_gfx950():
+    # the device code object embedded in the library targets gfx950
+    blob = open(LIB, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_host_entry_points_reject_bad_arguments():
+    import paged_kv_cache_83_amd as pk
+    from paged_kv_cache_83_amd import _lib
+    L = _lib.load()
+    assert L.pa_bytes_per_token(0, 8, 128, 2, 1) == -1
+    assert L.pa_blocks_for_tokens(-1, 16) == -1
+    g = _lib.pa_geom(80, 8, 128, 16, 32768, 1)
+    assert L.pa_bytes_per_block(ctypes.byref(g)) == 5242880
+    bad = _lib.pa_geom(80, 8, 128, 16, 32768, 7)
+    assert L.pa_bytes_per_block(ctypes.byref(bad)) == -1
+    # device entry points validate before touching any pointer (no GPU needed)
+    assert L.pa_decode(ctypes.byref(bad), None, None, 0, None, None, 1, 64, None, 1, None, 16, 0.0,
+                       None, None, 0, None) == -1
+    assert L.pa_append_kv(ctypes.byref(g), None, None, 99, None, None, None, 1, None) == -1
+    assert L.pa_copy_blocks(ctypes.byref(g), None, None, None, None, 3, None) == -1
+    # 65 query heads cannot be grouped over 8 KV heads
+    assert L.pa_decode(ctypes.byref(g), None, None, 0, None, None, 1, 65, None, 1, None, 16, 0.0,
+                       None, None, 0, None) == -1
+    # table too short for max_context_len
+    assert L.pa_decode(ctypes.byref(g), None, None, 0, None, None, 1, 64, None, 1, None, 17, 0.0,
+                       None, None, 0, None) == -1
+    # zero sequences is a no-op
+    assert L.pa_decode(ctypes.byref(g), None, None, 0, None, None, 0, 64, None, 1, None, 16, 0.0,
+                       None, None, 0, None) == 0
+    assert pk.bytes_per_token(80, 8, 128, 2) == 327680
+
+
+def test_workspace_sizing():
+    import paged_kv_cache_83_amd as pk
+    g = pk.Geometry(80, 8, 128, 16, 32768, "bf16")
+    ws = pk.decode_workspace_bytes(g, 16, 64, 32768)
+    # 16 seqs x 64 heads x splits x (128 + 2) floats
+    assert ws > 0 and ws % (16 * 64 * 130 * 4) == 0
+    assert pk.decode_workspace_bytes(g, 16, 64, 32768, blocks_per_split=4096) == 0
+    g1 = pk.Geometry(12, 12, 64, 16, 1024, "f32")
+    assert pk.decode_workspace_bytes(g1, 8, 12, 1024, kernel="generic") >= 0
+    with pytest.raises(Exception):
+        pk.decode_workspace_bytes(g1, 8, 12, 1024, kernel="bogus")

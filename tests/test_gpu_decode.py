@@ -1,0 +1,180 @@
+"""GPU parity of paged decode (append + pa_decode) against the oracle.
+
+Attention outputs must match the float64 oracle to max-abs-error <= 2e-2 with bf16
+inputs/outputs and <= 1e-5 with fp32; the append must be bit-exact; outputs must
+be bitwise identical under any permutation of physical blocks; unused slots are
+NaN-poisoned throughout."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_83_amd as pk
+from oracle import attention as oatt
+from tests.gpu_helpers import (BF16_TOL, F32_TOL, make_batch, max_abs_err, need_gpu,
+                               oracle_step, padded_tables, print_case, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 47, 64, 100, 257]
+
+
+def run_library(batch, layer, kernel="auto", bps=0, scale=0.0, tables=None, lengths=None,
+                max_ctx=None):
+    """Upload the batch, run the library's append + decode on one layer; returns
+    (out, k_pool, v_pool) in storage form."""
+    geom = pk.Geometry(batch.L, batch.Hkv, batch.d, batch.B, batch.N, batch.dtype)
+    K, V = to_dev(batch.k_pool, batch.dtype), to_dev(batch.v_pool, batch.dtype)
+    slots = torch.from_numpy(batch.slots_new).cuda()
+    pk.append_kv(geom, K, V, layer, to_dev(batch.k_new, batch.dtype),
+                 to_dev(batch.v_new, batch.dtype), slots)
+    tabs = padded_tables(batch.tables if tables is None else tables, batch.max_blocks)
+    lens = batch.lengths if lengths is None else lengths
+    max_ctx = int(max(lens)) if max_ctx is None else max_ctx
+    q = to_dev(batch.q, batch.dtype)
+    out = torch.empty_like(q)
+    ws_bytes = pk.decode_workspace_bytes(geom, q.shape[0], q.shape[1], max_ctx, bps, kernel)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    pk.decode(geom, K, V, layer, q, out, torch.from_numpy(tabs).cuda(),
+              torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max_ctx, scale=scale,
+              workspace=ws, blocks_per_split=bps, kernel=kernel)
+    torch.cuda.synchronize()
+    return to_host(out, batch.dtype), to_host(K, batch.dtype), to_host(V, batch.dtype)
+
+
+CASES = [
+    # name, dtype, L, N, Hq, Hkv, d, B, kernel, bps
+    ("mfma_d128_g8", "bf16", 2, 160, 64, 8, 128, 16, "mfma", 0),
+    ("mfma_d128_g8_split2", "bf16", 2, 160, 64, 8, 128, 16, "mfma", 2),
+    ("mfma_d128_g4", "bf16", 1, 160, 32, 8, 128, 16, "mfma", 4),
+    ("mfma_d64_g16", "bf16", 1, 160, 32, 2, 64, 16, "mfma", 0),
+    ("mfma_d256_g2", "bf16", 1, 160, 4, 2, 256, 16, "mfma", 6),
+    ("mfma_d128_mha", "bf16", 1, 160, 4, 4, 128, 16, "mfma", 0),
+    ("generic_bf16_d128_g8", "bf16", 1, 160, 16, 2, 128, 16, "generic", 4),
+    ("generic_bf16_b4", "bf16", 1, 700, 8, 2, 32, 4, "generic", 0),
+    ("generic_f32_d64_mha", "f32", 2, 160, 12, 12, 64, 16, "generic", 0),
+    ("generic_f32_d64_split", "f32", 1, 160, 6, 3, 64, 16, "generic", 2),
+    ("generic_f32_b32_g4", "f32", 1, 100, 8, 2, 128, 32, "generic", 0),
+    ("generic_f32_b1", "f32", 1, 1200, 2, 1, 16, 1, "generic", 64),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_decode_parity(case):
+    need_gpu()
+    name, dtype, L, N, Hq, Hkv, d, B, kernel, bps = case
+    print_case(test="decode_parity", case=name)
+    batch = make_batch(dtype, L, N, Hq, Hkv, d, B, RAGGED, seed=zlib.crc32(name.encode()) % 10000)
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    for layer in range(L):
+        out, K, V = run_library(batch, layer, kernel=kernel, bps=bps)
+        ek, ev, expect = oracle_step(batch, layer)
+        assert np.array_equal(K.view(np.uint8), ek.view(np.uint8)), "append mismatch"
+        assert np.array_equal(V.view(np.uint8), ev.view(np.uint8)), "append mismatch"
+        assert np.isfinite(out.astype(np.float32) if dtype == "f32" else out).all()
+        err = max_abs_err(out, expect, dtype)
+        assert err <= tol, (name, layer, err)
+
+
+def test_single_token_returns_its_value_bitwise():
+    need_gpu()
+    print_case(test="single_token")
+    for kernel, dtype, d in (("mfma", "bf16", 128), ("generic", "f32", 64), ("generic", "bf16", 64)):
+        batch = make_batch(dtype, 1, 8, 8, 2, d, 16, [1, 1, 1], seed=5)
+        out, _, _ = run_library(batch, 0, kernel=kernel)
+        for i in range(3):
+            for h in range(8):
+                assert np.array_equal(out[i, h], batch.v_new[i, h // 4]), (kernel, dtype)
+
+
+def test_zero_length_writes_zeros():
+    need_gpu()
+    print_case(test="zero_length")
+    for kernel, dtype, bps in (("mfma", "bf16", 0), ("mfma", "bf16", 2), ("generic", "f32", 2)):
+        batch = make_batch(dtype, 1, 64, 8, 2, 64 if dtype == "f32" else 128, 16, [0, 40, 0, 70],
+                           seed=9)
+        out, _, _ = run_library(batch, 0, kernel=kernel, bps=bps)
+        _, _, expect = oracle_step(batch, 0)
+        assert not np.any(out[0].view(np.uint8)) and not np.any(out[2].view(np.uint8))
+        assert max_abs_err(out, expect, dtype) <= (BF16_TOL if dtype == "bf16" else F32_TOL)
+
+
+@pytest.mark.parametrize("kernel,dtype,d", [("mfma", "bf16", 128), ("generic", "f32", 64)])
+def test_block_placement_invariance_bitwise(kernel, dtype, d):
+    """Same logical content under a different physical permutation: identical bits."""
+    need_gpu()
+    print_case(test="placement", kernel=kernel)
+    L, N, Hq, Hkv, B = 1, 200, 16, 2, 16
+    lengths = [33, 250, 7, 129]
+    a = make_batch(dtype, L, N, Hq, Hkv, d, B, lengths, seed=21)
+    b = make_batch(dtype, L, N, Hq, Hkv, d, B, lengths, seed=22)
+    # give b the same logical content as a: copy each token's K/V to b's placement
+    from oracle import layout as ol
+    for ta, tb, S in zip(a.tables, b.tables, lengths):
+        for lb in range(len(ta)):
+            b.k_pool[:, tb[lb]] = a.k_pool[:, ta[lb]]
+            b.v_pool[:, tb[lb]] = a.v_pool[:, ta[lb]]
+    b.q, b.k_new, b.v_new = a.q, a.k_new, a.v_new
+    assert b.tables != a.tables
+    out_a, _, _ = run_library(a, 0, kernel=kernel, bps=4)
+    out_b, _, _ = run_library(b, 0, kernel=kernel, bps=4)
+    assert np.array_equal(out_a.view(np.uint8), out_b.view(np.uint8))
+    del ol
+
+
+def test_split_count_invariance():
+    """One split against many: fp32 within 1e-6; bf16 MFMA within the bf16 tolerance."""
+    need_gpu()
+    print_case(test="splits")
+    lengths = [700, 1, 333, 1024]
+    f = make_batch("f32", 1, 300, 8, 4, 64, 16, lengths, seed=31)
+    one, _, _ = run_library(f, 0, kernel="generic", bps=1024)
+    many, _, _ = run_library(f, 0, kernel="generic", bps=2)
+    assert np.max(np.abs(one.astype(np.float64) - many.astype(np.float64))) <= 1e-6
+    b = make_batch("bf16", 1, 300, 64, 8, 128, 16, lengths, seed=32)
+    one, _, _ = run_library(b, 0, kernel="mfma", bps=1024)
+    many, _, _ = run_library(b, 0, kernel="mfma", bps=2)
+    _, _, expect = oracle_step(b, 0)
+    assert max_abs_err(one, expect, "bf16") <= BF16_TOL
+    assert max_abs_err(many, expect, "bf16") <= BF16_TOL
+
+
+def test_explicit_scale():
+    need_gpu()
+    print_case(test="scale")
+    batch = make_batch("f32", 1, 100, 4, 2, 64, 16, [50, 90], seed=41)
+    out, _, _ = run_library(batch, 0, kernel="generic", scale=0.3)
+    _, _, expect = oracle_step(batch, 0, scale=0.3)
+    assert max_abs_err(out, expect, "f32") <= F32_TOL
+    batch = make_batch("bf16", 1, 100, 16, 2, 128, 16, [50, 90], seed=42)
+    out, _, _ = run_library(batch, 0, kernel="mfma", scale=0.02)
+    _, _, expect = oracle_step(batch, 0, scale=0.02)
+    assert max_abs_err(out, expect, "bf16") <= BF16_TOL
+
+
+def test_auto_kernel_choice_matches_oracle():
+    need_gpu()
+    print_case(test="auto")
+    for dtype, d, B in (("bf16", 128, 16), ("f32", 64, 16), ("bf16", 64, 8)):
+        batch = make_batch(dtype, 1, 200, 16, 4, d, B, [5, 77, 300], seed=51)
+        out, _, _ = run_library(batch, 0)
+        _, _, expect = oracle_step(batch, 0)
+        assert max_abs_err(out, expect, dtype) <= (BF16_TOL if dtype == "bf16" else F32_TOL)
+
+
+def test_unsupported_and_bad_arguments():
+    need_gpu()
+    print_case(test="bad_args")
+    geom = pk.Geometry(1, 2, 128, 16, 8, "f32")
+    K, V = pk.alloc_pools(geom)
+    q = torch.zeros(1, 4, 128, device="cuda")
+    out = torch.empty_like(q)
+    tabs = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    lens = torch.ones(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(pk.PagedKVError):
+        pk.decode(geom, K, V, 0, q, out, tabs, lens, 16, kernel="mfma")    # fp32 has no MFMA path
+    with pytest.raises(pk.PagedKVError):
+        pk.decode(geom, K, V, 0, q, out, tabs, lens, 17)                    # table too short
+    with pytest.raises(ValueError):
+        pk.decode(geom, K, V, 0, q.to(torch.bfloat16), out, tabs, lens, 16)  # dtype mismatch

@@ -1,0 +1,120 @@
+"""GPU parity of the block data-movement kernels against the oracle (bit-exact):
+slot-mapped append, copy-on-write block copy, gather and scatter."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_83_amd as pk
+from oracle import kv_ops as okv
+from oracle import layout as olayout
+from synth import gen
+from tests.gpu_helpers import need_gpu, print_case, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+GEOMS = [
+    # dtype, L, N, Hkv, d, B
+    ("bf16", 3, 40, 8, 128, 16),
+    ("bf16", 2, 33, 2, 64, 1),
+    ("bf16", 2, 20, 3, 40, 4),      # d not a multiple of 8: element path
+    ("f32", 2, 24, 12, 64, 16),
+    ("f32", 1, 17, 1, 6, 32),       # d not a multiple of 4
+]
+
+
+def _pools(dtype, L, N, H, d, B, seed):
+    kp = gen.normal_values(seed, olayout.k_pool_shape(L, N, H, B, d), dtype)
+    vp = gen.normal_values(seed + 1, olayout.v_pool_shape(L, N, H, B, d), dtype)
+    return kp, vp
+
+
+@pytest.mark.parametrize("dtype,L,N,H,d,B", GEOMS)
+def test_append_bit_exact(dtype, L, N, H, d, B):
+    need_gpu()
+    print_case(test="append", dtype=dtype, L=L, N=N, H=H, d=d, B=B)
+    geom = pk.Geometry(L, H, d, B, N, dtype)
+    kp, vp = _pools(dtype, L, N, H, d, B, 10)
+    n = 37
+    rng = np.random.default_rng(4)
+    slots = rng.choice(N * B, size=n, replace=False).astype(np.int64)
+    slots[3] = -1                      # skipped token
+    slots[7] = N * B + 5               # out of range: the kernel's guard skips it
+    kn = gen.normal_values(20, (n, H, d), dtype)
+    vn = gen.normal_values(21, (n, H, d), dtype)
+    layer = L - 1
+    K, V = to_dev(kp, dtype), to_dev(vp, dtype)
+    pk.append_kv(geom, K, V, layer, to_dev(kn, dtype), to_dev(vn, dtype),
+                 torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    ok = slots.copy()
+    ok[7] = -1
+    ek, ev = okv.append_kv(kp, vp, layer, kn, vn, ok, B)
+    assert np.array_equal(to_host(K, dtype).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(to_host(V, dtype).view(np.uint8), ev.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,L,N,H,d,B", GEOMS)
+def test_copy_blocks_bit_exact(dtype, L, N, H, d, B):
+    need_gpu()
+    print_case(test="copy_blocks", dtype=dtype, L=L, N=N)
+    geom = pk.Geometry(L, H, d, B, N, dtype)
+    kp, vp = _pools(dtype, L, N, H, d, B, 30)
+    perm = np.random.default_rng(7).permutation(N)
+    src, dst = perm[:5].astype(np.int32), perm[5:10].astype(np.int32)
+    K, V = to_dev(kp, dtype), to_dev(vp, dtype)
+    pk.copy_blocks(geom, K, V, torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+    torch.cuda.synchronize()
+    ek, ev = okv.copy_blocks(kp, vp, src, dst)
+    assert np.array_equal(to_host(K, dtype).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(to_host(V, dtype).view(np.uint8), ev.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,L,N,H,d,B", GEOMS)
+def test_gather_scatter_bit_exact(dtype, L, N, H, d, B):
+    need_gpu()
+    print_case(test="gather_scatter", dtype=dtype, L=L, N=N)
+    geom = pk.Geometry(L, H, d, B, N, dtype)
+    kp, vp = _pools(dtype, L, N, H, d, B, 40)
+    rng = np.random.default_rng(9)
+    ids = rng.choice(N, size=min(N, 11), replace=False).astype(np.int32)
+    K, V = to_dev(kp, dtype), to_dev(vp, dtype)
+    per_block = pk.bytes_per_block(geom)
+    staging = torch.empty(len(ids) * per_block, dtype=torch.uint8, device="cuda")
+    pk.gather_blocks(geom, K, V, torch.from_numpy(ids).cuda(), staging)
+    torch.cuda.synchronize()
+    expect = okv.gather_blocks(kp, vp, ids)
+    assert np.array_equal(staging.cpu().numpy(), expect.view(np.uint8).reshape(-1))
+    # scatter the staged frames into other blocks of a different pool
+    k2p, v2p = _pools(dtype, L, N, H, d, B, 50)
+    new_ids = rng.permutation(N)[:len(ids)].astype(np.int32)
+    K2, V2 = to_dev(k2p, dtype), to_dev(v2p, dtype)
+    pk.scatter_blocks(geom, K2, V2, staging, torch.from_numpy(new_ids).cuda())
+    torch.cuda.synchronize()
+    ek, ev = okv.scatter_blocks(k2p, v2p, expect, new_ids)
+    assert np.array_equal(to_host(K2, dtype).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(to_host(V2, dtype).view(np.uint8), ev.view(np.uint8))
+
+
+def test_empty_and_guarded_calls():
+    need_gpu()
+    print_case(test="empty_calls")
+    geom = pk.Geometry(2, 2, 8, 4, 6, "bf16")
+    K, V = pk.alloc_pools(geom)
+    K.zero_()
+    V.zero_()
+    e32 = torch.empty(0, dtype=torch.int32, device="cuda")
+    pk.copy_blocks(geom, K, V, e32, e32)
+    staging = torch.empty(1, dtype=torch.uint8, device="cuda")
+    pk.gather_blocks(geom, K, V, e32, staging)
+    pk.scatter_blocks(geom, K, V, staging, e32)
+    e64 = torch.empty(0, dtype=torch.int64, device="cuda")
+    kn = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    pk.append_kv(geom, K, V, 0, kn, kn, e64)
+    # out-of-range ids are skipped by the kernels' own guards
+    bad = torch.tensor([-1, 6, 99], dtype=torch.int32, device="cuda")
+    ok = torch.tensor([0, 1, 2], dtype=torch.int32, device="cuda")
+    pk.copy_blocks(geom, K, V, bad, ok)
+    torch.cuda.synchronize()
+    assert int(K.view(torch.int16).abs().sum()) == 0
+    with pytest.raises(ValueError):
+        pk.gather_blocks(geom, K, V, ok, staging)      # staging too small: host check
