@@ -23,9 +23,14 @@
  * Memory layout (fixed by this interface)
  * ---------------------------------------------------------------------------
  * A pool is two device arrays of the geometry's element type (fp32 or bf16):
- *   K pool [L][N][H_kv][B][d]   element (layer, block, head, slot offset, dim)
- *   V pool [L][N][H_kv][d][B]   element (layer, block, head, dim, slot offset)
- * Each (layer, block, head) is one contiguous run of B*d elements in both.
+ *   K pool [L][N][H_kv][d/W][B][W]  element (layer, block, head, slot o, dim j) at
+ *                                   chunk j/W, slot o, position j%W; W = 32 when 32
+ *                                   divides d, else W = d (i.e. [L][N][H_kv][B][d])
+ *   V pool [L][N][H_kv][d][B]        element (layer, block, head, dim, slot offset)
+ * Each (layer, block, head) is one contiguous run of B*d elements in both. The
+ * 32-wide dimension chunks of K make every K load of the decode kernel cover
+ * whole 128-byte lines; V's dimension-major runs give 8 consecutive slots of one
+ * dimension per 16-byte load.
  * A slot is block * B + offset. A block table is int32 [n_seqs][max_blocks]
  * (row-major); entry j of row i is the physical block of sequence i's logical
  * block j. context_lens[i] is the number of tokens sequence i attends to.

@@ -38,7 +38,7 @@ def default_scale(head_dim: int) -> float:
 def rebuild_sequence(k_pool, v_pool, layer, table, length, block_size, dtype):
     """Contiguous K, V ([S, H_kv, d], float64) of one sequence from its block table."""
     num_kv_heads = k_pool.shape[2]
-    head_dim = k_pool.shape[4]
+    head_dim = v_pool.shape[3]              # V pool is [L, N, H_kv, d, B]
     K = np.zeros((length, num_kv_heads, head_dim), dtype=np.float64)
     V = np.zeros((length, num_kv_heads, head_dim), dtype=np.float64)
     num_blocks = -(-length // block_size)

@@ -9,11 +9,13 @@ The in-memory arrangement of a pool is a documented property of the library's
 interface, restated here independently (this module shares no code with the
 library):
 
-* K pool, shape [L, N, H_kv, B, d]: element (layer, p, head, o, j).
+* K pool, shape [L, N, H_kv, d/W, B, W] with W = 32 when 32 divides d and
+  W = d otherwise: element (layer, p, head, o, j) sits at chunk j // W, slot o,
+  position j % W (for W = d this is simply [L, N, H_kv, B, d]).
 * V pool, shape [L, N, H_kv, d, B]: element (layer, p, head, j, o).
   Within one (layer, block, head) both are one contiguous run of B*d elements;
-  K keeps each token's d values together, V keeps each dimension's B values
-  together.
+  K keeps each token's values together within 32-wide dimension chunks, V keeps
+  each dimension's B values together.
 * Staging buffer for gather/scatter: for the i-th listed block, M_block bytes
   laid out as [L][2][run], where index 0 holds the block's K run of that layer
   and index 1 its V run, each run copied as stored in the pool. This is the
@@ -28,8 +30,14 @@ from __future__ import annotations
 import numpy as np
 
 
+def k_chunk(head_dim: int) -> int:
+    """Width W of the K dimension chunks."""
+    return 32 if head_dim % 32 == 0 else head_dim
+
+
 def k_pool_shape(num_layers, num_blocks, num_kv_heads, block_size, head_dim):
-    return (num_layers, num_blocks, num_kv_heads, block_size, head_dim)
+    W = k_chunk(head_dim)
+    return (num_layers, num_blocks, num_kv_heads, head_dim // W, block_size, W)
 
 
 def v_pool_shape(num_layers, num_blocks, num_kv_heads, block_size, head_dim):
@@ -53,7 +61,7 @@ def slot_of(table, t: int, block_size: int) -> int:
 
 def read_k(k_pool: np.ndarray, layer: int, phys: int, head: int, offset: int) -> np.ndarray:
     """The d values of K stored for (layer, block phys, head, slot offset)."""
-    return k_pool[layer, phys, head, offset, :]
+    return k_pool[layer, phys, head, :, offset, :].reshape(-1)
 
 
 def read_v(v_pool: np.ndarray, layer: int, phys: int, head: int, offset: int) -> np.ndarray:
@@ -63,7 +71,8 @@ def read_v(v_pool: np.ndarray, layer: int, phys: int, head: int, offset: int) ->
 
 def read_k_tile(k_pool: np.ndarray, layer: int, phys: int, head: int) -> np.ndarray:
     """K of all B slots of one (layer, block, head), as [B, d] (slot-major)."""
-    return k_pool[layer, phys, head, :, :]
+    chunks = k_pool[layer, phys, head]                 # [d/W, B, W]
+    return np.concatenate([chunks[c] for c in range(chunks.shape[0])], axis=1)
 
 
 def read_v_tile(v_pool: np.ndarray, layer: int, phys: int, head: int) -> np.ndarray:
@@ -72,7 +81,8 @@ def read_v_tile(v_pool: np.ndarray, layer: int, phys: int, head: int) -> np.ndar
 
 
 def write_k(k_pool: np.ndarray, layer: int, phys: int, head: int, offset: int, values) -> None:
-    k_pool[layer, phys, head, offset, :] = values
+    nchunk, W = k_pool.shape[3], k_pool.shape[5]
+    k_pool[layer, phys, head, :, offset, :] = np.asarray(values).reshape(nchunk, W)
 
 
 def write_v(v_pool: np.ndarray, layer: int, phys: int, head: int, offset: int, values) -> None:

@@ -44,8 +44,16 @@ class Geometry:
         return 4 if self.dtype == "f32" else 2
 
     @property
+    def k_chunk(self) -> int:
+        """Width W of K's dimension chunks (32 when it divides head_dim, else head_dim)."""
+        return 32 if self.head_dim % 32 == 0 else self.head_dim
+
+    @property
     def k_pool_shape(self):
-        return (self.num_layers, self.num_blocks, self.num_kv_heads, self.block_size, self.head_dim)
+        """[L, N, H_kv, d/W, B, W], the K layout include/pa.h documents."""
+        W = self.k_chunk
+        return (self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim // W,
+                self.block_size, W)
 
     @property
     def v_pool_shape(self):

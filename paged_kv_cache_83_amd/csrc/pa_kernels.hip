@@ -15,10 +15,13 @@
 //     (copy a shared block into a fresh one) and "Asynchronous paged swapping"
 //     (move frames of bytes_per_block between the pool and a staging buffer).
 //
-// Pool layout (the interface fixes it): K [L][N][H_kv][B][d], V [L][N][H_kv][d][B].
-// Keeping V dimension-major inside a block means a 16-byte load of V gives 8
-// consecutive slots of one dimension, which is exactly the operand fragment the
-// PV matrix-core instruction wants; K is slot-major, which is what QK^T wants.
+// Pool layout (the interface fixes it): K [L][N][H_kv][d/W][B][W] with W = 32 when
+// 32 divides d (else W = d), V [L][N][H_kv][d][B]. Keeping V dimension-major inside
+// a block means a 16-byte load of V gives 8 consecutive slots of one dimension,
+// which is exactly the operand fragment the PV matrix-core instruction wants; K
+// is slot-major within 32-dimension chunks, which is what QK^T wants, and the
+// chunking lets each K load instruction cover whole 128-byte lines (rows of 64 B
+// adjacent in memory) so non-temporal streaming keeps its full bandwidth.
 
 #include <hip/hip_runtime.h>
 
@@ -78,6 +81,9 @@ __device__ __forceinline__ int clamp_len(const int32_t* lens, int i, int max_ctx
 
 __device__ __forceinline__ int guard_block(int p, int N) { return (p >= 0 && p < N) ? p : 0; }
 
+// Width of the K dimension chunks: 32 when it divides d, else the whole d.
+__host__ __device__ __forceinline__ int k_chunk(int D) { return (D % 32 == 0) ? 32 : D; }
+
 // =============================================================================
 // Append: token j's K/V go to slot slot_mapping[j] of one layer.
 // One thread moves VEC consecutive elements of one (token, head).
@@ -107,7 +113,9 @@ __global__ void append_kv_kernel(T* __restrict__ kpool, T* __restrict__ vpool,
     kv[e] = knew[src + e];
     vv[e] = vnew[src + e];
   }
-  T* kd = kpool + tile + (int64_t)o * D + (int64_t)c * VEC;
+  const int j0 = c * VEC;  // VEC divides the chunk width, so the run stays in one chunk
+  const int W = k_chunk(D);
+  T* kd = kpool + tile + (int64_t)(j0 / W) * B * W + (int64_t)o * W + (j0 % W);
 #pragma unroll
   for (int e = 0; e < VEC; ++e) kd[e] = kv[e];
   T* vd = vpool + tile + (int64_t)c * VEC * B + o;
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(256) void block_move_kernel(char* __restrict__ kpoo
 // =============================================================================
 // Decode, MFMA kernel: bf16 pool, B = 16, d in {64, 128, 256}, up to 16 query
 // heads per KV head. One wave = one work item (sequence i, KV head g, split s)
-// covering logical blocks [s*bps, min((s+1)*bps, nblk)), bps even.
+// covering logical blocks [s*bps, min((s+1)*bps, nblk)), bps even and <= 256.
 //
 // Per pair of blocks (32 keys) it issues two 16x16x32 bf16 MFMA chains:
 //   S^T[32 keys][16 q] = K[keys][d] . Q^T[d][q]     (d/32 steps, two row tiles)
@@ -181,16 +189,158 @@ __global__ __launch_bounds__(256) void block_move_kernel(char* __restrict__ kpoo
 // that lane l ends up holding the 8 scores of keys 8*gq .. 8*gq+7 (pair-local)
 // for query c -- which is exactly the B-operand fragment of the PV product, so
 // probabilities never leave registers. K rows and V^T rows are each fetched
-// with 16-byte loads straight from the pool.
+// with 16-byte loads straight from the pool into operand registers; the next
+// pair's loads are issued before the current pair is computed (two register
+// buffers), so every wave keeps one pair of blocks in flight at all times.
 // =============================================================================
+constexpr int kMfmaMaxBps = 256;  // table entries of one split, held 64 per register
+
 template <int D>
 struct MfmaCfg {
   static constexpr int KC = D / 32;  // QK k-steps
   static constexpr int DT = D / 16;  // PV row tiles
 };
 
+template <int D>
+struct PairFrags {
+  u32x4 k[2][MfmaCfg<D>::KC];
+  u32x4 v[MfmaCfg<D>::DT];
+};
+
+// K/V tiles are read exactly once per step: stream them past the caches
+// (non-temporal loads sustain ~12% more HBM read bandwidth on this part).
+__device__ __forceinline__ u32x4 stream_load16(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (hardware round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Max / sum over lanes l, l^16, l^32, l^48 (the four lane groups holding one
+// query's keys), through the gfx950 cross-row swap instructions.
+__device__ __forceinline__ float max_over_groups(float v) {
+  uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  u = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float v) {
+  uint32_t u = __float_as_uint(v);
+  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  u = __float_as_uint(v);
+  auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Block id at offset `off` (wave-uniform, < 256) of the split's table chunk.
+__device__ __forceinline__ int table_at(const int (&tb)[4], int off) {
+  const int l = off & 63;
+  switch (off >> 6) {
+    case 0: return __builtin_amdgcn_readlane(tb[0], l);
+    case 1: return __builtin_amdgcn_readlane(tb[1], l);
+    case 2: return __builtin_amdgcn_readlane(tb[2], l);
+    default: return __builtin_amdgcn_readlane(tb[3], l);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void issue_pair(PairFrags<D>& f, const uint16_t* __restrict__ kl,
+                                           const uint16_t* __restrict__ vl, int p0, int p1, int Hkv,
+                                           int g, int k_sel, int k_off0, int v_sel, int v_off,
+                                           int gq) {
+  constexpr int KC = MfmaCfg<D>::KC;
+  constexpr int DT = MfmaCfg<D>::DT;
+  constexpr int TILE = 16 * D;
+  const uint16_t* krow = kl + ((int64_t)(k_sel ? p1 : p0) * Hkv + g) * TILE;
+  const uint16_t* vrow = vl + ((int64_t)(v_sel ? p1 : p0) * Hkv + g) * TILE;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      f.k[t][kc] = stream_load16(krow + kc * 512 + (k_off0 + 4 * t) * 32 + 8 * gq);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) f.v[dt] = stream_load16(vrow + dt * 256 + v_off);
+}
+
+template <int D>
+__device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)[MfmaCfg<D>::KC],
+                                             f32x4 (&acc)[MfmaCfg<D>::DT], float& m_run,
+                                             float& l_run, int blk, int len, int gq,
+                                             float qk_scale) {
+  constexpr int KC = MfmaCfg<D>::KC;
+  constexpr int DT = MfmaCfg<D>::DT;
+  f32x4 sc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.k[t][kc]),
+                                                      qf[kc], sc[t], 0, 0, 0);
+  }
+  // Lane holds the scores of pair-local keys 8*gq + 4*t + e for query c.
+  const int pos0 = blk * 16 + 8 * gq;
+  float sv[8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sv[4 * t + e] = (pos0 + 4 * t + e < len) ? sc[t][e] * qk_scale : -INFINITY;
+  }
+  float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                   fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  mb = max_over_groups(mb);
+  const float m_new = fmaxf(m_run, mb);  // finite: the pair's first key is attended
+  float psum = 0.f;
+  uint32_t pw[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float pa = __builtin_amdgcn_exp2f(sv[e] - m_new);
+    const float pb = __builtin_amdgcn_exp2f(sv[e + 1] - m_new);
+    psum += pa + pb;
+    pw[e >> 1] = pack_bf16x2(pa, pb);
+  }
+  // Rescale only when some query's running maximum moved (alpha == 1 otherwise).
+  if (__any(m_new != m_run)) {
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = acc[dt] * alpha;
+  }
+  l_run += psum;
+  m_run = m_new;
+  const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+
+  // Slots at or past the length hold unspecified data (possibly NaN): their
+  // probability is 0, and their V elements are zeroed so 0 * V stays 0.
+  if (blk * 16 + 32 > len) {
+    u32x4 keep;
+#pragma unroll
+    for (int wv = 0; wv < 4; ++wv) {
+      const int p = pos0 + 2 * wv;
+      keep[wv] = (p < len ? 0x0000ffffu : 0u) | (p + 1 < len ? 0xffff0000u : 0u);
+    }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) f.v[dt] &= keep;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.v[dt]), pf,
+                                                      acc[dt], 0, 0, 0);
+}
+
 template <int D, bool DIRECT>
-__global__ __launch_bounds__(64) void decode_mfma_bf16_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2))) void decode_mfma_bf16_kernel(
     const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml, const int32_t* __restrict__ tables,
@@ -198,13 +348,14 @@ __global__ __launch_bounds__(64) void decode_mfma_bf16_kernel(
     int max_blocks, int max_ctx, int bps, int S_max, float qk_scale) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int DT = MfmaCfg<D>::DT;
-  constexpr int TILE = 16 * D;  // elements of one (block, head) run
 
+  // Work-group order: KV head fastest, so the waves reading the H_kv tiles of
+  // the same blocks (adjacent in the pool) start together.
   const int w = blockIdx.x;
-  const int s = w % S_max;
-  const int gi = w / S_max;
-  const int g = gi % Hkv;
-  const int i = gi / Hkv;
+  const int g = w % Hkv;
+  const int si = w / Hkv;
+  const int s = si % S_max;
+  const int i = si / S_max;
   const int lane = threadIdx.x;
   const int c = lane & 15;
   const int gq = lane >> 4;
@@ -218,14 +369,22 @@ __global__ __launch_bounds__(64) void decode_mfma_bf16_kernel(
     if (DIRECT && len == 0 && qvalid) {
       uint16_t* o = out + ((int64_t)i * Hq + h) * D;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[16 * dt + 4 * gq + e] = 0;
-      }
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) = make_uint2(0u, 0u);
     }
     return;
   }
   const int b1 = min(b0 + bps, nblk);
+
+  // The split's block ids, one per lane and register, read once ("load the
+  // physical block pointers on chip"); each pair takes its two ids by readlane.
+  const int32_t* trow = tables + (int64_t)i * max_blocks;
+  int tb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = b0 + 64 * k + lane;
+    tb[k] = (64 * k < b1 - b0 && idx < b1) ? guard_block(trow[idx], N) : 0;
+  }
 
   // Q fragments (B operand of QK): Q[h][32*kc + 8*gq .. +8]; zero for padded columns.
   bf16x8 qf[KC];
@@ -245,120 +404,54 @@ __global__ __launch_bounds__(64) void decode_mfma_bf16_kernel(
   float m_run = -INFINITY;
   float l_run = 0.f;
 
-  const int32_t* trow = tables + (int64_t)i * max_blocks;
   const uint16_t* kl = kpool + layer_off;
   const uint16_t* vl = vpool + layer_off;
   // Row r = c of each score tile holds pair-local key 8*(c>>2) + 4*t + (c&3):
   // block (c >> 3) of the pair, offset 8*((c>>2)&1) + 4*t + (c&3).
-  const int k_blk_sel = c >> 3;
+  const int k_sel = c >> 3;
   const int k_off0 = 8 * ((c >> 2) & 1) + (c & 3);
   // V^T fragment of lane: block (gq >> 1), dims 16*dt + c, slots 8*(gq&1) .. +8.
-  const int v_blk_sel = gq >> 1;
+  const int v_sel = gq >> 1;
   const int v_off = 16 * c + 8 * (gq & 1);
 
-  for (int base = b0; base < b1; base += 64) {
-    // The split's block ids, one per lane, read once ("load the physical block
-    // pointers on chip"); each pair below takes its two ids from lanes.
-    const int cnt = min(64, b1 - base);
-    int tb = 0;
-    if (lane < cnt) tb = guard_block(trow[base + lane], N);
-    for (int j = 0; j < cnt; j += 2) {
-      const int p0 = __builtin_amdgcn_readlane(tb, j);
-      const int p1 = (j + 1 < cnt) ? __builtin_amdgcn_readlane(tb, j + 1) : p0;
-      const int blk = base + j;
+  const int span = b1 - b0;
+  const int npairs = (span + 1) >> 1;
+  auto ids = [&](int pj, int& p0, int& p1) {
+    const int off = 2 * pj;
+    p0 = table_at(tb, off);
+    p1 = (off + 1 < span) ? table_at(tb, off + 1) : p0;
+  };
 
-      const uint16_t* krow = kl + ((int64_t)(k_blk_sel ? p1 : p0) * Hkv + g) * TILE;
-      const uint16_t* vrow = vl + ((int64_t)(v_blk_sel ? p1 : p0) * Hkv + g) * TILE;
-      uint4 kf[2][KC];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          kf[t][kc] = *reinterpret_cast<const uint4*>(krow + (k_off0 + 4 * t) * D + 32 * kc + 8 * gq);
-      }
-      uint4 vf[DT];
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        vf[dt] = *reinterpret_cast<const uint4*>(vrow + dt * 256 + v_off);
-
-      f32x4 sc[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[t][kc]),
-                                                          qf[kc], sc[t], 0, 0, 0);
-      }
-      // Lane holds scores of pair-local keys 8*gq + 4*t + e for query c.
-      const int pos0 = blk * 16 + 8 * gq;
-      float sv[8];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sv[4 * t + e] = (pos0 + 4 * t + e < len) ? sc[t][e] * qk_scale : -INFINITY;
-      }
-      float mb = sv[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mb = fmaxf(mb, sv[e]);
-      mb = fmaxf(mb, __shfl_xor(mb, 16));
-      mb = fmaxf(mb, __shfl_xor(mb, 32));
-      const float m_new = fmaxf(m_run, mb);  // finite: the pair's first key is attended
-      const float alpha = exp2f(m_run - m_new);
-      m_run = m_new;
-      float psum = 0.f;
-      uint32_t pw[4];
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float pa = exp2f(sv[e] - m_new);
-        const float pb = exp2f(sv[e + 1] - m_new);
-        psum += pa + pb;
-        pw[e >> 1] = (uint32_t)f32_to_bf16(pa) | ((uint32_t)f32_to_bf16(pb) << 16);
-      }
-      l_run = l_run * alpha + psum;
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
-
-      // Slots at or past the length hold unspecified data (possibly NaN): their
-      // probability is 0, and their V elements are zeroed so 0 * V stays 0.
-      if (blk * 16 + 32 > len) {
-        uint32_t keep[4];
-#pragma unroll
-        for (int wv = 0; wv < 4; ++wv) {
-          const int p = pos0 + 2 * wv;
-          keep[wv] = (p < len ? 0x0000ffffu : 0u) | (p + 1 < len ? 0xffff0000u : 0u);
-        }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          vf[dt].x &= keep[0];
-          vf[dt].y &= keep[1];
-          vf[dt].z &= keep[2];
-          vf[dt].w &= keep[3];
-        }
-      }
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        acc[dt] = acc[dt] * alpha;
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]), pf,
-                                                          acc[dt], 0, 0, 0);
-      }
+  PairFrags<D> fa, fb;
+  int p0, p1;
+  ids(0, p0, p1);
+  issue_pair<D>(fa, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
+  for (int pj = 0;;) {
+    if (pj + 1 < npairs) {
+      ids(pj + 1, p0, p1);
+      issue_pair<D>(fb, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
     }
+    compute_pair<D>(fa, qf, acc, m_run, l_run, b0 + 2 * pj, len, gq, qk_scale);
+    if (++pj >= npairs) break;
+    if (pj + 1 < npairs) {
+      ids(pj + 1, p0, p1);
+      issue_pair<D>(fa, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
+    }
+    compute_pair<D>(fb, qf, acc, m_run, l_run, b0 + 2 * pj, len, gq, qk_scale);
+    if (++pj >= npairs) break;
   }
 
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_over_groups(l_run);
   if (!qvalid) return;
   // acc[dt][e] = O^T[d = 16*dt + 4*gq + e][q = c]
   if (DIRECT) {
     const float inv = 1.f / l_run;
     uint16_t* o = out + ((int64_t)i * Hq + h) * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16(acc[dt][0] * inv) | ((uint32_t)f32_to_bf16(acc[dt][1] * inv) << 16);
-      pk.y = (uint32_t)f32_to_bf16(acc[dt][2] * inv) | ((uint32_t)f32_to_bf16(acc[dt][3] * inv) << 16);
-      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) = pk;
-    }
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) =
+          make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                     pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
   } else {
     const int64_t row = ((int64_t)i * Hq + h) * S_max + s;
     float* po = part_o + row * D;
@@ -426,6 +519,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(
 
   const int32_t* trow = tables + (int64_t)i * max_blocks;
   const int BD = B * D;
+  const int W = k_chunk(D);
   for (int blk = b0; blk < b1; ++blk) {
     const int p = guard_block(trow[blk], N);
     const T* kt = kpool + layer_off + ((int64_t)p * Hkv + g) * BD;
@@ -433,7 +527,10 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(
     const int valid = min(B, len - blk * B);
     __syncthreads();
     for (int idx = lane; idx < BD; idx += 64) {
-      Ks[idx] = to_f32<T>(kt[idx]);
+      // memory order of K: [d/W][B][W] -> LDS order [B][d]
+      const int jc = idx / (B * W), rem = idx - jc * (B * W);
+      const int o = rem / W, jj = rem - o * W;
+      Ks[o * D + jc * W + jj] = to_f32<T>(kt[idx]);
       Vs[idx] = to_f32<T>(vt[idx]);
     }
     __syncthreads();
@@ -531,17 +628,67 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     return;
   }
   const int64_t row0 = ((int64_t)i * Hq + h) * S_max;
+  const float* ml = part_ml + row0 * 2;
+  const float* po = part_o + row0 * D;
   float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_ml[(row0 + s) * 2]);
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
   M = wave_max(M);
   float Lsum = 0.f;
-  for (int s = lane; s < ns; s += 64)
-    Lsum += exp2f(part_ml[(row0 + s) * 2] - M) * part_ml[(row0 + s) * 2 + 1];
+  for (int s = lane; s < ns; s += 64) Lsum += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
   Lsum = wave_sum(Lsum);
   const float inv = 1.f / Lsum;
+
+  const int C4 = D >> 2;  // float4 columns of one partial row
+  if ((D & 3) == 0 && C4 <= 64 && (64 % C4) == 0) {
+    // Lane (grp, col): column col of every groups-th split, independent loads
+    // unrolled four deep, then the groups are summed across lanes.
+    const int groups = 64 / C4;
+    const int col = lane % C4;
+    const int grp = lane / C4;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = grp;
+    for (; s + 3 * groups < ns; s += 4 * groups) {
+      float4 v[4];
+      float wt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = *reinterpret_cast<const float4*>(po + (int64_t)(s + u * groups) * D + 4 * col);
+        wt[u] = ml[2 * (s + u * groups)];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float ww = exp2f(wt[u] - M);
+        a.x = fmaf(ww, v[u].x, a.x);
+        a.y = fmaf(ww, v[u].y, a.y);
+        a.z = fmaf(ww, v[u].z, a.z);
+        a.w = fmaf(ww, v[u].w, a.w);
+      }
+    }
+    for (; s < ns; s += groups) {
+      const float4 v = *reinterpret_cast<const float4*>(po + (int64_t)s * D + 4 * col);
+      const float ww = exp2f(ml[2 * s] - M);
+      a.x = fmaf(ww, v.x, a.x);
+      a.y = fmaf(ww, v.y, a.y);
+      a.z = fmaf(ww, v.z, a.z);
+      a.w = fmaf(ww, v.w, a.w);
+    }
+    for (int off = C4; off < 64; off <<= 1) {
+      a.x += __shfl_xor(a.x, off);
+      a.y += __shfl_xor(a.y, off);
+      a.z += __shfl_xor(a.z, off);
+      a.w += __shfl_xor(a.w, off);
+    }
+    if (grp == 0) {
+      o[4 * col + 0] = from_f32<T>(a.x * inv);
+      o[4 * col + 1] = from_f32<T>(a.y * inv);
+      o[4 * col + 2] = from_f32<T>(a.z * inv);
+      o[4 * col + 3] = from_f32<T>(a.w * inv);
+    }
+    return;
+  }
   for (int d = lane; d < D; d += 64) {
     float a = 0.f;
-    for (int s = 0; s < ns; ++s) a = fmaf(exp2f(part_ml[(row0 + s) * 2] - M), part_o[(row0 + s) * D + d], a);
+    for (int s = 0; s < ns; ++s) a = fmaf(exp2f(ml[2 * s] - M), po[(int64_t)s * D + d], a);
     o[d] = from_f32<T>(a * inv);
   }
 }
@@ -635,16 +782,21 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
   if (opts && opts->blocks_per_split > 0) {
     bps = opts->blocks_per_split;
   } else {
+    // Aim for about one work item per SIMD (256 CUs x 4): each item pays two
+    // dependent load latencies at start (block ids, then its first blocks), so
+    // fewer, longer items beat more, shorter ones once the chip is covered.
     const int64_t units = (int64_t)n_seqs * g->num_kv_heads;
-    if (units >= 1024 || units == 0) {
+    const int64_t target_items = 1024;
+    if (units >= target_items || units == 0) {
       bps = maxb;
     } else {
-      const int64_t want_splits = (4096 + units - 1) / units;
+      const int64_t want_splits = (target_items + units - 1) / units;
       bps = std::max<int64_t>(16, (maxb + want_splits - 1) / want_splits);
     }
   }
   bps = std::max<int64_t>(2, bps);
   bps += bps & 1;  // pairs of blocks never straddle two splits
+  if (k == 2) bps = std::min<int64_t>(bps, kMfmaMaxBps);
   if (bps > INT32_MAX / 2) bps = INT32_MAX / 2;
   int64_t S = maxb == 0 ? 1 : (maxb + bps - 1) / bps;
   plan->kernel = k;

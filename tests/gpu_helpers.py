@@ -102,7 +102,7 @@ def make_batch(dtype, L, N, Hq, Hkv, d, B, lengths, seed, poison=True) -> Decode
         for p in range(N):
             for o in range(B):
                 if not used[p, o]:
-                    k_pool[:, p, :, o, :] = nan
+                    k_pool[:, p, :, :, o, :] = nan
                     v_pool[:, p, :, :, o] = nan
     q = gen.normal_values(seed + 3, (n, Hq, d), dtype)
     k_new = gen.normal_values(seed + 4, (n, Hkv, d), dtype)

@@ -79,7 +79,10 @@ def test_workspace_sizing():
     ws = pk.decode_workspace_bytes(g, 16, 64, 32768)
     # 16 seqs x 64 heads x splits x (128 + 2) floats
     assert ws > 0 and ws % (16 * 64 * 130 * 4) == 0
-    assert pk.decode_workspace_bytes(g, 16, 64, 32768, blocks_per_split=4096) == 0
+    # one split per sequence writes the output directly (generic kernel) ...
+    assert pk.decode_workspace_bytes(g, 16, 64, 32768, blocks_per_split=4096, kernel="generic") == 0
+    # ... while the MFMA kernel caps a split at 256 blocks: 2048 blocks -> 8 splits
+    assert pk.decode_workspace_bytes(g, 16, 64, 32768, blocks_per_split=4096) == 16 * 64 * 8 * 130 * 4
     g1 = pk.Geometry(12, 12, 64, 16, 1024, "f32")
     assert pk.decode_workspace_bytes(g1, 8, 12, 1024, kernel="generic") >= 0
     with pytest.raises(Exception):

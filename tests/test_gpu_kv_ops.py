@@ -34,7 +34,7 @@ def test_append_bit_exact(dtype, L, N, H, d, B):
     print_case(test="append", dtype=dtype, L=L, N=N, H=H, d=d, B=B)
     geom = pk.Geometry(L, H, d, B, N, dtype)
     kp, vp = _pools(dtype, L, N, H, d, B, 10)
-    n = 37
+    n = min(37, N * B)
     rng = np.random.default_rng(4)
     slots = rng.choice(N * B, size=n, replace=False).astype(np.int64)
     slots[3] = -1                      # skipped token

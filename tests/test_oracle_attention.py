@@ -20,13 +20,15 @@ from synth import gen
 def place_flat(Ks, Vs, tables, L, N, H, B, d, layer=0, fill=np.nan, dtype=np.float32):
     kflat = np.full(L * N * H * B * d, fill, dtype=dtype)
     vflat = np.full(L * N * H * B * d, fill, dtype=dtype)
+    W = 32 if d % 32 == 0 else d          # K dimension-chunk width
     for K, V, table in zip(Ks, Vs, tables):
         for t in range(K.shape[0]):
             p, o = table[t // B], t % B
             for h in range(H):
+                run = ((layer * N + p) * H + h) * B * d
                 for j in range(d):
-                    kflat[((((layer * N + p) * H + h) * B + o) * d + j)] = K[t, h, j]
-                    vflat[((((layer * N + p) * H + h) * d + j) * B + o)] = V[t, h, j]
+                    kflat[run + (j // W) * B * W + o * W + j % W] = K[t, h, j]
+                    vflat[run + j * B + o] = V[t, h, j]
     return (kflat.reshape(layout.k_pool_shape(L, N, H, B, d)),
             vflat.reshape(layout.v_pool_shape(L, N, H, B, d)))
 
@@ -58,7 +60,7 @@ def _tables_from_manager(lengths, N, B, seed):
 @pytest.mark.parametrize("B", [1, 4, 16])
 def test_brute_force_tiny(B):
     rng = np.random.default_rng(7 + B)
-    L, N, Hq, Hkv, d = 2, 64, 4, 2, 8
+    L, N, Hq, Hkv, d = 2, 64, 4, 2, (64 if B == 4 else 8)
     lengths = [1, 17, 40]
     tables = _tables_from_manager(lengths, N, B, 11)
     Ks = [rng.standard_normal((S, Hkv, d)).astype(np.float32) for S in lengths]

@@ -8,10 +8,25 @@ import numpy as np
 
 from oracle import attention as att
 from oracle import kv_ops, layout
+from oracle import layout as olayout
 from oracle.block_manager import BlockManager
 from synth import gen
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "layout_tiny.json")))
+KCHUNK = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "layout_kchunk.json")))
+
+
+def test_k_chunk_offsets():
+    B, d = KCHUNK["block_size"], KCHUNK["head_dim"]
+    kp = np.zeros(olayout.k_pool_shape(1, 1, 1, B, d), np.float32)
+    for case in KCHUNK["cases"]:
+        vals = np.zeros(d, np.float32)
+        vals[case["j"]] = 1.0
+        k2 = kp.copy()
+        layout.write_k(k2, 0, 0, 0, case["o"], vals)
+        assert np.flatnonzero(k2.reshape(-1)).tolist() == [case["offset"]]
+        assert layout.read_k(k2, 0, 0, 0, case["o"])[case["j"]] == 1.0
+        assert layout.read_k_tile(k2, 0, 0, 0)[case["o"], case["j"]] == 1.0
 
 
 def _tiny_pools():
