@@ -225,6 +225,10 @@ pa_status pa_bm_seq_swap_out(pa_bm* bm, int32_t seq, const int32_t* logical, int
 /* Swap-in: give the listed non-resident logical blocks fresh physical blocks. */
 pa_status pa_bm_seq_swap_in(pa_bm* bm, int32_t seq, const int32_t* logical, int32_t n,
                             int32_t* phys_out);
+/* Reorder the free list: entry k becomes the current entry perm[k]. perm must be
+ * a permutation of 0..n-1 with n == pa_bm_num_free(bm). Lets a caller hand out
+ * freed frames in a fresh order (e.g. a seeded shuffle before a swap-in). */
+pa_status pa_bm_permute_free(pa_bm* bm, const int32_t* perm, int32_t n);
 pa_status pa_bm_seq_info(const pa_bm* bm, int32_t seq, int64_t* n_tokens, int32_t* n_blocks);
 /* Copy the table (up to cap entries) into table_out; *n_blocks gets its length. */
 pa_status pa_bm_seq_table(const pa_bm* bm, int32_t seq, int32_t* table_out, int32_t cap,

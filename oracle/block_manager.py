@@ -221,6 +221,14 @@ class BlockManager:
             out.append(p)
         return out
 
+    def permute_free(self, perm):
+        """Reorder the free queue: entry k becomes the current entry perm[k]."""
+        perm = [int(x) for x in perm]
+        if sorted(perm) != list(range(len(self.free))):
+            raise InvalidArgument("perm must be a permutation of the free positions")
+        cur = list(self.free)
+        self.free = deque(cur[k] for k in perm)
+
     def table(self, sid):
         self._check_seq(sid)
         return list(self.tables[sid])

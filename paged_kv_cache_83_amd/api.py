@@ -372,6 +372,11 @@ class BlockManager:
               "pa_bm_seq_swap_in")
         return out[:a.size].tolist()
 
+    def permute_free(self, perm):
+        """Free-list entry k becomes the current entry perm[k]."""
+        a = _i32arr(perm)
+        check(self._lib.pa_bm_permute_free(self._h, _p32(a), a.size), "pa_bm_permute_free")
+
     def info(self, seq: int):
         n, b = C.c_int64(), C.c_int32()
         check(self._lib.pa_bm_seq_info(self._h, seq, C.byref(n), C.byref(b)), "pa_bm_seq_info")

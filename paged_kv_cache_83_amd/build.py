@@ -1,6 +1,9 @@
 """Build libpa.so in place: hipcc for the gfx950 kernels, g++ for the host code.
 
-    python -m paged_kv_cache_83_amd.build
+    python paged_kv_cache_83_amd/build.py
+
+(Run it as a script, or load it by path: importing the package loads the
+library, which is what this file produces.)
 """
 
 from __future__ import annotations

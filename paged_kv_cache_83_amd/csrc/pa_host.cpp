@@ -349,6 +349,20 @@ pa_status pa_bm_seq_swap_in(pa_bm* bm, int32_t seq, const int32_t* logical, int3
   return PA_OK;
 }
 
+pa_status pa_bm_permute_free(pa_bm* bm, const int32_t* perm, int32_t n) {
+  if (!bm || n < 0 || (n > 0 && !perm) || (size_t)n != bm->free_list.size()) return PA_ERR_INVALID_ARG;
+  std::vector<char> seen(n, 0);
+  for (int32_t k = 0; k < n; ++k) {
+    if (perm[k] < 0 || perm[k] >= n || seen[perm[k]]) return PA_ERR_INVALID_ARG;
+    seen[perm[k]] = 1;
+  }
+  std::vector<int32_t> cur(bm->free_list.begin(), bm->free_list.end());
+  std::deque<int32_t> next;
+  for (int32_t k = 0; k < n; ++k) next.push_back(cur[perm[k]]);
+  bm->free_list.swap(next);
+  return PA_OK;
+}
+
 pa_status pa_bm_seq_info(const pa_bm* bm, int32_t seq, int64_t* n_tokens, int32_t* n_blocks) {
   if (!bm) return PA_ERR_INVALID_ARG;
   const Seq* q = bm->find(seq);

@@ -13,5 +13,9 @@ def pytest_configure(config):
     # The library is normally built beforehand (__graft_entry__.build()); build it
     # here only when it is missing entirely, so CPU test runs are self-contained.
     if not os.path.exists(_LIB):
-        from paged_kv_cache_83_amd import build as _build
-        _build.build()
+        import importlib.util
+        path = os.path.join(ROOT, "paged_kv_cache_83_amd", "build.py")
+        spec = importlib.util.spec_from_file_location("_pa_build", path)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()

@@ -218,3 +218,19 @@ def test_block_bytes_abi_matches_oracle():
         assert pk.pool_bytes(g) == L * 100 * H * B * d * g.elem_bytes
     for S in (0, 1, 15, 16, 17, 32768):
         assert pk.blocks_for_tokens(S, 16) == ofp.blocks_for_tokens(S, 16)
+
+
+def test_permute_free_matches_oracle():
+    order = list(range(16))
+    ref, lib = obm.BlockManager(16, 4, order), pk.BlockManager(16, 4, order)
+    for m in (ref, lib):
+        s = m.seq_new()
+        m.append(s, 10)
+    perm = np.random.default_rng(3).permutation(13).tolist()
+    ref.permute_free(perm)
+    lib.permute_free(perm)
+    assert lib.alloc(13) == ref.alloc(13)
+    with pytest.raises(pk.PagedKVError):
+        lib.permute_free([0])           # free list is empty now
+    with pytest.raises(obm.InvalidArgument):
+        ref.permute_free([0])
