@@ -1,24 +1,26 @@
 #!/usr/bin/env python3
 """Paged-KV decode benchmark on one MI355X.
 
-A step is one decode step of the whole batch across every layer: for each layer,
-pa_append_kv writes the batch's new keys and values into their slots, then
-pa_decode attends every query head over its sequence's paged cache (split-K
-partial kernel + combine). Inputs (pool, tables, queries) are resident in HBM
-before the timed region starts.
+Default workload (the headline): the 70B grouped-query geometry at 32K context
+(80 layers, 64 query / 8 KV heads, head dim 128, bf16, 16-slot blocks), 16
+sequences of 32,768 attended tokens in a 32,768-block pool (171.8 GB) with a
+seeded random physical block order. A step = for every layer, pa_append_kv of
+the batch's new keys/values, then pa_decode (split-K partial + combine). Inputs
+are resident in HBM before the timed region starts. Prints one JSON line whose
+`value` is KV bytes read per second (sum over sequences of attended tokens x
+bytes per token, all layers).
 
-Default workload: the 70B grouped-query geometry at 32K context (80 layers,
-64 query / 8 KV heads, head dim 128, bf16, 16-slot blocks), 16 sequences of
-32,768 attended tokens, 32,768-block pool (171.8 GB) in a seeded random
-physical order.
-
-Prints one JSON line. `value` is KV bytes read per second for the step
-(sum over sequences of attended tokens x bytes per token, all layers).
+Other workloads (--config): gpt2_fp32 and chat_ragged run the same decode step;
+fork_cow times copy-on-write copies + bulk suffix append + decode; offload
+times the gather -> host -> scatter round trip of half of each trajectory and
+checks that decode is bitwise identical before and after.
 """
 
 from __future__ import annotations
 
 import argparse
+import contextlib
+import hashlib
 import json
 import math
 import os
@@ -26,6 +28,9 @@ import sys
 import time
 
 import numpy as np
+
+PEAK_GBS = 8000.0
+METRIC = "paged-decode KV GB/s (% of HBM peak) + decode tokens/s, 70B-GQA 32K ctx"
 
 
 def parse():
@@ -42,17 +47,24 @@ def parse():
     ap.add_argument("--no-prof", action="store_true", help="do not record per-kernel events")
     ap.add_argument("--prof-every", type=int, default=8,
                     help="record kernel events around the decode of every k-th layer")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time steps after writing a 1 GiB buffer (flushes L2 and MALL)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--parity-samples", type=int, default=4)
+    ap.add_argument("--offload-fraction", type=float, default=1.0,
+                    help="offload workload: fraction of the chosen blocks moved (host RAM bound)")
     return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def profiled_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel
     source has changed since those counters were taken."""
-    import hashlib
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"decode_mfma_bf16_{workload}_hbm_counters.md")
     src = os.path.join(here, "paged_kv_cache_83_amd", "csrc", "pa_kernels.hip")
@@ -83,61 +95,71 @@ def calibrate_copy():
     dt = time.perf_counter() - t0
     print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n,
                       "seconds": dt, "GB_per_s_rw": 2 * n / dt / 1e9}), flush=True)
-    del src, dst
-    big = torch.ones(8 << 30, dtype=torch.bfloat16, device="cuda")   # 16 GiB, read once per sum
-    for _ in range(2):
-        big.sum(dtype=torch.float32)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    reps = 5
-    for _ in range(reps):
-        big.sum(dtype=torch.float32)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / reps
-    print(json.dumps({"calibration": "device read (sum)", "bytes_read": big.numel() * 2,
-                      "seconds": dt, "GB_per_s_read": big.numel() * 2 / dt / 1e9}), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
-              "supported (see the sharding note in DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
-    if args.calibrate_copy:
-        calibrate_copy()
-        return
+class Timer:
+    """Times a region on one stream with hipEvents (torch.cuda.Event records on
+    the stream passed in, which is the stream every library call uses)."""
 
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.t0 = time.perf_counter()
+        self.a = self.torch.cuda.Event(enable_timing=True)
+        self.b = self.torch.cuda.Event(enable_timing=True)
+        self.a.record(self.stream)
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record(self.stream)
+        self.torch.cuda.synchronize()
+        self.wall_ms = (time.perf_counter() - self.t0) * 1e3
+        self.ms = max(self.a.elapsed_time(self.b), 0.0)
+        return False
+
+
+def setup(args):
     import torch
     import paged_kv_cache_83_amd as pk
-    from synth import gen, get_config
-
+    from synth import get_config
     cfg = get_config(args.config)
-    if cfg.length_kind not in ("fixed", "uniform", "lognormal"):
-        print(f"bench.py: config {cfg.name} is not a plain decode batch", file=sys.stderr)
-        sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-
     geom = pk.Geometry(cfg.num_layers, cfg.num_kv_heads, cfg.head_dim, cfg.block_size,
                        cfg.num_blocks, cfg.dtype)
+    log(f"config={cfg.name} L={cfg.num_layers} n={cfg.num_seqs} Hq={cfg.num_q_heads} "
+        f"Hkv={cfg.num_kv_heads} d={cfg.head_dim} B={cfg.block_size} N={cfg.num_blocks} "
+        f"dtype={cfg.dtype} pool={2 * pk.pool_bytes(geom) / 1e9:.1f} GB")
+    gen_ = torch.Generator(device=dev)
+    gen_.manual_seed(cfg.seed)
+    k_pool, v_pool = pk.alloc_pools(geom, dev)
+    k_pool.normal_(generator=gen_)
+    v_pool.normal_(generator=gen_)
+    return torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool
+
+
+def to_np(torch, t, dtype):
+    t = t.contiguous().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else t.numpy()
+
+
+# =============================================================================
+# Decode workloads (gqa70b_32k, gpt2_fp32, chat_ragged)
+# =============================================================================
+def run_decode(args):
+    torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool = setup(args)
+    from paged_kv_cache_83_amd import steps
+    from synth import gen
     L, n, Hq, Hkv, d, B = (cfg.num_layers, cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
                            cfg.head_dim, cfg.block_size)
     lengths = gen.context_lengths(cfg)
     m_token = pk.bytes_per_token(L, Hkv, d, geom.elem_bytes)
-    print(f"[bench] config={cfg.name} L={L} n={n} Hq={Hq} Hkv={Hkv} d={d} B={B} N={cfg.num_blocks} "
-          f"dtype={cfg.dtype} pool={2 * pk.pool_bytes(geom) / 1e9:.1f} GB", file=sys.stderr, flush=True)
-
-    # ---- inputs resident in HBM -------------------------------------------------
-    gpu_gen = torch.Generator(device=dev)
-    gpu_gen.manual_seed(cfg.seed)
-    k_pool, v_pool = pk.alloc_pools(geom, dev)
-    k_pool.normal_(generator=gpu_gen)
-    v_pool.normal_(generator=gpu_gen)
-    q_all = torch.randn((L, n, Hq, d), generator=gpu_gen, device=dev).to(geom.torch_dtype)
-    k_new = torch.randn((L, n, Hkv, d), generator=gpu_gen, device=dev).to(geom.torch_dtype)
-    v_new = torch.randn((L, n, Hkv, d), generator=gpu_gen, device=dev).to(geom.torch_dtype)
+    q_all = torch.randn((L, n, Hq, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    k_new = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    v_new = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
 
     # host block bookkeeping: history, then the decode step's one new token each
     bm = pk.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
@@ -158,59 +180,62 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    # snapshot of the sampled sequences' blocks, before any library kernel writes the pool
+    # host copies of the sampled sequences' blocks, before any library kernel writes the pool
     rng = np.random.default_rng(cfg.seed)
     samples = [(int(rng.integers(0, n)), int(rng.integers(0, L))) for _ in range(args.parity_samples)]
     snap = {}
-    for (i, layer) in samples:
+
+    def take_snapshot(i, layer):
         ids = torch.from_numpy(np.asarray(tables_np[i, :math.ceil(lengths[i] / B)], np.int64)).to(dev)
-        snap[(i, layer)] = (k_pool[layer].index_select(0, ids).cpu(), v_pool[layer].index_select(0, ids).cpu(),
-                            ids.cpu().numpy())
+        snap[(i, layer)] = (k_pool[layer].index_select(0, ids).cpu(),
+                            v_pool[layer].index_select(0, ids).cpu(), ids.cpu().numpy())
+
+    for key in samples:
+        take_snapshot(*key)
 
     profiling = [False]
 
+    def around(layer, before):
+        if profiling[0] and layer % args.prof_every == 0:
+            pk.Profiler.enable(before)
+
     def step():
-        for layer in range(L):
-            pk.append_kv(geom, k_pool, v_pool, layer, k_new[layer], v_new[layer], slots, stream=stream)
-            # per-kernel events are recorded around the decode of every prof_every-th layer
-            sample = profiling[0] and layer % args.prof_every == 0
-            if sample:
-                pk.Profiler.enable(True)
-            pk.decode(geom, k_pool, v_pool, layer, q_all[layer], out[layer], tables, lens, max_ctx,
-                      workspace=ws, blocks_per_split=args.bps, kernel=args.kernel, stream=stream)
-            if sample:
-                pk.Profiler.enable(False)
+        steps.decode_step(geom, k_pool, v_pool, q_all, k_new, v_new, slots, tables, lens, max_ctx, out,
+                          ws, blocks_per_split=args.bps, kernel=args.kernel, stream=stream,
+                          around_decode=around)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+    log(f"warmup done ({args.warmup} steps)")
 
     if not args.no_prof:
         pk.Profiler.reset()
         profiling[0] = True
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with Timer(torch, stream) as t:
+        for _ in range(args.steps):
+            step()
     profiling[0] = False
-    gpu_ms = ev0.elapsed_time(ev1)
-    ms_per_step = max(gpu_ms, wall * 1e3) / args.steps
-    print(f"[bench] timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    ms_per_step = max(t.ms, t.wall_ms) / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+
+    cold = None
+    if args.cold:
+        flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        tot = 0.0
+        for _ in range(args.steps):
+            flush.add_(1.0)
+            with Timer(torch, stream) as tc:
+                step()
+            tot += tc.ms
+        cold = tot / args.steps
+        log(f"cold (1 GiB written before each step): {cold:.3f} ms/step")
 
     kv_bytes_step = int(lengths.sum()) * m_token
     value = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
-    tokens_per_s = n / (ms_per_step * 1e-3)
 
     # ---- roofline of the dominant kernel (decode partial), timed live ----------
-    roofline = None
-    kernel_ms = {}
+    roofline, kernel_ms = None, {}
     if not args.no_prof:
         for name in ("decode_partial", "decode_combine"):
             cnt, tot = pk.Profiler.read(name)
@@ -220,60 +245,56 @@ def main():
         if cnt:
             eb = geom.elem_bytes
             splits = max(1, ws_bytes // (n * Hq * (d + 2) * 4)) if ws_bytes else 1
-            per_launch = (int(lengths.sum()) * 2 * Hkv * d * eb          # K and V of attended tokens
-                          + n * Hq * d * eb                               # queries
-                          + 4 * int(sum(math.ceil(S / B) for S in lengths))  # block-table entries
+            per_launch = (int(lengths.sum()) * 2 * Hkv * d * eb                 # K and V of attended tokens
+                          + n * Hq * d * eb                                      # queries
+                          + 4 * int(sum(math.ceil(S / B) for S in lengths))       # block-table entries
                           + (n * Hq * splits * (d + 2) * 4 if ws_bytes else n * Hq * d * eb))
             avg_s = tot / cnt * 1e-3
             achieved = per_launch / avg_s / 1e9
-            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": 8000.0, "unit": "GB/s",
-                        "frac": round(achieved / 8000.0, 4),
-                        "traffic": profiled_traffic(cfg.name) if args.bps == 0 and args.kernel == "auto" else None,
-                        "kernel": "decode_mfma_bf16_kernel" if cfg.dtype == "bf16" else "decode_generic_kernel",
+            mfma = cfg.dtype == "bf16" and B == 16 and args.kernel != "generic"
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_GBS, 4),
+                        "traffic": profiled_traffic(cfg.name) if (mfma and args.bps == 0 and
+                                                                  args.kernel == "auto") else None,
+                        "kernel": "decode_mfma_bf16_kernel" if mfma else "decode_generic_kernel",
                         "bytes_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2)}
 
     # ---- parity on sampled (sequence, layer) outputs against the oracle ---------
-    parity = None
-    cpu_baseline = None
+    parity, cpu_baseline = None, None
     if args.parity_samples or not args.no_cpu_baseline:
         from oracle import attention as oatt
-        from oracle import kv_ops as okv
         from oracle import block_manager as obm
-        obm_ = obm.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
+        from oracle import kv_ops as okv
+        om = obm.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
         oseqs = []
         for S in lengths:
-            s = obm_.seq_new()
-            obm_.append(s, int(S) - 1)
+            s = om.seq_new()
+            om.append(s, int(S) - 1)
             oseqs.append(s)
-        oslots = [obm_.append(s, 1)[0][0] for s in oseqs]
-        otables = [obm_.table(s) for s in oseqs]
-
-        def to_np(t):
-            return t.view(torch.int16).numpy().view(np.uint16) if cfg.dtype == "bf16" else t.numpy()
+        oslots = [om.append(s, 1)[0][0] for s in oseqs]
+        otables = [om.table(s) for s in oseqs]
 
         def oracle_one(i, layer):
             kb, vb, ids = snap[(i, layer)]
-            # a local pool holding only this sequence's blocks, renumbered 0..nb-1
-            kloc = to_np(kb)[None]
-            vloc = to_np(vb)[None]
+            kloc, vloc = to_np(torch, kb, cfg.dtype)[None], to_np(torch, vb, cfg.dtype)[None]
             remap = {int(p): j for j, p in enumerate(ids)}
             table = [remap[p] for p in otables[i]]
             slot = remap[oslots[i] // B] * B + oslots[i] % B
-            kn = to_np(k_new[layer, i:i + 1].cpu())
-            vn = to_np(v_new[layer, i:i + 1].cpu())
+            kn = to_np(torch, k_new[layer, i:i + 1], cfg.dtype)
+            vn = to_np(torch, v_new[layer, i:i + 1], cfg.dtype)
             kloc, vloc = okv.append_kv(kloc, vloc, 0, kn, vn, [slot], B)
-            q = to_np(q_all[layer, i:i + 1].cpu())
+            q = to_np(torch, q_all[layer, i:i + 1], cfg.dtype)
             return oatt.paged_decode(q, kloc, vloc, 0, [table], [int(lengths[i])], B, cfg.dtype)[0]
 
         errs = []
-        for (i, layer) in samples[:args.parity_samples]:
+        for (i, layer) in samples:
             expect = oracle_one(i, layer)
             got = out[layer, i].float().cpu().numpy().astype(np.float64)
             errs.append(float(np.max(np.abs(got - expect))))
         tol = 2e-2 if cfg.dtype == "bf16" else 1e-5
-        parity = {"samples": len(errs), "max_abs_err": max(errs) if errs else None, "tol": tol,
-                  "ok": bool(errs) and max(errs) <= tol}
-        print(f"[bench] parity {parity}", file=sys.stderr, flush=True)
+        if errs:
+            parity = {"samples": len(errs), "max_abs_err": max(errs), "tol": tol, "ok": max(errs) <= tol}
+            log(f"parity {parity}")
 
         if not args.no_cpu_baseline:
             try:
@@ -282,30 +303,23 @@ def main():
                 threadpool_limits = None
             cores = len(os.sched_getaffinity(0))
             pairs = [(int(rng.integers(0, n)), int(rng.integers(0, L))) for _ in range(args.cpu_sample)]
-            for (i, layer) in pairs:
-                if (i, layer) not in snap:
-                    ids = torch.from_numpy(np.asarray(tables_np[i, :math.ceil(lengths[i] / B)], np.int64)).to(dev)
-                    snap[(i, layer)] = (k_pool[layer].index_select(0, ids).cpu(),
-                                        v_pool[layer].index_select(0, ids).cpu(), ids.cpu().numpy())
-            import contextlib
+            for key in pairs:
+                if key not in snap:
+                    take_snapshot(*key)
             limiter = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
             with limiter:
                 t0 = time.perf_counter()
                 for (i, layer) in pairs:
                     oracle_one(i, layer)
                 cpu_s = time.perf_counter() - t0
-            per_pair = cpu_s / len(pairs)
-            step_s = per_pair * n * L
-            cpu_tok = n / step_s
-            cpu_gbs = kv_bytes_step / step_s / 1e9
-            cpu_baseline = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-                            "tokens_per_s": round(cpu_tok, 4),
-                            "sample": f"{len(pairs)} (sequence, layer) decodes of the same workload "
-                                      f"(each {int(lengths[0])} tokens x {Hq} heads) timed in "
+            step_s = cpu_s / len(pairs) * n * L
+            cpu_baseline = {"value": round(kv_bytes_step / step_s / 1e9, 4), "unit": "GB/s", "cores": cores,
+                            "kind": "oracle", "tokens_per_s": round(n / step_s, 4),
+                            "sample": f"{len(pairs)} (sequence, layer) decodes of this workload timed in "
                                       f"{cpu_s:.1f} s, scaled to the {n}-sequence x {L}-layer step"}
 
     result = {
-        "metric": "paged-decode KV GB/s (% of HBM peak) + decode tokens/s, 70B-GQA 32K ctx",
+        "metric": METRIC if cfg.name == "gqa70b_32k" else f"paged-decode KV GB/s + tokens/s, {cfg.name}",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -321,14 +335,230 @@ def main():
                    "head_dim": d, "block_size": B, "num_seqs": n, "context_len": int(lengths.max()),
                    "pool_blocks": cfg.num_blocks, "kv_bytes_per_step": kv_bytes_step,
                    "global_batch": n, "seq_len": int(lengths.max()), "parallelism": "none (1 GPU)"},
-        "tokens_per_s": round(tokens_per_s, 2),
-        "pct_hbm_peak": round(100 * value / 8000.0, 2),
+        "tokens_per_s": round(n / (ms_per_step * 1e-3), 2),
+        "pct_hbm_peak": round(100 * value / PEAK_GBS, 2),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "kernels": kernel_ms,
         "parity": parity,
     }
+    if cold is not None:
+        result["cold_ms_per_step"] = round(cold, 4)
+        result["cold_value"] = round(kv_bytes_step / (cold * 1e-3) / 1e9, 2)
     print(json.dumps(result), flush=True)
+
+
+# =============================================================================
+# Fork + copy-on-write workload
+# =============================================================================
+def run_fork(args):
+    torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool = setup(args)
+    from paged_kv_cache_83_amd import steps
+    from synth import gen
+    L, Hq, Hkv, d, B = cfg.num_layers, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim, cfg.block_size
+    n = cfg.num_seqs
+    suffix = gen.suffix_lengths(cfg)
+    lengths = gen.context_lengths(cfg)
+    bm = pk.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
+    parent = bm.seq_new()
+    bm.append(parent, cfg.prefix_len)
+    branches = [bm.fork(parent) for _ in range(n)]
+    bulk_slots, pairs = [], []
+    for b, m in zip(branches, suffix):
+        s, p = bm.append(b, int(m) - 1)
+        bulk_slots.append(s)
+        pairs += p
+    dec_slots, cow = bm.append_batch(branches, [1] * n)
+    assert len(pairs) == n and not cow
+    bulk = torch.from_numpy(np.concatenate(bulk_slots)).to(dev)
+    n_bulk = bulk.numel()
+    max_blocks = max(bm.info(b)[1] for b in branches)
+    tables_np, lens_np = bm.build_tables(branches, max_blocks)
+    assert np.array_equal(lens_np, lengths)
+    tables = torch.from_numpy(np.ascontiguousarray(tables_np)).to(dev)
+    lens = torch.from_numpy(np.ascontiguousarray(lens_np)).to(dev)
+    dec = torch.from_numpy(dec_slots).to(dev)
+    kb = torch.randn((L, n_bulk, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    vb = torch.randn((L, n_bulk, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    q_all = torch.randn((L, n, Hq, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    kn = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    vn = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    out = torch.empty((L, n, Hq, d), dtype=geom.torch_dtype, device=dev)
+    max_ctx = int(lengths.max())
+    ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx)), dtype=torch.uint8, device=dev)
+    src = torch.tensor([p[0] for p in pairs], dtype=torch.int32, device=dev)
+    dst = torch.tensor([p[1] for p in pairs], dtype=torch.int32, device=dev)
+
+    def step():
+        pk.copy_blocks(geom, k_pool, v_pool, src, dst, stream=stream)
+        for layer in range(L):
+            pk.append_kv(geom, k_pool, v_pool, layer, kb[layer], vb[layer], bulk, stream=stream)
+        # the 64 branches share the prefix blocks: keep them cacheable
+        steps.decode_step(geom, k_pool, v_pool, q_all, kn, vn, dec, tables, lens, max_ctx, out, ws,
+                          stream=stream, kv_reuse=True)
+
+    for _ in range(args.warmup):
+        step()
+    pk.Profiler.reset()
+    pk.Profiler.enable(True)
+    with Timer(torch, stream) as t:
+        for _ in range(args.steps):
+            step()
+    pk.Profiler.enable(False)
+    ms = max(t.ms, t.wall_ms) / args.steps
+    m_token = pk.bytes_per_token(L, Hkv, d, geom.elem_bytes)
+    logical = int(lengths.sum()) * m_token
+    unique = (cfg.prefix_len + int(suffix.sum())) * m_token
+    kern = {}
+    for name in ("copy_blocks", "append", "decode_partial", "decode_combine"):
+        cnt, tot = pk.Profiler.read(name)
+        if cnt:
+            kern[name] = {"launches": cnt, "avg_us": round(1e3 * tot / cnt, 2)}
+    blk = pk.bytes_per_block(geom)
+    copy_gbs = (2 * n * blk) / (kern["copy_blocks"]["avg_us"] * 1e-6) / 1e9
+    result = {
+        "metric": "fork/copy-on-write step: decode tokens/s and logical KV GB/s, fork_cow",
+        "value": round(n / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "branches": n, "prefix_len": cfg.prefix_len,
+                   "suffix_tokens": int(suffix.sum()), "cow_pairs": len(pairs), "num_layers": L},
+        "logical_kv_GBps": round(logical / (ms * 1e-3) / 1e9, 1),
+        "unique_kv_GBps": round(unique / (ms * 1e-3) / 1e9, 1),
+        "copy_blocks_GBps_rw": round(copy_gbs, 1),
+        "kernels": kern,
+    }
+    print(json.dumps(result), flush=True)
+
+
+# =============================================================================
+# Offload round trip
+# =============================================================================
+def run_offload(args):
+    torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool = setup(args)
+    from paged_kv_cache_83_amd import steps
+    from synth import gen
+    L, Hq, Hkv, d, B, n = (cfg.num_layers, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                           cfg.block_size, cfg.num_seqs)
+    lengths = gen.context_lengths(cfg)
+    bm = pk.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
+    seqs = [bm.seq_new() for _ in range(n)]
+    for s, S in zip(seqs, lengths):
+        bm.append(s, int(S) - 1)
+    bm.append_batch(seqs, [1] * n)
+    q_all = torch.randn((L, n, Hq, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    kn = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    vn = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    max_ctx = int(lengths.max())
+    lens = torch.from_numpy(lengths.astype(np.int32)).to(dev)
+    ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx)), dtype=torch.uint8, device=dev)
+
+    def decode():
+        tabs = [bm.table(s) for s in seqs]
+        slots = torch.tensor([t[(int(S) - 1) // B] * B + (int(S) - 1) % B for t, S in zip(tabs, lengths)],
+                             dtype=torch.int64, device=dev)
+        tables_np, _ = bm.build_tables(seqs, max(len(t) for t in tabs))
+        out = torch.empty((L, n, Hq, d), dtype=geom.torch_dtype, device=dev)
+        steps.decode_step(geom, k_pool, v_pool, q_all, kn, vn, slots,
+                          torch.from_numpy(np.ascontiguousarray(tables_np)).to(dev), lens, max_ctx, out, ws,
+                          stream=stream)
+        torch.cuda.synchronize()
+        return out
+
+    before = decode()
+    blocks_per_seq = bm.info(seqs[0])[1]
+    choice = gen.offload_choice(cfg, blocks_per_seq)
+    keep = max(1, int(round(args.offload_fraction * choice.shape[1])))
+    choice = choice[:, :keep]
+    phys = [bm.swap_out(s, choice[k].tolist()) for k, s in enumerate(seqs)]
+    ids = torch.from_numpy(np.concatenate(phys).astype(np.int32)).to(dev)
+    per = pk.bytes_per_block(geom)
+    total = ids.numel() * per
+    log(f"offloading {ids.numel()} blocks = {total / 2**30:.1f} GiB to pinned host memory")
+    t0 = time.perf_counter()
+    host = torch.empty(total, dtype=torch.uint8, pin_memory=True)
+    log(f"pinned host buffer allocated in {time.perf_counter() - t0:.1f} s")
+    chunk = cfg.offload_chunk_blocks
+    staging = torch.empty(chunk * per, dtype=torch.uint8, device=dev)
+
+    legs = {"gather": [], "d2h": [], "h2d": [], "scatter": []}
+    marks = []
+
+    def mark(kind, start, m):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        marks.append((kind, m, ev))
+
+    def leg_times(start_ev):
+        prev = start_ev
+        for kind, m, ev in marks:
+            legs[kind].append((m, prev.elapsed_time(ev)))
+            prev = ev
+        marks.clear()
+
+    with Timer(torch, stream) as t_out:
+        steps.offload(geom, k_pool, v_pool, ids, host, staging, chunk, stream=stream, on_chunk=mark)
+    leg_times(t_out.a)
+    log(f"offload: {t_out.ms:.1f} ms")
+    # the freed frames may now be reused: scribble over them, then swap back in
+    k_pool[:, ids.long()] = float("nan")
+    v_pool[:, ids.long()] = float("nan")
+    bm.permute_free(gen.realloc_shuffle(cfg, bm.num_free()))
+    new_phys = [bm.swap_in(s, choice[k].tolist()) for k, s in enumerate(seqs)]
+    new_ids = torch.from_numpy(np.concatenate(new_phys).astype(np.int32)).to(dev)
+    with Timer(torch, stream) as t_in:
+        steps.restore(geom, k_pool, v_pool, new_ids, host, staging, chunk, stream=stream, on_chunk=mark)
+    leg_times(t_in.a)
+    log(f"restore: {t_in.ms:.1f} ms")
+    after = decode()
+    bit_exact = bool(torch.equal(before.view(torch.int16), after.view(torch.int16)))
+
+    def rate(kind, factor):
+        m = sum(x[0] for x in legs[kind])
+        ms = sum(x[1] for x in legs[kind])
+        return round(factor * m * per / (ms * 1e-3) / 1e9, 1), round(ms, 2)
+
+    g_gbs, g_ms = rate("gather", 2)
+    s_gbs, s_ms = rate("scatter", 2)
+    d_gbs, d_ms = rate("d2h", 1)
+    h_gbs, h_ms = rate("h2d", 1)
+    result = {
+        "metric": "offload round trip: gather/scatter GB/s (read+write), host link GB/s, offload",
+        "value": round(2 * total / ((t_out.ms + t_in.ms) * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": 1, "warmup": 0, "ms_per_step": round(t_out.ms + t_in.ms, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "num_seqs": n, "context_len": int(lengths.max()),
+                   "blocks_moved": int(ids.numel()), "bytes_moved": total, "chunk_blocks": chunk,
+                   "offload_fraction": args.offload_fraction},
+        "gather_GBps_rw": g_gbs, "gather_ms": g_ms, "scatter_GBps_rw": s_gbs, "scatter_ms": s_ms,
+        "d2h_GBps": d_gbs, "d2h_ms": d_ms, "h2d_GBps": h_gbs, "h2d_ms": h_ms,
+        "roofline": {"bound": "hbm", "kernel": "block_move_kernel (gather)", "achieved": g_gbs,
+                     "peak": PEAK_GBS, "unit": "GB/s", "frac": round(g_gbs / PEAK_GBS, 4), "traffic": None},
+        "decode_bitwise_equal_after_round_trip": bit_exact,
+    }
+    print(json.dumps(result), flush=True)
+    if not bit_exact:
+        sys.exit(1)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (see the sharding note in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    from synth import get_config
+    cfg = get_config(args.config)
+    if cfg.name == "offload":
+        run_offload(args)
+    elif cfg.length_kind == "fork":
+        run_fork(args)
+    else:
+        run_decode(args)
 
 
 if __name__ == "__main__":

@@ -113,7 +113,7 @@ int64_t pa_pool_bytes(const pa_geom* g);
 /* Slot-mapped write of new keys and values into one layer.
  * k_new, v_new: [n_tokens][H_kv][d] device arrays. slot_mapping: int64 [n_tokens]
  * device array; token j goes to block slot/B, offset slot%B; a negative slot
- * skips the token. Source: "KV Cache Management", "The PagedAttention virtual
+ * skips the token; slots must be distinct. Source: "KV Cache Management", "The PagedAttention virtual
  * memory model" (write into T[l] at offset o); "PagedAttention", "The real cache". */
 pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer,
                        const void* k_new, const void* v_new, const int64_t* slot_mapping,
@@ -123,6 +123,10 @@ pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t lay
 typedef struct {
   int32_t blocks_per_split; /* logical blocks per split-K work item (0 = choose; rounded up to even) */
   int32_t kernel;           /* 0 = choose, 1 = generic VALU kernel, 2 = MFMA kernel (bf16, B=16) */
+  int32_t kv_reuse;         /* 0: each K/V block is read once per step -> stream it past the
+                               caches (non-temporal loads); 1: blocks are shared by many
+                               sequences of the batch (forks, common prefixes) -> ordinary
+                               loads so repeats hit in L2 / Infinity Cache (MFMA kernel) */
 } pa_decode_opts;
 
 /* Workspace bytes pa_decode needs for these sizes and options (0 when the

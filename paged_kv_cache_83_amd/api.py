@@ -133,8 +133,8 @@ def append_kv(geom: Geometry, k_pool, v_pool, layer: int, k_new, v_new, slot_map
           "pa_append_kv")
 
 
-def _opts(blocks_per_split: int, kernel: int) -> _lib.pa_decode_opts:
-    return _lib.pa_decode_opts(int(blocks_per_split), int(kernel))
+def _opts(blocks_per_split: int, kernel: int, kv_reuse: bool = False) -> _lib.pa_decode_opts:
+    return _lib.pa_decode_opts(int(blocks_per_split), int(kernel), 1 if kv_reuse else 0)
 
 
 KERNELS = {"auto": 0, "generic": 1, "mfma": 2}
@@ -150,9 +150,10 @@ def decode_workspace_bytes(geom: Geometry, n_seqs: int, n_q_heads: int, max_cont
 
 def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, context_lens,
            max_context_len: int, scale: float = 0.0, workspace=None, blocks_per_split: int = 0,
-           kernel: str = "auto", stream=None):
+           kernel: str = "auto", stream=None, kv_reuse: bool = False):
     """out[i, h] = softmax attention of q[i, h] over sequence i's first
-    context_lens[i] tokens, read through block_tables[i]."""
+    context_lens[i] tokens, read through block_tables[i]. kv_reuse=True when many
+    sequences of the batch share blocks (keeps them cacheable)."""
     _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
     _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
     if q.dim() != 3 or q.shape[2] != geom.head_dim:
@@ -165,7 +166,7 @@ def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, con
     _dev(block_tables, "block_tables", torch.int32)
     _dev(context_lens, "context_lens", torch.int32, n)
     g = geom.c()
-    o = _opts(blocks_per_split, KERNELS[kernel])
+    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse)
     need = int(_L().pa_decode_workspace_bytes(C.byref(g), n, hq, max_context_len, C.byref(o)))
     ws_ptr, ws_bytes = None, 0
     if need:

@@ -86,17 +86,64 @@ __host__ __device__ __forceinline__ int k_chunk(int D) { return (D % 32 == 0) ? 
 
 // =============================================================================
 // Append: token j's K/V go to slot slot_mapping[j] of one layer.
-// One thread moves VEC consecutive elements of one (token, head).
+// One thread moves VEC consecutive dimensions (16 bytes) of one head of one
+// token. Its K lands as one 16-byte store inside the slot's row. V is
+// dimension-major inside a block, so one token's V is VEC scattered elements;
+// but when VEC tokens fill a VEC-aligned run of consecutive slots of one block
+// (bulk appends, in whatever order the runs of different sequences were
+// concatenated), the thread of the run's first token loads all VEC tokens'
+// values, transposes them in registers and writes each dimension's run as one
+// 16-byte store, and the other tokens of the run skip their V.
 // =============================================================================
+
+// VEC elements of T as one 16-byte access when they make up exactly 16 bytes
+// (the callers guarantee 16-byte alignment then), element by element otherwise.
 template <typename T, int VEC>
-__global__ void append_kv_kernel(T* __restrict__ kpool, T* __restrict__ vpool,
-                                 const T* __restrict__ knew, const T* __restrict__ vnew,
-                                 const int64_t* __restrict__ slots, int n_tok, int Hkv, int D,
-                                 int B, int64_t nslots, int64_t layer_off) {
+__device__ __forceinline__ void load_vec(T (&dst)[VEC], const T* src) {
+  if constexpr (VEC * sizeof(T) == 16) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+    __builtin_memcpy(&dst[0], &v, 16);
+  } else {
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) dst[u] = src[u];
+  }
+}
+template <typename T, int VEC>
+__device__ __forceinline__ void store_vec(T* dst, const T (&src)[VEC]) {
+  if constexpr (VEC * sizeof(T) == 16) {
+    u32x4 v;
+    __builtin_memcpy(&v, &src[0], 16);
+    *reinterpret_cast<u32x4*>(dst) = v;
+  } else {
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) dst[u] = src[u];
+  }
+}
+
+// Tokens first .. first+VEC-1 exist and occupy VEC consecutive slots starting at a
+// VEC-aligned slot of one block.
+template <int VEC>
+__device__ __forceinline__ bool aligned_run(const int64_t* __restrict__ slots, int64_t first,
+                                            int n_tok, int B, int64_t nslots) {
+  if (first < 0 || first + VEC > n_tok || (B % VEC) != 0) return false;
+  const int64_t s0 = slots[first];
+  if (s0 < 0 || s0 + VEC > nslots || (s0 % VEC) != 0) return false;
+#pragma unroll
+  for (int e = 1; e < VEC; ++e)
+    if (slots[first + e] != s0 + e) return false;
+  return true;
+}
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(256) void append_kv_kernel(T* __restrict__ kpool, T* __restrict__ vpool,
+                                                        const T* __restrict__ knew,
+                                                        const T* __restrict__ vnew,
+                                                        const int64_t* __restrict__ slots, int n_tok,
+                                                        int Hkv, int D, int B, int64_t nslots,
+                                                        int64_t layer_off) {
   const int chunks = D / VEC;
   const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t total = (int64_t)n_tok * Hkv * chunks;
-  if (tid >= total) return;
+  if (tid >= (int64_t)n_tok * Hkv * chunks) return;
   const int c = (int)(tid % chunks);
   const int64_t th = tid / chunks;
   const int h = (int)(th % Hkv);
@@ -105,22 +152,34 @@ __global__ void append_kv_kernel(T* __restrict__ kpool, T* __restrict__ vpool,
   if (slot < 0 || slot >= nslots) return;
   const int64_t p = slot / B;
   const int o = (int)(slot % B);
-  const int64_t src = (j * Hkv + h) * D + (int64_t)c * VEC;
-  const int64_t tile = layer_off + (p * Hkv + h) * (int64_t)B * D;
-  T kv[VEC], vv[VEC];
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) {
-    kv[e] = knew[src + e];
-    vv[e] = vnew[src + e];
-  }
-  const int j0 = c * VEC;  // VEC divides the chunk width, so the run stays in one chunk
+  const int d0 = c * VEC;  // VEC divides the K chunk width, so a run stays in one chunk
   const int W = k_chunk(D);
-  T* kd = kpool + tile + (int64_t)(j0 / W) * B * W + (int64_t)o * W + (j0 % W);
+  const int64_t tile = layer_off + (p * Hkv + h) * (int64_t)B * D;
+
+  T kv[VEC];
+  load_vec<T, VEC>(kv, knew + (j * Hkv + h) * D + d0);
+  store_vec<T, VEC>(kpool + tile + (int64_t)(d0 / W) * B * W + (int64_t)o * W + (d0 % W), kv);
+
+  T* vd = vpool + tile + (int64_t)d0 * B;
+  const int lead = o % VEC;  // position of this token inside its aligned slot run
+  if (aligned_run<VEC>(slots, j - lead, n_tok, B, nslots)) {
+    if (lead != 0) return;  // the run's first token writes the whole run
+    T vv[VEC][VEC];         // [token][dim]
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) kd[e] = kv[e];
-  T* vd = vpool + tile + (int64_t)c * VEC * B + o;
+    for (int e = 0; e < VEC; ++e) load_vec<T, VEC>(vv[e], vnew + ((j + e) * Hkv + h) * D + d0);
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) vd[(int64_t)e * B] = vv[e];
+    for (int u = 0; u < VEC; ++u) {
+      T row[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) row[e] = vv[e][u];
+      store_vec<T, VEC>(vd + (int64_t)u * B + o, row);
+    }
+    return;
+  }
+  T vv[VEC];
+  load_vec<T, VEC>(vv, vnew + (j * Hkv + h) * D + d0);
+#pragma unroll
+  for (int u = 0; u < VEC; ++u) vd[(int64_t)u * B + o] = vv[u];
 }
 
 // =============================================================================
@@ -207,10 +266,13 @@ struct PairFrags {
   u32x4 v[MfmaCfg<D>::DT];
 };
 
-// K/V tiles are read exactly once per step: stream them past the caches
-// (non-temporal loads sustain ~12% more HBM read bandwidth on this part).
-__device__ __forceinline__ u32x4 stream_load16(const uint16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// K/V tiles read once per step are streamed past the caches (non-temporal loads
+// sustain ~12% more HBM read bandwidth on this part); tiles shared by many
+// sequences of the batch use ordinary loads so the repeats hit in L2 / MALL.
+template <bool NT>
+__device__ __forceinline__ u32x4 kv_load16(const uint16_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -252,7 +314,7 @@ __device__ __forceinline__ int table_at(const int (&tb)[4], int off) {
   }
 }
 
-template <int D>
+template <int D, bool NT>
 __device__ __forceinline__ void issue_pair(PairFrags<D>& f, const uint16_t* __restrict__ kl,
                                            const uint16_t* __restrict__ vl, int p0, int p1, int Hkv,
                                            int g, int k_sel, int k_off0, int v_sel, int v_off,
@@ -266,10 +328,10 @@ __device__ __forceinline__ void issue_pair(PairFrags<D>& f, const uint16_t* __re
   for (int t = 0; t < 2; ++t) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      f.k[t][kc] = stream_load16(krow + kc * 512 + (k_off0 + 4 * t) * 32 + 8 * gq);
+      f.k[t][kc] = kv_load16<NT>(krow + kc * 512 + (k_off0 + 4 * t) * 32 + 8 * gq);
   }
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) f.v[dt] = stream_load16(vrow + dt * 256 + v_off);
+  for (int dt = 0; dt < DT; ++dt) f.v[dt] = kv_load16<NT>(vrow + dt * 256 + v_off);
 }
 
 template <int D>
@@ -339,7 +401,7 @@ __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)
                                                       acc[dt], 0, 0, 0);
 }
 
-template <int D, bool DIRECT>
+template <int D, bool DIRECT, bool NT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2))) void decode_mfma_bf16_kernel(
     const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out, float* __restrict__ part_o,
@@ -425,17 +487,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
   PairFrags<D> fa, fb;
   int p0, p1;
   ids(0, p0, p1);
-  issue_pair<D>(fa, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
+  issue_pair<D, NT>(fa, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
   for (int pj = 0;;) {
     if (pj + 1 < npairs) {
       ids(pj + 1, p0, p1);
-      issue_pair<D>(fb, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
+      issue_pair<D, NT>(fb, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
     }
     compute_pair<D>(fa, qf, acc, m_run, l_run, b0 + 2 * pj, len, gq, qk_scale);
     if (++pj >= npairs) break;
     if (pj + 1 < npairs) {
       ids(pj + 1, p0, p1);
-      issue_pair<D>(fa, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
+      issue_pair<D, NT>(fa, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
     }
     compute_pair<D>(fb, qf, acc, m_run, l_run, b0 + 2 * pj, len, gq, qk_scale);
     if (++pj >= npairs) break;
@@ -747,6 +809,7 @@ size_t generic_lds_bytes(int G, int D, int B) {
 
 struct DecodePlan {
   int kernel;  // 1 generic, 2 mfma
+  bool stream_kv;  // non-temporal K/V loads
   int bps;
   int S_max;
   bool direct;
@@ -785,13 +848,16 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
     // Aim for about one work item per SIMD (256 CUs x 4): each item pays two
     // dependent load latencies at start (block ids, then its first blocks), so
     // fewer, longer items beat more, shorter ones once the chip is covered.
+    // The generic kernel walks its blocks one at a time with a load latency per
+    // block, so it wants many short items instead.
     const int64_t units = (int64_t)n_seqs * g->num_kv_heads;
-    const int64_t target_items = 1024;
+    const int64_t target_items = k == 2 ? 1024 : 4096;
+    const int64_t min_bps = k == 2 ? 16 : 2;
     if (units >= target_items || units == 0) {
       bps = maxb;
     } else {
       const int64_t want_splits = (target_items + units - 1) / units;
-      bps = std::max<int64_t>(16, (maxb + want_splits - 1) / want_splits);
+      bps = std::max<int64_t>(min_bps, (maxb + want_splits - 1) / want_splits);
     }
   }
   bps = std::max<int64_t>(2, bps);
@@ -799,7 +865,9 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
   if (k == 2) bps = std::min<int64_t>(bps, kMfmaMaxBps);
   if (bps > INT32_MAX / 2) bps = INT32_MAX / 2;
   int64_t S = maxb == 0 ? 1 : (maxb + bps - 1) / bps;
+  if (opts && (opts->kv_reuse < 0 || opts->kv_reuse > 1)) return PA_ERR_INVALID_ARG;
   plan->kernel = k;
+  plan->stream_kv = !(opts && opts->kv_reuse == 1);
   plan->bps = (int)bps;
   plan->S_max = (int)S;
   plan->direct = S == 1;
@@ -890,12 +958,17 @@ pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, in
     ProfScope ps("decode_partial", st);
     const dim3 grid((unsigned)items), block(64);
     if (plan.kernel == 2) {
-#define PA_MFMA_LAUNCH(DD, DIR)                                                                   \
-  hipLaunchKernelGGL((decode_mfma_bf16_kernel<DD, DIR>), grid, block, 0, st,                      \
+#define PA_MFMA_LAUNCH_NT(DD, DIR, NTV)                                                           \
+  hipLaunchKernelGGL((decode_mfma_bf16_kernel<DD, DIR, NTV>), grid, block, 0, st,                 \
                      (const uint16_t*)k_pool, (const uint16_t*)v_pool, (const uint16_t*)q,         \
                      (uint16_t*)out, part_o, part_ml, block_tables, context_lens, layer_off,       \
                      g->num_blocks, Hkv, n_q_heads, G, max_blocks_per_seq, max_context_len,        \
                      plan.bps, plan.S_max, qk_scale)
+#define PA_MFMA_LAUNCH(DD, DIR)                                          \
+  do {                                                                   \
+    if (plan.stream_kv) PA_MFMA_LAUNCH_NT(DD, DIR, true);                \
+    else PA_MFMA_LAUNCH_NT(DD, DIR, false);                              \
+  } while (0)
       if (D == 64) {
         if (plan.direct) PA_MFMA_LAUNCH(64, true); else PA_MFMA_LAUNCH(64, false);
       } else if (D == 128) {
@@ -904,6 +977,7 @@ pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, in
         if (plan.direct) PA_MFMA_LAUNCH(256, true); else PA_MFMA_LAUNCH(256, false);
       }
 #undef PA_MFMA_LAUNCH
+#undef PA_MFMA_LAUNCH_NT
     } else {
       const size_t lds = generic_lds_bytes(G, D, B);
 #define PA_GEN_LAUNCH_R(T, DIR, RR)                                                               \

@@ -31,7 +31,7 @@ from .api import Geometry
 def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slots, tables, lens,
                 max_context_len: int, out_all, workspace, layers: Optional[Sequence[int]] = None,
                 blocks_per_split: int = 0, kernel: str = "auto", stream=None,
-                around_decode: Optional[Callable[[int, bool], None]] = None):
+                around_decode: Optional[Callable[[int, bool], None]] = None, kv_reuse: bool = False):
     """One decode step: for each layer, append the new tokens, then decode.
 
     q_all [L, n, H_q, d]; k_new_all / v_new_all [L, n_tok, H_kv, d]; slots int64
@@ -46,7 +46,7 @@ def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slo
             around_decode(layer, True)
         api.decode(geom, k_pool, v_pool, layer, q_all[layer], out_all[layer], tables, lens,
                    max_context_len, workspace=workspace, blocks_per_split=blocks_per_split,
-                   kernel=kernel, stream=stream)
+                   kernel=kernel, stream=stream, kv_reuse=kv_reuse)
         if around_decode is not None:
             around_decode(layer, False)
 

@@ -178,3 +178,28 @@ def test_unsupported_and_bad_arguments():
         pk.decode(geom, K, V, 0, q, out, tabs, lens, 17)                    # table too short
     with pytest.raises(ValueError):
         pk.decode(geom, K, V, 0, q.to(torch.bfloat16), out, tabs, lens, 16)  # dtype mismatch
+
+
+def test_kv_reuse_policy_same_result():
+    """Cached (kv_reuse) and streamed K/V loads compute the same bits."""
+    need_gpu()
+    print_case(test="kv_reuse")
+    batch = make_batch("bf16", 1, 200, 32, 4, 128, 16, [1, 40, 300, 777], seed=61)
+    geom = pk.Geometry(1, 4, 128, 16, 200, "bf16")
+    outs = []
+    for reuse in (False, True):
+        K, V = to_dev(batch.k_pool, "bf16"), to_dev(batch.v_pool, "bf16")
+        pk.append_kv(geom, K, V, 0, to_dev(batch.k_new, "bf16"), to_dev(batch.v_new, "bf16"),
+                     torch.from_numpy(batch.slots_new).cuda())
+        q = to_dev(batch.q, "bf16")
+        out = torch.empty_like(q)
+        ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, 4, 32, 777)), dtype=torch.uint8,
+                         device="cuda")
+        pk.decode(geom, K, V, 0, q, out, torch.from_numpy(padded_tables(batch.tables, batch.max_blocks)).cuda(),
+                  torch.from_numpy(batch.lengths.astype(np.int32)).cuda(), 777, workspace=ws,
+                  kv_reuse=reuse)
+        torch.cuda.synchronize()
+        outs.append(to_host(out, "bf16"))
+    assert np.array_equal(outs[0], outs[1])
+    _, _, expect = oracle_step(batch, 0)
+    assert max_abs_err(outs[0], expect, "bf16") <= BF16_TOL

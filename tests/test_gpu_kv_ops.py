@@ -118,3 +118,33 @@ def test_empty_and_guarded_calls():
     assert int(K.view(torch.int16).abs().sum()) == 0
     with pytest.raises(ValueError):
         pk.gather_blocks(geom, K, V, ok, staging)      # staging too small: host check
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64), ("bf16", 40)])
+def test_bulk_append_runs_bit_exact(dtype, d):
+    """Runs of consecutive slots from several sequences, concatenated in a
+    shuffled order and starting at arbitrary offsets (the case the 16-byte V
+    path serves), plus stray single tokens and skipped ones."""
+    need_gpu()
+    print_case(test="bulk_append", dtype=dtype, d=d)
+    L, N, H, B = 2, 96, 4, 16
+    geom = pk.Geometry(L, H, d, B, N, dtype)
+    kp, vp = _pools(dtype, L, N, H, d, B, 60)
+    rng = np.random.default_rng(11)
+    perm = rng.permutation(N)
+    runs, cursor = [], 0
+    for length, start in [(37, 8), (16, 0), (5, 3), (64, 0), (23, 8), (1, 15), (40, 5)]:
+        blocks = perm[cursor:cursor + (start + length + B - 1) // B]
+        cursor += len(blocks)
+        runs.append([int(blocks[(start + t) // B]) * B + (start + t) % B for t in range(length)])
+    order = rng.permutation(len(runs))
+    slots = np.concatenate([runs[k] for k in order] + [[-1, -1]]).astype(np.int64)
+    n = len(slots)
+    kn = gen.normal_values(61, (n, H, d), dtype)
+    vn = gen.normal_values(62, (n, H, d), dtype)
+    K, V = to_dev(kp, dtype), to_dev(vp, dtype)
+    pk.append_kv(geom, K, V, 1, to_dev(kn, dtype), to_dev(vn, dtype), torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    ek, ev = okv.append_kv(kp, vp, 1, kn, vn, slots, B)
+    assert np.array_equal(to_host(K, dtype).view(np.uint8), ek.view(np.uint8))
+    assert np.array_equal(to_host(V, dtype).view(np.uint8), ev.view(np.uint8))
