@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--parity-samples", type=int, default=4)
+    ap.add_argument("--unfused", action="store_true",
+                    help="append the step's tokens with a separate launch before each decode")
     ap.add_argument("--offload-fraction", type=float, default=1.0,
                     help="offload workload: fraction of the chosen blocks moved (host RAM bound)")
     return ap.parse_args()
@@ -202,7 +204,7 @@ def run_decode(args):
     def step():
         steps.decode_step(geom, k_pool, v_pool, q_all, k_new, v_new, slots, tables, lens, max_ctx, out,
                           ws, blocks_per_split=args.bps, kernel=args.kernel, stream=stream,
-                          around_decode=around)
+                          around_decode=around, fused=not args.unfused)
 
     for _ in range(args.warmup):
         step()
@@ -248,7 +250,8 @@ def run_decode(args):
             per_launch = (int(lengths.sum()) * 2 * Hkv * d * eb                 # K and V of attended tokens
                           + n * Hq * d * eb                                      # queries
                           + 4 * int(sum(math.ceil(S / B) for S in lengths))       # block-table entries
-                          + (n * Hq * splits * (d + 2) * 4 if ws_bytes else n * Hq * d * eb))
+                          + (n * Hq * splits * (d + 2) * 4 if ws_bytes else n * Hq * d * eb)
+                          + (0 if args.unfused else 4 * n * Hkv * d * eb))        # new K/V read + written
             avg_s = tot / cnt * 1e-3
             achieved = per_launch / avg_s / 1e9
             mfma = cfg.dtype == "bf16" and B == 16 and args.kernel != "generic"
@@ -334,7 +337,8 @@ def run_decode(args):
         "config": {"workload": cfg.name, "num_layers": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": d, "block_size": B, "num_seqs": n, "context_len": int(lengths.max()),
                    "pool_blocks": cfg.num_blocks, "kv_bytes_per_step": kv_bytes_step,
-                   "global_batch": n, "seq_len": int(lengths.max()), "parallelism": "none (1 GPU)"},
+                   "global_batch": n, "seq_len": int(lengths.max()), "parallelism": "none (1 GPU)",
+                   "append": "separate launch" if args.unfused else "fused into decode"},
         "tokens_per_s": round(n / (ms_per_step * 1e-3), 2),
         "pct_hbm_peak": round(100 * value / PEAK_GBS, 2),
         "roofline": roofline,
@@ -395,7 +399,7 @@ def run_fork(args):
             pk.append_kv(geom, k_pool, v_pool, layer, kb[layer], vb[layer], bulk, stream=stream)
         # the 64 branches share the prefix blocks: keep them cacheable
         steps.decode_step(geom, k_pool, v_pool, q_all, kn, vn, dec, tables, lens, max_ctx, out, ws,
-                          stream=stream, kv_reuse=True)
+                          stream=stream, kv_reuse=True, fused=not args.unfused)
 
     for _ in range(args.warmup):
         step()
@@ -461,7 +465,7 @@ def run_offload(args):
         out = torch.empty((L, n, Hq, d), dtype=geom.torch_dtype, device=dev)
         steps.decode_step(geom, k_pool, v_pool, q_all, kn, vn, slots,
                           torch.from_numpy(np.ascontiguousarray(tables_np)).to(dev), lens, max_ctx, out, ws,
-                          stream=stream)
+                          stream=stream, fused=not args.unfused)
         torch.cuda.synchronize()
         return out
 

@@ -152,6 +152,25 @@ pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, in
                     const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* One decode step's append and decode, fused: for each sequence i, the new
+ * token's key and value (k_new[i], v_new[i], [n_seqs][H_kv][d] device arrays)
+ * are written at position context_lens[i] - 1, i.e. into block
+ * block_tables[i][(len-1)/B] at offset (len-1)%B, and then out is computed as
+ * pa_decode computes it over the first context_lens[i] tokens, that one
+ * included. The pool afterwards holds exactly what pa_append_kv with
+ * slot = table[(len-1)/B]*B + (len-1)%B followed by pa_decode leaves. The
+ * block holding position len-1 must be owned by sequence i alone (a shared tail
+ * block is copied first, by copy-on-write) and context_lens[i] == 0 writes
+ * nothing. Source: "KV Cache Management", "The PagedAttention virtual memory
+ * model" (a step writes its token at offset o of its current block, then
+ * attends over the table); "PagedAttention", "The real cache". */
+pa_status pa_decode_append(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer,
+                           const void* q, const void* k_new, const void* v_new, void* out,
+                           int32_t n_seqs, int32_t n_q_heads, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, float scale, const pa_decode_opts* opts,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Copy-on-write block copy: for each k, block dst[k] <- block src[k] in every
  * layer, K and V, all B slots. src, dst: int32 [n_pairs] device arrays; no dst
  * may appear as a src or twice. Source: "KV Cache Management", "Zero-copy

@@ -148,12 +148,8 @@ def decode_workspace_bytes(geom: Geometry, n_seqs: int, n_q_heads: int, max_cont
                                               C.byref(o)))
 
 
-def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, context_lens,
-           max_context_len: int, scale: float = 0.0, workspace=None, blocks_per_split: int = 0,
-           kernel: str = "auto", stream=None, kv_reuse: bool = False):
-    """out[i, h] = softmax attention of q[i, h] over sequence i's first
-    context_lens[i] tokens, read through block_tables[i]. kv_reuse=True when many
-    sequences of the batch share blocks (keeps them cacheable)."""
+def _decode_args(geom: Geometry, k_pool, v_pool, q, out, block_tables, context_lens,
+                 max_context_len, workspace, o):
     _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
     _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
     if q.dim() != 3 or q.shape[2] != geom.head_dim:
@@ -166,7 +162,6 @@ def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, con
     _dev(block_tables, "block_tables", torch.int32)
     _dev(context_lens, "context_lens", torch.int32, n)
     g = geom.c()
-    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse)
     need = int(_L().pa_decode_workspace_bytes(C.byref(g), n, hq, max_context_len, C.byref(o)))
     ws_ptr, ws_bytes = None, 0
     if need:
@@ -174,11 +169,44 @@ def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, con
             raise ValueError(f"decode needs a workspace of {need} bytes")
         _dev(workspace, "workspace")
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    return g, n, hq, ws_ptr, ws_bytes
+
+
+def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, context_lens,
+           max_context_len: int, scale: float = 0.0, workspace=None, blocks_per_split: int = 0,
+           kernel: str = "auto", stream=None, kv_reuse: bool = False):
+    """out[i, h] = softmax attention of q[i, h] over sequence i's first
+    context_lens[i] tokens, read through block_tables[i]. kv_reuse=True when many
+    sequences of the batch share blocks (keeps them cacheable)."""
+    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse)
+    g, n, hq, ws_ptr, ws_bytes = _decode_args(geom, k_pool, v_pool, q, out, block_tables,
+                                              context_lens, max_context_len, workspace, o)
     check(_L().pa_decode(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(q), _ptr(out), n, hq,
                          _ptr(block_tables), int(block_tables.shape[1]), _ptr(context_lens),
                          int(max_context_len), float(scale), C.byref(o), ws_ptr, ws_bytes,
                          _stream(stream, q.device)),
           "pa_decode")
+
+
+def decode_append(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out, block_tables,
+                  context_lens, max_context_len: int, scale: float = 0.0, workspace=None,
+                  blocks_per_split: int = 0, kernel: str = "auto", stream=None,
+                  kv_reuse: bool = False):
+    """Write each sequence's new token (k_new[i], v_new[i]: [n_seqs, H_kv, d]) at
+    position context_lens[i] - 1 through its block table, then decode as
+    `decode` does, in one launch."""
+    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse)
+    g, n, hq, ws_ptr, ws_bytes = _decode_args(geom, k_pool, v_pool, q, out, block_tables,
+                                              context_lens, max_context_len, workspace, o)
+    per = geom.num_kv_heads * geom.head_dim
+    _dev(k_new, "k_new", geom.torch_dtype, n * per)
+    _dev(v_new, "v_new", geom.torch_dtype, n * per)
+    check(_L().pa_decode_append(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(q),
+                                _ptr(k_new), _ptr(v_new), _ptr(out), n, hq, _ptr(block_tables),
+                                int(block_tables.shape[1]), _ptr(context_lens),
+                                int(max_context_len), float(scale), C.byref(o), ws_ptr, ws_bytes,
+                                _stream(stream, q.device)),
+          "pa_decode_append")
 
 
 def _ids(t, what, n=None):

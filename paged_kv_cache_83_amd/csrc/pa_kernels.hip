@@ -401,10 +401,14 @@ __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)
                                                       acc[dt], 0, 0, 0);
 }
 
-template <int D, bool DIRECT, bool NT>
+// APPEND: the step's new token of every sequence (position len-1) comes in
+// knew/vnew [n][H_kv][d]; the work item holding that position writes it into the
+// pool and uses it from registers (K by address, V by element) while attending.
+template <int D, bool DIRECT, bool NT, bool APPEND>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2))) void decode_mfma_bf16_kernel(
-    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
-    const uint16_t* __restrict__ q, uint16_t* __restrict__ out, float* __restrict__ part_o,
+    uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ knew,
+    const uint16_t* __restrict__ vnew, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, int64_t layer_off, int N, int Hkv, int Hq, int G,
     int max_blocks, int max_ctx, int bps, int S_max, float qk_scale) {
@@ -468,6 +472,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
 
   const uint16_t* kl = kpool + layer_off;
   const uint16_t* vl = vpool + layer_off;
+
+  // The appended token is written into the pool by the item whose split holds
+  // its block, before that item reads the block: the whole work group is this
+  // one wave, so a work-group fence after the stores makes them visible to the
+  // loads of every lane below.
+  if (APPEND && len > 0 && ((len - 1) >> 4) >= b0 && ((len - 1) >> 4) < b1) {
+    const int pos = len - 1;
+    const uint16_t* knew_row = knew + ((int64_t)i * Hkv + g) * D;
+    const uint16_t* vnew_row = vnew + ((int64_t)i * Hkv + g) * D;
+    const int pn = guard_block(trow[pos >> 4], N);
+    const int on = pos & 15;
+    uint16_t* kt = kpool + layer_off + ((int64_t)pn * Hkv + g) * (16 * D);
+    uint16_t* vt = vpool + layer_off + ((int64_t)pn * Hkv + g) * (16 * D);
+    if (lane < D / 8) {  // K row: lane moves dims 8*lane .. +8 (a 32-dim chunk takes 4 lanes)
+      const u32x4 kv8 = *reinterpret_cast<const u32x4*>(knew_row + 8 * lane);
+      *reinterpret_cast<u32x4*>(kt + (lane >> 2) * 512 + on * 32 + 8 * (lane & 3)) = kv8;
+    }
+    for (int d = lane; d < D; d += 64) vt[d * 16 + on] = vnew_row[d];  // V column
+    __threadfence_block();
+  }
+
   // Row r = c of each score tile holds pair-local key 8*(c>>2) + 4*t + (c&3):
   // block (c >> 3) of the pair, offset 8*((c>>2)&1) + 4*t + (c&3).
   const int k_sel = c >> 3;
@@ -537,9 +562,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
 constexpr int kGenMaxAcc = 64;  // largest G*d / 64 the generic kernel accepts
 
 // R = accumulators per lane, ceil(G*d / 64) rounded up to one of 1, 4, 16, 64.
-template <typename T, bool DIRECT, int R>
+template <typename T, bool DIRECT, int R, bool APPEND>
 __global__ __launch_bounds__(64) void decode_generic_kernel(
-    const T* __restrict__ kpool, const T* __restrict__ vpool, const T* __restrict__ q,
+    T* __restrict__ kpool, T* __restrict__ vpool, const T* __restrict__ q,
+    const T* __restrict__ knew, const T* __restrict__ vnew,
     T* __restrict__ out, float* __restrict__ part_o, float* __restrict__ part_ml,
     const int32_t* __restrict__ tables, const int32_t* __restrict__ lens, int64_t layer_off, int N,
     int Hkv, int Hq, int G, int D, int B, int max_blocks, int max_ctx, int bps, int S_max,
@@ -582,10 +608,13 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(
   const int32_t* trow = tables + (int64_t)i * max_blocks;
   const int BD = B * D;
   const int W = k_chunk(D);
+  // APPEND: the item holding position len-1 writes the step's new token there
+  // and uses it from the inputs (the pool's copy may not be visible yet).
+  const int new_pos = (APPEND && len > 0 && (len - 1) / B >= b0 && (len - 1) / B < b1) ? len - 1 : -1;
   for (int blk = b0; blk < b1; ++blk) {
     const int p = guard_block(trow[blk], N);
-    const T* kt = kpool + layer_off + ((int64_t)p * Hkv + g) * BD;
-    const T* vt = vpool + layer_off + ((int64_t)p * Hkv + g) * BD;
+    T* kt = kpool + layer_off + ((int64_t)p * Hkv + g) * BD;
+    T* vt = vpool + layer_off + ((int64_t)p * Hkv + g) * BD;
     const int valid = min(B, len - blk * B);
     __syncthreads();
     for (int idx = lane; idx < BD; idx += 64) {
@@ -594,6 +623,19 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(
       const int o = rem / W, jj = rem - o * W;
       Ks[o * D + jc * W + jj] = to_f32<T>(kt[idx]);
       Vs[idx] = to_f32<T>(vt[idx]);
+    }
+    if (APPEND && new_pos >= 0 && new_pos / B == blk) {
+      const int o = new_pos % B;
+      const T* kr = knew + ((int64_t)i * Hkv + g) * D;
+      const T* vr = vnew + ((int64_t)i * Hkv + g) * D;
+      __syncthreads();
+      for (int j = lane; j < D; j += 64) {
+        const T kv = kr[j], vv = vr[j];
+        kt[(j / W) * B * W + o * W + (j % W)] = kv;
+        vt[j * B + o] = vv;
+        Ks[o * D + j] = to_f32<T>(kv);
+        Vs[j * B + o] = to_f32<T>(vv);
+      }
     }
     __syncthreads();
     for (int idx = lane; idx < G * B; idx += 64) {
@@ -930,12 +972,15 @@ size_t pa_decode_workspace_bytes(const pa_geom* g, int32_t n_seqs, int32_t n_q_h
   return plan.ws;
 }
 
-pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, int32_t layer,
-                    const void* q, void* out, int32_t n_seqs, int32_t n_q_heads,
-                    const int32_t* block_tables, int32_t max_blocks_per_seq,
-                    const int32_t* context_lens, int32_t max_context_len, float scale,
-                    const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+// pa_decode and pa_decode_append share this: knew/vnew are null for a plain decode.
+static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer,
+                             const void* q, const void* knew, const void* vnew, void* out,
+                             int32_t n_seqs, int32_t n_q_heads, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             int32_t max_context_len, float scale, const pa_decode_opts* opts,
+                             void* workspace, size_t workspace_bytes, void* stream) {
   DecodePlan plan;
   pa_status st0 = make_plan(g, n_seqs, n_q_heads, max_context_len, opts, &plan);
   if (st0 != PA_OK) return st0;
@@ -944,6 +989,8 @@ pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, in
   if ((int64_t)max_blocks_per_seq * B < max_context_len) return PA_ERR_INVALID_ARG;
   if (n_seqs == 0) return PA_OK;
   if (!k_pool || !v_pool || !q || !out || !block_tables || !context_lens) return PA_ERR_INVALID_ARG;
+  const bool append = knew != nullptr;
+  if (append != (vnew != nullptr)) return PA_ERR_INVALID_ARG;
   if (!plan.direct && (!workspace || workspace_bytes < plan.ws)) return PA_ERR_WORKSPACE;
   const int64_t items = (int64_t)n_seqs * Hkv * plan.S_max;
   if (items > INT32_MAX) return PA_ERR_UNSUPPORTED;
@@ -958,12 +1005,18 @@ pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, in
     ProfScope ps("decode_partial", st);
     const dim3 grid((unsigned)items), block(64);
     if (plan.kernel == 2) {
-#define PA_MFMA_LAUNCH_NT(DD, DIR, NTV)                                                           \
-  hipLaunchKernelGGL((decode_mfma_bf16_kernel<DD, DIR, NTV>), grid, block, 0, st,                 \
-                     (const uint16_t*)k_pool, (const uint16_t*)v_pool, (const uint16_t*)q,         \
-                     (uint16_t*)out, part_o, part_ml, block_tables, context_lens, layer_off,       \
-                     g->num_blocks, Hkv, n_q_heads, G, max_blocks_per_seq, max_context_len,        \
-                     plan.bps, plan.S_max, qk_scale)
+#define PA_MFMA_LAUNCH_X(DD, DIR, NTV, APP)                                                       \
+  hipLaunchKernelGGL((decode_mfma_bf16_kernel<DD, DIR, NTV, APP>), grid, block, 0, st,            \
+                     (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)q,                     \
+                     (const uint16_t*)knew, (const uint16_t*)vnew, (uint16_t*)out, part_o,         \
+                     part_ml, block_tables, context_lens, layer_off, g->num_blocks, Hkv,          \
+                     n_q_heads, G, max_blocks_per_seq, max_context_len, plan.bps, plan.S_max,      \
+                     qk_scale)
+#define PA_MFMA_LAUNCH_NT(DD, DIR, NTV)                     \
+  do {                                                      \
+    if (append) PA_MFMA_LAUNCH_X(DD, DIR, NTV, true);       \
+    else PA_MFMA_LAUNCH_X(DD, DIR, NTV, false);             \
+  } while (0)
 #define PA_MFMA_LAUNCH(DD, DIR)                                          \
   do {                                                                   \
     if (plan.stream_kv) PA_MFMA_LAUNCH_NT(DD, DIR, true);                \
@@ -978,13 +1031,20 @@ pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, in
       }
 #undef PA_MFMA_LAUNCH
 #undef PA_MFMA_LAUNCH_NT
+#undef PA_MFMA_LAUNCH_X
     } else {
       const size_t lds = generic_lds_bytes(G, D, B);
-#define PA_GEN_LAUNCH_R(T, DIR, RR)                                                               \
-  hipLaunchKernelGGL((decode_generic_kernel<T, DIR, RR>), grid, block, lds, st, (const T*)k_pool, \
-                     (const T*)v_pool, (const T*)q, (T*)out, part_o, part_ml, block_tables,        \
-                     context_lens, layer_off, g->num_blocks, Hkv, n_q_heads, G, D, B,              \
-                     max_blocks_per_seq, max_context_len, plan.bps, plan.S_max, qk_scale)
+#define PA_GEN_LAUNCH_X(T, DIR, RR, APP)                                                          \
+  hipLaunchKernelGGL((decode_generic_kernel<T, DIR, RR, APP>), grid, block, lds, st, (T*)k_pool,  \
+                     (T*)v_pool, (const T*)q, (const T*)knew, (const T*)vnew, (T*)out, part_o,     \
+                     part_ml, block_tables, context_lens, layer_off, g->num_blocks, Hkv,          \
+                     n_q_heads, G, D, B, max_blocks_per_seq, max_context_len, plan.bps,            \
+                     plan.S_max, qk_scale)
+#define PA_GEN_LAUNCH_R(T, DIR, RR)                      \
+  do {                                                   \
+    if (append) PA_GEN_LAUNCH_X(T, DIR, RR, true);       \
+    else PA_GEN_LAUNCH_X(T, DIR, RR, false);             \
+  } while (0)
 #define PA_GEN_LAUNCH(T, DIR)                         \
   do {                                                \
     const int need = (G * D + 63) / 64;               \
@@ -998,6 +1058,7 @@ pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, in
       } else {
         if (plan.direct) PA_GEN_LAUNCH(uint16_t, true); else PA_GEN_LAUNCH(uint16_t, false);
       }
+#undef PA_GEN_LAUNCH_X
 #undef PA_GEN_LAUNCH_R
 #undef PA_GEN_LAUNCH
     }
@@ -1017,6 +1078,31 @@ pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, in
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;
+}
+
+extern "C" {
+
+pa_status pa_decode(const pa_geom* g, const void* k_pool, const void* v_pool, int32_t layer,
+                    const void* q, void* out, int32_t n_seqs, int32_t n_q_heads,
+                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                    const int32_t* context_lens, int32_t max_context_len, float scale,
+                    const pa_decode_opts* opts, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return decode_impl(g, const_cast<void*>(k_pool), const_cast<void*>(v_pool), layer, q, nullptr,
+                     nullptr, out, n_seqs, n_q_heads, block_tables, max_blocks_per_seq, context_lens,
+                     max_context_len, scale, opts, workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer,
+                           const void* q, const void* k_new, const void* v_new, void* out,
+                           int32_t n_seqs, int32_t n_q_heads, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           int32_t max_context_len, float scale, const pa_decode_opts* opts,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_seqs > 0 && (!k_new || !v_new)) return PA_ERR_INVALID_ARG;
+  return decode_impl(g, k_pool, v_pool, layer, q, k_new, v_new, out, n_seqs, n_q_heads,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, opts,
+                     workspace, workspace_bytes, stream);
 }
 
 static pa_status block_move(int mode, const char* name, const pa_geom* g, void* k_pool,

@@ -6,7 +6,8 @@ the order the pages give, on one stream:
 * decode_step    -- per layer: write the batch's new K/V into their slots, then
                     decode every sequence through its block table ("KV Cache
                     Management", "The PagedAttention virtual memory model";
-                    "PagedAttention", "The real cache").
+                    "PagedAttention", "The real cache"); by default both in
+                    one fused launch.
 * cow_copy       -- the block copies copy-on-write asks for before a write into a
                     shared block ("Zero-copy deliberation via copy-on-write
                     branching").
@@ -31,22 +32,33 @@ from .api import Geometry
 def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slots, tables, lens,
                 max_context_len: int, out_all, workspace, layers: Optional[Sequence[int]] = None,
                 blocks_per_split: int = 0, kernel: str = "auto", stream=None,
-                around_decode: Optional[Callable[[int, bool], None]] = None, kv_reuse: bool = False):
+                around_decode: Optional[Callable[[int, bool], None]] = None, kv_reuse: bool = False,
+                fused: bool = True):
     """One decode step: for each layer, append the new tokens, then decode.
 
     q_all [L, n, H_q, d]; k_new_all / v_new_all [L, n_tok, H_kv, d]; slots int64
     [n_tok]; tables int32 [n, max_blocks]; lens int32 [n]; out_all [L, n, H_q, d].
+    fused=True (one new token per sequence, at position lens[i] - 1 of its table,
+    n_tok == n) does both in one launch per layer and ignores `slots`;
+    fused=False issues the slot-mapped append and the decode separately.
     around_decode(layer, before) is called just before and after each layer's
     decode call (host side, e.g. to switch per-kernel timing on and off).
     """
     for layer in (range(geom.num_layers) if layers is None else layers):
-        api.append_kv(geom, k_pool, v_pool, layer, k_new_all[layer], v_new_all[layer], slots,
-                      stream=stream)
+        if not fused:
+            api.append_kv(geom, k_pool, v_pool, layer, k_new_all[layer], v_new_all[layer], slots,
+                          stream=stream)
         if around_decode is not None:
             around_decode(layer, True)
-        api.decode(geom, k_pool, v_pool, layer, q_all[layer], out_all[layer], tables, lens,
-                   max_context_len, workspace=workspace, blocks_per_split=blocks_per_split,
-                   kernel=kernel, stream=stream, kv_reuse=kv_reuse)
+        if fused:
+            api.decode_append(geom, k_pool, v_pool, layer, q_all[layer], k_new_all[layer],
+                              v_new_all[layer], out_all[layer], tables, lens, max_context_len,
+                              workspace=workspace, blocks_per_split=blocks_per_split,
+                              kernel=kernel, stream=stream, kv_reuse=kv_reuse)
+        else:
+            api.decode(geom, k_pool, v_pool, layer, q_all[layer], out_all[layer], tables, lens,
+                       max_context_len, workspace=workspace, blocks_per_split=blocks_per_split,
+                       kernel=kernel, stream=stream, kv_reuse=kv_reuse)
         if around_decode is not None:
             around_decode(layer, False)
 
