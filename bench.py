@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--parity-samples", type=int, default=4)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--unfused", action="store_true",
                     help="append the step's tokens with a separate launch before each decode")
     ap.add_argument("--offload-fraction", type=float, default=1.0,
@@ -122,6 +124,49 @@ class Timer:
         return False
 
 
+class StepTimes:
+    """hipEvents between consecutive steps on one stream: per-step median, min, max."""
+
+    def __init__(self, torch, stream, n):
+        self.stream = stream
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        self.i = 0
+
+    def mark(self):
+        self.ev[self.i].record(self.stream)
+        self.i += 1
+
+    def summary(self):
+        ms = sorted(self.ev[k].elapsed_time(self.ev[k + 1]) for k in range(self.i - 1))
+        if not ms:
+            return None
+        return {"median": round(ms[len(ms) // 2], 4), "min": round(ms[0], 4), "max": round(ms[-1], 4)}
+
+
+def make_runner(torch, stream, step, use_graph):
+    """Returns a callable running one step: `step` itself, or the replay of a
+    HIP graph holding one captured step (captured after the eager warm-up)."""
+    if not use_graph:
+        return step
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    log("captured one step in a HIP graph")
+    return g.replay
+
+
+def timed_steps(torch, stream, run, steps):
+    st = StepTimes(torch, stream, steps)
+    with Timer(torch, stream) as t:
+        for _ in range(steps):
+            st.mark()
+            run()
+        st.mark()
+    return t, st.summary()
+
+
 def setup(args):
     import torch
     import paged_kv_cache_83_amd as pk
@@ -129,7 +174,10 @@ def setup(args):
     cfg = get_config(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
+    # one ordinary (default-priority) stream for all work: graph capture needs a
+    # stream other than the legacy default one
+    stream = torch.cuda.Stream(dev)
+    torch.cuda.set_stream(stream)
     geom = pk.Geometry(cfg.num_layers, cfg.num_kv_heads, cfg.head_dim, cfg.block_size,
                        cfg.num_blocks, cfg.dtype)
     log(f"config={cfg.name} L={cfg.num_layers} n={cfg.num_seqs} Hq={cfg.num_q_heads} "
@@ -210,16 +258,17 @@ def run_decode(args):
         step()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps)")
+    run = make_runner(torch, stream, step, args.graph)
+    if args.graph:
+        run()
 
-    if not args.no_prof:
+    if not args.no_prof and not args.graph:
         pk.Profiler.reset()
         profiling[0] = True
-    with Timer(torch, stream) as t:
-        for _ in range(args.steps):
-            step()
+    t, step_ms = timed_steps(torch, stream, run, args.steps)
     profiling[0] = False
     ms_per_step = max(t.ms, t.wall_ms) / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step {step_ms}")
 
     cold = None
     if args.cold:
@@ -228,7 +277,7 @@ def run_decode(args):
         for _ in range(args.steps):
             flush.add_(1.0)
             with Timer(torch, stream) as tc:
-                step()
+                run()
             tot += tc.ms
         cold = tot / args.steps
         log(f"cold (1 GiB written before each step): {cold:.3f} ms/step")
@@ -238,7 +287,7 @@ def run_decode(args):
 
     # ---- roofline of the dominant kernel (decode partial), timed live ----------
     roofline, kernel_ms = None, {}
-    if not args.no_prof:
+    if not args.no_prof and not args.graph:
         for name in ("decode_partial", "decode_combine"):
             cnt, tot = pk.Profiler.read(name)
             if cnt:
@@ -338,7 +387,9 @@ def run_decode(args):
                    "head_dim": d, "block_size": B, "num_seqs": n, "context_len": int(lengths.max()),
                    "pool_blocks": cfg.num_blocks, "kv_bytes_per_step": kv_bytes_step,
                    "global_batch": n, "seq_len": int(lengths.max()), "parallelism": "none (1 GPU)",
-                   "append": "separate launch" if args.unfused else "fused into decode"},
+                   "append": "separate launch" if args.unfused else "fused into decode",
+                   "launch": "hip graph replay" if args.graph else "eager"},
+        "step_ms": step_ms,
         "tokens_per_s": round(n / (ms_per_step * 1e-3), 2),
         "pct_hbm_peak": round(100 * value / PEAK_GBS, 2),
         "roofline": roofline,
@@ -403,11 +454,12 @@ def run_fork(args):
 
     for _ in range(args.warmup):
         step()
+    run = make_runner(torch, stream, step, args.graph)
+    if args.graph:
+        run()
     pk.Profiler.reset()
-    pk.Profiler.enable(True)
-    with Timer(torch, stream) as t:
-        for _ in range(args.steps):
-            step()
+    pk.Profiler.enable(not args.graph)
+    t, step_ms = timed_steps(torch, stream, run, args.steps)
     pk.Profiler.enable(False)
     ms = max(t.ms, t.wall_ms) / args.steps
     m_token = pk.bytes_per_token(L, Hkv, d, geom.elem_bytes)
@@ -419,7 +471,7 @@ def run_fork(args):
         if cnt:
             kern[name] = {"launches": cnt, "avg_us": round(1e3 * tot / cnt, 2)}
     blk = pk.bytes_per_block(geom)
-    copy_gbs = (2 * n * blk) / (kern["copy_blocks"]["avg_us"] * 1e-6) / 1e9
+    copy_gbs = (2 * n * blk) / (kern["copy_blocks"]["avg_us"] * 1e-6) / 1e9 if kern else None
     result = {
         "metric": "fork/copy-on-write step: decode tokens/s and logical KV GB/s, fork_cow",
         "value": round(n / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -429,7 +481,9 @@ def run_fork(args):
                    "suffix_tokens": int(suffix.sum()), "cow_pairs": len(pairs), "num_layers": L},
         "logical_kv_GBps": round(logical / (ms * 1e-3) / 1e9, 1),
         "unique_kv_GBps": round(unique / (ms * 1e-3) / 1e9, 1),
-        "copy_blocks_GBps_rw": round(copy_gbs, 1),
+        "copy_blocks_GBps_rw": round(copy_gbs, 1) if copy_gbs else None,
+        "step_ms": step_ms,
+        "launch": "hip graph replay" if args.graph else "eager",
         "kernels": kern,
     }
     print(json.dumps(result), flush=True)

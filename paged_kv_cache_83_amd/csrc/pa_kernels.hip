@@ -254,10 +254,17 @@ __global__ __launch_bounds__(256) void block_move_kernel(char* __restrict__ kpoo
 // =============================================================================
 constexpr int kMfmaMaxBps = 256;  // table entries of one split, held 64 per register
 
+#ifndef PA_MFMA_STAGES
+#define PA_MFMA_STAGES 2
+#endif
+#ifndef PA_MFMA_WPE
+#define PA_MFMA_WPE 2
+#endif
 template <int D>
 struct MfmaCfg {
   static constexpr int KC = D / 32;  // QK k-steps
   static constexpr int DT = D / 16;  // PV row tiles
+  static constexpr int kStages = PA_MFMA_STAGES;  // pairs of blocks in flight per wave
 };
 
 template <int D>
@@ -303,22 +310,21 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// Block id at offset `off` (wave-uniform, < 256) of the split's table chunk.
+// Block id at offset `off` (wave-uniform, < 256) of the split's table chunk:
+// register off / 64 of lane off % 64, picked without branches.
 __device__ __forceinline__ int table_at(const int (&tb)[4], int off) {
-  const int l = off & 63;
-  switch (off >> 6) {
-    case 0: return __builtin_amdgcn_readlane(tb[0], l);
-    case 1: return __builtin_amdgcn_readlane(tb[1], l);
-    case 2: return __builtin_amdgcn_readlane(tb[2], l);
-    default: return __builtin_amdgcn_readlane(tb[3], l);
-  }
+  const int r = off >> 6;
+  const int v = r == 0 ? tb[0] : r == 1 ? tb[1] : r == 2 ? tb[2] : tb[3];
+  return __builtin_amdgcn_readlane(v, off & 63);
 }
 
+// new_key: pair-local index (0..31) of the token appended in this launch, whose
+// K row is taken from knew_row (its pool slot may not hold it yet), or -1.
 template <int D, bool NT>
 __device__ __forceinline__ void issue_pair(PairFrags<D>& f, const uint16_t* __restrict__ kl,
                                            const uint16_t* __restrict__ vl, int p0, int p1, int Hkv,
                                            int g, int k_sel, int k_off0, int v_sel, int v_off,
-                                           int gq) {
+                                           int gq, int new_key, const uint16_t* knew_row) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int DT = MfmaCfg<D>::DT;
   constexpr int TILE = 16 * D;
@@ -329,18 +335,42 @@ __device__ __forceinline__ void issue_pair(PairFrags<D>& f, const uint16_t* __re
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
       f.k[t][kc] = kv_load16<NT>(krow + kc * 512 + (k_off0 + 4 * t) * 32 + 8 * gq);
+    if (16 * k_sel + k_off0 + 4 * t == new_key) {  // lane-divergent: plain loads
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        f.k[t][kc] = *reinterpret_cast<const u32x4*>(knew_row + 32 * kc + 8 * gq);
+    }
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) f.v[dt] = kv_load16<NT>(vrow + dt * 256 + v_off);
 }
 
+// new_pos: position of the token appended in this launch, or -1. Its V is
+// substituted into the lane's V^T fragments from vnew (dims 16*dt + c: low half
+// of vnew[dt/2] for even dt, high half for odd dt).
 template <int D>
 __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)[MfmaCfg<D>::KC],
                                              f32x4 (&acc)[MfmaCfg<D>::DT], float& m_run,
                                              float& l_run, int blk, int len, int gq,
-                                             float qk_scale) {
+                                             float qk_scale, int new_pos,
+                                             const uint32_t (&vnew)[MfmaCfg<D>::DT / 2]) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int DT = MfmaCfg<D>::DT;
+  if (new_pos >= blk * 16 && new_pos < blk * 16 + 32) {  // wave-uniform
+    const int e = new_pos - blk * 16 - 8 * gq;            // the lane holds pair-local keys 8*gq .. +8
+    if (e >= 0 && e < 8) {
+      const int word = e >> 1;
+      const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint32_t nv = (dt & 1) ? (vnew[dt >> 1] >> 16) : (vnew[dt >> 1] & 0xffffu);
+        const uint32_t ins = (e & 1) ? (nv << 16) : nv;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv)
+          f.v[dt][wv] = (wv == word) ? ((f.v[dt][wv] & keep) | ins) : f.v[dt][wv];
+      }
+    }
+  }
   f32x4 sc[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -405,7 +435,7 @@ __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)
 // knew/vnew [n][H_kv][d]; the work item holding that position writes it into the
 // pool and uses it from registers (K by address, V by element) while attending.
 template <int D, bool DIRECT, bool NT, bool APPEND>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : 2))) void decode_mfma_bf16_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : PA_MFMA_WPE))) void decode_mfma_bf16_kernel(
     uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ out, float* __restrict__ part_o,
@@ -473,16 +503,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
   const uint16_t* kl = kpool + layer_off;
   const uint16_t* vl = vpool + layer_off;
 
-  // The appended token is written into the pool by the item whose split holds
-  // its block, before that item reads the block: the whole work group is this
-  // one wave, so a work-group fence after the stores makes them visible to the
-  // loads of every lane below.
+  // The appended token: the item whose split holds its block writes it into the
+  // pool and, without waiting for those stores, uses it from the inputs (K row
+  // by address, V by element) wherever the pair loads would return its slot.
+  int new_pos = -1;
+  const uint16_t* knew_row = knew;
+  uint32_t vnw[DT / 2];
+#pragma unroll
+  for (int k = 0; k < DT / 2; ++k) vnw[k] = 0;
   if (APPEND && len > 0 && ((len - 1) >> 4) >= b0 && ((len - 1) >> 4) < b1) {
-    const int pos = len - 1;
-    const uint16_t* knew_row = knew + ((int64_t)i * Hkv + g) * D;
+    new_pos = len - 1;
+    knew_row = knew + ((int64_t)i * Hkv + g) * D;
     const uint16_t* vnew_row = vnew + ((int64_t)i * Hkv + g) * D;
-    const int pn = guard_block(trow[pos >> 4], N);
-    const int on = pos & 15;
+    const int pn = guard_block(trow[new_pos >> 4], N);
+    const int on = new_pos & 15;
     uint16_t* kt = kpool + layer_off + ((int64_t)pn * Hkv + g) * (16 * D);
     uint16_t* vt = vpool + layer_off + ((int64_t)pn * Hkv + g) * (16 * D);
     if (lane < D / 8) {  // K row: lane moves dims 8*lane .. +8 (a 32-dim chunk takes 4 lanes)
@@ -490,7 +524,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
       *reinterpret_cast<u32x4*>(kt + (lane >> 2) * 512 + on * 32 + 8 * (lane & 3)) = kv8;
     }
     for (int d = lane; d < D; d += 64) vt[d * 16 + on] = vnew_row[d];  // V column
-    __threadfence_block();
+#pragma unroll
+    for (int k = 0; k < DT / 2; ++k)
+      vnw[k] = (uint32_t)vnew_row[32 * k + c] | ((uint32_t)vnew_row[32 * k + 16 + c] << 16);
   }
 
   // Row r = c of each score tile holds pair-local key 8*(c>>2) + 4*t + (c&3):
@@ -509,23 +545,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
     p1 = (off + 1 < span) ? table_at(tb, off + 1) : p0;
   };
 
-  PairFrags<D> fa, fb;
-  int p0, p1;
-  ids(0, p0, p1);
-  issue_pair<D, NT>(fa, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
-  for (int pj = 0;;) {
-    if (pj + 1 < npairs) {
-      ids(pj + 1, p0, p1);
-      issue_pair<D, NT>(fb, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
+  // NS pairs in flight: the loads of pair pj + NS - 1 are issued just before
+  // pair pj is computed, into the buffer pair pj - 1 has released. The steady
+  // loop issues unconditionally, so the wait before each compute covers only
+  // the older pair (a conditional issue would make the compiler wait for all
+  // outstanding loads, draining the pipeline every iteration); the last pairs
+  // are drained by an unrolled tail.
+  constexpr int NS = MfmaCfg<D>::kStages;
+  PairFrags<D> f[NS];
+  auto issue_at = [&](PairFrags<D>& fr, int pj) {
+    int p0, p1;
+    ids(pj, p0, p1);
+    issue_pair<D, NT>(fr, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq,
+                      new_pos >= 0 ? new_pos - 16 * (b0 + 2 * pj) : -1, knew_row);
+  };
+  int pj = 0;
+  if (npairs >= 2 * NS - 1) {
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) issue_at(f[st], st);
+    for (; pj + 2 * NS - 1 <= npairs; pj += NS) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        issue_at(f[(st + NS - 1) % NS], pj + st + NS - 1);
+        compute_pair<D>(f[st], qf, acc, m_run, l_run, b0 + 2 * (pj + st), len, gq, qk_scale,
+                        new_pos, vnw);
+      }
     }
-    compute_pair<D>(fa, qf, acc, m_run, l_run, b0 + 2 * pj, len, gq, qk_scale);
-    if (++pj >= npairs) break;
-    if (pj + 1 < npairs) {
-      ids(pj + 1, p0, p1);
-      issue_pair<D, NT>(fa, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq);
-    }
-    compute_pair<D>(fb, qf, acc, m_run, l_run, b0 + 2 * pj, len, gq, qk_scale);
-    if (++pj >= npairs) break;
+  } else {
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < npairs) issue_at(f[st], st);
+  }
+  // npairs - pj pairs remain (at most 2*NS - 2); pairs pj .. pj+NS-2 are in flight.
+#pragma unroll
+  for (int k = 0; k < 2 * NS - 2; ++k) {
+    if (pj + k >= npairs) break;
+    if (pj + k + NS - 1 < npairs) issue_at(f[(k + NS - 1) % NS], pj + k + NS - 1);
+    compute_pair<D>(f[k % NS], qf, acc, m_run, l_run, b0 + 2 * (pj + k), len, gq, qk_scale, new_pos,
+                    vnw);
   }
 
   l_run = sum_over_groups(l_run);

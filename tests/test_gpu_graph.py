@@ -1,0 +1,75 @@
+"""A whole decode step (every layer's fused append + decode, and the combine
+launches of split plans) captured in a HIP graph and replayed must give the
+same bits as the eager launches, on every replay.
+
+Between replays the program does its own eager work on the same stream (an
+eager decode into another buffer, a NaN refill of the graph's output) and
+synchronises, so a replay that skipped a node or reused stale memory would
+show up as a mismatch."""
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_83_amd as pk
+from paged_kv_cache_83_amd import steps
+from tests.gpu_helpers import make_batch, need_gpu, padded_tables, print_case, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, dtype, L, N, Hq, Hkv, d, B, lengths, bps, kernel
+    ("mfma_direct", "bf16", 3, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 0, "auto"),
+    ("mfma_split", "bf16", 2, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 4, "mfma"),
+    ("generic_f32_split", "f32", 2, 300, 12, 12, 64, 16, [5, 250, 900, 33], 2, "generic"),
+]
+
+
+def _bits(t):
+    return t.contiguous().view(torch.uint8).cpu().numpy()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_graph_replay_matches_eager(case):
+    need_gpu()
+    name, dtype, L, N, Hq, Hkv, d, B, lengths, bps, kernel = case
+    print_case(test="graph_replay", case=name)
+    batch = make_batch(dtype, L, N, Hq, Hkv, d, B, lengths, seed=71, poison=False)
+    geom = pk.Geometry(L, Hkv, d, B, N, dtype)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        K, V = to_dev(batch.k_pool, dtype), to_dev(batch.v_pool, dtype)
+        n = len(lengths)
+        q_all = torch.stack([to_dev(batch.q, dtype)] * L)
+        kn = torch.stack([to_dev(batch.k_new, dtype)] * L)
+        vn = torch.stack([to_dev(batch.v_new, dtype)] * L)
+        tabs = torch.from_numpy(padded_tables(batch.tables, batch.max_blocks)).cuda()
+        lens = torch.from_numpy(np.asarray(lengths, np.int32)).cuda()
+        max_ctx = max(lengths)
+        ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, bps, kernel)),
+                         dtype=torch.uint8, device="cuda")
+        out_eager = torch.empty_like(q_all)
+        out_graph = torch.full_like(q_all, float("nan"))
+        other = torch.empty_like(q_all)
+
+    def step(out):
+        steps.decode_step(geom, K, V, q_all, kn, vn, None, tabs, lens, max_ctx, out, ws,
+                          blocks_per_split=bps, kernel=kernel, stream=s)
+
+    step(out_eager)
+    torch.cuda.synchronize()
+    ref, k_ref, v_ref = _bits(out_eager), _bits(K), _bits(V)
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step(out_graph)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        with torch.cuda.stream(s):
+            out_graph.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(out_graph), ref), (name, rep)
+        assert np.array_equal(_bits(K), k_ref) and np.array_equal(_bits(V), v_ref), (name, rep)
+        step(other)                      # eager work between replays, same workspace
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(other), ref), (name, rep)
