@@ -120,18 +120,20 @@ __device__ __forceinline__ void store_vec(T* dst, const T (&src)[VEC]) {
   }
 }
 
-// Tokens first .. first+VEC-1 exist and occupy VEC consecutive slots starting at a
-// VEC-aligned slot of one block.
-template <int VEC>
-__device__ __forceinline__ bool aligned_run(const int64_t* __restrict__ slots, int64_t first,
-                                            int n_tok, int B, int64_t nslots) {
-  if (first < 0 || first + VEC > n_tok || (B % VEC) != 0) return false;
-  const int64_t s0 = slots[first];
-  if (s0 < 0 || s0 + VEC > nslots || (s0 % VEC) != 0) return false;
-#pragma unroll
-  for (int e = 1; e < VEC; ++e)
-    if (slots[first + e] != s0 + e) return false;
-  return true;
+// One work group per (16 consecutive tokens, KV head). The chunk's K and V rows
+// are read with 16-byte loads into LDS while the slots load (the source addresses
+// do not depend on them); then each K piece goes to its place in the K tile, and
+// V, whose tile keeps one row of B slots per dimension, is written from its
+// transposed LDS copy with the lanes along the slots: tokens in consecutive
+// slots of one block give contiguous stores. Every token carries its own
+// destination, so any slot mapping is handled.
+constexpr int kAppendChunk = 16;
+constexpr int kXcds = 8;  // accelerator complex dies of the part, which take work groups in turn
+
+template <typename T>
+constexpr size_t append_lds_bytes(int D) {
+  return kAppendChunk * sizeof(int64_t) + (size_t)kAppendChunk * D * sizeof(T) +
+         (size_t)D * (kAppendChunk + 1) * sizeof(T);
 }
 
 template <typename T, int VEC>
@@ -141,45 +143,63 @@ __global__ __launch_bounds__(256) void append_kv_kernel(T* __restrict__ kpool, T
                                                         const int64_t* __restrict__ slots, int n_tok,
                                                         int Hkv, int D, int B, int64_t nslots,
                                                         int64_t layer_off) {
-  const int chunks = D / VEC;
-  const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (tid >= (int64_t)n_tok * Hkv * chunks) return;
-  const int c = (int)(tid % chunks);
-  const int64_t th = tid / chunks;
-  const int h = (int)(th % Hkv);
-  const int64_t j = th / Hkv;
-  const int64_t slot = slots[j];
-  if (slot < 0 || slot >= nslots) return;
-  const int64_t p = slot / B;
-  const int o = (int)(slot % B);
-  const int d0 = c * VEC;  // VEC divides the K chunk width, so a run stays in one chunk
-  const int W = k_chunk(D);
-  const int64_t tile = layer_off + (p * Hkv + h) * (int64_t)B * D;
-
-  T kv[VEC];
-  load_vec<T, VEC>(kv, knew + (j * Hkv + h) * D + d0);
-  store_vec<T, VEC>(kpool + tile + (int64_t)(d0 / W) * B * W + (int64_t)o * W + (d0 % W), kv);
-
-  T* vd = vpool + tile + (int64_t)d0 * B;
-  const int lead = o % VEC;  // position of this token inside its aligned slot run
-  if (aligned_run<VEC>(slots, j - lead, n_tok, B, nslots)) {
-    if (lead != 0) return;  // the run's first token writes the whole run
-    T vv[VEC][VEC];         // [token][dim]
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) load_vec<T, VEC>(vv[e], vnew + ((j + e) * Hkv + h) * D + d0);
-#pragma unroll
-    for (int u = 0; u < VEC; ++u) {
-      T row[VEC];
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) row[e] = vv[e][u];
-      store_vec<T, VEC>(vd + (int64_t)u * B + o, row);
+  extern __shared__ __align__(16) unsigned char append_smem[];
+  constexpr int LD = kAppendChunk + 1;  // padded row of the transposed V chunk
+  int64_t* s_slot = reinterpret_cast<int64_t*>(append_smem);
+  T* s_k = reinterpret_cast<T*>(append_smem + kAppendChunk * sizeof(int64_t));  // [token][D]
+  T* s_v = s_k + kAppendChunk * D;                                                // [D][LD]
+  // Work groups go to the 8 XCDs round-robin; give each XCD a contiguous range of
+  // (head, chunk) items so that neighbouring chunks, which share the V rows of a
+  // block they straddle, are written through the same L2 one after the other.
+  const int64_t nchunks = ((int64_t)n_tok + kAppendChunk - 1) / kAppendChunk;
+  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
+  const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (item >= nchunks * Hkv) return;
+  const int h = (int)(item / nchunks);
+  const int64_t j0 = (item - (int64_t)h * nchunks) * kAppendChunk;
+  const int tid = threadIdx.x;
+  const int nk = (int)min<int64_t>(kAppendChunk, n_tok - j0);  // tokens in this chunk
+  if (tid < kAppendChunk) {
+    int64_t sl = -1;
+    if (tid < nk) {
+      sl = slots[j0 + tid];
+      if (sl < 0 || sl >= nslots) sl = -1;  // negative: skip; out of range: ignored
     }
-    return;
+    s_slot[tid] = sl;
   }
-  T vv[VEC];
-  load_vec<T, VEC>(vv, vnew + (j * Hkv + h) * D + d0);
+  const int pieces = D / VEC;
+  for (int idx = tid; idx < nk * pieces; idx += blockDim.x) {
+    const int k = idx / pieces, d0 = (idx - k * pieces) * VEC;
+    const int64_t row = ((j0 + k) * Hkv + h) * D + d0;
+    T kv[VEC], vv[VEC];
+    load_vec<T, VEC>(kv, knew + row);
+    load_vec<T, VEC>(vv, vnew + row);
+    store_vec<T, VEC>(s_k + k * D + d0, kv);
 #pragma unroll
-  for (int u = 0; u < VEC; ++u) vd[(int64_t)u * B + o] = vv[u];
+    for (int u = 0; u < VEC; ++u) s_v[(d0 + u) * LD + k] = vv[u];
+  }
+  __syncthreads();
+  const int W = k_chunk(D);  // VEC divides W: a piece stays in one K chunk
+  for (int idx = tid; idx < nk * pieces; idx += blockDim.x) {
+    const int k = idx / pieces, d0 = (idx - k * pieces) * VEC;
+    const int64_t sl = s_slot[k];
+    if (sl < 0) continue;
+    const int64_t p = sl / B;
+    const int o = (int)(sl - p * B);
+    T kv[VEC];
+    load_vec<T, VEC>(kv, s_k + k * D + d0);
+    store_vec<T, VEC>(kpool + layer_off + (p * Hkv + h) * (int64_t)B * D + (int64_t)(d0 / W) * B * W +
+                          (int64_t)o * W + (d0 % W),
+                      kv);
+  }
+  for (int idx = tid; idx < kAppendChunk * D; idx += blockDim.x) {
+    const int k = idx % kAppendChunk, d = idx / kAppendChunk;
+    const int64_t sl = s_slot[k];
+    if (sl < 0) continue;
+    const int64_t p = sl / B;
+    const int o = (int)(sl - p * B);
+    vpool[layer_off + (p * Hkv + h) * (int64_t)B * D + (int64_t)d * B + o] = s_v[d * LD + k];
+  }
 }
 
 // =============================================================================
@@ -991,31 +1011,29 @@ pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t lay
   const int D = g->head_dim, B = g->block_size, H = g->num_kv_heads;
   const int64_t layer_off = (int64_t)layer * g->num_blocks * H * B * D;
   const int64_t nslots = (int64_t)g->num_blocks * B;
+  const size_t lds = g->dtype == PA_BF16 ? append_lds_bytes<uint16_t>(D) : append_lds_bytes<float>(D);
+  if (lds > 65536) return PA_ERR_UNSUPPORTED;
   ProfScope ps("append", st);
+  const int64_t items = ((int64_t)n_tokens + kAppendChunk - 1) / kAppendChunk * H;
+  const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;  // a multiple of the XCD count
+  if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)wgs);
   if (g->dtype == PA_BF16) {
-    const bool v8 = D % 8 == 0;
-    const int vec = v8 ? 8 : 1;
-    const int64_t total = (int64_t)n_tokens * H * (D / vec);
-    const int64_t blocks = (total + 255) / 256;
-    if (v8)
-      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 8>), dim3((unsigned)blocks), dim3(256), 0, st,
+    if (D % 8 == 0)
+      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 8>), grid, dim3(256), lds, st,
                          (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_new,
                          (const uint16_t*)v_new, slot_mapping, n_tokens, H, D, B, nslots, layer_off);
     else
-      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 1>), dim3((unsigned)blocks), dim3(256), 0, st,
+      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 1>), grid, dim3(256), lds, st,
                          (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_new,
                          (const uint16_t*)v_new, slot_mapping, n_tokens, H, D, B, nslots, layer_off);
   } else {
-    const bool v4 = D % 4 == 0;
-    const int vec = v4 ? 4 : 1;
-    const int64_t total = (int64_t)n_tokens * H * (D / vec);
-    const int64_t blocks = (total + 255) / 256;
-    if (v4)
-      hipLaunchKernelGGL((append_kv_kernel<float, 4>), dim3((unsigned)blocks), dim3(256), 0, st,
+    if (D % 4 == 0)
+      hipLaunchKernelGGL((append_kv_kernel<float, 4>), grid, dim3(256), lds, st,
                          (float*)k_pool, (float*)v_pool, (const float*)k_new, (const float*)v_new,
                          slot_mapping, n_tokens, H, D, B, nslots, layer_off);
     else
-      hipLaunchKernelGGL((append_kv_kernel<float, 1>), dim3((unsigned)blocks), dim3(256), 0, st,
+      hipLaunchKernelGGL((append_kv_kernel<float, 1>), grid, dim3(256), lds, st,
                          (float*)k_pool, (float*)v_pool, (const float*)k_new, (const float*)v_new,
                          slot_mapping, n_tokens, H, D, B, nslots, layer_off);
   }
