@@ -130,3 +130,63 @@ def test_mutant_no_copy_on_write(monkeypatch):
     monkeypatch.setattr(obm.BlockManager, "append", _append_without_cow)
     _raises(TB.test_p3_fork_example)
     _raises(TB.test_figure5, "figure5_cow")
+
+
+# ---------------------------------------------------------------------------
+# Chunked prefill oracle
+import oracle.prefill as opf  # noqa: E402
+from tests import test_oracle_prefill as TP  # noqa: E402
+
+
+def _chunk_attention_off_by_one(q_rows, k_rows, v_rows, K_hist, V_hist, scale):
+    K_all = np.concatenate([K_hist, k_rows], axis=0)
+    V_all = np.concatenate([V_hist, v_rows], axis=0)
+    c = K_hist.shape[0]
+    out = np.zeros(q_rows.shape)
+    for t in range(q_rows.shape[0]):
+        visible = c + t                               # wrong: a token does not see itself
+        out[t] = att.attend(q_rows[t], K_all[:visible], V_all[:visible], scale)
+    return out
+
+
+def _chunk_attention_no_causal(q_rows, k_rows, v_rows, K_hist, V_hist, scale):
+    K_all = np.concatenate([K_hist, k_rows], axis=0)
+    V_all = np.concatenate([V_hist, v_rows], axis=0)
+    return np.stack([att.attend(q_rows[t], K_all, V_all, scale)   # wrong: sees later chunk tokens
+                     for t in range(q_rows.shape[0])])
+
+
+def _chunk_attention_no_history(q_rows, k_rows, v_rows, K_hist, V_hist, scale):
+    return chunk_attention_orig(q_rows, k_rows, v_rows, K_hist[:0], V_hist[:0], scale)
+
+
+def _chunk_slots_relative(tables, q_start, ctx_lens, block_size):
+    return chunk_slots_orig(tables, q_start, [0] * len(ctx_lens), block_size)  # wrong: ignores history
+
+
+chunk_attention_orig = opf.chunk_attention
+chunk_slots_orig = opf.chunk_slots
+
+
+def test_mutant_prefill_causal_off_by_one(monkeypatch):
+    monkeypatch.setattr(opf, "chunk_attention", _chunk_attention_off_by_one)
+    _raises(TP.test_empty_history_is_causal_self_attention, 16)
+    _raises(TP.test_one_token_chunks_equal_decode)
+
+
+def test_mutant_prefill_no_causal_mask(monkeypatch):
+    monkeypatch.setattr(opf, "chunk_attention", _chunk_attention_no_causal)
+    _raises(TP.test_empty_history_is_causal_self_attention, 4)
+    _raises(TP.test_chunked_equals_monolithic, 5)
+
+
+def test_mutant_prefill_history_dropped(monkeypatch):
+    monkeypatch.setattr(opf, "chunk_attention", _chunk_attention_no_history)
+    _raises(TP.test_history_visible_and_chunk_causal)
+    _raises(TP.test_brute_force_tiny)
+
+
+def test_mutant_prefill_slots_relative(monkeypatch):
+    monkeypatch.setattr(opf, "chunk_slots", _chunk_slots_relative)
+    _raises(TP.test_chunk_written_at_table_positions)
+    _raises(TP.test_chunked_equals_monolithic, 16)
