@@ -171,6 +171,33 @@ pa_status pa_decode_append(const pa_geom* g, void* k_pool, void* v_pool, int32_t
                            int32_t max_context_len, float scale, const pa_decode_opts* opts,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Chunked-prefill (multi-query) paged attention, one layer. Source: "KV Cache
+ * Management", section "Chunked prefill mechanics": the queries of a chunk
+ * attend over every cached token of their sequence and, inside the chunk, over
+ * the tokens at or before their own position; the chunk's keys and values are
+ * written into the sequence's paged blocks.
+ * Batch of n_seqs chunks packed by rows: chunk i owns rows q_start[i] ..
+ * q_start[i+1]-1 (q_start: int32 [n_seqs+1] device array, non-decreasing, last
+ * entry n_tokens) of q, out [n_tokens][n_q_heads][d] and k_new, v_new
+ * [n_tokens][H_kv][d] (pool dtype). ctx_lens[i] (int32 device) tokens of sequence
+ * i are already cached; the chunk's row r is position ctx_lens[i] + r - q_start[i].
+ * block_tables row i ([n_seqs][max_blocks_per_seq] int32 device) must already
+ * cover ctx_lens[i] + chunk length tokens (the blocks the chunk is written into
+ * must be owned by sequence i alone). The call first writes each row's K/V at
+ * its position, then out[row][h] = sum over visible positions t of
+ * softmax_t(scale * q . K_t) V_t, KV head h / (n_q_heads / H_kv), visible = 0 ..
+ * the row's own position. max_q_len bounds every chunk length and sizes the
+ * launch; max_context_len bounds ctx_lens[i] + chunk length (values are clamped
+ * to these bounds, never read past them). scale <= 0 means 1/sqrt(d).
+ * Implemented for bf16 pools with B = 16, d in {64, 128} and n_q_heads / H_kv
+ * dividing 32; other geometries return PA_ERR_UNSUPPORTED. */
+pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer, const void* q,
+                     const void* k_new, const void* v_new, void* out, int32_t n_seqs,
+                     int32_t n_tokens, int32_t n_q_heads, const int32_t* q_start,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* ctx_lens, int32_t max_q_len, int32_t max_context_len,
+                     float scale, void* stream);
+
 /* Copy-on-write block copy: for each k, block dst[k] <- block src[k] in every
  * layer, K and V, all B slots. src, dst: int32 [n_pairs] device arrays; no dst
  * may appear as a src or twice. Source: "KV Cache Management", "Zero-copy

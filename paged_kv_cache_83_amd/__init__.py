@@ -11,7 +11,6 @@ from ._lib import (DoubleFreeError, OutOfBlocksError, PagedKVError, LIB_PATH,  #
 from .api import (BlockManager, Geometry, Profiler, alloc_pools, append_kv,  # noqa: F401
                   blocks_for_tokens, bytes_per_block, bytes_per_token, copy_blocks,
                   copy_to_device, copy_to_host, decode, decode_append, decode_workspace_bytes,
-                  gather_blocks,
-                  pool_bytes, scatter_blocks)
+                  gather_blocks, pool_bytes, prefill, scatter_blocks)
 
 _load()

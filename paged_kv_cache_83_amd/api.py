@@ -209,6 +209,36 @@ def decode_append(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, o
           "pa_decode_append")
 
 
+def prefill(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out, q_start, block_tables,
+            ctx_lens, max_q_len: int, max_context_len: int, scale: float = 0.0, stream=None):
+    """Chunked prefill of one layer: chunk i = rows q_start[i]..q_start[i+1]-1 of q
+    [n_tok, H_q, d] / k_new, v_new [n_tok, H_kv, d], at positions ctx_lens[i] + r.
+    Writes the chunks' K/V through block_tables, then attends causally; out gets
+    [n_tok, H_q, d]."""
+    _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
+    _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
+    if q.dim() != 3 or q.shape[2] != geom.head_dim:
+        raise ValueError("q must be [n_tokens, n_q_heads, head_dim]")
+    n_tok, hq = int(q.shape[0]), int(q.shape[1])
+    _dev(q, "q", geom.torch_dtype)
+    _dev(out, "out", geom.torch_dtype, q.numel())
+    per = geom.num_kv_heads * geom.head_dim
+    _dev(k_new, "k_new", geom.torch_dtype, n_tok * per)
+    _dev(v_new, "v_new", geom.torch_dtype, n_tok * per)
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [n_seqs, max_blocks]")
+    n = int(block_tables.shape[0])
+    _dev(block_tables, "block_tables", torch.int32)
+    _dev(q_start, "q_start", torch.int32, n + 1)
+    _dev(ctx_lens, "ctx_lens", torch.int32, n)
+    g = geom.c()
+    check(_L().pa_prefill(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(q), _ptr(k_new),
+                          _ptr(v_new), _ptr(out), n, n_tok, hq, _ptr(q_start), _ptr(block_tables),
+                          int(block_tables.shape[1]), _ptr(ctx_lens), int(max_q_len),
+                          int(max_context_len), float(scale), _stream(stream, q.device)),
+          "pa_prefill")
+
+
 def _ids(t, what, n=None):
     _dev(t, what, torch.int32, n)
 

@@ -33,174 +33,16 @@
 #include <vector>
 
 #include "../../include/pa.h"
+#include "pa_device.h"
+#include "pa_append.h"
 
 namespace {
 
-typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-  return __uint_as_float(static_cast<uint32_t>(h) << 16);
-}
-
-// Round to nearest even; NaN stays a quiet NaN of the same sign.
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x0040u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
-}
-
-template <typename T> __device__ __forceinline__ float to_f32(T v);
-template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
-template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
-
-template <typename T> __device__ __forceinline__ T from_f32(float v);
-template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
-template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float v) { return f32_to_bf16(v); }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
-// Attended length of sequence i, clamped into [0, max_ctx].
-__device__ __forceinline__ int clamp_len(const int32_t* lens, int i, int max_ctx) {
-  int len = lens[i];
-  return len < 0 ? 0 : (len > max_ctx ? max_ctx : len);
-}
-
-__device__ __forceinline__ int guard_block(int p, int N) { return (p >= 0 && p < N) ? p : 0; }
-
-// Width of the K dimension chunks: 32 when it divides d, else the whole d.
-__host__ __device__ __forceinline__ int k_chunk(int D) { return (D % 32 == 0) ? 32 : D; }
+using namespace pa_detail;
 
 // =============================================================================
 // Append: token j's K/V go to slot slot_mapping[j] of one layer.
-// One thread moves VEC consecutive dimensions (16 bytes) of one head of one
-// token. Its K lands as one 16-byte store inside the slot's row. V is
-// dimension-major inside a block, so one token's V is VEC scattered elements;
-// but when VEC tokens fill a VEC-aligned run of consecutive slots of one block
-// (bulk appends, in whatever order the runs of different sequences were
-// concatenated), the thread of the run's first token loads all VEC tokens'
-// values, transposes them in registers and writes each dimension's run as one
-// 16-byte store, and the other tokens of the run skip their V.
 // =============================================================================
-
-// VEC elements of T as one 16-byte access when they make up exactly 16 bytes
-// (the callers guarantee 16-byte alignment then), element by element otherwise.
-template <typename T, int VEC>
-__device__ __forceinline__ void load_vec(T (&dst)[VEC], const T* src) {
-  if constexpr (VEC * sizeof(T) == 16) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(src);
-    __builtin_memcpy(&dst[0], &v, 16);
-  } else {
-#pragma unroll
-    for (int u = 0; u < VEC; ++u) dst[u] = src[u];
-  }
-}
-template <typename T, int VEC>
-__device__ __forceinline__ void store_vec(T* dst, const T (&src)[VEC]) {
-  if constexpr (VEC * sizeof(T) == 16) {
-    u32x4 v;
-    __builtin_memcpy(&v, &src[0], 16);
-    *reinterpret_cast<u32x4*>(dst) = v;
-  } else {
-#pragma unroll
-    for (int u = 0; u < VEC; ++u) dst[u] = src[u];
-  }
-}
-
-// One work group per (16 consecutive tokens, KV head). The chunk's K and V rows
-// are read with 16-byte loads into LDS while the slots load (the source addresses
-// do not depend on them); then each K piece goes to its place in the K tile, and
-// V, whose tile keeps one row of B slots per dimension, is written from its
-// transposed LDS copy with the lanes along the slots: tokens in consecutive
-// slots of one block give contiguous stores. Every token carries its own
-// destination, so any slot mapping is handled.
-constexpr int kAppendChunk = 16;
-constexpr int kXcds = 8;  // accelerator complex dies of the part, which take work groups in turn
-
-template <typename T>
-constexpr size_t append_lds_bytes(int D) {
-  return kAppendChunk * sizeof(int64_t) + (size_t)kAppendChunk * D * sizeof(T) +
-         (size_t)D * (kAppendChunk + 1) * sizeof(T);
-}
-
-template <typename T, int VEC>
-__global__ __launch_bounds__(256) void append_kv_kernel(T* __restrict__ kpool, T* __restrict__ vpool,
-                                                        const T* __restrict__ knew,
-                                                        const T* __restrict__ vnew,
-                                                        const int64_t* __restrict__ slots, int n_tok,
-                                                        int Hkv, int D, int B, int64_t nslots,
-                                                        int64_t layer_off) {
-  extern __shared__ __align__(16) unsigned char append_smem[];
-  constexpr int LD = kAppendChunk + 1;  // padded row of the transposed V chunk
-  int64_t* s_slot = reinterpret_cast<int64_t*>(append_smem);
-  T* s_k = reinterpret_cast<T*>(append_smem + kAppendChunk * sizeof(int64_t));  // [token][D]
-  T* s_v = s_k + kAppendChunk * D;                                                // [D][LD]
-  // Work groups go to the 8 XCDs round-robin; give each XCD a contiguous range of
-  // (head, chunk) items so that neighbouring chunks, which share the V rows of a
-  // block they straddle, are written through the same L2 one after the other.
-  const int64_t nchunks = ((int64_t)n_tok + kAppendChunk - 1) / kAppendChunk;
-  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
-  const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (item >= nchunks * Hkv) return;
-  const int h = (int)(item / nchunks);
-  const int64_t j0 = (item - (int64_t)h * nchunks) * kAppendChunk;
-  const int tid = threadIdx.x;
-  const int nk = (int)min<int64_t>(kAppendChunk, n_tok - j0);  // tokens in this chunk
-  if (tid < kAppendChunk) {
-    int64_t sl = -1;
-    if (tid < nk) {
-      sl = slots[j0 + tid];
-      if (sl < 0 || sl >= nslots) sl = -1;  // negative: skip; out of range: ignored
-    }
-    s_slot[tid] = sl;
-  }
-  const int pieces = D / VEC;
-  for (int idx = tid; idx < nk * pieces; idx += blockDim.x) {
-    const int k = idx / pieces, d0 = (idx - k * pieces) * VEC;
-    const int64_t row = ((j0 + k) * Hkv + h) * D + d0;
-    T kv[VEC], vv[VEC];
-    load_vec<T, VEC>(kv, knew + row);
-    load_vec<T, VEC>(vv, vnew + row);
-    store_vec<T, VEC>(s_k + k * D + d0, kv);
-#pragma unroll
-    for (int u = 0; u < VEC; ++u) s_v[(d0 + u) * LD + k] = vv[u];
-  }
-  __syncthreads();
-  const int W = k_chunk(D);  // VEC divides W: a piece stays in one K chunk
-  for (int idx = tid; idx < nk * pieces; idx += blockDim.x) {
-    const int k = idx / pieces, d0 = (idx - k * pieces) * VEC;
-    const int64_t sl = s_slot[k];
-    if (sl < 0) continue;
-    const int64_t p = sl / B;
-    const int o = (int)(sl - p * B);
-    T kv[VEC];
-    load_vec<T, VEC>(kv, s_k + k * D + d0);
-    store_vec<T, VEC>(kpool + layer_off + (p * Hkv + h) * (int64_t)B * D + (int64_t)(d0 / W) * B * W +
-                          (int64_t)o * W + (d0 % W),
-                      kv);
-  }
-  for (int idx = tid; idx < kAppendChunk * D; idx += blockDim.x) {
-    const int k = idx % kAppendChunk, d = idx / kAppendChunk;
-    const int64_t sl = s_slot[k];
-    if (sl < 0) continue;
-    const int64_t p = sl / B;
-    const int o = (int)(sl - p * B);
-    vpool[layer_off + (p * Hkv + h) * (int64_t)B * D + (int64_t)d * B + o] = s_v[d * LD + k];
-  }
-}
 
 // =============================================================================
 // Whole-block moves. A "run" is one (layer, block, K-or-V) stretch of
@@ -300,34 +142,6 @@ template <bool NT>
 __device__ __forceinline__ u32x4 kv_load16(const uint16_t* p) {
   if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   else return *reinterpret_cast<const u32x4*>(p);
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-
-// Two fp32 -> packed bf16 (hardware round to nearest even).
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  f32x2_t v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-// Max / sum over lanes l, l^16, l^32, l^48 (the four lane groups holding one
-// query's keys), through the gfx950 cross-row swap instructions.
-__device__ __forceinline__ float max_over_groups(float v) {
-  uint32_t u = __float_as_uint(v);
-  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  u = __float_as_uint(v);
-  auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float sum_over_groups(float v) {
-  uint32_t u = __float_as_uint(v);
-  auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  u = __float_as_uint(v);
-  auto b = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Block id at offset `off` (wave-uniform, < 256) of the split's table chunk:
@@ -877,12 +691,6 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
 // =============================================================================
 // Host-side helpers: argument checks, launch timing.
 // =============================================================================
-bool geom_ok(const pa_geom* g) {
-  return g && g->num_layers > 0 && g->num_kv_heads > 0 && g->head_dim > 0 && g->block_size > 0 &&
-         g->num_blocks > 0 && (g->dtype == PA_F32 || g->dtype == PA_BF16);
-}
-int64_t esize(const pa_geom* g) { return g->dtype == PA_F32 ? 4 : 2; }
-
 struct ProfRec {
   std::string name;
   hipEvent_t a, b;
@@ -897,30 +705,6 @@ bool g_prof_on = false;
 std::vector<ProfRec> g_prof_pending;
 std::vector<ProfAcc> g_prof_acc;
 
-struct ProfScope {
-  const char* name;
-  hipStream_t st;
-  hipEvent_t a = nullptr, b = nullptr;
-  bool on;
-  ProfScope(const char* n, hipStream_t s) : name(n), st(s), on(false) {
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    if (!g_prof_on) return;
-    if (hipEventCreate(&a) != hipSuccess) return;
-    if (hipEventCreate(&b) != hipSuccess) {
-      (void)hipEventDestroy(a);
-      return;
-    }
-    on = hipEventRecord(a, st) == hipSuccess;
-  }
-  ~ProfScope() {
-    if (!on) return;
-    (void)hipEventRecord(b, st);
-    std::lock_guard<std::mutex> lk(g_prof_mu);
-    g_prof_pending.push_back({name, a, b});
-  }
-};
-
-pa_status launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
 size_t generic_lds_bytes(int G, int D, int B) {
   return sizeof(float) * ((size_t)G * D + 2 * (size_t)B * D + (size_t)G * B + G + 64);
@@ -996,6 +780,25 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
 
 }  // namespace
 
+namespace pa_detail {
+ProfScope::ProfScope(const char* n, hipStream_t s) : name(n), st(s), on(false) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) return;
+  if (hipEventCreate(&a) != hipSuccess) return;
+  if (hipEventCreate(&b) != hipSuccess) {
+    (void)hipEventDestroy(a);
+    return;
+  }
+  on = hipEventRecord(a, st) == hipSuccess;
+}
+ProfScope::~ProfScope() {
+  if (!on) return;
+  (void)hipEventRecord(b, st);
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  g_prof_pending.push_back({name, a, b});
+}
+}  // namespace pa_detail
+
 // =============================================================================
 // C ABI
 // =============================================================================
@@ -1020,22 +823,24 @@ pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t lay
   const dim3 grid((unsigned)wgs);
   if (g->dtype == PA_BF16) {
     if (D % 8 == 0)
-      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 8>), grid, dim3(256), lds, st,
+      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 8, SlotsFromArray>), grid, dim3(256), lds, st,
                          (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_new,
-                         (const uint16_t*)v_new, slot_mapping, n_tokens, H, D, B, nslots, layer_off);
+                         (const uint16_t*)v_new, SlotsFromArray{slot_mapping}, n_tokens, H, D, B, nslots,
+                         layer_off);
     else
-      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 1>), grid, dim3(256), lds, st,
+      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 1, SlotsFromArray>), grid, dim3(256), lds, st,
                          (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_new,
-                         (const uint16_t*)v_new, slot_mapping, n_tokens, H, D, B, nslots, layer_off);
+                         (const uint16_t*)v_new, SlotsFromArray{slot_mapping}, n_tokens, H, D, B, nslots,
+                         layer_off);
   } else {
     if (D % 4 == 0)
-      hipLaunchKernelGGL((append_kv_kernel<float, 4>), grid, dim3(256), lds, st,
+      hipLaunchKernelGGL((append_kv_kernel<float, 4, SlotsFromArray>), grid, dim3(256), lds, st,
                          (float*)k_pool, (float*)v_pool, (const float*)k_new, (const float*)v_new,
-                         slot_mapping, n_tokens, H, D, B, nslots, layer_off);
+                         SlotsFromArray{slot_mapping}, n_tokens, H, D, B, nslots, layer_off);
     else
-      hipLaunchKernelGGL((append_kv_kernel<float, 1>), grid, dim3(256), lds, st,
+      hipLaunchKernelGGL((append_kv_kernel<float, 1, SlotsFromArray>), grid, dim3(256), lds, st,
                          (float*)k_pool, (float*)v_pool, (const float*)k_new, (const float*)v_new,
-                         slot_mapping, n_tokens, H, D, B, nslots, layer_off);
+                         SlotsFromArray{slot_mapping}, n_tokens, H, D, B, nslots, layer_off);
   }
   return launch_status();
 }

@@ -1,0 +1,342 @@
+// Chunked-prefill (multi-query) paged attention for gfx950.
+//
+// Source: "KV Cache Management", section "Chunked prefill mechanics". A prompt is
+// processed in chunks; the queries of chunk k attend over the keys and values of
+// every earlier chunk, already in paged blocks, and over the chunk's own tokens
+// with a lower-triangular causal mask; the chunk's keys and values are written
+// into the sequence's paged blocks. Writing them first and then attending over
+// the pool with the causal mask gives the same outputs (every query sees exactly
+// the positions at or before its own) and lets one kernel read every key through
+// the block table ("The PagedAttention virtual memory model").
+//
+// Kernel shape. A work group (4 waves) owns one tile of 128 query rows of one
+// (chunk, KV head): the G query heads of the group times 128/G consecutive chunk
+// tokens, 32 rows per wave, as two 16-column MFMA tiles. It walks the visible
+// keys in pairs of blocks (32 keys). Each pair's K and V tiles (4 per pair) are
+// loaded once for the 128 rows into LDS with 16-byte loads, double-buffered so
+// the next pair's loads are in flight while the current pair is computed, then
+// read as MFMA operand fragments at the same offsets the decode kernel uses on
+// the pool (the LDS image has the pool's tile layout):
+//   S^T[32 keys][16 rows] = K[keys][d] . Q^T[d][rows]     (two tiles of rows)
+//   O^T[d][16 rows]      += V^T[d][keys] . P^T[keys][rows]
+// with the online-softmax update of the same section between them. Work-group
+// order is XCD-aware: the tiles of one (chunk, KV head) run one after another on
+// one XCD, so its history is read from HBM once and from that XCD's L2 after.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/pa.h"
+#include "pa_append.h"
+#include "pa_device.h"
+
+namespace {
+
+using namespace pa_detail;
+
+constexpr int kPfWaves = 4;
+constexpr int kPfRowsPerWave = 32;                  // two 16-column MFMA tiles
+constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // query rows per work group
+
+template <int D>
+struct PfCfg {
+  static constexpr int KC = D / 32;                        // QK k-steps
+  static constexpr int DT = D / 16;                        // PV row tiles
+  static constexpr int TILE_BYTES = 16 * D * 2;            // one (block, head) K or V tile
+  static constexpr int PAIR_BYTES = 4 * TILE_BYTES;        // K0, K1, V0, V1
+  static constexpr int LOADS = PAIR_BYTES / (16 * 64 * kPfWaves);  // 16-byte loads per thread
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_bf16_kernel(
+    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ out, ChunkBatch cb,
+    const int32_t* __restrict__ tables, int64_t layer_off, int N, int Hkv, int Hq, int max_blocks,
+    int n_tiles, float qk_scale) {
+  constexpr int KC = PfCfg<D>::KC;
+  constexpr int DT = PfCfg<D>::DT;
+  constexpr int TILE = PfCfg<D>::TILE_BYTES;
+  constexpr int PAIR = PfCfg<D>::PAIR_BYTES;
+  constexpr int LOADS = PfCfg<D>::LOADS;
+  constexpr int TQ = kPfRows / G;        // chunk tokens per work group
+  constexpr int TW = kPfRowsPerWave / G;  // chunk tokens per wave
+  extern __shared__ __align__(16) unsigned char pf_smem[];  // two pair buffers
+
+  const int64_t items = (int64_t)cb.n_seqs * Hkv * n_tiles;
+  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
+  const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (item >= items) return;  // whole work group
+  const int tile = (int)(item % n_tiles);
+  const int64_t ig = item / n_tiles;
+  const int g = (int)(ig % Hkv);
+  const int i = (int)(ig / Hkv);
+  int a, q_len, ctx;
+  cb.chunk(i, a, q_len, ctx);
+  const int t0 = tile * TQ;
+  if (t0 >= q_len) return;  // whole work group
+  const int kmax = ctx + min(t0 + TQ, q_len);  // keys [0, kmax) are visible to some row
+  const int nblk = (kmax + 15) >> 4;
+  const int npairs = (nblk + 1) >> 1;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, c = lane & 15, gq = lane >> 4;
+
+  // Query rows of this wave: row r = 16*ct + c is token t0 + TW*wave + r/G,
+  // query head g*G + r%G. Rows past the chunk end get zero queries (finite
+  // scores) and are not written.
+  bf16x8 qf[2][KC];
+  int qpos[2];
+  bool rvalid[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int r = 16 * ct + c;
+    const int tok = t0 + TW * wave + r / G;
+    rvalid[ct] = tok < q_len;
+    qpos[ct] = rvalid[ct] ? ctx + tok : kmax - 1;
+    const uint16_t* qrow = q + ((int64_t)(a + (rvalid[ct] ? tok : 0)) * Hq + g * G + r % G) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (rvalid[ct]) v = *reinterpret_cast<const u32x4*>(qrow + 32 * kc + 8 * gq);
+      qf[ct][kc] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x4 acc[2][DT];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};
+  float l_run[2] = {0.f, 0.f};
+
+  const int32_t* trow = tables + (int64_t)i * max_blocks;
+  const char* kl = reinterpret_cast<const char*>(kpool + layer_off);
+  const char* vl = reinterpret_cast<const char*>(vpool + layer_off);
+
+  // Pair image in LDS: [K blk0][K blk1][V blk0][V blk1], each tile as in the pool.
+  u32x4 pre[LOADS];
+  auto fetch = [&](int pj) {
+    const int b0 = 2 * pj;
+    const int p0 = guard_block(trow[b0], N);
+    const int p1 = (b0 + 1 < nblk) ? guard_block(trow[b0 + 1], N) : p0;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int off = (u * 256 + tid) * 16;  // byte offset in the pair image
+      const int tl = off / TILE;
+      const int p = (tl & 1) ? p1 : p0;
+      const char* base = (tl < 2 ? kl : vl) + ((int64_t)p * Hkv + g) * TILE;
+      pre[u] = *reinterpret_cast<const u32x4*>(base + (off - tl * TILE));
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u)
+      *reinterpret_cast<u32x4*>(pf_smem + buf * PAIR + (u * 256 + tid) * 16) = pre[u];
+  };
+
+  // Score row c of each tile holds pair-local key 8*(c>>2) + 4*t + (c&3): block
+  // (c >> 3) of the pair, offset 8*((c>>2)&1) + 4*t + (c&3). V^T fragment of a
+  // lane: block (gq >> 1), dims 16*dt + c, slots 8*(gq&1) .. +8.
+  const int k_sel = c >> 3;
+  const int k_off0 = 8 * ((c >> 2) & 1) + (c & 3);
+  const int v_sel = gq >> 1;
+  const int v_off = 32 * c + 16 * (gq & 1);  // bytes
+
+  auto compute = [&](int pj, int buf) {
+    const unsigned char* img = pf_smem + buf * PAIR;
+    u32x4 kf[2][KC], vf[DT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kf[t][kc] = *reinterpret_cast<const u32x4*>(img + k_sel * TILE + kc * 1024 +
+                                                    (k_off0 + 4 * t) * 64 + 16 * gq);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      vf[dt] = *reinterpret_cast<const u32x4*>(img + (2 + v_sel) * TILE + dt * 512 + v_off);
+    const int key0 = 32 * pj + 8 * gq;  // this lane's keys: key0 + 4*t + e (scores), key0 + e (V)
+    if (32 * pj + 32 > kmax) {          // slots past the valid data: V zeroed (0 * NaN guard)
+      u32x4 keep;
+#pragma unroll
+      for (int wv = 0; wv < 4; ++wv) {
+        const int p = key0 + 2 * wv;
+        keep[wv] = (p < kmax ? 0x0000ffffu : 0u) | (p + 1 < kmax ? 0xffff0000u : 0u);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vf[dt] &= keep;
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      f32x4 sc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[t][kc]),
+                                                          qf[ct][kc], sc[t], 0, 0, 0);
+      }
+      float sv[8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          sv[4 * t + e] = (key0 + 4 * t + e <= qpos[ct]) ? sc[t][e] * qk_scale : -INFINITY;
+      float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mb = max_over_groups(mb);
+      // finite: key 0 is visible to every row, so the first pair sets a finite maximum
+      const float m_new = fmaxf(m_run[ct], mb);
+      float psum = 0.f;
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float pa = __builtin_amdgcn_exp2f(sv[e] - m_new);
+        const float pb = __builtin_amdgcn_exp2f(sv[e + 1] - m_new);
+        psum += pa + pb;
+        pw[e >> 1] = pack_bf16x2(pa, pb);
+      }
+      if (__any(m_new != m_run[ct])) {
+        const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_new);
+        l_run[ct] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[ct][dt] = acc[ct][dt] * alpha;
+      }
+      l_run[ct] += psum;
+      m_run[ct] = m_new;
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
+                                                              pf, acc[ct][dt], 0, 0, 0);
+    }
+  };
+
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  for (int pj = 0; pj < npairs; ++pj) {
+    const bool more = pj + 1 < npairs;  // uniform across the work group
+    if (more) fetch(pj + 1);
+    compute(pj, pj & 1);
+    if (more) stash((pj + 1) & 1);
+    __syncthreads();
+  }
+
+  // acc[ct][dt][e] = O^T[d = 16*dt + 4*gq + e][row 16*ct + c]
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const float l = sum_over_groups(l_run[ct]);
+    if (!rvalid[ct]) continue;
+    const int r = 16 * ct + c;
+    const int tok = t0 + TW * wave + r / G;
+    const float inv = 1.f / l;
+    uint16_t* o = out + ((int64_t)(a + tok) * Hq + g * G + r % G) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) =
+          make_uint2(pack_bf16x2(acc[ct][dt][0] * inv, acc[ct][dt][1] * inv),
+                     pack_bf16x2(acc[ct][dt][2] * inv, acc[ct][dt][3] * inv));
+  }
+}
+
+template <int D, int G>
+void launch_prefill(dim3 grid, size_t lds, hipStream_t st, const uint16_t* kp, const uint16_t* vp,
+                    const uint16_t* q, uint16_t* out, ChunkBatch cb, const int32_t* tables,
+                    int64_t layer_off, int N, int Hkv, int Hq, int max_blocks, int n_tiles,
+                    float qk_scale) {
+  hipLaunchKernelGGL((prefill_mfma_bf16_kernel<D, G>), grid, dim3(256), lds, st, kp, vp, q, out, cb,
+                     tables, layer_off, N, Hkv, Hq, max_blocks, n_tiles, qk_scale);
+}
+
+template <int D>
+bool launch_prefill_g(int G, dim3 grid, size_t lds, hipStream_t st, const uint16_t* kp,
+                      const uint16_t* vp, const uint16_t* q, uint16_t* out, ChunkBatch cb,
+                      const int32_t* tables, int64_t layer_off, int N, int Hkv, int Hq,
+                      int max_blocks, int n_tiles, float qk_scale) {
+#define PA_PF_CASE(GG)                                                                     \
+  case GG:                                                                                \
+    launch_prefill<D, GG>(grid, lds, st, kp, vp, q, out, cb, tables, layer_off, N, Hkv, Hq, \
+                          max_blocks, n_tiles, qk_scale);                                  \
+    return true;
+  switch (G) {
+    PA_PF_CASE(1)
+    PA_PF_CASE(2)
+    PA_PF_CASE(4)
+    PA_PF_CASE(8)
+    PA_PF_CASE(16)
+    PA_PF_CASE(32)
+    default:
+      return false;
+  }
+#undef PA_PF_CASE
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer, const void* q,
+                     const void* k_new, const void* v_new, void* out, int32_t n_seqs,
+                     int32_t n_tokens, int32_t n_q_heads, const int32_t* q_start,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* ctx_lens, int32_t max_q_len, int32_t max_context_len,
+                     float scale, void* stream) {
+  if (!geom_ok(g) || layer < 0 || layer >= g->num_layers || n_seqs < 0 || n_tokens < 0 ||
+      n_q_heads <= 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+    return PA_ERR_INVALID_ARG;
+  const int B = g->block_size, D = g->head_dim, Hkv = g->num_kv_heads;
+  if (n_q_heads % Hkv != 0 || max_q_len > max_context_len) return PA_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * B < max_context_len) return PA_ERR_INVALID_ARG;
+  const int G = n_q_heads / Hkv;
+  if (g->dtype != PA_BF16 || B != 16 || (D != 64 && D != 128) || G > 32 || 32 % G != 0)
+    return PA_ERR_UNSUPPORTED;
+  if (n_seqs == 0 || n_tokens == 0 || max_q_len == 0) return PA_OK;
+  if (!k_pool || !v_pool || !q || !k_new || !v_new || !out || !q_start || !block_tables || !ctx_lens)
+    return PA_ERR_INVALID_ARG;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t layer_off = (int64_t)layer * g->num_blocks * Hkv * B * D;
+  const ChunkBatch cb{q_start, ctx_lens, n_seqs, n_tokens, max_q_len, max_context_len};
+
+  {  // the chunks' keys and values go to their positions through the block tables
+    ProfScope ps("prefill_append", st);
+    const int64_t items = ((int64_t)n_tokens + kAppendChunk - 1) / kAppendChunk * Hkv;
+    const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
+    if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    const SlotsFromTables src{cb, block_tables, max_blocks_per_seq, B, g->num_blocks};
+    hipLaunchKernelGGL((append_kv_kernel<uint16_t, 8, SlotsFromTables>), dim3((unsigned)wgs),
+                       dim3(256), append_lds_bytes<uint16_t>(D), st, (uint16_t*)k_pool,
+                       (uint16_t*)v_pool, (const uint16_t*)k_new, (const uint16_t*)v_new, src,
+                       n_tokens, Hkv, D, B, (int64_t)g->num_blocks * B, layer_off);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  {
+    ProfScope ps("prefill_attention", st);
+    const int TQ = kPfRows / G;
+    const int n_tiles = (max_q_len + TQ - 1) / TQ;
+    const int64_t items = (int64_t)n_seqs * Hkv * n_tiles;
+    const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
+    if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
+    const float qk_scale = scale * kLog2e;
+    const dim3 grid((unsigned)wgs);
+    const size_t lds = 2 * (size_t)(D == 64 ? PfCfg<64>::PAIR_BYTES : PfCfg<128>::PAIR_BYTES);
+    const bool ok =
+        D == 64 ? launch_prefill_g<64>(G, grid, lds, st, (const uint16_t*)k_pool,
+                                       (const uint16_t*)v_pool, (const uint16_t*)q, (uint16_t*)out,
+                                       cb, block_tables, layer_off, g->num_blocks, Hkv, n_q_heads,
+                                       max_blocks_per_seq, n_tiles, qk_scale)
+                : launch_prefill_g<128>(G, grid, lds, st, (const uint16_t*)k_pool,
+                                        (const uint16_t*)v_pool, (const uint16_t*)q, (uint16_t*)out,
+                                        cb, block_tables, layer_off, g->num_blocks, Hkv, n_q_heads,
+                                        max_blocks_per_seq, n_tiles, qk_scale);
+    if (!ok) return PA_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+"""GPU parity of chunked prefill (pa_prefill) against the oracle.
+
+"KV Cache Management", section "Chunked prefill mechanics": each chunk's queries
+attend over the cached tokens and, causally, over the chunk; the chunk's K/V go
+into its paged blocks. The pools must match the oracle bit for bit and the
+outputs within 2e-2 (bf16). Every slot that holds no history, including the slots
+the chunks are written into, is NaN before the call. Splitting a prompt into
+chunks must reproduce the monolithic pass bit for bit, and outputs must not
+depend on which physical blocks hold the data."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_83_amd as pk
+from oracle import block_manager as obm
+from oracle import layout as olayout
+from oracle import prefill as opf
+from synth import gen
+from tests.gpu_helpers import (BF16_TOL, max_abs_err, need_gpu, padded_tables, print_case, to_dev,
+                               to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+def make_prefill_batch(Hq, Hkv, d, ctx, qlens, seed, N=None, L=1, B=16, free_order=None):
+    """History of ctx[i] tokens then a chunk of qlens[i] tokens per sequence,
+    reserved by the oracle block manager; NaN everywhere except the history."""
+    need = sum(-(-(c + q) // B) for c, q in zip(ctx, qlens))
+    N = N or need + 8
+    order = gen.permutation(seed, N) if free_order is None else free_order
+    bm = obm.BlockManager(N, B, order)
+    tables = []
+    for c, ql in zip(ctx, qlens):
+        s = bm.seq_new()
+        bm.append(s, int(c))
+        bm.append(s, int(ql))
+        tables.append(bm.table(s))
+    kp = gen.normal_values(seed + 1, olayout.k_pool_shape(L, N, Hkv, B, d), "bf16")
+    vp = gen.normal_values(seed + 2, olayout.v_pool_shape(L, N, Hkv, B, d), "bf16")
+    used = np.zeros((N, B), dtype=bool)
+    for t, c in zip(tables, ctx):
+        for pos in range(int(c)):
+            used[t[pos // B], pos % B] = True
+    nan = np.uint16(0x7FC0)
+    for p in range(N):
+        for o in range(B):
+            if not used[p, o]:
+                kp[:, p, :, :, o, :] = nan
+                vp[:, p, :, :, o] = nan
+    n_tok = int(sum(qlens))
+    q_start = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = gen.normal_values(seed + 3, (n_tok, Hq, d), "bf16")
+    kn = gen.normal_values(seed + 4, (n_tok, Hkv, d), "bf16")
+    vn = gen.normal_values(seed + 5, (n_tok, Hkv, d), "bf16")
+    return dict(N=N, L=L, B=B, Hq=Hq, Hkv=Hkv, d=d, tables=tables, kp=kp, vp=vp, q=q, kn=kn, vn=vn,
+                q_start=q_start, ctx=np.asarray(ctx, np.int32), qlens=np.asarray(qlens))
+
+
+def run_prefill(b, layer=0, tables=None, kp=None, vp=None):
+    geom = pk.Geometry(b["L"], b["Hkv"], b["d"], b["B"], b["N"], "bf16")
+    K = to_dev(b["kp"] if kp is None else kp, "bf16")
+    V = to_dev(b["vp"] if vp is None else vp, "bf16")
+    tabs = b["tables"] if tables is None else tables
+    max_blocks = max(1, max(len(t) for t in tabs))
+    q = to_dev(b["q"], "bf16")
+    out = torch.full_like(q, float("nan"))
+    max_ctx = int(max(int(c) + int(ql) for c, ql in zip(b["ctx"], b["qlens"])))
+    pk.prefill(geom, K, V, layer, q, to_dev(b["kn"], "bf16"), to_dev(b["vn"], "bf16"), out,
+               torch.from_numpy(b["q_start"]).cuda(),
+               torch.from_numpy(padded_tables(tabs, max_blocks)).cuda(),
+               torch.from_numpy(b["ctx"]).cuda(), int(max(b["qlens"])), max_ctx)
+    torch.cuda.synchronize()
+    return to_host(out, "bf16"), to_host(K, "bf16"), to_host(V, "bf16")
+
+
+def oracle_prefill(b, layer=0):
+    return opf.paged_prefill(b["q"], b["kn"], b["vn"], b["kp"], b["vp"], layer, b["tables"],
+                             b["q_start"], b["ctx"], b["B"], "bf16")
+
+
+CASES = [
+    # name, Hq, Hkv, d, ctx, qlens
+    ("d128_g8", 64, 8, 128, [0, 5, 16, 300, 700], [1, 17, 16, 33, 130]),
+    ("d128_g8_long_chunk", 16, 2, 128, [0, 48], [300, 257]),
+    ("d64_g4", 16, 4, 64, [3, 0, 129], [40, 77, 64]),
+    ("d128_mha", 4, 4, 128, [0, 10], [200, 129]),
+    ("d64_g16", 32, 2, 64, [7, 260], [9, 21]),
+    ("d128_g32", 64, 2, 128, [0, 31], [6, 13]),
+    ("d128_g2", 8, 4, 128, [1, 100], [70, 1]),
+    ("with_empty_chunk", 16, 2, 128, [12, 40, 0], [5, 0, 3]),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_parity(case):
+    need_gpu()
+    name, Hq, Hkv, d, ctx, qlens = case
+    print_case(test="prefill_parity", case=name)
+    b = make_prefill_batch(Hq, Hkv, d, ctx, qlens, seed=zlib.crc32(name.encode()) % 10000)
+    out, K, V = run_prefill(b)
+    ek, ev, expect = oracle_prefill(b)
+    assert np.array_equal(K.view(np.uint8), ek.view(np.uint8)), "K pool"
+    assert np.array_equal(V.view(np.uint8), ev.view(np.uint8)), "V pool"
+    assert np.isfinite(olayout.widen(out, "bf16")).all()
+    err = max_abs_err(out, expect, "bf16")
+    assert err <= BF16_TOL, (name, err)
+
+
+@pytest.mark.parametrize("chunk", [16, 48, 100])
+def test_chunks_reproduce_monolithic_bitwise(chunk):
+    """One prompt of 300 tokens: one call over the whole prompt vs calls over
+    consecutive chunks (each appending its K/V), same physical blocks."""
+    need_gpu()
+    print_case(test="prefill_chunked", chunk=chunk)
+    S, Hq, Hkv, d = 300, 32, 4, 128
+    mono = make_prefill_batch(Hq, Hkv, d, [0], [S], seed=41)
+    out_m, Km, Vm = run_prefill(mono)
+    geom = pk.Geometry(1, Hkv, d, 16, mono["N"], "bf16")
+    K, V = to_dev(mono["kp"], "bf16"), to_dev(mono["vp"], "bf16")
+    tab = torch.from_numpy(padded_tables(mono["tables"], len(mono["tables"][0]))).cuda()
+    outs = []
+    for c in range(0, S, chunk):
+        ql = min(chunk, S - c)
+        q = to_dev(mono["q"][c:c + ql], "bf16")
+        out = torch.full_like(q, float("nan"))
+        pk.prefill(geom, K, V, 0, q, to_dev(mono["kn"][c:c + ql], "bf16"),
+                   to_dev(mono["vn"][c:c + ql], "bf16"), out,
+                   torch.tensor([0, ql], dtype=torch.int32, device="cuda"), tab,
+                   torch.tensor([c], dtype=torch.int32, device="cuda"), ql, S)
+        outs.append(to_host(out, "bf16"))
+    torch.cuda.synchronize()
+    assert np.array_equal(np.concatenate(outs).view(np.uint8), out_m.view(np.uint8))
+    assert np.array_equal(to_host(K, "bf16").view(np.uint8), Km.view(np.uint8))
+    assert np.array_equal(to_host(V, "bf16").view(np.uint8), Vm.view(np.uint8))
+
+
+def test_placement_invariance_bitwise():
+    need_gpu()
+    print_case(test="prefill_placement")
+    Hq, Hkv, d, ctx, qlens = 16, 2, 128, [70, 0, 33], [40, 20, 65]
+    a = make_prefill_batch(Hq, Hkv, d, ctx, qlens, seed=51)
+    b = make_prefill_batch(Hq, Hkv, d, ctx, qlens, seed=52, N=a["N"])
+    for ta, tb in zip(a["tables"], b["tables"]):
+        for lb in range(len(ta)):
+            b["kp"][:, tb[lb]] = a["kp"][:, ta[lb]]
+            b["vp"][:, tb[lb]] = a["vp"][:, ta[lb]]
+    b["q"], b["kn"], b["vn"] = a["q"], a["kn"], a["vn"]
+    assert a["tables"] != b["tables"]
+    out_a, _, _ = run_prefill(a)
+    out_b, _, _ = run_prefill(b)
+    assert np.array_equal(out_a.view(np.uint8), out_b.view(np.uint8))
+
+
+def test_prefill_bad_arguments():
+    need_gpu()
+    print_case(test="prefill_bad_args")
+    q_start = torch.tensor([0, 1], dtype=torch.int32, device="cuda")
+    ctx = torch.zeros(1, dtype=torch.int32, device="cuda")
+    tab = torch.zeros(1, 1, dtype=torch.int32, device="cuda")
+    geom = pk.Geometry(1, 2, 64, 16, 4, "f32")                 # fp32: not implemented
+    K, V = pk.alloc_pools(geom)
+    q = torch.zeros(1, 4, 64, device="cuda")
+    kn = torch.zeros(1, 2, 64, device="cuda")
+    with pytest.raises(pk.PagedKVError):
+        pk.prefill(geom, K, V, 0, q, kn, kn, torch.empty_like(q), q_start, tab, ctx, 1, 1)
+    geom = pk.Geometry(1, 2, 64, 16, 4, "bf16")
+    K, V = pk.alloc_pools(geom)
+    q, kn = q.to(torch.bfloat16), kn.to(torch.bfloat16)
+    with pytest.raises(pk.PagedKVError):                      # chunk longer than the context bound
+        pk.prefill(geom, K, V, 0, q, kn, kn, torch.empty_like(q), q_start, tab, ctx, 2, 1)
+    with pytest.raises(pk.PagedKVError):                      # table too short for the context
+        pk.prefill(geom, K, V, 0, q, kn, kn, torch.empty_like(q), q_start, tab, ctx, 1, 17)
+    with pytest.raises(pk.PagedKVError):                      # 3 query heads per KV head: unsupported
+        pk.prefill(geom, K, V, 0, torch.zeros(1, 6, 64, device="cuda", dtype=torch.bfloat16), kn, kn,
+                   torch.zeros(1, 6, 64, device="cuda", dtype=torch.bfloat16), q_start, tab, ctx, 1, 1)
