@@ -30,6 +30,7 @@ import time
 import numpy as np
 
 PEAK_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0   # dense bf16 matrix-core peak of the part
 METRIC = "paged-decode KV GB/s (% of HBM peak) + decode tokens/s, 70B-GQA 32K ctx"
 
 
@@ -490,6 +491,159 @@ def run_fork(args):
 
 
 # =============================================================================
+# Chunked prefill
+# =============================================================================
+def run_prefill(args):
+    torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool = setup(args)
+    from synth import gen
+    L, n, Hq, Hkv, d, B = (cfg.num_layers, cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
+                           cfg.head_dim, cfg.block_size)
+    C = cfg.chunk_len
+    hist = gen.prefill_histories(cfg)
+    bm = pk.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
+    seqs = [bm.seq_new() for _ in range(n)]
+    for s_, c in zip(seqs, hist):
+        if c:
+            bm.append(s_, int(c))
+        bm.append(s_, C)
+    max_blocks = max(bm.info(s_)[1] for s_ in seqs)
+    tables_np, lens_np = bm.build_tables(seqs, max_blocks)
+    assert np.array_equal(lens_np, hist + C)
+    n_tok = n * C
+    q_all = torch.randn((L, n_tok, Hq, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    k_all = torch.randn((L, n_tok, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    v_all = torch.randn((L, n_tok, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    out = torch.empty_like(q_all)
+    q_start = torch.arange(0, n_tok + 1, C, dtype=torch.int32, device=dev)
+    tables = torch.from_numpy(np.ascontiguousarray(tables_np)).to(dev)
+    ctx = torch.from_numpy(hist.astype(np.int32)).to(dev)
+    max_ctx = int((hist + C).max())
+    torch.cuda.synchronize()
+
+    profiling = [False]
+
+    def step():
+        for layer in range(L):
+            prof = profiling[0] and layer % args.prof_every == 0
+            if prof:
+                pk.Profiler.enable(True)
+            pk.prefill(geom, k_pool, v_pool, layer, q_all[layer], k_all[layer], v_all[layer],
+                       out[layer], q_start, tables, ctx, C, max_ctx, stream=stream)
+            if prof:
+                pk.Profiler.enable(False)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    run = make_runner(torch, stream, step, args.graph)
+    if args.graph:
+        run()
+    if not args.no_prof and not args.graph:
+        pk.Profiler.reset()
+        profiling[0] = True
+    t, step_ms = timed_steps(torch, stream, run, args.steps)
+    profiling[0] = False
+    ms = max(t.ms, t.wall_ms) / args.steps
+    # causal attention FLOPs: 2 per multiply-add, QK^T and PV, over the visible keys
+    macs_layer = sum(2 * Hq * d * (C * int(c) + C * (C + 1) // 2) for c in hist)
+    flops_step = 2 * macs_layer * L
+    value = flops_step / (ms * 1e-3) / 1e12
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    kern, roofline = {}, None
+    if not args.no_prof and not args.graph:
+        for name in ("prefill_append", "prefill_attention"):
+            cnt, tot = pk.Profiler.read(name)
+            if cnt:
+                kern[name] = {"launches": cnt, "avg_us": round(1e3 * tot / cnt, 2)}
+        if "prefill_attention" in kern:
+            avg_s = kern["prefill_attention"]["avg_us"] * 1e-6
+            ach = 2 * macs_layer / avg_s / 1e12
+            roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "kernel": "prefill_mfma_bf16_kernel", "flops_per_launch": 2 * macs_layer,
+                        "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    # parity on sampled (chunk, layer) outputs; cpu baseline = the oracle on a sample
+    parity, cpu_baseline = None, None
+    if args.parity_samples or not args.no_cpu_baseline:
+        from oracle import prefill as opf
+        from oracle import block_manager as obm
+        om = obm.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
+        otables = []
+        for c in hist:
+            s_ = om.seq_new()
+            if c:
+                om.append(s_, int(c))
+            om.append(s_, C)
+            otables.append(om.table(s_))
+        rng = np.random.default_rng(cfg.seed)
+
+        def oracle_one(i, layer):
+            # the chunk's history is untouched by the step (it writes positions
+            # hist[i] .. hist[i]+C-1 only), so the pool after the run serves
+            ids = otables[i]
+            idx = torch.as_tensor(ids, dtype=torch.long, device=dev)
+            kb = to_np(torch, k_pool[layer].index_select(0, idx), cfg.dtype)[None]
+            vb = to_np(torch, v_pool[layer].index_select(0, idx), cfg.dtype)[None]
+            rows = slice(i * C, (i + 1) * C)
+            qs = np.array([0, C], dtype=np.int64)
+            _, _, o = opf.paged_prefill(to_np(torch, q_all[layer, rows], cfg.dtype),
+                                        to_np(torch, k_all[layer, rows], cfg.dtype),
+                                        to_np(torch, v_all[layer, rows], cfg.dtype), kb, vb, 0,
+                                        [list(range(len(ids)))], qs, [int(hist[i])], B, cfg.dtype)
+            return o
+
+        errs = []
+        for _ in range(args.parity_samples):
+            i, layer = int(rng.integers(0, n)), int(rng.integers(0, L))
+            expect = oracle_one(i, layer)
+            got = out[layer, i * C:(i + 1) * C].float().cpu().numpy().astype(np.float64)
+            errs.append(float(np.max(np.abs(got - expect))))
+        if errs:
+            parity = {"samples": len(errs), "max_abs_err": max(errs), "tol": 2e-2, "ok": max(errs) <= 2e-2}
+            log(f"parity {parity}")
+        if not args.no_cpu_baseline:
+            try:
+                from threadpoolctl import threadpool_limits
+            except Exception:  # pragma: no cover
+                threadpool_limits = None
+            cores = len(os.sched_getaffinity(0))
+            pairs = [(int(rng.integers(0, n)), int(rng.integers(0, L))) for _ in range(args.cpu_sample // 8)]
+            limiter = threadpool_limits(limits=cores) if threadpool_limits else contextlib.nullcontext()
+            with limiter:
+                t0 = time.perf_counter()
+                flops = 0
+                for (i, layer) in pairs:
+                    oracle_one(i, layer)
+                    flops += 4 * Hq * d * (C * int(hist[i]) + C * (C + 1) // 2)
+                cpu_s = time.perf_counter() - t0
+            cpu_baseline = {"value": round(flops / cpu_s / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+                            "kind": "oracle", "tokens_per_s": round(len(pairs) * C / cpu_s / L, 4),
+                            "sample": f"{len(pairs)} (chunk, layer) prefills of this workload timed in "
+                                      f"{cpu_s:.1f} s; rate in causal attention FLOP/s"}
+
+    result = {
+        "metric": "chunked-prefill attention TFLOP/s (causal) + prefill tokens/s, prefill_chunks",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, seeded random block placement)",
+        "config": {"workload": cfg.name, "num_layers": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": d, "block_size": B, "num_seqs": n, "chunk_len": C,
+                   "histories": sorted(set(int(c) for c in hist)), "prompt_len": cfg.length_max,
+                   "launch": "hip graph replay" if args.graph else "eager"},
+        "step_ms": step_ms,
+        "tokens_per_s": round(n_tok / (ms * 1e-3), 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "kernels": kern,
+        "parity": parity,
+    }
+    print(json.dumps(result), flush=True)
+
+
+# =============================================================================
 # Offload round trip
 # =============================================================================
 def run_offload(args):
@@ -613,6 +767,8 @@ def main():
     cfg = get_config(args.config)
     if cfg.name == "offload":
         run_offload(args)
+    elif cfg.length_kind == "prefill":
+        run_prefill(args)
     elif cfg.length_kind == "fork":
         run_fork(args)
     else:

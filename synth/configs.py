@@ -17,6 +17,10 @@ Shapes follow the workloads the pages describe:
 * ``offload``     -- the 70B geometry at 131,072 tokens with half of each
   trajectory's blocks moved to a host tier and back ("KV Cache Management",
   section "Asynchronous paged swapping").
+* ``prefill_chunks`` -- the 70B geometry prefilling 2,048-token prompts in
+  512-token chunks ("KV Cache Management", section "Chunked prefill
+  mechanics", Figure 8): the batch holds chunk k = 1..4 of different prompts,
+  i.e. histories of 0, 512, 1,024 and 1,536 cached tokens.
 
 Seeds: workload k (1-based, in the order above) uses master seed 8300 + k.
 """
@@ -52,6 +56,8 @@ class Workload:
     # offload workload
     offload_fraction: float = 0.0
     offload_chunk_blocks: int = 0
+    # chunked-prefill workload: prompt length (length_max) cut into chunks
+    chunk_len: int = 0
     notes: str = ""
     extra: Dict[str, float] = field(default_factory=dict)
 
@@ -102,6 +108,12 @@ CONFIGS = [
         length_kind="fixed", length_min=131072, length_max=131072,
         offload_fraction=0.5, offload_chunk_blocks=512,
         notes="4 x 131,072-token trajectories; half of each one's blocks offloaded",
+    ),
+    Workload(
+        name="prefill_chunks", index=6, num_layers=80, num_q_heads=64, num_kv_heads=8,
+        head_dim=128, block_size=16, dtype="bf16", num_blocks=4096, num_seqs=16,
+        length_kind="prefill", length_min=2048, length_max=2048, chunk_len=512,
+        notes="16 prompts of 2,048 tokens in 512-token chunks; sequence i runs chunk (i mod 4) + 1",
     ),
 ]
 

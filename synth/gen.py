@@ -40,7 +40,16 @@ def context_lengths(cfg: Workload) -> np.ndarray:
         return np.full(n, cfg.length_min, dtype=np.int64)
     if cfg.length_kind == "fork":
         return cfg.prefix_len + suffix_lengths(cfg)
+    if cfg.length_kind == "prefill":
+        return prefill_histories(cfg) + cfg.chunk_len
     raise ValueError(cfg.length_kind)
+
+
+def prefill_histories(cfg: Workload) -> np.ndarray:
+    """Cached tokens before each sequence's chunk: sequence i runs chunk
+    (i mod K) + 1 of a prompt of length_max tokens cut into K chunks."""
+    k = cfg.length_max // cfg.chunk_len
+    return (np.arange(cfg.num_seqs) % k * cfg.chunk_len).astype(np.int64)
 
 
 def suffix_lengths(cfg: Workload) -> np.ndarray:

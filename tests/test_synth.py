@@ -47,3 +47,12 @@ def test_bf16_rounding_ties_to_even():
     x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -0.0, np.inf], np.float32)
     bits = gen.f32_to_bf16_bits(x).tolist()
     assert bits == [0x3F80, 0x3F82, 0x8000, 0x7F80]
+
+
+def test_prefill_recipe():
+    c = get_config("prefill_chunks")
+    h = gen.prefill_histories(c)
+    assert h.tolist() == [0, 512, 1024, 1536] * 4
+    assert np.array_equal(gen.context_lengths(c), h + 512)
+    assert (gen.context_lengths(c) <= c.length_max).all()
+    assert c.seed == 8306
