@@ -190,3 +190,64 @@ def test_mutant_prefill_slots_relative(monkeypatch):
     monkeypatch.setattr(opf, "chunk_slots", _chunk_slots_relative)
     _raises(TP.test_chunk_written_at_table_positions)
     _raises(TP.test_chunked_equals_monolithic, 16)
+
+
+# ---------------------------------------------------------------------------
+# Tiered residency (asynchronous swapping)
+from tests import test_oracle_tiering as TT  # noqa: E402
+
+
+def _finish_to_front(self, sid, logical):
+    self._check_logical(sid, logical)
+    pend = self.pending.get(sid, {})
+    for lb in logical:
+        if pend.get(lb, ("",))[0] != "out":
+            raise obm.InvalidArgument("nothing in flight")
+    host = self.host.setdefault(sid, {})
+    for lb in logical:
+        _, p, frame = pend.pop(lb)
+        self.ref[p] -= 1
+        if self.ref[p] == 0:
+            self.free.appendleft(p)                    # wrong: the FIFO takes freed ids at the back
+        self.tables[sid][lb] = obm.NOT_RESIDENT
+        host[lb] = frame
+
+
+def _begin_frees_at_once(self, sid, logical):
+    phys, first = begin_orig(self, sid, logical)
+    for p in phys:                                     # wrong: frees before the copy completed
+        self.ref[p] -= 1
+        if self.ref[p] == 0:
+            self.free.append(p)
+        self.ref[p] += 1                               # keep the counts so finish still works
+    return phys, first
+
+
+def _swap_in_finish_keeps_frames(self, sid, logical):
+    pend = self.pending.get(sid, {})
+    for lb in logical:
+        if pend.get(lb, ("",))[0] != "in":
+            raise obm.InvalidArgument("nothing in flight")
+    for lb in logical:
+        _, p, frame = pend.pop(lb)
+        self.tables[sid][lb] = p
+        del self.host[sid][lb]                         # wrong: the frame never returns to the pool
+
+
+begin_orig = obm.BlockManager.swap_out_begin
+
+
+def test_mutant_swap_finish_fifo_front(monkeypatch):
+    monkeypatch.setattr(obm.BlockManager, "swap_out_finish", _finish_to_front)
+    _raises(TT.test_migration_follows_the_pages_steps)
+
+
+def test_mutant_swap_frees_before_copy(monkeypatch):
+    monkeypatch.setattr(obm.BlockManager, "swap_out_begin", _begin_frees_at_once)
+    _raises(TT.test_migration_follows_the_pages_steps)
+
+
+def test_mutant_swap_in_leaks_frames(monkeypatch):
+    monkeypatch.setattr(obm.BlockManager, "swap_in_finish", _swap_in_finish_keeps_frames)
+    _raises(TT.test_migration_follows_the_pages_steps)
+    _raises(TT.test_random_migrations_conserve_blocks_and_frames)
