@@ -76,7 +76,8 @@ typedef enum {
   PA_ERR_NOT_FOUND = -4,     /* unknown sequence id                             */
   PA_ERR_HIP = -5,           /* a HIP runtime call or launch failed             */
   PA_ERR_WORKSPACE = -6,     /* decode workspace too small                      */
-  PA_ERR_UNSUPPORTED = -7    /* geometry outside what the kernels implement     */
+  PA_ERR_UNSUPPORTED = -7,   /* geometry outside what the kernels implement     */
+  PA_ERR_OUT_OF_FRAMES = -8  /* the host frame pool has no free run long enough  */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -235,7 +236,9 @@ pa_status pa_prof_read(const char* kernel, int64_t* launches, double* total_ms);
  * length per sequence. Appends allocate at block boundaries; a write into a
  * partly filled block whose count is above 1 first takes a fresh block and
  * reports a (src, dst) copy for pa_copy_blocks. Every call checks its
- * preconditions before changing anything. Not thread-safe. */
+ * preconditions before changing anything. Every call takes the manager's
+ * mutex, so calls from several threads (e.g. the completion steps of
+ * asynchronous migrations, run on a HIP host-function thread) are serialised. */
 typedef struct pa_bm pa_bm;
 
 pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
@@ -247,6 +250,9 @@ int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
 
 /* Raw allocator: take n blocks (count 1), all or none. */
 pa_status pa_bm_alloc(pa_bm* bm, int32_t n, int32_t* ids_out);
+/* The free queue front to back: the first min(cap, size) ids go to ids_out,
+ * *n_out gets the queue length. */
+pa_status pa_bm_free_list(const pa_bm* bm, int32_t* ids_out, int32_t cap, int32_t* n_out);
 /* One more reference to each listed (allocated) block. */
 pa_status pa_bm_incref(pa_bm* bm, const int32_t* ids, int32_t n);
 /* Drop one reference from each listed block; a block reaching 0 returns to the
@@ -288,9 +294,121 @@ pa_status pa_bm_seq_table(const pa_bm* bm, int32_t seq, int32_t* table_out, int3
 pa_status pa_bm_build_tables(const pa_bm* bm, const int32_t* seqs, int32_t n, int32_t max_blocks,
                              int32_t pad, int32_t* tables_out, int32_t* lens_out);
 /* Check internal invariants: every count covers the table references to its
- * block, the free list holds each zero-count block exactly once and nothing
- * else, and every table has ceil(length / B) entries. PA_OK if consistent. */
+ * block (and the blocks reserved by swap-ins in flight), the free list holds
+ * each zero-count block exactly once and nothing else, every table has
+ * ceil(length / B) entries, and every used host frame is held by exactly one
+ * host-tier or in-flight entry. PA_OK if consistent. */
 pa_status pa_bm_validate(const pa_bm* bm);
+
+/* ---------------------------------------------------------------- tiered residency */
+/* Source: "KV Cache Management", section "Asynchronous paged swapping". Each
+ * table entry carries a residency tag. A migration to the host takes a
+ * contiguous run of frames from a pinned host pool at its start (step 1) while
+ * the blocks stay allocated and readable; the copy runs in the background
+ * (step 2); its completion retags the entries as host-resident with their frame
+ * indices and pushes the vacated blocks to the back of the free queue (step 3).
+ * The return path reserves fresh blocks at its start and, on completion, points
+ * the entries at them and returns the frames to the pool. A sequence with a
+ * migration in flight cannot be forked or released, and an append cannot write
+ * into a tail block that is host-resident or in flight. Host-resident entries
+ * read -1 in pa_bm_seq_table / pa_bm_build_tables. The manager holds only the
+ * frame bookkeeping; the bytes live in the buffer a pa_swapper owns. */
+typedef enum {
+  PA_TIER_HBM = 0,         /* resident in the device pool; index = block id           */
+  PA_TIER_HOST = 1,        /* in host memory; index = host frame (-1: swapped out by
+                              pa_bm_seq_swap_out, no frame of the pool)                */
+  PA_TIER_PENDING_OUT = 2, /* copy to the host in flight; index = block id (still valid) */
+  PA_TIER_PENDING_IN = 3   /* copy back in flight; index = host frame                  */
+} pa_tier;
+
+/* Give the manager a host pool of num_frames frames (frames 0..num_frames-1).
+ * Runs are handed out first fit from the lowest frame; a freed run merges with
+ * free neighbours. Only one pool per manager (PA_ERR_INVALID_ARG otherwise). */
+pa_status pa_bm_attach_host_pool(pa_bm* bm, int32_t num_frames);
+/* Free frames of the attached pool, -1 without one. */
+int32_t pa_bm_host_frames_free(const pa_bm* bm);
+/* Free runs of the host pool in increasing start order (first min(cap, count)
+ * into starts/lengths); *n_out gets the number of runs. */
+pa_status pa_bm_host_free_runs(const pa_bm* bm, int32_t* starts, int32_t* lengths, int32_t cap,
+                               int32_t* n_out);
+/* Residency tag (a pa_tier value) and index of logical block `logical` of seq. */
+pa_status pa_bm_block_tier(const pa_bm* bm, int32_t seq, int32_t logical, int32_t* tier,
+                           int32_t* index);
+/* Step 1 for the n listed logical blocks (distinct, all PA_TIER_HBM, n >= 1):
+ * reserve frames first .. first+n-1 (logical[k] goes to frame first + k) and
+ * mark the entries PA_TIER_PENDING_OUT. phys_out[k] receives the block to copy
+ * from. PA_ERR_OUT_OF_FRAMES if no free run of n frames exists. */
+pa_status pa_bm_swap_out_begin(pa_bm* bm, int32_t seq, const int32_t* logical, int32_t n,
+                               int32_t* phys_out, int32_t* first_frame_out);
+/* Step 3, after the copy has completed: the entries become PA_TIER_HOST and the
+ * sequence's references to their blocks are dropped (a block reaching count 0
+ * goes to the back of the free queue). Every entry must be PENDING_OUT. */
+pa_status pa_bm_swap_out_finish(pa_bm* bm, int32_t seq, const int32_t* logical, int32_t n);
+/* Return path: for PA_TIER_HOST entries holding a frame, take n fresh blocks
+ * from the free queue (all or none: PA_ERR_OUT_OF_BLOCKS) and mark the entries
+ * PA_TIER_PENDING_IN. phys_out[k] / frames_out[k]: destination block and
+ * source frame of logical[k]. The table keeps -1 until the finish step. */
+pa_status pa_bm_swap_in_begin(pa_bm* bm, int32_t seq, const int32_t* logical, int32_t n,
+                              int32_t* phys_out, int32_t* frames_out);
+/* After the copy back has completed: entries point at their new blocks
+ * (PA_TIER_HBM) and their frames return to the pool. Every entry must be
+ * PENDING_IN. */
+pa_status pa_bm_swap_in_finish(pa_bm* bm, int32_t seq, const int32_t* logical, int32_t n);
+
+/* ---------------------------------------------------------------- asynchronous swapper */
+/* Moves blocks between the device pool and a pinned host frame pool in the
+ * background, following "KV Cache Management", section "Asynchronous paged
+ * swapping" (copy stream, pinned frames, completion callback that retags the
+ * table) and its pipelined chunked reload. The swapper owns a page-locked host
+ * buffer of num_frames frames (frame f at byte f * frame_bytes, one block in the
+ * staging layout of pa_gather_blocks), a device staging buffer of chunk_blocks
+ * blocks and a copy stream of its own (default priority). Work of one swapper
+ * runs in issue order on that stream; the completion step of each migration
+ * (pa_bm_swap_out_finish / pa_bm_swap_in_finish) runs on the HIP runtime's
+ * host-function thread when its copies have finished.
+ * The block manager must outlive the swapper; one swapper per manager. */
+typedef struct pa_swapper pa_swapper;
+
+/* k_pool, v_pool: the device pools of geometry g. chunk_blocks = 0 picks about
+ * 256 MiB of staging. Attaches a host pool of num_frames frames to bm. Allocates
+ * (hipHostMalloc, hipMalloc); PA_ERR_HIP if that fails. */
+pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_pool,
+                            int32_t num_frames, int32_t chunk_blocks, pa_swapper** out);
+/* Waits for every migration (pa_swapper_sync), then frees the buffers. The
+ * manager keeps its frame bookkeeping; host-tier entries lose their bytes. */
+pa_status pa_swapper_destroy(pa_swapper* s);
+/* Move the n listed logical blocks of seq to the host: pa_bm_swap_out_begin
+ * now (errors from it are returned and nothing is queued), then per chunk a
+ * gather kernel and one device-to-host copy into the reserved run of frames,
+ * then the completion step. The copies are ordered after all work queued on
+ * after_stream before this call (NULL: no ordering), so the kernels that wrote
+ * these blocks must be queued there. The blocks stay readable by decode until
+ * the completion step frees them; nothing may write them meanwhile. Returns
+ * once the work is queued. A HIP failure after the reservation leaves the
+ * entries in flight and makes every later call return PA_ERR_HIP. */
+pa_status pa_swap_out_async(pa_swapper* s, int32_t seq, const int32_t* logical, int32_t n,
+                            void* after_stream);
+/* Bring the n listed host-tier blocks of seq back: pa_bm_swap_in_begin now
+ * (fresh blocks from the front of the free queue), then per chunk one
+ * host-to-device copy per run of consecutive frames and a scatter kernel into
+ * the fresh blocks, then the completion step (table remapped, frames freed).
+ * Ordered after after_stream as above: blocks freed before this call may still
+ * be in use by kernels queued there. */
+pa_status pa_swap_in_async(pa_swapper* s, int32_t seq, const int32_t* logical, int32_t n,
+                           void* after_stream);
+/* Make `stream` wait (on the device) for every copy queued so far. */
+pa_status pa_swapper_fence(pa_swapper* s, void* stream);
+/* Block the calling thread until every queued migration, completion step
+ * included, has finished. Returns the first error a completion step reported. */
+pa_status pa_swapper_sync(pa_swapper* s);
+/* Migrations whose completion step has not run yet; -1 for NULL. */
+int32_t pa_swapper_pending(const pa_swapper* s);
+/* Any of the outputs may be NULL: the pinned frame buffer, the copy stream
+ * (hipStream_t), bytes per frame, blocks per chunk, and the bytes moved by
+ * completed swap-outs and swap-ins. */
+pa_status pa_swapper_info(const pa_swapper* s, void** host_frames, void** stream,
+                          int64_t* frame_bytes, int32_t* chunk_blocks, int64_t* bytes_out,
+                          int64_t* bytes_in);
 
 #ifdef __cplusplus
 }

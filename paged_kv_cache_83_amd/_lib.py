@@ -16,7 +16,9 @@ PA_OK = 0
 STATUS_NAMES = {
     0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_OUT_OF_BLOCKS", -3: "PA_ERR_DOUBLE_FREE",
     -4: "PA_ERR_NOT_FOUND", -5: "PA_ERR_HIP", -6: "PA_ERR_WORKSPACE", -7: "PA_ERR_UNSUPPORTED",
+    -8: "PA_ERR_OUT_OF_FRAMES",
 }
+PA_TIER_HBM, PA_TIER_HOST, PA_TIER_PENDING_OUT, PA_TIER_PENDING_IN = 0, 1, 2, 3
 PA_F32, PA_BF16 = 0, 1
 
 
@@ -78,6 +80,23 @@ SIGNATURES = {
     "pa_bm_seq_table": (_i32, [_vp, _i32, _pi32, _i32, _pi32]),
     "pa_bm_build_tables": (_i32, [_vp, _pi32, _i32, _i32, _i32, _pi32, _pi32]),
     "pa_bm_validate": (_i32, [_vp]),
+    "pa_bm_free_list": (_i32, [_vp, _pi32, _i32, _pi32]),
+    "pa_bm_attach_host_pool": (_i32, [_vp, _i32]),
+    "pa_bm_host_frames_free": (_i32, [_vp]),
+    "pa_bm_host_free_runs": (_i32, [_vp, _pi32, _pi32, _i32, _pi32]),
+    "pa_bm_block_tier": (_i32, [_vp, _i32, _i32, _pi32, _pi32]),
+    "pa_bm_swap_out_begin": (_i32, [_vp, _i32, _pi32, _i32, _pi32, _pi32]),
+    "pa_bm_swap_out_finish": (_i32, [_vp, _i32, _pi32, _i32]),
+    "pa_bm_swap_in_begin": (_i32, [_vp, _i32, _pi32, _i32, _pi32, _pi32]),
+    "pa_bm_swap_in_finish": (_i32, [_vp, _i32, _pi32, _i32]),
+    "pa_swapper_create": (_i32, [_pg, _vp, _vp, _vp, _i32, _i32, C.POINTER(_vp)]),
+    "pa_swapper_destroy": (_i32, [_vp]),
+    "pa_swap_out_async": (_i32, [_vp, _i32, _pi32, _i32, _vp]),
+    "pa_swap_in_async": (_i32, [_vp, _i32, _pi32, _i32, _vp]),
+    "pa_swapper_fence": (_i32, [_vp, _vp]),
+    "pa_swapper_sync": (_i32, [_vp]),
+    "pa_swapper_pending": (_i32, [_vp]),
+    "pa_swapper_info": (_i32, [_vp, C.POINTER(_vp), C.POINTER(_vp), _pi64, _pi32, _pi64, _pi64]),
 }
 
 _lib = None
@@ -116,6 +135,10 @@ class DoubleFreeError(PagedKVError):
     pass
 
 
+class OutOfFramesError(PagedKVError):
+    pass
+
+
 def check(status: int, what: str) -> None:
     if status == PA_OK:
         return
@@ -123,4 +146,6 @@ def check(status: int, what: str) -> None:
         raise OutOfBlocksError(status, what)
     if status == -3:
         raise DoubleFreeError(status, what)
+    if status == -8:
+        raise OutOfFramesError(status, what)
     raise PagedKVError(status, what)

@@ -462,3 +462,135 @@ class BlockManager:
 
     def validate(self):
         check(self._lib.pa_bm_validate(self._h), "pa_bm_validate")
+
+    def free_list(self):
+        """The free queue, front to back."""
+        n = C.c_int32()
+        out = np.empty(max(self.num_blocks, 1), np.int32)
+        check(self._lib.pa_bm_free_list(self._h, _p32(out), out.size, C.byref(n)), "pa_bm_free_list")
+        return out[:n.value].tolist()
+
+    # ---- tiered residency ("Asynchronous paged swapping") -------------------
+    def attach_host_pool(self, num_frames: int):
+        check(self._lib.pa_bm_attach_host_pool(self._h, int(num_frames)), "pa_bm_attach_host_pool")
+
+    def host_frames_free(self) -> int:
+        return int(self._lib.pa_bm_host_frames_free(self._h))
+
+    def host_free_runs(self):
+        """Free runs of the host frame pool as [(start, length)], by start."""
+        n = C.c_int32()
+        check(self._lib.pa_bm_host_free_runs(self._h, None, None, 0, C.byref(n)), "pa_bm_host_free_runs")
+        st, ln = np.empty(max(n.value, 1), np.int32), np.empty(max(n.value, 1), np.int32)
+        check(self._lib.pa_bm_host_free_runs(self._h, _p32(st), _p32(ln), n.value, C.byref(n)),
+              "pa_bm_host_free_runs")
+        return list(zip(st[:n.value].tolist(), ln[:n.value].tolist()))
+
+    def tier(self, seq: int, logical: int):
+        """(tag, index) of one table entry; tags are the PA_TIER_* values."""
+        t, i = C.c_int32(), C.c_int32()
+        check(self._lib.pa_bm_block_tier(self._h, seq, logical, C.byref(t), C.byref(i)),
+              "pa_bm_block_tier")
+        return t.value, i.value
+
+    def swap_out_begin(self, seq: int, logical):
+        """Returns (physical blocks, first host frame)."""
+        a = _i32arr(logical)
+        phys, first = np.empty(max(a.size, 1), np.int32), C.c_int32()
+        check(self._lib.pa_bm_swap_out_begin(self._h, seq, _p32(a), a.size, _p32(phys),
+                                             C.byref(first)), "pa_bm_swap_out_begin")
+        return phys[:a.size].tolist(), first.value
+
+    def swap_out_finish(self, seq: int, logical):
+        a = _i32arr(logical)
+        check(self._lib.pa_bm_swap_out_finish(self._h, seq, _p32(a), a.size), "pa_bm_swap_out_finish")
+
+    def swap_in_begin(self, seq: int, logical):
+        """Returns (new physical blocks, host frames)."""
+        a = _i32arr(logical)
+        phys, frames = np.empty(max(a.size, 1), np.int32), np.empty(max(a.size, 1), np.int32)
+        check(self._lib.pa_bm_swap_in_begin(self._h, seq, _p32(a), a.size, _p32(phys),
+                                            _p32(frames)), "pa_bm_swap_in_begin")
+        return phys[:a.size].tolist(), frames[:a.size].tolist()
+
+    def swap_in_finish(self, seq: int, logical):
+        a = _i32arr(logical)
+        check(self._lib.pa_bm_swap_in_finish(self._h, seq, _p32(a), a.size), "pa_bm_swap_in_finish")
+
+
+class Swapper:
+    """Asynchronous block migration between the device pool and pinned host frames
+    (pa_swapper_*). Copies run on the swapper's own stream; each migration's
+    completion step retags the block manager's table when its copies are done.
+
+    `after` (swap_out / swap_in): the stream whose earlier work the copies must
+    follow; None means the current stream of the pools' device, 0 means none."""
+
+    def __init__(self, geom: Geometry, bm: BlockManager, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                 num_frames: int, chunk_blocks: int = 0):
+        _dev(k_pool, "k_pool")
+        _dev(v_pool, "v_pool")
+        self._lib = _L()
+        self._bm, self._k, self._v = bm, k_pool, v_pool     # kept alive with the swapper
+        self.device = k_pool.device
+        h = C.c_void_p()
+        g = geom.c()
+        check(self._lib.pa_swapper_create(C.byref(g), bm._h, _ptr(k_pool), _ptr(v_pool),
+                                          int(num_frames), int(chunk_blocks), C.byref(h)),
+              "pa_swapper_create")
+        self._h = h
+        self.num_frames = int(num_frames)
+        host, stream, fb, cb = C.c_void_p(), C.c_void_p(), C.c_int64(), C.c_int32()
+        check(self._lib.pa_swapper_info(h, C.byref(host), C.byref(stream), C.byref(fb), C.byref(cb),
+                                        None, None), "pa_swapper_info")
+        self.frame_bytes, self.chunk_blocks = fb.value, cb.value
+        self._host_ptr, self._stream_ptr = host.value, stream.value
+        self.stream = torch.cuda.ExternalStream(self._stream_ptr, device=self.device)
+
+    def _after(self, after):
+        if after is None:
+            return torch.cuda.current_stream(self.device).cuda_stream
+        return _stream(after, self.device)
+
+    def swap_out(self, seq: int, logical, after=None):
+        a = _i32arr(logical)
+        check(self._lib.pa_swap_out_async(self._h, seq, _p32(a), a.size, self._after(after)),
+              "pa_swap_out_async")
+
+    def swap_in(self, seq: int, logical, after=None):
+        a = _i32arr(logical)
+        check(self._lib.pa_swap_in_async(self._h, seq, _p32(a), a.size, self._after(after)),
+              "pa_swap_in_async")
+
+    def fence(self, stream=None):
+        """Make `stream` (default: current) wait on the device for the copies queued so far."""
+        check(self._lib.pa_swapper_fence(self._h, _stream(stream, self.device)), "pa_swapper_fence")
+
+    def sync(self):
+        check(self._lib.pa_swapper_sync(self._h), "pa_swapper_sync")
+
+    def pending(self) -> int:
+        return int(self._lib.pa_swapper_pending(self._h))
+
+    def bytes_moved(self):
+        """(bytes of completed swap-outs, bytes of completed swap-ins)."""
+        o, i = C.c_int64(), C.c_int64()
+        check(self._lib.pa_swapper_info(self._h, None, None, None, None, C.byref(o), C.byref(i)),
+              "pa_swapper_info")
+        return o.value, i.value
+
+    def host_frames(self) -> np.ndarray:
+        """The pinned frame buffer as uint8 [num_frames, frame_bytes] (no copy)."""
+        buf = (C.c_uint8 * (self.num_frames * self.frame_bytes)).from_address(self._host_ptr)
+        return np.ctypeslib.as_array(buf).reshape(self.num_frames, self.frame_bytes)
+
+    def close(self):
+        if getattr(self, "_h", None):
+            h, self._h = self._h, None
+            check(self._lib.pa_swapper_destroy(h), "pa_swapper_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -35,6 +35,7 @@
 #include "../../include/pa.h"
 #include "pa_device.h"
 #include "pa_append.h"
+#include "pa_move.h"
 
 namespace {
 
@@ -43,58 +44,6 @@ using namespace pa_detail;
 // =============================================================================
 // Append: token j's K/V go to slot slot_mapping[j] of one layer.
 // =============================================================================
-
-// =============================================================================
-// Whole-block moves. A "run" is one (layer, block, K-or-V) stretch of
-// H_kv*B*d elements, contiguous in the pool. MODE 0: pool -> pool (copy-on-write
-// copy, ids_a = src, ids_b = dst). MODE 1: pool -> staging (gather). MODE 2:
-// staging -> pool (scatter). One work-group moves one run.
-// =============================================================================
-template <int MODE, typename V>
-__global__ __launch_bounds__(256) void block_move_kernel(char* __restrict__ kpool,
-                                                         char* __restrict__ vpool,
-                                                         char* __restrict__ staging,
-                                                         const int32_t* __restrict__ ids_a,
-                                                         const int32_t* __restrict__ ids_b,
-                                                         int L, int N, int64_t run_bytes) {
-  const int64_t r = blockIdx.x;
-  const int kv = (int)(r & 1);
-  const int layer = (int)((r >> 1) % L);
-  const int64_t i = (r >> 1) / L;
-  char* pool = kv ? vpool : kpool;
-  const char* src;
-  char* dst;
-  if (MODE == 0) {
-    int a = ids_a[i], b = ids_b[i];
-    if (a < 0 || a >= N || b < 0 || b >= N) return;
-    src = pool + ((int64_t)layer * N + a) * run_bytes;
-    dst = pool + ((int64_t)layer * N + b) * run_bytes;
-  } else {
-    int a = ids_a[i];
-    if (a < 0 || a >= N) return;
-    char* p = pool + ((int64_t)layer * N + a) * run_bytes;
-    char* s = staging + (((i * L) + layer) * 2 + kv) * run_bytes;
-    src = (MODE == 1) ? p : s;
-    dst = (MODE == 1) ? s : p;
-  }
-  const V* sv = reinterpret_cast<const V*>(src);
-  V* dv = reinterpret_cast<V*>(dst);
-  const int64_t n = run_bytes / (int64_t)sizeof(V);
-  constexpr int U = 4;
-  for (int64_t base = threadIdx.x; base < n; base += (int64_t)blockDim.x * U) {
-    V tmp[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t k = base + (int64_t)u * blockDim.x;
-      if (k < n) tmp[u] = __builtin_nontemporal_load(sv + k);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int64_t k = base + (int64_t)u * blockDim.x;
-      if (k < n) __builtin_nontemporal_store(tmp[u], dv + k);
-    }
-  }
-}
 
 // =============================================================================
 // Decode, MFMA kernel: bf16 pool, B = 16, d in {64, 128, 256}, up to 16 query
@@ -998,9 +947,12 @@ static pa_status block_move(int mode, const char* name, const pa_geom* g, void* 
   hipStream_t st = (hipStream_t)stream;
   ProfScope ps(name, st);
   const dim3 grid((unsigned)runs), block(256);
-#define PA_MOVE(M, V)                                                                             \
-  hipLaunchKernelGGL((block_move_kernel<M, V>), grid, block, 0, st, (char*)k_pool, (char*)v_pool, \
-                     (char*)staging, ids_a, ids_b, g->num_layers, g->num_blocks, run)
+#define PA_MOVE(M, V)                                                                  \
+  hipLaunchKernelGGL((block_move_kernel<M, V, PtrIds, PtrIds>), grid, block, 0, st,        \
+                     (char*)k_pool,                                                         \
+                     (char*)v_pool, (char*)staging, PtrIds{ids_a},                          \
+                     PtrIds{mode == 0 ? ids_b : ids_a},                                     \
+                     g->num_layers, g->num_blocks, run)
 #define PA_MOVE_MODE(M)                                            \
   do {                                                             \
     if (run % 16 == 0) PA_MOVE(M, u32x4);                          \
