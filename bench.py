@@ -13,7 +13,9 @@ bytes per token, all layers).
 Other workloads (--config): gpt2_fp32 and chat_ragged run the same decode step;
 fork_cow times copy-on-write copies + bulk suffix append + decode; offload
 times the gather -> host -> scatter round trip of half of each trajectory and
-checks that decode is bitwise identical before and after.
+checks that decode is bitwise identical before and after; offload_overlap runs
+the headline decode batch while one more trajectory goes to pinned host memory
+and back through the asynchronous swapper.
 """
 
 from __future__ import annotations
@@ -57,6 +59,10 @@ def parse():
                     help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--unfused", action="store_true",
                     help="append the step's tokens with a separate launch before each decode")
+    ap.add_argument("--chunk-blocks", type=int, default=-1,
+                    help="offload_overlap: blocks per staging chunk (-1 = the workload's, 0 = library default)")
+    ap.add_argument("--move-wgs", type=int, default=0,
+                    help="offload_overlap: work-groups per swap gather/scatter launch (0 = library default)")
     ap.add_argument("--offload-fraction", type=float, default=1.0,
                     help="offload workload: fraction of the chosen blocks moved (host RAM bound)")
     return ap.parse_args()
@@ -754,6 +760,219 @@ def run_offload(args):
         sys.exit(1)
 
 
+# =============================================================================
+# Overlapped asynchronous offload
+# =============================================================================
+PEAK_HOST_LINK_GBS = 64.0   # PCIe Gen5 x16, one direction
+
+
+def run_overlap(args):
+    """The gqa70b_32k decode batch steps on the compute stream while one more
+    trajectory goes to pinned host memory and back through pa_swapper.
+
+    Phase A: decode alone. Phase B: the round trip alone (freed blocks poisoned
+    and the free queue reshuffled before the way back, decode of the trajectory
+    compared bit for bit). Phase C: the swap-out is queued, then enough decode
+    steps to cover it; once its completion step has run the free queue is
+    reshuffled again and the swap-in is queued, followed by more decode steps.
+    Reports the host-link rates alone and overlapped, the decode slowdown and
+    the fraction of the migration's time hidden behind decode."""
+    torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool = setup(args)
+    from paged_kv_cache_83_amd import steps
+    from synth import gen
+    L, n, Hq, Hkv, d, B = (cfg.num_layers, cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
+                           cfg.head_dim, cfg.block_size)
+    lengths = gen.context_lengths(cfg)
+    bm = pk.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
+    seqs = [bm.seq_new() for _ in range(n)]
+    for s, S in zip(seqs, lengths):
+        bm.append(s, int(S) - 1)
+    slots_np, cow = bm.append_batch(seqs, [1] * n)
+    assert not cow
+    mover = bm.seq_new()
+    bm.append(mover, cfg.mover_len)
+    nblk = bm.info(mover)[1]
+    lbs = list(range(nblk))
+    max_blocks = max(bm.info(s)[1] for s in seqs)
+    tables_np, lens_np = bm.build_tables(seqs, max_blocks)
+    slots = torch.from_numpy(slots_np).to(dev)
+    tables = torch.from_numpy(np.ascontiguousarray(tables_np)).to(dev)
+    lens = torch.from_numpy(np.ascontiguousarray(lens_np)).to(dev)
+    max_ctx = int(lengths.max())
+    dt = geom.torch_dtype
+    q_all = torch.randn((L, n, Hq, d), generator=gen_, device=dev).to(dt)
+    k_new = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(dt)
+    v_new = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(dt)
+    out = torch.empty((L, n, Hq, d), dtype=dt, device=dev)
+    ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx)), dtype=torch.uint8,
+                     device=dev)
+    q_m = torch.randn((L, 1, Hq, d), generator=gen_, device=dev).to(dt)
+    ws_m = torch.empty(max(1, pk.decode_workspace_bytes(geom, 1, Hq, cfg.mover_len)),
+                       dtype=torch.uint8, device=dev)
+
+    def step():
+        steps.decode_step(geom, k_pool, v_pool, q_all, k_new, v_new, slots, tables, lens, max_ctx,
+                          out, ws, stream=stream, fused=not args.unfused)
+
+    def decode_mover():
+        t = torch.from_numpy(np.asarray([bm.table(mover)], np.int32)).to(dev)
+        ln = torch.tensor([cfg.mover_len], dtype=torch.int32, device=dev)
+        o = torch.empty((L, 1, Hq, d), dtype=dt, device=dev)
+        for layer in range(L):
+            pk.decode(geom, k_pool, v_pool, layer, q_m[layer], o[layer], t, ln, cfg.mover_len,
+                      workspace=ws_m, stream=stream)
+        torch.cuda.synchronize()
+        return o
+
+    # ---- phase A: decode alone ----------------------------------------------
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_a, st_a = timed_steps(torch, stream, step, args.steps)
+    dec_ms = st_a["median"]
+    out_ref = out.clone()
+    mover_ref = decode_mover()
+    log(f"decode alone: {dec_ms:.3f} ms/step (median of {args.steps})")
+
+    chunk = cfg.offload_chunk_blocks if args.chunk_blocks < 0 else args.chunk_blocks
+    sw = pk.Swapper(geom, bm, k_pool, v_pool, nblk, chunk, args.move_wgs)
+    moved = nblk * sw.frame_bytes
+    log(f"trajectory: {cfg.mover_len} tokens = {nblk} blocks = {moved / 2**30:.2f} GiB, "
+        f"chunks of {sw.chunk_blocks} blocks")
+    ev = lambda: torch.cuda.Event(enable_timing=True)    # noqa: E731
+
+    side = torch.cuda.Stream(dev)      # idle stream: marks issue and completion times
+
+    def migrate(kind, after):
+        a, b = ev(), ev()
+        a.record(side)
+        (sw.swap_out if kind == "out" else sw.swap_in)(mover, lbs, after=after)
+        sw.fence(side)
+        b.record(side)
+        return a, b
+
+    def poison_and_shuffle(poison):
+        if poison:
+            free = torch.as_tensor(bm.free_list(), dtype=torch.long, device=dev)
+            k_pool.index_fill_(1, free, float("nan"))
+            v_pool.index_fill_(1, free, float("nan"))
+        bm.permute_free(gen.realloc_shuffle(cfg, bm.num_free()))
+
+    # ---- phase B: round trip alone ------------------------------------------
+    torch.cuda.synchronize()
+    if not args.no_prof:
+        pk.Profiler.reset()
+        pk.Profiler.enable(True)
+    o_a, o_b = migrate("out", stream)
+    sw.sync()
+    assert all(bm.tier(mover, lb)[0] == pk.PA_TIER_HOST for lb in lbs)
+    poison_and_shuffle(True)
+    i_a, i_b = migrate("in", stream)       # ordered after the poisoning on the compute stream
+    sw.sync()
+    side.synchronize()
+    pk.Profiler.enable(False)
+    out_ms_alone, in_ms_alone = o_a.elapsed_time(o_b), i_a.elapsed_time(i_b)
+    mig_alone = out_ms_alone + in_ms_alone
+    alone_ok = bool(torch.equal(decode_mover().view(torch.int16), mover_ref.view(torch.int16)))
+    log(f"round trip alone: out {out_ms_alone:.1f} ms, in {in_ms_alone:.1f} ms, bitwise {alone_ok}")
+    kern = {}
+    if not args.no_prof:
+        for name in ("swap_gather", "swap_scatter"):
+            cnt, tot = pk.Profiler.read(name)
+            if cnt:
+                kern[name] = {"launches": cnt, "avg_us": round(1e3 * tot / cnt, 2),
+                              "GBps_rw": round(2 * moved / (tot * 1e-3) / 1e9, 1)}
+
+    # ---- phase C: round trip behind decode -----------------------------------
+    k1 = int(math.ceil(out_ms_alone / dec_ms)) + 2
+    k2 = int(math.ceil(in_ms_alone / dec_ms)) + 2
+    torch.cuda.synchronize()
+    times = StepTimes(torch, stream, k1 + k2)
+    c_a = ev()
+    c_a.record(stream)
+    o_a, o_b = migrate("out", stream)
+    for _ in range(k1):
+        times.mark()
+        step()
+    sw.sync()                                # host waits for the completion step only
+    poison_and_shuffle(False)                # host-side: fresh blocks differ from the old ones
+    # No kernel queued on the compute stream touches the trajectory's blocks (the
+    # batch never frees a block), so the way back needs no ordering after it.
+    i_a, i_b = migrate("in", 0)
+    for _ in range(k2):
+        times.mark()
+        step()
+    times.mark()
+    c_b = ev()
+    c_b.record(stream)
+    sw.sync()
+    torch.cuda.synchronize()
+    out_ms_ov, in_ms_ov = o_a.elapsed_time(o_b), i_a.elapsed_time(i_b)
+    compute_ms = c_a.elapsed_time(c_b)
+    total_ms = max(compute_ms, c_a.elapsed_time(i_b))
+    serial_ms = (k1 + k2) * dec_ms + mig_alone
+    hidden = (serial_ms - total_ms) / mig_alone
+    st_c = times.summary()
+    batch_ok = bool(torch.equal(out.view(torch.int16), out_ref.view(torch.int16)))
+    mover_ok = bool(torch.equal(decode_mover().view(torch.int16), mover_ref.view(torch.int16)))
+    log(f"overlapped: {k1}+{k2} steps in {compute_ms:.1f} ms (alone {(k1 + k2) * dec_ms:.1f}), "
+        f"out {out_ms_ov:.1f} ms, in {in_ms_ov:.1f} ms, hidden {hidden:.3f}")
+
+    # ---- CPU baseline: the oracle's gather + scatter on a sample of blocks -----
+    cpu_baseline = None
+    if not args.no_cpu_baseline:
+        from oracle import kv_ops as okv
+        sample = bm.table(mover)[:16]
+        idx = torch.as_tensor(sample, dtype=torch.long, device=dev)
+        kb = to_np(torch, k_pool.index_select(1, idx), cfg.dtype)
+        vb = to_np(torch, v_pool.index_select(1, idx), cfg.dtype)
+        ids = list(range(len(sample)))
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < 10.0:
+            st = okv.gather_blocks(kb, vb, ids)
+            okv.scatter_blocks(kb, vb, st, ids[::-1])
+            reps += 1
+        cpu_s = time.perf_counter() - t0
+        cpu_baseline = {"value": round(2 * reps * len(sample) * sw.frame_bytes / cpu_s / 1e9, 3),
+                        "unit": "GB/s", "cores": 1, "kind": "oracle",
+                        "sample": f"{reps} gather + scatter passes of {len(sample)} blocks of this "
+                                  f"workload through the oracle's kv_ops in {cpu_s:.1f} s"}
+
+    link_ov = 2 * moved / ((out_ms_ov + in_ms_ov) * 1e-3) / 1e9
+    result = {
+        "metric": "host-link GB/s of a 16K-token 70B trajectory round trip overlapped with "
+                  "70B-GQA 32K decode",
+        "value": round(link_ov, 2), "unit": "GB/s", "n_gpus": 1, "steps": k1 + k2,
+        "warmup": args.warmup, "ms_per_step": round(compute_ms / (k1 + k2), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) pools, seeded block placement)",
+        "config": {"workload": cfg.name, "num_seqs": n, "context_len": int(lengths.max()),
+                   "mover_tokens": cfg.mover_len, "mover_blocks": nblk, "bytes_each_way": moved,
+                   "chunk_blocks": sw.chunk_blocks, "pool_blocks": cfg.num_blocks},
+        "decode_ms_alone": dec_ms, "decode_step_ms_overlapped": st_c,
+        "decode_slowdown": round(compute_ms / ((k1 + k2) * dec_ms), 4),
+        "swap_out_ms": {"alone": round(out_ms_alone, 2), "overlapped": round(out_ms_ov, 2)},
+        "swap_in_ms": {"alone": round(in_ms_alone, 2), "overlapped": round(in_ms_ov, 2)},
+        "d2h_GBps": {"alone": round(moved / out_ms_alone / 1e6, 2),
+                     "overlapped": round(moved / out_ms_ov / 1e6, 2)},
+        "h2d_GBps": {"alone": round(moved / in_ms_alone / 1e6, 2),
+                     "overlapped": round(moved / in_ms_ov / 1e6, 2)},
+        "overlap": {"serial_ms": round(serial_ms, 2), "overlapped_ms": round(total_ms, 2),
+                    "hidden_fraction_of_migration": round(hidden, 4)},
+        "roofline": {"bound": "host link", "achieved": round(link_ov, 2), "peak": PEAK_HOST_LINK_GBS,
+                     "unit": "GB/s", "frac": round(link_ov / PEAK_HOST_LINK_GBS, 4), "traffic": None,
+                     "note": "DMA copies, one direction at a time; peak = PCIe Gen5 x16 per direction"},
+        "cpu_baseline": cpu_baseline,
+        "kernels": kern,
+        "parity": {"round_trip_alone_bitwise": alone_ok, "batch_decode_during_overlap_bitwise": batch_ok,
+                   "round_trip_overlapped_bitwise": mover_ok},
+    }
+    sw.close()
+    print(json.dumps(result), flush=True)
+    if not (alone_ok and batch_ok and mover_ok):
+        sys.exit(1)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -767,6 +986,8 @@ def main():
     cfg = get_config(args.config)
     if cfg.name == "offload":
         run_offload(args)
+    elif cfg.name == "offload_overlap":
+        run_overlap(args)
     elif cfg.length_kind == "prefill":
         run_prefill(args)
     elif cfg.length_kind == "fork":

@@ -323,8 +323,11 @@ typedef enum {
 
 /* Give the manager a host pool of num_frames frames (frames 0..num_frames-1).
  * Runs are handed out first fit from the lowest frame; a freed run merges with
- * free neighbours. Only one pool per manager (PA_ERR_INVALID_ARG otherwise). */
+ * free neighbours. One pool per manager (PA_ERR_INVALID_ARG if one is attached). */
 pa_status pa_bm_attach_host_pool(pa_bm* bm, int32_t num_frames);
+/* Remove the host pool; PA_ERR_INVALID_ARG if none is attached or a frame is in
+ * use (an entry is host-resident or in flight). */
+pa_status pa_bm_detach_host_pool(pa_bm* bm);
 /* Free frames of the attached pool, -1 without one. */
 int32_t pa_bm_host_frames_free(const pa_bm* bm);
 /* Free runs of the host pool in increasing start order (first min(cap, count)
@@ -361,21 +364,35 @@ pa_status pa_bm_swap_in_finish(pa_bm* bm, int32_t seq, const int32_t* logical, i
  * swapping" (copy stream, pinned frames, completion callback that retags the
  * table) and its pipelined chunked reload. The swapper owns a page-locked host
  * buffer of num_frames frames (frame f at byte f * frame_bytes, one block in the
- * staging layout of pa_gather_blocks), a device staging buffer of chunk_blocks
- * blocks and a copy stream of its own (default priority). Work of one swapper
- * runs in issue order on that stream; the completion step of each migration
+ * staging layout of pa_gather_blocks), two device staging buffers of
+ * chunk_blocks blocks, and two streams of its own (default priority): one for
+ * the gather / scatter kernels and one for the DMA copies, so that packing chunk
+ * k+1 overlaps the copy of chunk k. The kernels use a few work-groups only,
+ * paced to the host link. Chunks of all migrations alternate between the two
+ * staging buffers in issue order; the completion step of each migration
  * (pa_bm_swap_out_finish / pa_bm_swap_in_finish) runs on the HIP runtime's
- * host-function thread when its copies have finished.
- * The block manager must outlive the swapper; one swapper per manager. */
+ * host-function thread when its last copy or kernel has finished.
+ * The block manager must outlive the swapper; one swapper per manager at a time. */
 typedef struct pa_swapper pa_swapper;
 
-/* k_pool, v_pool: the device pools of geometry g. chunk_blocks = 0 picks about
- * 256 MiB of staging. Attaches a host pool of num_frames frames to bm. Allocates
+/* Swapper tuning; pass NULL for the defaults. */
+typedef struct {
+  int32_t chunk_blocks; /* blocks per staging buffer (0 = about 64 MiB)                       */
+  int32_t move_wgs;     /* work-groups per gather / scatter launch (0 = 512)                  */
+  int32_t direct;       /* 1: no staging and no kernels; each block moves as two strided DMA
+                           copies (K and V: L rows of one run each, the pool's layer pitch)
+                           straight between the pool and its frame, on the DMA stream */
+} pa_swap_opts;
+
+/* k_pool, v_pool: the device pools of geometry g. Attaches a host pool of
+ * num_frames frames to bm (see pa_bm_attach_host_pool). Allocates
  * (hipHostMalloc, hipMalloc); PA_ERR_HIP if that fails. */
 pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_pool,
-                            int32_t num_frames, int32_t chunk_blocks, pa_swapper** out);
-/* Waits for every migration (pa_swapper_sync), then frees the buffers. The
- * manager keeps its frame bookkeeping; host-tier entries lose their bytes. */
+                            int32_t num_frames, const pa_swap_opts* opts, pa_swapper** out);
+/* Waits for every migration (pa_swapper_sync), then frees the buffers and
+ * detaches the host pool from the manager when no frame is in use. Entries
+ * still host-resident keep their frame bookkeeping but lose their bytes (bring
+ * them back first); the pool then stays attached. */
 pa_status pa_swapper_destroy(pa_swapper* s);
 /* Move the n listed logical blocks of seq to the host: pa_bm_swap_out_begin
  * now (errors from it are returned and nothing is queued), then per chunk a
@@ -396,19 +413,19 @@ pa_status pa_swap_out_async(pa_swapper* s, int32_t seq, const int32_t* logical, 
  * be in use by kernels queued there. */
 pa_status pa_swap_in_async(pa_swapper* s, int32_t seq, const int32_t* logical, int32_t n,
                            void* after_stream);
-/* Make `stream` wait (on the device) for every copy queued so far. */
+/* Make `stream` wait (on the device) for every copy and kernel queued so far. */
 pa_status pa_swapper_fence(pa_swapper* s, void* stream);
 /* Block the calling thread until every queued migration, completion step
  * included, has finished. Returns the first error a completion step reported. */
 pa_status pa_swapper_sync(pa_swapper* s);
 /* Migrations whose completion step has not run yet; -1 for NULL. */
 int32_t pa_swapper_pending(const pa_swapper* s);
-/* Any of the outputs may be NULL: the pinned frame buffer, the copy stream
- * (hipStream_t), bytes per frame, blocks per chunk, and the bytes moved by
- * completed swap-outs and swap-ins. */
-pa_status pa_swapper_info(const pa_swapper* s, void** host_frames, void** stream,
-                          int64_t* frame_bytes, int32_t* chunk_blocks, int64_t* bytes_out,
-                          int64_t* bytes_in);
+/* Any of the outputs may be NULL: the pinned frame buffer, the kernel and DMA
+ * streams (hipStream_t), bytes per frame, blocks per chunk, and the bytes moved
+ * by completed swap-outs and swap-ins. */
+pa_status pa_swapper_info(const pa_swapper* s, void** host_frames, void** kernel_stream,
+                          void** dma_stream, int64_t* frame_bytes, int32_t* chunk_blocks,
+                          int64_t* bytes_out, int64_t* bytes_in);
 
 #ifdef __cplusplus
 }

@@ -27,6 +27,10 @@ class pa_geom(C.Structure):
                 ("block_size", C.c_int32), ("num_blocks", C.c_int32), ("dtype", C.c_int32)]
 
 
+class pa_swap_opts(C.Structure):
+    _fields_ = [("chunk_blocks", C.c_int32), ("move_wgs", C.c_int32), ("direct", C.c_int32)]
+
+
 class pa_decode_opts(C.Structure):
     _fields_ = [("blocks_per_split", C.c_int32), ("kernel", C.c_int32), ("kv_reuse", C.c_int32)]
 
@@ -82,6 +86,7 @@ SIGNATURES = {
     "pa_bm_validate": (_i32, [_vp]),
     "pa_bm_free_list": (_i32, [_vp, _pi32, _i32, _pi32]),
     "pa_bm_attach_host_pool": (_i32, [_vp, _i32]),
+    "pa_bm_detach_host_pool": (_i32, [_vp]),
     "pa_bm_host_frames_free": (_i32, [_vp]),
     "pa_bm_host_free_runs": (_i32, [_vp, _pi32, _pi32, _i32, _pi32]),
     "pa_bm_block_tier": (_i32, [_vp, _i32, _i32, _pi32, _pi32]),
@@ -89,14 +94,15 @@ SIGNATURES = {
     "pa_bm_swap_out_finish": (_i32, [_vp, _i32, _pi32, _i32]),
     "pa_bm_swap_in_begin": (_i32, [_vp, _i32, _pi32, _i32, _pi32, _pi32]),
     "pa_bm_swap_in_finish": (_i32, [_vp, _i32, _pi32, _i32]),
-    "pa_swapper_create": (_i32, [_pg, _vp, _vp, _vp, _i32, _i32, C.POINTER(_vp)]),
+    "pa_swapper_create": (_i32, [_pg, _vp, _vp, _vp, _i32, C.POINTER(pa_swap_opts), C.POINTER(_vp)]),
     "pa_swapper_destroy": (_i32, [_vp]),
     "pa_swap_out_async": (_i32, [_vp, _i32, _pi32, _i32, _vp]),
     "pa_swap_in_async": (_i32, [_vp, _i32, _pi32, _i32, _vp]),
     "pa_swapper_fence": (_i32, [_vp, _vp]),
     "pa_swapper_sync": (_i32, [_vp]),
     "pa_swapper_pending": (_i32, [_vp]),
-    "pa_swapper_info": (_i32, [_vp, C.POINTER(_vp), C.POINTER(_vp), _pi64, _pi32, _pi64, _pi64]),
+    "pa_swapper_info": (_i32, [_vp, C.POINTER(_vp), C.POINTER(_vp), C.POINTER(_vp), _pi64, _pi32,
+                               _pi64, _pi64]),
 }
 
 _lib = None

@@ -474,6 +474,9 @@ class BlockManager:
     def attach_host_pool(self, num_frames: int):
         check(self._lib.pa_bm_attach_host_pool(self._h, int(num_frames)), "pa_bm_attach_host_pool")
 
+    def detach_host_pool(self):
+        check(self._lib.pa_bm_detach_host_pool(self._h), "pa_bm_detach_host_pool")
+
     def host_frames_free(self) -> int:
         return int(self._lib.pa_bm_host_frames_free(self._h))
 
@@ -527,7 +530,7 @@ class Swapper:
     follow; None means the current stream of the pools' device, 0 means none."""
 
     def __init__(self, geom: Geometry, bm: BlockManager, k_pool: torch.Tensor, v_pool: torch.Tensor,
-                 num_frames: int, chunk_blocks: int = 0):
+                 num_frames: int, chunk_blocks: int = 0, move_wgs: int = 0, direct: bool = False):
         _dev(k_pool, "k_pool")
         _dev(v_pool, "v_pool")
         self._lib = _L()
@@ -535,17 +538,21 @@ class Swapper:
         self.device = k_pool.device
         h = C.c_void_p()
         g = geom.c()
+        opts = _lib.pa_swap_opts(int(chunk_blocks), int(move_wgs), 1 if direct else 0)
         check(self._lib.pa_swapper_create(C.byref(g), bm._h, _ptr(k_pool), _ptr(v_pool),
-                                          int(num_frames), int(chunk_blocks), C.byref(h)),
+                                          int(num_frames), C.byref(opts), C.byref(h)),
               "pa_swapper_create")
         self._h = h
         self.num_frames = int(num_frames)
-        host, stream, fb, cb = C.c_void_p(), C.c_void_p(), C.c_int64(), C.c_int32()
-        check(self._lib.pa_swapper_info(h, C.byref(host), C.byref(stream), C.byref(fb), C.byref(cb),
-                                        None, None), "pa_swapper_info")
+        host, ks, ds = C.c_void_p(), C.c_void_p(), C.c_void_p()
+        fb, cb = C.c_int64(), C.c_int32()
+        check(self._lib.pa_swapper_info(h, C.byref(host), C.byref(ks), C.byref(ds), C.byref(fb),
+                                        C.byref(cb), None, None), "pa_swapper_info")
         self.frame_bytes, self.chunk_blocks = fb.value, cb.value
-        self._host_ptr, self._stream_ptr = host.value, stream.value
-        self.stream = torch.cuda.ExternalStream(self._stream_ptr, device=self.device)
+        self._host_ptr = host.value
+        # (kernel stream, DMA stream), e.g. for a profiler; use fence() to order work after them
+        self.streams = (torch.cuda.ExternalStream(ks.value, device=self.device),
+                        torch.cuda.ExternalStream(ds.value, device=self.device))
 
     def _after(self, after):
         if after is None:
@@ -563,7 +570,7 @@ class Swapper:
               "pa_swap_in_async")
 
     def fence(self, stream=None):
-        """Make `stream` (default: current) wait on the device for the copies queued so far."""
+        """Make `stream` (default: current) wait on the device for the work queued so far."""
         check(self._lib.pa_swapper_fence(self._h, _stream(stream, self.device)), "pa_swapper_fence")
 
     def sync(self):
@@ -575,8 +582,8 @@ class Swapper:
     def bytes_moved(self):
         """(bytes of completed swap-outs, bytes of completed swap-ins)."""
         o, i = C.c_int64(), C.c_int64()
-        check(self._lib.pa_swapper_info(self._h, None, None, None, None, C.byref(o), C.byref(i)),
-              "pa_swapper_info")
+        check(self._lib.pa_swapper_info(self._h, None, None, None, None, None, C.byref(o),
+                                        C.byref(i)), "pa_swapper_info")
         return o.value, i.value
 
     def host_frames(self) -> np.ndarray:

@@ -535,6 +535,16 @@ pa_status pa_bm_attach_host_pool(pa_bm* bm, int32_t num_frames) {
   return bm->host_pool ? PA_OK : PA_ERR_INVALID_ARG;
 }
 
+pa_status pa_bm_detach_host_pool(pa_bm* bm) {
+  if (!bm) return PA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(bm->mu);
+  if (!bm->host_pool || bm->host_pool->num_free() != bm->host_pool->num_frames)
+    return PA_ERR_INVALID_ARG;
+  delete bm->host_pool;
+  bm->host_pool = nullptr;
+  return PA_OK;
+}
+
 int32_t pa_bm_host_frames_free(const pa_bm* bm) {
   if (!bm) return -1;
   std::lock_guard<std::mutex> lk(bm->mu);

@@ -952,7 +952,7 @@ static pa_status block_move(int mode, const char* name, const pa_geom* g, void* 
                      (char*)k_pool,                                                         \
                      (char*)v_pool, (char*)staging, PtrIds{ids_a},                          \
                      PtrIds{mode == 0 ? ids_b : ids_a},                                     \
-                     g->num_layers, g->num_blocks, run)
+                     g->num_layers, g->num_blocks, run, runs)
 #define PA_MOVE_MODE(M)                                            \
   do {                                                             \
     if (run % 16 == 0) PA_MOVE(M, u32x4);                          \

@@ -11,11 +11,14 @@
 // and the entries point at the new blocks once it has completed.
 //
 // A block is not contiguous in the pool (each layer's K and V live in their own
-// region), so each chunk of blocks is first packed into a device staging buffer
-// by a gather kernel (one work-group per 32 KiB run), then moved by one DMA
-// copy into the run of host frames; the way back is one DMA copy per run of
-// consecutive frames, then a scatter kernel. Everything of one swapper is
-// ordered on its own stream, so one staging buffer serves every chunk.
+// region), so each chunk of blocks is packed into a device staging buffer by a
+// gather kernel and moved by one DMA copy into the run of host frames; the way
+// back is one DMA copy per run of consecutive frames, then a scatter kernel.
+// Two staging buffers alternate between a kernel stream and a DMA stream, so
+// the gather of chunk k+1 runs while chunk k crosses the host link. The gather
+// and scatter use only a few work-groups: they have to keep ahead of the link
+// (tens of GB/s), not run at HBM speed, and the rest of the GPU stays with the
+// decode that the migration is meant to hide behind.
 
 #include <hip/hip_runtime.h>
 
@@ -34,6 +37,11 @@
 
 using namespace pa_detail;
 
+// Work-groups of one gather / scatter launch. Too few and the launch waits for
+// CU slots behind decode, stalling the link; 512 keeps the link at full rate
+// while decode is running.
+constexpr int32_t kDefaultMoveWgs = 512;
+
 struct pa_swapper {
   pa_geom g{};
   pa_bm* bm = nullptr;
@@ -41,14 +49,20 @@ struct pa_swapper {
   void* v_pool = nullptr;
   int32_t num_frames = 0;
   int32_t chunk_blocks = 0;
+  int32_t move_wgs = 0;
+  bool direct = false;      // strided DMA straight from / to the pool, no staging
   int64_t frame_bytes = 0;  // one block: 2 * L runs
   int64_t run_bytes = 0;    // one (layer, K-or-V) run of a block
   char* host = nullptr;     // pinned, num_frames * frame_bytes
-  char* staging = nullptr;  // device, chunk_blocks * frame_bytes
-  hipStream_t stream = nullptr;
-  hipEvent_t after = nullptr;  // marks the caller's stream before a migration
-  hipEvent_t done = nullptr;   // marks the copy stream for pa_swapper_fence
-  std::mutex issue_mu;         // one issuing thread at a time
+  char* staging[2] = {nullptr, nullptr};  // device, chunk_blocks * frame_bytes each
+  hipStream_t kstream = nullptr;          // gather / scatter kernels
+  hipStream_t dstream = nullptr;          // DMA copies over the host link
+  hipEvent_t full[2] = {nullptr, nullptr};   // staging[b] written by its producer
+  hipEvent_t empty[2] = {nullptr, nullptr};  // staging[b] drained by its consumer
+  hipEvent_t after = nullptr;   // marks the caller's stream before a migration
+  hipEvent_t done[2] = {nullptr, nullptr};   // marks both streams for pa_swapper_fence
+  int next_buf = 0;             // staging buffers alternate across chunks and migrations
+  std::mutex issue_mu;          // one issuing thread at a time
   std::atomic<int32_t> pending{0};
   std::atomic<int32_t> error{PA_OK};
   std::atomic<int64_t> bytes_out{0};
@@ -58,8 +72,9 @@ struct pa_swapper {
 namespace {
 
 // The completion step of one migration, run by the HIP runtime on its
-// host-function thread once everything queued before it on the copy stream has
-// finished. It makes no HIP calls.
+// host-function thread once the migration's last copy or kernel has finished
+// (every earlier chunk precedes it through stream order and the hand-over
+// events). It makes no HIP calls.
 struct Job {
   pa_swapper* s;
   int32_t seq;
@@ -82,46 +97,83 @@ void finish_job(void* p) {
   s->pending.fetch_sub(1);
 }
 
-// Gather (MODE 1) or scatter (MODE 2) of blocks ids[0..m) against staging frames
-// 0..m-1, in launches of at most kArgIds ids carried in the kernel arguments.
+// Gather (MODE 1) or scatter (MODE 2) of blocks ids[0..m) against staging
+// frames 0..m-1 of `stg` on the kernel stream, in launches of at most kArgIds
+// ids carried in the kernel arguments.
 template <int MODE>
-bool move_chunk(pa_swapper* s, const int32_t* ids, int32_t m) {
-  ProfScope ps(MODE == 1 ? "swap_gather" : "swap_scatter", s->stream);
+bool move_chunk(pa_swapper* s, char* stg, const int32_t* ids, int32_t m) {
+  ProfScope ps(MODE == 1 ? "swap_gather" : "swap_scatter", s->kstream);
   for (int32_t a = 0; a < m; a += kArgIds) {
     const int32_t c = std::min(kArgIds, m - a);
     ArgIds arg;
     for (int32_t k = 0; k < kArgIds; ++k) arg.v[k] = k < c ? ids[a + k] : -1;
-    const dim3 grid((unsigned)((int64_t)c * s->g.num_layers * 2)), block(256);
-    char* stg = s->staging + (int64_t)a * s->frame_bytes;
+    const int64_t runs = (int64_t)c * s->g.num_layers * 2;
+    const dim3 grid((unsigned)std::min<int64_t>(runs, s->move_wgs)), block(256);
+    char* dst = stg + (int64_t)a * s->frame_bytes;
     if (s->run_bytes % 16 == 0)
       hipLaunchKernelGGL((block_move_kernel<MODE, u32x4, ArgIds, NoIds>), grid, block, 0,
-                         s->stream, (char*)s->k_pool, (char*)s->v_pool, stg, arg, NoIds{},
-                         s->g.num_layers, s->g.num_blocks, s->run_bytes);
+                         s->kstream, (char*)s->k_pool, (char*)s->v_pool, dst, arg, NoIds{},
+                         s->g.num_layers, s->g.num_blocks, s->run_bytes, runs);
     else if (s->run_bytes % 4 == 0)
       hipLaunchKernelGGL((block_move_kernel<MODE, uint32_t, ArgIds, NoIds>), grid, block, 0,
-                         s->stream, (char*)s->k_pool, (char*)s->v_pool, stg, arg, NoIds{},
-                         s->g.num_layers, s->g.num_blocks, s->run_bytes);
+                         s->kstream, (char*)s->k_pool, (char*)s->v_pool, dst, arg, NoIds{},
+                         s->g.num_layers, s->g.num_blocks, s->run_bytes, runs);
     else
       hipLaunchKernelGGL((block_move_kernel<MODE, uint16_t, ArgIds, NoIds>), grid, block, 0,
-                         s->stream, (char*)s->k_pool, (char*)s->v_pool, stg, arg, NoIds{},
-                         s->g.num_layers, s->g.num_blocks, s->run_bytes);
+                         s->kstream, (char*)s->k_pool, (char*)s->v_pool, dst, arg, NoIds{},
+                         s->g.num_layers, s->g.num_blocks, s->run_bytes, runs);
     if (hipGetLastError() != hipSuccess) return false;
   }
   return true;
 }
 
+// Next staging buffer: `producer` waits until its previous consumer is done.
+int take_buffer(pa_swapper* s, hipStream_t producer, bool* ok) {
+  const int b = s->next_buf;
+  s->next_buf ^= 1;
+  *ok = *ok && hipStreamWaitEvent(producer, s->empty[b], 0) == hipSuccess;
+  return b;
+}
+
+// Hand buffer b from the producer stream to the consumer stream.
+bool hand_over(pa_swapper* s, int b, hipStream_t producer, hipStream_t consumer) {
+  return hipEventRecord(s->full[b], producer) == hipSuccess &&
+         hipStreamWaitEvent(consumer, s->full[b], 0) == hipSuccess;
+}
+
+// The stream that touches the pool (kernel stream, or the DMA stream in direct
+// mode) follows the caller's stream.
 bool order_after(pa_swapper* s, void* after_stream) {
   if (!after_stream) return true;
   return hipEventRecord(s->after, (hipStream_t)after_stream) == hipSuccess &&
-         hipStreamWaitEvent(s->stream, s->after, 0) == hipSuccess;
+         hipStreamWaitEvent(s->direct ? s->dstream : s->kstream, s->after, 0) == hipSuccess;
 }
 
-// Queue the completion step; on failure the migration stays in flight and the
-// swapper reports PA_ERR_HIP from then on.
-pa_status queue_finish(pa_swapper* s, Job* job, bool issued_ok) {
+// Direct mode: block `phys` <-> frame `frame` as two strided copies (K, V), each
+// L rows of one run: pool pitch N * run, frame pitch 2 * run (the staging layout).
+bool direct_copy(pa_swapper* s, int32_t phys, int32_t frame, bool to_host) {
+  const size_t run = (size_t)s->run_bytes, pitch = (size_t)s->g.num_blocks * run;
+  char* f = s->host + (int64_t)frame * s->frame_bytes;
+  char* pools[2] = {(char*)s->k_pool, (char*)s->v_pool};
+  for (int kv = 0; kv < 2; ++kv) {
+    char* p = pools[kv] + (size_t)phys * run;
+    char* h = f + kv * run;
+    hipError_t e = to_host ? hipMemcpy2DAsync(h, 2 * run, p, pitch, run, s->g.num_layers,
+                                              hipMemcpyDeviceToHost, s->dstream)
+                           : hipMemcpy2DAsync(p, pitch, h, 2 * run, run, s->g.num_layers,
+                                              hipMemcpyHostToDevice, s->dstream);
+    if (e != hipSuccess) return false;
+  }
+  return true;
+}
+
+// Queue the completion step behind the migration's last operation, on `last`;
+// on failure the migration stays in flight and the swapper reports PA_ERR_HIP
+// from then on.
+pa_status queue_finish(pa_swapper* s, hipStream_t last, Job* job, bool issued_ok) {
   if (issued_ok) {
     s->pending.fetch_add(1);
-    if (hipLaunchHostFunc(s->stream, finish_job, job) == hipSuccess) return PA_OK;
+    if (hipLaunchHostFunc(last, finish_job, job) == hipSuccess) return PA_OK;
     s->pending.fetch_sub(1);
   }
   delete job;
@@ -130,12 +182,18 @@ pa_status queue_finish(pa_swapper* s, Job* job, bool issued_ok) {
 }
 
 void release(pa_swapper* s) {
-  if (s->stream) (void)hipStreamSynchronize(s->stream);
+  if (s->kstream) (void)hipStreamSynchronize(s->kstream);
+  if (s->dstream) (void)hipStreamSynchronize(s->dstream);
   if (s->host) (void)hipHostFree(s->host);
-  if (s->staging) (void)hipFree(s->staging);
+  for (int b = 0; b < 2; ++b) {
+    if (s->staging[b]) (void)hipFree(s->staging[b]);
+    if (s->full[b]) (void)hipEventDestroy(s->full[b]);
+    if (s->empty[b]) (void)hipEventDestroy(s->empty[b]);
+    if (s->done[b]) (void)hipEventDestroy(s->done[b]);
+  }
   if (s->after) (void)hipEventDestroy(s->after);
-  if (s->done) (void)hipEventDestroy(s->done);
-  if (s->stream) (void)hipStreamDestroy(s->stream);
+  if (s->kstream) (void)hipStreamDestroy(s->kstream);
+  if (s->dstream) (void)hipStreamDestroy(s->dstream);
   delete s;
 }
 
@@ -144,15 +202,19 @@ void release(pa_swapper* s) {
 extern "C" {
 
 pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_pool,
-                            int32_t num_frames, int32_t chunk_blocks, pa_swapper** out) {
+                            int32_t num_frames, const pa_swap_opts* opts, pa_swapper** out) {
   if (!out) return PA_ERR_INVALID_ARG;
   *out = nullptr;
-  if (!geom_ok(g) || !bm || !k_pool || !v_pool || num_frames <= 0 || chunk_blocks < 0)
+  int32_t chunk_blocks = opts ? opts->chunk_blocks : 0;
+  const int32_t move_wgs = opts && opts->move_wgs ? opts->move_wgs : kDefaultMoveWgs;
+  const bool direct = opts && opts->direct;
+  if (!geom_ok(g) || !bm || !k_pool || !v_pool || num_frames <= 0 || chunk_blocks < 0 ||
+      move_wgs < 0)
     return PA_ERR_INVALID_ARG;
   const int64_t run = (int64_t)g->num_kv_heads * g->block_size * g->head_dim * esize(g);
   const int64_t frame = 2 * (int64_t)g->num_layers * run;
-  if (chunk_blocks == 0)  // about 256 MiB of staging, at least one block
-    chunk_blocks = (int32_t)std::max<int64_t>(1, std::min<int64_t>(4096, (256ll << 20) / frame));
+  if (chunk_blocks == 0)  // about 64 MiB per staging buffer, at least one block
+    chunk_blocks = (int32_t)std::max<int64_t>(1, std::min<int64_t>(4096, (64ll << 20) / frame));
   pa_swapper* s = new (std::nothrow) pa_swapper();
   if (!s) return PA_ERR_INVALID_ARG;
   s->g = *g;
@@ -161,14 +223,21 @@ pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_p
   s->v_pool = v_pool;
   s->num_frames = num_frames;
   s->chunk_blocks = chunk_blocks;
+  s->move_wgs = move_wgs;
+  s->direct = direct;
   s->frame_bytes = frame;
   s->run_bytes = run;
-  bool ok = hipStreamCreateWithFlags(&s->stream, hipStreamNonBlocking) == hipSuccess &&
+  bool ok = hipStreamCreateWithFlags(&s->kstream, hipStreamNonBlocking) == hipSuccess &&
+            hipStreamCreateWithFlags(&s->dstream, hipStreamNonBlocking) == hipSuccess &&
             hipEventCreateWithFlags(&s->after, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&s->done, hipEventDisableTiming) == hipSuccess &&
-            hipMalloc((void**)&s->staging, (size_t)chunk_blocks * frame) == hipSuccess &&
             hipHostMalloc((void**)&s->host, (size_t)num_frames * frame, hipHostMallocDefault) ==
                 hipSuccess;
+  for (int b = 0; ok && b < 2; ++b)
+    ok = hipEventCreateWithFlags(&s->full[b], hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&s->empty[b], hipEventDisableTiming) == hipSuccess &&
+         hipEventCreateWithFlags(&s->done[b], hipEventDisableTiming) == hipSuccess &&
+         (direct || hipMalloc((void**)&s->staging[b], (size_t)chunk_blocks * frame) == hipSuccess) &&
+         hipEventRecord(s->empty[b], s->kstream) == hipSuccess;   // both start drained
   if (!ok) {
     release(s);
     return PA_ERR_HIP;
@@ -184,7 +253,9 @@ pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_p
 
 pa_status pa_swapper_sync(pa_swapper* s) {
   if (!s) return PA_ERR_INVALID_ARG;
-  if (hipStreamSynchronize(s->stream) != hipSuccess) return PA_ERR_HIP;
+  if (hipStreamSynchronize(s->kstream) != hipSuccess ||
+      hipStreamSynchronize(s->dstream) != hipSuccess)
+    return PA_ERR_HIP;
   // The stream has drained; its host functions may still be finishing.
   const auto t0 = std::chrono::steady_clock::now();
   while (s->pending.load() > 0) {
@@ -197,6 +268,7 @@ pa_status pa_swapper_sync(pa_swapper* s) {
 pa_status pa_swapper_destroy(pa_swapper* s) {
   if (!s) return PA_ERR_INVALID_ARG;
   pa_status st = pa_swapper_sync(s);
+  (void)pa_bm_detach_host_pool(s->bm);   // kept while entries hold frames
   release(s);
   return st;
 }
@@ -211,18 +283,26 @@ pa_status pa_swap_out_async(pa_swapper* s, int32_t seq, const int32_t* logical, 
   pa_status st = pa_bm_swap_out_begin(s->bm, seq, logical, n, phys.data(), &first);
   if (st != PA_OK) return st;
   Job* job = new (std::nothrow) Job{s, seq, true, std::vector<int32_t>(logical, logical + n)};
-  bool ok = job && order_after(s, after_stream);
-  for (int32_t c0 = 0; ok && c0 < n; c0 += s->chunk_blocks) {
-    const int32_t m = std::min(s->chunk_blocks, n - c0);
-    ok = move_chunk<1>(s, phys.data() + c0, m) &&
-         hipMemcpyAsync(s->host + (int64_t)(first + c0) * s->frame_bytes, s->staging,
-                        (size_t)m * s->frame_bytes, hipMemcpyDeviceToHost, s->stream) == hipSuccess;
-  }
   if (!job) {
-    s->error.store(PA_ERR_HIP);
+    s->error.store(PA_ERR_HIP);   // the reservation stands; nothing was queued
     return PA_ERR_HIP;
   }
-  return queue_finish(s, job, ok);
+  bool ok = order_after(s, after_stream);
+  if (s->direct) {
+    for (int32_t k = 0; ok && k < n; ++k) ok = direct_copy(s, phys[k], first + k, true);
+    return queue_finish(s, s->dstream, job, ok);
+  }
+  for (int32_t c0 = 0; ok && c0 < n; c0 += s->chunk_blocks) {
+    const int32_t m = std::min(s->chunk_blocks, n - c0);
+    const int b = take_buffer(s, s->kstream, &ok);
+    ok = ok && move_chunk<1>(s, s->staging[b], phys.data() + c0, m) &&
+         hand_over(s, b, s->kstream, s->dstream) &&
+         hipMemcpyAsync(s->host + (int64_t)(first + c0) * s->frame_bytes, s->staging[b],
+                        (size_t)m * s->frame_bytes, hipMemcpyDeviceToHost, s->dstream) ==
+             hipSuccess &&
+         hipEventRecord(s->empty[b], s->dstream) == hipSuccess;
+  }
+  return queue_finish(s, s->dstream, job, ok);
 }
 
 pa_status pa_swap_in_async(pa_swapper* s, int32_t seq, const int32_t* logical, int32_t n,
@@ -234,43 +314,54 @@ pa_status pa_swap_in_async(pa_swapper* s, int32_t seq, const int32_t* logical, i
   pa_status st = pa_bm_swap_in_begin(s->bm, seq, logical, n, phys.data(), frames.data());
   if (st != PA_OK) return st;
   Job* job = new (std::nothrow) Job{s, seq, false, std::vector<int32_t>(logical, logical + n)};
-  bool ok = job && order_after(s, after_stream);
+  if (!job) {
+    s->error.store(PA_ERR_HIP);   // the reservation stands; nothing was queued
+    return PA_ERR_HIP;
+  }
+  bool ok = order_after(s, after_stream);
+  if (s->direct) {
+    for (int32_t k = 0; ok && k < n; ++k) ok = direct_copy(s, phys[k], frames[k], false);
+    return queue_finish(s, s->dstream, job, ok);
+  }
   for (int32_t c0 = 0; ok && c0 < n; c0 += s->chunk_blocks) {
     const int32_t m = std::min(s->chunk_blocks, n - c0);
+    const int b = take_buffer(s, s->dstream, &ok);
     for (int32_t k = 0; ok && k < m;) {  // one copy per run of consecutive frames
       int32_t e = k + 1;
       while (e < m && frames[c0 + e] == frames[c0 + e - 1] + 1) ++e;
-      ok = hipMemcpyAsync(s->staging + (int64_t)k * s->frame_bytes,
+      ok = hipMemcpyAsync(s->staging[b] + (int64_t)k * s->frame_bytes,
                           s->host + (int64_t)frames[c0 + k] * s->frame_bytes,
                           (size_t)(e - k) * s->frame_bytes, hipMemcpyHostToDevice,
-                          s->stream) == hipSuccess;
+                          s->dstream) == hipSuccess;
       k = e;
     }
-    ok = ok && move_chunk<2>(s, phys.data() + c0, m);
+    ok = ok && hand_over(s, b, s->dstream, s->kstream) &&
+         move_chunk<2>(s, s->staging[b], phys.data() + c0, m) &&
+         hipEventRecord(s->empty[b], s->kstream) == hipSuccess;
   }
-  if (!job) {
-    s->error.store(PA_ERR_HIP);
-    return PA_ERR_HIP;
-  }
-  return queue_finish(s, job, ok);
+  return queue_finish(s, s->kstream, job, ok);
 }
 
 pa_status pa_swapper_fence(pa_swapper* s, void* stream) {
   if (!s) return PA_ERR_INVALID_ARG;
-  return hipEventRecord(s->done, s->stream) == hipSuccess &&
-                 hipStreamWaitEvent((hipStream_t)stream, s->done, 0) == hipSuccess
-             ? PA_OK
-             : PA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(s->issue_mu);
+  hipStream_t own[2] = {s->kstream, s->dstream};
+  for (int b = 0; b < 2; ++b)
+    if (hipEventRecord(s->done[b], own[b]) != hipSuccess ||
+        hipStreamWaitEvent((hipStream_t)stream, s->done[b], 0) != hipSuccess)
+      return PA_ERR_HIP;
+  return PA_OK;
 }
 
 int32_t pa_swapper_pending(const pa_swapper* s) { return s ? s->pending.load() : -1; }
 
-pa_status pa_swapper_info(const pa_swapper* s, void** host_frames, void** stream,
-                          int64_t* frame_bytes, int32_t* chunk_blocks, int64_t* bytes_out,
-                          int64_t* bytes_in) {
+pa_status pa_swapper_info(const pa_swapper* s, void** host_frames, void** kernel_stream,
+                          void** dma_stream, int64_t* frame_bytes, int32_t* chunk_blocks,
+                          int64_t* bytes_out, int64_t* bytes_in) {
   if (!s) return PA_ERR_INVALID_ARG;
   if (host_frames) *host_frames = s->host;
-  if (stream) *stream = s->stream;
+  if (kernel_stream) *kernel_stream = s->kstream;
+  if (dma_stream) *dma_stream = s->dstream;
   if (frame_bytes) *frame_bytes = s->frame_bytes;
   if (chunk_blocks) *chunk_blocks = s->chunk_blocks;
   if (bytes_out) *bytes_out = s->bytes_out.load();

@@ -21,6 +21,11 @@ Shapes follow the workloads the pages describe:
   512-token chunks ("KV Cache Management", section "Chunked prefill
   mechanics", Figure 8): the batch holds chunk k = 1..4 of different prompts,
   i.e. histories of 0, 512, 1,024 and 1,536 cached tokens.
+* ``offload_overlap`` -- the ``gqa70b_32k`` decode batch keeps stepping while one
+  more 16,384-token trajectory (the 70B example of "KV Cache Management",
+  section "Retain, Evict, Recompute, or Offload", Figure 10) moves to pinned
+  host memory and back on a copy stream of its own (same page, section
+  "Asynchronous paged swapping").
 
 Seeds: workload k (1-based, in the order above) uses master seed 8300 + k.
 """
@@ -58,6 +63,8 @@ class Workload:
     offload_chunk_blocks: int = 0
     # chunked-prefill workload: prompt length (length_max) cut into chunks
     chunk_len: int = 0
+    # overlapped-offload workload: tokens of the trajectory that migrates
+    mover_len: int = 0
     notes: str = ""
     extra: Dict[str, float] = field(default_factory=dict)
 
@@ -114,6 +121,13 @@ CONFIGS = [
         head_dim=128, block_size=16, dtype="bf16", num_blocks=4096, num_seqs=16,
         length_kind="prefill", length_min=2048, length_max=2048, chunk_len=512,
         notes="16 prompts of 2,048 tokens in 512-token chunks; sequence i runs chunk (i mod 4) + 1",
+    ),
+    Workload(
+        name="offload_overlap", index=7, num_layers=80, num_q_heads=64, num_kv_heads=8,
+        head_dim=128, block_size=16, dtype="bf16", num_blocks=32768 + 1024, num_seqs=16,
+        length_kind="fixed", length_min=32768, length_max=32768, mover_len=16384,
+        offload_chunk_blocks=64,
+        notes="gqa70b_32k decode batch + one 16,384-token trajectory swapped out and back",
     ),
 ]
 

@@ -33,7 +33,8 @@ class Setup:
     """Pools with seeded values, an oracle manager and the library's manager
     built from the same free order and the same appends, and a swapper."""
 
-    def __init__(self, dtype, L, N, Hkv, d, B, lengths, seed, frames, chunk):
+    def __init__(self, dtype, L, N, Hkv, d, B, lengths, seed, frames, chunk, move_wgs=0,
+                 direct=False):
         self.dtype, self.L, self.N, self.Hkv, self.d, self.B = dtype, L, N, Hkv, d, B
         self.geom = pk.Geometry(L, Hkv, d, B, N, dtype)
         self.kp = gen.normal_values(seed + 1, olayout.k_pool_shape(L, N, Hkv, B, d), dtype)
@@ -50,7 +51,7 @@ class Setup:
             self.ref.append(s, int(n))
             self.seqs.append(s)
         self.K, self.V = to_dev(self.kp, dtype), to_dev(self.vp, dtype)
-        self.sw = pk.Swapper(self.geom, self.bm, self.K, self.V, frames, chunk)
+        self.sw = pk.Swapper(self.geom, self.bm, self.K, self.V, frames, chunk, move_wgs, direct)
 
     def same_state(self):
         assert list(self.ref.free) == self.bm.free_list()
@@ -93,21 +94,26 @@ class Setup:
 
 
 ROUND_TRIP = [
-    # name, dtype, L, N, Hkv, d, B, lengths, frames, chunk
-    ("bf16_d128", "bf16", 2, 64, 2, 128, 16, [300, 170, 40], 40, 3),
-    ("bf16_one_chunk", "bf16", 3, 48, 1, 64, 16, [400], 32, 0),
-    ("f32_d64", "f32", 2, 40, 2, 64, 8, [100, 60], 24, 5),
-    ("bf16_odd_run", "bf16", 3, 64, 1, 36, 1, [50, 9], 40, 7),        # run of 72 bytes
-    ("bf16_tiny_run", "bf16", 1, 64, 1, 5, 3, [70, 20], 40, 4),       # run of 30 bytes
+    # name, dtype, L, N, Hkv, d, B, lengths, frames, chunk, work-groups per move launch
+    ("bf16_d128", "bf16", 2, 64, 2, 128, 16, [300, 170, 40], 40, 3, 0),
+    ("bf16_one_wg", "bf16", 2, 64, 2, 128, 16, [300, 170, 40], 40, 4, 1),
+    ("bf16_one_chunk", "bf16", 3, 48, 1, 64, 16, [400], 32, 0, 100000),
+    ("f32_d64", "f32", 2, 40, 2, 64, 8, [100, 60], 24, 5, 7),
+    ("bf16_odd_run", "bf16", 3, 64, 1, 36, 1, [50, 9], 40, 7, 0),       # run of 72 bytes
+    ("bf16_tiny_run", "bf16", 1, 64, 1, 5, 3, [70, 20], 40, 4, 0),      # run of 30 bytes
+    # direct mode: strided DMA between pool and frames (the work-group column is unused)
+    ("direct_bf16_d128", "bf16", 2, 64, 2, 128, 16, [300, 170, 40], 40, 0, -1),
+    ("direct_f32_d64", "f32", 2, 40, 2, 64, 8, [100, 60], 24, 0, -1),
+    ("direct_tiny_run", "bf16", 1, 64, 1, 5, 3, [70, 20], 40, 0, -1),
 ]
 
 
 @pytest.mark.parametrize("case", ROUND_TRIP, ids=[c[0] for c in ROUND_TRIP])
 def test_round_trip_bit_exact(case):
     need_gpu()
-    name, dtype, L, N, Hkv, d, B, lengths, frames, chunk = case
+    name, dtype, L, N, Hkv, d, B, lengths, frames, chunk, wgs = case
     print_case(test="swap_round_trip", case=name)
-    su = Setup(dtype, L, N, Hkv, d, B, lengths, 830, frames, chunk)
+    su = Setup(dtype, L, N, Hkv, d, B, lengths, 830, frames, chunk, max(wgs, 0), wgs < 0)
     rng = np.random.default_rng(31)
     s = su.seqs[0]
     nb = len(su.ref.table(s))
@@ -139,13 +145,14 @@ def test_round_trip_bit_exact(case):
     su.sw.close()
 
 
-def test_noncontiguous_frames_and_wide_chunks():
+@pytest.mark.parametrize("direct", [False, True], ids=["staged", "direct"])
+def test_noncontiguous_frames_and_wide_chunks(direct):
     """Two migrations out, one back that interleaves their frames (one copy per
     run of consecutive frames), and chunks of more than 256 blocks (several
     kernel launches per chunk)."""
     need_gpu()
-    print_case(test="swap_wide_chunks")
-    su = Setup("f32", 1, 900, 1, 64, 16, [16 * 620], 831, 700, 300)
+    print_case(test="swap_wide_chunks", direct=direct)
+    su = Setup("f32", 1, 900, 1, 64, 16, [16 * 620], 831, 700, 300, direct=direct)
     s = su.seqs[0]
     a, b = list(range(0, 300)), list(range(300, 610))
     before = {lb: su.block_bytes(su.kp, su.vp, su.ref.table(s)[lb]) for lb in range(620)}
@@ -187,13 +194,14 @@ def _decode(su, seqs, q, stream=None, tabs=None):
     return out
 
 
-def test_decode_overlapping_migration_is_unchanged():
-    """Decode runs on the compute stream while the swapper's stream moves one
+@pytest.mark.parametrize("direct", [False, True], ids=["staged", "direct"])
+def test_decode_overlapping_migration_is_unchanged(direct):
+    """Decode runs on the compute stream while the swapper's streams move one
     sequence out and back: every output equals the output with no migration."""
     need_gpu()
-    print_case(test="swap_overlap_decode")
+    print_case(test="swap_overlap_decode", direct=direct)
     lengths = [2000, 1500, 3000, 700, 2400]
-    su = Setup("bf16", 2, 1400, 2, 128, 16, lengths, 832, 400, 32)
+    su = Setup("bf16", 2, 1400, 2, 128, 16, lengths, 832, 400, 32, direct=direct)
     mover, others = su.seqs[2], [s for s in su.seqs if s != su.seqs[2]]
     Hq = 16
     q_o = to_dev(gen.normal_values(9, (len(others), Hq, 128), "bf16"), "bf16")
@@ -250,7 +258,7 @@ def test_errors_change_nothing():
     with pytest.raises(pk.PagedKVError):
         su.sw.swap_out(s, [])
     with pytest.raises(pk.PagedKVError):                 # the manager already has a host pool
-        pk.Swapper(su.geom, su.bm, su.K, su.V, 4)
+        pk.Swapper(su.geom, su.bm, su.K, su.V, 6)
     assert su.sw.pending() == 0
     assert snap() == before
     su.sw.swap_out(s, [1, 2])
@@ -261,3 +269,31 @@ def test_errors_change_nothing():
     su.ref.swap_out_finish(s, [1, 2])
     su.same_state()
     su.sw.close()
+
+
+def test_swapper_lifetime_and_options():
+    """Destroying a swapper detaches its pool when no frame is in use, so a new
+    one (other options) can take over; while an entry holds a frame it stays."""
+    need_gpu()
+    print_case(test="swap_lifetime")
+    su = Setup("bf16", 2, 40, 2, 64, 16, [16 * 12], 834, 16, 0)
+    s = su.seqs[0]
+    before = {lb: su.block_bytes(su.kp, su.vp, su.ref.table(s)[lb]) for lb in range(12)}
+    su.sw.close()
+    su.sw = pk.Swapper(su.geom, su.bm, su.K, su.V, 16, chunk_blocks=5, move_wgs=3)
+    assert su.sw.chunk_blocks == 5
+    su.swap_out(s, list(range(12)))
+    su.sw.sync()
+    su.ref.swap_out_finish(s, list(range(12)))
+    with pytest.raises(pk.PagedKVError):
+        su.bm.detach_host_pool()                         # 12 frames in use
+    su.poison_free_blocks()
+    su.swap_in(s, list(range(11, -1, -1)))
+    su.sw.sync()
+    su.ref.swap_in_finish(s, list(range(11, -1, -1)))
+    su.same_state()
+    K, V = to_host(su.K, "bf16"), to_host(su.V, "bf16")
+    for lb in range(12):
+        assert np.array_equal(su.block_bytes(K, V, su.bm.table(s)[lb]), before[lb])
+    su.sw.close()
+    assert su.bm.host_frames_free() == -1                # detached
