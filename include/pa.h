@@ -362,7 +362,7 @@ pa_status pa_bm_swap_in_finish(pa_bm* bm, int32_t seq, const int32_t* logical, i
 /* Moves blocks between the device pool and a pinned host frame pool in the
  * background, following "KV Cache Management", section "Asynchronous paged
  * swapping" (copy stream, pinned frames, completion callback that retags the
- * table) and its pipelined chunked reload. The swapper owns a page-locked host
+ * table) and its paragraph on the pipelined chunked reload. The swapper owns a page-locked host
  * buffer of num_frames frames (frame f at byte f * frame_bytes, one block in the
  * staging layout of pa_gather_blocks), two device staging buffers of
  * chunk_blocks blocks, and two streams of its own (default priority): one for

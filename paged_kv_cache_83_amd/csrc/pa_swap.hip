@@ -6,9 +6,10 @@
 // contiguous run; the copy is queued on a dedicated copy stream so that it
 // overlaps compute; when it completes, a host callback retags the entries as
 // host-resident and returns the vacated blocks to the free queue. The same
-// section (and "Speculative prefetch and pipelined chunked reload") gives the
-// return path: fresh blocks are reserved, the copy back is queued in chunks,
-// and the entries point at the new blocks once it has completed.
+// section gives the return path (its paragraphs on speculative prefetch and on
+// the pipelined chunked reload): fresh blocks are reserved, the copy back is
+// queued in chunks, and the entries point at the new blocks once it has
+// completed.
 //
 // A block is not contiguous in the pool (each layer's K and V live in their own
 // region), so each chunk of blocks is packed into a device staging buffer by a
@@ -54,6 +55,7 @@ struct pa_swapper {
   int64_t frame_bytes = 0;  // one block: 2 * L runs
   int64_t run_bytes = 0;    // one (layer, K-or-V) run of a block
   char* host = nullptr;     // pinned, num_frames * frame_bytes
+  char* host_dev = nullptr; // the same buffer as the device addresses it
   char* staging[2] = {nullptr, nullptr};  // device, chunk_blocks * frame_bytes each
   hipStream_t kstream = nullptr;          // gather / scatter kernels
   hipStream_t dstream = nullptr;          // DMA copies over the host link
@@ -133,6 +135,16 @@ int take_buffer(pa_swapper* s, hipStream_t producer, bool* ok) {
   s->next_buf ^= 1;
   *ok = *ok && hipStreamWaitEvent(producer, s->empty[b], 0) == hipSuccess;
   return b;
+}
+
+// One contiguous copy over the host link on the DMA stream. Both sides are
+// given as device addresses (the pinned buffer's device view) with the copy kind
+// that asks for the DMA engines rather than compute units, so that the copy
+// takes no CU slots from the decode running beside it. The ROCm 7.2 runtime
+// honours it; the HIP runtime bundled with PyTorch 2.10 (ROCm 7.0) still serves
+// device-to-host copies with a blit kernel in a torch process (measured).
+bool link_copy(pa_swapper* s, void* dst, const void* src, size_t bytes) {
+  return hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDeviceNoCU, s->dstream) == hipSuccess;
 }
 
 // Hand buffer b from the producer stream to the consumer stream.
@@ -231,7 +243,8 @@ pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_p
             hipStreamCreateWithFlags(&s->dstream, hipStreamNonBlocking) == hipSuccess &&
             hipEventCreateWithFlags(&s->after, hipEventDisableTiming) == hipSuccess &&
             hipHostMalloc((void**)&s->host, (size_t)num_frames * frame, hipHostMallocDefault) ==
-                hipSuccess;
+                hipSuccess &&
+            hipHostGetDevicePointer((void**)&s->host_dev, s->host, 0) == hipSuccess;
   for (int b = 0; ok && b < 2; ++b)
     ok = hipEventCreateWithFlags(&s->full[b], hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&s->empty[b], hipEventDisableTiming) == hipSuccess &&
@@ -297,9 +310,8 @@ pa_status pa_swap_out_async(pa_swapper* s, int32_t seq, const int32_t* logical, 
     const int b = take_buffer(s, s->kstream, &ok);
     ok = ok && move_chunk<1>(s, s->staging[b], phys.data() + c0, m) &&
          hand_over(s, b, s->kstream, s->dstream) &&
-         hipMemcpyAsync(s->host + (int64_t)(first + c0) * s->frame_bytes, s->staging[b],
-                        (size_t)m * s->frame_bytes, hipMemcpyDeviceToHost, s->dstream) ==
-             hipSuccess &&
+         link_copy(s, s->host_dev + (int64_t)(first + c0) * s->frame_bytes, s->staging[b],
+                   (size_t)m * s->frame_bytes) &&
          hipEventRecord(s->empty[b], s->dstream) == hipSuccess;
   }
   return queue_finish(s, s->dstream, job, ok);
@@ -329,10 +341,9 @@ pa_status pa_swap_in_async(pa_swapper* s, int32_t seq, const int32_t* logical, i
     for (int32_t k = 0; ok && k < m;) {  // one copy per run of consecutive frames
       int32_t e = k + 1;
       while (e < m && frames[c0 + e] == frames[c0 + e - 1] + 1) ++e;
-      ok = hipMemcpyAsync(s->staging[b] + (int64_t)k * s->frame_bytes,
-                          s->host + (int64_t)frames[c0 + k] * s->frame_bytes,
-                          (size_t)(e - k) * s->frame_bytes, hipMemcpyHostToDevice,
-                          s->dstream) == hipSuccess;
+      ok = link_copy(s, s->staging[b] + (int64_t)k * s->frame_bytes,
+                     s->host_dev + (int64_t)frames[c0 + k] * s->frame_bytes,
+                     (size_t)(e - k) * s->frame_bytes);
       k = e;
     }
     ok = ok && hand_over(s, b, s->dstream, s->kstream) &&
