@@ -251,3 +251,48 @@ def test_mutant_swap_in_leaks_frames(monkeypatch):
     monkeypatch.setattr(obm.BlockManager, "swap_in_finish", _swap_in_finish_keeps_frames)
     _raises(TT.test_migration_follows_the_pages_steps)
     _raises(TT.test_random_migrations_conserve_blocks_and_frames)
+
+
+# ---- FP8 storage ------------------------------------------------------------
+import oracle.fp8 as ofp8  # noqa: E402
+from tests import test_oracle_fp8 as T8  # noqa: E402
+
+encode_orig = ofp8.encode
+scale_orig = ofp8.scale_exponent
+dequant_orig = ofp8.dequantize_vector
+
+
+def _encode_ties_away(values):
+    v = np.asarray(values, dtype=np.float64)
+    codes = encode_orig(v)
+    a = np.abs(v)
+    lo = ofp8.TABLE[codes & 0x7F]
+    # wrong: at an exact midpoint take the larger magnitude instead of the even code
+    nxt = ofp8.TABLE[np.minimum((codes & 0x7F) + 1, 0x7E)]
+    up = (a == (lo + nxt) / 2) & (nxt > lo)          # a tie that went to the smaller code
+    return np.where(up, codes + 1, codes).astype(np.uint8)
+
+
+def _scale_floor_rule(amax):
+    if amax == 0.0:
+        return 0
+    return max(-127, min(127, math.frexp(float(amax))[1] - 9))   # wrong: may overflow 448
+
+
+def _dequant_no_scale(codes, scale_byte):
+    return ofp8.decode(codes)                                      # wrong: scale dropped
+
+
+def test_mutant_fp8_ties_away(monkeypatch):
+    monkeypatch.setattr(ofp8, "encode", _encode_ties_away)
+    _raises(T8.test_encode_matches_torch_including_ties)
+
+
+def test_mutant_fp8_scale_floor(monkeypatch):
+    monkeypatch.setattr(ofp8, "scale_exponent", _scale_floor_rule)
+    _raises(T8.test_scale_rule_brute_force)
+
+
+def test_mutant_fp8_scale_dropped(monkeypatch):
+    monkeypatch.setattr(ofp8, "dequantize_vector", _dequant_no_scale)
+    _raises(T8.test_decode_equals_bf16_oracle_on_representable_values)
