@@ -18,6 +18,10 @@
  *     function" and "Inference Lab increment".
  *   - Block gather/scatter and the host copy: "KV Cache Management", section
  *     "Asynchronous paged swapping".
+ *   - One-byte (FP8) storage: b_elem = 1 in Eq. (1) of "KV Cache Management",
+ *     section "From Context Tokens to KV State". The pages name no format or
+ *     scale; the library uses OCP FP8 E4M3 elements with one power-of-two scale
+ *     per (token, KV head) for K and for V (see PA_FP8 below).
  *
  * ---------------------------------------------------------------------------
  * Memory layout (fixed by this interface)
@@ -37,6 +41,14 @@
  * Staging (gather/scatter): for the i-th listed block, bytes_per_block bytes
  * laid out [L][2][run]: that layer's K run of the block, then its V run, each
  * exactly as stored in the pool.
+ * FP8 pools (PA_FP8) are bytes [L][N][H_kv][B*d + B]: each (layer, block, head)
+ * tile holds the B*d element codes in the same order as above (K: [d/W][B][W],
+ * V: [d][B]) followed by B scale bytes, one per slot. A slot's d values x
+ * (one token of one head) are stored as codes c_j = E4M3(x_j * 2^-e), rounded
+ * to nearest with ties to the even code, and the byte e + 127, where e is the
+ * smallest integer with max_j |x_j| <= 448 * 2^e (clamped to [-127, 127]; e = 0
+ * when all x_j are 0); the stored values are E4M3(c_j) * 2^e. Queries, outputs
+ * and new K/V rows of an FP8 pool are bf16.
  *
  * ---------------------------------------------------------------------------
  * Conventions
@@ -56,7 +68,8 @@
  *   their own memory accesses against out-of-range ids and lengths (an
  *   out-of-range slot is skipped, an out-of-range block id is read as block 0,
  *   a length is clamped), so bad indices give wrong numbers, never a fault.
- * Dtypes: q, out and both pools share one dtype; arithmetic is fp32.
+ * Dtypes: q, out and both pools share one dtype (bf16 for q, out and new rows
+ *   of an FP8 pool); arithmetic is fp32.
  */
 #ifndef PA_H_
 #define PA_H_
@@ -80,7 +93,8 @@ typedef enum {
   PA_ERR_OUT_OF_FRAMES = -8  /* the host frame pool has no free run long enough  */
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* PA_FP8: E4M3 codes with per-(token, head) power-of-two scales (layout above). */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_FP8 = 2 } pa_dtype;
 
 /* Pool geometry: L layers, H_kv KV heads of dimension d, blocks of B slots,
  * N physical blocks, element type dtype (a pa_dtype value). */
@@ -102,11 +116,13 @@ int32_t pa_version(void);
  * tp == 1 gives Eq. (1) of "KV Cache Management". Returns -1 on bad input. */
 int64_t pa_bytes_per_token(int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
                            int32_t elem_bytes, int32_t tp);
-/* M_block = 2*L*H_kv*B*d*b ("The PagedAttention virtual memory model"); -1 on bad geometry. */
+/* M_block = 2*L*H_kv*B*d*b ("The PagedAttention virtual memory model"), plus for
+ * FP8 pools the 2*L*H_kv*B scale bytes; -1 on bad geometry. */
 int64_t pa_bytes_per_block(const pa_geom* g);
 /* ceil(tokens / block_size); -1 on bad input. */
 int64_t pa_blocks_for_tokens(int64_t tokens, int32_t block_size);
-/* Bytes of one pool array (K or V): L*N*H_kv*B*d*b; -1 on bad geometry. */
+/* Bytes of one pool array (K or V): L*N*H_kv*B*d*b (+ L*N*H_kv*B scale bytes
+ * for FP8); -1 on bad geometry. */
 int64_t pa_pool_bytes(const pa_geom* g);
 
 /* ------------------------------------------------------------ device entry points */

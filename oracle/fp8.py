@@ -105,6 +105,14 @@ def quantize_vector(x):
     return encode(x * 2.0 ** -e), e + SCALE_BIAS
 
 
+def quantize_rows(X):
+    """quantize_vector applied to every row of X [n, d]: (codes [n, d], bytes [n])."""
+    X = np.asarray(X, dtype=np.float64)
+    e = np.array([scale_exponent(a) for a in np.max(np.abs(X), axis=1)], dtype=np.int64)
+    codes = encode(X * np.ldexp(1.0, -e)[:, None])
+    return codes, (e + SCALE_BIAS).astype(np.uint8)
+
+
 def dequantize_vector(codes, scale_byte) -> np.ndarray:
     return decode(codes) * 2.0 ** (int(scale_byte) - SCALE_BIAS)
 

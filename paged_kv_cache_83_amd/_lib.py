@@ -19,7 +19,7 @@ STATUS_NAMES = {
     -8: "PA_ERR_OUT_OF_FRAMES",
 }
 PA_TIER_HBM, PA_TIER_HOST, PA_TIER_PENDING_OUT, PA_TIER_PENDING_IN = 0, 1, 2, 3
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_FP8 = 0, 1, 2
 
 
 class pa_geom(C.Structure):

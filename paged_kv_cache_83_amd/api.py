@@ -18,8 +18,8 @@ import torch
 from . import _lib
 from ._lib import check
 
-_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16}
-_CODE = {"f32": _lib.PA_F32, "bf16": _lib.PA_BF16}
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+_CODE = {"f32": _lib.PA_F32, "bf16": _lib.PA_BF16, "fp8": _lib.PA_FP8}
 
 
 @dataclass(frozen=True)
@@ -29,7 +29,7 @@ class Geometry:
     head_dim: int
     block_size: int
     num_blocks: int
-    dtype: str  # "f32" or "bf16"
+    dtype: str  # "f32", "bf16" or "fp8" (E4M3 codes with per-(token, head) scales)
 
     def c(self) -> _lib.pa_geom:
         return _lib.pa_geom(self.num_layers, self.num_kv_heads, self.head_dim, self.block_size,
@@ -37,11 +37,24 @@ class Geometry:
 
     @property
     def torch_dtype(self) -> torch.dtype:
+        """Storage type of the pools (uint8 bytes for fp8)."""
         return _TORCH[self.dtype]
 
     @property
+    def io_dtype(self) -> torch.dtype:
+        """Type of queries, outputs and new K/V rows: bf16 for fp8 pools."""
+        return torch.bfloat16 if self.dtype == "fp8" else _TORCH[self.dtype]
+
+    @property
     def elem_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
+
+    @property
+    def tile_bytes(self) -> int:
+        """Bytes of one (layer, block, head) tile of K (or V): B*d elements, and
+        for fp8 the B scale bytes after them."""
+        extra = self.block_size if self.dtype == "fp8" else 0
+        return self.block_size * self.head_dim * self.elem_bytes + extra
 
     @property
     def k_chunk(self) -> int:
@@ -50,19 +63,24 @@ class Geometry:
 
     @property
     def k_pool_shape(self):
-        """[L, N, H_kv, d/W, B, W], the K layout include/pa.h documents."""
+        """[L, N, H_kv, d/W, B, W], the K layout include/pa.h documents; fp8 pools
+        are bytes [L, N, H_kv, tile_bytes]."""
+        if self.dtype == "fp8":
+            return (self.num_layers, self.num_blocks, self.num_kv_heads, self.tile_bytes)
         W = self.k_chunk
         return (self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim // W,
                 self.block_size, W)
 
     @property
     def v_pool_shape(self):
+        if self.dtype == "fp8":
+            return (self.num_layers, self.num_blocks, self.num_kv_heads, self.tile_bytes)
         return (self.num_layers, self.num_blocks, self.num_kv_heads, self.head_dim, self.block_size)
 
     @property
     def pool_numel(self) -> int:
-        return (self.num_layers * self.num_blocks * self.num_kv_heads * self.block_size
-                * self.head_dim)
+        per_tile = self.tile_bytes if self.dtype == "fp8" else self.block_size * self.head_dim
+        return self.num_layers * self.num_blocks * self.num_kv_heads * per_tile
 
 
 def _L():
@@ -124,8 +142,8 @@ def append_kv(geom: Geometry, k_pool, v_pool, layer: int, k_new, v_new, slot_map
     _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
     _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
     per = geom.num_kv_heads * geom.head_dim
-    _dev(k_new, "k_new", geom.torch_dtype, n * per)
-    _dev(v_new, "v_new", geom.torch_dtype, n * per)
+    _dev(k_new, "k_new", geom.io_dtype, n * per)
+    _dev(v_new, "v_new", geom.io_dtype, n * per)
     _dev(slot_mapping, "slot_mapping", torch.int64)
     g = geom.c()
     check(_L().pa_append_kv(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(k_new),
@@ -155,8 +173,8 @@ def _decode_args(geom: Geometry, k_pool, v_pool, q, out, block_tables, context_l
     if q.dim() != 3 or q.shape[2] != geom.head_dim:
         raise ValueError("q must be [n_seqs, n_q_heads, head_dim]")
     n, hq = int(q.shape[0]), int(q.shape[1])
-    _dev(q, "q", geom.torch_dtype)
-    _dev(out, "out", geom.torch_dtype, q.numel())
+    _dev(q, "q", geom.io_dtype)
+    _dev(out, "out", geom.io_dtype, q.numel())
     if block_tables.dim() != 2 or block_tables.shape[0] != n:
         raise ValueError("block_tables must be [n_seqs, max_blocks]")
     _dev(block_tables, "block_tables", torch.int32)
@@ -199,8 +217,8 @@ def decode_append(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, o
     g, n, hq, ws_ptr, ws_bytes = _decode_args(geom, k_pool, v_pool, q, out, block_tables,
                                               context_lens, max_context_len, workspace, o)
     per = geom.num_kv_heads * geom.head_dim
-    _dev(k_new, "k_new", geom.torch_dtype, n * per)
-    _dev(v_new, "v_new", geom.torch_dtype, n * per)
+    _dev(k_new, "k_new", geom.io_dtype, n * per)
+    _dev(v_new, "v_new", geom.io_dtype, n * per)
     check(_L().pa_decode_append(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(q),
                                 _ptr(k_new), _ptr(v_new), _ptr(out), n, hq, _ptr(block_tables),
                                 int(block_tables.shape[1]), _ptr(context_lens),
@@ -220,11 +238,11 @@ def prefill(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out, q_
     if q.dim() != 3 or q.shape[2] != geom.head_dim:
         raise ValueError("q must be [n_tokens, n_q_heads, head_dim]")
     n_tok, hq = int(q.shape[0]), int(q.shape[1])
-    _dev(q, "q", geom.torch_dtype)
-    _dev(out, "out", geom.torch_dtype, q.numel())
+    _dev(q, "q", geom.io_dtype)
+    _dev(out, "out", geom.io_dtype, q.numel())
     per = geom.num_kv_heads * geom.head_dim
-    _dev(k_new, "k_new", geom.torch_dtype, n_tok * per)
-    _dev(v_new, "v_new", geom.torch_dtype, n_tok * per)
+    _dev(k_new, "k_new", geom.io_dtype, n_tok * per)
+    _dev(v_new, "v_new", geom.io_dtype, n_tok * per)
     if block_tables.dim() != 2:
         raise ValueError("block_tables must be [n_seqs, max_blocks]")
     n = int(block_tables.shape[0])

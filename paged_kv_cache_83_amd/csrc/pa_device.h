@@ -113,9 +113,16 @@ __device__ __forceinline__ float sum_over_groups(float v) {
 
 inline bool geom_ok(const pa_geom* g) {
   return g && g->num_layers > 0 && g->num_kv_heads > 0 && g->head_dim > 0 && g->block_size > 0 &&
-         g->num_blocks > 0 && (g->dtype == PA_F32 || g->dtype == PA_BF16);
+         g->num_blocks > 0 && (g->dtype == PA_F32 || g->dtype == PA_BF16 || g->dtype == PA_FP8);
 }
-inline int64_t esize(const pa_geom* g) { return g->dtype == PA_F32 ? 4 : 2; }
+inline int64_t esize(const pa_geom* g) {
+  return g->dtype == PA_F32 ? 4 : g->dtype == PA_BF16 ? 2 : 1;
+}
+// Bytes of one (layer, block, head) tile of K or V: B*d elements, and for FP8
+// pools the B scale bytes that follow them.
+inline int64_t tile_bytes(const pa_geom* g) {
+  return (int64_t)g->block_size * g->head_dim * esize(g) + (g->dtype == PA_FP8 ? g->block_size : 0);
+}
 
 inline pa_status launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
 

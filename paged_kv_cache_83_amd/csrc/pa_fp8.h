@@ -1,0 +1,361 @@
+// One-byte KV storage (PA_FP8): the quantizing append and the decode kernel.
+//
+// Format (the pages give b_elem = 1 and no scale, "KV Cache Management",
+// section "From Context Tokens to KV State", Eq. (1)): OCP FP8 E4M3 codes and,
+// per (token, KV head), one power-of-two scale 2^e stored as the byte e + 127,
+// with e the smallest integer such that max|x| <= 448 * 2^e. A (layer, block,
+// head) tile is the B*d codes in the bf16 element order (K [d/W][B][W], V
+// [d][B]) followed by the B scale bytes of its slots.
+//
+// Decode keeps the bf16 matrix-core path: E4M3 converts to bf16 exactly
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1), the K scale of each key multiplies
+// its score and the V scale of each key its probability before the PV product,
+// both as exact power-of-two scalings in fp32 (v_ldexp_f32). The bytes read per
+// key and head fall from 2*d*2 to 2*(d+1).
+#pragma once
+
+#include "pa_device.h"
+
+namespace pa_detail {
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kFp8ScaleBias = 127;
+
+// Smallest e with amax <= 448 * 2^e, clamped to [-127, 127]; 0 for amax == 0.
+// amax = f * 2^x with f in [0.5, 1) and x = E - 126 for a normal float with
+// exponent field E; 448 = 0.875 * 2^9, so e = x - 9 when f <= 0.875 (the
+// significand 1.m <= 1.75, i.e. m <= 0x600000) and x - 8 otherwise. Integer
+// logic only, so every caller takes the same decision. amax must be finite.
+__device__ __forceinline__ int fp8_scale_exp(float amax) {
+  const uint32_t b = __float_as_uint(amax);
+  if (b == 0u) return 0;
+  const int E = (int)(b >> 23);
+  if (E == 0) return -127;  // below 2^-126: 448 * 2^-127 already covers it
+  const int x = E - 126;
+  const int e = (b & 0x7fffffu) <= 0x600000u ? x - 9 : x - 8;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Eight E4M3 codes (bytes of w, lowest first) as bf16, exactly.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[0], 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[1], 1.0f, true);
+  const u32x4 u = {__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                   __builtin_bit_cast(uint32_t, c), __builtin_bit_cast(uint32_t, d)};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ int byte_of(u32x2 w, int k) {  // k compile-time after unrolling
+  return (int)((w[k >> 2] >> (8 * (k & 3))) & 0xffu);
+}
+
+// ---------------------------------------------------------------------------
+// Quantizing append: one wave per (token, KV head). The wave reduces max|x|
+// over the head's d values, derives e, and writes the d codes and the scale
+// byte of K and of V into the token's slot. k_new / v_new: bf16 [n][H][d].
+// ---------------------------------------------------------------------------
+
+// Slot of the token appended for sequence j of a decode step: position
+// lens[j] - 1 through row j of the block tables (-1 when there is none).
+struct SlotsFromLens {
+  const int32_t* tables;
+  const int32_t* lens;
+  int max_blocks;
+  int max_ctx;
+  int B;
+  int N;
+  __device__ int64_t operator()(int64_t j) const {
+    const int len = clamp_len(lens, (int)j, max_ctx);
+    if (len == 0) return -1;
+    const int pos = len - 1;
+    const int lb = pos / B;
+    if (lb >= max_blocks) return -1;
+    const int p = tables[j * max_blocks + lb];
+    if (p < 0 || p >= N) return -1;
+    return (int64_t)p * B + pos % B;
+  }
+};
+
+template <typename SlotSrc>
+__global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ kpool,
+                                                        uint8_t* __restrict__ vpool,
+                                                        const uint16_t* __restrict__ knew,
+                                                        const uint16_t* __restrict__ vnew,
+                                                        SlotSrc slots, int64_t n_tok, int H, int D,
+                                                        int B, int64_t nslots, int64_t layer_off) {
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (item >= n_tok * H) return;
+  const int64_t j = item / H;
+  const int h = (int)(item % H);
+  const int64_t slot = slots(j);
+  if (slot < 0 || slot >= nslots) return;
+  const int64_t p = slot / B;
+  const int o = (int)(slot % B);
+  const int64_t TB = (int64_t)B * D + B;
+  const int W = k_chunk(D);
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    const uint16_t* row = (kv ? vnew : knew) + (j * H + h) * D;
+    uint8_t* t = (kv ? vpool : kpool) + layer_off + (p * H + h) * TB;
+    float amax = 0.f;
+    for (int d = lane; d < D; d += 64) amax = fmaxf(amax, fabsf(bf16_to_f32(row[d])));
+    amax = wave_max(amax);
+    const int e = fp8_scale_exp(amax);
+    for (int d = lane; d < D; d += 64) {
+      const float x = __builtin_amdgcn_ldexpf(bf16_to_f32(row[d]), -e);
+      const uint8_t code = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xff);
+      const int64_t off = kv ? (int64_t)d * B + o : (int64_t)(d / W) * B * W + (int64_t)o * W + d % W;
+      t[off] = code;
+    }
+    if (lane == 0) t[(int64_t)B * D + o] = (uint8_t)(e + kFp8ScaleBias);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Decode, FP8 pool, matrix cores: B = 16, d in {64, 128}, up to 16 query heads
+// per KV head. The work decomposition, the score-row / key assignment, the
+// split-K partials and the pipelining are those of the bf16 kernel; per pair
+// of blocks a lane loads 8-byte code fragments (K: 8 dims of one key; V: 8 keys
+// of one dim) and the 8 K and 8 V scale bytes of its 8 keys.
+// ---------------------------------------------------------------------------
+template <int D>
+struct Fp8Frags {
+  u32x2 k[2][D / 32];
+  u32x2 v[D / 16];
+  u32x2 ks, vs;
+};
+
+template <bool NT>
+__device__ __forceinline__ u32x2 kv_load8(const uint8_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+  else return *reinterpret_cast<const u32x2*>(p);
+}
+
+__device__ __forceinline__ int fp8_table_at(const int (&tb)[4], int off) {
+  const int r = off >> 6;
+  const int v = r == 0 ? tb[0] : r == 1 ? tb[1] : r == 2 ? tb[2] : tb[3];
+  return __builtin_amdgcn_readlane(v, off & 63);
+}
+
+template <int D, bool NT>
+__device__ __forceinline__ void fp8_issue_pair(Fp8Frags<D>& f, const uint8_t* __restrict__ kl,
+                                               const uint8_t* __restrict__ vl, int p0, int p1,
+                                               int Hkv, int g, int k_sel, int k_off0, int v_sel,
+                                               int v_off, int s_off, int gq) {
+  constexpr int KC = D / 32;
+  constexpr int DT = D / 16;
+  constexpr int TB = 16 * D + 16;
+  const uint8_t* kt = kl + ((int64_t)(k_sel ? p1 : p0) * Hkv + g) * TB;
+  const uint8_t* ks = kl + ((int64_t)(v_sel ? p1 : p0) * Hkv + g) * TB;
+  const uint8_t* vt = vl + ((int64_t)(v_sel ? p1 : p0) * Hkv + g) * TB;
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      f.k[t][kc] = kv_load8<NT>(kt + kc * 512 + (k_off0 + 4 * t) * 32 + 8 * gq);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) f.v[dt] = kv_load8<NT>(vt + dt * 256 + v_off);
+  f.ks = kv_load8<NT>(ks + 16 * D + s_off);
+  f.vs = kv_load8<NT>(vt + 16 * D + s_off);
+}
+
+template <int D>
+__device__ __forceinline__ void fp8_compute_pair(Fp8Frags<D>& f, const bf16x8 (&qf)[D / 32],
+                                                 f32x4 (&acc)[D / 16], float& m_run, float& l_run,
+                                                 int blk, int len, int gq, float qk_scale) {
+  constexpr int KC = D / 32;
+  constexpr int DT = D / 16;
+  f32x4 sc[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+      sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(f.k[t][kc]), qf[kc], sc[t], 0, 0, 0);
+  }
+  // Lane holds the scores of pair-local keys 8*gq + 4*t + e for query c; byte
+  // 4*t + e of f.ks is that key's K scale.
+  const int pos0 = blk * 16 + 8 * gq;
+  float sv[8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sv[4 * t + e] = (pos0 + 4 * t + e < len)
+                          ? __builtin_amdgcn_ldexpf(sc[t][e] * qk_scale,
+                                                    byte_of(f.ks, 4 * t + e) - kFp8ScaleBias)
+                          : -INFINITY;
+  float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                   fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+  mb = max_over_groups(mb);
+  const float m_new = fmaxf(m_run, mb);  // finite: the pair's first key is attended
+  float psum = 0.f;
+  uint32_t pw[4];
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) {
+    const float pa = __builtin_amdgcn_exp2f(sv[e] - m_new);
+    const float pb = __builtin_amdgcn_exp2f(sv[e + 1] - m_new);
+    psum += pa + pb;
+    // The PV operand carries each key's V scale (an exact power of two).
+    pw[e >> 1] = pack_bf16x2(__builtin_amdgcn_ldexpf(pa, byte_of(f.vs, e) - kFp8ScaleBias),
+                             __builtin_amdgcn_ldexpf(pb, byte_of(f.vs, e + 1) - kFp8ScaleBias));
+  }
+  if (__any(m_new != m_run)) {
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] = acc[dt] * alpha;
+  }
+  l_run += psum;
+  m_run = m_new;
+  const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+
+  // Slots at or past the length hold unspecified bytes (possibly NaN codes):
+  // their codes become 0 so that 0 * V stays 0.
+  if (blk * 16 + 32 > len) {
+    u32x2 keep = {0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (pos0 + k < len) keep[k >> 2] |= 0xffu << (8 * (k & 3));
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) f.v[dt] &= keep;
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(f.v[dt]), pf, acc[dt], 0, 0, 0);
+}
+
+template <int D, bool DIRECT, bool NT, int NS>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_fp8_kernel(
+    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ out, float* __restrict__ part_o,
+    float* __restrict__ part_ml, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lens, int64_t layer_off, int N, int Hkv, int Hq, int G,
+    int max_blocks, int max_ctx, int bps, int S_max, float qk_scale) {
+  constexpr int KC = D / 32;
+  constexpr int DT = D / 16;
+
+  const int w = blockIdx.x;
+  const int g = w % Hkv;
+  const int si = w / Hkv;
+  const int s = si % S_max;
+  const int i = si / S_max;
+  const int lane = threadIdx.x;
+  const int c = lane & 15;
+  const int gq = lane >> 4;
+
+  const int len = clamp_len(lens, i, max_ctx);
+  const int nblk = (len + 15) >> 4;
+  const int b0 = s * bps;
+  const int h = g * G + c;
+  const bool qvalid = c < G;
+  if (b0 >= nblk) {
+    if (DIRECT && len == 0 && qvalid) {
+      uint16_t* o = out + ((int64_t)i * Hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) = make_uint2(0u, 0u);
+    }
+    return;
+  }
+  const int b1 = min(b0 + bps, nblk);
+
+  const int32_t* trow = tables + (int64_t)i * max_blocks;
+  int tb[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = b0 + 64 * k + lane;
+    tb[k] = (64 * k < b1 - b0 && idx < b1) ? guard_block(trow[idx], N) : 0;
+  }
+
+  bf16x8 qf[KC];
+  {
+    const uint16_t* qrow = q + ((int64_t)i * Hq + (qvalid ? h : 0)) * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qvalid) v = *reinterpret_cast<const uint4*>(qrow + 32 * kc + 8 * gq);
+      qf[kc] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x4 acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  const uint8_t* kl = kpool + layer_off;
+  const uint8_t* vl = vpool + layer_off;
+  // Score row c of each tile holds pair-local key 8*(c>>2) + 4*t + (c&3).
+  const int k_sel = c >> 3;
+  const int k_off0 = 8 * ((c >> 2) & 1) + (c & 3);
+  // V^T fragment: block (gq >> 1), dims 16*dt + c, slots 8*(gq&1) .. +8; the
+  // lane's 8 keys are the same slots of the same block, whose scales it reads.
+  const int v_sel = gq >> 1;
+  const int v_off = 16 * c + 8 * (gq & 1);
+  const int s_off = 8 * (gq & 1);
+
+  const int span = b1 - b0;
+  const int npairs = (span + 1) >> 1;
+  auto issue_at = [&](Fp8Frags<D>& fr, int pj) {
+    const int off = 2 * pj;
+    const int p0 = fp8_table_at(tb, off);
+    const int p1 = (off + 1 < span) ? fp8_table_at(tb, off + 1) : p0;
+    fp8_issue_pair<D, NT>(fr, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, s_off, gq);
+  };
+  // NS pairs in flight; steady loop issues unconditionally, the tail drains
+  // (the structure of the bf16 kernel).
+  Fp8Frags<D> f[NS];
+  int pj = 0;
+  if (npairs >= 2 * NS - 1) {
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) issue_at(f[st], st);
+    for (; pj + 2 * NS - 1 <= npairs; pj += NS) {
+#pragma unroll
+      for (int st = 0; st < NS; ++st) {
+        issue_at(f[(st + NS - 1) % NS], pj + st + NS - 1);
+        fp8_compute_pair<D>(f[st], qf, acc, m_run, l_run, b0 + 2 * (pj + st), len, gq, qk_scale);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < npairs) issue_at(f[st], st);
+  }
+#pragma unroll
+  for (int k = 0; k < 2 * NS - 2; ++k) {
+    if (pj + k >= npairs) break;
+    if (pj + k + NS - 1 < npairs) issue_at(f[(k + NS - 1) % NS], pj + k + NS - 1);
+    fp8_compute_pair<D>(f[k % NS], qf, acc, m_run, l_run, b0 + 2 * (pj + k), len, gq, qk_scale);
+  }
+
+  l_run = sum_over_groups(l_run);
+  if (!qvalid) return;
+  if (DIRECT) {
+    const float inv = 1.f / l_run;
+    uint16_t* o = out + ((int64_t)i * Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) =
+          make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                     pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
+  } else {
+    const int64_t row = ((int64_t)i * Hq + h) * S_max + s;
+    float* po = part_o + row * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * gq) =
+          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (gq == 0) {
+      part_ml[row * 2 + 0] = m_run;
+      part_ml[row * 2 + 1] = l_run;
+    }
+  }
+}
+
+}  // namespace pa_detail

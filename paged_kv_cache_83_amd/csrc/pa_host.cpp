@@ -40,10 +40,16 @@ constexpr int32_t kNotResident = -1;
 
 bool geom_ok(const pa_geom* g) {
   return g && g->num_layers > 0 && g->num_kv_heads > 0 && g->head_dim > 0 && g->block_size > 0 &&
-         g->num_blocks > 0 && (g->dtype == PA_F32 || g->dtype == PA_BF16);
+         g->num_blocks > 0 && (g->dtype == PA_F32 || g->dtype == PA_BF16 || g->dtype == PA_FP8);
 }
 
-int64_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : 2; }
+int64_t elem_bytes(int32_t dtype) { return dtype == PA_F32 ? 4 : dtype == PA_BF16 ? 2 : 1; }
+
+// One (layer, block, head) tile: B*d elements, then B scale bytes for FP8.
+int64_t tile_bytes(const pa_geom* g) {
+  return (int64_t)g->block_size * g->head_dim * elem_bytes(g->dtype) +
+         (g->dtype == PA_FP8 ? g->block_size : 0);
+}
 
 // One entry of a migration in flight: the HBM block and the host frame it
 // moves between; out = true for HBM -> host.
@@ -215,8 +221,7 @@ int64_t pa_bytes_per_token(int32_t L, int32_t H_kv, int32_t d, int32_t b, int32_
 
 int64_t pa_bytes_per_block(const pa_geom* g) {
   if (!geom_ok(g)) return -1;
-  return 2 * (int64_t)g->num_layers * g->num_kv_heads * g->block_size * g->head_dim *
-         elem_bytes(g->dtype);
+  return 2 * (int64_t)g->num_layers * g->num_kv_heads * tile_bytes(g);
 }
 
 int64_t pa_blocks_for_tokens(int64_t tokens, int32_t B) {
@@ -226,8 +231,7 @@ int64_t pa_blocks_for_tokens(int64_t tokens, int32_t B) {
 
 int64_t pa_pool_bytes(const pa_geom* g) {
   if (!geom_ok(g)) return -1;
-  return (int64_t)g->num_layers * g->num_blocks * g->num_kv_heads * g->block_size * g->head_dim *
-         elem_bytes(g->dtype);
+  return (int64_t)g->num_layers * g->num_blocks * g->num_kv_heads * tile_bytes(g);
 }
 
 // ------------------------------------------------------------------ block manager

@@ -36,6 +36,7 @@
 #include "pa_device.h"
 #include "pa_append.h"
 #include "pa_move.h"
+#include "pa_fp8.h"
 
 namespace {
 
@@ -64,6 +65,10 @@ using namespace pa_detail;
 // buffers), so every wave keeps one pair of blocks in flight at all times.
 // =============================================================================
 constexpr int kMfmaMaxBps = 256;  // table entries of one split, held 64 per register
+
+#ifndef PA_FP8_STAGES
+#define PA_FP8_STAGES 2  // pairs of blocks in flight per wave, FP8 kernel
+#endif
 
 #ifndef PA_MFMA_STAGES
 #define PA_MFMA_STAGES 2
@@ -660,7 +665,7 @@ size_t generic_lds_bytes(int G, int D, int B) {
 }
 
 struct DecodePlan {
-  int kernel;  // 1 generic, 2 mfma
+  int kernel;  // 1 generic, 2 mfma (bf16 pool), 3 mfma (fp8 pool)
   bool stream_kv;  // non-temporal K/V loads
   int bps;
   int S_max;
@@ -673,10 +678,12 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
   if (!geom_ok(g) || n_seqs < 0 || Hq <= 0 || max_ctx < 0) return PA_ERR_INVALID_ARG;
   if (Hq % g->num_kv_heads != 0) return PA_ERR_INVALID_ARG;
   const int D = g->head_dim, B = g->block_size, G = Hq / g->num_kv_heads;
-  const bool mfma_ok = g->dtype == PA_BF16 && B == 16 && (D == 64 || D == 128 || D == 256) && G <= 16;
+  const bool fp8 = g->dtype == PA_FP8;
+  const bool mfma_ok = B == 16 && G <= 16 &&
+                       (fp8 ? (D == 64 || D == 128) : (g->dtype == PA_BF16 && (D == 64 || D == 128 || D == 256)));
   const size_t gen_lds = generic_lds_bytes(G, D, B);
-  const bool gen_ok = B <= 64 && D <= 256 && B * D <= 4096 && G * D <= 64 * kGenMaxAcc && G <= 64 &&
-                      gen_lds <= 65536;
+  const bool gen_ok = !fp8 && B <= 64 && D <= 256 && B * D <= 4096 && G * D <= 64 * kGenMaxAcc &&
+                      G <= 64 && gen_lds <= 65536;
   const int want = opts ? opts->kernel : 0;
   int k;
   if (want == 1) {
@@ -684,9 +691,9 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
     k = 1;
   } else if (want == 2) {
     if (!mfma_ok) return PA_ERR_UNSUPPORTED;
-    k = 2;
+    k = fp8 ? 3 : 2;
   } else if (want == 0) {
-    if (mfma_ok) k = 2;
+    if (mfma_ok) k = fp8 ? 3 : 2;
     else if (gen_ok) k = 1;
     else return PA_ERR_UNSUPPORTED;
   } else {
@@ -703,8 +710,8 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
     // The generic kernel walks its blocks one at a time with a load latency per
     // block, so it wants many short items instead.
     const int64_t units = (int64_t)n_seqs * g->num_kv_heads;
-    const int64_t target_items = k == 2 ? 1024 : 4096;
-    const int64_t min_bps = k == 2 ? 16 : 2;
+    const int64_t target_items = k >= 2 ? 1024 : 4096;
+    const int64_t min_bps = k >= 2 ? 16 : 2;
     if (units >= target_items || units == 0) {
       bps = maxb;
     } else {
@@ -714,7 +721,7 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
   }
   bps = std::max<int64_t>(2, bps);
   bps += bps & 1;  // pairs of blocks never straddle two splits
-  if (k == 2) bps = std::min<int64_t>(bps, kMfmaMaxBps);
+  if (k >= 2) bps = std::min<int64_t>(bps, kMfmaMaxBps);
   if (bps > INT32_MAX / 2) bps = INT32_MAX / 2;
   int64_t S = maxb == 0 ? 1 : (maxb + bps - 1) / bps;
   if (opts && (opts->kv_reuse < 0 || opts->kv_reuse > 1)) return PA_ERR_INVALID_ARG;
@@ -763,6 +770,16 @@ pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t lay
   const int D = g->head_dim, B = g->block_size, H = g->num_kv_heads;
   const int64_t layer_off = (int64_t)layer * g->num_blocks * H * B * D;
   const int64_t nslots = (int64_t)g->num_blocks * B;
+  if (g->dtype == PA_FP8) {  // one wave per (token, head), 4 per work group
+    ProfScope ps("append", st);
+    const int64_t wgs = ((int64_t)n_tokens * H + 3) / 4;
+    if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((append_fp8_kernel<SlotsFromArray>), dim3((unsigned)wgs), dim3(256), 0, st,
+                       (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, SlotsFromArray{slot_mapping}, (int64_t)n_tokens, H,
+                       D, B, nslots, (int64_t)layer * g->num_blocks * H * tile_bytes(g));
+    return launch_status();
+  }
   const size_t lds = g->dtype == PA_BF16 ? append_lds_bytes<uint16_t>(D) : append_lds_bytes<float>(D);
   if (lds > 65536) return PA_ERR_UNSUPPORTED;
   ProfScope ps("append", st);
@@ -830,10 +847,42 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   const int64_t layer_off = (int64_t)layer * g->num_blocks * Hkv * B * D;
   float* part_o = (float*)workspace;
   float* part_ml = plan.direct ? nullptr : part_o + (size_t)n_seqs * n_q_heads * plan.S_max * D;
+  if (plan.kernel == 3 && append) {  // FP8: quantize the step's tokens into the pool first
+    ProfScope ps("append", st);
+    const int64_t wgs = ((int64_t)n_seqs * Hkv + 3) / 4;
+    hipLaunchKernelGGL((append_fp8_kernel<SlotsFromLens>), dim3((unsigned)wgs), dim3(256), 0, st,
+                       (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)knew,
+                       (const uint16_t*)vnew,
+                       SlotsFromLens{block_tables, context_lens, max_blocks_per_seq, max_context_len,
+                                     B, g->num_blocks},
+                       (int64_t)n_seqs, Hkv, D, B, (int64_t)g->num_blocks * B,
+                       (int64_t)layer * g->num_blocks * Hkv * tile_bytes(g));
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
   {
     ProfScope ps("decode_partial", st);
     const dim3 grid((unsigned)items), block(64);
-    if (plan.kernel == 2) {
+    if (plan.kernel == 3) {
+      const int64_t off8 = (int64_t)layer * g->num_blocks * Hkv * tile_bytes(g);
+#define PA_FP8_LAUNCH_X(DD, DIR, NTV)                                                              \
+  hipLaunchKernelGGL((decode_mfma_fp8_kernel<DD, DIR, NTV, PA_FP8_STAGES>), grid, block, 0, st,     \
+                     (const uint8_t*)k_pool, (const uint8_t*)v_pool, (const uint16_t*)q,            \
+                     (uint16_t*)out, part_o, part_ml, block_tables, context_lens, off8,           \
+                     g->num_blocks, Hkv, n_q_heads, G, max_blocks_per_seq, max_context_len,       \
+                     plan.bps, plan.S_max, qk_scale)
+#define PA_FP8_LAUNCH(DD, DIR)                                   \
+  do {                                                           \
+    if (plan.stream_kv) PA_FP8_LAUNCH_X(DD, DIR, true);          \
+    else PA_FP8_LAUNCH_X(DD, DIR, false);                        \
+  } while (0)
+      if (D == 64) {
+        if (plan.direct) PA_FP8_LAUNCH(64, true); else PA_FP8_LAUNCH(64, false);
+      } else {
+        if (plan.direct) PA_FP8_LAUNCH(128, true); else PA_FP8_LAUNCH(128, false);
+      }
+#undef PA_FP8_LAUNCH
+#undef PA_FP8_LAUNCH_X
+    } else if (plan.kernel == 2) {
 #define PA_MFMA_LAUNCH_X(DD, DIR, NTV, APP)                                                       \
   hipLaunchKernelGGL((decode_mfma_bf16_kernel<DD, DIR, NTV, APP>), grid, block, 0, st,            \
                      (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)q,                     \
@@ -896,7 +945,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   if (!plan.direct) {
     ProfScope ps("decode_combine", st);
     const dim3 grid((unsigned)((int64_t)n_seqs * n_q_heads)), block(64);
-    if (g->dtype == PA_F32)
+    if (g->dtype == PA_F32)  // bf16 output for bf16 and fp8 pools
       hipLaunchKernelGGL((decode_combine_kernel<float>), grid, block, 0, st, part_o, part_ml,
                          (float*)out, context_lens, n_q_heads, D, B, plan.S_max, plan.bps,
                          max_context_len);
@@ -941,7 +990,7 @@ static pa_status block_move(int mode, const char* name, const pa_geom* g, void* 
   if (n == 0) return PA_OK;
   if (!k_pool || !v_pool || !ids_a || (mode == 0 && !ids_b) || (mode != 0 && !staging))
     return PA_ERR_INVALID_ARG;
-  const int64_t run = (int64_t)g->num_kv_heads * g->block_size * g->head_dim * esize(g);
+  const int64_t run = (int64_t)g->num_kv_heads * tile_bytes(g);
   const int64_t runs = (int64_t)n * g->num_layers * 2;
   if (runs > INT32_MAX) return PA_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
@@ -957,7 +1006,8 @@ static pa_status block_move(int mode, const char* name, const pa_geom* g, void* 
   do {                                                             \
     if (run % 16 == 0) PA_MOVE(M, u32x4);                          \
     else if (run % 4 == 0) PA_MOVE(M, uint32_t);                   \
-    else PA_MOVE(M, uint16_t);                                     \
+    else if (run % 2 == 0) PA_MOVE(M, uint16_t);                   \
+    else PA_MOVE(M, uint8_t);                                      \
   } while (0)
   if (mode == 0) PA_MOVE_MODE(0);
   else if (mode == 1) PA_MOVE_MODE(1);

@@ -120,8 +120,12 @@ bool move_chunk(pa_swapper* s, char* stg, const int32_t* ids, int32_t m) {
       hipLaunchKernelGGL((block_move_kernel<MODE, uint32_t, ArgIds, NoIds>), grid, block, 0,
                          s->kstream, (char*)s->k_pool, (char*)s->v_pool, dst, arg, NoIds{},
                          s->g.num_layers, s->g.num_blocks, s->run_bytes, runs);
-    else
+    else if (s->run_bytes % 2 == 0)
       hipLaunchKernelGGL((block_move_kernel<MODE, uint16_t, ArgIds, NoIds>), grid, block, 0,
+                         s->kstream, (char*)s->k_pool, (char*)s->v_pool, dst, arg, NoIds{},
+                         s->g.num_layers, s->g.num_blocks, s->run_bytes, runs);
+    else
+      hipLaunchKernelGGL((block_move_kernel<MODE, uint8_t, ArgIds, NoIds>), grid, block, 0,
                          s->kstream, (char*)s->k_pool, (char*)s->v_pool, dst, arg, NoIds{},
                          s->g.num_layers, s->g.num_blocks, s->run_bytes, runs);
     if (hipGetLastError() != hipSuccess) return false;
@@ -223,7 +227,7 @@ pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_p
   if (!geom_ok(g) || !bm || !k_pool || !v_pool || num_frames <= 0 || chunk_blocks < 0 ||
       move_wgs < 0)
     return PA_ERR_INVALID_ARG;
-  const int64_t run = (int64_t)g->num_kv_heads * g->block_size * g->head_dim * esize(g);
+  const int64_t run = (int64_t)g->num_kv_heads * tile_bytes(g);
   const int64_t frame = 2 * (int64_t)g->num_layers * run;
   if (chunk_blocks == 0)  // about 64 MiB per staging buffer, at least one block
     chunk_blocks = (int32_t)std::max<int64_t>(1, std::min<int64_t>(4096, (64ll << 20) / frame));

@@ -194,3 +194,13 @@ def test_append_quantizes_at_table_slots():
                                   fp8.dequantize_vector(*fp8.quantize_vector(kx)))
             assert np.array_equal(fp8.read_v(vp2, 1, s // B, h, s % B, B, d),
                                   fp8.dequantize_vector(*fp8.quantize_vector(vx)))
+
+
+def test_quantize_rows_equals_per_vector():
+    rng = np.random.default_rng(23)
+    X = rng.standard_normal((40, 64)) * 10.0 ** rng.uniform(-5, 5, (40, 1))
+    X[3] = 0.0
+    codes, sb = fp8.quantize_rows(X)
+    for r in range(40):
+        c, b = fp8.quantize_vector(X[r])
+        assert np.array_equal(codes[r], c) and sb[r] == b
