@@ -72,13 +72,26 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def decode_kernel_source_sha() -> str:
+    """sha256 prefix of the bf16 matrix-core decode kernel's source: its section of
+    pa_kernels.hip (from its banner to the generic kernel's) and the device
+    helpers it includes. Edits elsewhere in the file leave it unchanged."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(here, "paged_kv_cache_83_amd", "csrc")
+    text = open(os.path.join(csrc, "pa_kernels.hip"), "rb").read()
+    a = text.index(b"// Decode, MFMA kernel:")
+    b = text.index(b"// Decode, generic kernel")
+    h = hashlib.sha256(text[a:b])
+    h.update(open(os.path.join(csrc, "pa_device.h"), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def profiled_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel
     source has changed since those counters were taken."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"decode_mfma_bf16_{workload}_hbm_counters.md")
-    src = os.path.join(here, "paged_kv_cache_83_amd", "csrc", "pa_kernels.hip")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -86,7 +99,7 @@ def profiled_traffic(workload: str):
         if ":" in line and line.split(":", 1)[0].strip() in ("source_sha256_prefix", "traffic_bytes_per_launch"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    sha = decode_kernel_source_sha()
     if fields.get("source_sha256_prefix") != sha or "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
@@ -193,9 +206,27 @@ def setup(args):
     gen_ = torch.Generator(device=dev)
     gen_.manual_seed(cfg.seed)
     k_pool, v_pool = pk.alloc_pools(geom, dev)
-    k_pool.normal_(generator=gen_)
-    v_pool.normal_(generator=gen_)
+    if cfg.dtype == "fp8":
+        fill_fp8_pools(torch, pk, geom, gen_, k_pool, v_pool, dev)
+    else:
+        k_pool.normal_(generator=gen_)
+        v_pool.normal_(generator=gen_)
     return torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool
+
+
+def fill_fp8_pools(torch, pk, geom, gen_, k_pool, v_pool, dev, chunk_slots=1 << 18):
+    """Every slot of an FP8 pool gets seeded N(0,1) K/V rows (bf16), quantized by the
+    library's own append (codes and scales as the decode step would write them)."""
+    nslots = geom.num_blocks * geom.block_size
+    Hkv, d = geom.num_kv_heads, geom.head_dim
+    for layer in range(geom.num_layers):
+        for a in range(0, nslots, chunk_slots):
+            m = min(chunk_slots, nslots - a)
+            kn = torch.randn((m, Hkv, d), generator=gen_, device=dev).to(torch.bfloat16)
+            vn = torch.randn((m, Hkv, d), generator=gen_, device=dev).to(torch.bfloat16)
+            slots = torch.arange(a, a + m, dtype=torch.int64, device=dev)
+            pk.append_kv(geom, k_pool, v_pool, layer, kn, vn, slots)
+    torch.cuda.synchronize()
 
 
 def to_np(torch, t, dtype):
@@ -213,10 +244,13 @@ def run_decode(args):
     L, n, Hq, Hkv, d, B = (cfg.num_layers, cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
                            cfg.head_dim, cfg.block_size)
     lengths = gen.context_lengths(cfg)
-    m_token = pk.bytes_per_token(L, Hkv, d, geom.elem_bytes)
-    q_all = torch.randn((L, n, Hq, d), generator=gen_, device=dev).to(geom.torch_dtype)
-    k_new = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
-    v_new = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    fp8 = cfg.dtype == "fp8"
+    # bytes of K and V per token over all layers (FP8: plus one scale byte per head, K and V)
+    m_token = pk.bytes_per_block(geom) // B
+    io = geom.io_dtype
+    q_all = torch.randn((L, n, Hq, d), generator=gen_, device=dev).to(io)
+    k_new = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(io)
+    v_new = torch.randn((L, n, Hkv, d), generator=gen_, device=dev).to(io)
 
     # host block bookkeeping: history, then the decode step's one new token each
     bm = pk.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
@@ -232,7 +266,7 @@ def run_decode(args):
     tables = torch.from_numpy(np.ascontiguousarray(tables_np)).to(dev)
     lens = torch.from_numpy(np.ascontiguousarray(lens_np)).to(dev)
     max_ctx = int(lengths.max())
-    out = torch.empty((L, n, Hq, d), dtype=geom.torch_dtype, device=dev)
+    out = torch.empty((L, n, Hq, d), dtype=io, device=dev)
     ws_bytes = pk.decode_workspace_bytes(geom, n, Hq, max_ctx, args.bps, args.kernel)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
@@ -295,27 +329,30 @@ def run_decode(args):
     # ---- roofline of the dominant kernel (decode partial), timed live ----------
     roofline, kernel_ms = None, {}
     if not args.no_prof and not args.graph:
-        for name in ("decode_partial", "decode_combine"):
+        for name in ("decode_partial", "decode_combine", "append"):
             cnt, tot = pk.Profiler.read(name)
             if cnt:
                 kernel_ms[name] = {"launches": cnt, "avg_us": 1e3 * tot / cnt}
         cnt, tot = pk.Profiler.read("decode_partial")
         if cnt:
             eb = geom.elem_bytes
+            ib = 2 if fp8 else eb                                                # q / out element bytes
             splits = max(1, ws_bytes // (n * Hq * (d + 2) * 4)) if ws_bytes else 1
-            per_launch = (int(lengths.sum()) * 2 * Hkv * d * eb                 # K and V of attended tokens
-                          + n * Hq * d * eb                                      # queries
+            per_launch = (int(lengths.sum()) * 2 * Hkv * (d * eb + (1 if fp8 else 0))  # K and V (+ scales)
+                          + n * Hq * d * ib                                      # queries
                           + 4 * int(sum(math.ceil(S / B) for S in lengths))       # block-table entries
-                          + (n * Hq * splits * (d + 2) * 4 if ws_bytes else n * Hq * d * eb)
-                          + (0 if args.unfused else 4 * n * Hkv * d * eb))        # new K/V read + written
+                          + (n * Hq * splits * (d + 2) * 4 if ws_bytes else n * Hq * d * ib)
+                          + (0 if (args.unfused or fp8) else 4 * n * Hkv * d * eb))  # fused new K/V
             avg_s = tot / cnt * 1e-3
             achieved = per_launch / avg_s / 1e9
-            mfma = cfg.dtype == "bf16" and B == 16 and args.kernel != "generic"
+            mfma = cfg.dtype in ("bf16", "fp8") and B == 16 and args.kernel != "generic"
+            kname = ("decode_mfma_fp8_kernel" if fp8 else "decode_mfma_bf16_kernel") if mfma \
+                else "decode_generic_kernel"
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / PEAK_GBS, 4),
-                        "traffic": profiled_traffic(cfg.name) if (mfma and args.bps == 0 and
-                                                                  args.kernel == "auto") else None,
-                        "kernel": "decode_mfma_bf16_kernel" if mfma else "decode_generic_kernel",
+                        "traffic": profiled_traffic(cfg.name) if (mfma and not fp8 and args.bps == 0
+                                                                  and args.kernel == "auto") else None,
+                        "kernel": kname,
                         "bytes_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2)}
 
     # ---- parity on sampled (sequence, layer) outputs against the oracle ---------
@@ -333,16 +370,22 @@ def run_decode(args):
         oslots = [om.append(s, 1)[0][0] for s in oseqs]
         otables = [om.table(s) for s in oseqs]
 
+        from oracle import fp8 as ofp8
+        io_name = "bf16" if fp8 else cfg.dtype
+
         def oracle_one(i, layer):
             kb, vb, ids = snap[(i, layer)]
             kloc, vloc = to_np(torch, kb, cfg.dtype)[None], to_np(torch, vb, cfg.dtype)[None]
             remap = {int(p): j for j, p in enumerate(ids)}
             table = [remap[p] for p in otables[i]]
             slot = remap[oslots[i] // B] * B + oslots[i] % B
-            kn = to_np(torch, k_new[layer, i:i + 1], cfg.dtype)
-            vn = to_np(torch, v_new[layer, i:i + 1], cfg.dtype)
+            kn = to_np(torch, k_new[layer, i:i + 1], io_name)
+            vn = to_np(torch, v_new[layer, i:i + 1], io_name)
+            q = to_np(torch, q_all[layer, i:i + 1], io_name)
+            if fp8:
+                kloc, vloc = ofp8.append_kv(kloc, vloc, 0, kn, vn, [slot], B)
+                return ofp8.paged_decode(q, kloc, vloc, 0, [table], [int(lengths[i])], B)[0]
             kloc, vloc = okv.append_kv(kloc, vloc, 0, kn, vn, [slot], B)
-            q = to_np(torch, q_all[layer, i:i + 1], cfg.dtype)
             return oatt.paged_decode(q, kloc, vloc, 0, [table], [int(lengths[i])], B, cfg.dtype)[0]
 
         errs = []
@@ -350,7 +393,7 @@ def run_decode(args):
             expect = oracle_one(i, layer)
             got = out[layer, i].float().cpu().numpy().astype(np.float64)
             errs.append(float(np.max(np.abs(got - expect))))
-        tol = 2e-2 if cfg.dtype == "bf16" else 1e-5
+        tol = 1e-5 if cfg.dtype == "f32" else 2e-2
         if errs:
             parity = {"samples": len(errs), "max_abs_err": max(errs), "tol": tol, "ok": max(errs) <= tol}
             log(f"parity {parity}")
@@ -361,7 +404,9 @@ def run_decode(args):
             except Exception:  # pragma: no cover
                 threadpool_limits = None
             cores = len(os.sched_getaffinity(0))
-            pairs = [(int(rng.integers(0, n)), int(rng.integers(0, L))) for _ in range(args.cpu_sample)]
+            # the FP8 oracle dequantizes every tile in numpy (~4.5 s per 32K-token pair)
+            n_pairs = max(2, args.cpu_sample // 12) if fp8 else args.cpu_sample
+            pairs = [(int(rng.integers(0, n)), int(rng.integers(0, L))) for _ in range(n_pairs)]
             for key in pairs:
                 if key not in snap:
                     take_snapshot(*key)

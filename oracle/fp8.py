@@ -176,16 +176,35 @@ def append_kv(k_pool, v_pool, layer, k_new, v_new, slots, block_size, dtype="bf1
     return kp, vp
 
 
+def read_k_tile(k_pool, layer, phys, head, block_size, head_dim) -> np.ndarray:
+    """Dequantized K of all B slots of one (layer, block, head), as [B, d]."""
+    W = layout.k_chunk(head_dim)
+    kt = k_pool[layer, phys, head]
+    codes = kt[:block_size * head_dim].reshape(head_dim // W, block_size, W)
+    codes = np.concatenate([codes[c] for c in range(head_dim // W)], axis=1)   # [B, d]
+    scales = kt[block_size * head_dim:].astype(np.int64) - SCALE_BIAS
+    return decode(codes) * np.ldexp(1.0, scales)[:, None]
+
+
+def read_v_tile(v_pool, layer, phys, head, block_size, head_dim) -> np.ndarray:
+    """Dequantized V of all B slots of one (layer, block, head), as [B, d]."""
+    vt = v_pool[layer, phys, head]
+    codes = vt[:block_size * head_dim].reshape(head_dim, block_size).T            # [B, d]
+    scales = vt[block_size * head_dim:].astype(np.int64) - SCALE_BIAS
+    return decode(codes) * np.ldexp(1.0, scales)[:, None]
+
+
 def rebuild_sequence(k_pool, v_pool, layer, table, length, block_size, head_dim):
     """Dequantized contiguous K, V ([S, H_kv, d] float64) of one sequence."""
     num_kv_heads = k_pool.shape[2]
     K = np.zeros((length, num_kv_heads, head_dim), dtype=np.float64)
     V = np.zeros((length, num_kv_heads, head_dim), dtype=np.float64)
-    for t in range(length):
-        phys, off = int(table[t // block_size]), t % block_size
+    for lb in range(-(-length // block_size)):
+        phys, first = int(table[lb]), lb * block_size
+        valid = min(block_size, length - first)      # the last block may be partly filled
         for h in range(num_kv_heads):
-            K[t, h] = read_k(k_pool, layer, phys, h, off, block_size, head_dim)
-            V[t, h] = read_v(v_pool, layer, phys, h, off, block_size, head_dim)
+            K[first:first + valid, h] = read_k_tile(k_pool, layer, phys, h, block_size, head_dim)[:valid]
+            V[first:first + valid, h] = read_v_tile(v_pool, layer, phys, h, block_size, head_dim)[:valid]
     return K, V
 
 

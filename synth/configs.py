@@ -21,6 +21,8 @@ Shapes follow the workloads the pages describe:
   512-token chunks ("KV Cache Management", section "Chunked prefill
   mechanics", Figure 8): the batch holds chunk k = 1..4 of different prompts,
   i.e. histories of 0, 512, 1,024 and 1,536 cached tokens.
+* ``gqa70b_32k_fp8`` -- ``gqa70b_32k`` with b_elem = 1 ("KV Cache Management",
+  section "From Context Tokens to KV State", Eq. (1): one byte for FP8).
 * ``offload_overlap`` -- the ``gqa70b_32k`` decode batch keeps stepping while one
   more 16,384-token trajectory (the 70B example of "KV Cache Management",
   section "Retain, Evict, Recompute, or Offload", Figure 10) moves to pinned
@@ -45,7 +47,7 @@ class Workload:
     num_kv_heads: int
     head_dim: int
     block_size: int
-    dtype: str                 # "f32" or "bf16"
+    dtype: str                 # "f32", "bf16" or "fp8" (one-byte pool, bf16 queries)
     num_blocks: int            # physical blocks in the pool
     num_seqs: int
     # length recipe (interpreted by synth.gen.context_lengths)
@@ -74,7 +76,7 @@ class Workload:
 
     @property
     def elem_bytes(self) -> int:
-        return 4 if self.dtype == "f32" else 2
+        return {"f32": 4, "bf16": 2, "fp8": 1}[self.dtype]
 
     @property
     def group(self) -> int:
@@ -128,6 +130,12 @@ CONFIGS = [
         length_kind="fixed", length_min=32768, length_max=32768, mover_len=16384,
         offload_chunk_blocks=64,
         notes="gqa70b_32k decode batch + one 16,384-token trajectory swapped out and back",
+    ),
+    Workload(
+        name="gqa70b_32k_fp8", index=8, num_layers=80, num_q_heads=64, num_kv_heads=8,
+        head_dim=128, block_size=16, dtype="fp8", num_blocks=32768, num_seqs=16,
+        length_kind="fixed", length_min=32768, length_max=32768,
+        notes="gqa70b_32k with one-byte E4M3 storage (per-token, per-head scales)",
     ),
 ]
 

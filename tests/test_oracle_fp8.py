@@ -204,3 +204,22 @@ def test_quantize_rows_equals_per_vector():
     for r in range(40):
         c, b = fp8.quantize_vector(X[r])
         assert np.array_equal(codes[r], c) and sb[r] == b
+
+
+def test_tile_reads_equal_slot_reads():
+    L, N, H, B, d = 2, 4, 2, 4, 64
+    rng = np.random.default_rng(29)
+    kp = np.zeros(fp8.pool_shape(L, N, H, B, d), np.uint8)
+    vp = np.zeros_like(kp)
+    for p in range(N):
+        for h in range(H):
+            for o in range(B):
+                fp8.write_token(kp, vp, 1, p, h, o, rng.standard_normal(d) * 5,
+                                rng.standard_normal(d) / 3, B, d)
+    for p in range(N):
+        for h in range(H):
+            kt = fp8.read_k_tile(kp, 1, p, h, B, d)
+            vt = fp8.read_v_tile(vp, 1, p, h, B, d)
+            for o in range(B):
+                assert np.array_equal(kt[o], fp8.read_k(kp, 1, p, h, o, B, d))
+                assert np.array_equal(vt[o], fp8.read_v(vp, 1, p, h, o, B, d))

@@ -259,7 +259,6 @@ from tests import test_oracle_fp8 as T8  # noqa: E402
 
 encode_orig = ofp8.encode
 scale_orig = ofp8.scale_exponent
-dequant_orig = ofp8.dequantize_vector
 
 
 def _encode_ties_away(values):
@@ -279,8 +278,10 @@ def _scale_floor_rule(amax):
     return max(-127, min(127, math.frexp(float(amax))[1] - 9))   # wrong: may overflow 448
 
 
-def _dequant_no_scale(codes, scale_byte):
-    return ofp8.decode(codes)                                      # wrong: scale dropped
+def _v_tile_no_scale(v_pool, layer, phys, head, block_size, head_dim):
+    vt = v_pool[layer, phys, head]
+    codes = vt[:block_size * head_dim].reshape(head_dim, block_size).T
+    return ofp8.decode(codes)                                      # wrong: scale bytes ignored
 
 
 def test_mutant_fp8_ties_away(monkeypatch):
@@ -294,5 +295,5 @@ def test_mutant_fp8_scale_floor(monkeypatch):
 
 
 def test_mutant_fp8_scale_dropped(monkeypatch):
-    monkeypatch.setattr(ofp8, "dequantize_vector", _dequant_no_scale)
+    monkeypatch.setattr(ofp8, "read_v_tile", _v_tile_no_scale)
     _raises(T8.test_decode_equals_bf16_oracle_on_representable_values)
