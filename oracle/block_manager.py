@@ -27,6 +27,10 @@ Passages followed:
   indices) and the vacated accelerator blocks pushed to the free queue. The
   return path mirrors it: fresh blocks are reserved first, the entries point at
   them once the copy back completes, and the host frames are released.
+* "KV Cache Management", section "Prefix Caching Across Turns" (block-aligned
+  truncation): a request that hits a cached prefix starts with the cached full
+  blocks as the first entries of its table, one more reference each, and a
+  length of that many whole blocks; its own tokens go into fresh blocks.
 
 Every operation checks all of its preconditions before it changes anything, so a
 failed call leaves the manager exactly as it was.
@@ -188,6 +192,20 @@ class BlockManager:
         self._next_seq += 1
         self.tables[sid] = []
         self.lengths[sid] = 0
+        return sid
+
+    def seq_from_blocks(self, ids):
+        """New sequence whose table is `ids` (allocated blocks, one more reference
+        each) and whose length is len(ids) * B."""
+        ids = [int(b) for b in ids]
+        for b in ids:
+            if not 0 <= b < self.num_blocks or self.ref[b] == 0:
+                raise InvalidArgument(f"block {b} is not allocated")
+        sid = self.seq_new()
+        for b in ids:
+            self.ref[b] += 1
+        self.tables[sid] = ids
+        self.lengths[sid] = len(ids) * self.block_size
         return sid
 
     def fork(self, parent):

@@ -297,3 +297,128 @@ def test_mutant_fp8_scale_floor(monkeypatch):
 def test_mutant_fp8_scale_dropped(monkeypatch):
     monkeypatch.setattr(ofp8, "read_v_tile", _v_tile_no_scale)
     _raises(T8.test_decode_equals_bf16_oracle_on_representable_values)
+
+
+# ---- prefix cache (oracle/radix.py) --------------------------------------------------
+import oracle.radix as orx                                         # noqa: E402
+from tests import test_oracle_radix as TR                          # noqa: E402
+
+match_orig = orx.RadixCache.match
+walk_orig = orx.RadixCache._walk
+insert_orig = orx.RadixCache.insert
+
+
+def _match_no_truncation(self, tokens):
+    s_match, s_usable, blocks, handle = match_orig(self, tokens)
+    return s_match, s_match, blocks, handle                        # wrong: partial tail counted
+
+
+def _evict_most_recent(self, target_free):
+    out = []
+    while self.bm.num_free() < target_free:
+        cand = self.dormant_leaves()
+        if not cand:
+            break
+        leaf = max(cand, key=lambda n: (n.last_access, n.id))      # wrong: MRU first
+        self.bm.free_blocks(leaf.block_ids)
+        del leaf.parent.children[self._key(leaf.prefix_tokens, 0)]
+        del self.nodes[leaf.id]
+        out.append(leaf.id)
+    return out
+
+
+def _dormant_any(self):
+    # wrong: internal nodes count as candidates (children are dropped with them)
+    return [n for n in self.nodes.values() if n is not self.root and n.ref_count == 0
+            and all(c.ref_count == 0 for c in n.children.values())]
+
+
+def _evict_internal(self, target_free):
+    out = []
+    while self.bm.num_free() < target_free:
+        cand = _dormant_any(self)
+        if not cand:
+            break
+        node = min(cand, key=lambda n: (n.last_access, n.id))
+        stack = [node]
+        while stack:
+            n = stack.pop()
+            stack += list(n.children.values())
+            self.bm.free_blocks(n.block_ids)
+            del self.nodes[n.id]
+            out.append(n.id)
+        del node.parent.children[self._key(node.prefix_tokens, 0)]
+    return out
+
+
+def _match_no_pin(self, tokens):
+    s_match, s_usable, blocks, handle = match_orig(self, tokens)
+    n = self.nodes[handle]
+    while n is not self.root:                                      # wrong: pins undone at once
+        n.ref_count -= 1
+        n = n.parent
+    return s_match, s_usable, blocks, 0
+
+
+def _insert_adopts_all(self, tokens, blocks):
+    adopted = insert_orig(self, tokens, blocks)
+    nb = min(len(blocks), len(tokens) // self.B)
+    self.bm.incref([int(b) for b in blocks[:nb - adopted]])        # wrong: duplicates referenced too
+    return adopted
+
+
+def _walk_tail_plus_one(self, tokens):
+    path, partial, pb, s_match = walk_orig(self, tokens)
+    if s_match % self.B and s_match < len(tokens):
+        s_match += 1                                               # wrong: one token too many
+    return path, partial, pb, s_match
+
+
+def _insert_split_unpinned(self, tokens, blocks):
+    adopted = insert_orig(self, tokens, blocks)
+    for n in self.nodes.values():                                  # wrong: split parts lose pins
+        if n is not self.root and n.children and n.last_access == self.clock:
+            n.ref_count = 0
+    return adopted
+
+
+def _fails(fn, *args):
+    """The pin must fail: a failed assertion or the block manager refusing an
+    operation the mutant made inconsistent."""
+    with pytest.raises((AssertionError, obm.BlockManagerError)):
+        fn(*args)
+
+
+def test_mutant_radix_no_truncation(monkeypatch):
+    monkeypatch.setattr(orx.RadixCache, "match", _match_no_truncation)
+    _fails(TR.test_truncation_example)
+
+
+def test_mutant_radix_mru_eviction(monkeypatch):
+    monkeypatch.setattr(orx.RadixCache, "evict", _evict_most_recent)
+    _fails(TR.test_lru_order, 0)
+
+
+def test_mutant_radix_internal_eviction(monkeypatch):
+    monkeypatch.setattr(orx.RadixCache, "evict", _evict_internal)
+    _fails(TR.test_child_first)
+
+
+def test_mutant_radix_match_without_pin(monkeypatch):
+    monkeypatch.setattr(orx.RadixCache, "match", _match_no_pin)
+    _fails(TR.test_figure6_eviction)
+
+
+def test_mutant_radix_adopts_duplicates(monkeypatch):
+    monkeypatch.setattr(orx.RadixCache, "insert", _insert_adopts_all)
+    _fails(TR.test_brute_force_prefixes, 0, 4)
+
+
+def test_mutant_radix_partial_block_off_by_one(monkeypatch):
+    monkeypatch.setattr(orx.RadixCache, "_walk", _walk_tail_plus_one)
+    _fails(TR.test_brute_force_prefixes, 0, 4)
+
+
+def test_mutant_radix_split_drops_pins(monkeypatch):
+    monkeypatch.setattr(orx.RadixCache, "insert", _insert_split_unpinned)
+    _fails(TR.test_pin_counts, 0)
