@@ -15,7 +15,9 @@ fork_cow times copy-on-write copies + bulk suffix append + decode; offload
 times the gather -> host -> scatter round trip of half of each trajectory and
 checks that decode is bitwise identical before and after; offload_overlap runs
 the headline decode batch while one more trajectory goes to pinned host memory
-and back through the asynchronous swapper.
+and back through the asynchronous swapper; prefill_chunks times chunked
+prefill; prefix_reuse serves requests that share a cached system prompt through
+the radix prefix cache and prefills only their novel tokens.
 """
 
 from __future__ import annotations
@@ -55,6 +57,8 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--parity-samples", type=int, default=4)
+    ap.add_argument("--no-baseline-leg", action="store_true",
+                    help="prefix_reuse: skip the no-reuse comparison leg")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--unfused", action="store_true",
@@ -1028,6 +1032,293 @@ def run_overlap(args):
         sys.exit(1)
 
 
+# =============================================================================
+# Prefix reuse through the radix cache
+# =============================================================================
+def admit(bm, tree, prompts, block_size, watermark, clock=None):
+    """Admit a batch through the prefix cache: match every prompt (pinning the
+    cached path), evict dormant leaves if the free pool would fall below the
+    watermark, then start each sequence from its cached full blocks and reserve
+    blocks for the rest. Works on the library's or the oracle's objects.
+    `clock` (optional list of 3 floats) accumulates seconds spent matching,
+    evicting and reserving."""
+    c0 = time.perf_counter()
+    matches = [tree.match(p) for p in prompts]
+    need = sum(-(-(len(p) - m[1]) // block_size) for p, m in zip(prompts, matches))
+    c1 = time.perf_counter()
+    evicted = []
+    if bm.num_free() < need + watermark:
+        evicted = tree.evict(need + watermark)
+    c2 = time.perf_counter()
+    seqs = []
+    for p, m in zip(prompts, matches):
+        sid = bm.seq_from_blocks(m[2])
+        bm.append(sid, len(p) - m[1])
+        seqs.append(sid)
+    if clock is not None:
+        clock[0] += c1 - c0
+        clock[1] += c2 - c1
+        clock[2] += time.perf_counter() - c2
+    return seqs, [m[3] for m in matches], [m[1] for m in matches], evicted
+
+
+def retire(bm, tree, prompts, seqs, handles):
+    """Index the finished requests' blocks, drop their pins, release them."""
+    adopted = []
+    for p, sid, h in zip(prompts, seqs, handles):
+        adopted.append(tree.insert(p, bm.table(sid)))
+        tree.unpin(h)
+        bm.release(sid)
+    return adopted
+
+
+def run_prefix_reuse(args):
+    torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool = setup(args)
+    from synth import gen
+    L, n, Hq, Hkv, d, B = (cfg.num_layers, cfg.num_seqs, cfg.num_q_heads, cfg.num_kv_heads,
+                           cfg.head_dim, cfg.block_size)
+    P, C = cfg.prefix_len, cfg.chunk_len
+    budget, watermark = int(cfg.extra["budget_blocks"]), int(cfg.extra["watermark_blocks"])
+    n_steps = args.warmup + args.steps
+    system, novel = gen.prefix_reuse_tokens(cfg, n_steps)
+    prompts_of = [[np.concatenate([system, novel[k, i]]) for i in range(n)] for k in range(n_steps)]
+    S = P + C
+    maxb = -(-S // B)
+    bm = pk.BlockManager(budget, B)
+    tree = pk.RadixCache(bm)
+
+    # the system prompt's K/V per layer (inputs), written once by a cold prefill
+    k_sys = torch.randn((L, P, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    v_sys = torch.randn((L, P, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    q_all = torch.randn((L, n * C, Hq, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    k_all = torch.randn((L, n * C, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    v_all = torch.randn((L, n * C, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    out = torch.empty_like(q_all)
+
+    sid0 = bm.seq_new()
+    bm.append(sid0, P)
+    t0 = torch.tensor([bm.table(sid0)], dtype=torch.int32, device=dev)
+    zero1 = torch.zeros(1, dtype=torch.int32, device=dev)
+    qs0 = torch.tensor([0, P], dtype=torch.int32, device=dev)
+    q_sys = torch.empty((P, Hq, d), dtype=geom.torch_dtype, device=dev)
+    o_sys = torch.empty_like(q_sys)
+    with Timer(torch, stream) as tc:
+        for layer in range(L):
+            q_sys.normal_(generator=gen_)
+            pk.prefill(geom, k_pool, v_pool, layer, q_sys, k_sys[layer], v_sys[layer], o_sys, qs0, t0,
+                       zero1, P, P, stream=stream)
+    cold_ms = tc.ms
+    tree.insert(system, bm.table(sid0))
+    bm.release(sid0)
+    log(f"cold prefill of the {P}-token system prompt: {cold_ms:.2f} ms (80 layers, q drawn per layer)")
+
+    q_start = torch.arange(0, n * C + 1, C, dtype=torch.int32, device=dev)
+    tables_h = torch.empty((n, maxb), dtype=torch.int32).pin_memory()
+    ctx_h = torch.empty(n, dtype=torch.int32).pin_memory()
+    tables_d = torch.empty((n, maxb), dtype=torch.int32, device=dev)
+    ctx_d = torch.empty(n, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+
+    profiling = [False]
+    record = []          # per step: usable lengths, evicted ids, adopted counts
+    host_s = [0.0, 0.0]  # admission (including tables and their copy), retirement
+    parts = [0.0] * 5    # match, evict, reserve, build tables, queue table copies
+
+    def step(k):
+        prompts = prompts_of[k]
+        h0 = time.perf_counter()
+        seqs, handles, usable, evicted = admit(bm, tree, prompts, B, watermark, parts)
+        if any(u != P for u in usable):
+            raise RuntimeError(f"step {k}: cached prefix lost ({usable}); the budget is too small")
+        ha = time.perf_counter()
+        tabs, lens = bm.build_tables(seqs, maxb)
+        tables_h.numpy()[:] = tabs
+        ctx_h.numpy()[:] = np.asarray(usable, np.int32)
+        hb = time.perf_counter()
+        tables_d.copy_(tables_h, non_blocking=True)
+        ctx_d.copy_(ctx_h, non_blocking=True)
+        h1 = time.perf_counter()
+        parts[3] += hb - ha
+        parts[4] += h1 - hb
+        for layer in range(L):
+            prof = profiling[0] and layer % args.prof_every == 0
+            if prof:
+                pk.Profiler.enable(True)
+            pk.prefill(geom, k_pool, v_pool, layer, q_all[layer], k_all[layer], v_all[layer],
+                       out[layer], q_start, tables_d, ctx_d, C, S, stream=stream)
+            if prof:
+                pk.Profiler.enable(False)
+        h2 = time.perf_counter()
+        adopted = retire(bm, tree, prompts, seqs, handles)
+        h3 = time.perf_counter()
+        host_s[0] += h1 - h0
+        host_s[1] += h3 - h2
+        record.append((list(usable), list(evicted), adopted))
+        stream.synchronize()   # the step ends when its outputs are ready (time to first token)
+
+    for k in range(args.warmup):
+        step(k)
+    host_s[:] = [0.0, 0.0]
+    parts[:] = [0.0] * 5
+    if not args.no_prof:
+        pk.Profiler.reset()
+        profiling[0] = True
+    with Timer(torch, stream) as t:
+        for k in range(args.warmup, n_steps):
+            step(k)
+    profiling[0] = False
+    ms = max(t.ms, t.wall_ms) / args.steps
+    evicted_timed = sum(len(r[1]) for r in record[args.warmup:])
+    value = n / (ms * 1e-3)
+    info = tree.info()
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step, {value:.1f} requests/s; evicted "
+        f"{evicted_timed} nodes; tree {info}")
+
+    kern, roofline = {}, None
+    macs_layer = sum(2 * Hq * d * (C * P + C * (C + 1) // 2) for _ in range(n))
+    if not args.no_prof:
+        for name in ("prefill_append", "prefill_attention"):
+            cnt, tot = pk.Profiler.read(name)
+            if cnt:
+                kern[name] = {"launches": cnt, "avg_us": round(1e3 * tot / cnt, 2)}
+        if "prefill_attention" in kern:
+            avg_s = kern["prefill_attention"]["avg_us"] * 1e-6
+            ach = 2 * macs_layer / avg_s / 1e12
+            roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "kernel": "prefill_mfma_bf16_kernel", "flops_per_launch": 2 * macs_layer,
+                        "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    # host cost of one lookup of a full prompt (cached path of 4,096 tokens), through the binding
+    probe = prompts_of[-1][0]
+    reps = 2000
+    h0 = time.perf_counter()
+    for _ in range(reps):
+        _, _, _, h = tree.match(probe)
+        tree.unpin(h)
+    match_us = (time.perf_counter() - h0) / reps * 1e6
+
+    # parity: sampled (request, layer) outputs of the last step against the oracle,
+    # which takes the history from the inputs (the system prompt's K/V), not the pool
+    parity, cpu_baseline, radix_parity = None, None, None
+    if args.parity_samples or not args.no_cpu_baseline:
+        from oracle import attention as oatt
+        from oracle import layout as olayout
+        from oracle import prefill as opf
+        rng = np.random.default_rng(cfg.seed)
+        scale = oatt.default_scale(d)
+
+        def oracle_one(i, layer):
+            rows = slice(i * C, (i + 1) * C)
+            w = lambda x: olayout.widen(to_np(torch, x, cfg.dtype), cfg.dtype)  # noqa: E731
+            return opf.chunk_attention(w(q_all[layer, rows]), w(k_all[layer, rows]), w(v_all[layer, rows]),
+                                       w(k_sys[layer]), w(v_sys[layer]), scale)
+
+        errs = []
+        for _ in range(args.parity_samples):
+            i, layer = int(rng.integers(0, n)), int(rng.integers(0, L))
+            expect = oracle_one(i, layer)
+            got = out[layer, i * C:(i + 1) * C].float().cpu().numpy().astype(np.float64)
+            errs.append(float(np.max(np.abs(got - expect))))
+        if errs:
+            parity = {"samples": len(errs), "max_abs_err": max(errs), "tol": 2e-2,
+                      "ok": max(errs) <= 2e-2}
+            log(f"parity {parity}")
+
+        # the same admission / retirement sequence on the oracle block manager and tree
+        from oracle import block_manager as obm
+        from oracle import radix as orx
+        om = obm.BlockManager(budget, B)
+        ot = orx.RadixCache(om)
+        s0 = om.seq_new()
+        om.append(s0, P)
+        ot.insert(system, om.table(s0))
+        om.release(s0)
+        same = True
+        for k in range(n_steps):
+            prompts = prompts_of[k]
+            seqs, handles, usable, evicted = admit(om, ot, prompts, B, watermark)
+            adopted = retire(om, ot, prompts, seqs, handles)
+            same &= (list(usable), list(evicted), adopted) == record[k]
+        for _ in range(reps):                          # the timed lookups touched the tree too
+            _, _, _, h = ot.match(probe)
+            ot.unpin(h)
+        onodes = {x.id: (x.parent.id, x.ref_count, x.last_access, list(x.prefix_tokens),
+                         list(x.block_ids)) for x in ot.nodes.values() if x is not ot.root}
+        same &= onodes == tree.nodes() and list(om.free) == bm.free_list()
+        radix_parity = {"steps": n_steps, "requests": n * n_steps, "identical": bool(same)}
+        log(f"radix parity {radix_parity}")
+
+        if not args.no_cpu_baseline:
+            cores = len(os.sched_getaffinity(0))
+            pairs = [(int(rng.integers(0, n)), int(rng.integers(0, L))) for _ in range(max(1, args.cpu_sample // 12))]
+            c0 = time.perf_counter()
+            for (i, layer) in pairs:
+                oracle_one(i, layer)
+            per_pair = (time.perf_counter() - c0) / len(pairs)
+            c1 = time.perf_counter()
+            _, _, _, h = ot.match(probe)
+            ot.unpin(h)
+            radix_s = time.perf_counter() - c1
+            per_req = per_pair * L + radix_s
+            cpu_baseline = {"value": round(1.0 / per_req, 6), "unit": "requests/s", "cores": cores,
+                            "kind": "oracle",
+                            "sample": f"{len(pairs)} (request, layer) chunk attentions of this workload "
+                                      f"({per_pair:.2f} s each) x {L} layers + one oracle prefix match "
+                                      f"({radix_s * 1e3:.1f} ms)"}
+
+    # no reuse: the same requests prefilled from scratch (4,128 tokens each) in the rest of the pool
+    nr = None
+    if not args.no_baseline_leg:
+        tables_nr = (budget + torch.arange(n * maxb, dtype=torch.int32, device=dev)).view(n, maxb)
+        q_nr = torch.randn((n * S, Hq, d), generator=gen_, device=dev).to(geom.torch_dtype)
+        k_nr = torch.randn((n * S, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+        v_nr = torch.randn((n * S, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+        o_nr = torch.empty_like(q_nr)
+        qs_nr = torch.arange(0, n * S + 1, S, dtype=torch.int32, device=dev)
+        z_nr = torch.zeros(n, dtype=torch.int32, device=dev)
+        pk.prefill(geom, k_pool, v_pool, 0, q_nr, k_nr, v_nr, o_nr, qs_nr, tables_nr, z_nr, S, S,
+                   stream=stream)
+        with Timer(torch, stream) as tn:
+            for layer in range(L):
+                pk.prefill(geom, k_pool, v_pool, layer, q_nr, k_nr, v_nr, o_nr, qs_nr, tables_nr, z_nr,
+                           S, S, stream=stream)
+        nr_ms = max(tn.ms, tn.wall_ms)
+        nr = {"ms_per_step": round(nr_ms, 3), "requests_per_s": round(n / (nr_ms * 1e-3), 2),
+              "prefill_tokens": n * S, "speedup_with_reuse": round(nr_ms / ms, 1),
+              "note": "same 16 prompts prefilled from token 0 (attention + K/V write, 80 layers); "
+                      "one step, inputs reused across layers"}
+        log(f"no reuse: {nr}")
+
+    result = {
+        "metric": "prefix-hit prefill requests/s (radix prefix cache + paged prefill attention), "
+                  "70B-GQA, 4,096 cached + 32 novel tokens",
+        "value": round(value, 2), "unit": "requests/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded token ids and N(0,1) Q/K/V)",
+        "config": {"workload": cfg.name, "num_layers": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": d, "block_size": B, "requests_per_step": n, "prefix_tokens": P,
+                   "novel_tokens": C, "cache_budget_blocks": budget, "watermark_blocks": watermark,
+                   "launch": "eager"},
+        "host": {"admit_us_per_request": round(host_s[0] / (args.steps * n) * 1e6, 2),
+                 "retire_us_per_request": round(host_s[1] / (args.steps * n) * 1e6, 2),
+                 "admit_parts_us_per_request": {
+                     k_: round(v_ / (args.steps * n) * 1e6, 2) for k_, v_ in
+                     zip(("match", "evict", "reserve", "build_tables", "queue_copies"), parts)},
+                 "match_unpin_us_4128_tokens": round(match_us, 2),
+                 "evicted_nodes_timed": evicted_timed, "tree": info},
+        "cold_system_prefill_ms": round(cold_ms, 3),
+        "no_reuse": nr,
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "kernels": kern,
+        "parity": parity,
+        "radix_parity": radix_parity,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -1045,6 +1336,8 @@ def main():
         run_overlap(args)
     elif cfg.length_kind == "prefill":
         run_prefill(args)
+    elif cfg.length_kind == "prefix":
+        run_prefix_reuse(args)
     elif cfg.length_kind == "fork":
         run_fork(args)
     else:

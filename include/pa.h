@@ -261,6 +261,8 @@ pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* fr
                        pa_bm** out);
 void pa_bm_destroy(pa_bm* bm);
 int32_t pa_bm_num_free(const pa_bm* bm);
+/* Tokens per block, -1 for NULL. */
+int32_t pa_bm_block_size(const pa_bm* bm);
 /* Reference count of a block, -1 if the id is out of range. */
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t block);
 
@@ -276,6 +278,11 @@ pa_status pa_bm_incref(pa_bm* bm, const int32_t* ids, int32_t n);
 pa_status pa_bm_free_blocks(pa_bm* bm, const int32_t* ids, int32_t n);
 
 pa_status pa_bm_seq_new(pa_bm* bm, int32_t* seq_out);
+/* New sequence whose table is the n listed (allocated) blocks, each gaining a
+ * reference, and whose length is n * block_size: a request that hit a cached
+ * prefix starts from its full blocks ("KV Cache Management", section "Prefix
+ * Caching Across Turns", block-aligned truncation). n may be 0. */
+pa_status pa_bm_seq_from_blocks(pa_bm* bm, const int32_t* ids, int32_t n, int32_t* seq_out);
 /* Child gets a copy of the parent's table and length; every block gains a reference. */
 pa_status pa_bm_seq_fork(pa_bm* bm, int32_t parent, int32_t* child_out);
 /* Reserve n_tokens more positions. slots_out (may be NULL) receives n_tokens
@@ -442,6 +449,69 @@ int32_t pa_swapper_pending(const pa_swapper* s);
 pa_status pa_swapper_info(const pa_swapper* s, void** host_frames, void** kernel_stream,
                           void** dma_stream, int64_t* frame_bytes, int32_t* chunk_blocks,
                           int64_t* bytes_out, int64_t* bytes_in);
+
+/* ---------------------------------------------------------------- radix prefix cache */
+/* Source: "KV Cache Management", section "Prefix Caching Across Turns" (Table 4,
+ * Definition 0.2, "Longest prefix matching", "Dynamic radix eviction",
+ * Figure 6). A host-side index of cached KV blocks over a block manager. Each
+ * node binds a run of token ids to the physical blocks that hold them, with a
+ * parent, children, a reference count (requests currently using it) and a last
+ * access time; non-branching runs share one node. Only whole blocks are indexed:
+ * edges split at block boundaries, and a node's children are keyed by the
+ * block_size tokens of their first block. The tree holds one block-manager
+ * reference per block it indexes and drops it on eviction; the block manager must
+ * outlive the tree. Node ids are assigned 1, 2, ... in creation order (0 is the
+ * root) and never reused. A logical clock ticks once per match and per insert.
+ * Every call takes the tree's mutex. */
+typedef struct pa_radix pa_radix;
+
+pa_status pa_radix_create(pa_bm* bm, pa_radix** out);
+/* Drops the tree's reference on every indexed block, then frees the tree. */
+pa_status pa_radix_destroy(pa_radix* r);
+/* Longest prefix match of tokens[0..n_tokens): *s_match gets the number of
+ * leading tokens found in the tree (token level, into a partly matching block),
+ * *s_usable = floor(s_match / block_size) * block_size, and blocks_out the
+ * s_usable / block_size block ids that hold them, in order. Every node on the
+ * matched path (including one used only in part) gains a pin and gets the new
+ * clock value as its last access; *handle names the deepest such node (0 when
+ * nothing was matched) and pa_radix_unpin(handle) removes exactly these pins.
+ * PA_ERR_INVALID_ARG, with nothing changed, if cap < s_usable / block_size. */
+pa_status pa_radix_match(pa_radix* r, const int32_t* tokens, int64_t n_tokens, int64_t* s_match,
+                         int64_t* s_usable, int32_t* blocks_out, int32_t cap, int32_t* n_blocks,
+                         int64_t* handle);
+/* Remove one pin from the node and each of its ancestors. PA_ERR_NOT_FOUND for
+ * an unknown (or evicted) node, PA_ERR_INVALID_ARG if some node on the path has
+ * no pin; handle 0 is a no-op. */
+pa_status pa_radix_unpin(pa_radix* r, int64_t handle);
+/* Index a finished request: blocks[k] holds tokens[k*B .. (k+1)*B). Only the
+ * first min(n_blocks, n_tokens / B) whole blocks count. Blocks already indexed
+ * under the same tokens stay as they are (the caller's copies are not taken);
+ * the rest form one new node below the longest matched path (a node matched in
+ * part is split at the block boundary first) and gain one reference each.
+ * *adopted (may be NULL) gets the number of blocks taken. PA_ERR_INVALID_ARG,
+ * with nothing changed, if a block to be taken is not allocated. */
+pa_status pa_radix_insert(pa_radix* r, const int32_t* tokens, int64_t n_tokens,
+                          const int32_t* blocks, int32_t n_blocks, int32_t* adopted);
+/* Leaf-first LRU eviction: while the block manager has fewer than target_free
+ * free blocks, remove the dormant leaf (no pin, no children) with the oldest
+ * last access (ties: lower id), dropping the tree's reference on its blocks;
+ * a parent left without children and pins becomes a candidate in turn. The
+ * first min(cap, count) evicted ids go to ids_out in order; *n_evicted (may be
+ * NULL) gets the count. Stops early when no candidate is left. */
+pa_status pa_radix_evict(pa_radix* r, int32_t target_free, int64_t* ids_out, int32_t cap,
+                         int32_t* n_evicted);
+/* Counts (any output may be NULL): nodes (root excluded), indexed blocks,
+ * dormant leaves (eviction candidates), pinned nodes. */
+pa_status pa_radix_info(const pa_radix* r, int64_t* nodes, int64_t* blocks, int64_t* dormant,
+                        int64_t* pinned);
+/* Ids of all nodes (root excluded) in increasing order: the first min(cap, n)
+ * to ids_out, *n_out gets n. */
+pa_status pa_radix_node_ids(const pa_radix* r, int64_t* ids_out, int64_t cap, int64_t* n_out);
+/* One node: meta_out[0..3] = parent id, pin count, last access, number of
+ * blocks; its tokens (up to tok_cap) and blocks (up to blk_cap) are copied out.
+ * PA_ERR_NOT_FOUND for an unknown id. */
+pa_status pa_radix_node(const pa_radix* r, int64_t id, int64_t* meta_out, int32_t* tokens_out,
+                        int64_t tok_cap, int32_t* blocks_out, int32_t blk_cap);
 
 #ifdef __cplusplus
 }

@@ -148,16 +148,18 @@ class RadixCache:
         nb = min(len(blocks), len(tokens) // B)
         tokens, blocks = tokens[:nb * B], [int(b) for b in blocks[:nb]]
         path, partial, pb, _ = self._walk(tokens)
-        t = self._tick()
-        touched = path + ([partial] if partial is not None and pb > 0 else [])
-        for n in touched:
-            n.last_access = t
-        node = path[-1] if path else self.root
         done = sum(len(n.block_ids) for n in path)
-        if partial is not None and pb > 0:
-            if done + pb >= nb:                      # every block already indexed
-                return 0
-            # split the partly matched node after its first pb blocks
+        split = partial is not None and pb > 0
+        start = done + (pb if split else 0)           # first block the tree lacks
+        if start < nb:
+            self.bm.incref(blocks[start:])            # checks every id before any change
+        t = self._tick()
+        for n in path + ([partial] if split else []):
+            n.last_access = t
+        if start >= nb:                               # every block already indexed
+            return 0
+        node = path[-1] if path else self.root
+        if split:                                     # the partly matched node splits after pb blocks
             upper = Node(self._next_id, partial.prefix_tokens[:pb * B], partial.block_ids[:pb],
                          partial.parent)
             self._next_id += 1
@@ -169,15 +171,12 @@ class RadixCache:
             partial.block_ids = partial.block_ids[pb:]
             partial.parent = upper
             upper.children[self._key(partial.prefix_tokens, 0)] = partial
-            node, done = upper, done + pb
-        if done >= nb:
-            return 0
-        new = Node(self._next_id, tokens[done * B:], blocks[done:], node)
+            node = upper
+        new = Node(self._next_id, tokens[start * B:], blocks[start:], node)
         self._next_id += 1
         self.nodes[new.id] = new
         new.last_access = t
         node.children[self._key(new.prefix_tokens, 0)] = new
-        self.bm.incref(new.block_ids)
         return len(new.block_ids)
 
     # ---- eviction ------------------------------------------------------------

@@ -9,7 +9,7 @@ fallback implementation.
 from ._lib import (DoubleFreeError, OutOfBlocksError, OutOfFramesError, PagedKVError,  # noqa: F401
                    LIB_PATH, PA_TIER_HBM, PA_TIER_HOST, PA_TIER_PENDING_IN, PA_TIER_PENDING_OUT,
                    load as _load)
-from .api import (BlockManager, Geometry, Profiler, Swapper, alloc_pools, append_kv,  # noqa: F401
+from .api import (BlockManager, Geometry, Profiler, RadixCache, Swapper, alloc_pools, append_kv,  # noqa: F401
                   blocks_for_tokens, bytes_per_block, bytes_per_token, copy_blocks,
                   copy_to_device, copy_to_host, decode, decode_append, decode_workspace_bytes,
                   gather_blocks, pool_bytes, prefill, scatter_blocks)

@@ -68,11 +68,13 @@ SIGNATURES = {
     "pa_bm_create": (_i32, [_i32, _i32, _pi32, C.POINTER(_vp)]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_num_free": (_i32, [_vp]),
+    "pa_bm_block_size": (_i32, [_vp]),
     "pa_bm_refcount": (_i32, [_vp, _i32]),
     "pa_bm_alloc": (_i32, [_vp, _i32, _pi32]),
     "pa_bm_incref": (_i32, [_vp, _pi32, _i32]),
     "pa_bm_free_blocks": (_i32, [_vp, _pi32, _i32]),
     "pa_bm_seq_new": (_i32, [_vp, _pi32]),
+    "pa_bm_seq_from_blocks": (_i32, [_vp, _pi32, _i32, _pi32]),
     "pa_bm_seq_fork": (_i32, [_vp, _i32, _pi32]),
     "pa_bm_seq_append": (_i32, [_vp, _i32, _i32, _pi64, _pi32, _pi32, _pi32]),
     "pa_bm_append_batch": (_i32, [_vp, _pi32, _pi32, _i32, _pi64, _pi32, _pi32, _pi32]),
@@ -103,6 +105,15 @@ SIGNATURES = {
     "pa_swapper_pending": (_i32, [_vp]),
     "pa_swapper_info": (_i32, [_vp, C.POINTER(_vp), C.POINTER(_vp), C.POINTER(_vp), _pi64, _pi32,
                                _pi64, _pi64]),
+    "pa_radix_create": (_i32, [_vp, C.POINTER(_vp)]),
+    "pa_radix_destroy": (_i32, [_vp]),
+    "pa_radix_match": (_i32, [_vp, _pi32, _i64, _pi64, _pi64, _pi32, _i32, _pi32, _pi64]),
+    "pa_radix_unpin": (_i32, [_vp, _i64]),
+    "pa_radix_insert": (_i32, [_vp, _pi32, _i64, _pi32, _i32, _pi32]),
+    "pa_radix_evict": (_i32, [_vp, _i32, _pi64, _i32, _pi32]),
+    "pa_radix_info": (_i32, [_vp, _pi64, _pi64, _pi64, _pi64]),
+    "pa_radix_node_ids": (_i32, [_vp, _pi64, _i64, _pi64]),
+    "pa_radix_node": (_i32, [_vp, _i64, _pi64, _pi32, _i64, _pi32, _i32]),
 }
 
 _lib = None

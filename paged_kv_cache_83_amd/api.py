@@ -408,6 +408,15 @@ class BlockManager:
         check(self._lib.pa_bm_seq_new(self._h, C.byref(s)), "pa_bm_seq_new")
         return s.value
 
+    def seq_from_blocks(self, ids) -> int:
+        """New sequence starting from the listed cached full blocks (one more
+        reference each), length len(ids) * block_size."""
+        a = _i32arr(ids)
+        s = C.c_int32()
+        check(self._lib.pa_bm_seq_from_blocks(self._h, _p32(a), a.size, C.byref(s)),
+              "pa_bm_seq_from_blocks")
+        return s.value
+
     def fork(self, parent: int) -> int:
         s = C.c_int32()
         check(self._lib.pa_bm_seq_fork(self._h, parent, C.byref(s)), "pa_bm_seq_fork")
@@ -537,6 +546,91 @@ class BlockManager:
     def swap_in_finish(self, seq: int, logical):
         a = _i32arr(logical)
         check(self._lib.pa_bm_swap_in_finish(self._h, seq, _p32(a), a.size), "pa_bm_swap_in_finish")
+
+
+class RadixCache:
+    """Radix prefix cache of libpa over a BlockManager (host only): longest
+    prefix match with block-aligned truncation, insertion of finished requests,
+    leaf-first LRU eviction. Keeps the BlockManager alive."""
+
+    def __init__(self, bm: BlockManager):
+        self._lib = _L()
+        self.bm = bm
+        self.block_size = bm.block_size
+        h = C.c_void_p()
+        check(self._lib.pa_radix_create(bm._h, C.byref(h)), "pa_radix_create")
+        self._h = h
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self._lib.pa_radix_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def match(self, tokens):
+        """(s_match, s_usable, block ids of the usable prefix, handle); pins the path."""
+        t = _i32arr(tokens)
+        out = np.empty(t.size // self.block_size + 1, np.int32)
+        sm, su, h = C.c_int64(), C.c_int64(), C.c_int64()
+        nb = C.c_int32()
+        check(self._lib.pa_radix_match(self._h, _p32(t), t.size, C.byref(sm), C.byref(su), _p32(out),
+                                       out.size, C.byref(nb), C.byref(h)), "pa_radix_match")
+        return int(sm.value), int(su.value), out[:nb.value].tolist(), int(h.value)
+
+    def unpin(self, handle: int):
+        check(self._lib.pa_radix_unpin(self._h, int(handle)), "pa_radix_unpin")
+
+    def insert(self, tokens, blocks) -> int:
+        """Index a finished request's whole blocks; returns how many were adopted."""
+        t, b = _i32arr(tokens), _i32arr(blocks)
+        n = C.c_int32()
+        check(self._lib.pa_radix_insert(self._h, _p32(t), t.size, _p32(b), b.size, C.byref(n)),
+              "pa_radix_insert")
+        return int(n.value)
+
+    def evict(self, target_free: int):
+        """Evict dormant leaves, LRU first, until target_free blocks are free;
+        returns the evicted node ids in order."""
+        cap = max(1, self.info()["nodes"])
+        out = np.empty(cap, np.int64)
+        n = C.c_int32()
+        check(self._lib.pa_radix_evict(self._h, int(target_free), _p64(out), cap, C.byref(n)),
+              "pa_radix_evict")
+        return out[:n.value].tolist()
+
+    def info(self):
+        v = [C.c_int64() for _ in range(4)]
+        check(self._lib.pa_radix_info(self._h, *[C.byref(x) for x in v]), "pa_radix_info")
+        return dict(zip(("nodes", "blocks", "dormant", "pinned"), (int(x.value) for x in v)))
+
+    def node_ids(self):
+        n = C.c_int64()
+        check(self._lib.pa_radix_node_ids(self._h, None, 0, C.byref(n)), "pa_radix_node_ids")
+        out = np.empty(max(1, n.value), np.int64)
+        check(self._lib.pa_radix_node_ids(self._h, _p64(out), out.size, C.byref(n)),
+              "pa_radix_node_ids")
+        return out[:n.value].tolist()
+
+    def node(self, node_id: int):
+        """(parent, pins, last access, tokens, blocks) of one node."""
+        meta = np.zeros(4, np.int64)
+        check(self._lib.pa_radix_node(self._h, node_id, _p64(meta), None, 0, None, 0),
+              "pa_radix_node")
+        nb = int(meta[3])
+        toks = np.empty(max(1, nb * self.block_size), np.int32)
+        blks = np.empty(max(1, nb), np.int32)
+        check(self._lib.pa_radix_node(self._h, node_id, _p64(meta), _p32(toks), toks.size,
+                                      _p32(blks), blks.size), "pa_radix_node")
+        return (int(meta[0]), int(meta[1]), int(meta[2]), toks[:nb * self.block_size].tolist(),
+                blks[:nb].tolist())
+
+    def nodes(self):
+        return {i: self.node(i) for i in self.node_ids()}
 
 
 class Swapper:

@@ -6,6 +6,7 @@
 //
 // Block manager: "KV Cache Management", sections "The PagedAttention virtual
 // memory model" (allocate at o == 0, write in place otherwise; FIFO free list),
+// "Prefix Caching Across Turns" (a request starts from cached full blocks),
 // "Zero-copy deliberation via copy-on-write branching" (fork, copy-on-write,
 // release) and "Asynchronous paged swapping" (frames leave and re-enter the
 // pool); "PagedAttention" (Inference book, ch. 14) for the error contract
@@ -271,6 +272,8 @@ int32_t pa_bm_num_free(const pa_bm* bm) {
   return (int32_t)bm->free_list.size();
 }
 
+int32_t pa_bm_block_size(const pa_bm* bm) { return bm ? bm->block_size : -1; }
+
 int32_t pa_bm_refcount(const pa_bm* bm, int32_t b) {
   if (!bm || b < 0 || b >= bm->num_blocks) return -1;
   std::lock_guard<std::mutex> lk(bm->mu);
@@ -324,6 +327,21 @@ pa_status pa_bm_seq_new(pa_bm* bm, int32_t* seq_out) {
   std::lock_guard<std::mutex> lk(bm->mu);
   int32_t s = bm->next_seq++;
   bm->seqs.emplace(s, Seq());
+  *seq_out = s;
+  return PA_OK;
+}
+
+pa_status pa_bm_seq_from_blocks(pa_bm* bm, const int32_t* ids, int32_t n, int32_t* seq_out) {
+  if (!bm || !seq_out || n < 0 || (n > 0 && !ids)) return PA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(bm->mu);
+  for (int32_t i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= bm->num_blocks || bm->ref[ids[i]] == 0) return PA_ERR_INVALID_ARG;
+  Seq q;
+  q.table.assign(ids, ids + n);
+  q.len = (int64_t)n * bm->block_size;
+  for (int32_t b : q.table) ++bm->ref[b];
+  int32_t s = bm->next_seq++;
+  bm->seqs.emplace(s, std::move(q));
   *seq_out = s;
   return PA_OK;
 }

@@ -1,4 +1,4 @@
-"""The five decode workloads, as geometry plus a recipe for their random parts.
+"""The workloads, as geometry plus a recipe for their random parts.
 
 Shapes follow the workloads the pages describe:
 
@@ -28,6 +28,13 @@ Shapes follow the workloads the pages describe:
   section "Retain, Evict, Recompute, or Offload", Figure 10) moves to pinned
   host memory and back on a copy stream of its own (same page, section
   "Asynchronous paged swapping").
+* ``prefix_reuse`` -- requests to the 70B geometry that share a 4,096-token
+  system prompt and bring 32 novel tokens each ("KV Cache Management", section
+  "Prefix Caching Across Turns", Napkin Math 0.4): the radix prefix cache
+  resolves the prompt, only the novel tokens are prefilled over the cached
+  history, and the finished requests' blocks are indexed and evicted leaf-first
+  (LRU) under a 384-block budget (the 256-block prompt plus room for four
+  batches), so that every step from the fourth on evicts.
 
 Seeds: workload k (1-based, in the order above) uses master seed 8300 + k.
 """
@@ -136,6 +143,14 @@ CONFIGS = [
         head_dim=128, block_size=16, dtype="fp8", num_blocks=32768, num_seqs=16,
         length_kind="fixed", length_min=32768, length_max=32768,
         notes="gqa70b_32k with one-byte E4M3 storage (per-token, per-head scales)",
+    ),
+    Workload(
+        name="prefix_reuse", index=9, num_layers=80, num_q_heads=64, num_kv_heads=8,
+        head_dim=128, block_size=16, dtype="bf16", num_blocks=384 + 16 * 258 + 32, num_seqs=16,
+        length_kind="prefix", prefix_len=4096, chunk_len=32,
+        notes="16 requests per step: 4,096 cached system tokens + 32 novel tokens each; the "
+              "prefix cache runs in the first 384 blocks, the no-reuse comparison in the rest",
+        extra={"budget_blocks": 384, "watermark_blocks": 32},
     ),
 ]
 

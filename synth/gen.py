@@ -16,7 +16,7 @@ import numpy as np
 from .configs import Workload
 
 # Sub-stream indices (fixed forever: changing one changes every input).
-_LENGTHS, _FREE_ORDER, _SUFFIX, _OFFLOAD, _VALUES, _REALLOC = range(6)
+_LENGTHS, _FREE_ORDER, _SUFFIX, _OFFLOAD, _VALUES, _REALLOC, _TOKENS = range(7)
 
 
 def _stream(seed: int, which: int) -> np.random.Generator:
@@ -42,6 +42,8 @@ def context_lengths(cfg: Workload) -> np.ndarray:
         return cfg.prefix_len + suffix_lengths(cfg)
     if cfg.length_kind == "prefill":
         return prefill_histories(cfg) + cfg.chunk_len
+    if cfg.length_kind == "prefix":
+        return np.full(n, cfg.prefix_len + cfg.chunk_len, dtype=np.int64)
     raise ValueError(cfg.length_kind)
 
 
@@ -117,3 +119,14 @@ def value_seed(cfg: Workload, tag: int) -> int:
 
 # Tags for value tensors (stable).
 TAG_Q, TAG_KNEW, TAG_VNEW, TAG_KPOOL, TAG_VPOOL, TAG_KHIST, TAG_VHIST = range(7)
+
+
+def prefix_reuse_tokens(cfg: Workload, n_steps: int, vocab: int = 32000):
+    """Token ids of the prefix-reuse workload: one shared system prompt of
+    cfg.prefix_len tokens and, for each of n_steps steps, cfg.num_seqs requests of
+    cfg.chunk_len novel tokens (int32 arrays; the prompt of a request is the
+    system prompt followed by its novel tokens)."""
+    rng = _stream(cfg.seed, _TOKENS)
+    system = rng.integers(0, vocab, cfg.prefix_len).astype(np.int32)
+    novel = rng.integers(0, vocab, (n_steps, cfg.num_seqs, cfg.chunk_len)).astype(np.int32)
+    return system, novel
