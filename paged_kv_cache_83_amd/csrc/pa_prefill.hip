@@ -13,13 +13,20 @@
 // (chunk, KV head): the G query heads of the group times 128/G consecutive chunk
 // tokens, 32 rows per wave, as two 16-column MFMA tiles. It walks the visible
 // keys in pairs of blocks (32 keys). Each pair's K and V tiles (4 per pair) are
-// loaded once for the 128 rows into LDS with 16-byte loads, double-buffered so
-// the next pair's loads are in flight while the current pair is computed, then
-// read as MFMA operand fragments at the same offsets the decode kernel uses on
-// the pool (the LDS image has the pool's tile layout):
+// loaded once for the 128 rows straight from global memory into LDS (16 bytes
+// per lane), two pairs ahead of use in three rotating images, then read as MFMA
+// operand fragments at the same offsets the decode kernel uses on the pool (the
+// LDS image has the pool's tile layout):
 //   S^T[32 keys][16 rows] = K[keys][d] . Q^T[d][rows]     (two tiles of rows)
 //   O^T[d][16 rows]      += V^T[d][keys] . P^T[keys][rows]
-// with the online-softmax update of the same section between them. Work-group
+// with the online-softmax update of the same section between them. The QK^T
+// products of the next pair are issued before the softmax of the current one,
+// so the matrix cores and the vector ALUs work at the same time. The vector
+// work per pair is kept small: the causal mask only on pairs that cross some
+// row's position, the softmax scale folded into the exponent's FMA, and the
+// accumulators rescaled only when a row's maximum has grown by more than 2^8
+// over the reference it exponentiates against (the result is the same; the
+// reference is only a bound on the size of the probabilities). Work-group
 // order is XCD-aware: the tiles of one (chunk, KV head) run one after another on
 // one XCD, so its history is read from HBM once and from that XCD's L2 after.
 
@@ -39,6 +46,18 @@ using namespace pa_detail;
 constexpr int kPfWaves = 4;
 constexpr int kPfRowsPerWave = 32;                  // two 16-column MFMA tiles
 constexpr int kPfRows = kPfWaves * kPfRowsPerWave;  // query rows per work group
+
+// Wait until at most N of this wave's global-to-LDS loads are in flight and its
+// LDS reads have completed, then synchronise the work group. Written out because
+// the barrier intrinsic with a fence waits for every outstanding load.
+template <int N>
+__device__ __forceinline__ void lds_wait_sync() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Growth of a row's maximum (log2 units) tolerated before the accumulators are
+// rescaled to a new reference.
+constexpr float kLazyLog2 = 8.0f;
 
 template <int D>
 struct PfCfg {
@@ -62,7 +81,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int LOADS = PfCfg<D>::LOADS;
   constexpr int TQ = kPfRows / G;        // chunk tokens per work group
   constexpr int TW = kPfRowsPerWave / G;  // chunk tokens per wave
-  extern __shared__ __align__(16) unsigned char pf_smem[];  // two pair buffers
+  extern __shared__ __align__(16) unsigned char pf_smem[];  // three pair images
 
   const int64_t items = (int64_t)cb.n_seqs * Hkv * n_tiles;
   const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
@@ -81,7 +100,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int npairs = (nblk + 1) >> 1;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, c = lane & 15, gq = lane >> 4;
+  // the wave index is uniform; readfirstlane lets the compiler keep what derives
+  // from it (tile choice, load bases) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, c = lane & 15, gq = lane >> 4;
 
   // Query rows of this wave: row r = 16*ct + c is token t0 + TW*wave + r/G,
   // query head g*G + r%G. Rows past the chunk end get zero queries (finite
@@ -104,6 +126,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   }
 
+  // Smallest query position of the wave (its first row, or every row past the
+  // chunk end): pairs wholly at or below it need no causal mask.
+  const int qmin = (t0 + TW * wave < q_len) ? ctx + t0 + TW * wave : kmax - 1;
+
   f32x4 acc[2][DT];
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
@@ -117,24 +143,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const char* vl = reinterpret_cast<const char*>(vpool + layer_off);
 
   // Pair image in LDS: [K blk0][K blk1][V blk0][V blk1], each tile as in the pool.
-  u32x4 pre[LOADS];
-  auto fetch = [&](int pj) {
+  // Three images rotate: the pair whose softmax and PV are being done, the next
+  // pair (its keys are read for QK^T one step early) and the pair after that
+  // (its loads in flight). Loads go from global memory straight into LDS: lane
+  // l of wave w puts its 16 bytes at image offset 16 * (256 u + 64 w + l), the
+  // same place the thread's own store would. The compiler does not order these
+  // loads against LDS reads, so each step waits for them itself (vmcnt) before
+  // its one barrier.
+  const char* kg = kl + (int64_t)g * TILE;  // head g's tile in block 0
+  const char* vg = vl + (int64_t)g * TILE;
+  const int64_t blk_stride = (int64_t)Hkv * TILE;
+  auto issue = [&](int pj, int buf) {
     const int b0 = 2 * pj;
     const int p0 = guard_block(trow[b0], N);
     const int p1 = (b0 + 1 < nblk) ? guard_block(trow[b0 + 1], N) : p0;
+    unsigned char* img = pf_smem + buf;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int off = (u * 256 + tid) * 16;  // byte offset in the pair image
-      const int tl = off / TILE;
+      const int woff = (u * 256 + wave * 64) * 16;  // the wave's first byte in the image
+      const int tl = woff / TILE;                   // tile of the whole wave
       const int p = (tl & 1) ? p1 : p0;
-      const char* base = (tl < 2 ? kl : vl) + ((int64_t)p * Hkv + g) * TILE;
-      pre[u] = *reinterpret_cast<const u32x4*>(base + (off - tl * TILE));
+      const char* base = (tl < 2 ? kg : vg) + p * blk_stride + (woff - tl * TILE);
+      __builtin_amdgcn_global_load_lds(base + lane * 16,
+                                       (__attribute__((address_space(3))) void*)(img + woff), 16,
+                                       0, 0);
     }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < LOADS; ++u)
-      *reinterpret_cast<u32x4*>(pf_smem + buf * PAIR + (u * 256 + tid) * 16) = pre[u];
   };
 
   // Score row c of each tile holds pair-local key 8*(c>>2) + 4*t + (c&3): block
@@ -145,9 +178,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int v_sel = gq >> 1;
   const int v_off = 32 * c + 16 * (gq & 1);  // bytes
 
-  auto compute = [&](int pj, int buf) {
-    const unsigned char* img = pf_smem + buf * PAIR;
-    u32x4 kf[2][KC], vf[DT];
+  // S^T of one pair for both row tiles: K fragments from the pair's image, then
+  // the QK^T products (their results are consumed one step later).
+  auto scores = [&](int buf, f32x4 (&sc)[2][2]) {
+    const unsigned char* img = pf_smem + buf;
+    u32x4 kf[2][KC];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -155,8 +190,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         kf[t][kc] = *reinterpret_cast<const u32x4*>(img + k_sel * TILE + kc * 1024 +
                                                     (k_off0 + 4 * t) * 64 + 16 * gq);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      vf[dt] = *reinterpret_cast<const u32x4*>(img + (2 + v_sel) * TILE + dt * 512 + v_off);
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        sc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          sc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, kf[t][kc]), qf[ct][kc], sc[ct][t], 0, 0, 0);
+      }
+  };
+
+  // Softmax update and PV of pair pj from its scores and its V image.
+  auto finish = [&](int pj, const u32x4 (&vin)[DT], const f32x4 (&sc)[2][2]) {
+    u32x4 vf[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vf[dt] = vin[dt];
     const int key0 = 32 * pj + 8 * gq;  // this lane's keys: key0 + 4*t + e (scores), key0 + e (V)
     if (32 * pj + 32 > kmax) {          // slots past the valid data: V zeroed (0 * NaN guard)
       u32x4 keep;
@@ -168,46 +217,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) vf[dt] &= keep;
     }
+    // Scores stay unscaled through the mask and the maximum (the scale is
+    // positive); the scale enters in the exponent: p = 2^(s * c - m * c).
+    const bool diag = 32 * pj + 31 > qmin;  // uniform: some key of the pair is above some row
+    float m_new[2];
+    uint32_t pw[2][4];
+    float psum[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      f32x4 sc[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[t][kc]),
-                                                          qf[ct][kc], sc[t], 0, 0, 0);
-      }
       float sv[8];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sv[4 * t + e] = (key0 + 4 * t + e <= qpos[ct]) ? sc[t][e] * qk_scale : -INFINITY;
+        for (int e = 0; e < 4; ++e) sv[4 * t + e] = sc[ct][t][e];
+      if (diag) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (key0 + 4 * t + e > qpos[ct]) sv[4 * t + e] = -INFINITY;
+      }
       float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                        fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
       mb = max_over_groups(mb);
-      // finite: key 0 is visible to every row, so the first pair sets a finite maximum
-      const float m_new = fmaxf(m_run[ct], mb);
-      float psum = 0.f;
-      uint32_t pw[4];
+      // The reference maximum of a row moves only when the true maximum passes
+      // it by more than kLazyLog2 (in log2 units): until then p stays below
+      // 2^kLazyLog2, which bf16 and the fp32 sums hold as exactly as p <= 1,
+      // and the accumulators need no rescaling. The first pair always sets it
+      // (m_run = -inf; key 0 is visible to every row, so mb is finite).
+      const float m_cand = fmaxf(m_run[ct], mb);
+      m_new[ct] = ((m_cand - m_run[ct]) * qk_scale > kLazyLog2) ? m_cand : m_run[ct];
+      const float ms = -m_new[ct] * qk_scale;
+      psum[ct] = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float pa = __builtin_amdgcn_exp2f(sv[e] - m_new);
-        const float pb = __builtin_amdgcn_exp2f(sv[e + 1] - m_new);
-        psum += pa + pb;
-        pw[e >> 1] = pack_bf16x2(pa, pb);
+        const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk_scale, ms));
+        const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], qk_scale, ms));
+        psum[ct] += pa + pb;
+        pw[ct][e >> 1] = pack_bf16x2(pa, pb);
       }
-      if (__any(m_new != m_run[ct])) {
-        const float alpha = __builtin_amdgcn_exp2f(m_run[ct] - m_new);
+    }
+    if (__any(m_new[0] != m_run[0] || m_new[1] != m_run[1])) {
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float alpha = __builtin_amdgcn_exp2f((m_run[ct] - m_new[ct]) * qk_scale);  // 1 if unchanged
         l_run[ct] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[ct][dt] = acc[ct][dt] * alpha;
       }
-      l_run[ct] += psum;
-      m_run[ct] = m_new;
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, make_uint4(pw[0], pw[1], pw[2], pw[3]));
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      l_run[ct] += psum[ct];
+      m_run[ct] = m_new[ct];
+      const bf16x8 pf =
+          __builtin_bit_cast(bf16x8, make_uint4(pw[ct][0], pw[ct][1], pw[ct][2], pw[ct][3]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[dt]),
@@ -215,16 +279,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     }
   };
 
-  fetch(0);
-  stash(0);
-  __syncthreads();
-  for (int pj = 0; pj < npairs; ++pj) {
-    const bool more = pj + 1 < npairs;  // uniform across the work group
-    if (more) fetch(pj + 1);
-    compute(pj, pj & 1);
-    if (more) stash((pj + 1) & 1);
-    __syncthreads();
+  // Step pj: loads of pair pj+2 go out; V of pair pj is read; once pair pj+1
+  // has landed (every wave waited for its own loads, then the barrier), its
+  // QK^T products are issued, and the softmax and PV of pair pj run while the
+  // matrix cores work on them.
+  // b_cur, b_next, b_new: byte offsets of the images of pairs pj, pj+1, pj+2.
+  int b_cur = 0, b_next = PAIR, b_new = 2 * PAIR;
+  auto step = [&](int pj, const f32x4 (&sc_cur)[2][2], f32x4 (&sc_next)[2][2]) {
+    if (pj + 2 < npairs) issue(pj + 2, b_new);
+    u32x4 vf[DT];
+    const unsigned char* img = pf_smem + b_cur;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      vf[dt] = *reinterpret_cast<const u32x4*>(img + (2 + v_sel) * TILE + dt * 512 + v_off);
+    if (pj + 1 < npairs) {
+      if (pj + 2 < npairs)
+        lds_wait_sync<LOADS>();  // pair pj+1 landed; pair pj+2 may still be in flight
+      else
+        lds_wait_sync<0>();
+      scores(b_next, sc_next);
+    }
+    finish(pj, vf, sc_cur);
+    const int b_old = b_cur;
+    b_cur = b_next;
+    b_next = b_new;
+    b_new = b_old;
+  };
+  issue(0, 0);
+  if (npairs > 1) {
+    issue(1, PAIR);
+    lds_wait_sync<LOADS>();
+  } else {
+    lds_wait_sync<0>();
   }
+  f32x4 sa[2][2], sb[2][2];
+  scores(0, sa);
+  int pj = 0;
+  for (; pj + 1 < npairs; pj += 2) {  // npairs is uniform across the work group
+    step(pj, sa, sb);
+    step(pj + 1, sb, sa);
+  }
+  if (pj < npairs) step(pj, sa, sb);
 
   // acc[ct][dt][e] = O^T[d = 16*dt + 4*gq + e][row 16*ct + c]
 #pragma unroll
@@ -323,7 +418,7 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
     const float qk_scale = scale * kLog2e;
     const dim3 grid((unsigned)wgs);
-    const size_t lds = 2 * (size_t)(D == 64 ? PfCfg<64>::PAIR_BYTES : PfCfg<128>::PAIR_BYTES);
+    const size_t lds = 3 * (size_t)(D == 64 ? PfCfg<64>::PAIR_BYTES : PfCfg<128>::PAIR_BYTES);
     const bool ok =
         D == 64 ? launch_prefill_g<64>(G, grid, lds, st, (const uint16_t*)k_pool,
                                        (const uint16_t*)v_pool, (const uint16_t*)q, (uint16_t*)out,
