@@ -24,6 +24,7 @@ from __future__ import annotations
 
 import argparse
 import contextlib
+import gc
 import hashlib
 import json
 import math
@@ -57,6 +58,8 @@ def parse():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--parity-samples", type=int, default=4)
+    ap.add_argument("--pf-splits", type=int, default=0,
+                    help="prefill key splits (0 = library's choice, 1 = none)")
     ap.add_argument("--no-baseline-leg", action="store_true",
                     help="prefix_reuse: skip the no-reuse comparison leg")
     ap.add_argument("--graph", action="store_true",
@@ -1079,7 +1082,7 @@ def run_prefix_reuse(args):
                            cfg.head_dim, cfg.block_size)
     P, C = cfg.prefix_len, cfg.chunk_len
     budget, watermark = int(cfg.extra["budget_blocks"]), int(cfg.extra["watermark_blocks"])
-    n_steps = args.warmup + args.steps
+    n_steps = args.warmup + args.steps + 1      # the last batch measures latency alone
     system, novel = gen.prefix_reuse_tokens(cfg, n_steps)
     prompts_of = [[np.concatenate([system, novel[k, i]]) for i in range(n)] for k in range(n_steps)]
     S = P + C
@@ -1113,10 +1116,17 @@ def run_prefix_reuse(args):
     log(f"cold prefill of the {P}-token system prompt: {cold_ms:.2f} ms (80 layers, q drawn per layer)")
 
     q_start = torch.arange(0, n * C + 1, C, dtype=torch.int32, device=dev)
-    tables_h = torch.empty((n, maxb), dtype=torch.int32).pin_memory()
-    ctx_h = torch.empty(n, dtype=torch.int32).pin_memory()
-    tables_d = torch.empty((n, maxb), dtype=torch.int32, device=dev)
-    ctx_d = torch.empty(n, dtype=torch.int32, device=dev)
+    pf_ws = torch.empty(max(1, pk.prefill_workspace_bytes(geom, n * C, Hq, args.pf_splits)),
+                        dtype=torch.uint8, device=dev)
+    # two sets of tables: the host fills one while kernels of the previous batch
+    # still read the other; an event per set says when its upload has run
+    tables_h = [torch.empty((n, maxb), dtype=torch.int32).pin_memory() for _ in range(2)]
+    ctx_h = [torch.empty(n, dtype=torch.int32).pin_memory() for _ in range(2)]
+    tables_d = [torch.empty((n, maxb), dtype=torch.int32, device=dev) for _ in range(2)]
+    ctx_d = [torch.empty(n, dtype=torch.int32, device=dev) for _ in range(2)]
+    uploaded = [torch.cuda.Event() for _ in range(2)]
+    for e in uploaded:
+        e.record(stream)
     torch.cuda.synchronize()
 
     profiling = [False]
@@ -1125,18 +1135,25 @@ def run_prefix_reuse(args):
     parts = [0.0] * 5    # match, evict, reserve, build tables, queue table copies
 
     def step(k):
+        """Admit batch k, queue its 80 layers, retire it. No wait for the device:
+        the host admits batch k+1 while the kernels of batch k run. Blocks that
+        eviction or release hands out again are only written by kernels queued
+        later on the same stream."""
         prompts = prompts_of[k]
+        buf = k % 2
         h0 = time.perf_counter()
         seqs, handles, usable, evicted = admit(bm, tree, prompts, B, watermark, parts)
         if any(u != P for u in usable):
             raise RuntimeError(f"step {k}: cached prefix lost ({usable}); the budget is too small")
         ha = time.perf_counter()
         tabs, lens = bm.build_tables(seqs, maxb)
-        tables_h.numpy()[:] = tabs
-        ctx_h.numpy()[:] = np.asarray(usable, np.int32)
+        uploaded[buf].synchronize()   # the upload two batches ago has left this pinned set
+        tables_h[buf].numpy()[:] = tabs
+        ctx_h[buf].numpy()[:] = np.asarray(usable, np.int32)
         hb = time.perf_counter()
-        tables_d.copy_(tables_h, non_blocking=True)
-        ctx_d.copy_(ctx_h, non_blocking=True)
+        tables_d[buf].copy_(tables_h[buf], non_blocking=True)
+        ctx_d[buf].copy_(ctx_h[buf], non_blocking=True)
+        uploaded[buf].record(stream)
         h1 = time.perf_counter()
         parts[3] += hb - ha
         parts[4] += h1 - hb
@@ -1145,7 +1162,8 @@ def run_prefix_reuse(args):
             if prof:
                 pk.Profiler.enable(True)
             pk.prefill(geom, k_pool, v_pool, layer, q_all[layer], k_all[layer], v_all[layer],
-                       out[layer], q_start, tables_d, ctx_d, C, S, stream=stream)
+                       out[layer], q_start, tables_d[buf], ctx_d[buf], C, S, stream=stream,
+                       splits=args.pf_splits, workspace=pf_ws)
             if prof:
                 pk.Profiler.enable(False)
         h2 = time.perf_counter()
@@ -1154,21 +1172,31 @@ def run_prefix_reuse(args):
         host_s[0] += h1 - h0
         host_s[1] += h3 - h2
         record.append((list(usable), list(evicted), adopted))
-        stream.synchronize()   # the step ends when its outputs are ready (time to first token)
 
     for k in range(args.warmup):
         step(k)
+    torch.cuda.synchronize()
+    # the host loop allocates small Python objects (block id lists): move what
+    # exists now out of the collector's view, so a full collection over
+    # everything torch allocated does not land inside the timed steps
+    gc.collect()
+    gc.freeze()
     host_s[:] = [0.0, 0.0]
     parts[:] = [0.0] * 5
     if not args.no_prof:
         pk.Profiler.reset()
         profiling[0] = True
     with Timer(torch, stream) as t:
-        for k in range(args.warmup, n_steps):
+        for k in range(args.warmup, args.warmup + args.steps):
             step(k)
     profiling[0] = False
     ms = max(t.ms, t.wall_ms) / args.steps
     evicted_timed = sum(len(r[1]) for r in record[args.warmup:])
+    host_timed, parts_timed = list(host_s), list(parts)
+    # one more batch on its own: admission to outputs ready (time to first token of the batch)
+    with Timer(torch, stream) as tl:
+        step(n_steps - 1)
+    latency_ms = max(tl.ms, tl.wall_ms)
     value = n / (ms * 1e-3)
     info = tree.info()
     log(f"timed {args.steps} steps: {ms:.3f} ms/step, {value:.1f} requests/s; evicted "
@@ -1177,7 +1205,7 @@ def run_prefix_reuse(args):
     kern, roofline = {}, None
     macs_layer = sum(2 * Hq * d * (C * P + C * (C + 1) // 2) for _ in range(n))
     if not args.no_prof:
-        for name in ("prefill_append", "prefill_attention"):
+        for name in ("prefill_append", "prefill_attention", "prefill_combine"):
             cnt, tot = pk.Profiler.read(name)
             if cnt:
                 kern[name] = {"launches": cnt, "avg_us": round(1e3 * tot / cnt, 2)}
@@ -1188,6 +1216,8 @@ def run_prefix_reuse(args):
                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
                         "kernel": "prefill_mfma_bf16_kernel", "flops_per_launch": 2 * macs_layer,
                         "avg_launch_us": round(avg_s * 1e6, 2)}
+            if "prefill_combine" in kern:
+                roofline["combine_avg_us"] = kern["prefill_combine"]["avg_us"]
 
     # host cost of one lookup of a full prompt (cached path of 4,096 tokens), through the binding
     probe = prompts_of[-1][0]
@@ -1301,13 +1331,14 @@ def run_prefix_reuse(args):
                    "head_dim": d, "block_size": B, "requests_per_step": n, "prefix_tokens": P,
                    "novel_tokens": C, "cache_budget_blocks": budget, "watermark_blocks": watermark,
                    "launch": "eager"},
-        "host": {"admit_us_per_request": round(host_s[0] / (args.steps * n) * 1e6, 2),
-                 "retire_us_per_request": round(host_s[1] / (args.steps * n) * 1e6, 2),
+        "host": {"admit_us_per_request": round(host_timed[0] / (args.steps * n) * 1e6, 2),
+                 "retire_us_per_request": round(host_timed[1] / (args.steps * n) * 1e6, 2),
                  "admit_parts_us_per_request": {
                      k_: round(v_ / (args.steps * n) * 1e6, 2) for k_, v_ in
-                     zip(("match", "evict", "reserve", "build_tables", "queue_copies"), parts)},
+                     zip(("match", "evict", "reserve", "build_tables", "queue_copies"), parts_timed)},
                  "match_unpin_us_4128_tokens": round(match_us, 2),
                  "evicted_nodes_timed": evicted_timed, "tree": info},
+        "batch_latency_ms": round(latency_ms, 3),
         "cold_system_prefill_ms": round(cold_ms, 3),
         "no_reuse": nr,
         "roofline": roofline,

@@ -207,13 +207,27 @@ pa_status pa_decode_append(const pa_geom* g, void* k_pool, void* v_pool, int32_t
  * launch; max_context_len bounds ctx_lens[i] + chunk length (values are clamped
  * to these bounds, never read past them). scale <= 0 means 1/sqrt(d).
  * Implemented for bf16 pools with B = 16, d in {64, 128} and n_q_heads / H_kv
- * dividing 32; other geometries return PA_ERR_UNSUPPORTED. */
+ * dividing 32; other geometries return PA_ERR_UNSUPPORTED.
+ * Splits: the visible keys of each tile of query rows may be cut into n_splits
+ * ranges processed in parallel, whose partial results (unnormalised output,
+ * maximum, sum) go to the caller's workspace and are merged by the same
+ * online-softmax rule (section "Chunked prefill mechanics"). n_splits = 1: no
+ * split, no workspace; 2..16: that many (PA_ERR_WORKSPACE if workspace_bytes is
+ * below pa_prefill_workspace_bytes for it); 0: chosen from the launch size (up
+ * to 4, for batches too small to fill the device), falling back to 1 when the
+ * workspace is missing or too small. */
 pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer, const void* q,
                      const void* k_new, const void* v_new, void* out, int32_t n_seqs,
                      int32_t n_tokens, int32_t n_q_heads, const int32_t* q_start,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* ctx_lens, int32_t max_q_len, int32_t max_context_len,
-                     float scale, void* stream);
+                     float scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                     void* stream);
+/* Device workspace bytes pa_prefill needs for n_splits splits of n_tokens rows
+ * (n_splits 0: the most the automatic choice uses; 1: 0 bytes); 0 for bad
+ * arguments. */
+size_t pa_prefill_workspace_bytes(const pa_geom* g, int32_t n_tokens, int32_t n_q_heads,
+                                  int32_t n_splits);
 
 /* Copy-on-write block copy: for each k, block dst[k] <- block src[k] in every
  * layer, K and V, all B slots. src, dst: int32 [n_pairs] device arrays; no dst

@@ -227,12 +227,22 @@ def decode_append(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, o
           "pa_decode_append")
 
 
+def prefill_workspace_bytes(geom: Geometry, n_tokens: int, n_q_heads: int, splits: int = 0) -> int:
+    """Workspace bytes prefill needs for `splits` splits (0: the most the automatic
+    choice uses)."""
+    g = geom.c()
+    return int(_L().pa_prefill_workspace_bytes(C.byref(g), n_tokens, n_q_heads, splits))
+
+
 def prefill(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out, q_start, block_tables,
-            ctx_lens, max_q_len: int, max_context_len: int, scale: float = 0.0, stream=None):
+            ctx_lens, max_q_len: int, max_context_len: int, scale: float = 0.0, stream=None,
+            splits: int = 0, workspace=None):
     """Chunked prefill of one layer: chunk i = rows q_start[i]..q_start[i+1]-1 of q
     [n_tok, H_q, d] / k_new, v_new [n_tok, H_kv, d], at positions ctx_lens[i] + r.
     Writes the chunks' K/V through block_tables, then attends causally; out gets
-    [n_tok, H_q, d]."""
+    [n_tok, H_q, d]. splits: 0 = automatic (uses `workspace` when given and large
+    enough), 1 = none, k = k splits (needs `workspace`, a device tensor of at least
+    prefill_workspace_bytes bytes)."""
     _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
     _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
     if q.dim() != 3 or q.shape[2] != geom.head_dim:
@@ -249,11 +259,15 @@ def prefill(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out, q_
     _dev(block_tables, "block_tables", torch.int32)
     _dev(q_start, "q_start", torch.int32, n + 1)
     _dev(ctx_lens, "ctx_lens", torch.int32, n)
+    if workspace is not None and (not workspace.is_cuda or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
     g = geom.c()
     check(_L().pa_prefill(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(q), _ptr(k_new),
                           _ptr(v_new), _ptr(out), n, n_tok, hq, _ptr(q_start), _ptr(block_tables),
                           int(block_tables.shape[1]), _ptr(ctx_lens), int(max_q_len),
-                          int(max_context_len), float(scale), _stream(stream, q.device)),
+                          int(max_context_len), float(scale), int(splits), _ptr(workspace),
+                          0 if workspace is None else workspace.numel() * workspace.element_size(),
+                          _stream(stream, q.device)),
           "pa_prefill")
 
 

@@ -55,6 +55,21 @@ __device__ __forceinline__ void lds_wait_sync() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Splitting the visible keys of a tile across work groups (for batches too small
+// to fill the chip): each split writes its unnormalised output, its reference
+// maximum (log2 units) and its sum, and a second kernel merges them with the
+// online-softmax rule ("Chunked prefill mechanics": the m, l, O recurrence).
+constexpr int kPfMaxSplits = 16;
+constexpr int kPfAutoMaxSplits = 4;
+constexpr int kPfTargetWgs = 512;       // two resident work groups per CU
+constexpr int kPfMinPairsPerSplit = 8;
+
+struct PfSplit {
+  int n;           // splits per tile; 1: outputs are written directly
+  float* part_o;   // [n_tokens][Hq][n][D], when n > 1
+  float* part_ml;  // [n_tokens][Hq][n][2]: reference maximum (log2 units), sum
+};
+
 // Growth of a row's maximum (log2 units) tolerated before the accumulators are
 // rescaled to a new reference.
 constexpr float kLazyLog2 = 8.0f;
@@ -73,7 +88,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out, ChunkBatch cb,
     const int32_t* __restrict__ tables, int64_t layer_off, int N, int Hkv, int Hq, int max_blocks,
-    int n_tiles, float qk_scale) {
+    int n_tiles, float qk_scale, PfSplit sp) {
   constexpr int KC = PfCfg<D>::KC;
   constexpr int DT = PfCfg<D>::DT;
   constexpr int TILE = PfCfg<D>::TILE_BYTES;
@@ -83,12 +98,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int TW = kPfRowsPerWave / G;  // chunk tokens per wave
   extern __shared__ __align__(16) unsigned char pf_smem[];  // three pair images
 
-  const int64_t items = (int64_t)cb.n_seqs * Hkv * n_tiles;
+  const int64_t items = (int64_t)cb.n_seqs * Hkv * n_tiles * sp.n;
   const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
   const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (item >= items) return;  // whole work group
-  const int tile = (int)(item % n_tiles);
-  const int64_t ig = item / n_tiles;
+  const int split = (int)(item % sp.n);  // splits, then tiles, of one (chunk, head) are adjacent
+  const int tile = (int)((item / sp.n) % n_tiles);
+  const int64_t ig = item / sp.n / n_tiles;
   const int g = (int)(ig % Hkv);
   const int i = (int)(ig / Hkv);
   int a, q_len, ctx;
@@ -98,6 +114,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const int kmax = ctx + min(t0 + TQ, q_len);  // keys [0, kmax) are visible to some row
   const int nblk = (kmax + 15) >> 4;
   const int npairs = (nblk + 1) >> 1;
+  // this split's pairs [pbeg, pend); the causal diagonal falls in the last split
+  const int pbeg = (int)((int64_t)split * npairs / sp.n);
+  const int pend = (int)((int64_t)(split + 1) * npairs / sp.n);
 
   const int tid = threadIdx.x;
   // the wave index is uniform; readfirstlane lets the compiler keep what derives
@@ -245,9 +264,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       // 2^kLazyLog2, which bf16 and the fp32 sums hold as exactly as p <= 1,
       // and the accumulators need no rescaling. The first pair always sets it
       // (m_run = -inf; key 0 is visible to every row, so mb is finite).
+      // A row may see no key of a split at all (a later split than its
+      // position): its maximum stays -inf and its probabilities 0.
       const float m_cand = fmaxf(m_run[ct], mb);
       m_new[ct] = ((m_cand - m_run[ct]) * qk_scale > kLazyLog2) ? m_cand : m_run[ct];
-      const float ms = -m_new[ct] * qk_scale;
+      const float ms = (m_new[ct] == -INFINITY) ? 0.f : -m_new[ct] * qk_scale;
       psum[ct] = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
@@ -260,7 +281,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     if (__any(m_new[0] != m_run[0] || m_new[1] != m_run[1])) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const float alpha = __builtin_amdgcn_exp2f((m_run[ct] - m_new[ct]) * qk_scale);  // 1 if unchanged
+        const float alpha = (m_new[ct] == m_run[ct])
+                                ? 1.f
+                                : __builtin_amdgcn_exp2f((m_run[ct] - m_new[ct]) * qk_scale);
         l_run[ct] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[ct][dt] = acc[ct][dt] * alpha;
@@ -286,14 +309,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // b_cur, b_next, b_new: byte offsets of the images of pairs pj, pj+1, pj+2.
   int b_cur = 0, b_next = PAIR, b_new = 2 * PAIR;
   auto step = [&](int pj, const f32x4 (&sc_cur)[2][2], f32x4 (&sc_next)[2][2]) {
-    if (pj + 2 < npairs) issue(pj + 2, b_new);
+    if (pj + 2 < pend) issue(pj + 2, b_new);
     u32x4 vf[DT];
     const unsigned char* img = pf_smem + b_cur;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       vf[dt] = *reinterpret_cast<const u32x4*>(img + (2 + v_sel) * TILE + dt * 512 + v_off);
-    if (pj + 1 < npairs) {
-      if (pj + 2 < npairs)
+    if (pj + 1 < pend) {
+      if (pj + 2 < pend)
         lds_wait_sync<LOADS>();  // pair pj+1 landed; pair pj+2 may still be in flight
       else
         lds_wait_sync<0>();
@@ -305,21 +328,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     b_next = b_new;
     b_new = b_old;
   };
-  issue(0, 0);
-  if (npairs > 1) {
-    issue(1, PAIR);
+  if (pbeg < pend) {
+  issue(pbeg, 0);
+  if (pend - pbeg > 1) {
+    issue(pbeg + 1, PAIR);
     lds_wait_sync<LOADS>();
   } else {
     lds_wait_sync<0>();
   }
   f32x4 sa[2][2], sb[2][2];
   scores(0, sa);
-  int pj = 0;
-  for (; pj + 1 < npairs; pj += 2) {  // npairs is uniform across the work group
+  int pj = pbeg;
+  for (; pj + 1 < pend; pj += 2) {  // the range is uniform across the work group
     step(pj, sa, sb);
     step(pj + 1, sb, sa);
   }
-  if (pj < npairs) step(pj, sa, sb);
+  if (pj < pend) step(pj, sa, sb);
+  }  // pbeg < pend (uniform); an empty split writes m = -inf, l = 0, O = 0
 
   // acc[ct][dt][e] = O^T[d = 16*dt + 4*gq + e][row 16*ct + c]
 #pragma unroll
@@ -328,34 +353,75 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     if (!rvalid[ct]) continue;
     const int r = 16 * ct + c;
     const int tok = t0 + TW * wave + r / G;
-    const float inv = 1.f / l;
-    uint16_t* o = out + ((int64_t)(a + tok) * Hq + g * G + r % G) * D;
+    const int64_t row = (int64_t)(a + tok) * Hq + g * G + r % G;
+    if (sp.n == 1) {
+      const float inv = 1.f / l;
+      uint16_t* o = out + row * D;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) =
-          make_uint2(pack_bf16x2(acc[ct][dt][0] * inv, acc[ct][dt][1] * inv),
-                     pack_bf16x2(acc[ct][dt][2] * inv, acc[ct][dt][3] * inv));
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) =
+            make_uint2(pack_bf16x2(acc[ct][dt][0] * inv, acc[ct][dt][1] * inv),
+                       pack_bf16x2(acc[ct][dt][2] * inv, acc[ct][dt][3] * inv));
+    } else {
+      const int64_t slot = row * sp.n + split;
+      float* po = sp.part_o + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * gq) = acc[ct][dt];
+      if (gq == 0)
+        *reinterpret_cast<float2*>(sp.part_ml + slot * 2) =
+            make_float2(m_run[ct] == -INFINITY ? -INFINITY : m_run[ct] * qk_scale, l);
+    }
   }
+}
+
+// Merges the splits of every output row: weights 2^(m_s - M), normalised by
+// the weighted sums. D/4 lanes per row (16-byte loads of four dimensions), so a
+// 256-thread work group merges 1024/D rows.
+template <int D>
+__global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __restrict__ part_o,
+                                                              const float* __restrict__ part_ml,
+                                                              uint16_t* __restrict__ out,
+                                                              int64_t rows, int S) {
+  constexpr int LPR = D / 4;  // lanes per row
+  const int64_t row = (int64_t)blockIdx.x * (256 / LPR) + threadIdx.x / LPR;
+  if (row >= rows) return;
+  const int col = 4 * (threadIdx.x % LPR);
+  const float* ml = part_ml + row * S * 2;
+  // finite: the split holding pair 0 gives every row key 0
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * s]);
+  float L = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < S; ++s) {
+    const float w = __builtin_amdgcn_exp2f(ml[2 * s] - M);  // 0 for an empty split
+    L = fmaf(w, ml[2 * s + 1], L);
+    const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + (row * S + s) * D + col);
+    o += w * v;
+  }
+  const float inv = 1.f / L;
+  *reinterpret_cast<uint2*>(out + row * D + col) =
+      make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
 }
 
 template <int D, int G>
 void launch_prefill(dim3 grid, size_t lds, hipStream_t st, const uint16_t* kp, const uint16_t* vp,
                     const uint16_t* q, uint16_t* out, ChunkBatch cb, const int32_t* tables,
                     int64_t layer_off, int N, int Hkv, int Hq, int max_blocks, int n_tiles,
-                    float qk_scale) {
+                    float qk_scale, PfSplit sp) {
   hipLaunchKernelGGL((prefill_mfma_bf16_kernel<D, G>), grid, dim3(256), lds, st, kp, vp, q, out, cb,
-                     tables, layer_off, N, Hkv, Hq, max_blocks, n_tiles, qk_scale);
+                     tables, layer_off, N, Hkv, Hq, max_blocks, n_tiles, qk_scale, sp);
 }
 
 template <int D>
 bool launch_prefill_g(int G, dim3 grid, size_t lds, hipStream_t st, const uint16_t* kp,
                       const uint16_t* vp, const uint16_t* q, uint16_t* out, ChunkBatch cb,
                       const int32_t* tables, int64_t layer_off, int N, int Hkv, int Hq,
-                      int max_blocks, int n_tiles, float qk_scale) {
+                      int max_blocks, int n_tiles, float qk_scale, PfSplit sp) {
 #define PA_PF_CASE(GG)                                                                     \
   case GG:                                                                                \
     launch_prefill<D, GG>(grid, lds, st, kp, vp, q, out, cb, tables, layer_off, N, Hkv, Hq, \
-                          max_blocks, n_tiles, qk_scale);                                  \
+                          max_blocks, n_tiles, qk_scale, sp);                              \
     return true;
   switch (G) {
     PA_PF_CASE(1)
@@ -370,18 +436,41 @@ bool launch_prefill_g(int G, dim3 grid, size_t lds, hipStream_t st, const uint16
 #undef PA_PF_CASE
 }
 
+// Splits for a launch of `items` tiles whose longest walk is max_pairs pairs: as
+// many as bring the grid to two resident work groups per CU, at least
+// kPfMinPairsPerSplit pairs each.
+int auto_splits(int64_t items, int max_pairs) {
+  if (items >= kPfTargetWgs) return 1;
+  int s = (int)((kPfTargetWgs + items - 1) / items);
+  s = std::min(s, std::max(1, max_pairs / kPfMinPairsPerSplit));
+  return std::max(1, std::min(s, kPfAutoMaxSplits));
+}
+
+size_t split_bytes(int64_t n_tokens, int Hq, int D, int S) {
+  return S > 1 ? (size_t)S * n_tokens * Hq * (D + 2) * sizeof(float) : 0;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t pa_prefill_workspace_bytes(const pa_geom* g, int32_t n_tokens, int32_t n_q_heads,
+                                  int32_t n_splits) {
+  if (!geom_ok(g) || n_tokens < 0 || n_q_heads <= 0 || n_splits < 0 || n_splits > kPfMaxSplits)
+    return 0;
+  return split_bytes(n_tokens, n_q_heads, g->head_dim, n_splits == 0 ? kPfAutoMaxSplits : n_splits);
+}
 
 pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer, const void* q,
                      const void* k_new, const void* v_new, void* out, int32_t n_seqs,
                      int32_t n_tokens, int32_t n_q_heads, const int32_t* q_start,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* ctx_lens, int32_t max_q_len, int32_t max_context_len,
-                     float scale, void* stream) {
+                     float scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
+                     void* stream) {
   if (!geom_ok(g) || layer < 0 || layer >= g->num_layers || n_seqs < 0 || n_tokens < 0 ||
-      n_q_heads <= 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0)
+      n_q_heads <= 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0 ||
+      n_splits < 0 || n_splits > kPfMaxSplits)
     return PA_ERR_INVALID_ARG;
   const int B = g->block_size, D = g->head_dim, Hkv = g->num_kv_heads;
   if (n_q_heads % Hkv != 0 || max_q_len > max_context_len) return PA_ERR_INVALID_ARG;
@@ -392,6 +481,15 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
   if (n_seqs == 0 || n_tokens == 0 || max_q_len == 0) return PA_OK;
   if (!k_pool || !v_pool || !q || !k_new || !v_new || !out || !q_start || !block_tables || !ctx_lens)
     return PA_ERR_INVALID_ARG;
+  const int TQ = kPfRows / G;
+  const int n_tiles = (max_q_len + TQ - 1) / TQ;
+  const int64_t tiles = (int64_t)n_seqs * Hkv * n_tiles;
+  const int max_pairs = ((max_context_len + 15) / 16 + 1) / 2;
+  int S = n_splits == 0 ? auto_splits(tiles, max_pairs) : n_splits;
+  if (S > 1 && (!workspace || workspace_bytes < split_bytes(n_tokens, n_q_heads, D, S))) {
+    if (n_splits != 0) return PA_ERR_WORKSPACE;
+    S = 1;  // automatic choice without room for partials: no split
+  }
   hipStream_t st = (hipStream_t)stream;
   const int64_t layer_off = (int64_t)layer * g->num_blocks * Hkv * B * D;
   const ChunkBatch cb{q_start, ctx_lens, n_seqs, n_tokens, max_q_len, max_context_len};
@@ -408,11 +506,14 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
                        n_tokens, Hkv, D, B, (int64_t)g->num_blocks * B, layer_off);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
+  PfSplit sp{S, nullptr, nullptr};
+  if (S > 1) {
+    sp.part_o = static_cast<float*>(workspace);
+    sp.part_ml = sp.part_o + (int64_t)n_tokens * n_q_heads * S * D;
+  }
   {
     ProfScope ps("prefill_attention", st);
-    const int TQ = kPfRows / G;
-    const int n_tiles = (max_q_len + TQ - 1) / TQ;
-    const int64_t items = (int64_t)n_seqs * Hkv * n_tiles;
+    const int64_t items = tiles * S;
     const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
     if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
@@ -423,12 +524,26 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
         D == 64 ? launch_prefill_g<64>(G, grid, lds, st, (const uint16_t*)k_pool,
                                        (const uint16_t*)v_pool, (const uint16_t*)q, (uint16_t*)out,
                                        cb, block_tables, layer_off, g->num_blocks, Hkv, n_q_heads,
-                                       max_blocks_per_seq, n_tiles, qk_scale)
+                                       max_blocks_per_seq, n_tiles, qk_scale, sp)
                 : launch_prefill_g<128>(G, grid, lds, st, (const uint16_t*)k_pool,
                                         (const uint16_t*)v_pool, (const uint16_t*)q, (uint16_t*)out,
                                         cb, block_tables, layer_off, g->num_blocks, Hkv, n_q_heads,
-                                        max_blocks_per_seq, n_tiles, qk_scale);
+                                        max_blocks_per_seq, n_tiles, qk_scale, sp);
     if (!ok) return PA_ERR_UNSUPPORTED;
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  }
+  if (S > 1) {
+    ProfScope ps("prefill_combine", st);
+    const int64_t rows = (int64_t)n_tokens * n_q_heads;
+    const int rows_per_wg = 1024 / D;
+    const int64_t wgs = (rows + rows_per_wg - 1) / rows_per_wg;
+    if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    if (D == 64)
+      hipLaunchKernelGGL((prefill_combine_kernel<64>), dim3((unsigned)wgs), dim3(256), 0, st,
+                         sp.part_o, sp.part_ml, (uint16_t*)out, rows, S);
+    else
+      hipLaunchKernelGGL((prefill_combine_kernel<128>), dim3((unsigned)wgs), dim3(256), 0, st,
+                         sp.part_o, sp.part_ml, (uint16_t*)out, rows, S);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;

@@ -58,8 +58,11 @@ def make_prefill_batch(Hq, Hkv, d, ctx, qlens, seed, N=None, L=1, B=16, free_ord
                 q_start=q_start, ctx=np.asarray(ctx, np.int32), qlens=np.asarray(qlens))
 
 
-def run_prefill(b, layer=0, tables=None, kp=None, vp=None):
+def run_prefill(b, layer=0, tables=None, kp=None, vp=None, splits=0, ws_bytes=None):
     geom = pk.Geometry(b["L"], b["Hkv"], b["d"], b["B"], b["N"], "bf16")
+    ws = None
+    if ws_bytes is not None:
+        ws = torch.full((max(1, ws_bytes // 4),), float("nan"), device="cuda")   # NaN: unwritten partials show
     K = to_dev(b["kp"] if kp is None else kp, "bf16")
     V = to_dev(b["vp"] if vp is None else vp, "bf16")
     tabs = b["tables"] if tables is None else tables
@@ -70,7 +73,8 @@ def run_prefill(b, layer=0, tables=None, kp=None, vp=None):
     pk.prefill(geom, K, V, layer, q, to_dev(b["kn"], "bf16"), to_dev(b["vn"], "bf16"), out,
                torch.from_numpy(b["q_start"]).cuda(),
                torch.from_numpy(padded_tables(tabs, max_blocks)).cuda(),
-               torch.from_numpy(b["ctx"]).cuda(), int(max(b["qlens"])), max_ctx)
+               torch.from_numpy(b["ctx"]).cuda(), int(max(b["qlens"])), max_ctx, splits=splits,
+               workspace=ws)
     torch.cuda.synchronize()
     return to_host(out, "bf16"), to_host(K, "bf16"), to_host(V, "bf16")
 
@@ -106,6 +110,54 @@ def test_prefill_parity(case):
     assert np.isfinite(olayout.widen(out, "bf16")).all()
     err = max_abs_err(out, expect, "bf16")
     assert err <= BF16_TOL, (name, err)
+
+
+@pytest.mark.parametrize("splits", [2, 4, 16])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_split_parity(case, splits):
+    """The visible keys of every tile cut into `splits` ranges whose partials are
+    merged by a second kernel: same pools, outputs within tolerance. Short
+    contexts leave later splits with no key at all for some rows (or no pair)."""
+    need_gpu()
+    name, Hq, Hkv, d, ctx, qlens = case
+    print_case(test="prefill_split_parity", case=name, splits=splits)
+    b = make_prefill_batch(Hq, Hkv, d, ctx, qlens, seed=zlib.crc32(name.encode()) % 10000)
+    geom = pk.Geometry(b["L"], b["Hkv"], b["d"], b["B"], b["N"], "bf16")
+    n_tok = int(sum(qlens))
+    ws = pk.prefill_workspace_bytes(geom, n_tok, Hq, splits)
+    assert ws == splits * n_tok * Hq * (d + 2) * 4
+    out, K, V = run_prefill(b, splits=splits, ws_bytes=ws)
+    ek, ev, expect = oracle_prefill(b)
+    assert np.array_equal(K.view(np.uint8), ek.view(np.uint8)), "K pool"
+    assert np.array_equal(V.view(np.uint8), ev.view(np.uint8)), "V pool"
+    assert np.isfinite(olayout.widen(out, "bf16")).all()
+    err = max_abs_err(out, expect, "bf16")
+    assert err <= BF16_TOL, (name, splits, err)
+
+
+def test_prefill_split_workspace_rules():
+    """An explicit split count without room for its partials is refused; the
+    automatic choice without room runs unsplit (bitwise the plain call); with
+    room it may split (a small batch over a long history), within tolerance."""
+    need_gpu()
+    print_case(test="prefill_split_workspace")
+    Hq, Hkv, d = 16, 2, 128
+    b = make_prefill_batch(Hq, Hkv, d, [700, 1200], [20, 9], seed=61)
+    geom = pk.Geometry(b["L"], b["Hkv"], b["d"], b["B"], b["N"], "bf16")
+    n_tok = 29
+    need4 = pk.prefill_workspace_bytes(geom, n_tok, Hq, 4)
+    with pytest.raises(pk.PagedKVError):
+        run_prefill(b, splits=4, ws_bytes=need4 - 4)
+    with pytest.raises(pk.PagedKVError):
+        run_prefill(b, splits=4)                              # no workspace at all
+    plain, _, _ = run_prefill(b)
+    small, _, _ = run_prefill(b, splits=0, ws_bytes=64)
+    assert np.array_equal(plain.view(np.uint8), small.view(np.uint8))
+    auto, _, _ = run_prefill(b, splits=0, ws_bytes=pk.prefill_workspace_bytes(geom, n_tok, Hq, 0))
+    _, _, expect = oracle_prefill(b)
+    assert max_abs_err(auto, expect, "bf16") <= BF16_TOL
+    assert pk.prefill_workspace_bytes(geom, n_tok, Hq, 1) == 0
+    assert pk.prefill_workspace_bytes(geom, n_tok, Hq, 17) == 0      # out of range
 
 
 @pytest.mark.parametrize("chunk", [16, 48, 100])
