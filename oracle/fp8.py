@@ -223,3 +223,32 @@ def paged_decode(q, k_pool, v_pool, layer, tables, lengths, block_size, q_dtype=
                                 head_dim)
         out[i] = attention.attend(qf[i], K, V, scale)
     return out
+
+
+def paged_prefill(q, k_new, v_new, k_pool, v_pool, layer, tables, q_start, ctx_lens, block_size,
+                  q_dtype="bf16", scale=None, chunks=None):
+    """Chunked prefill over FP8 pools: (pools after the chunks are written, float64
+    outputs [n_tok, H_q, d]).
+
+    "KV Cache Management", section "Chunked prefill mechanics": chunk i's row t
+    attends over the cached positions and the chunk's positions 0 .. t. Reading
+    taken for one-byte storage (the page names no order for a quantized cache):
+    the chunk is written first and every key and value is then read back as
+    stored, so the chunk's own rows enter quantized, as the cached ones do (the
+    same order the decode step follows: the new token is appended, then attended).
+    """
+    from . import prefill as _prefill
+    head_dim = q.shape[2]
+    if scale is None or scale == 0.0:
+        scale = attention.default_scale(head_dim)
+    slots = _prefill.chunk_slots(tables, q_start, ctx_lens, block_size)
+    kp, vp = append_kv(k_pool, v_pool, layer, k_new, v_new, slots, block_size, q_dtype)
+    qf = layout.widen(q, q_dtype)
+    out = np.zeros(qf.shape, dtype=np.float64)
+    idx = range(len(ctx_lens)) if chunks is None else chunks
+    for i in idx:
+        a, b = _prefill.chunk_bounds(q_start, i)
+        c = int(ctx_lens[i])
+        K, V = rebuild_sequence(kp, vp, layer, tables[i], c + (b - a), block_size, head_dim)
+        out[a:b] = _prefill.chunk_attention(qf[a:b], K[c:], V[c:], K[:c], V[:c], scale)
+    return kp, vp, out

@@ -422,3 +422,32 @@ def test_mutant_radix_partial_block_off_by_one(monkeypatch):
 def test_mutant_radix_split_drops_pins(monkeypatch):
     monkeypatch.setattr(orx.RadixCache, "insert", _insert_split_unpinned)
     _fails(TR.test_pin_counts, 0)
+
+
+# ---- FP8 chunked prefill (oracle/fp8.paged_prefill) -----------------------------------
+from tests import test_oracle_fp8_prefill as T8P                   # noqa: E402
+
+fp8_prefill_orig = ofp8.paged_prefill
+
+
+def _fp8_prefill_attend_before_write(q, k_new, v_new, k_pool, v_pool, layer, tables, q_start,
+                                     ctx_lens, block_size, q_dtype="bf16", scale=None, chunks=None):
+    import oracle.prefill as opf_
+    kp, vp, _ = fp8_prefill_orig(q, k_new, v_new, k_pool, v_pool, layer, tables, q_start, ctx_lens,
+                                 block_size, q_dtype, scale, chunks)
+    d = q.shape[2]
+    sc = att.default_scale(d) if not scale else scale
+    qf, kf, vf = (layout.widen(x, q_dtype) for x in (q, k_new, v_new))
+    out = np.zeros(qf.shape)
+    for i in range(len(ctx_lens)):
+        a, b = opf_.chunk_bounds(q_start, i)
+        c = int(ctx_lens[i])
+        K, V = ofp8.rebuild_sequence(k_pool, v_pool, layer, tables[i], c, block_size, d)
+        # wrong: the chunk's own rows enter unquantized (attended before the write)
+        out[a:b] = opf_.chunk_attention(qf[a:b], kf[a:b], vf[a:b], K, V, sc)
+    return kp, vp, out
+
+
+def test_mutant_fp8_prefill_attends_unquantized_chunk(monkeypatch):
+    monkeypatch.setattr(ofp8, "paged_prefill", _fp8_prefill_attend_before_write)
+    _raises(T8P.test_one_token_chunks_are_decode_steps)
