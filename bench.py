@@ -221,19 +221,36 @@ def setup(args):
     return torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool
 
 
-def fill_fp8_pools(torch, pk, geom, gen_, k_pool, v_pool, dev, chunk_slots=1 << 18):
-    """Every slot of an FP8 pool gets seeded N(0,1) K/V rows (bf16), quantized by the
-    library's own append (codes and scales as the decode step would write them)."""
-    nslots = geom.num_blocks * geom.block_size
-    Hkv, d = geom.num_kv_heads, geom.head_dim
-    for layer in range(geom.num_layers):
-        for a in range(0, nslots, chunk_slots):
-            m = min(chunk_slots, nslots - a)
-            kn = torch.randn((m, Hkv, d), generator=gen_, device=dev).to(torch.bfloat16)
-            vn = torch.randn((m, Hkv, d), generator=gen_, device=dev).to(torch.bfloat16)
-            slots = torch.arange(a, a + m, dtype=torch.int64, device=dev)
-            pk.append_kv(geom, k_pool, v_pool, layer, kn, vn, slots)
-    torch.cuda.synchronize()
+def fill_fp8_pools(torch, pk, geom, gen_, k_pool, v_pool, dev, chunk_blocks=8192):
+    """Every slot of an FP8 pool gets seeded N(0,1) K/V rows (rounded to bf16),
+    quantized with plain torch operations on the device: per (token, head) the
+    power-of-two scale 2^e with e the smallest integer such that max|x| <= 448 * 2^e,
+    torch's float8_e4m3fn cast of x * 2^-e, the byte e + 127, laid out in the pool's
+    documented tile format (K codes [d/W][B][W], V codes [d][B], then the B scale
+    bytes). The pools are input data: neither the library nor the oracle writes
+    them."""
+    L, N, H, B, d = (geom.num_layers, geom.num_blocks, geom.num_kv_heads, geom.block_size,
+                     geom.head_dim)
+    W = geom.k_chunk
+    for layer in range(L):
+        for b0 in range(0, N, chunk_blocks):
+            nb = min(chunk_blocks, N - b0)
+            for pool, is_k in ((k_pool, True), (v_pool, False)):
+                x = torch.randn((nb, B, H, d), generator=gen_, device=dev).to(torch.bfloat16).float()
+                amax = x.abs().amax(-1)
+                m, ex = torch.frexp(amax)
+                e = torch.where(m <= 0.875, ex - 9, ex - 8).clamp(-127, 127)
+                e = torch.where(amax == 0, torch.zeros_like(e), e)
+                codes = (x * torch.exp2(-e.float()).unsqueeze(-1)).to(torch.float8_e4m3fn)
+                codes = codes.view(torch.uint8)
+                if is_k:
+                    tile = codes.view(nb, B, H, d // W, W).permute(0, 2, 3, 1, 4).reshape(nb, H, B * d)
+                else:
+                    tile = codes.permute(0, 2, 3, 1).reshape(nb, H, d * B)
+                pool[layer, b0:b0 + nb, :, :B * d] = tile
+                pool[layer, b0:b0 + nb, :, B * d:] = (e + 127).to(torch.uint8).permute(0, 2, 1)
+    if k_pool.is_cuda:
+        torch.cuda.synchronize()
 
 
 def to_np(torch, t, dtype):
@@ -568,9 +585,11 @@ def run_prefill(args):
     tables_np, lens_np = bm.build_tables(seqs, max_blocks)
     assert np.array_equal(lens_np, hist + C)
     n_tok = n * C
-    q_all = torch.randn((L, n_tok, Hq, d), generator=gen_, device=dev).to(geom.torch_dtype)
-    k_all = torch.randn((L, n_tok, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
-    v_all = torch.randn((L, n_tok, Hkv, d), generator=gen_, device=dev).to(geom.torch_dtype)
+    fp8 = cfg.dtype == "fp8"
+    io_name = "bf16" if fp8 else cfg.dtype
+    q_all = torch.randn((L, n_tok, Hq, d), generator=gen_, device=dev).to(geom.io_dtype)
+    k_all = torch.randn((L, n_tok, Hkv, d), generator=gen_, device=dev).to(geom.io_dtype)
+    v_all = torch.randn((L, n_tok, Hkv, d), generator=gen_, device=dev).to(geom.io_dtype)
     out = torch.empty_like(q_all)
     q_start = torch.arange(0, n_tok + 1, C, dtype=torch.int32, device=dev)
     tables = torch.from_numpy(np.ascontiguousarray(tables_np)).to(dev)
@@ -619,13 +638,14 @@ def run_prefill(args):
             ach = 2 * macs_layer / avg_s / 1e12
             roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                        "kernel": "prefill_mfma_bf16_kernel", "flops_per_launch": 2 * macs_layer,
+                        "kernel": "prefill_mfma_kernel", "flops_per_launch": 2 * macs_layer,
                         "avg_launch_us": round(avg_s * 1e6, 2)}
 
     # parity on sampled (chunk, layer) outputs; cpu baseline = the oracle on a sample
     parity, cpu_baseline = None, None
     if args.parity_samples or not args.no_cpu_baseline:
         from oracle import prefill as opf
+        from oracle import fp8 as ofp8
         from oracle import block_manager as obm
         om = obm.BlockManager(cfg.num_blocks, B, gen.free_order(cfg))
         otables = []
@@ -642,14 +662,19 @@ def run_prefill(args):
             # hist[i] .. hist[i]+C-1 only), so the pool after the run serves
             ids = otables[i]
             idx = torch.as_tensor(ids, dtype=torch.long, device=dev)
-            kb = to_np(torch, k_pool[layer].index_select(0, idx), cfg.dtype)[None]
-            vb = to_np(torch, v_pool[layer].index_select(0, idx), cfg.dtype)[None]
             rows = slice(i * C, (i + 1) * C)
             qs = np.array([0, C], dtype=np.int64)
-            _, _, o = opf.paged_prefill(to_np(torch, q_all[layer, rows], cfg.dtype),
-                                        to_np(torch, k_all[layer, rows], cfg.dtype),
-                                        to_np(torch, v_all[layer, rows], cfg.dtype), kb, vb, 0,
-                                        [list(range(len(ids)))], qs, [int(hist[i])], B, cfg.dtype)
+            qr, kr, vr = (to_np(torch, x[layer, rows], io_name) for x in (q_all, k_all, v_all))
+            if fp8:   # pool bytes as filled (torch), the chunk quantized by the oracle itself
+                kb = k_pool[layer].index_select(0, idx).cpu().numpy()[None]
+                vb = v_pool[layer].index_select(0, idx).cpu().numpy()[None]
+                _, _, o = ofp8.paged_prefill(qr, kr, vr, kb, vb, 0, [list(range(len(ids)))], qs,
+                                             [int(hist[i])], B)
+                return o
+            kb = to_np(torch, k_pool[layer].index_select(0, idx), cfg.dtype)[None]
+            vb = to_np(torch, v_pool[layer].index_select(0, idx), cfg.dtype)[None]
+            _, _, o = opf.paged_prefill(qr, kr, vr, kb, vb, 0, [list(range(len(ids)))], qs,
+                                        [int(hist[i])], B, cfg.dtype)
             return o
 
         errs = []
@@ -657,9 +682,11 @@ def run_prefill(args):
             i, layer = int(rng.integers(0, n)), int(rng.integers(0, L))
             expect = oracle_one(i, layer)
             got = out[layer, i * C:(i + 1) * C].float().cpu().numpy().astype(np.float64)
-            errs.append(float(np.max(np.abs(got - expect))))
+            scale_ = np.maximum(1.0, np.max(np.abs(expect), axis=-1, keepdims=True)) if fp8 else 1.0
+            errs.append(float(np.max(np.abs(got - expect) / scale_)))
         if errs:
-            parity = {"samples": len(errs), "max_abs_err": max(errs), "tol": 2e-2, "ok": max(errs) <= 2e-2}
+            parity = {"samples": len(errs), ("max_rel_err" if fp8 else "max_abs_err"): max(errs),
+                      "tol": 2e-2, "ok": max(errs) <= 2e-2}
             log(f"parity {parity}")
         if not args.no_cpu_baseline:
             try:
@@ -682,11 +709,12 @@ def run_prefill(args):
                                       f"{cpu_s:.1f} s; rate in causal attention FLOP/s"}
 
     result = {
-        "metric": "chunked-prefill attention TFLOP/s (causal) + prefill tokens/s, prefill_chunks",
+        "metric": f"chunked-prefill attention TFLOP/s (causal) + prefill tokens/s, {cfg.name}",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
-        "data": "synthetic (seeded N(0,1) Q/K/V, seeded random block placement)",
+        "data": "synthetic (seeded N(0,1) Q/K/V, seeded random block placement"
+                + (", history quantized to E4M3 by torch)" if fp8 else ")"),
         "config": {"workload": cfg.name, "num_layers": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": d, "block_size": B, "num_seqs": n, "chunk_len": C,
                    "histories": sorted(set(int(c) for c in hist)), "prompt_len": cfg.length_max,
@@ -1214,7 +1242,7 @@ def run_prefix_reuse(args):
             ach = 2 * macs_layer / avg_s / 1e12
             roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                        "kernel": "prefill_mfma_bf16_kernel", "flops_per_launch": 2 * macs_layer,
+                        "kernel": "prefill_mfma_kernel", "flops_per_launch": 2 * macs_layer,
                         "avg_launch_us": round(avg_s * 1e6, 2)}
             if "prefill_combine" in kern:
                 roofline["combine_avg_us"] = kern["prefill_combine"]["avg_us"]

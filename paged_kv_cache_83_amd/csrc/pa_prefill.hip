@@ -38,6 +38,7 @@
 #include "../../include/pa.h"
 #include "pa_append.h"
 #include "pa_device.h"
+#include "pa_fp8.h"
 
 namespace {
 
@@ -74,6 +75,12 @@ struct PfSplit {
 // rescaled to a new reference.
 constexpr float kLazyLog2 = 8.0f;
 
+// This wave's LDS accesses have completed; then synchronise the work group
+// (no wait for global loads still in flight into registers).
+__device__ __forceinline__ void lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <int D>
 struct PfCfg {
   static constexpr int KC = D / 32;                        // QK k-steps
@@ -83,17 +90,25 @@ struct PfCfg {
   static constexpr int LOADS = PAIR_BYTES / (16 * 64 * kPfWaves);  // 16-byte loads per thread
 };
 
-template <int D, int G>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_bf16_kernel(
-    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
+// The same kernel serves bf16 pools (FP8 = false: tiles go straight from HBM
+// into LDS) and one-byte pools (FP8 = true: each thread loads its share of the
+// pair's E4M3 codes and scale bytes a step ahead into registers, converts them
+// exactly to fp32, applies the power-of-two scale of their key (v_ldexp_f32)
+// and writes bf16 into the same LDS image the bf16 path builds, so everything
+// after the staging is shared; code x 2^e is a bf16 number exactly unless it is
+// below the normal range, 2^-126, where it rounds).
+template <int D, int G, bool FP8>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
+    const char* __restrict__ kpool, const char* __restrict__ vpool,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out, ChunkBatch cb,
     const int32_t* __restrict__ tables, int64_t layer_off, int N, int Hkv, int Hq, int max_blocks,
     int n_tiles, float qk_scale, PfSplit sp) {
   constexpr int KC = PfCfg<D>::KC;
   constexpr int DT = PfCfg<D>::DT;
-  constexpr int TILE = PfCfg<D>::TILE_BYTES;
+  constexpr int TILE = PfCfg<D>::TILE_BYTES;  // one bf16 tile in the LDS image
   constexpr int PAIR = PfCfg<D>::PAIR_BYTES;
   constexpr int LOADS = PfCfg<D>::LOADS;
+  constexpr int PTILE = FP8 ? 16 * D + 16 : TILE;  // one tile in the pool (codes + scales)
   constexpr int TQ = kPfRows / G;        // chunk tokens per work group
   constexpr int TW = kPfRowsPerWave / G;  // chunk tokens per wave
   extern __shared__ __align__(16) unsigned char pf_smem[];  // three pair images
@@ -158,8 +173,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   float l_run[2] = {0.f, 0.f};
 
   const int32_t* trow = tables + (int64_t)i * max_blocks;
-  const char* kl = reinterpret_cast<const char*>(kpool + layer_off);
-  const char* vl = reinterpret_cast<const char*>(vpool + layer_off);
+  const char* kl = kpool + layer_off;  // layer_off in bytes
+  const char* vl = vpool + layer_off;
 
   // Pair image in LDS: [K blk0][K blk1][V blk0][V blk1], each tile as in the pool.
   // Three images rotate: the pair whose softmax and PV are being done, the next
@@ -169,9 +184,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // same place the thread's own store would. The compiler does not order these
   // loads against LDS reads, so each step waits for them itself (vmcnt) before
   // its one barrier.
-  const char* kg = kl + (int64_t)g * TILE;  // head g's tile in block 0
-  const char* vg = vl + (int64_t)g * TILE;
-  const int64_t blk_stride = (int64_t)Hkv * TILE;
+  const char* kg = kl + (int64_t)g * PTILE;  // head g's tile in block 0
+  const char* vg = vl + (int64_t)g * PTILE;
+  const int64_t blk_stride = (int64_t)Hkv * PTILE;
   auto issue = [&](int pj, int buf) {
     const int b0 = 2 * pj;
     const int p0 = guard_block(trow[b0], N);
@@ -186,6 +201,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       __builtin_amdgcn_global_load_lds(base + lane * 16,
                                        (__attribute__((address_space(3))) void*)(img + woff), 16,
                                        0, 0);
+    }
+  };
+
+  // FP8 staging. Piece u of a thread is the 8 elements whose bf16 form sits at
+  // image offset 16 * (256 u + tid): in the pool, 8 code bytes at element
+  // offset el of tile tl, plus the scale bytes of their keys (K: one key, the
+  // slot of the piece's row; V: 8 consecutive slots of one dimension).
+  struct Raw {
+    u32x2 code[LOADS];
+    u32x2 scale[LOADS];  // K: low byte; V: 8 bytes, one per slot
+  };
+  auto load_raw = [&](int pj, Raw& r) {
+    const int b0 = 2 * pj;
+    const int p0 = guard_block(trow[b0], N);
+    const int p1 = (b0 + 1 < nblk) ? guard_block(trow[b0 + 1], N) : p0;
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int woff = (u * 256 + wave * 64) * 16;
+      const int tl = woff / TILE;                      // the same for all lanes of a wave
+      const int el = (woff - tl * TILE) / 2 + lane * 8;  // first element of the piece
+      const int p = (tl & 1) ? p1 : p0;
+      const char* t = (tl < 2 ? kg : vg) + p * blk_stride;
+      r.code[u] = *reinterpret_cast<const u32x2*>(t + el);
+      if (tl < 2) {
+        const uint32_t sb = (uint8_t)t[16 * D + ((el >> 5) & 15)];  // K: key = row of the W-chunk
+        r.scale[u] = u32x2{sb, 0u};
+      } else {
+        r.scale[u] = *reinterpret_cast<const u32x2*>(t + 16 * D + (el & 15));  // V: slots el%16 ..
+      }
+    }
+  };
+  auto stash_raw = [&](const Raw& r, int buf) {
+#pragma unroll
+    for (int u = 0; u < LOADS; ++u) {
+      const int woff = (u * 256 + wave * 64) * 16;
+      const int tl = woff / TILE;
+      const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(r.code[u][0], false);  // codes 0, 1
+      const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(r.code[u][0], true);   // codes 2, 3
+      const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(r.code[u][1], false);
+      const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(r.code[u][1], true);
+      float x[8] = {f0[0], f0[1], f1[0], f1[1], f2[0], f2[1], f3[0], f3[1]};
+      if (tl < 2) {
+        const int e = (int)r.scale[u][0] - kFp8ScaleBias;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[k] = __builtin_amdgcn_ldexpf(x[k], e);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          x[k] = __builtin_amdgcn_ldexpf(
+              x[k], (int)((r.scale[u][k >> 2] >> (8 * (k & 3))) & 0xffu) - kFp8ScaleBias);
+      }
+      const u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                       pack_bf16x2(x[6], x[7])};
+      *reinterpret_cast<u32x4*>(pf_smem + buf + woff + lane * 16) = w;
     }
   };
 
@@ -308,15 +377,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // matrix cores work on them.
   // b_cur, b_next, b_new: byte offsets of the images of pairs pj, pj+1, pj+2.
   int b_cur = 0, b_next = PAIR, b_new = 2 * PAIR;
+  Raw raw;  // FP8: the pair after next, in registers
   auto step = [&](int pj, const f32x4 (&sc_cur)[2][2], f32x4 (&sc_next)[2][2]) {
-    if (pj + 2 < pend) issue(pj + 2, b_new);
+    if constexpr (FP8) {
+      if (pj + 2 < pend) stash_raw(raw, b_new);
+      if (pj + 3 < pend) load_raw(pj + 3, raw);
+    } else {
+      if (pj + 2 < pend) issue(pj + 2, b_new);
+    }
     u32x4 vf[DT];
     const unsigned char* img = pf_smem + b_cur;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       vf[dt] = *reinterpret_cast<const u32x4*>(img + (2 + v_sel) * TILE + dt * 512 + v_off);
     if (pj + 1 < pend) {
-      if (pj + 2 < pend)
+      if constexpr (FP8)
+        lds_sync();  // this wave's stores of pair pj+1 (last step) are done; then all waves'
+      else if (pj + 2 < pend)
         lds_wait_sync<LOADS>();  // pair pj+1 landed; pair pj+2 may still be in flight
       else
         lds_wait_sync<0>();
@@ -329,12 +406,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     b_new = b_old;
   };
   if (pbeg < pend) {
-  issue(pbeg, 0);
-  if (pend - pbeg > 1) {
-    issue(pbeg + 1, PAIR);
-    lds_wait_sync<LOADS>();
+  if constexpr (FP8) {
+    load_raw(pbeg, raw);
+    stash_raw(raw, 0);
+    if (pend - pbeg > 1) {
+      load_raw(pbeg + 1, raw);
+      stash_raw(raw, PAIR);
+    }
+    if (pend - pbeg > 2) load_raw(pbeg + 2, raw);
+    lds_sync();
   } else {
-    lds_wait_sync<0>();
+    issue(pbeg, 0);
+    if (pend - pbeg > 1) {
+      issue(pbeg + 1, PAIR);
+      lds_wait_sync<LOADS>();
+    } else {
+      lds_wait_sync<0>();
+    }
   }
   f32x4 sa[2][2], sb[2][2];
   scores(0, sa);
@@ -404,24 +492,24 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __res
       make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
 }
 
-template <int D, int G>
-void launch_prefill(dim3 grid, size_t lds, hipStream_t st, const uint16_t* kp, const uint16_t* vp,
+template <int D, int G, bool FP8>
+void launch_prefill(dim3 grid, size_t lds, hipStream_t st, const char* kp, const char* vp,
                     const uint16_t* q, uint16_t* out, ChunkBatch cb, const int32_t* tables,
                     int64_t layer_off, int N, int Hkv, int Hq, int max_blocks, int n_tiles,
                     float qk_scale, PfSplit sp) {
-  hipLaunchKernelGGL((prefill_mfma_bf16_kernel<D, G>), grid, dim3(256), lds, st, kp, vp, q, out, cb,
+  hipLaunchKernelGGL((prefill_mfma_kernel<D, G, FP8>), grid, dim3(256), lds, st, kp, vp, q, out, cb,
                      tables, layer_off, N, Hkv, Hq, max_blocks, n_tiles, qk_scale, sp);
 }
 
-template <int D>
-bool launch_prefill_g(int G, dim3 grid, size_t lds, hipStream_t st, const uint16_t* kp,
-                      const uint16_t* vp, const uint16_t* q, uint16_t* out, ChunkBatch cb,
+template <int D, bool FP8>
+bool launch_prefill_g(int G, dim3 grid, size_t lds, hipStream_t st, const char* kp,
+                      const char* vp, const uint16_t* q, uint16_t* out, ChunkBatch cb,
                       const int32_t* tables, int64_t layer_off, int N, int Hkv, int Hq,
                       int max_blocks, int n_tiles, float qk_scale, PfSplit sp) {
 #define PA_PF_CASE(GG)                                                                     \
   case GG:                                                                                \
-    launch_prefill<D, GG>(grid, lds, st, kp, vp, q, out, cb, tables, layer_off, N, Hkv, Hq, \
-                          max_blocks, n_tiles, qk_scale, sp);                              \
+    launch_prefill<D, GG, FP8>(grid, lds, st, kp, vp, q, out, cb, tables, layer_off, N, Hkv,  \
+                               Hq, max_blocks, n_tiles, qk_scale, sp);                     \
     return true;
   switch (G) {
     PA_PF_CASE(1)
@@ -476,7 +564,8 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
   if (n_q_heads % Hkv != 0 || max_q_len > max_context_len) return PA_ERR_INVALID_ARG;
   if ((int64_t)max_blocks_per_seq * B < max_context_len) return PA_ERR_INVALID_ARG;
   const int G = n_q_heads / Hkv;
-  if (g->dtype != PA_BF16 || B != 16 || (D != 64 && D != 128) || G > 32 || 32 % G != 0)
+  const bool fp8 = g->dtype == PA_FP8;
+  if ((g->dtype != PA_BF16 && !fp8) || B != 16 || (D != 64 && D != 128) || G > 32 || 32 % G != 0)
     return PA_ERR_UNSUPPORTED;
   if (n_seqs == 0 || n_tokens == 0 || max_q_len == 0) return PA_OK;
   if (!k_pool || !v_pool || !q || !k_new || !v_new || !out || !q_start || !block_tables || !ctx_lens)
@@ -491,10 +580,21 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
     S = 1;  // automatic choice without room for partials: no split
   }
   hipStream_t st = (hipStream_t)stream;
-  const int64_t layer_off = (int64_t)layer * g->num_blocks * Hkv * B * D;
+  const int64_t tile_b = fp8 ? (int64_t)B * D + B : (int64_t)B * D * 2;  // bytes per pool tile
+  const int64_t layer_off = (int64_t)layer * g->num_blocks * Hkv * tile_b;   // bytes
   const ChunkBatch cb{q_start, ctx_lens, n_seqs, n_tokens, max_q_len, max_context_len};
 
-  {  // the chunks' keys and values go to their positions through the block tables
+  if (fp8) {  // the chunks' rows are quantized into their positions (one wave per row and head)
+    ProfScope ps("prefill_append", st);
+    const int64_t wgs = ((int64_t)n_tokens * Hkv + 3) / 4;
+    if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    const SlotsFromTables src{cb, block_tables, max_blocks_per_seq, B, g->num_blocks};
+    hipLaunchKernelGGL((append_fp8_kernel<SlotsFromTables>), dim3((unsigned)wgs), dim3(256), 0, st,
+                       (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, src, (int64_t)n_tokens, Hkv, D, B,
+                       (int64_t)g->num_blocks * B, layer_off);
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+  } else {  // the chunks' keys and values go to their positions through the block tables
     ProfScope ps("prefill_append", st);
     const int64_t items = ((int64_t)n_tokens + kAppendChunk - 1) / kAppendChunk * Hkv;
     const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
@@ -503,7 +603,7 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
     hipLaunchKernelGGL((append_kv_kernel<uint16_t, 8, SlotsFromTables>), dim3((unsigned)wgs),
                        dim3(256), append_lds_bytes<uint16_t>(D), st, (uint16_t*)k_pool,
                        (uint16_t*)v_pool, (const uint16_t*)k_new, (const uint16_t*)v_new, src,
-                       n_tokens, Hkv, D, B, (int64_t)g->num_blocks * B, layer_off);
+                       n_tokens, Hkv, D, B, (int64_t)g->num_blocks * B, layer_off / 2);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   PfSplit sp{S, nullptr, nullptr};
@@ -520,15 +620,17 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
     const float qk_scale = scale * kLog2e;
     const dim3 grid((unsigned)wgs);
     const size_t lds = 3 * (size_t)(D == 64 ? PfCfg<64>::PAIR_BYTES : PfCfg<128>::PAIR_BYTES);
-    const bool ok =
-        D == 64 ? launch_prefill_g<64>(G, grid, lds, st, (const uint16_t*)k_pool,
-                                       (const uint16_t*)v_pool, (const uint16_t*)q, (uint16_t*)out,
-                                       cb, block_tables, layer_off, g->num_blocks, Hkv, n_q_heads,
-                                       max_blocks_per_seq, n_tiles, qk_scale, sp)
-                : launch_prefill_g<128>(G, grid, lds, st, (const uint16_t*)k_pool,
-                                        (const uint16_t*)v_pool, (const uint16_t*)q, (uint16_t*)out,
-                                        cb, block_tables, layer_off, g->num_blocks, Hkv, n_q_heads,
-                                        max_blocks_per_seq, n_tiles, qk_scale, sp);
+    const char* kp = static_cast<const char*>(k_pool);
+    const char* vp = static_cast<const char*>(v_pool);
+    const uint16_t* qq = static_cast<const uint16_t*>(q);
+    uint16_t* oo = static_cast<uint16_t*>(out);
+#define PA_PF_LAUNCH(DD, F8)                                                                  \
+  launch_prefill_g<DD, F8>(G, grid, lds, st, kp, vp, qq, oo, cb, block_tables, layer_off,     \
+                           g->num_blocks, Hkv, n_q_heads, max_blocks_per_seq, n_tiles, qk_scale, \
+                           sp)
+    const bool ok = D == 64 ? (fp8 ? PA_PF_LAUNCH(64, true) : PA_PF_LAUNCH(64, false))
+                            : (fp8 ? PA_PF_LAUNCH(128, true) : PA_PF_LAUNCH(128, false));
+#undef PA_PF_LAUNCH
     if (!ok) return PA_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }

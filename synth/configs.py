@@ -35,6 +35,7 @@ Shapes follow the workloads the pages describe:
   history, and the finished requests' blocks are indexed and evicted leaf-first
   (LRU) under a 384-block budget (the 256-block prompt plus room for four
   batches), so that every step from the fourth on evicts.
+* ``prefill_chunks_fp8`` -- ``prefill_chunks`` on one-byte E4M3 pools.
 
 Seeds: workload k (1-based, in the order above) uses master seed 8300 + k.
 """
@@ -151,6 +152,12 @@ CONFIGS = [
         notes="16 requests per step: 4,096 cached system tokens + 32 novel tokens each; the "
               "prefix cache runs in the first 384 blocks, the no-reuse comparison in the rest",
         extra={"budget_blocks": 384, "watermark_blocks": 32},
+    ),
+    Workload(
+        name="prefill_chunks_fp8", index=10, num_layers=80, num_q_heads=64, num_kv_heads=8,
+        head_dim=128, block_size=16, dtype="fp8", num_blocks=4096, num_seqs=16,
+        length_kind="prefill", length_min=2048, length_max=2048, chunk_len=512,
+        notes="prefill_chunks on one-byte E4M3 pools (the chunks are quantized as they are written)",
     ),
 ]
 

@@ -290,7 +290,9 @@ def test_fp8_unsupported_geometries():
     with pytest.raises(pk.PagedKVError):                            # generic kernel: bf16 / fp32 only
         pk.decode(geom, K, V, 0, q, torch.empty_like(q), tab, ln, 1, kernel="generic")
     kn = torch.zeros(1, 2, 64, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(pk.PagedKVError):                            # chunked prefill: bf16 pools only
-        pk.prefill(geom, K, V, 0, q, kn, kn, torch.empty_like(q),
+    geom8 = pk.Geometry(1, 2, 64, 8, 8, "fp8")
+    K8, V8 = pk.alloc_pools(geom8)
+    with pytest.raises(pk.PagedKVError):                            # chunked prefill: B = 16 only
+        pk.prefill(geom8, K8, V8, 0, q, kn, kn, torch.empty_like(q),
                    torch.tensor([0, 1], dtype=torch.int32, device="cuda"), tab,
                    torch.zeros(1, dtype=torch.int32, device="cuda"), 1, 1)
