@@ -34,6 +34,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "../../include/pa.h"
 #include "pa_append.h"
@@ -92,11 +93,11 @@ struct PfCfg {
 
 // The same kernel serves bf16 pools (FP8 = false: tiles go straight from HBM
 // into LDS) and one-byte pools (FP8 = true: each thread loads its share of the
-// pair's E4M3 codes and scale bytes a step ahead into registers, converts them
-// exactly to fp32, applies the power-of-two scale of their key (v_ldexp_f32)
-// and writes bf16 into the same LDS image the bf16 path builds, so everything
-// after the staging is shared; code x 2^e is a bf16 number exactly unless it is
-// below the normal range, 2^-126, where it rounds).
+// pair's E4M3 codes and scale bytes a step ahead into registers and converts
+// them to bf16 with the power-of-two scale of their key in the conversion
+// instruction (round to nearest even of code x 2^e, exact unless below bf16's
+// normal range, 2^-126), writing into the same LDS image the bf16 path builds,
+// so everything after the staging is shared).
 template <int D, int G, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_mfma_kernel(
     const char* __restrict__ kpool, const char* __restrict__ vpool,
@@ -208,14 +209,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // image offset 16 * (256 u + tid): in the pool, 8 code bytes at element
   // offset el of tile tl, plus the scale bytes of their keys (K: one key, the
   // slot of the piece's row; V: 8 consecutive slots of one dimension).
+  constexpr int KP = LOADS / 2;  // pieces from K tiles (the first half); the rest from V
   struct Raw {
     u32x2 code[LOADS];
-    u32x2 scale[LOADS];  // K: low byte; V: 8 bytes, one per slot
+    uint32_t ks;       // K: the scale byte of piece u in byte u
+    u32x2 vs[KP];      // V: 8 bytes each, one per slot
   };
   auto load_raw = [&](int pj, Raw& r) {
     const int b0 = 2 * pj;
     const int p0 = guard_block(trow[b0], N);
     const int p1 = (b0 + 1 < nblk) ? guard_block(trow[b0 + 1], N) : p0;
+    r.ks = 0u;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int woff = (u * 256 + wave * 64) * 16;
@@ -224,36 +228,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const int p = (tl & 1) ? p1 : p0;
       const char* t = (tl < 2 ? kg : vg) + p * blk_stride;
       r.code[u] = *reinterpret_cast<const u32x2*>(t + el);
-      if (tl < 2) {
-        const uint32_t sb = (uint8_t)t[16 * D + ((el >> 5) & 15)];  // K: key = row of the W-chunk
-        r.scale[u] = u32x2{sb, 0u};
-      } else {
-        r.scale[u] = *reinterpret_cast<const u32x2*>(t + 16 * D + (el & 15));  // V: slots el%16 ..
-      }
+      if (u < KP)  // K: one key, the slot of the W-chunk row
+        r.ks |= (uint32_t)(uint8_t)t[16 * D + ((el >> 5) & 15)] << (8 * u);
+      else         // V: slots el % 16 .. + 7 of one dimension
+        r.vs[u - KP] = *reinterpret_cast<const u32x2*>(t + 16 * D + (el & 15));
     }
   };
+  // The conversion takes the scale as an fp32 operand: 2^(b - 127) is the float
+  // whose bits are b << 23 (a scale byte of 0 gives 0: rows with max |x| <=
+  // 448 * 2^-127 become 0). Its bf16 pair result is used as a whole 32-bit word.
+  auto cvt2 = [](uint32_t word, float scale, auto hi_half) -> uint32_t {
+    if constexpr (decltype(hi_half)::value)
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, scale, true));
+    else
+      return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, scale, false));
+  };
+  using lo_t = std::integral_constant<bool, false>;
+  using hi_t = std::integral_constant<bool, true>;
   auto stash_raw = [&](const Raw& r, int buf) {
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
       const int woff = (u * 256 + wave * 64) * 16;
-      const int tl = woff / TILE;
-      const auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(r.code[u][0], false);  // codes 0, 1
-      const auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(r.code[u][0], true);   // codes 2, 3
-      const auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(r.code[u][1], false);
-      const auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(r.code[u][1], true);
-      float x[8] = {f0[0], f0[1], f1[0], f1[1], f2[0], f2[1], f3[0], f3[1]};
-      if (tl < 2) {
-        const int e = (int)r.scale[u][0] - kFp8ScaleBias;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[k] = __builtin_amdgcn_ldexpf(x[k], e);
-      } else {
+      u32x4 w;
+      if (u < KP) {  // K: the 8 codes of one key, one scale
+        const float sk = __uint_as_float(((r.ks >> (8 * u)) & 0xffu) << 23);
+        w = u32x4{cvt2(r.code[u][0], sk, lo_t{}), cvt2(r.code[u][0], sk, hi_t{}),
+                  cvt2(r.code[u][1], sk, lo_t{}), cvt2(r.code[u][1], sk, hi_t{})};
+      } else {  // V: 8 keys; each code pair converted with both keys' scales, halves merged
+        float sv[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k)
-          x[k] = __builtin_amdgcn_ldexpf(
-              x[k], (int)((r.scale[u][k >> 2] >> (8 * (k & 3))) & 0xffu) - kFp8ScaleBias);
+          sv[k] = __uint_as_float(((r.vs[u - KP][k >> 2] >> (8 * (k & 3))) & 0xffu) << 23);
+        const uint32_t m = 0x0000ffffu;
+        w = u32x4{(cvt2(r.code[u][0], sv[0], lo_t{}) & m) | (cvt2(r.code[u][0], sv[1], lo_t{}) & ~m),
+                  (cvt2(r.code[u][0], sv[2], hi_t{}) & m) | (cvt2(r.code[u][0], sv[3], hi_t{}) & ~m),
+                  (cvt2(r.code[u][1], sv[4], lo_t{}) & m) | (cvt2(r.code[u][1], sv[5], lo_t{}) & ~m),
+                  (cvt2(r.code[u][1], sv[6], hi_t{}) & m) | (cvt2(r.code[u][1], sv[7], hi_t{}) & ~m)};
       }
-      const u32x4 w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
-                       pack_bf16x2(x[6], x[7])};
       *reinterpret_cast<u32x4*>(pf_smem + buf + woff + lane * 16) = w;
     }
   };
@@ -381,7 +392,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   auto step = [&](int pj, const f32x4 (&sc_cur)[2][2], f32x4 (&sc_next)[2][2]) {
     if constexpr (FP8) {
       if (pj + 2 < pend) stash_raw(raw, b_new);
-      if (pj + 3 < pend) load_raw(pj + 3, raw);
     } else {
       if (pj + 2 < pend) issue(pj + 2, b_new);
     }
@@ -398,6 +408,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       else
         lds_wait_sync<0>();
       scores(b_next, sc_next);
+    }
+    if constexpr (FP8) {  // after the K fragments of pair pj+1 are consumed
+      if (pj + 3 < pend) load_raw(pj + 3, raw);
     }
     finish(pj, vf, sc_cur);
     const int b_old = b_cur;
