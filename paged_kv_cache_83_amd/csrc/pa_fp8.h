@@ -115,6 +115,120 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ k
   }
 }
 
+// Bulk form for d = 128, B = 16: a work group quantizes 16 consecutive rows of
+// one head. Thread t handles piece t % 16 (8 dimensions) of row t / 16, for K
+// and for V; the row's maximum comes from its 16 lanes. K pieces leave as
+// 8-byte stores into the chunked layout. V goes through LDS: when 8 rows land
+// in 8 consecutive slots of one block starting at a multiple of 8 (a chunk of
+// a prompt), each dimension's 8 codes leave as one 8-byte store; otherwise as
+// single bytes. The codes are those of the general kernel (same scale rule,
+// same conversion instruction).
+template <typename SlotSrc>
+__global__ __launch_bounds__(256) void append_fp8_rows16_kernel(uint8_t* __restrict__ kpool,
+                                                               uint8_t* __restrict__ vpool,
+                                                               const uint16_t* __restrict__ knew,
+                                                               const uint16_t* __restrict__ vnew,
+                                                               SlotSrc slots, int64_t n_tok, int H,
+                                                               int64_t nslots, int64_t layer_off) {
+  constexpr int D = 128, B = 16, W = 32;
+  constexpr int64_t TB = (int64_t)B * D + B;
+  __shared__ uint8_t vcodes[16][D];  // [row][dimension]
+  __shared__ int64_t rslot[16];
+  const int h = (int)(blockIdx.x % H);
+  const int64_t grp = blockIdx.x / H;
+  const int t = threadIdx.x, r = t >> 4, piece = t & 15;
+  const int64_t j = grp * 16 + r;
+  int64_t slot = -1;
+  if (j < n_tok) {
+    slot = slots(j);
+    if (slot < 0 || slot >= nslots) slot = -1;
+  }
+  if (piece == 0) rslot[r] = slot;
+  const int64_t p = slot >= 0 ? slot / B : 0;
+  const int o = slot >= 0 ? (int)(slot % B) : 0;
+#pragma unroll
+  for (int kv = 0; kv < 2; ++kv) {
+    u32x4 raw = {0u, 0u, 0u, 0u};
+    if (j < n_tok) raw = *reinterpret_cast<const u32x4*>((kv ? vnew : knew) + (j * H + h) * D + 8 * piece);
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(raw[k] << 16);
+      x[2 * k + 1] = __uint_as_float(raw[k] & 0xffff0000u);
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+    const int e = fp8_scale_exp(amax);
+    uint32_t c[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x[4 * k], -e),
+                                              __builtin_amdgcn_ldexpf(x[4 * k + 1], -e), 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x[4 * k + 2], -e),
+                                          __builtin_amdgcn_ldexpf(x[4 * k + 3], -e), w, true);
+      c[k] = (uint32_t)w;
+    }
+    uint8_t* tile = (kv ? vpool : kpool) + layer_off + (p * H + h) * TB;
+    if (kv == 0) {
+      if (slot >= 0) {
+        const int d0 = 8 * piece;
+        *reinterpret_cast<u32x2*>(tile + (d0 / W) * B * W + o * W + d0 % W) = u32x2{c[0], c[1]};
+      }
+    } else {
+      *reinterpret_cast<u32x2*>(&vcodes[r][8 * piece]) = u32x2{c[0], c[1]};
+    }
+    if (piece == 0 && slot >= 0) tile[(int64_t)B * D + o] = (uint8_t)(e + kFp8ScaleBias);
+  }
+  __syncthreads();
+  // V: thread t writes dimension t % 128 of rows 8 * (t / 128) .. + 7
+  const int d = t & (D - 1), hf = t >> 7;
+  const int64_t s0 = rslot[8 * hf];
+  bool contig = s0 >= 0 && (s0 % 8) == 0;
+#pragma unroll
+  for (int k = 1; k < 8; ++k) contig = contig && rslot[8 * hf + k] == s0 + k;
+  if (contig) {
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      lo |= (uint32_t)vcodes[8 * hf + k][d] << (8 * k);
+      hi |= (uint32_t)vcodes[8 * hf + 4 + k][d] << (8 * k);
+    }
+    uint8_t* tile = vpool + layer_off + ((s0 / B) * H + h) * TB;
+    *reinterpret_cast<u32x2*>(tile + (int64_t)d * B + s0 % B) = u32x2{lo, hi};
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int64_t sk = rslot[8 * hf + k];
+      if (sk < 0) continue;
+      uint8_t* tile = vpool + layer_off + ((sk / B) * H + h) * TB;
+      tile[(int64_t)d * B + sk % B] = vcodes[8 * hf + k][d];
+    }
+  }
+}
+
+// The quantizing append for n_tok rows: the bulk form when the geometry allows,
+// the general one otherwise. Returns false if the grid would be too large.
+template <typename SlotSrc>
+inline bool launch_append_fp8(hipStream_t st, uint8_t* kpool, uint8_t* vpool, const uint16_t* knew,
+                              const uint16_t* vnew, SlotSrc slots, int64_t n_tok, int H, int D,
+                              int B, int64_t nslots, int64_t layer_off) {
+  if (D == 128 && B == 16) {
+    const int64_t wgs = (n_tok + 15) / 16 * H;
+    if (wgs > INT32_MAX) return false;
+    hipLaunchKernelGGL((append_fp8_rows16_kernel<SlotSrc>), dim3((unsigned)wgs), dim3(256), 0, st,
+                       kpool, vpool, knew, vnew, slots, n_tok, H, nslots, layer_off);
+    return true;
+  }
+  const int64_t wgs = (n_tok * H + 3) / 4;  // one wave per (row, head)
+  if (wgs > INT32_MAX) return false;
+  hipLaunchKernelGGL((append_fp8_kernel<SlotSrc>), dim3((unsigned)wgs), dim3(256), 0, st, kpool,
+                     vpool, knew, vnew, slots, n_tok, H, D, B, nslots, layer_off);
+  return true;
+}
+
 // ---------------------------------------------------------------------------
 // Decode, FP8 pool, matrix cores: B = 16, d in {64, 128}, up to 16 query heads
 // per KV head. The work decomposition, the score-row / key assignment, the

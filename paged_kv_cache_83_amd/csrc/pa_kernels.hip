@@ -770,14 +770,12 @@ pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t lay
   const int D = g->head_dim, B = g->block_size, H = g->num_kv_heads;
   const int64_t layer_off = (int64_t)layer * g->num_blocks * H * B * D;
   const int64_t nslots = (int64_t)g->num_blocks * B;
-  if (g->dtype == PA_FP8) {  // one wave per (token, head), 4 per work group
+  if (g->dtype == PA_FP8) {
     ProfScope ps("append", st);
-    const int64_t wgs = ((int64_t)n_tokens * H + 3) / 4;
-    if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((append_fp8_kernel<SlotsFromArray>), dim3((unsigned)wgs), dim3(256), 0, st,
-                       (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)k_new,
-                       (const uint16_t*)v_new, SlotsFromArray{slot_mapping}, (int64_t)n_tokens, H,
-                       D, B, nslots, (int64_t)layer * g->num_blocks * H * tile_bytes(g));
+    if (!launch_append_fp8(st, (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)k_new,
+                           (const uint16_t*)v_new, SlotsFromArray{slot_mapping}, (int64_t)n_tokens,
+                           H, D, B, nslots, (int64_t)layer * g->num_blocks * H * tile_bytes(g)))
+      return PA_ERR_UNSUPPORTED;
     return launch_status();
   }
   const size_t lds = g->dtype == PA_BF16 ? append_lds_bytes<uint16_t>(D) : append_lds_bytes<float>(D);
@@ -849,14 +847,13 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   float* part_ml = plan.direct ? nullptr : part_o + (size_t)n_seqs * n_q_heads * plan.S_max * D;
   if (plan.kernel == 3 && append) {  // FP8: quantize the step's tokens into the pool first
     ProfScope ps("append", st);
-    const int64_t wgs = ((int64_t)n_seqs * Hkv + 3) / 4;
-    hipLaunchKernelGGL((append_fp8_kernel<SlotsFromLens>), dim3((unsigned)wgs), dim3(256), 0, st,
-                       (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)knew,
-                       (const uint16_t*)vnew,
-                       SlotsFromLens{block_tables, context_lens, max_blocks_per_seq, max_context_len,
-                                     B, g->num_blocks},
-                       (int64_t)n_seqs, Hkv, D, B, (int64_t)g->num_blocks * B,
-                       (int64_t)layer * g->num_blocks * Hkv * tile_bytes(g));
+    if (!launch_append_fp8(st, (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)knew,
+                           (const uint16_t*)vnew,
+                           SlotsFromLens{block_tables, context_lens, max_blocks_per_seq,
+                                         max_context_len, B, g->num_blocks},
+                           (int64_t)n_seqs, Hkv, D, B, (int64_t)g->num_blocks * B,
+                           (int64_t)layer * g->num_blocks * Hkv * tile_bytes(g)))
+      return PA_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   {

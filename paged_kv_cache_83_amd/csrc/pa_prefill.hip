@@ -599,13 +599,11 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
 
   if (fp8) {  // the chunks' rows are quantized into their positions (one wave per row and head)
     ProfScope ps("prefill_append", st);
-    const int64_t wgs = ((int64_t)n_tokens * Hkv + 3) / 4;
-    if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
     const SlotsFromTables src{cb, block_tables, max_blocks_per_seq, B, g->num_blocks};
-    hipLaunchKernelGGL((append_fp8_kernel<SlotsFromTables>), dim3((unsigned)wgs), dim3(256), 0, st,
-                       (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)k_new,
-                       (const uint16_t*)v_new, src, (int64_t)n_tokens, Hkv, D, B,
-                       (int64_t)g->num_blocks * B, layer_off);
+    if (!launch_append_fp8(st, (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)k_new,
+                           (const uint16_t*)v_new, src, (int64_t)n_tokens, Hkv, D, B,
+                           (int64_t)g->num_blocks * B, layer_off))
+      return PA_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   } else {  // the chunks' keys and values go to their positions through the block tables
     ProfScope ps("prefill_append", st);
