@@ -595,6 +595,8 @@ def run_prefill(args):
     tables = torch.from_numpy(np.ascontiguousarray(tables_np)).to(dev)
     ctx = torch.from_numpy(hist.astype(np.int32)).to(dev)
     max_ctx = int((hist + C).max())
+    pf_ws = torch.empty(max(1, pk.prefill_workspace_bytes(geom, n_tok, Hq, args.pf_splits)),
+                        dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     profiling = [False]
@@ -605,7 +607,8 @@ def run_prefill(args):
             if prof:
                 pk.Profiler.enable(True)
             pk.prefill(geom, k_pool, v_pool, layer, q_all[layer], k_all[layer], v_all[layer],
-                       out[layer], q_start, tables, ctx, C, max_ctx, stream=stream)
+                       out[layer], q_start, tables, ctx, C, max_ctx, stream=stream,
+                       splits=args.pf_splits, workspace=pf_ws)
             if prof:
                 pk.Profiler.enable(False)
 
@@ -629,17 +632,31 @@ def run_prefill(args):
 
     kern, roofline = {}, None
     if not args.no_prof and not args.graph:
-        for name in ("prefill_append", "prefill_attention"):
+        for name in ("prefill_append", "prefill_attention", "prefill_combine"):
             cnt, tot = pk.Profiler.read(name)
             if cnt:
                 kern[name] = {"launches": cnt, "avg_us": round(1e3 * tot / cnt, 2)}
         if "prefill_attention" in kern:
             avg_s = kern["prefill_attention"]["avg_us"] * 1e-6
-            ach = 2 * macs_layer / avg_s / 1e12
-            roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                        "kernel": "prefill_mfma_kernel", "flops_per_launch": 2 * macs_layer,
-                        "avg_launch_us": round(avg_s * 1e6, 2)}
+            # algorithmic bytes of one launch: the visible K/V (history and chunk,
+            # pool bytes per token and head), the queries and outputs (bf16)
+            kv_tok = 2 * d * (1 if fp8 else geom.elem_bytes) + (2 if fp8 else 0)
+            bytes_layer = int(sum(int(c) + C for c in hist)) * Hkv * kv_tok + 2 * n_tok * Hq * d * 2
+            flops_layer = 2 * macs_layer
+            if flops_layer / bytes_layer >= PEAK_BF16_TFLOPS * 1e12 / (PEAK_GBS * 1e9):
+                ach = flops_layer / avg_s / 1e12
+                roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                            "traffic": None, "kernel": "prefill_mfma_kernel",
+                            "flops_per_launch": flops_layer, "avg_launch_us": round(avg_s * 1e6, 2)}
+            else:
+                ach = bytes_layer / avg_s / 1e9
+                roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS,
+                            "unit": "GB/s", "frac": round(ach / PEAK_GBS, 4), "traffic": None,
+                            "kernel": "prefill_mfma_kernel", "bytes_per_launch": bytes_layer,
+                            "avg_launch_us": round(avg_s * 1e6, 2)}
+            if "prefill_combine" in kern:
+                roofline["combine_avg_us"] = kern["prefill_combine"]["avg_us"]
 
     # parity on sampled (chunk, layer) outputs; cpu baseline = the oracle on a sample
     parity, cpu_baseline = None, None
@@ -718,6 +735,7 @@ def run_prefill(args):
         "config": {"workload": cfg.name, "num_layers": L, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": d, "block_size": B, "num_seqs": n, "chunk_len": C,
                    "histories": sorted(set(int(c) for c in hist)), "prompt_len": cfg.length_max,
+                   "splits": args.pf_splits,
                    "launch": "hip graph replay" if args.graph else "eager"},
         "step_ms": step_ms,
         "tokens_per_s": round(n_tok / (ms * 1e-3), 1),
@@ -1393,7 +1411,7 @@ def main():
         run_offload(args)
     elif cfg.name == "offload_overlap":
         run_overlap(args)
-    elif cfg.length_kind == "prefill":
+    elif cfg.length_kind in ("prefill", "verify"):
         run_prefill(args)
     elif cfg.length_kind == "prefix":
         run_prefix_reuse(args)

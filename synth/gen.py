@@ -40,7 +40,7 @@ def context_lengths(cfg: Workload) -> np.ndarray:
         return np.full(n, cfg.length_min, dtype=np.int64)
     if cfg.length_kind == "fork":
         return cfg.prefix_len + suffix_lengths(cfg)
-    if cfg.length_kind == "prefill":
+    if cfg.length_kind in ("prefill", "verify"):
         return prefill_histories(cfg) + cfg.chunk_len
     if cfg.length_kind == "prefix":
         return np.full(n, cfg.prefix_len + cfg.chunk_len, dtype=np.int64)
@@ -49,7 +49,10 @@ def context_lengths(cfg: Workload) -> np.ndarray:
 
 def prefill_histories(cfg: Workload) -> np.ndarray:
     """Cached tokens before each sequence's chunk: sequence i runs chunk
-    (i mod K) + 1 of a prompt of length_max tokens cut into K chunks."""
+    (i mod K) + 1 of a prompt of length_max tokens cut into K chunks; for the
+    verify workload every sequence holds length_max - chunk_len tokens."""
+    if cfg.length_kind == "verify":
+        return np.full(cfg.num_seqs, cfg.length_max - cfg.chunk_len, dtype=np.int64)
     k = cfg.length_max // cfg.chunk_len
     return (np.arange(cfg.num_seqs) % k * cfg.chunk_len).astype(np.int64)
 
