@@ -81,8 +81,9 @@ def log(msg):
 
 def decode_kernel_source_sha() -> str:
     """sha256 prefix of the bf16 matrix-core decode kernel's source: its section of
-    pa_kernels.hip (from its banner to the generic kernel's) and the device
-    helpers it includes. Edits elsewhere in the file leave it unchanged."""
+    pa_kernels.hip (from its banner to the generic kernel's), the device helpers
+    and the pair-load helpers it includes. Edits elsewhere in the file leave it
+    unchanged."""
     here = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(here, "paged_kv_cache_83_amd", "csrc")
     text = open(os.path.join(csrc, "pa_kernels.hip"), "rb").read()
@@ -90,6 +91,7 @@ def decode_kernel_source_sha() -> str:
     b = text.index(b"// Decode, generic kernel")
     h = hashlib.sha256(text[a:b])
     h.update(open(os.path.join(csrc, "pa_device.h"), "rb").read())
+    h.update(open(os.path.join(csrc, "pa_pairs.h"), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -595,7 +597,8 @@ def run_prefill(args):
     tables = torch.from_numpy(np.ascontiguousarray(tables_np)).to(dev)
     ctx = torch.from_numpy(hist.astype(np.int32)).to(dev)
     max_ctx = int((hist + C).max())
-    pf_ws = torch.empty(max(1, pk.prefill_workspace_bytes(geom, n_tok, Hq, args.pf_splits)),
+    pf_ws = torch.empty(max(1, pk.prefill_workspace_bytes(geom, n, n_tok, Hq, C, max_ctx,
+                                                           args.pf_splits)),
                         dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
@@ -632,12 +635,17 @@ def run_prefill(args):
 
     kern, roofline = {}, None
     if not args.no_prof and not args.graph:
-        for name in ("prefill_append", "prefill_attention", "prefill_combine"):
+        for name in ("prefill_append", "prefill_attention", "prefill_short", "prefill_combine"):
             cnt, tot = pk.Profiler.read(name)
             if cnt:
                 kern[name] = {"launches": cnt, "avg_us": round(1e3 * tot / cnt, 2)}
-        if "prefill_attention" in kern:
-            avg_s = kern["prefill_attention"]["avg_us"] * 1e-6
+        # the attention kernel the library chose: 128-row tiles, or one wave per
+        # (chunk, KV head, split) for chunks of at most 32 query rows per KV head
+        attn = next((k for k in ("prefill_short", "prefill_attention") if k in kern), None)
+        kname = {"prefill_short": "prefill_short_kernel",
+                 "prefill_attention": "prefill_mfma_kernel"}.get(attn)
+        if attn:
+            avg_s = kern[attn]["avg_us"] * 1e-6
             # algorithmic bytes of one launch: the visible K/V (history and chunk,
             # pool bytes per token and head), the queries and outputs (bf16)
             kv_tok = 2 * d * (1 if fp8 else geom.elem_bytes) + (2 if fp8 else 0)
@@ -647,13 +655,13 @@ def run_prefill(args):
                 ach = flops_layer / avg_s / 1e12
                 roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                            "traffic": None, "kernel": "prefill_mfma_kernel",
+                            "traffic": None, "kernel": kname,
                             "flops_per_launch": flops_layer, "avg_launch_us": round(avg_s * 1e6, 2)}
             else:
                 ach = bytes_layer / avg_s / 1e9
                 roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_GBS,
                             "unit": "GB/s", "frac": round(ach / PEAK_GBS, 4), "traffic": None,
-                            "kernel": "prefill_mfma_kernel", "bytes_per_launch": bytes_layer,
+                            "kernel": kname, "bytes_per_launch": bytes_layer,
                             "avg_launch_us": round(avg_s * 1e6, 2)}
             if "prefill_combine" in kern:
                 roofline["combine_avg_us"] = kern["prefill_combine"]["avg_us"]
@@ -1162,7 +1170,7 @@ def run_prefix_reuse(args):
     log(f"cold prefill of the {P}-token system prompt: {cold_ms:.2f} ms (80 layers, q drawn per layer)")
 
     q_start = torch.arange(0, n * C + 1, C, dtype=torch.int32, device=dev)
-    pf_ws = torch.empty(max(1, pk.prefill_workspace_bytes(geom, n * C, Hq, args.pf_splits)),
+    pf_ws = torch.empty(max(1, pk.prefill_workspace_bytes(geom, n, n * C, Hq, C, S, args.pf_splits)),
                         dtype=torch.uint8, device=dev)
     # two sets of tables: the host fills one while kernels of the previous batch
     # still read the other; an event per set says when its upload has run

@@ -206,16 +206,20 @@ pa_status pa_decode_append(const pa_geom* g, void* k_pool, void* v_pool, int32_t
  * the row's own position. max_q_len bounds every chunk length and sizes the
  * launch; max_context_len bounds ctx_lens[i] + chunk length (values are clamped
  * to these bounds, never read past them). scale <= 0 means 1/sqrt(d).
- * Implemented for bf16 pools with B = 16, d in {64, 128} and n_q_heads / H_kv
- * dividing 32; other geometries return PA_ERR_UNSUPPORTED.
- * Splits: the visible keys of each tile of query rows may be cut into n_splits
+ * Implemented for bf16 and FP8 (E4M3, per-token scales) pools with B = 16,
+ * d in {64, 128} and n_q_heads / H_kv dividing 32; other geometries return
+ * PA_ERR_UNSUPPORTED.
+ * Splits: the visible keys of each group of query rows may be cut into n_splits
  * ranges processed in parallel, whose partial results (unnormalised output,
  * maximum, sum) go to the caller's workspace and are merged by the same
  * online-softmax rule (section "Chunked prefill mechanics"). n_splits = 1: no
- * split, no workspace; 2..16: that many (PA_ERR_WORKSPACE if workspace_bytes is
- * below pa_prefill_workspace_bytes for it); 0: chosen from the launch size (up
- * to 4, for batches too small to fill the device), falling back to 1 when the
- * workspace is missing or too small. */
+ * split, no workspace; 2..64: that many (PA_ERR_WORKSPACE if workspace_bytes is
+ * below pa_prefill_workspace_bytes for the same arguments); 0: chosen from the
+ * launch shape, falling back to no split when the workspace is missing or too
+ * small. Short chunks on bf16 pools (n_q_heads / H_kv x max_q_len <= 32, e.g. a
+ * few draft tokens per sequence) are computed one wave per (chunk, KV head,
+ * split), the automatic choice splitting long histories into up to 64 ranges of
+ * at most 256 blocks; longer chunks in 128-row tiles with up to 4 splits. */
 pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer, const void* q,
                      const void* k_new, const void* v_new, void* out, int32_t n_seqs,
                      int32_t n_tokens, int32_t n_q_heads, const int32_t* q_start,
@@ -223,10 +227,11 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
                      const int32_t* ctx_lens, int32_t max_q_len, int32_t max_context_len,
                      float scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
                      void* stream);
-/* Device workspace bytes pa_prefill needs for n_splits splits of n_tokens rows
- * (n_splits 0: the most the automatic choice uses; 1: 0 bytes); 0 for bad
- * arguments. */
-size_t pa_prefill_workspace_bytes(const pa_geom* g, int32_t n_tokens, int32_t n_q_heads,
+/* Device workspace bytes pa_prefill needs when called with these arguments (0:
+ * none; also 0 for bad or unsupported arguments). The automatic choice
+ * (n_splits 0) uses exactly this much when given it. */
+size_t pa_prefill_workspace_bytes(const pa_geom* g, int32_t n_seqs, int32_t n_tokens,
+                                  int32_t n_q_heads, int32_t max_q_len, int32_t max_context_len,
                                   int32_t n_splits);
 
 /* Copy-on-write block copy: for each k, block dst[k] <- block src[k] in every

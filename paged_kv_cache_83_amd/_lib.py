@@ -57,7 +57,7 @@ SIGNATURES = {
                                 _vp, _i32, _f32, _popts, _vp, _sz, _vp]),
     "pa_prefill": (_i32, [_pg, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
                           _i32, _vp, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
-    "pa_prefill_workspace_bytes": (_sz, [_pg, _i32, _i32, _i32]),
+    "pa_prefill_workspace_bytes": (_sz, [_pg, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_copy_blocks": (_i32, [_pg, _vp, _vp, _vp, _vp, _i32, _vp]),
     "pa_gather_blocks": (_i32, [_pg, _vp, _vp, _vp, _i32, _vp, _vp]),
     "pa_scatter_blocks": (_i32, [_pg, _vp, _vp, _vp, _vp, _i32, _vp]),

@@ -227,11 +227,13 @@ def decode_append(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, o
           "pa_decode_append")
 
 
-def prefill_workspace_bytes(geom: Geometry, n_tokens: int, n_q_heads: int, splits: int = 0) -> int:
-    """Workspace bytes prefill needs for `splits` splits (0: the most the automatic
-    choice uses)."""
+def prefill_workspace_bytes(geom: Geometry, n_seqs: int, n_tokens: int, n_q_heads: int,
+                            max_q_len: int, max_context_len: int, splits: int = 0) -> int:
+    """Workspace bytes prefill needs for these arguments (splits 0: what the
+    automatic choice uses)."""
     g = geom.c()
-    return int(_L().pa_prefill_workspace_bytes(C.byref(g), n_tokens, n_q_heads, splits))
+    return int(_L().pa_prefill_workspace_bytes(C.byref(g), n_seqs, n_tokens, n_q_heads, max_q_len,
+                                                max_context_len, splits))
 
 
 def prefill(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out, q_start, block_tables,

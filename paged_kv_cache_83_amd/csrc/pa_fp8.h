@@ -15,6 +15,7 @@
 #pragma once
 
 #include "pa_device.h"
+#include "pa_pairs.h"
 
 namespace pa_detail {
 
@@ -249,12 +250,6 @@ __device__ __forceinline__ u32x2 kv_load8(const uint8_t* p) {
   else return *reinterpret_cast<const u32x2*>(p);
 }
 
-__device__ __forceinline__ int fp8_table_at(const int (&tb)[4], int off) {
-  const int r = off >> 6;
-  const int v = r == 0 ? tb[0] : r == 1 ? tb[1] : r == 2 ? tb[2] : tb[3];
-  return __builtin_amdgcn_readlane(v, off & 63);
-}
-
 template <int D, bool NT>
 __device__ __forceinline__ void fp8_issue_pair(Fp8Frags<D>& f, const uint8_t* __restrict__ kl,
                                                const uint8_t* __restrict__ vl, int p0, int p1,
@@ -418,8 +413,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int npairs = (span + 1) >> 1;
   auto issue_at = [&](Fp8Frags<D>& fr, int pj) {
     const int off = 2 * pj;
-    const int p0 = fp8_table_at(tb, off);
-    const int p1 = (off + 1 < span) ? fp8_table_at(tb, off + 1) : p0;
+    const int p0 = table_at(tb, off);
+    const int p1 = (off + 1 < span) ? table_at(tb, off + 1) : p0;
     fp8_issue_pair<D, NT>(fr, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, s_off, gq);
   };
   // NS pairs in flight; steady loop issues unconditionally, the tail drains

@@ -29,6 +29,9 @@
 // reference is only a bound on the size of the probabilities). Work-group
 // order is XCD-aware: the tiles of one (chunk, KV head) run one after another on
 // one XCD, so its history is read from HBM once and from that XCD's L2 after.
+// Chunks of at most 32 query rows per KV head take a second kernel,
+// prefill_short_kernel: one wave holds all of them and streams the history
+// through registers like the decode kernel.
 
 #include <hip/hip_runtime.h>
 
@@ -40,6 +43,7 @@
 #include "pa_append.h"
 #include "pa_device.h"
 #include "pa_fp8.h"
+#include "pa_pairs.h"
 
 namespace {
 
@@ -61,7 +65,7 @@ __device__ __forceinline__ void lds_wait_sync() {
 // to fill the chip): each split writes its unnormalised output, its reference
 // maximum (log2 units) and its sum, and a second kernel merges them with the
 // online-softmax rule ("Chunked prefill mechanics": the m, l, O recurrence).
-constexpr int kPfMaxSplits = 16;
+constexpr int kPfMaxSplits = 64;
 constexpr int kPfAutoMaxSplits = 4;
 constexpr int kPfTargetWgs = 512;       // two resident work groups per CU
 constexpr int kPfMinPairsPerSplit = 8;
@@ -505,6 +509,251 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __res
       make_uint2(pack_bf16x2(o[0] * inv, o[1] * inv), pack_bf16x2(o[2] * inv, o[3] * inv));
 }
 
+// Short chunks: at most 32 query rows per KV head (G x chunk length <= 32, a
+// few tokens per sequence, as when a draft's tokens are verified against a long
+// history). A 128-row tile would leave most of its waves on padding, so one wave
+// per (chunk, KV head, split of the keys) holds every row of the chunk as CT
+// 16-column MFMA tiles and takes each pair of blocks from the pool straight into
+// operand registers, the way the decode kernel does (two pairs in flight, no
+// LDS); the pair's K and V fragments serve all CT tiles, so the history is read
+// once. Row r = 16*ct + c is chunk token r / G, query head g*G + r % G; its keys
+// stop at its own position, so pairs reaching past the chunk's first position
+// are masked per column, and slots at or past the chunk's end get zero
+// probability and zeroed V. Splits cover bps blocks each (even, at most 256: the
+// table entries of a split sit in four registers of the wave); with more than
+// one, each writes its partial result in the layout prefill_combine_kernel
+// merges. With CT = 2 and d = 128 the wave holds 64 accumulators, 32 query and
+// 128 fragment registers per lane, beyond the 256 of two waves per SIMD: it
+// runs alone on its SIMD, which the launch sizes for (about one wave per SIMD).
+template <int D, int CT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128 ? 1 : PA_MFMA_WPE))) void prefill_short_kernel(
+    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ out, ChunkBatch cb,
+    const int32_t* __restrict__ tables, int64_t layer_off, int N, int Hkv, int Hq, int G,
+    int max_blocks, int bps, float qk_scale, PfSplit sp) {
+  constexpr int KC = MfmaCfg<D>::KC;
+  constexpr int DT = MfmaCfg<D>::DT;
+  constexpr int NS = MfmaCfg<D>::kStages;
+
+  // KV head fastest, then split: the waves reading one sequence's blocks start together.
+  const int w = blockIdx.x;
+  const int g = w % Hkv;
+  const int si = w / Hkv;
+  const int s = si % sp.n;
+  const int i = si / sp.n;
+  if (i >= cb.n_seqs) return;
+  const int lane = threadIdx.x;
+  const int c = lane & 15;
+  const int gq = lane >> 4;
+  int a, q_len, ctx;
+  cb.chunk(i, a, q_len, ctx);
+  if (q_len == 0) return;
+  const int total = ctx + q_len;  // keys [0, total) exist; row t sees [0, ctx + t]
+  const int nblk = (total + 15) >> 4;
+  const int b0 = s * bps;
+  const int b1 = min(b0 + bps, nblk);
+
+  bf16x8 qf[CT][KC];
+  int lim[CT];
+  bool rvalid[CT];
+  int64_t orow[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int r = 16 * ct + c;
+    const int t = r / G;
+    rvalid[ct] = t < q_len;
+    lim[ct] = rvalid[ct] ? ctx + t + 1 : total;  // padding columns: zero queries, any limit
+    orow[ct] = (int64_t)(a + (rvalid[ct] ? t : 0)) * Hq + g * G + r % G;
+    const uint16_t* qrow = q + orow[ct] * D;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (rvalid[ct]) v = *reinterpret_cast<const u32x4*>(qrow + 32 * kc + 8 * gq);
+      qf[ct][kc] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x4 acc[CT][DT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[CT], l_run[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    m_run[ct] = -INFINITY;
+    l_run[ct] = 0.f;
+  }
+
+  if (b0 < b1) {  // uniform; an empty split (past the chunk's end) writes m = -inf, l = 0, O = 0
+    const int32_t* trow = tables + (int64_t)i * max_blocks;
+    int tb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int idx = b0 + 64 * k + lane;
+      tb[k] = (64 * k < b1 - b0 && idx < b1) ? guard_block(trow[idx], N) : 0;
+    }
+    const uint16_t* kl = kpool + layer_off;
+    const uint16_t* vl = vpool + layer_off;
+    // Score row c of each tile holds pair-local key 8*(c>>2) + 4*t + (c&3); the
+    // lane's V^T fragment is block (gq >> 1), dims 16*dt + c, slots 8*(gq&1) .. +8.
+    const int k_sel = c >> 3;
+    const int k_off0 = 8 * ((c >> 2) & 1) + (c & 3);
+    const int v_sel = gq >> 1;
+    const int v_off = 16 * c + 8 * (gq & 1);
+    const int span = b1 - b0;
+    const int npairs = (span + 1) >> 1;
+    auto issue_at = [&](PairFrags<D>& fr, int pj) {
+      const int off = 2 * pj;
+      const int p0 = table_at(tb, off);
+      const int p1 = (off + 1 < span) ? table_at(tb, off + 1) : p0;
+      issue_pair<D, true>(fr, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq, -1, nullptr);
+      // Keep the loads ahead of the products of the pair before them: moved
+      // below its first product they would start only after that pair's wait.
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // One pair: S^T for every tile, the masked online-softmax update (the scale
+    // enters in the exponent, p = 2^(s*c - m*c); the reference maximum moves
+    // only when passed by more than kLazyLog2), then O^T += V^T P^T per tile.
+    auto compute = [&](PairFrags<D>& f, int pj) {
+      const int k0 = 16 * (b0 + 2 * pj);  // first key of the pair
+      f32x4 sc[CT][2];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          sc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            sc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, f.k[t][kc]), qf[ct][kc], sc[ct][t], 0, 0, 0);
+        }
+      const int key0 = k0 + 8 * gq;  // the lane's keys: key0 + 4*t + e (scores), key0 + e (V)
+      if (k0 + 32 > total) {  // uniform: slots past the data hold anything (0 * NaN guard)
+        u32x4 keep;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) {
+          const int p = key0 + 2 * wv;
+          keep[wv] = (p < total ? 0x0000ffffu : 0u) | (p + 1 < total ? 0xffff0000u : 0u);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) f.v[dt] &= keep;
+      }
+      const bool masked = k0 + 32 > ctx + 1;  // uniform: some key past the first row's position
+      float m_new[CT], psum[CT];
+      uint32_t pw[CT][4];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        float sv[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[4 * t + e] = sc[ct][t][e];
+        if (masked) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (key0 + 4 * t + e >= lim[ct]) sv[4 * t + e] = -INFINITY;
+        }
+        float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        mb = max_over_groups(mb);
+        // A column may see no key of this split yet (its maximum stays -inf and
+        // its probabilities 0).
+        const float m_cand = fmaxf(m_run[ct], mb);
+        m_new[ct] = ((m_cand - m_run[ct]) * qk_scale > kLazyLog2) ? m_cand : m_run[ct];
+        const float ms = (m_new[ct] == -INFINITY) ? 0.f : -m_new[ct] * qk_scale;
+        psum[ct] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk_scale, ms));
+          const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], qk_scale, ms));
+          psum[ct] += pa + pb;
+          pw[ct][e >> 1] = pack_bf16x2(pa, pb);
+        }
+      }
+      bool moved = false;
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) moved = moved || m_new[ct] != m_run[ct];
+      if (__any(moved)) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const float alpha = (m_new[ct] == m_run[ct])
+                                  ? 1.f
+                                  : __builtin_amdgcn_exp2f((m_run[ct] - m_new[ct]) * qk_scale);
+          l_run[ct] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[ct][dt] = acc[ct][dt] * alpha;
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        l_run[ct] += psum[ct];
+        m_run[ct] = m_new[ct];
+        const bf16x8 pf =
+            __builtin_bit_cast(bf16x8, make_uint4(pw[ct][0], pw[ct][1], pw[ct][2], pw[ct][3]));
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.v[dt]),
+                                                                pf, acc[ct][dt], 0, 0, 0);
+      }
+    };
+
+    // NS pairs in flight, as in the decode kernel: the steady loop issues
+    // unconditionally, an unrolled tail drains the last pairs.
+    PairFrags<D> f[NS];
+    int pj = 0;
+    if (npairs >= 2 * NS - 1) {
+#pragma unroll
+      for (int st = 0; st < NS - 1; ++st) issue_at(f[st], st);
+      for (; pj + 2 * NS - 1 <= npairs; pj += NS) {
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          issue_at(f[(st + NS - 1) % NS], pj + st + NS - 1);
+          compute(f[st], pj + st);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < NS - 1; ++st)
+        if (st < npairs) issue_at(f[st], st);
+    }
+#pragma unroll
+    for (int k = 0; k < 2 * NS - 2; ++k) {
+      if (pj + k >= npairs) break;
+      if (pj + k + NS - 1 < npairs) issue_at(f[(k + NS - 1) % NS], pj + k + NS - 1);
+      compute(f[k % NS], pj + k);
+    }
+  }
+
+  // acc[ct][dt][e] = O^T[d = 16*dt + 4*gq + e][row 16*ct + c]
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const float l = sum_over_groups(l_run[ct]);
+    if (!rvalid[ct]) continue;
+    if (sp.n == 1) {
+      const float inv = 1.f / l;
+      uint16_t* o = out + orow[ct] * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) =
+            make_uint2(pack_bf16x2(acc[ct][dt][0] * inv, acc[ct][dt][1] * inv),
+                       pack_bf16x2(acc[ct][dt][2] * inv, acc[ct][dt][3] * inv));
+    } else {
+      const int64_t slot = orow[ct] * sp.n + s;
+      float* po = sp.part_o + slot * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<f32x4*>(po + 16 * dt + 4 * gq) = acc[ct][dt];
+      if (gq == 0)
+        *reinterpret_cast<float2*>(sp.part_ml + slot * 2) =
+            make_float2(m_run[ct] == -INFINITY ? -INFINITY : m_run[ct] * qk_scale, l);
+    }
+  }
+}
+
 template <int D, int G, bool FP8>
 void launch_prefill(dim3 grid, size_t lds, hipStream_t st, const char* kp, const char* vp,
                     const uint16_t* q, uint16_t* out, ChunkBatch cb, const int32_t* tables,
@@ -551,15 +800,94 @@ size_t split_bytes(int64_t n_tokens, int Hq, int D, int S) {
   return S > 1 ? (size_t)S * n_tokens * Hq * (D + 2) * sizeof(float) : 0;
 }
 
+// Short-chunk kernel: about one wave per SIMD once the batch is split (each
+// wave pays two dependent load latencies at start, block ids then its first
+// pair, so fewer, longer waves beat more, shorter ones), at least 16 blocks each.
+constexpr int64_t kPfShortTargetWaves = 1024;
+constexpr int64_t kPfShortMinBps = 16;
+
+struct PfPlan {
+  bool short_path;  // prefill_short_kernel, else prefill_mfma_kernel
+  int CT;           // short: 16-column tiles of query rows (1 or 2)
+  int S;            // splits of the keys
+  int bps;          // short: blocks per split
+  int n_tiles;      // tile kernel: 128-row tiles per (chunk, KV head)
+};
+
+// Launch shape of pa_prefill (arguments already checked). Chunks of at most 32
+// query rows per KV head take the short kernel when their keys fit in at most
+// kPfMaxSplits splits of kMfmaMaxBps blocks (with n_splits > 0: exactly that many
+// splits); everything else takes the tile kernel.
+PfPlan pf_plan(int n_seqs, int Hkv, int G, int max_q_len, int max_ctx, int n_splits, bool fp8) {
+  PfPlan p{};
+  const int64_t maxb = ((int64_t)max_ctx + 15) / 16;
+  if (!fp8 && (int64_t)G * max_q_len <= 32 && maxb > 0) {
+    int64_t S, bps;
+    if (n_splits > 0) {
+      S = n_splits;
+      bps = (maxb + S - 1) / S;
+    } else {
+      const int64_t units = (int64_t)n_seqs * Hkv;
+      const int64_t want = units >= kPfShortTargetWaves ? 1 : (kPfShortTargetWaves + units - 1) / units;
+      bps = std::max(kPfShortMinBps, (maxb + want - 1) / want);
+      bps = std::min<int64_t>(bps + (bps & 1), kMfmaMaxBps);
+      S = (maxb + bps - 1) / bps;
+    }
+    bps = std::max<int64_t>(2, bps + (bps & 1));  // pairs never straddle two splits
+    if (bps <= kMfmaMaxBps && S <= kPfMaxSplits) {
+      p.short_path = true;
+      p.CT = G * max_q_len <= 16 ? 1 : 2;
+      p.S = (int)S;
+      p.bps = (int)bps;
+      return p;
+    }
+  }
+  const int TQ = kPfRows / G;
+  p.n_tiles = (max_q_len + TQ - 1) / TQ;
+  const int64_t tiles = (int64_t)n_seqs * Hkv * p.n_tiles;
+  const int max_pairs = (int)((maxb + 1) / 2);
+  p.S = n_splits == 0 ? auto_splits(tiles, max_pairs) : n_splits;
+  return p;
+}
+
+// The tile kernel without splits: what an automatic choice falls back to when
+// the caller's workspace cannot hold the partials.
+PfPlan pf_plan_unsplit(int G, int max_q_len) {
+  PfPlan p{};
+  const int TQ = kPfRows / G;
+  p.n_tiles = (max_q_len + TQ - 1) / TQ;
+  p.S = 1;
+  return p;
+}
+
+// Argument checks shared by pa_prefill and pa_prefill_workspace_bytes.
+pa_status pf_check(const pa_geom* g, int32_t n_seqs, int32_t n_tokens, int32_t n_q_heads,
+                   int32_t max_q_len, int32_t max_context_len, int32_t n_splits) {
+  if (!geom_ok(g) || n_seqs < 0 || n_tokens < 0 || n_q_heads <= 0 || max_q_len < 0 ||
+      max_context_len < 0 || n_splits < 0 || n_splits > kPfMaxSplits)
+    return PA_ERR_INVALID_ARG;
+  const int B = g->block_size, D = g->head_dim, Hkv = g->num_kv_heads;
+  if (n_q_heads % Hkv != 0 || max_q_len > max_context_len) return PA_ERR_INVALID_ARG;
+  const int G = n_q_heads / Hkv;
+  if ((g->dtype != PA_BF16 && g->dtype != PA_FP8) || B != 16 || (D != 64 && D != 128) || G > 32 ||
+      32 % G != 0)
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-size_t pa_prefill_workspace_bytes(const pa_geom* g, int32_t n_tokens, int32_t n_q_heads,
+size_t pa_prefill_workspace_bytes(const pa_geom* g, int32_t n_seqs, int32_t n_tokens,
+                                  int32_t n_q_heads, int32_t max_q_len, int32_t max_context_len,
                                   int32_t n_splits) {
-  if (!geom_ok(g) || n_tokens < 0 || n_q_heads <= 0 || n_splits < 0 || n_splits > kPfMaxSplits)
+  if (pf_check(g, n_seqs, n_tokens, n_q_heads, max_q_len, max_context_len, n_splits) != PA_OK)
     return 0;
-  return split_bytes(n_tokens, n_q_heads, g->head_dim, n_splits == 0 ? kPfAutoMaxSplits : n_splits);
+  if (n_seqs == 0 || n_tokens == 0 || max_q_len == 0) return 0;
+  const PfPlan p = pf_plan(n_seqs, g->num_kv_heads, n_q_heads / g->num_kv_heads, max_q_len,
+                           max_context_len, n_splits, g->dtype == PA_FP8);
+  return split_bytes(n_tokens, n_q_heads, g->head_dim, p.S);
 }
 
 pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer, const void* q,
@@ -569,29 +897,26 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
                      const int32_t* ctx_lens, int32_t max_q_len, int32_t max_context_len,
                      float scale, int32_t n_splits, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  if (!geom_ok(g) || layer < 0 || layer >= g->num_layers || n_seqs < 0 || n_tokens < 0 ||
-      n_q_heads <= 0 || max_q_len < 0 || max_context_len < 0 || max_blocks_per_seq < 0 ||
-      n_splits < 0 || n_splits > kPfMaxSplits)
-    return PA_ERR_INVALID_ARG;
+  {
+    const pa_status st =
+        pf_check(g, n_seqs, n_tokens, n_q_heads, max_q_len, max_context_len, n_splits);
+    if (st == PA_ERR_INVALID_ARG) return st;
+    if (layer < 0 || layer >= g->num_layers || max_blocks_per_seq < 0) return PA_ERR_INVALID_ARG;
+    if ((int64_t)max_blocks_per_seq * g->block_size < max_context_len) return PA_ERR_INVALID_ARG;
+    if (st != PA_OK) return st;
+  }
   const int B = g->block_size, D = g->head_dim, Hkv = g->num_kv_heads;
-  if (n_q_heads % Hkv != 0 || max_q_len > max_context_len) return PA_ERR_INVALID_ARG;
-  if ((int64_t)max_blocks_per_seq * B < max_context_len) return PA_ERR_INVALID_ARG;
   const int G = n_q_heads / Hkv;
   const bool fp8 = g->dtype == PA_FP8;
-  if ((g->dtype != PA_BF16 && !fp8) || B != 16 || (D != 64 && D != 128) || G > 32 || 32 % G != 0)
-    return PA_ERR_UNSUPPORTED;
   if (n_seqs == 0 || n_tokens == 0 || max_q_len == 0) return PA_OK;
   if (!k_pool || !v_pool || !q || !k_new || !v_new || !out || !q_start || !block_tables || !ctx_lens)
     return PA_ERR_INVALID_ARG;
-  const int TQ = kPfRows / G;
-  const int n_tiles = (max_q_len + TQ - 1) / TQ;
-  const int64_t tiles = (int64_t)n_seqs * Hkv * n_tiles;
-  const int max_pairs = ((max_context_len + 15) / 16 + 1) / 2;
-  int S = n_splits == 0 ? auto_splits(tiles, max_pairs) : n_splits;
-  if (S > 1 && (!workspace || workspace_bytes < split_bytes(n_tokens, n_q_heads, D, S))) {
+  PfPlan plan = pf_plan(n_seqs, Hkv, G, max_q_len, max_context_len, n_splits, fp8);
+  if (plan.S > 1 && (!workspace || workspace_bytes < split_bytes(n_tokens, n_q_heads, D, plan.S))) {
     if (n_splits != 0) return PA_ERR_WORKSPACE;
-    S = 1;  // automatic choice without room for partials: no split
+    plan = pf_plan_unsplit(G, max_q_len);  // automatic choice without room for partials
   }
+  const int S = plan.S;
   hipStream_t st = (hipStream_t)stream;
   const int64_t tile_b = fp8 ? (int64_t)B * D + B : (int64_t)B * D * 2;  // bytes per pool tile
   const int64_t layer_off = (int64_t)layer * g->num_blocks * Hkv * tile_b;   // bytes
@@ -623,26 +948,47 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
     sp.part_ml = sp.part_o + (int64_t)n_tokens * n_q_heads * S * D;
   }
   {
-    ProfScope ps("prefill_attention", st);
-    const int64_t items = tiles * S;
-    const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
-    if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    ProfScope ps(plan.short_path ? "prefill_short" : "prefill_attention", st);
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
     const float qk_scale = scale * kLog2e;
-    const dim3 grid((unsigned)wgs);
-    const size_t lds = 3 * (size_t)(D == 64 ? PfCfg<64>::PAIR_BYTES : PfCfg<128>::PAIR_BYTES);
     const char* kp = static_cast<const char*>(k_pool);
     const char* vp = static_cast<const char*>(v_pool);
     const uint16_t* qq = static_cast<const uint16_t*>(q);
     uint16_t* oo = static_cast<uint16_t*>(out);
+    if (plan.short_path) {
+      const int64_t waves = (int64_t)n_seqs * Hkv * S;
+      if (waves > INT32_MAX) return PA_ERR_UNSUPPORTED;
+      const dim3 grid((unsigned)waves);
+      const uint16_t* kp16 = reinterpret_cast<const uint16_t*>(kp);
+      const uint16_t* vp16 = reinterpret_cast<const uint16_t*>(vp);
+      const int64_t off = layer_off / 2;  // elements
+#define PA_PF_SHORT(DD, CC)                                                                   \
+  hipLaunchKernelGGL((prefill_short_kernel<DD, CC>), grid, dim3(64), 0, st, kp16, vp16, qq, oo, \
+                     cb, block_tables, off, g->num_blocks, Hkv, n_q_heads, G, max_blocks_per_seq, \
+                     plan.bps, qk_scale, sp)
+      if (D == 64) {
+        if (plan.CT == 1) PA_PF_SHORT(64, 1);
+        else PA_PF_SHORT(64, 2);
+      } else {
+        if (plan.CT == 1) PA_PF_SHORT(128, 1);
+        else PA_PF_SHORT(128, 2);
+      }
+#undef PA_PF_SHORT
+    } else {
+      const int64_t items = (int64_t)n_seqs * Hkv * plan.n_tiles * S;
+      const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
+      if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+      const dim3 grid((unsigned)wgs);
+      const size_t lds = 3 * (size_t)(D == 64 ? PfCfg<64>::PAIR_BYTES : PfCfg<128>::PAIR_BYTES);
 #define PA_PF_LAUNCH(DD, F8)                                                                  \
   launch_prefill_g<DD, F8>(G, grid, lds, st, kp, vp, qq, oo, cb, block_tables, layer_off,     \
-                           g->num_blocks, Hkv, n_q_heads, max_blocks_per_seq, n_tiles, qk_scale, \
-                           sp)
-    const bool ok = D == 64 ? (fp8 ? PA_PF_LAUNCH(64, true) : PA_PF_LAUNCH(64, false))
-                            : (fp8 ? PA_PF_LAUNCH(128, true) : PA_PF_LAUNCH(128, false));
+                           g->num_blocks, Hkv, n_q_heads, max_blocks_per_seq, plan.n_tiles,   \
+                           qk_scale, sp)
+      const bool ok = D == 64 ? (fp8 ? PA_PF_LAUNCH(64, true) : PA_PF_LAUNCH(64, false))
+                              : (fp8 ? PA_PF_LAUNCH(128, true) : PA_PF_LAUNCH(128, false));
 #undef PA_PF_LAUNCH
-    if (!ok) return PA_ERR_UNSUPPORTED;
+      if (!ok) return PA_ERR_UNSUPPORTED;
+    }
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   if (S > 1) {

@@ -87,3 +87,25 @@ def test_workspace_sizing():
     assert pk.decode_workspace_bytes(g1, 8, 12, 1024, kernel="generic") >= 0
     with pytest.raises(Exception):
         pk.decode_workspace_bytes(g1, 8, 12, 1024, kernel="bogus")
+
+
+def test_prefill_workspace_sizing():
+    """The prefill launch plan as the workspace query reports it (host only)."""
+    import paged_kv_cache_83_amd as pk
+    g = pk.Geometry(80, 8, 128, 16, 32768, "bf16")
+    row = 64 * 130 * 4                                  # one token: 64 heads x (128 + 2) floats
+    # 16 sequences x 4 draft tokens over 32,764 cached: short chunks (8 x 4 = 32 rows
+    # per KV head), 128 waves before splitting -> 8 splits of 256 blocks
+    assert pk.prefill_workspace_bytes(g, 16, 64, 64, 4, 32768) == 8 * 64 * row
+    assert pk.prefill_workspace_bytes(g, 16, 64, 64, 4, 32768, 3) == 3 * 64 * row
+    # one sequence, short history: 63 blocks in splits of at least 16 -> 4
+    assert pk.prefill_workspace_bytes(g, 1, 4, 64, 4, 1000) == 4 * 4 * row
+    # long chunks (8 x 33 > 32 rows): 128-row tiles, at most 4 automatic splits
+    assert pk.prefill_workspace_bytes(g, 16, 16 * 2048, 64, 2048, 4096) == 0
+    assert pk.prefill_workspace_bytes(g, 1, 33, 64, 33, 32768) == 4 * 33 * row
+    # explicit counts are honoured; 1 needs nothing; out of range and bad shapes give 0
+    assert pk.prefill_workspace_bytes(g, 16, 64, 64, 4, 32768, 1) == 0
+    assert pk.prefill_workspace_bytes(g, 16, 64, 64, 4, 32768, 64) == 64 * 64 * row
+    assert pk.prefill_workspace_bytes(g, 16, 64, 64, 4, 32768, 65) == 0
+    assert pk.prefill_workspace_bytes(g, 16, 64, 60, 4, 32768) == 0       # 60 heads over 8
+    assert pk.prefill_workspace_bytes(g, 16, 64, 64, 5, 4) == 0           # chunk past the bound

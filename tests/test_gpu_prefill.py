@@ -79,6 +79,13 @@ def run_prefill(b, layer=0, tables=None, kp=None, vp=None, splits=0, ws_bytes=No
     return to_host(out, "bf16"), to_host(K, "bf16"), to_host(V, "bf16")
 
 
+def ws_bytes_for(b, splits):
+    geom = pk.Geometry(b["L"], b["Hkv"], b["d"], b["B"], b["N"], "bf16")
+    max_ctx = int(max(int(c) + int(ql) for c, ql in zip(b["ctx"], b["qlens"])))
+    return pk.prefill_workspace_bytes(geom, len(b["qlens"]), int(sum(b["qlens"])), b["Hq"],
+                                      int(max(b["qlens"])), max_ctx, splits)
+
+
 def oracle_prefill(b, layer=0):
     return opf.paged_prefill(b["q"], b["kn"], b["vn"], b["kp"], b["vp"], layer, b["tables"],
                              b["q_start"], b["ctx"], b["B"], "bf16")
@@ -96,8 +103,22 @@ CASES = [
     ("with_empty_chunk", 16, 2, 128, [12, 40, 0], [5, 0, 3]),
 ]
 
+# Short chunks (query heads per KV head x longest chunk <= 32): one wave per
+# (chunk, KV head, split) holds all rows. Histories from empty to several
+# thousand tokens; chunks that start inside a block, cross one, end on one.
+SHORT_CASES = [
+    ("verify_g8_q4", 64, 8, 128, [700, 1200, 3, 0, 30], [4, 4, 4, 4, 4]),
+    ("verify_g8_q2_one_tile", 16, 2, 128, [500, 31, 1000], [2, 1, 2]),
+    ("verify_g4_q8_d64", 16, 4, 64, [1000, 257, 17], [8, 5, 8]),
+    ("verify_g16_q2_d64_long", 32, 2, 64, [4100, 100], [2, 1]),
+    ("verify_mha_q32", 4, 4, 128, [300, 0, 16], [32, 7, 16]),
+    ("verify_g8_with_empty", 16, 2, 128, [12, 40, 0], [2, 0, 3]),
+    ("verify_g2_q16_long", 8, 4, 128, [5000, 2047], [16, 9]),
+    ("verify_g8_q4_8k", 16, 2, 128, [8188, 77], [4, 3]),      # 2 splits: 256 blocks each
+]
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+
+@pytest.mark.parametrize("case", CASES + SHORT_CASES, ids=[c[0] for c in CASES + SHORT_CASES])
 def test_prefill_parity(case):
     need_gpu()
     name, Hq, Hkv, d, ctx, qlens = case
@@ -113,7 +134,7 @@ def test_prefill_parity(case):
 
 
 @pytest.mark.parametrize("splits", [2, 4, 16])
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("case", CASES + SHORT_CASES, ids=[c[0] for c in CASES + SHORT_CASES])
 def test_prefill_split_parity(case, splits):
     """The visible keys of every tile cut into `splits` ranges whose partials are
     merged by a second kernel: same pools, outputs within tolerance. Short
@@ -122,9 +143,8 @@ def test_prefill_split_parity(case, splits):
     name, Hq, Hkv, d, ctx, qlens = case
     print_case(test="prefill_split_parity", case=name, splits=splits)
     b = make_prefill_batch(Hq, Hkv, d, ctx, qlens, seed=zlib.crc32(name.encode()) % 10000)
-    geom = pk.Geometry(b["L"], b["Hkv"], b["d"], b["B"], b["N"], "bf16")
     n_tok = int(sum(qlens))
-    ws = pk.prefill_workspace_bytes(geom, n_tok, Hq, splits)
+    ws = ws_bytes_for(b, splits)
     assert ws == splits * n_tok * Hq * (d + 2) * 4
     out, K, V = run_prefill(b, splits=splits, ws_bytes=ws)
     ek, ev, expect = oracle_prefill(b)
@@ -143,9 +163,8 @@ def test_prefill_split_workspace_rules():
     print_case(test="prefill_split_workspace")
     Hq, Hkv, d = 16, 2, 128
     b = make_prefill_batch(Hq, Hkv, d, [700, 1200], [20, 9], seed=61)
-    geom = pk.Geometry(b["L"], b["Hkv"], b["d"], b["B"], b["N"], "bf16")
     n_tok = 29
-    need4 = pk.prefill_workspace_bytes(geom, n_tok, Hq, 4)
+    need4 = ws_bytes_for(b, 4)
     with pytest.raises(pk.PagedKVError):
         run_prefill(b, splits=4, ws_bytes=need4 - 4)
     with pytest.raises(pk.PagedKVError):
@@ -153,11 +172,12 @@ def test_prefill_split_workspace_rules():
     plain, _, _ = run_prefill(b)
     small, _, _ = run_prefill(b, splits=0, ws_bytes=64)
     assert np.array_equal(plain.view(np.uint8), small.view(np.uint8))
-    auto, _, _ = run_prefill(b, splits=0, ws_bytes=pk.prefill_workspace_bytes(geom, n_tok, Hq, 0))
+    auto, _, _ = run_prefill(b, splits=0, ws_bytes=ws_bytes_for(b, 0))
     _, _, expect = oracle_prefill(b)
     assert max_abs_err(auto, expect, "bf16") <= BF16_TOL
-    assert pk.prefill_workspace_bytes(geom, n_tok, Hq, 1) == 0
-    assert pk.prefill_workspace_bytes(geom, n_tok, Hq, 17) == 0      # out of range
+    assert ws_bytes_for(b, 1) == 0
+    assert ws_bytes_for(b, 64) == 64 * n_tok * Hq * (d + 2) * 4
+    assert ws_bytes_for(b, 65) == 0                                  # out of range
 
 
 @pytest.mark.parametrize("chunk", [16, 48, 100])
@@ -203,6 +223,27 @@ def test_placement_invariance_bitwise():
     out_a, _, _ = run_prefill(a)
     out_b, _, _ = run_prefill(b)
     assert np.array_equal(out_a.view(np.uint8), out_b.view(np.uint8))
+
+
+def test_short_chunk_split_choices():
+    """Short chunks over a long history: the automatic choice splits them when it
+    has room (and says how much it needs), runs them unsplit without room, and an
+    explicit count that would need more than 256 blocks per split goes to the
+    128-row tiles; every choice within tolerance of the oracle."""
+    need_gpu()
+    print_case(test="short_chunk_split_choices")
+    Hq, Hkv, d = 64, 8, 128
+    b = make_prefill_batch(Hq, Hkv, d, [5000, 4500, 61], [4, 3, 4], seed=97)
+    n_tok = 11
+    _, _, expect = oracle_prefill(b)
+    auto_ws = ws_bytes_for(b, 0)
+    assert auto_ws > 0 and auto_ws % (n_tok * Hq * (d + 2) * 4) == 0
+    for splits, ws in ((0, auto_ws), (0, None), (0, 64), (1, None), (2, ws_bytes_for(b, 2)),
+                       (64, ws_bytes_for(b, 64))):
+        out, _, _ = run_prefill(b, splits=splits, ws_bytes=ws)
+        assert np.isfinite(olayout.widen(out, "bf16")).all()
+        err = max_abs_err(out, expect, "bf16")
+        assert err <= BF16_TOL, (splits, ws, err)
 
 
 def test_prefill_bad_arguments():

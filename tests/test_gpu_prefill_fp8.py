@@ -67,10 +67,11 @@ def run_fp8_prefill(b, splits=1, dtype="fp8", kp=None, vp=None):
     out = torch.full_like(q, float("nan"))
     n_tok = q.shape[0]
     ws = None
-    if splits > 1:
-        ws = torch.full((pk.prefill_workspace_bytes(geom, n_tok, b["Hq"], splits) // 4,),
-                        float("nan"), device="cuda")
     max_ctx = int(max(int(c) + int(ql) for c, ql in zip(b["ctx"], b["qlens"])))
+    if splits > 1:
+        ws = torch.full((pk.prefill_workspace_bytes(geom, len(b["qlens"]), n_tok, b["Hq"],
+                                                    int(max(b["qlens"])), max_ctx, splits) // 4,),
+                        float("nan"), device="cuda")
     pk.prefill(geom, K, V, 0, q, to_dev(b["kn"], "bf16"), to_dev(b["vn"], "bf16"), out,
                torch.from_numpy(b["q_start"]).cuda(),
                torch.from_numpy(padded_tables(tabs, max(len(t) for t in tabs))).cuda(),
