@@ -80,6 +80,13 @@ struct PfSplit {
 // rescaled to a new reference.
 constexpr float kLazyLog2 = 8.0f;
 
+// Vector ALU instructions placed after each QK^T product of the next pair in a
+// steady step (the softmax of the current pair is spread over them).
+#ifndef PA_PF_VALU_PER_MFMA
+#define PA_PF_VALU_PER_MFMA 8
+#endif
+constexpr int kPfValuPerMfma = PA_PF_VALU_PER_MFMA;
+
 // This wave's LDS accesses have completed; then synchronise the work group
 // (no wait for global loads still in flight into registers).
 __device__ __forceinline__ void lds_sync() {
@@ -176,6 +183,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     for (int dt = 0; dt < DT; ++dt) acc[ct][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-INFINITY, -INFINITY};
   float l_run[2] = {0.f, 0.f};
+  float ms[2] = {0.f, 0.f};                // -m_run * c (0 while m_run = -inf)
+  float thr[2] = {-INFINITY, -INFINITY};   // m_run + kLazyLog2 / c
+  const float lazy_gap = kLazyLog2 / qk_scale;
 
   const int32_t* trow = tables + (int64_t)i * max_blocks;
   const char* kl = kpool + layer_off;  // layer_off in bytes
@@ -304,13 +314,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       }
   };
 
-  // Softmax update and PV of pair pj from its scores and its V image.
-  auto finish = [&](int pj, const u32x4 (&vin)[DT], const f32x4 (&sc)[2][2]) {
+  // Softmax update and PV of pair pj from its scores and its V image. EDGE:
+  // the pair may hold keys above some row's position or past the valid data
+  // (else it is known to hold neither, and the products of the next pair,
+  // issued just before, are interleaved with the softmax).
+  //
+  // Scores stay unscaled through the mask and the maximum (the scale is
+  // positive); the scale enters in the exponent: p = 2^(s * c + ms), ms = -m * c
+  // for the row's reference maximum m. The reference moves only when a score
+  // passes it by more than kLazyLog2 (log2 units), i.e. exceeds thr = m +
+  // kLazyLog2 / c: until then p stays below 2^kLazyLog2, which bf16 and the fp32
+  // sums hold as exactly as p <= 1, and the accumulators need no rescaling. The
+  // test is per lane (its 8 scores against thr); only when some lane of the wave
+  // passes is the exact row maximum formed across the row's four lane groups,
+  // the references of the rows that passed moved to it, their accumulators
+  // rescaled and the probabilities recomputed. The first pair always moves it
+  // (m = -inf; key 0 is visible to every row). A row may see no key of a split
+  // at all (a later split than its position): m stays -inf, ms 0, p 0.
+  auto finish = [&](int pj, const u32x4 (&vin)[DT], const f32x4 (&sc)[2][2], auto edge) {
+    constexpr bool EDGE = decltype(edge)::value;
     u32x4 vf[DT];
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vf[dt] = vin[dt];
     const int key0 = 32 * pj + 8 * gq;  // this lane's keys: key0 + 4*t + e (scores), key0 + e (V)
-    if (32 * pj + 32 > kmax) {          // slots past the valid data: V zeroed (0 * NaN guard)
+    if (EDGE && 32 * pj + 32 > kmax) {  // slots past the valid data: V zeroed (0 * NaN guard)
       u32x4 keep;
 #pragma unroll
       for (int wv = 0; wv < 4; ++wv) {
@@ -320,63 +347,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) vf[dt] &= keep;
     }
-    // Scores stay unscaled through the mask and the maximum (the scale is
-    // positive); the scale enters in the exponent: p = 2^(s * c - m * c).
-    const bool diag = 32 * pj + 31 > qmin;  // uniform: some key of the pair is above some row
-    float m_new[2];
+    const bool diag = EDGE && 32 * pj + 31 > qmin;  // uniform: some key of the pair is above some row
+    float sv[2][8], lmax[2], psum[2];
     uint32_t pw[2][4];
-    float psum[2];
+    bool pass = false;
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
-      float sv[8];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sv[4 * t + e] = sc[ct][t][e];
+        for (int e = 0; e < 4; ++e) sv[ct][4 * t + e] = sc[ct][t][e];
       if (diag) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (key0 + 4 * t + e > qpos[ct]) sv[4 * t + e] = -INFINITY;
+            if (key0 + 4 * t + e > qpos[ct]) sv[ct][4 * t + e] = -INFINITY;
       }
-      float mb = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      mb = max_over_groups(mb);
-      // The reference maximum of a row moves only when the true maximum passes
-      // it by more than kLazyLog2 (in log2 units): until then p stays below
-      // 2^kLazyLog2, which bf16 and the fp32 sums hold as exactly as p <= 1,
-      // and the accumulators need no rescaling. The first pair always sets it
-      // (m_run = -inf; key 0 is visible to every row, so mb is finite).
-      // A row may see no key of a split at all (a later split than its
-      // position): its maximum stays -inf and its probabilities 0.
-      const float m_cand = fmaxf(m_run[ct], mb);
-      m_new[ct] = ((m_cand - m_run[ct]) * qk_scale > kLazyLog2) ? m_cand : m_run[ct];
-      const float ms = (m_new[ct] == -INFINITY) ? 0.f : -m_new[ct] * qk_scale;
-      psum[ct] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk_scale, ms));
-        const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], qk_scale, ms));
-        psum[ct] += pa + pb;
-        pw[ct][e >> 1] = pack_bf16x2(pa, pb);
-      }
+      lmax[ct] = fmaxf(fmaxf(fmaxf(sv[ct][0], sv[ct][1]), fmaxf(sv[ct][2], sv[ct][3])),
+                       fmaxf(fmaxf(sv[ct][4], sv[ct][5]), fmaxf(sv[ct][6], sv[ct][7])));
+      pass = pass || lmax[ct] > thr[ct];
     }
-    if (__any(m_new[0] != m_run[0] || m_new[1] != m_run[1])) {
+    auto probs = [&]() {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const float alpha = (m_new[ct] == m_run[ct])
-                                ? 1.f
-                                : __builtin_amdgcn_exp2f((m_run[ct] - m_new[ct]) * qk_scale);
+        psum[ct] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[ct][e], qk_scale, ms[ct]));
+          const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[ct][e + 1], qk_scale, ms[ct]));
+          psum[ct] += pa + pb;
+          pw[ct][e >> 1] = pack_bf16x2(pa, pb);
+        }
+      }
+    };
+    probs();
+    if constexpr (!EDGE) {
+      // One scheduling region holds the K fragment reads and QK^T products of
+      // the next pair and this softmax: spread the vector work between the
+      // products, so the matrix core and the vector ALU work at the same time
+      // within the wave (by default the products would all issue first). The
+      // empty asm keeps the probabilities in this region (the compiler would
+      // otherwise sink them past the reference test, next to their use).
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        asm volatile("" : "+v"(psum[ct]), "+v"(pw[ct][0]), "+v"(pw[ct][1]), "+v"(pw[ct][2]),
+                     "+v"(pw[ct][3]));
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KC, 0);  // LDS reads
+#pragma unroll
+      for (int k = 0; k < 4 * KC; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kPfValuPerMfma, 0);  // vector ALU
+      }
+    }
+    if (__any(pass)) {  // uniform, rare
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float mb = max_over_groups(lmax[ct]);
+        const float m_new = mb > thr[ct] ? mb : m_run[ct];
+        const float alpha =
+            m_new == m_run[ct] ? 1.f : __builtin_amdgcn_exp2f((m_run[ct] - m_new) * qk_scale);
         l_run[ct] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[ct][dt] = acc[ct][dt] * alpha;
+        m_run[ct] = m_new;
+        ms[ct] = m_new == -INFINITY ? 0.f : -m_new * qk_scale;
+        thr[ct] = m_new + lazy_gap;
       }
+      probs();
     }
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) {
       l_run[ct] += psum[ct];
-      m_run[ct] = m_new[ct];
       const bf16x8 pf =
           __builtin_bit_cast(bf16x8, make_uint4(pw[ct][0], pw[ct][1], pw[ct][2], pw[ct][3]));
 #pragma unroll
@@ -389,34 +431,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // Step pj: loads of pair pj+2 go out; V of pair pj is read; once pair pj+1
   // has landed (every wave waited for its own loads, then the barrier), its
   // QK^T products are issued, and the softmax and PV of pair pj run while the
-  // matrix cores work on them.
+  // matrix cores work on them. Steady steps (edge = false): the pairs the step
+  // loads exist and pair pj needs no mask, so the step has no branch before its
+  // reference test.
   // b_cur, b_next, b_new: byte offsets of the images of pairs pj, pj+1, pj+2.
   int b_cur = 0, b_next = PAIR, b_new = 2 * PAIR;
   Raw raw;  // FP8: the pair after next, in registers
-  auto step = [&](int pj, const f32x4 (&sc_cur)[2][2], f32x4 (&sc_next)[2][2]) {
+  using edge_t = std::integral_constant<bool, true>;
+  using steady_t = std::integral_constant<bool, false>;
+  auto step = [&](int pj, const f32x4 (&sc_cur)[2][2], f32x4 (&sc_next)[2][2], auto edge) {
+    constexpr bool EDGE = decltype(edge)::value;
     if constexpr (FP8) {
-      if (pj + 2 < pend) stash_raw(raw, b_new);
+      if (!EDGE || pj + 2 < pend) stash_raw(raw, b_new);
     } else {
-      if (pj + 2 < pend) issue(pj + 2, b_new);
+      if (!EDGE || pj + 2 < pend) issue(pj + 2, b_new);
     }
     u32x4 vf[DT];
     const unsigned char* img = pf_smem + b_cur;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       vf[dt] = *reinterpret_cast<const u32x4*>(img + (2 + v_sel) * TILE + dt * 512 + v_off);
-    if (pj + 1 < pend) {
+    if (!EDGE || pj + 1 < pend) {
       if constexpr (FP8)
         lds_sync();  // this wave's stores of pair pj+1 (last step) are done; then all waves'
-      else if (pj + 2 < pend)
+      else if (!EDGE || pj + 2 < pend)
         lds_wait_sync<LOADS>();  // pair pj+1 landed; pair pj+2 may still be in flight
       else
         lds_wait_sync<0>();
       scores(b_next, sc_next);
     }
     if constexpr (FP8) {  // after the K fragments of pair pj+1 are consumed
-      if (pj + 3 < pend) load_raw(pj + 3, raw);
+      if (!EDGE || pj + 3 < pend) load_raw(pj + 3, raw);
     }
-    finish(pj, vf, sc_cur);
+    finish(pj, vf, sc_cur, edge);
     const int b_old = b_cur;
     b_cur = b_next;
     b_next = b_new;
@@ -443,12 +490,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   }
   f32x4 sa[2][2], sb[2][2];
   scores(0, sa);
-  int pj = pbeg;
-  for (; pj + 1 < pend; pj += 2) {  // the range is uniform across the work group
-    step(pj, sa, sb);
-    step(pj + 1, sb, sa);
+  int pj = pbeg;  // the ranges below are uniform across the work group
+  {
+    // pairs wholly at or below the tile's first position whose step needs no
+    // test of the pairs after it (bf16: pair pj+2 exists; FP8: pj+3 as well)
+    const int psteady = min((ctx + t0 + 1) >> 5, pend - (FP8 ? 3 : 2));
+    for (; pj + 1 < psteady; pj += 2) {
+      step(pj, sa, sb, steady_t{});
+      step(pj + 1, sb, sa, steady_t{});
+    }
   }
-  if (pj < pend) step(pj, sa, sb);
+  for (; pj + 1 < pend; pj += 2) {
+    step(pj, sa, sb, edge_t{});
+    step(pj + 1, sb, sa, edge_t{});
+  }
+  if (pj < pend) step(pj, sa, sb, edge_t{});
   }  // pbeg < pend (uniform); an empty split writes m = -inf, l = 0, O = 0
 
   // acc[ct][dt][e] = O^T[d = 16*dt + 4*gq + e][row 16*ct + c]
