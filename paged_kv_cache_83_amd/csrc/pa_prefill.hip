@@ -213,7 +213,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const int tl = woff / TILE;                   // tile of the whole wave
       const int p = (tl & 1) ? p1 : p0;
       const char* base = (tl < 2 ? kg : vg) + p * blk_stride + (woff - tl * TILE);
-      __builtin_amdgcn_global_load_lds(base + lane * 16,
+      // The base is uniform; pinning it to scalar registers lets the load take
+      // it as its scalar base with the lane's 16-byte offset, instead of a
+      // 64-bit vector address computed per load.
+      // (readfirstlane returns a signed int: both halves are widened as
+      // unsigned 32-bit words, so the low word is not sign-extended.)
+      const uint64_t bu = reinterpret_cast<uint64_t>(base);
+      const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32));
+      const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu);
+      const uint64_t bs = ((uint64_t)bhi << 32) | (uint64_t)blo;
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(bs) + lane * 16,
                                        (__attribute__((address_space(3))) void*)(img + woff), 16,
                                        0, 0);
     }
