@@ -1186,7 +1186,7 @@ def run_prefix_reuse(args):
     profiling = [False]
     record = []          # per step: usable lengths, evicted ids, adopted counts
     host_s = [0.0, 0.0]  # admission (including tables and their copy), retirement
-    parts = [0.0] * 5    # match, evict, reserve, build tables, queue table copies
+    parts = [0.0] * 6    # match, evict, reserve, build tables, queue table copies, wait
 
     def step(k):
         """Admit batch k, queue its 80 layers, retire it. No wait for the device:
@@ -1201,7 +1201,9 @@ def run_prefix_reuse(args):
             raise RuntimeError(f"step {k}: cached prefix lost ({usable}); the budget is too small")
         ha = time.perf_counter()
         tabs, lens = bm.build_tables(seqs, maxb)
+        hw0 = time.perf_counter()
         uploaded[buf].synchronize()   # the upload two batches ago has left this pinned set
+        hw1 = time.perf_counter()
         tables_h[buf].numpy()[:] = tabs
         ctx_h[buf].numpy()[:] = np.asarray(usable, np.int32)
         hb = time.perf_counter()
@@ -1209,8 +1211,9 @@ def run_prefix_reuse(args):
         ctx_d[buf].copy_(ctx_h[buf], non_blocking=True)
         uploaded[buf].record(stream)
         h1 = time.perf_counter()
-        parts[3] += hb - ha
+        parts[3] += (hb - ha) - (hw1 - hw0)
         parts[4] += h1 - hb
+        parts[5] += hw1 - hw0  # the host is ahead of the device: not host work
         for layer in range(L):
             prof = profiling[0] and layer % args.prof_every == 0
             if prof:
@@ -1223,7 +1226,7 @@ def run_prefix_reuse(args):
         h2 = time.perf_counter()
         adopted = retire(bm, tree, prompts, seqs, handles)
         h3 = time.perf_counter()
-        host_s[0] += h1 - h0
+        host_s[0] += (h1 - h0) - (hw1 - hw0)
         host_s[1] += h3 - h2
         record.append((list(usable), list(evicted), adopted))
 
@@ -1236,7 +1239,7 @@ def run_prefix_reuse(args):
     gc.collect()
     gc.freeze()
     host_s[:] = [0.0, 0.0]
-    parts[:] = [0.0] * 5
+    parts[:] = [0.0] * 6
     if not args.no_prof:
         pk.Profiler.reset()
         profiling[0] = True
@@ -1390,6 +1393,8 @@ def run_prefix_reuse(args):
                  "admit_parts_us_per_request": {
                      k_: round(v_ / (args.steps * n) * 1e6, 2) for k_, v_ in
                      zip(("match", "evict", "reserve", "build_tables", "queue_copies"), parts_timed)},
+                 "wait_for_free_table_set_us_per_request": round(parts_timed[5] / (args.steps * n) * 1e6,
+                                                                 2),
                  "match_unpin_us_4128_tokens": round(match_us, 2),
                  "evicted_nodes_timed": evicted_timed, "tree": info},
         "batch_latency_ms": round(latency_ms, 3),
