@@ -268,3 +268,28 @@ def test_prefill_bad_arguments():
     with pytest.raises(pk.PagedKVError):                      # 3 query heads per KV head: unsupported
         pk.prefill(geom, K, V, 0, torch.zeros(1, 6, 64, device="cuda", dtype=torch.bfloat16), kn, kn,
                    torch.zeros(1, 6, 64, device="cuda", dtype=torch.bfloat16), q_start, tab, ctx, 1, 1)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
+def test_prefill_random_batches(seed):
+    """Seeded random batches: chunk lengths 0..200 over histories 0..1,500 (tiles
+    whose first position falls anywhere in a pair, walks shorter and longer than
+    the steady-step threshold), random head groupings and split counts."""
+    need_gpu()
+    rng = np.random.default_rng(7000 + seed)
+    Hq, Hkv, d = [(64, 8, 128), (16, 4, 64), (32, 2, 128), (8, 8, 64)][seed]
+    n = int(rng.integers(3, 8))
+    ctx = [int(x) for x in rng.integers(0, 1501, n)]
+    qlens = [int(x) if rng.random() > 0.15 else 0 for x in rng.integers(1, 201, n)]
+    qlens[0] = max(qlens[0], 1)
+    splits = [1, 0, 3, 8][seed]
+    print_case(test="prefill_random_batches", seed=seed, ctx=ctx, qlens=qlens, splits=splits)
+    b = make_prefill_batch(Hq, Hkv, d, ctx, qlens, seed=8100 + seed)
+    out, K, V = run_prefill(b, splits=splits, ws_bytes=ws_bytes_for(b, splits) if splits != 1 else None)
+    ek, ev, expect = oracle_prefill(b)
+    assert np.array_equal(K.view(np.uint8), ek.view(np.uint8)), "K pool"
+    assert np.array_equal(V.view(np.uint8), ev.view(np.uint8)), "V pool"
+    rows = int(sum(qlens))
+    assert np.isfinite(olayout.widen(out[:rows], "bf16")).all()
+    err = max_abs_err(out, expect, "bf16")
+    assert err <= BF16_TOL, (seed, err)

@@ -182,3 +182,26 @@ def test_fp8_equals_bf16_kernel_on_representable_values():
     out8, _, _ = run_fp8_prefill(b, kp=kp8, vp=vp8)
     out16, _, _ = run_fp8_prefill(b, dtype="bf16", kp=kb, vp=vb)
     assert np.array_equal(out8.view(np.uint8), out16.view(np.uint8))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fp8_prefill_random_batches(seed):
+    """Seeded random batches on FP8 pools: chunk lengths 1..200 over histories
+    0..1,500, so the staged walk meets its steady-step threshold at every offset."""
+    need_gpu()
+    rng = np.random.default_rng(7100 + seed)
+    Hq, Hkv, d = [(64, 8, 128), (16, 4, 64)][seed]
+    n = int(rng.integers(3, 7))
+    ctx = [int(x) for x in rng.integers(0, 1501, n)]
+    qlens = [int(x) for x in rng.integers(1, 201, n)]
+    splits = [1, 3][seed]
+    print_case(test="fp8_prefill_random_batches", seed=seed, ctx=ctx, qlens=qlens, splits=splits)
+    b = make_fp8_prefill(Hq, Hkv, d, ctx, qlens, seed=8200 + seed)
+    out, K, V = run_fp8_prefill(b, splits=splits)
+    ek, ev, expect = fp8.paged_prefill(b["q"], b["kn"], b["vn"], b["kp"], b["vp"], 0, b["tables"],
+                                       b["q_start"], b["ctx"], b["B"])
+    assert np.array_equal(K, ek), "K pool"
+    assert np.array_equal(V, ev), "V pool"
+    assert np.isfinite(olayout.widen(out, "bf16")).all()
+    err = rel_err(out, expect)
+    assert err <= 2e-2, (seed, err)
