@@ -76,6 +76,15 @@ struct PfSplit {
   float* part_ml;  // [n_tokens][Hq][n][2]: reference maximum (log2 units), sum
 };
 
+// Pairs of blocks in flight per wave in the short-chunk kernel (bf16 and FP8
+// pools).
+#ifndef PA_SHORT_STAGES
+#define PA_SHORT_STAGES 2
+#endif
+#ifndef PA_FP8_SHORT_STAGES
+#define PA_FP8_SHORT_STAGES 3
+#endif
+
 // Growth of a row's maximum (log2 units) tolerated before the accumulators are
 // rescaled to a new reference.
 constexpr float kLazyLog2 = 8.0f;
@@ -590,15 +599,22 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __res
 // merges. With CT = 2 and d = 128 the wave holds 64 accumulators, 32 query and
 // 128 fragment registers per lane, beyond the 256 of two waves per SIMD: it
 // runs alone on its SIMD, which the launch sizes for (about one wave per SIMD).
-template <int D, int CT>
+//
+// FP8 pools (E4M3 codes with a power-of-two scale per token and head): the
+// pair's codes and scale bytes come in as the FP8 decode kernel loads them
+// (8-byte fragments), the codes are converted to bf16 exactly in registers,
+// each key's K scale multiplies its score (ldexp, exact) and its V scale is
+// folded into its probability in the PV operand, as in the FP8 decode kernel.
+template <int D, int CT, bool FP8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128 ? 1 : PA_MFMA_WPE))) void prefill_short_kernel(
-    const uint16_t* __restrict__ kpool, const uint16_t* __restrict__ vpool,
+    const char* __restrict__ kpool, const char* __restrict__ vpool,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out, ChunkBatch cb,
     const int32_t* __restrict__ tables, int64_t layer_off, int N, int Hkv, int Hq, int G,
     int max_blocks, int bps, float qk_scale, PfSplit sp) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int DT = MfmaCfg<D>::DT;
-  constexpr int NS = MfmaCfg<D>::kStages;
+  constexpr int NS = FP8 ? PA_FP8_SHORT_STAGES : PA_SHORT_STAGES;
+  using Frags = std::conditional_t<FP8, Fp8Frags<D>, PairFrags<D>>;
 
   // KV head fastest, then split: the waves reading one sequence's blocks start together.
   const int w = blockIdx.x;
@@ -658,21 +674,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128
       const int idx = b0 + 64 * k + lane;
       tb[k] = (64 * k < b1 - b0 && idx < b1) ? guard_block(trow[idx], N) : 0;
     }
-    const uint16_t* kl = kpool + layer_off;
-    const uint16_t* vl = vpool + layer_off;
+    const char* kl = kpool + layer_off;  // layer_off in bytes
+    const char* vl = vpool + layer_off;
     // Score row c of each tile holds pair-local key 8*(c>>2) + 4*t + (c&3); the
-    // lane's V^T fragment is block (gq >> 1), dims 16*dt + c, slots 8*(gq&1) .. +8.
+    // lane's V^T fragment is block (gq >> 1), dims 16*dt + c, slots 8*(gq&1) .. +8
+    // (FP8: the lane's 8 keys are those slots, whose scale bytes it loads).
     const int k_sel = c >> 3;
     const int k_off0 = 8 * ((c >> 2) & 1) + (c & 3);
     const int v_sel = gq >> 1;
     const int v_off = 16 * c + 8 * (gq & 1);
     const int span = b1 - b0;
     const int npairs = (span + 1) >> 1;
-    auto issue_at = [&](PairFrags<D>& fr, int pj) {
+    auto issue_at = [&](Frags& fr, int pj) {
       const int off = 2 * pj;
       const int p0 = table_at(tb, off);
       const int p1 = (off + 1 < span) ? table_at(tb, off + 1) : p0;
-      issue_pair<D, true>(fr, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq, -1, nullptr);
+      if constexpr (FP8)
+        fp8_issue_pair<D, true>(fr, reinterpret_cast<const uint8_t*>(kl),
+                                reinterpret_cast<const uint8_t*>(vl), p0, p1, Hkv, g, k_sel, k_off0,
+                                v_sel, v_off, 8 * (gq & 1), gq);
+      else
+        issue_pair<D, true>(fr, reinterpret_cast<const uint16_t*>(kl),
+                            reinterpret_cast<const uint16_t*>(vl), p0, p1, Hkv, g, k_sel, k_off0,
+                            v_sel, v_off, gq, -1, nullptr);
       // Keep the loads ahead of the products of the pair before them: moved
       // below its first product they would start only after that pair's wait.
       __builtin_amdgcn_sched_barrier(0);
@@ -681,8 +705,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128
     // One pair: S^T for every tile, the masked online-softmax update (the scale
     // enters in the exponent, p = 2^(s*c - m*c); the reference maximum moves
     // only when passed by more than kLazyLog2), then O^T += V^T P^T per tile.
-    auto compute = [&](PairFrags<D>& f, int pj) {
+    auto compute = [&](Frags& f, int pj) {
       const int k0 = 16 * (b0 + 2 * pj);  // first key of the pair
+      bf16x8 kb[2][KC];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          if constexpr (FP8) kb[t][kc] = fp8x8_to_bf16(f.k[t][kc]);
+          else kb[t][kc] = __builtin_bit_cast(bf16x8, f.k[t][kc]);
+        }
       f32x4 sc[CT][2];
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct)
@@ -691,19 +723,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128
           sc[ct][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc)
-            sc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, f.k[t][kc]), qf[ct][kc], sc[ct][t], 0, 0, 0);
+            sc[ct][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[t][kc], qf[ct][kc], sc[ct][t],
+                                                                0, 0, 0);
         }
       const int key0 = k0 + 8 * gq;  // the lane's keys: key0 + 4*t + e (scores), key0 + e (V)
       if (k0 + 32 > total) {  // uniform: slots past the data hold anything (0 * NaN guard)
-        u32x4 keep;
+        if constexpr (FP8) {
+          u32x2 keep = {0u, 0u};
 #pragma unroll
-        for (int wv = 0; wv < 4; ++wv) {
-          const int p = key0 + 2 * wv;
-          keep[wv] = (p < total ? 0x0000ffffu : 0u) | (p + 1 < total ? 0xffff0000u : 0u);
+          for (int k = 0; k < 8; ++k)
+            if (key0 + k < total) keep[k >> 2] |= 0xffu << (8 * (k & 3));
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) f.v[dt] &= keep;
+        } else {
+          u32x4 keep;
+#pragma unroll
+          for (int wv = 0; wv < 4; ++wv) {
+            const int p = key0 + 2 * wv;
+            keep[wv] = (p < total ? 0x0000ffffu : 0u) | (p + 1 < total ? 0xffff0000u : 0u);
+          }
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) f.v[dt] &= keep;
         }
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) f.v[dt] &= keep;
       }
       const bool masked = k0 + 32 > ctx + 1;  // uniform: some key past the first row's position
       float m_new[CT], psum[CT];
@@ -714,7 +755,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) sv[4 * t + e] = sc[ct][t][e];
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (FP8)  // the key's K scale, exactly
+              sv[4 * t + e] = __builtin_amdgcn_ldexpf(sc[ct][t][e],
+                                                      byte_of(f.ks, 4 * t + e) - kFp8ScaleBias);
+            else
+              sv[4 * t + e] = sc[ct][t][e];
+          }
         if (masked) {
 #pragma unroll
           for (int t = 0; t < 2; ++t)
@@ -736,7 +783,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128
           const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], qk_scale, ms));
           const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e + 1], qk_scale, ms));
           psum[ct] += pa + pb;
-          pw[ct][e >> 1] = pack_bf16x2(pa, pb);
+          if constexpr (FP8)  // the PV operand carries each key's V scale
+            pw[ct][e >> 1] =
+                pack_bf16x2(__builtin_amdgcn_ldexpf(pa, byte_of(f.vs, e) - kFp8ScaleBias),
+                            __builtin_amdgcn_ldexpf(pb, byte_of(f.vs, e + 1) - kFp8ScaleBias));
+          else
+            pw[ct][e >> 1] = pack_bf16x2(pa, pb);
         }
       }
       bool moved = false;
@@ -753,6 +805,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128
           for (int dt = 0; dt < DT; ++dt) acc[ct][dt] = acc[ct][dt] * alpha;
         }
       }
+      bf16x8 vb[DT];  // the V^T fragments as bf16, shared by the tiles
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        if constexpr (FP8) vb[dt] = fp8x8_to_bf16(f.v[dt]);
+        else vb[dt] = __builtin_bit_cast(bf16x8, f.v[dt]);
+      }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         l_run[ct] += psum[ct];
@@ -761,14 +819,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128
             __builtin_bit_cast(bf16x8, make_uint4(pw[ct][0], pw[ct][1], pw[ct][2], pw[ct][3]));
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f.v[dt]),
-                                                                pf, acc[ct][dt], 0, 0, 0);
+          acc[ct][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[dt], pf, acc[ct][dt], 0, 0, 0);
       }
     };
 
     // NS pairs in flight, as in the decode kernel: the steady loop issues
     // unconditionally, an unrolled tail drains the last pairs.
-    PairFrags<D> f[NS];
+    Frags f[NS];
     int pj = 0;
     if (npairs >= 2 * NS - 1) {
 #pragma unroll
@@ -886,7 +943,7 @@ struct PfPlan {
 PfPlan pf_plan(int n_seqs, int Hkv, int G, int max_q_len, int max_ctx, int n_splits, bool fp8) {
   PfPlan p{};
   const int64_t maxb = ((int64_t)max_ctx + 15) / 16;
-  if (!fp8 && (int64_t)G * max_q_len <= 32 && maxb > 0) {
+  if ((int64_t)G * max_q_len <= 32 && maxb > 0) {
     int64_t S, bps;
     if (n_splits > 0) {
       S = n_splits;
@@ -1024,20 +1081,19 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
       const int64_t waves = (int64_t)n_seqs * Hkv * S;
       if (waves > INT32_MAX) return PA_ERR_UNSUPPORTED;
       const dim3 grid((unsigned)waves);
-      const uint16_t* kp16 = reinterpret_cast<const uint16_t*>(kp);
-      const uint16_t* vp16 = reinterpret_cast<const uint16_t*>(vp);
-      const int64_t off = layer_off / 2;  // elements
-#define PA_PF_SHORT(DD, CC)                                                                   \
-  hipLaunchKernelGGL((prefill_short_kernel<DD, CC>), grid, dim3(64), 0, st, kp16, vp16, qq, oo, \
-                     cb, block_tables, off, g->num_blocks, Hkv, n_q_heads, G, max_blocks_per_seq, \
-                     plan.bps, qk_scale, sp)
-      if (D == 64) {
-        if (plan.CT == 1) PA_PF_SHORT(64, 1);
-        else PA_PF_SHORT(64, 2);
+#define PA_PF_SHORT(DD, CC, F8)                                                                  \
+  hipLaunchKernelGGL((prefill_short_kernel<DD, CC, F8>), grid, dim3(64), 0, st, kp, vp, qq, oo,  \
+                     cb, block_tables, layer_off, g->num_blocks, Hkv, n_q_heads, G,              \
+                     max_blocks_per_seq, plan.bps, qk_scale, sp)
+#define PA_PF_SHORT_D(DD, F8)          \
+  if (plan.CT == 1) PA_PF_SHORT(DD, 1, F8); \
+  else PA_PF_SHORT(DD, 2, F8);
+      if (fp8) {
+        if (D == 64) { PA_PF_SHORT_D(64, true) } else { PA_PF_SHORT_D(128, true) }
       } else {
-        if (plan.CT == 1) PA_PF_SHORT(128, 1);
-        else PA_PF_SHORT(128, 2);
+        if (D == 64) { PA_PF_SHORT_D(64, false) } else { PA_PF_SHORT_D(128, false) }
       }
+#undef PA_PF_SHORT_D
 #undef PA_PF_SHORT
     } else {
       const int64_t items = (int64_t)n_seqs * Hkv * plan.n_tiles * S;

@@ -39,6 +39,7 @@ Shapes follow the workloads the pages describe:
 * ``spec_verify`` -- the ``gqa70b_32k`` batch taking 4 new tokens per sequence in
   one multi-query pass (a short chunk over a 32,764-token history: "Chunked
   prefill mechanics" with a chunk of 4), as when draft tokens are checked.
+* ``spec_verify_fp8`` -- ``spec_verify`` on one-byte E4M3 pools.
 
 Seeds: workload k (1-based, in the order above) uses master seed 8300 + k.
 """
@@ -167,6 +168,12 @@ CONFIGS = [
         head_dim=128, block_size=16, dtype="bf16", num_blocks=32768, num_seqs=16,
         length_kind="verify", length_min=32768, length_max=32768, chunk_len=4,
         notes="the gqa70b_32k batch checking 4 new tokens per sequence in one pass (32,764 cached)",
+    ),
+    Workload(
+        name="spec_verify_fp8", index=12, num_layers=80, num_q_heads=64, num_kv_heads=8,
+        head_dim=128, block_size=16, dtype="fp8", num_blocks=32768, num_seqs=16,
+        length_kind="verify", length_min=32768, length_max=32768, chunk_len=4,
+        notes="spec_verify on one-byte E4M3 pools",
     ),
 ]
 

@@ -68,10 +68,10 @@ def run_fp8_prefill(b, splits=1, dtype="fp8", kp=None, vp=None):
     n_tok = q.shape[0]
     ws = None
     max_ctx = int(max(int(c) + int(ql) for c, ql in zip(b["ctx"], b["qlens"])))
-    if splits > 1:
-        ws = torch.full((pk.prefill_workspace_bytes(geom, len(b["qlens"]), n_tok, b["Hq"],
-                                                    int(max(b["qlens"])), max_ctx, splits) // 4,),
-                        float("nan"), device="cuda")
+    if splits != 1:  # 0: the automatic choice, given the workspace it asks for
+        need = pk.prefill_workspace_bytes(geom, len(b["qlens"]), n_tok, b["Hq"],
+                                          int(max(b["qlens"])), max_ctx, splits)
+        ws = torch.full((max(1, need // 4),), float("nan"), device="cuda")
     pk.prefill(geom, K, V, 0, q, to_dev(b["kn"], "bf16"), to_dev(b["vn"], "bf16"), out,
                torch.from_numpy(b["q_start"]).cuda(),
                torch.from_numpy(padded_tables(tabs, max(len(t) for t in tabs))).cuda(),
@@ -96,7 +96,20 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+# Short chunks (query heads per KV head x longest chunk <= 32): the one-wave
+# kernel on FP8 pools; splits 0 = the automatic choice with its workspace.
+SHORT_CASES = [
+    ("verify_g8_q4", 64, 8, 128, [700, 1200, 3, 0, 30], [4, 4, 4, 4, 4], 1),
+    ("verify_g8_q4_split8", 64, 8, 128, [700, 1200, 3, 0, 30], [4, 4, 4, 4, 4], 8),
+    ("verify_g8_q2_one_tile", 16, 2, 128, [500, 31, 1000], [2, 1, 2], 1),
+    ("verify_g4_q8_d64_split3", 16, 4, 64, [1000, 257, 17], [8, 5, 8], 3),
+    ("verify_g16_q2_d64_long_auto", 32, 2, 64, [4100, 100], [2, 1], 0),
+    ("verify_mha_q32", 4, 4, 128, [300, 0, 16], [32, 7, 16], 1),
+    ("verify_g8_with_empty_auto", 16, 2, 128, [12, 40, 0], [2, 0, 3], 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES + SHORT_CASES, ids=[c[0] for c in CASES + SHORT_CASES])
 def test_fp8_prefill_parity(case):
     need_gpu()
     name, Hq, Hkv, d, ctx, qlens, splits = case
@@ -149,13 +162,16 @@ def test_fp8_chunks_reproduce_monolithic_bitwise(chunk):
     assert np.array_equal(K.cpu().numpy(), Km) and np.array_equal(V.cpu().numpy(), Vm)
 
 
-def test_fp8_equals_bf16_kernel_on_representable_values():
+@pytest.mark.parametrize("ctx,qlens", [([100, 0, 33], [40, 70, 1]), ([300, 7, 64], [4, 3, 4])],
+                         ids=["tiles", "short"])
+def test_fp8_equals_bf16_kernel_on_representable_values(ctx, qlens):
     """History and chunk rows that E4M3 x 2^e represents exactly: the FP8 pools and
-    bf16 pools holding the same values give the same output bits."""
+    bf16 pools holding the same values give the same output bits (128-row tiles:
+    both stage the same bf16 image; short chunks: the scales are powers of two
+    applied to exact products and sums)."""
     need_gpu()
-    print_case(test="fp8_prefill_vs_bf16")
+    print_case(test="fp8_prefill_vs_bf16", ctx=ctx, qlens=qlens)
     Hq, Hkv, d, B = 16, 2, 128, 16
-    ctx, qlens = [100, 0, 33], [40, 70, 1]
     b = make_fp8_prefill(Hq, Hkv, d, ctx, qlens, seed=77)
     N = b["N"]
     rng = np.random.default_rng(78)
