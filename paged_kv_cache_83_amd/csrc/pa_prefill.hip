@@ -82,7 +82,7 @@ struct PfSplit {
 #define PA_SHORT_STAGES 2
 #endif
 #ifndef PA_FP8_SHORT_STAGES
-#define PA_FP8_SHORT_STAGES 3
+#define PA_FP8_SHORT_STAGES 2
 #endif
 
 // Growth of a row's maximum (log2 units) tolerated before the accumulators are
@@ -596,9 +596,12 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __res
 // probability and zeroed V. Splits cover bps blocks each (even, at most 256: the
 // table entries of a split sit in four registers of the wave); with more than
 // one, each writes its partial result in the layout prefill_combine_kernel
-// merges. With CT = 2 and d = 128 the wave holds 64 accumulators, 32 query and
-// 128 fragment registers per lane, beyond the 256 of two waves per SIMD: it
-// runs alone on its SIMD, which the launch sizes for (about one wave per SIMD).
+// merges. With CT = 2 and d = 128 on bf16 pools the wave holds 64 accumulator,
+// 32 query and 128 fragment registers per lane, beyond the 256 of two waves per
+// SIMD: it runs alone on its SIMD, which the launch sizes for (about one wave
+// per SIMD). FP8 fragments are half as large, so that variant keeps the
+// two-wave budget (with two registers spilled), which measured faster than one
+// wave per SIMD with three pairs in flight.
 //
 // FP8 pools (E4M3 codes with a power-of-two scale per token and head): the
 // pair's codes and scale bytes come in as the FP8 decode kernel loads them
@@ -606,7 +609,7 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __res
 // each key's K scale multiplies its score (ldexp, exact) and its V scale is
 // folded into its probability in the PV operand, as in the FP8 decode kernel.
 template <int D, int CT, bool FP8>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(CT * D > 128 ? 1 : PA_MFMA_WPE))) void prefill_short_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((CT * D > 128 && !FP8) ? 1 : PA_MFMA_WPE))) void prefill_short_kernel(
     const char* __restrict__ kpool, const char* __restrict__ vpool,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out, ChunkBatch cb,
     const int32_t* __restrict__ tables, int64_t layer_off, int N, int Hkv, int Hq, int G,
