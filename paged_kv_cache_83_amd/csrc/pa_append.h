@@ -143,6 +143,28 @@ __global__ __launch_bounds__(256) void append_kv_kernel(T* __restrict__ kpool, T
                           (int64_t)o * W + (d0 % W),
                       kv);
   }
+  if constexpr (sizeof(T) == 2) {
+    // The usual bulk case: the chunk's 16 tokens fill one whole block in order.
+    // Each V row of the tile is then 16 consecutive slots, written as two
+    // 16-byte stores (8 slots each) instead of 16 element stores.
+    bool whole = B == kAppendChunk && nk == kAppendChunk && s_slot[0] >= 0 && s_slot[0] % B == 0;
+#pragma unroll
+    for (int k = 1; k < kAppendChunk; ++k) whole = whole && s_slot[k] == s_slot[0] + k;
+    if (whole) {  // uniform: every thread read the same slots
+      const int64_t p = s_slot[0] / B;
+      T* tile = vpool + layer_off + (p * Hkv + h) * (int64_t)B * D;
+      for (int idx = tid; idx < 2 * D; idx += blockDim.x) {
+        const int d = idx >> 1, half = idx & 1;
+        const T* src = s_v + d * LD + 8 * half;
+        uint32_t w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          w[u] = (uint32_t)src[2 * u] | ((uint32_t)src[2 * u + 1] << 16);
+        *reinterpret_cast<uint4*>(tile + (int64_t)d * B + 8 * half) = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      return;
+    }
+  }
   for (int idx = tid; idx < kAppendChunk * D; idx += blockDim.x) {
     const int k = idx % kAppendChunk, d = idx / kAppendChunk;
     const int64_t sl = s_slot[k];
