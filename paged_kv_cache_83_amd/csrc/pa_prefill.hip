@@ -459,9 +459,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   using steady_t = std::integral_constant<bool, false>;
   auto step = [&](int pj, const f32x4 (&sc_cur)[2][2], f32x4 (&sc_next)[2][2], auto edge) {
     constexpr bool EDGE = decltype(edge)::value;
-    if constexpr (FP8) {
-      if (!EDGE || pj + 2 < pend) stash_raw(raw, b_new);
-    } else {
+    if constexpr (!FP8) {
       if (!EDGE || pj + 2 < pend) issue(pj + 2, b_new);
     }
     u32x4 vf[DT];
@@ -478,7 +476,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         lds_wait_sync<0>();
       scores(b_next, sc_next);
     }
-    if constexpr (FP8) {  // after the K fragments of pair pj+1 are consumed
+    if constexpr (FP8) {
+      // pair pj+2 into the free image (every wave finished reading it before the
+      // last barrier; the next barrier waits for these stores), converted while
+      // the products of pair pj+1 run; then the codes of pair pj+3 are loaded
+      if (!EDGE || pj + 2 < pend) stash_raw(raw, b_new);
       if (!EDGE || pj + 3 < pend) load_raw(pj + 3, raw);
     }
     finish(pj, vf, sc_cur, edge);
