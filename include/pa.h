@@ -53,9 +53,10 @@
  * ---------------------------------------------------------------------------
  * Conventions
  * ---------------------------------------------------------------------------
- * Ownership: the caller allocates and owns every device and host buffer; the
- *   device entry points never allocate device memory. Decode split partials live
- *   in a caller-provided workspace (size from pa_decode_workspace_bytes).
+ * Ownership: the caller allocates and owns every device and host buffer; no
+ *   entry point allocates device or pinned memory. Decode split partials live
+ *   in a caller-provided workspace (size from pa_decode_workspace_bytes); the
+ *   swapper works in caller buffers sized by pa_swapper_buffer_bytes.
  * Streams: `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *   Device entry points only enqueue work and return; results are visible after
  *   the caller synchronises the stream.
@@ -354,7 +355,7 @@ pa_status pa_bm_validate(const pa_bm* bm);
  * migration in flight cannot be forked or released, and an append cannot write
  * into a tail block that is host-resident or in flight. Host-resident entries
  * read -1 in pa_bm_seq_table / pa_bm_build_tables. The manager holds only the
- * frame bookkeeping; the bytes live in the buffer a pa_swapper owns. */
+ * frame bookkeeping; the bytes live in the pinned buffer a pa_swapper moves them into. */
 typedef enum {
   PA_TIER_HBM = 0,         /* resident in the device pool; index = block id           */
   PA_TIER_HOST = 1,        /* in host memory; index = host frame (-1: swapped out by
@@ -404,37 +405,54 @@ pa_status pa_bm_swap_in_finish(pa_bm* bm, int32_t seq, const int32_t* logical, i
 /* Moves blocks between the device pool and a pinned host frame pool in the
  * background, following "KV Cache Management", section "Asynchronous paged
  * swapping" (copy stream, pinned frames, completion callback that retags the
- * table) and its paragraph on the pipelined chunked reload. The swapper owns a page-locked host
- * buffer of num_frames frames (frame f at byte f * frame_bytes, one block in the
- * staging layout of pa_gather_blocks), two device staging buffers of
- * chunk_blocks blocks, and two streams of its own (default priority): one for
- * the gather / scatter kernels and one for the DMA copies, so that packing chunk
- * k+1 overlaps the copy of chunk k. The kernels use a few work-groups only,
- * paced to the host link. Chunks of all migrations alternate between the two
- * staging buffers in issue order; the completion step of each migration
- * (pa_bm_swap_out_finish / pa_bm_swap_in_finish) runs on the HIP runtime's
- * host-function thread when its last copy or kernel has finished.
- * The block manager must outlive the swapper; one swapper per manager at a time. */
+ * table) and its paragraph on the pipelined chunked reload. The caller owns the
+ * memory: a page-locked host buffer of num_frames frames (frame f at byte
+ * f * frame_bytes, one block in the staging layout of pa_gather_blocks) and a
+ * device staging buffer split into two halves of chunk_blocks blocks. The
+ * swapper creates only two streams of its own (default priority), one for the
+ * gather / scatter kernels and one for the DMA copies, so that packing chunk
+ * k+1 overlaps the copy of chunk k, and the events that hand the halves between
+ * them. The kernels use a few work-groups only, paced to the host link. Chunks
+ * of all migrations alternate between the two halves in issue order; the
+ * completion step of each migration (pa_bm_swap_out_finish /
+ * pa_bm_swap_in_finish) runs on the HIP runtime's host-function thread when its
+ * last copy or kernel has finished. The block manager and both buffers must
+ * outlive the swapper; one swapper per manager at a time. */
 typedef struct pa_swapper pa_swapper;
 
 /* Swapper tuning; pass NULL for the defaults. */
 typedef struct {
-  int32_t chunk_blocks; /* blocks per staging buffer (0 = about 64 MiB)                       */
+  int32_t chunk_blocks; /* blocks per staging half (0 = about 64 MiB)                          */
   int32_t move_wgs;     /* work-groups per gather / scatter launch (0 = 512)                  */
   int32_t direct;       /* 1: no staging and no kernels; each block moves as two strided DMA
                            copies (K and V: L rows of one run each, the pool's layer pitch)
                            straight between the pool and its frame, on the DMA stream */
 } pa_swap_opts;
 
-/* k_pool, v_pool: the device pools of geometry g. Attaches a host pool of
- * num_frames frames to bm (see pa_bm_attach_host_pool). Allocates
- * (hipHostMalloc, hipMalloc); PA_ERR_HIP if that fails. */
+/* Buffer sizes a swapper of num_frames frames with these options needs (either
+ * output may be NULL): *host_bytes = num_frames * bytes_per_block of pinned host
+ * memory, *staging_bytes = 2 * chunk_blocks * bytes_per_block of device memory
+ * (0 in direct mode). PA_ERR_INVALID_ARG for bad input. */
+pa_status pa_swapper_buffer_bytes(const pa_geom* g, int32_t num_frames, const pa_swap_opts* opts,
+                                  size_t* host_bytes, size_t* staging_bytes);
+
+/* k_pool, v_pool: the device pools of geometry g. host_frames: page-locked host
+ * memory (hipHostMalloc, or a pinned torch tensor) of host_bytes bytes; staging:
+ * device memory of staging_bytes bytes (may be NULL in direct mode). Attaches a
+ * host pool of num_frames frames to bm (see pa_bm_attach_host_pool). Allocates
+ * no memory. PA_ERR_WORKSPACE if a buffer is smaller than
+ * pa_swapper_buffer_bytes says, PA_ERR_INVALID_ARG if host_frames is not
+ * page-locked, PA_ERR_HIP if a stream or event cannot be created. */
 pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_pool,
-                            int32_t num_frames, const pa_swap_opts* opts, pa_swapper** out);
-/* Waits for every migration (pa_swapper_sync), then frees the buffers and
- * detaches the host pool from the manager when no frame is in use. Entries
- * still host-resident keep their frame bookkeeping but lose their bytes (bring
- * them back first); the pool then stays attached. */
+                            int32_t num_frames, const pa_swap_opts* opts, void* host_frames,
+                            size_t host_bytes, void* staging, size_t staging_bytes,
+                            pa_swapper** out);
+/* Waits for every migration (pa_swapper_sync), detaches the host pool from the
+ * manager and frees the swapper's streams and events; the caller may then free
+ * its two buffers. Refuses, changing nothing, while a frame is in use (an entry
+ * is host-resident or in flight: bring it back or release its sequence first;
+ * PA_ERR_INVALID_ARG) or while a completion step has not run after the wait
+ * (PA_ERR_HIP); the swapper then stays usable. */
 pa_status pa_swapper_destroy(pa_swapper* s);
 /* Move the n listed logical blocks of seq to the host: pa_bm_swap_out_begin
  * now (errors from it are returned and nothing is queued), then per chunk a
@@ -462,9 +480,9 @@ pa_status pa_swapper_fence(pa_swapper* s, void* stream);
 pa_status pa_swapper_sync(pa_swapper* s);
 /* Migrations whose completion step has not run yet; -1 for NULL. */
 int32_t pa_swapper_pending(const pa_swapper* s);
-/* Any of the outputs may be NULL: the pinned frame buffer, the kernel and DMA
- * streams (hipStream_t), bytes per frame, blocks per chunk, and the bytes moved
- * by completed swap-outs and swap-ins. */
+/* Any of the outputs may be NULL: the caller's pinned frame buffer, the kernel
+ * and DMA streams (hipStream_t), bytes per frame, blocks per staging half, and
+ * the bytes moved by completed swap-outs and swap-ins. */
 pa_status pa_swapper_info(const pa_swapper* s, void** host_frames, void** kernel_stream,
                           void** dma_stream, int64_t* frame_bytes, int32_t* chunk_blocks,
                           int64_t* bytes_out, int64_t* bytes_in);
@@ -516,7 +534,11 @@ pa_status pa_radix_insert(pa_radix* r, const int32_t* tokens, int64_t n_tokens,
  * last access (ties: lower id), dropping the tree's reference on its blocks;
  * a parent left without children and pins becomes a candidate in turn. The
  * first min(cap, count) evicted ids go to ids_out in order; *n_evicted (may be
- * NULL) gets the count. Stops early when no candidate is left. */
+ * NULL) gets the count. Stops early when no candidate is left. If the block
+ * manager refuses to drop a leaf's references (PA_ERR_DOUBLE_FREE: a block the
+ * tree indexes was freed behind its back), that leaf is left untouched, still a
+ * candidate, and the call returns the error; leaves evicted before it stay
+ * evicted and are reported as above. */
 pa_status pa_radix_evict(pa_radix* r, int32_t target_free, int64_t* ids_out, int32_t cap,
                          int32_t* n_evicted);
 /* Counts (any output may be NULL): nodes (root excluded), indexed blocks,

@@ -97,7 +97,10 @@ SIGNATURES = {
     "pa_bm_swap_out_finish": (_i32, [_vp, _i32, _pi32, _i32]),
     "pa_bm_swap_in_begin": (_i32, [_vp, _i32, _pi32, _i32, _pi32, _pi32]),
     "pa_bm_swap_in_finish": (_i32, [_vp, _i32, _pi32, _i32]),
-    "pa_swapper_create": (_i32, [_pg, _vp, _vp, _vp, _i32, C.POINTER(pa_swap_opts), C.POINTER(_vp)]),
+    "pa_swapper_buffer_bytes": (_i32, [_pg, _i32, C.POINTER(pa_swap_opts), C.POINTER(_sz),
+                                       C.POINTER(_sz)]),
+    "pa_swapper_create": (_i32, [_pg, _vp, _vp, _vp, _i32, C.POINTER(pa_swap_opts), _vp, _sz, _vp,
+                                 _sz, C.POINTER(_vp)]),
     "pa_swapper_destroy": (_i32, [_vp]),
     "pa_swap_out_async": (_i32, [_vp, _i32, _pi32, _i32, _vp]),
     "pa_swap_in_async": (_i32, [_vp, _i32, _pi32, _i32, _vp]),

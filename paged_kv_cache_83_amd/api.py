@@ -649,10 +649,18 @@ class RadixCache:
         return {i: self.node(i) for i in self.node_ids()}
 
 
+# Buffers of swappers whose destroy call was refused while the object was being
+# collected: the library still addresses them, so they are kept for the process.
+_HELD_BY_LIBRARY = []
+
+
 class Swapper:
     """Asynchronous block migration between the device pool and pinned host frames
-    (pa_swapper_*). Copies run on the swapper's own stream; each migration's
+    (pa_swapper_*). Copies run on the swapper's own streams; each migration's
     completion step retags the block manager's table when its copies are done.
+    The pinned frame buffer and the device staging buffer are allocated here
+    with torch (sizes from pa_swapper_buffer_bytes) and handed to the library,
+    which allocates no memory of its own.
 
     `after` (swap_out / swap_in): the stream whose earlier work the copies must
     follow; None means the current stream of the pools' device, 0 means none."""
@@ -667,8 +675,16 @@ class Swapper:
         h = C.c_void_p()
         g = geom.c()
         opts = _lib.pa_swap_opts(int(chunk_blocks), int(move_wgs), 1 if direct else 0)
+        hb, sb = C.c_size_t(), C.c_size_t()
+        check(self._lib.pa_swapper_buffer_bytes(C.byref(g), int(num_frames), C.byref(opts),
+                                                C.byref(hb), C.byref(sb)), "pa_swapper_buffer_bytes")
+        self._host = torch.empty(max(1, hb.value), dtype=torch.uint8, pin_memory=True)
+        self._staging = (torch.empty(sb.value, dtype=torch.uint8, device=self.device)
+                         if sb.value else None)
         check(self._lib.pa_swapper_create(C.byref(g), bm._h, _ptr(k_pool), _ptr(v_pool),
-                                          int(num_frames), C.byref(opts), C.byref(h)),
+                                          int(num_frames), C.byref(opts), self._host.data_ptr(),
+                                          hb.value, _ptr(self._staging) if sb.value else None,
+                                          sb.value, C.byref(h)),
               "pa_swapper_create")
         self._h = h
         self.num_frames = int(num_frames)
@@ -720,12 +736,16 @@ class Swapper:
         return np.ctypeslib.as_array(buf).reshape(self.num_frames, self.frame_bytes)
 
     def close(self):
+        """Destroy the swapper. Raises (and leaves the swapper usable) while an
+        entry still holds a frame or a migration has not completed."""
         if getattr(self, "_h", None):
-            h, self._h = self._h, None
-            check(self._lib.pa_swapper_destroy(h), "pa_swapper_destroy")
+            check(self._lib.pa_swapper_destroy(self._h), "pa_swapper_destroy")
+            self._h = None
+            self._host = self._staging = None
 
     def __del__(self):
         try:
             self.close()
         except Exception:
-            pass
+            # refused: the library still uses both buffers, so they must outlive it
+            _HELD_BY_LIBRARY.append((getattr(self, "_host", None), getattr(self, "_staging", None)))

@@ -328,10 +328,13 @@ pa_status pa_radix_evict(pa_radix* r, int32_t target_free, int64_t* ids_out, int
   while (!r->lru.empty() && pa_bm_num_free(r->bm) < target_free) {
     auto first = r->lru.begin();
     Node* leaf = r->nodes.at(first->second);
+    // The block manager's call is all or nothing: when it refuses (a block lost
+    // the tree's reference behind its back) the leaf stays as it is, still a
+    // candidate, and the call stops with the leaves evicted so far.
+    rc = pa_bm_free_blocks(r->bm, leaf->blocks.data(), (int32_t)leaf->blocks.size());
+    if (rc != PA_OK) break;
     r->lru.erase(first);
     leaf->in_lru = false;
-    rc = pa_bm_free_blocks(r->bm, leaf->blocks.data(), (int32_t)leaf->blocks.size());
-    if (rc != PA_OK) break;   // a block lost its reference behind the tree's back
     Node* p = leaf->parent;
     pa_radix::erase_kid(p, leaf, block_hash(leaf->tokens.data(), r->B), leaf->tokens[0]);
     r->n_blocks -= (int64_t)leaf->blocks.size();

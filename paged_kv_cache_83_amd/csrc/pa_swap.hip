@@ -54,9 +54,9 @@ struct pa_swapper {
   bool direct = false;      // strided DMA straight from / to the pool, no staging
   int64_t frame_bytes = 0;  // one block: 2 * L runs
   int64_t run_bytes = 0;    // one (layer, K-or-V) run of a block
-  char* host = nullptr;     // pinned, num_frames * frame_bytes
+  char* host = nullptr;     // caller's pinned buffer, num_frames * frame_bytes
   char* host_dev = nullptr; // the same buffer as the device addresses it
-  char* staging[2] = {nullptr, nullptr};  // device, chunk_blocks * frame_bytes each
+  char* staging[2] = {nullptr, nullptr};  // halves of the caller's device staging buffer
   hipStream_t kstream = nullptr;          // gather / scatter kernels
   hipStream_t dstream = nullptr;          // DMA copies over the host link
   hipEvent_t full[2] = {nullptr, nullptr};   // staging[b] written by its producer
@@ -197,12 +197,12 @@ pa_status queue_finish(pa_swapper* s, hipStream_t last, Job* job, bool issued_ok
   return PA_ERR_HIP;
 }
 
+// Frees what the swapper itself created (streams, events, the object); the
+// frame and staging buffers belong to the caller.
 void release(pa_swapper* s) {
   if (s->kstream) (void)hipStreamSynchronize(s->kstream);
   if (s->dstream) (void)hipStreamSynchronize(s->dstream);
-  if (s->host) (void)hipHostFree(s->host);
   for (int b = 0; b < 2; ++b) {
-    if (s->staging[b]) (void)hipFree(s->staging[b]);
     if (s->full[b]) (void)hipEventDestroy(s->full[b]);
     if (s->empty[b]) (void)hipEventDestroy(s->empty[b]);
     if (s->done[b]) (void)hipEventDestroy(s->done[b]);
@@ -213,24 +213,61 @@ void release(pa_swapper* s) {
   delete s;
 }
 
+struct SwapSizes {
+  int64_t run, frame;
+  int32_t chunk_blocks, move_wgs;
+  bool direct;
+  size_t host_bytes, staging_bytes;
+};
+
+pa_status swap_sizes(const pa_geom* g, int32_t num_frames, const pa_swap_opts* opts, SwapSizes* z) {
+  int32_t chunk_blocks = opts ? opts->chunk_blocks : 0;
+  const int32_t move_wgs = opts && opts->move_wgs ? opts->move_wgs : kDefaultMoveWgs;
+  if (!geom_ok(g) || num_frames <= 0 || chunk_blocks < 0 || move_wgs < 0) return PA_ERR_INVALID_ARG;
+  z->run = (int64_t)g->num_kv_heads * tile_bytes(g);
+  z->frame = 2 * (int64_t)g->num_layers * z->run;
+  if (chunk_blocks == 0)  // about 64 MiB per staging half, at least one block
+    chunk_blocks = (int32_t)std::max<int64_t>(1, std::min<int64_t>(4096, (64ll << 20) / z->frame));
+  z->chunk_blocks = chunk_blocks;
+  z->move_wgs = move_wgs;
+  z->direct = opts && opts->direct;
+  z->host_bytes = (size_t)num_frames * (size_t)z->frame;
+  z->staging_bytes = z->direct ? 0 : 2 * (size_t)chunk_blocks * (size_t)z->frame;
+  return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
+pa_status pa_swapper_buffer_bytes(const pa_geom* g, int32_t num_frames, const pa_swap_opts* opts,
+                                  size_t* host_bytes, size_t* staging_bytes) {
+  SwapSizes z;
+  const pa_status st = swap_sizes(g, num_frames, opts, &z);
+  if (st != PA_OK) return st;
+  if (host_bytes) *host_bytes = z.host_bytes;
+  if (staging_bytes) *staging_bytes = z.staging_bytes;
+  return PA_OK;
+}
+
 pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_pool,
-                            int32_t num_frames, const pa_swap_opts* opts, pa_swapper** out) {
+                            int32_t num_frames, const pa_swap_opts* opts, void* host_frames,
+                            size_t host_bytes, void* staging, size_t staging_bytes,
+                            pa_swapper** out) {
   if (!out) return PA_ERR_INVALID_ARG;
   *out = nullptr;
-  int32_t chunk_blocks = opts ? opts->chunk_blocks : 0;
-  const int32_t move_wgs = opts && opts->move_wgs ? opts->move_wgs : kDefaultMoveWgs;
-  const bool direct = opts && opts->direct;
-  if (!geom_ok(g) || !bm || !k_pool || !v_pool || num_frames <= 0 || chunk_blocks < 0 ||
-      move_wgs < 0)
+  SwapSizes z;
+  pa_status st = swap_sizes(g, num_frames, opts, &z);
+  if (st != PA_OK) return st;
+  if (!bm || !k_pool || !v_pool || !host_frames || (!z.direct && !staging))
     return PA_ERR_INVALID_ARG;
-  const int64_t run = (int64_t)g->num_kv_heads * tile_bytes(g);
-  const int64_t frame = 2 * (int64_t)g->num_layers * run;
-  if (chunk_blocks == 0)  // about 64 MiB per staging buffer, at least one block
-    chunk_blocks = (int32_t)std::max<int64_t>(1, std::min<int64_t>(4096, (64ll << 20) / frame));
+  if (host_bytes < z.host_bytes || staging_bytes < z.staging_bytes) return PA_ERR_WORKSPACE;
+  // The frames must be page-locked host memory that the device can address.
+  char* host_dev = nullptr;
+  if (hipHostGetDevicePointer((void**)&host_dev, host_frames, 0) != hipSuccess || !host_dev) {
+    (void)hipGetLastError();
+    return PA_ERR_INVALID_ARG;
+  }
   pa_swapper* s = new (std::nothrow) pa_swapper();
   if (!s) return PA_ERR_INVALID_ARG;
   s->g = *g;
@@ -238,28 +275,30 @@ pa_status pa_swapper_create(const pa_geom* g, pa_bm* bm, void* k_pool, void* v_p
   s->k_pool = k_pool;
   s->v_pool = v_pool;
   s->num_frames = num_frames;
-  s->chunk_blocks = chunk_blocks;
-  s->move_wgs = move_wgs;
-  s->direct = direct;
-  s->frame_bytes = frame;
-  s->run_bytes = run;
+  s->chunk_blocks = z.chunk_blocks;
+  s->move_wgs = z.move_wgs;
+  s->direct = z.direct;
+  s->frame_bytes = z.frame;
+  s->run_bytes = z.run;
+  s->host = (char*)host_frames;
+  s->host_dev = host_dev;
+  if (!z.direct) {
+    s->staging[0] = (char*)staging;
+    s->staging[1] = (char*)staging + (size_t)z.chunk_blocks * (size_t)z.frame;
+  }
   bool ok = hipStreamCreateWithFlags(&s->kstream, hipStreamNonBlocking) == hipSuccess &&
             hipStreamCreateWithFlags(&s->dstream, hipStreamNonBlocking) == hipSuccess &&
-            hipEventCreateWithFlags(&s->after, hipEventDisableTiming) == hipSuccess &&
-            hipHostMalloc((void**)&s->host, (size_t)num_frames * frame, hipHostMallocDefault) ==
-                hipSuccess &&
-            hipHostGetDevicePointer((void**)&s->host_dev, s->host, 0) == hipSuccess;
+            hipEventCreateWithFlags(&s->after, hipEventDisableTiming) == hipSuccess;
   for (int b = 0; ok && b < 2; ++b)
     ok = hipEventCreateWithFlags(&s->full[b], hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&s->empty[b], hipEventDisableTiming) == hipSuccess &&
          hipEventCreateWithFlags(&s->done[b], hipEventDisableTiming) == hipSuccess &&
-         (direct || hipMalloc((void**)&s->staging[b], (size_t)chunk_blocks * frame) == hipSuccess) &&
          hipEventRecord(s->empty[b], s->kstream) == hipSuccess;   // both start drained
   if (!ok) {
     release(s);
     return PA_ERR_HIP;
   }
-  pa_status st = pa_bm_attach_host_pool(bm, num_frames);
+  st = pa_bm_attach_host_pool(bm, num_frames);
   if (st != PA_OK) {
     release(s);
     return st;
@@ -284,8 +323,16 @@ pa_status pa_swapper_sync(pa_swapper* s) {
 
 pa_status pa_swapper_destroy(pa_swapper* s) {
   if (!s) return PA_ERR_INVALID_ARG;
-  pa_status st = pa_swapper_sync(s);
-  (void)pa_bm_detach_host_pool(s->bm);   // kept while entries hold frames
+  const pa_status st = pa_swapper_sync(s);
+  // A completion step still to run would touch the swapper: keep it.
+  if (s->pending.load() > 0) return PA_ERR_HIP;
+  // Frames still held by host-resident or in-flight entries keep the pool
+  // attached and the swapper alive: their bytes are in the caller's buffer and
+  // only this swapper can bring them back.
+  if (pa_bm_host_frames_free(s->bm) >= 0) {   // (unless the caller detached it already)
+    const pa_status dt = pa_bm_detach_host_pool(s->bm);
+    if (dt != PA_OK) return dt;
+  }
   release(s);
   return st;
 }

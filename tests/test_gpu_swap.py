@@ -273,7 +273,9 @@ def test_errors_change_nothing():
 
 def test_swapper_lifetime_and_options():
     """Destroying a swapper detaches its pool when no frame is in use, so a new
-    one (other options) can take over; while an entry holds a frame it stays."""
+    one (other options) can take over; while an entry holds a frame the destroy
+    call is refused, nothing is freed, and a later swap-in still restores the
+    bytes from the caller-owned pinned buffer."""
     need_gpu()
     print_case(test="swap_lifetime")
     su = Setup("bf16", 2, 40, 2, 64, 16, [16 * 12], 834, 16, 0)
@@ -282,11 +284,16 @@ def test_swapper_lifetime_and_options():
     su.sw.close()
     su.sw = pk.Swapper(su.geom, su.bm, su.K, su.V, 16, chunk_blocks=5, move_wgs=3)
     assert su.sw.chunk_blocks == 5
+    assert su.sw._host_ptr == su.sw._host.data_ptr()     # the frames are the caller's buffer
+    assert su.sw._staging.numel() == 2 * 5 * su.sw.frame_bytes
     su.swap_out(s, list(range(12)))
     su.sw.sync()
     su.ref.swap_out_finish(s, list(range(12)))
     with pytest.raises(pk.PagedKVError):
         su.bm.detach_host_pool()                         # 12 frames in use
+    with pytest.raises(pk.PagedKVError):
+        su.sw.close()                                    # refused: the frames hold the only copy
+    assert su.sw.pending() == 0 and su.bm.host_frames_free() == 4
     su.poison_free_blocks()
     su.swap_in(s, list(range(11, -1, -1)))
     su.sw.sync()

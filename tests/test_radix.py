@@ -203,3 +203,59 @@ def test_seq_from_blocks_matches_oracle():
     with pytest.raises(pk.PagedKVError):
         bm.seq_from_blocks([3])
     assert bm.num_free() == 8
+
+
+def _evict_raw(tree, target):
+    """pa_radix_evict through the C interface: (status, evicted ids)."""
+    out = np.zeros(16, np.int64)
+    n = C.c_int32(-1)
+    rc = tree._lib.pa_radix_evict(tree._h, target, out.ctypes.data_as(C.POINTER(C.c_int64)), 16,
+                                  C.byref(n))
+    return rc, out[:n.value].tolist()
+
+
+def test_evict_refused_leaf_is_left_untouched():
+    """A block the tree indexes is freed behind its back: the eviction that
+    reaches its leaf returns PA_ERR_DOUBLE_FREE and leaves that leaf in the tree
+    and among the candidates; leaves evicted before it in the same call stay
+    evicted. Once the reference is restored, the same leaf is evicted."""
+    bm = pk.BlockManager(16, 4)
+    tree = pk.RadixCache(bm)
+    sc.run_request(bm, tree, list(range(8)))            # older dormant leaf, 2 blocks
+    sc.run_request(bm, tree, list(range(100, 108)))     # newer dormant leaf, 2 blocks
+    nodes = tree.nodes()
+    (old_id, old), (new_id, new) = sorted(nodes.items(), key=lambda kv: kv[1][2])
+    assert bm.num_free() == 12
+    # the newer leaf loses one of its references behind the tree
+    bm.free_blocks([new[4][1]])
+    assert bm.num_free() == 13
+    info = tree.info()
+    rc, ids = _evict_raw(tree, 16)
+    assert rc == -3 and ids == [old_id]                 # old evicted, new refused
+    assert tree.nodes() == {new_id: new}
+    assert tree.info() == {"nodes": 1, "blocks": 2, "dormant": 1, "pinned": 0}
+    assert info["dormant"] == 2
+    # nothing changes on a second attempt, and the leaf is still the candidate
+    free = bm.free_list()
+    assert _evict_raw(tree, 16) == (-3, [])
+    assert tree.nodes() == {new_id: new} and bm.free_list() == free
+    # restore the reference (the block is taken off the free list again) and retry
+    taken = bm.alloc(len(free))
+    assert new[4][1] in taken
+    bm.free_blocks([b for b in taken if b != new[4][1]])
+    assert _evict_raw(tree, 16) == (0, [new_id])
+    assert tree.info()["nodes"] == 0 and bm.num_free() == 16
+    bm.validate()
+
+
+def test_evict_refused_head_changes_nothing():
+    """The LRU head itself is refused: nothing is evicted, the tree and the free
+    list are unchanged."""
+    bm = pk.BlockManager(16, 4)
+    tree = pk.RadixCache(bm)
+    sc.run_request(bm, tree, list(range(12)))
+    (nid, node), = tree.nodes().items()
+    bm.free_blocks([node[4][0]])
+    free, info = bm.free_list(), tree.info()
+    assert _evict_raw(tree, 16) == (-3, [])
+    assert tree.nodes() == {nid: node} and tree.info() == info and bm.free_list() == free
