@@ -69,9 +69,15 @@ def free_order(cfg: Workload) -> np.ndarray:
     return rng.permutation(cfg.num_blocks).astype(np.int32)
 
 
-def realloc_shuffle(cfg: Workload, n: int) -> np.ndarray:
-    """A permutation of n items, used to reshuffle free blocks before a swap-in."""
-    rng = _stream(cfg.seed, _REALLOC)
+def realloc_shuffle(cfg: Workload, n: int, round_index: int = 0) -> np.ndarray:
+    """A permutation of n items, used to reshuffle free blocks before a swap-in.
+    Round k > 0 (e.g. the k-th pass of a multi-pass round trip) draws from its
+    own child of the same sub-stream; round 0 is the sub-stream itself."""
+    if round_index == 0:
+        rng = _stream(cfg.seed, _REALLOC)
+    else:
+        child = np.random.SeedSequence(cfg.seed).spawn(8)[_REALLOC].spawn(round_index + 1)[round_index]
+        rng = np.random.default_rng(child)
     return rng.permutation(n).astype(np.int64)
 
 
