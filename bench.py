@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="gqa70b_32k")
     ap.add_argument("--bps", type=int, default=0, help="blocks per split (0 = library default)")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma", "valu"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=48,
                     help="(sequence, layer) pairs the oracle times for the CPU baseline")
@@ -66,6 +66,11 @@ def parse():
                     help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--unfused", action="store_true",
                     help="append the step's tokens with a separate launch before each decode")
+    ap.add_argument("--wg-waves", type=int, default=0,
+                    help="streaming VALU kernel: waves per workgroup (0 = library default)")
+    ap.add_argument("--no-merge", action="store_true",
+                    help="merge decode splits with a separate launch even where the kernel can "
+                         "merge them in its own launch")
     ap.add_argument("--chunk-blocks", type=int, default=-1,
                     help="offload_overlap: blocks per staging chunk (-1 = the workload's, 0 = library default)")
     ap.add_argument("--move-wgs", type=int, default=0,
@@ -293,8 +298,10 @@ def run_decode(args):
     lens = torch.from_numpy(np.ascontiguousarray(lens_np)).to(dev)
     max_ctx = int(lengths.max())
     out = torch.empty((L, n, Hq, d), dtype=io, device=dev)
-    ws_bytes = pk.decode_workspace_bytes(geom, n, Hq, max_ctx, args.bps, args.kernel)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    merge = not args.no_merge
+    ws_bytes = pk.decode_workspace_bytes(geom, n, Hq, max_ctx, args.bps, args.kernel, merge,
+                                         args.wg_waves)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)   # merge counters start at 0
     torch.cuda.synchronize()
 
     # host copies of the sampled sequences' blocks, before any library kernel writes the pool
@@ -319,7 +326,8 @@ def run_decode(args):
     def step():
         steps.decode_step(geom, k_pool, v_pool, q_all, k_new, v_new, slots, tables, lens, max_ctx, out,
                           ws, blocks_per_split=args.bps, kernel=args.kernel, stream=stream,
-                          around_decode=around, fused=not args.unfused)
+                          around_decode=around, fused=not args.unfused, merge=merge,
+                          waves_per_group=args.wg_waves)
 
     for _ in range(args.warmup):
         step()
@@ -363,7 +371,9 @@ def run_decode(args):
         if cnt:
             eb = geom.elem_bytes
             ib = 2 if fp8 else eb                                                # q / out element bytes
-            splits = max(1, ws_bytes // (n * Hq * (d + 2) * 4)) if ws_bytes else 1
+            splits = max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, args.bps, args.kernel,
+                                                      False, args.wg_waves)
+                         // (n * Hq * (d + 2) * 4)) if ws_bytes else 1
             per_launch = (int(lengths.sum()) * 2 * Hkv * (d * eb + (1 if fp8 else 0))  # K and V (+ scales)
                           + n * Hq * d * ib                                      # queries
                           + 4 * int(sum(math.ceil(S / B) for S in lengths))       # block-table entries
@@ -371,9 +381,11 @@ def run_decode(args):
                           + (0 if (args.unfused or fp8) else 4 * n * Hkv * d * eb))  # fused new K/V
             avg_s = tot / cnt * 1e-3
             achieved = per_launch / avg_s / 1e9
-            mfma = cfg.dtype in ("bf16", "fp8") and B == 16 and args.kernel != "generic"
-            kname = ("decode_mfma_fp8_kernel" if fp8 else "decode_mfma_bf16_kernel") if mfma \
-                else "decode_generic_kernel"
+            mfma = cfg.dtype in ("bf16", "fp8") and B == 16 and args.kernel in ("auto", "mfma")
+            valu = not mfma and B == 16 and d in (64, 128) and Hq // Hkv in (1, 2, 4, 8) \
+                and args.kernel in ("auto", "valu")
+            kname = (("decode_mfma_fp8_kernel" if fp8 else "decode_mfma_bf16_kernel") if mfma
+                     else "decode_valu_kernel" if valu else "decode_generic_kernel")
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / PEAK_GBS, 4),
                         "traffic": profiled_traffic(cfg.name) if (mfma and not fp8 and args.bps == 0
@@ -466,6 +478,8 @@ def run_decode(args):
                    "pool_blocks": cfg.num_blocks, "kv_bytes_per_step": kv_bytes_step,
                    "global_batch": n, "seq_len": int(lengths.max()), "parallelism": "none (1 GPU)",
                    "append": "separate launch" if args.unfused else "fused into decode",
+                   "split_merge": "separate launch" if (args.no_merge or "decode_combine" in kernel_ms)
+                   else "inside the decode launch (where splits exist)",
                    "launch": "hip graph replay" if args.graph else "eager"},
         "step_ms": step_ms,
         "tokens_per_s": round(n / (ms_per_step * 1e-3), 2),
@@ -473,6 +487,10 @@ def run_decode(args):
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "kernels": kernel_ms,
+        "kernels_timing": ("hipEvent pairs the library records on the launch stream around every "
+                           f"{args.prof_every}th layer's launches; a pair adds about 2 us to a short "
+                           "kernel, so the rocprofv3 trace under profiles/ is the reference for short "
+                           "kernels (the combine above all)") if kernel_ms else None,
         "parity": parity,
     }
     if cold is not None:

@@ -140,11 +140,25 @@ pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t lay
 /* Decode tuning; pass NULL for the defaults. */
 typedef struct {
   int32_t blocks_per_split; /* logical blocks per split-K work item (0 = choose; rounded up to even) */
-  int32_t kernel;           /* 0 = choose, 1 = generic VALU kernel, 2 = MFMA kernel (bf16, B=16) */
+  int32_t kernel;           /* 0 = choose, 1 = generic kernel (LDS-staged, any B <= 64, d <= 256),
+                               2 = MFMA kernel (bf16 or FP8 pools, B = 16), 3 = streaming VALU
+                               kernel (fp32 or bf16 pools, B = 16, d in {64, 128}, 1, 2 or 4
+                               query heads per KV head, or 8 with d = 128); the choice takes
+                               MFMA, then the streaming VALU kernel, then the generic one */
   int32_t kv_reuse;         /* 0: each K/V block is read once per step -> stream it past the
                                caches (non-temporal loads); 1: blocks are shared by many
                                sequences of the batch (forks, common prefixes) -> ordinary
                                loads so repeats hit in L2 / Infinity Cache (MFMA kernel) */
+  int32_t merge;            /* 0: split partials are merged by a second launch; 1: merged inside
+                               the decode launch by the last split of each (sequence, KV head) to
+                               finish (streaming VALU kernel; other kernels keep the second
+                               launch). The workspace then ends with one int32 counter per
+                               (sequence, KV head), which must be zero before the workspace's
+                               first such call (allocate it zeroed); every call leaves them zero.
+                               Two calls sharing a workspace must not overlap. */
+  int32_t waves_per_group;  /* streaming VALU kernel: waves per workgroup, which split the
+                               workgroup's blocks and merge in LDS (0 = choose; capped at 16 for
+                               one query head per KV head with 256-byte rows, else 8) */
 } pa_decode_opts;
 
 /* Workspace bytes pa_decode needs for these sizes and options (0 when the

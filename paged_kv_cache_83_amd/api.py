@@ -151,17 +151,22 @@ def append_kv(geom: Geometry, k_pool, v_pool, layer: int, k_new, v_new, slot_map
           "pa_append_kv")
 
 
-def _opts(blocks_per_split: int, kernel: int, kv_reuse: bool = False) -> _lib.pa_decode_opts:
-    return _lib.pa_decode_opts(int(blocks_per_split), int(kernel), 1 if kv_reuse else 0)
+def _opts(blocks_per_split: int, kernel: int, kv_reuse: bool = False,
+          merge: bool = False, waves_per_group: int = 0) -> _lib.pa_decode_opts:
+    return _lib.pa_decode_opts(int(blocks_per_split), int(kernel), 1 if kv_reuse else 0,
+                               1 if merge else 0, int(waves_per_group))
 
 
-KERNELS = {"auto": 0, "generic": 1, "mfma": 2}
+KERNELS = {"auto": 0, "generic": 1, "mfma": 2, "valu": 3}
 
 
 def decode_workspace_bytes(geom: Geometry, n_seqs: int, n_q_heads: int, max_context_len: int,
-                           blocks_per_split: int = 0, kernel: str = "auto") -> int:
+                           blocks_per_split: int = 0, kernel: str = "auto",
+                           merge: bool = False, waves_per_group: int = 0) -> int:
+    """Bytes of decode workspace for these sizes and options. With merge=True the
+    workspace must be allocated zeroed (torch.zeros) before its first use."""
     g = geom.c()
-    o = _opts(blocks_per_split, KERNELS[kernel])
+    o = _opts(blocks_per_split, KERNELS[kernel], False, merge, waves_per_group)
     return int(_L().pa_decode_workspace_bytes(C.byref(g), n_seqs, n_q_heads, max_context_len,
                                               C.byref(o)))
 
@@ -192,11 +197,13 @@ def _decode_args(geom: Geometry, k_pool, v_pool, q, out, block_tables, context_l
 
 def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, context_lens,
            max_context_len: int, scale: float = 0.0, workspace=None, blocks_per_split: int = 0,
-           kernel: str = "auto", stream=None, kv_reuse: bool = False):
+           kernel: str = "auto", stream=None, kv_reuse: bool = False, merge: bool = False,
+           waves_per_group: int = 0):
     """out[i, h] = softmax attention of q[i, h] over sequence i's first
     context_lens[i] tokens, read through block_tables[i]. kv_reuse=True when many
-    sequences of the batch share blocks (keeps them cacheable)."""
-    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse)
+    sequences of the batch share blocks (keeps them cacheable). merge=True merges
+    the splits inside the decode launch (the workspace must start zeroed)."""
+    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse, merge, waves_per_group)
     g, n, hq, ws_ptr, ws_bytes = _decode_args(geom, k_pool, v_pool, q, out, block_tables,
                                               context_lens, max_context_len, workspace, o)
     check(_L().pa_decode(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(q), _ptr(out), n, hq,
@@ -209,11 +216,11 @@ def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, con
 def decode_append(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out, block_tables,
                   context_lens, max_context_len: int, scale: float = 0.0, workspace=None,
                   blocks_per_split: int = 0, kernel: str = "auto", stream=None,
-                  kv_reuse: bool = False):
+                  kv_reuse: bool = False, merge: bool = False, waves_per_group: int = 0):
     """Write each sequence's new token (k_new[i], v_new[i]: [n_seqs, H_kv, d]) at
     position context_lens[i] - 1 through its block table, then decode as
     `decode` does, in one launch."""
-    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse)
+    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse, merge, waves_per_group)
     g, n, hq, ws_ptr, ws_bytes = _decode_args(geom, k_pool, v_pool, q, out, block_tables,
                                               context_lens, max_context_len, workspace, o)
     per = geom.num_kv_heads * geom.head_dim

@@ -111,6 +111,120 @@ __device__ __forceinline__ float sum_over_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Loads and stores of split partials. COH = true: agent-scope relaxed atomic
+// accesses, which the compiler emits as coherent (sc1) loads and stores, so a
+// partial written by a work item on one XCD is read correctly by the work item
+// that merges it on another without writing back or invalidating any L2.
+template <bool COH>
+__device__ __forceinline__ float part_ld(const float* p) {
+  if constexpr (COH)
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+template <bool COH>
+__device__ __forceinline__ float4 part_ld4(const float* p) {
+  if constexpr (COH)
+    return make_float4(part_ld<true>(p), part_ld<true>(p + 1), part_ld<true>(p + 2), part_ld<true>(p + 3));
+  else
+    return *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ void part_st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the ns split partials of one (sequence, query head) with the
+// online-softmax rule of "KV Cache Management", section "Chunked prefill
+// mechanics": M = max_s m_s, w_s = 2^(m_s - M), out = sum_s w_s o_s / sum_s w_s l_s
+// (m in log2 units: scores were scaled by log2 e). po: the ns rows of D floats,
+// ml: their ns (m, l) pairs. One wave, ns >= 1; writes the D outputs. COH picks
+// coherent loads (partials written by other work items of the same launch);
+// the arithmetic, hence every output bit, is the same either way.
+template <typename T, bool COH = false>
+__device__ __forceinline__ void merge_split_row(const float* __restrict__ po,
+                                                const float* __restrict__ ml, int ns, int D,
+                                                T* __restrict__ o, int lane) {
+  float M = -INFINITY;
+  for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_ld<COH>(ml + 2 * s));
+  M = wave_max(M);
+  float Lsum = 0.f;
+  for (int s = lane; s < ns; s += 64)
+    Lsum += exp2f(part_ld<COH>(ml + 2 * s) - M) * part_ld<COH>(ml + 2 * s + 1);
+  Lsum = wave_sum(Lsum);
+  const float inv = 1.f / Lsum;
+
+  const int C4 = D >> 2;  // float4 columns of one partial row
+  if ((D & 3) == 0 && C4 <= 64 && (64 % C4) == 0) {
+    // Lane (grp, col): column col of every groups-th split, independent loads
+    // unrolled four deep, then the groups are summed across lanes.
+    const int groups = 64 / C4;
+    const int col = lane % C4;
+    const int grp = lane / C4;
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+    int s = grp;
+    for (; s + 3 * groups < ns; s += 4 * groups) {
+      float4 v[4];
+      float wt[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = part_ld4<COH>(po + (int64_t)(s + u * groups) * D + 4 * col);
+        wt[u] = part_ld<COH>(ml + 2 * (s + u * groups));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float ww = exp2f(wt[u] - M);
+        a.x = fmaf(ww, v[u].x, a.x);
+        a.y = fmaf(ww, v[u].y, a.y);
+        a.z = fmaf(ww, v[u].z, a.z);
+        a.w = fmaf(ww, v[u].w, a.w);
+      }
+    }
+    for (; s < ns; s += groups) {
+      const float4 v = part_ld4<COH>(po + (int64_t)s * D + 4 * col);
+      const float ww = exp2f(part_ld<COH>(ml + 2 * s) - M);
+      a.x = fmaf(ww, v.x, a.x);
+      a.y = fmaf(ww, v.y, a.y);
+      a.z = fmaf(ww, v.z, a.z);
+      a.w = fmaf(ww, v.w, a.w);
+    }
+    for (int off = C4; off < 64; off <<= 1) {
+      a.x += __shfl_xor(a.x, off);
+      a.y += __shfl_xor(a.y, off);
+      a.z += __shfl_xor(a.z, off);
+      a.w += __shfl_xor(a.w, off);
+    }
+    if (grp == 0) {
+      o[4 * col + 0] = from_f32<T>(a.x * inv);
+      o[4 * col + 1] = from_f32<T>(a.y * inv);
+      o[4 * col + 2] = from_f32<T>(a.z * inv);
+      o[4 * col + 3] = from_f32<T>(a.w * inv);
+    }
+    return;
+  }
+  for (int d = lane; d < D; d += 64) {
+    float a = 0.f;
+    for (int s = 0; s < ns; ++s)
+      a = fmaf(exp2f(part_ld<COH>(ml + 2 * s) - M), part_ld<COH>(po + (int64_t)s * D + d), a);
+    o[d] = from_f32<T>(a * inv);
+  }
+}
+
+// Split arrival for the merge inside the decode kernel, called by every lane of
+// a work item after it has written its partials with part_st_coherent; counter
+// belongs to the item's (sequence, KV head) and counts the splits that have
+// finished. The item's coherent stores complete before it counts itself, so
+// the wave that finds ns - 1 splits counted before it -- the last, for which
+// true is returned -- reads every partial with coherent loads (merge_split_row
+// with COH), merges, and puts the counter back to 0.
+__device__ __forceinline__ bool split_arrive_last(int* counter, int ns, int lane) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int prev = 0;
+  if (lane == 0) prev = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0);
+  asm volatile("" ::: "memory");
+  return prev == ns - 1;
+}
+
 inline bool geom_ok(const pa_geom* g) {
   return g && g->num_layers > 0 && g->num_kv_heads > 0 && g->head_dim > 0 && g->block_size > 0 &&
          g->num_blocks > 0 && (g->dtype == PA_F32 || g->dtype == PA_BF16 || g->dtype == PA_FP8);

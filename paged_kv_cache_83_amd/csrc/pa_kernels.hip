@@ -25,6 +25,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -38,6 +39,7 @@
 #include "pa_move.h"
 #include "pa_fp8.h"
 #include "pa_pairs.h"
+#include "pa_valu.h"
 
 namespace {
 
@@ -513,69 +515,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     return;
   }
   const int64_t row0 = ((int64_t)i * Hq + h) * S_max;
-  const float* ml = part_ml + row0 * 2;
-  const float* po = part_o + row0 * D;
-  float M = -INFINITY;
-  for (int s = lane; s < ns; s += 64) M = fmaxf(M, ml[2 * s]);
-  M = wave_max(M);
-  float Lsum = 0.f;
-  for (int s = lane; s < ns; s += 64) Lsum += exp2f(ml[2 * s] - M) * ml[2 * s + 1];
-  Lsum = wave_sum(Lsum);
-  const float inv = 1.f / Lsum;
-
-  const int C4 = D >> 2;  // float4 columns of one partial row
-  if ((D & 3) == 0 && C4 <= 64 && (64 % C4) == 0) {
-    // Lane (grp, col): column col of every groups-th split, independent loads
-    // unrolled four deep, then the groups are summed across lanes.
-    const int groups = 64 / C4;
-    const int col = lane % C4;
-    const int grp = lane / C4;
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-    int s = grp;
-    for (; s + 3 * groups < ns; s += 4 * groups) {
-      float4 v[4];
-      float wt[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        v[u] = *reinterpret_cast<const float4*>(po + (int64_t)(s + u * groups) * D + 4 * col);
-        wt[u] = ml[2 * (s + u * groups)];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float ww = exp2f(wt[u] - M);
-        a.x = fmaf(ww, v[u].x, a.x);
-        a.y = fmaf(ww, v[u].y, a.y);
-        a.z = fmaf(ww, v[u].z, a.z);
-        a.w = fmaf(ww, v[u].w, a.w);
-      }
-    }
-    for (; s < ns; s += groups) {
-      const float4 v = *reinterpret_cast<const float4*>(po + (int64_t)s * D + 4 * col);
-      const float ww = exp2f(ml[2 * s] - M);
-      a.x = fmaf(ww, v.x, a.x);
-      a.y = fmaf(ww, v.y, a.y);
-      a.z = fmaf(ww, v.z, a.z);
-      a.w = fmaf(ww, v.w, a.w);
-    }
-    for (int off = C4; off < 64; off <<= 1) {
-      a.x += __shfl_xor(a.x, off);
-      a.y += __shfl_xor(a.y, off);
-      a.z += __shfl_xor(a.z, off);
-      a.w += __shfl_xor(a.w, off);
-    }
-    if (grp == 0) {
-      o[4 * col + 0] = from_f32<T>(a.x * inv);
-      o[4 * col + 1] = from_f32<T>(a.y * inv);
-      o[4 * col + 2] = from_f32<T>(a.z * inv);
-      o[4 * col + 3] = from_f32<T>(a.w * inv);
-    }
-    return;
-  }
-  for (int d = lane; d < D; d += 64) {
-    float a = 0.f;
-    for (int s = 0; s < ns; ++s) a = fmaf(exp2f(ml[2 * s] - M), po[(int64_t)s * D + d], a);
-    o[d] = from_f32<T>(a * inv);
-  }
+  merge_split_row<T>(part_o + row0 * D, part_ml + row0 * 2, ns, D, o, lane);
 }
 
 // =============================================================================
@@ -600,13 +540,36 @@ size_t generic_lds_bytes(int G, int D, int B) {
   return sizeof(float) * ((size_t)G * D + 2 * (size_t)B * D + (size_t)G * B + G + 64);
 }
 
+// Blocks per iteration of the streaming VALU kernel (its ValuCfg::BPI).
+int valu_bpi(const pa_geom* g) {
+  const int bytes = g->head_dim * (int)esize(g);
+  return 4 / (bytes <= 128 ? 1 : bytes / 128);
+}
+// LDS bytes of a VALU workgroup of W waves (ValuLds) and its largest W.
+size_t valu_lds_bytes(const pa_geom* g, int G, int W) {
+  const int es = (int)esize(g), D = g->head_dim;
+  const int bytes = D * es;
+  const int kpi = 64 / (bytes <= 128 ? 1 : bytes / 128);
+  const size_t qs = (size_t)G * D * es / 4;
+  const size_t ps = (size_t)G * kpi * (es == 2 ? 1 : 2) / 2 + 4;
+  const size_t mg = (size_t)G * (D + 2);
+  return 4 * (qs + (size_t)W * (ps + mg));
+}
+int valu_wmax(const pa_geom* g, int G) {   // ValuWg::WMAX
+  return (G == 1 && g->head_dim * esize(g) == 256) ? 16 : 8;
+}
+
 struct DecodePlan {
-  int kernel;  // 1 generic, 2 mfma (bf16 pool), 3 mfma (fp8 pool)
+  int kernel;  // 1 generic, 2 mfma (bf16 pool), 3 mfma (fp8 pool), 4 streaming VALU
   bool stream_kv;  // non-temporal K/V loads
-  int bps;
+  int bps;         // blocks per split (work item; for the VALU kernel a workgroup)
+  int bpw;         // VALU kernel: blocks per wave
+  int wg_waves;    // VALU kernel: waves per workgroup
   int S_max;
   bool direct;
+  bool merge;       // splits merged inside the decode launch (counters after the partials)
   size_t ws;
+  size_t counters_off;
 };
 
 pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ctx,
@@ -620,6 +583,8 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
   const size_t gen_lds = generic_lds_bytes(G, D, B);
   const bool gen_ok = !fp8 && B <= 64 && D <= 256 && B * D <= 4096 && G * D <= 64 * kGenMaxAcc &&
                       G <= 64 && gen_lds <= 65536;
+  const bool valu_ok = !fp8 && B == 16 && (D == 64 || D == 128) &&
+                       (G == 1 || G == 2 || G == 4 || (G == 8 && D == 128));
   const int want = opts ? opts->kernel : 0;
   int k;
   if (want == 1) {
@@ -628,8 +593,12 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
   } else if (want == 2) {
     if (!mfma_ok) return PA_ERR_UNSUPPORTED;
     k = fp8 ? 3 : 2;
+  } else if (want == 3) {
+    if (!valu_ok) return PA_ERR_UNSUPPORTED;
+    k = 4;
   } else if (want == 0) {
     if (mfma_ok) k = fp8 ? 3 : 2;
+    else if (valu_ok) k = 4;
     else if (gen_ok) k = 1;
     else return PA_ERR_UNSUPPORTED;
   } else {
@@ -645,9 +614,11 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
     // fewer, longer items beat more, shorter ones once the chip is covered.
     // The generic kernel walks its blocks one at a time with a load latency per
     // block, so it wants many short items instead.
+    // The streaming VALU kernel runs two waves per SIMD and takes four blocks
+    // per iteration: about two items per SIMD, at least one iteration each.
     const int64_t units = (int64_t)n_seqs * g->num_kv_heads;
-    const int64_t target_items = k >= 2 ? 1024 : 4096;
-    const int64_t min_bps = k >= 2 ? 16 : 2;
+    const int64_t target_items = k == 4 ? 2048 : k >= 2 ? 1024 : 4096;
+    const int64_t min_bps = k == 4 ? valu_bpi(g) : k >= 2 ? 16 : 2;
     if (units >= target_items || units == 0) {
       bps = maxb;
     } else {
@@ -657,16 +628,35 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
   }
   bps = std::max<int64_t>(2, bps);
   bps += bps & 1;  // pairs of blocks never straddle two splits
-  if (k >= 2) bps = std::min<int64_t>(bps, kMfmaMaxBps);
+  int64_t bpw = 0, W = 1;
+  if (k == 4) {
+    // The VALU kernel: bps blocks per wave (whole iterations, at most 64: a
+    // wave's block ids sit in one register); a workgroup of W waves covers as
+    // much of the longest sequence as W allows, its waves merged in LDS.
+    const int64_t bpi = valu_bpi(g);
+    bpw = std::min<int64_t>(64, (bps + bpi - 1) / bpi * bpi);
+    const int64_t want_w = opts && opts->waves_per_group > 0 ? opts->waves_per_group : 1;
+    W = std::max<int64_t>(1, std::min<int64_t>({want_w, (int64_t)valu_wmax(g, G), (maxb + bpw - 1) / bpw}));
+    while (W > 1 && valu_lds_bytes(g, G, (int)W) > 65536) --W;
+    bps = bpw * W;
+  } else if (k >= 2) {
+    bps = std::min<int64_t>(bps, kMfmaMaxBps);
+  }
   if (bps > INT32_MAX / 2) bps = INT32_MAX / 2;
   int64_t S = maxb == 0 ? 1 : (maxb + bps - 1) / bps;
   if (opts && (opts->kv_reuse < 0 || opts->kv_reuse > 1)) return PA_ERR_INVALID_ARG;
+  if (opts && (opts->merge < 0 || opts->merge > 1 || opts->waves_per_group < 0)) return PA_ERR_INVALID_ARG;
   plan->kernel = k;
   plan->stream_kv = !(opts && opts->kv_reuse == 1);
   plan->bps = (int)bps;
+  plan->bpw = (int)bpw;
+  plan->wg_waves = (int)W;
   plan->S_max = (int)S;
   plan->direct = S == 1;
-  plan->ws = plan->direct ? 0 : (size_t)n_seqs * Hq * S * (D + 2) * sizeof(float);
+  plan->merge = !plan->direct && opts && opts->merge == 1 && k == 4;
+  const size_t parts = plan->direct ? 0 : (size_t)n_seqs * Hq * S * (D + 2) * sizeof(float);
+  plan->counters_off = parts;
+  plan->ws = parts + (plan->merge ? ((size_t)n_seqs * g->num_kv_heads * sizeof(int32_t) + 15) / 16 * 16 : 0);
   return PA_OK;
 }
 
@@ -781,6 +771,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   const int64_t layer_off = (int64_t)layer * g->num_blocks * Hkv * B * D;
   float* part_o = (float*)workspace;
   float* part_ml = plan.direct ? nullptr : part_o + (size_t)n_seqs * n_q_heads * plan.S_max * D;
+  int* counters = plan.merge ? (int*)((char*)workspace + plan.counters_off) : nullptr;
   if (plan.kernel == 3 && append) {  // FP8: quantize the step's tokens into the pool first
     ProfScope ps("append", st);
     if (!launch_append_fp8(st, (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)knew,
@@ -843,6 +834,34 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
 #undef PA_MFMA_LAUNCH
 #undef PA_MFMA_LAUNCH_NT
 #undef PA_MFMA_LAUNCH_X
+    } else if (plan.kernel == 4) {
+#define PA_VALU_LAUNCH_X(T, DD, GG, NTV)                                                          \
+  hipLaunchKernelGGL((decode_valu_kernel<T, DD, GG, NTV>), grid, dim3(64 * plan.wg_waves),         \
+                     valu_lds_bytes(g, G, plan.wg_waves), st, (T*)k_pool,                          \
+                     (T*)v_pool, (const T*)q, (const T*)knew, (const T*)vnew, (T*)out, part_o,     \
+                     part_ml, block_tables, context_lens, layer_off, g->num_blocks, Hkv,          \
+                     n_q_heads, max_blocks_per_seq, max_context_len, plan.bpw, plan.S_max,         \
+                     qk_scale, plan.direct ? 1 : 0, append ? 1 : 0, counters)
+#define PA_VALU_LAUNCH_G(T, DD, NTV)                  \
+  do {                                                \
+    if (G == 1) PA_VALU_LAUNCH_X(T, DD, 1, NTV);      \
+    else if (G == 2) PA_VALU_LAUNCH_X(T, DD, 2, NTV); \
+    else PA_VALU_LAUNCH_X(T, DD, 4, NTV);             \
+  } while (0)
+#define PA_VALU_LAUNCH(T, NTV)                                          \
+  do {                                                                  \
+    if (D == 64) PA_VALU_LAUNCH_G(T, 64, NTV);                          \
+    else if (G == 8) PA_VALU_LAUNCH_X(T, 128, 8, NTV);                  \
+    else PA_VALU_LAUNCH_G(T, 128, NTV);                                 \
+  } while (0)
+      if (g->dtype == PA_F32) {
+        if (plan.stream_kv) PA_VALU_LAUNCH(float, true); else PA_VALU_LAUNCH(float, false);
+      } else {
+        if (plan.stream_kv) PA_VALU_LAUNCH(uint16_t, true); else PA_VALU_LAUNCH(uint16_t, false);
+      }
+#undef PA_VALU_LAUNCH
+#undef PA_VALU_LAUNCH_G
+#undef PA_VALU_LAUNCH_X
     } else {
       const size_t lds = generic_lds_bytes(G, D, B);
 #define PA_GEN_LAUNCH_X(T, DIR, RR, APP)                                                          \
@@ -875,7 +894,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
     }
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
-  if (!plan.direct) {
+  if (!plan.direct && !plan.merge) {
     ProfScope ps("decode_combine", st);
     const dim3 grid((unsigned)((int64_t)n_seqs * n_q_heads)), block(64);
     if (g->dtype == PA_F32)  // bf16 output for bf16 and fp8 pools

@@ -1,0 +1,492 @@
+// Streaming paged decode on the vector ALUs (gfx950, wave64): fp32 or bf16
+// pools with 16-slot blocks, head dim 64 or 128, 1, 2 or 4 query heads per KV
+// head (and 8 at head dim 128). It is the decode path for pools and shapes the matrix-core kernel
+// does not take (fp32 pools above all), and the vector-ALU alternative that
+// shows what the matrix cores buy on the grouped shapes.
+//
+// "KV Cache Management", section "The PagedAttention virtual memory model":
+// the kernel takes the block table as an input, loads the physical block ids
+// on chip and walks the logical blocks; section "Chunked prefill mechanics":
+// the running maximum m and normaliser l, with the accumulator rescaled by
+// exp(m_prev - m_new) as each tile of keys arrives.
+//
+// One wave = one work item (sequence i, KV head g, split s), no barrier other
+// than the wave's own LDS ordering. Per iteration it takes KPI keys (64 / LPK
+// keys, BPI = KPI / 16 blocks; LPK lanes share a key so that each holds 128
+// bytes of its row: 8 K loads and 8 V loads per lane and iteration):
+//   scores:  lane (key k, part p) holds the key's K row dims [p*KE, (p+1)*KE)
+//            in registers (the slot's row of every 32-wide chunk, KL 16-byte
+//            loads) and dots it with the group's queries, read from LDS as
+//            broadcasts; fp32 pools use FMAs, bf16 pools v_dot2_f32_bf16
+//            (two products per instruction, fp32 accumulation). Parts of one
+//            key are summed across lanes.
+//   softmax: per query head a wave maximum, exp2 of the scaled scores, a
+//            rescale of the accumulators only when the head's maximum moved.
+//            Probabilities go to LDS (fp32, or bf16 for the bf16 dot).
+//   P.V:     lane l holds dims l + 64 r (r < D/64) of every key: the V tile is
+//            dimension-major, so each dim's 16 slots of a block are 16*b
+//            contiguous bytes (4 or 2 loads); products with the probabilities
+//            read back from LDS as broadcasts.
+// The K registers of iteration it+1 are loaded as soon as the scores of it are
+// formed and the V registers of it+1 as soon as its P.V is done, so one
+// iteration of loads is always in flight; the last iteration is peeled so the
+// steady loop issues unconditionally (a conditional issue makes the compiler
+// wait for every outstanding load).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "pa_device.h"
+
+namespace pa_detail {
+
+template <typename T, int D>
+struct ValuCfg {
+  static constexpr int ES = (int)sizeof(T);
+  // lanes per key: each lane holds 128 bytes of its key's row (8 loads), which
+  // keeps a wave's K and V registers at 64 VGPRs whatever the element size
+  static constexpr int LPK = (D * ES <= 128) ? 1 : (D * ES) / 128;
+  static constexpr int KPI = 64 / LPK;            // keys per iteration
+  static constexpr int BPI = KPI / 16;            // blocks per iteration
+  static constexpr int KE = D / LPK;              // K elements per lane
+  static constexpr int EPL = 16 / ES;             // elements per 16-byte load
+  static constexpr int KL = KE / EPL;             // K loads per lane
+  static constexpr int DPL = D / 64;              // head dims per lane in P.V
+  static constexpr int VPB = 16 / EPL;            // loads per (block, dim): 16 slots
+  static_assert(D % 64 == 0 && KE % 32 == 0 && BPI >= 1, "head dim 64 or 128");
+};
+
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
+
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// a.b over the element pairs of one 32-bit word each (bf16) plus c, in fp32.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_v, a),
+                                         __builtin_bit_cast(bf16x2_v, b), c, false);
+}
+
+// acc += sum over the 16 bytes of k . q (4 fp32 products or 8 bf16 products).
+template <typename T>
+__device__ __forceinline__ float dot16(const u32x4& k, const u32x4& q, float acc) {
+  if constexpr (sizeof(T) == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(k[e]), __uint_as_float(q[e]), acc);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc = dot2_bf16(k[e], q[e], acc);
+  }
+  return acc;
+}
+
+// Workgroup shape of the kernel: up to WMAX waves. 16 where one query head per
+// KV head and 256-byte K rows (fp32 d = 64, bf16 d = 128) keep the kernel
+// within the 128 registers a full CU of waves leaves each; 8 otherwise.
+template <typename T, int D, int G>
+struct ValuWg {
+  static constexpr int WMAX = (G == 1 && D * (int)sizeof(T) == 256) ? 16 : 8;
+};
+
+// LDS words of a workgroup of W waves: the group's queries, then per wave its
+// probabilities and its (o, m, l) for the merge across waves.
+template <typename T, int D, int G>
+struct ValuLds {
+  static constexpr int ES = (int)sizeof(T);
+  static constexpr int QS = G * D * ES / 4;
+  static constexpr int PS = G * ValuCfg<T, D>::KPI * (ES == 2 ? 1 : 2) / 2 + 4;
+  static constexpr int MG = G * (D + 2);
+  static constexpr int PER_WAVE = PS + MG;
+};
+
+// Work item = workgroup (sequence i, KV head g, split s) of W waves: wave wv
+// takes blocks [s*bps + wv*bpw, +bpw) of the sequence (bps = W*bpw); the waves'
+// results are merged through LDS. A split that covers the whole sequence
+// writes the output; otherwise it writes its merged partial (o, m, l) to the
+// workspace, merged by the combine launch or, with counters (in-kernel merge),
+// by the last split of (i, g) to finish.
+// APPEND (runtime flag): the step's new token of sequence i (position len-1)
+// comes in knew/vnew [n][H_kv][d]; the wave holding that position writes it
+// into the pool and reads it from the inputs (K row by address, V element by
+// register) while attending.
+template <typename T, int D, int G, bool NT>
+__global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kernel(
+    T* __restrict__ kpool, T* __restrict__ vpool, const T* __restrict__ q,
+    const T* __restrict__ knew, const T* __restrict__ vnew, T* __restrict__ out,
+    float* __restrict__ part_o, float* __restrict__ part_ml, const int32_t* __restrict__ tables,
+    const int32_t* __restrict__ lens, int64_t layer_off, int N, int Hkv, int Hq, int max_blocks,
+    int max_ctx, int bpw, int S_max, float qk_scale, int direct, int append,
+    int* __restrict__ counters) {
+  using C = ValuCfg<T, D>;
+  using LW = ValuLds<T, D, G>;
+  constexpr int ES = C::ES, KPI = C::KPI, BPI = C::BPI, KE = C::KE, EPL = C::EPL, KL = C::KL;
+  constexpr int DPL = C::DPL, VPB = C::VPB;
+  constexpr int TILE = 16 * D;                       // elements of one (block, head) tile
+  constexpr bool BF = sizeof(T) == 2;
+  extern __shared__ __attribute__((aligned(16))) uint32_t lds_valu[];
+  const int W = blockDim.x >> 6;
+  const int wv = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // queries (as stored: fp32 words or bf16 pairs), then per wave: probabilities
+  // of one iteration, and (o, m, l) of each head for the merge across waves
+  uint32_t* qs = lds_valu;
+  uint32_t* ps = lds_valu + LW::QS + wv * LW::PER_WAVE;
+  float* mg_base = reinterpret_cast<float*>(lds_valu + LW::QS + LW::PS);   // + wave * PER_WAVE
+
+  const int w = blockIdx.x;
+  const int g = w % Hkv;
+  const int si = w / Hkv;
+  const int s = si % S_max;
+  const int i = si / S_max;
+  const int k = lane % KPI;        // key of the lane in the score phase
+  const int part = lane / KPI;     // which KE-dim slice of it
+
+  const int bps = W * bpw;         // blocks of one split (workgroup)
+  const int len = clamp_len(lens, i, max_ctx);
+  const int nblk = (len + 15) >> 4;
+  const int B0 = s * bps;
+  if (B0 >= nblk) {   // the whole workgroup (uniform)
+    if (direct && len == 0) {
+      T* o = out + ((int64_t)i * Hq + (int64_t)g * G) * D;
+      for (int e = threadIdx.x; e < G * D; e += blockDim.x) o[e] = from_f32<T>(0.f);
+    }
+    return;
+  }
+  const int n_act = min(W, (nblk - B0 + bpw - 1) / bpw);   // waves with blocks
+  const bool active = wv < n_act;
+  const int b0 = B0 + wv * bpw;
+  const int b1 = min(b0 + bpw, nblk);
+  const int span = active ? b1 - b0 : 1;
+  const int lim = min(len, b1 * 16);  // keys at or past lim belong to a later wave / split or past the length
+
+  // The wave's block ids (at most 64), one per lane, read once.
+  const int32_t* trow = tables + (int64_t)i * max_blocks;
+  const int tb = (active && lane < span) ? guard_block(trow[b0 + lane], N) : 0;
+  // The group's G query rows (contiguous in q): loaded now into registers, put
+  // in LDS once the first K/V loads are on their way.
+  constexpr int QPIECES = G * D * ES / 16;
+  constexpr int QPT = (QPIECES + 63) / 64;   // pieces per thread of a one-wave workgroup
+  u32x4 qreg[QPT];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((int64_t)i * Hq + (int64_t)g * G) * D);
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int e = threadIdx.x + j * (int)blockDim.x;
+      qreg[j] = e < QPIECES ? src[e] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const T* kl = kpool + layer_off + (int64_t)g * TILE;   // + block * Hkv * TILE
+  const T* vl = vpool + layer_off + (int64_t)g * TILE;
+  const int64_t bstride = (int64_t)Hkv * TILE;
+
+  // The appended token (position len-1), if this wave's blocks hold it.
+  int new_pos = -1;
+  const T* knew_row = knew;
+  const T* vnew_row = vnew;
+  if (append && active && len > 0 && ((len - 1) >> 4) >= b0 && ((len - 1) >> 4) < b1) {
+    new_pos = len - 1;
+    knew_row = knew + ((int64_t)i * Hkv + g) * D;
+    vnew_row = vnew + ((int64_t)i * Hkv + g) * D;
+    const int64_t tile = (int64_t)__builtin_amdgcn_readlane(tb, (new_pos >> 4) - b0) * bstride;
+    const int on = new_pos & 15;
+    T* kt = kpool + layer_off + (int64_t)g * TILE + tile;
+    T* vt = vpool + layer_off + (int64_t)g * TILE + tile;
+    for (int e = lane; e < D; e += 64) {
+      kt[(e >> 5) * 512 + on * 32 + (e & 31)] = knew_row[e];
+      vt[e * 16 + on] = vnew_row[e];
+    }
+  }
+
+  float acc[G][DPL];
+  float m_run[G], l_part[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    l_part[h] = 0.f;
+#pragma unroll
+    for (int r = 0; r < DPL; ++r) acc[h][r] = 0.f;
+  }
+
+  // The queries to LDS. One wave: its own writes, ordered for its reads below
+  // by LDS order (no workgroup barrier, which would also wait for the K/V loads
+  // just issued); several waves: every thread writes its pieces, then a
+  // barrier that waits for LDS only.
+  auto store_queries = [&]() {
+    u32x4* dst = reinterpret_cast<u32x4*>(qs);
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int e = threadIdx.x + j * (int)blockDim.x;
+      if (e < QPIECES) dst[e] = qreg[j];
+    }
+    if (W == 1) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+  };
+  if (!active) store_queries();   // the barrier is reached by every wave
+
+  if (active) {
+    // Block id of the wave's block b (wave-uniform b, clamped into its range:
+    // blocks past it are read but fully masked).
+    auto blk_id = [&](int b) { return __builtin_amdgcn_readlane(tb, min(b, span - 1)); };
+    // A wave-uniform value held in a vector register, so that compares against
+    // it are vector compares (no scalar condition registers held across the
+    // unrolled selects below).
+    auto in_vgpr = [](int x) {
+      int v;
+      asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(x));
+      return v;
+    };
+
+    u32x4 kr[KL];
+    u32x4 vr[BPI][DPL][VPB];
+    auto issue_k = [&](int it) {
+      // the lane's block: entry it*BPI + k/16 of the wave's range, fetched from its lane
+      const int idv = __shfl(tb, min(it * BPI + (k >> 4), span - 1));
+      const T* base = kl + (int64_t)idv * bstride + (k & 15) * 32 + (int64_t)part * (KE / 32) * 512;
+      const bool is_new = new_pos >= 0 && (b0 + it * BPI) * 16 + k == new_pos;
+      // one load per piece from a per-lane address: the new token's lanes read the input row
+      const T* nb = knew_row + part * KE;
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        const int e0 = j * EPL;                       // element of the lane's slice
+        const T* pa = is_new ? nb + e0 : base + (e0 >> 5) * 512 + (e0 & 31);
+        kr[j] = ld16<NT>(pa);
+      }
+    };
+    auto issue_v = [&](int it) {
+#pragma unroll
+      for (int b = 0; b < BPI; ++b) {
+        const T* base = vl + (int64_t)blk_id(it * BPI + b) * bstride;
+#pragma unroll
+        for (int r = 0; r < DPL; ++r)
+#pragma unroll
+          for (int u = 0; u < VPB; ++u) vr[b][r][u] = ld16<NT>(base + (lane + 64 * r) * 16 + u * EPL);
+      }
+    };
+
+    auto scores_softmax = [&](int it) {
+      const int pos0 = (b0 + it * BPI) * 16;
+      float sc[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+          const u32x4 qv = *reinterpret_cast<const u32x4*>(qs + (h * D + part * KE + j * EPL) * ES / 4);
+          a = dot16<T>(kr[j], qv, a);
+        }
+        if constexpr (C::LPK >= 2) a += __shfl_xor(a, KPI);
+        if constexpr (C::LPK >= 4) a += __shfl_xor(a, 2 * KPI);
+        sc[h] = (pos0 + k < lim) ? a * qk_scale : -INFINITY;
+        // with 8 heads the scheduler would otherwise read every head's queries
+        // ahead (64 fragments, more registers than a wave has)
+        if constexpr (G >= 8) __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float m_new = fmaxf(m_run[h], wave_max(sc[h]));  // finite: the first key is attended
+        const float p = __builtin_amdgcn_exp2f(sc[h] - m_new);
+        if (m_new != m_run[h]) {   // wave-uniform
+          const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
+          l_part[h] *= alpha;
+#pragma unroll
+          for (int r = 0; r < DPL; ++r) acc[h][r] *= alpha;
+        }
+        m_run[h] = m_new;
+        if (part == 0) {
+          l_part[h] += p;
+          if constexpr (BF) reinterpret_cast<uint16_t*>(ps)[h * KPI + k] = f32_to_bf16(p);
+          else reinterpret_cast<float*>(ps)[h * KPI + k] = p;
+        }
+      }
+    };
+
+    // Only the last iteration of a wave's range can hold masked keys (blocks
+    // past the range, slots past the length) or the appended token: both lie
+    // in the sequence's last block, the last block of the last range. Its V
+    // registers are fixed up here, outside the steady loop, so the loop's V
+    // registers carry no conditional updates (which would make the compiler
+    // copy them, and wait for every load in flight to do so).
+    auto fix_last_v = [&](int it) {
+      const int pos0 = (b0 + it * BPI) * 16;
+      if (new_pos >= pos0 && new_pos < pos0 + KPI) {   // wave-uniform: the appended token's V
+        const int kk = in_vgpr(new_pos - pos0);
+#pragma unroll
+        for (int r = 0; r < DPL; ++r) {
+          const uint32_t nv = BF ? (uint32_t)reinterpret_cast<const uint16_t*>(vnew_row)[lane + 64 * r]
+                                 : reinterpret_cast<const uint32_t*>(vnew_row)[lane + 64 * r];
+          const uint32_t nw = BF ? ((kk & 1) ? (nv << 16) : nv) : nv;
+          const uint32_t keep = BF ? ((kk & 1) ? 0x0000ffffu : 0xffff0000u) : 0u;
+#pragma unroll
+          for (int b = 0; b < BPI; ++b)
+#pragma unroll
+            for (int u = 0; u < VPB; ++u)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {   // word c holds slots (u*EPL + c*EPL/4 ..)
+                const int key0 = b * 16 + u * EPL + c * (EPL / 4);
+                const uint32_t wd = vr[b][r][u][c];
+                const bool hit = BF ? ((kk >> 1) == (key0 >> 1)) : (kk == key0);
+                vr[b][r][u][c] = hit ? ((wd & keep) | nw) : wd;
+              }
+        }
+      }
+      if (pos0 + KPI > lim) {   // wave-uniform: zero the V of masked keys (their data may be NaN)
+        const int nval = in_vgpr(lim - pos0);   // keys 0 .. nval-1 of the iteration are attended
+#pragma unroll
+        for (int b = 0; b < BPI; ++b)
+#pragma unroll
+          for (int r = 0; r < DPL; ++r)
+#pragma unroll
+            for (int u = 0; u < VPB; ++u)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const int key0 = b * 16 + u * EPL + c * (EPL / 4);
+                const uint32_t wd = vr[b][r][u][c];
+                if constexpr (BF)
+                  vr[b][r][u][c] = key0 + 1 < nval ? wd : (key0 < nval ? (wd & 0x0000ffffu) : 0u);
+                else
+                  vr[b][r][u][c] = key0 < nval ? wd : 0u;
+              }
+      }
+    };
+
+    auto pv = [&]() {
+      // The probabilities were written by the score phase of this same wave, in
+      // its own LDS region: LDS executes one wave's instructions in order, so
+      // only the compiler must keep the reads below the writes (a workgroup
+      // barrier would also wait for the next iteration's loads in flight).
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int b = 0; b < BPI; ++b)
+#pragma unroll
+          for (int u = 0; u < VPB; ++u) {
+            const u32x4 pv4 = *reinterpret_cast<const u32x4*>(
+                ps + (h * KPI + b * 16 + u * EPL) * ES / 4);
+#pragma unroll
+            for (int r = 0; r < DPL; ++r) acc[h][r] = dot16<T>(vr[b][r][u], pv4, acc[h][r]);
+          }
+        if constexpr (G >= 8) __builtin_amdgcn_sched_barrier(0);   // as in the score phase
+      }
+    };
+
+    const int n_it = (span + BPI - 1) / BPI;
+    issue_k(0);
+    issue_v(0);
+    store_queries();
+    for (int it = 0; it + 1 < n_it; ++it) {
+      scores_softmax(it);
+      __builtin_amdgcn_sched_barrier(0);   // the K registers are free only after the scores
+      issue_k(it + 1);
+      pv();
+      __builtin_amdgcn_sched_barrier(0);   // likewise the V registers after P.V
+      issue_v(it + 1);
+    }
+    scores_softmax(n_it - 1);
+    fix_last_v(n_it - 1);
+    pv();
+
+    // l: the sum over the wave of each lane's own keys
+#pragma unroll
+    for (int h = 0; h < G; ++h) l_part[h] = wave_sum(l_part[h]);
+  }
+
+  const int ns = (nblk + bps - 1) / bps;   // splits (workgroups) of this sequence
+  const bool whole = direct || ns == 1;    // this split covers the sequence
+  const bool coherent = counters != nullptr;
+  // The workgroup's result for head h -- maximum M, sum L, unnormalised o of
+  // the lane's dims -- goes out as the output or as the split's partial.
+  auto finish = [&](int h, float M, float L, const float (&o)[DPL]) {
+    if (whole && (direct || coherent)) {   // the output, normalised
+      const float inv = 1.f / L;
+      T* op = out + ((int64_t)i * Hq + (int64_t)g * G + h) * D;
+#pragma unroll
+      for (int r = 0; r < DPL; ++r) op[lane + 64 * r] = from_f32<T>(o[r] * inv);
+    } else {   // the split's partial (with the combine launch, also for a one-split sequence)
+      const int64_t row = ((int64_t)i * Hq + (int64_t)g * G + h) * S_max + s;
+      if (coherent) {
+#pragma unroll
+        for (int r = 0; r < DPL; ++r) part_st_coherent(part_o + row * D + lane + 64 * r, o[r]);
+        if (lane == 0) {
+          part_st_coherent(part_ml + row * 2 + 0, M);
+          part_st_coherent(part_ml + row * 2 + 1, L);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < DPL; ++r) part_o[row * D + lane + 64 * r] = o[r];
+        if (lane == 0) {
+          part_ml[row * 2 + 0] = M;
+          part_ml[row * 2 + 1] = L;
+        }
+      }
+    }
+  };
+
+  if (W == 1) {   // one wave: its registers are the workgroup's result
+#pragma unroll
+    for (int h = 0; h < G; ++h) finish(h, m_run[h], l_part[h], acc[h]);
+  } else {
+    if (active) {   // the wave's (o, m, l) to LDS
+      float* mg = mg_base + (int64_t)wv * LW::PER_WAVE;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+#pragma unroll
+        for (int r = 0; r < DPL; ++r) mg[h * (D + 2) + lane + 64 * r] = acc[h][r];
+        if (lane == 0) {
+          mg[h * (D + 2) + D] = m_run[h];
+          mg[h * (D + 2) + D + 1] = l_part[h];
+        }
+      }
+    }
+    __syncthreads();   // every active wave's (o, m, l) is in LDS
+    // Merge across the workgroup's waves, same rule as across splits; wave wv
+    // takes heads wv, wv + W, ...
+#pragma unroll 1
+    for (int h = wv; h < G; h += W) {
+      float M = -INFINITY;
+      for (int x = 0; x < n_act; ++x) M = fmaxf(M, mg_base[x * LW::PER_WAVE + h * (D + 2) + D]);
+      float L = 0.f;
+      float o[DPL];
+#pragma unroll
+      for (int r = 0; r < DPL; ++r) o[r] = 0.f;
+      for (int x = 0; x < n_act; ++x) {
+        const float* mgx = mg_base + x * LW::PER_WAVE + h * (D + 2);
+        const float wt = exp2f(mgx[D] - M);
+        L = fmaf(wt, mgx[D + 1], L);
+#pragma unroll
+        for (int r = 0; r < DPL; ++r) o[r] = fmaf(wt, mgx[lane + 64 * r], o[r]);
+      }
+      finish(h, M, L, o);
+    }
+  }
+  if (!coherent || whole) return;
+  // In-kernel merge across splits: every wave's partial stores complete, then
+  // wave 0 counts the split; the last split of (i, g) merges all of them.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (wv == 0 && split_arrive_last(counters + (int64_t)i * Hkv + g, ns, lane)) {
+#pragma unroll 1
+    for (int h = 0; h < G; ++h) {
+      const int64_t row0 = ((int64_t)i * Hq + (int64_t)g * G + h) * S_max;
+      merge_split_row<T, true>(part_o + row0 * D, part_ml + row0 * 2, ns, D,
+                               out + ((int64_t)i * Hq + (int64_t)g * G + h) * D, lane);
+    }
+    if (lane == 0) __hip_atomic_store(counters + (int64_t)i * Hkv + g, 0, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace pa_detail

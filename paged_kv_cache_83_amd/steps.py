@@ -33,7 +33,7 @@ def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slo
                 max_context_len: int, out_all, workspace, layers: Optional[Sequence[int]] = None,
                 blocks_per_split: int = 0, kernel: str = "auto", stream=None,
                 around_decode: Optional[Callable[[int, bool], None]] = None, kv_reuse: bool = False,
-                fused: bool = True):
+                fused: bool = True, merge: bool = False, waves_per_group: int = 0):
     """One decode step: for each layer, append the new tokens, then decode.
 
     q_all [L, n, H_q, d]; k_new_all / v_new_all [L, n_tok, H_kv, d]; slots int64
@@ -41,6 +41,7 @@ def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slo
     fused=True (one new token per sequence, at position lens[i] - 1 of its table,
     n_tok == n) does both in one launch per layer and ignores `slots`;
     fused=False issues the slot-mapped append and the decode separately.
+    merge=True merges the splits inside the decode launch (zeroed workspace).
     around_decode(layer, before) is called just before and after each layer's
     decode call (host side, e.g. to switch per-kernel timing on and off).
     """
@@ -54,11 +55,13 @@ def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slo
             api.decode_append(geom, k_pool, v_pool, layer, q_all[layer], k_new_all[layer],
                               v_new_all[layer], out_all[layer], tables, lens, max_context_len,
                               workspace=workspace, blocks_per_split=blocks_per_split,
-                              kernel=kernel, stream=stream, kv_reuse=kv_reuse)
+                              kernel=kernel, stream=stream, kv_reuse=kv_reuse, merge=merge,
+                              waves_per_group=waves_per_group)
         else:
             api.decode(geom, k_pool, v_pool, layer, q_all[layer], out_all[layer], tables, lens,
                        max_context_len, workspace=workspace, blocks_per_split=blocks_per_split,
-                       kernel=kernel, stream=stream, kv_reuse=kv_reuse)
+                       kernel=kernel, stream=stream, kv_reuse=kv_reuse, merge=merge,
+                              waves_per_group=waves_per_group)
         if around_decode is not None:
             around_decode(layer, False)
 

@@ -21,9 +21,10 @@ RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 47, 64, 100, 257]
 
 
 def run_library(batch, layer, kernel="auto", bps=0, scale=0.0, tables=None, lengths=None,
-                max_ctx=None):
+                max_ctx=None, merge=False, ws=None, waves=0):
     """Upload the batch, run the library's append + decode on one layer; returns
-    (out, k_pool, v_pool) in storage form."""
+    (out, k_pool, v_pool) in storage form. merge=True merges the splits inside
+    the decode launch (zeroed workspace, or the one passed in)."""
     geom = pk.Geometry(batch.L, batch.Hkv, batch.d, batch.B, batch.N, batch.dtype)
     K, V = to_dev(batch.k_pool, batch.dtype), to_dev(batch.v_pool, batch.dtype)
     slots = torch.from_numpy(batch.slots_new).cuda()
@@ -34,11 +35,13 @@ def run_library(batch, layer, kernel="auto", bps=0, scale=0.0, tables=None, leng
     max_ctx = int(max(lens)) if max_ctx is None else max_ctx
     q = to_dev(batch.q, batch.dtype)
     out = torch.empty_like(q)
-    ws_bytes = pk.decode_workspace_bytes(geom, q.shape[0], q.shape[1], max_ctx, bps, kernel)
-    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws_bytes = pk.decode_workspace_bytes(geom, q.shape[0], q.shape[1], max_ctx, bps, kernel,
+                                             merge, waves)
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     pk.decode(geom, K, V, layer, q, out, torch.from_numpy(tabs).cuda(),
               torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max_ctx, scale=scale,
-              workspace=ws, blocks_per_split=bps, kernel=kernel)
+              workspace=ws, blocks_per_split=bps, kernel=kernel, merge=merge, waves_per_group=waves)
     torch.cuda.synchronize()
     return to_host(out, batch.dtype), to_host(K, batch.dtype), to_host(V, batch.dtype)
 
@@ -57,6 +60,15 @@ CASES = [
     ("generic_f32_d64_split", "f32", 1, 160, 6, 3, 64, 16, "generic", 2),
     ("generic_f32_b32_g4", "f32", 1, 100, 8, 2, 128, 32, "generic", 0),
     ("generic_f32_b1", "f32", 1, 1200, 2, 1, 16, 1, "generic", 64),
+    ("valu_f32_d64_mha", "f32", 2, 160, 12, 12, 64, 16, "valu", 0),
+    ("valu_f32_d64_g2_split2", "f32", 1, 160, 6, 3, 64, 16, "valu", 2),
+    ("valu_f32_d128_g4", "f32", 1, 160, 8, 2, 128, 16, "valu", 0),
+    ("valu_f32_d128_g8_split3", "f32", 1, 160, 16, 2, 128, 16, "valu", 3),
+    ("valu_bf16_d128_g8", "bf16", 1, 160, 64, 8, 128, 16, "valu", 0),
+    ("valu_bf16_d128_g8_split2", "bf16", 1, 160, 16, 2, 128, 16, "valu", 2),
+    ("valu_bf16_d64_g2_split6", "bf16", 1, 160, 8, 4, 64, 16, "valu", 6),
+    ("valu_bf16_d128_mha", "bf16", 1, 160, 4, 4, 128, 16, "valu", 64),
+    ("valu_bf16_d64_g4", "bf16", 2, 160, 16, 4, 64, 16, "valu", 0),
 ]
 
 
@@ -80,7 +92,8 @@ def test_decode_parity(case):
 def test_single_token_returns_its_value_bitwise():
     need_gpu()
     print_case(test="single_token")
-    for kernel, dtype, d in (("mfma", "bf16", 128), ("generic", "f32", 64), ("generic", "bf16", 64)):
+    for kernel, dtype, d in (("mfma", "bf16", 128), ("generic", "f32", 64), ("generic", "bf16", 64),
+                             ("valu", "f32", 64), ("valu", "bf16", 128), ("valu", "f32", 128)):
         batch = make_batch(dtype, 1, 8, 8, 2, d, 16, [1, 1, 1], seed=5)
         out, _, _ = run_library(batch, 0, kernel=kernel)
         for i in range(3):
@@ -91,7 +104,8 @@ def test_single_token_returns_its_value_bitwise():
 def test_zero_length_writes_zeros():
     need_gpu()
     print_case(test="zero_length")
-    for kernel, dtype, bps in (("mfma", "bf16", 0), ("mfma", "bf16", 2), ("generic", "f32", 2)):
+    for kernel, dtype, bps in (("mfma", "bf16", 0), ("mfma", "bf16", 2), ("generic", "f32", 2),
+                               ("valu", "f32", 2), ("valu", "f32", 0), ("valu", "bf16", 2)):
         batch = make_batch(dtype, 1, 64, 8, 2, 64 if dtype == "f32" else 128, 16, [0, 40, 0, 70],
                            seed=9)
         out, _, _ = run_library(batch, 0, kernel=kernel, bps=bps)
@@ -100,12 +114,13 @@ def test_zero_length_writes_zeros():
         assert max_abs_err(out, expect, dtype) <= (BF16_TOL if dtype == "bf16" else F32_TOL)
 
 
-@pytest.mark.parametrize("kernel,dtype,d", [("mfma", "bf16", 128), ("generic", "f32", 64)])
-def test_block_placement_invariance_bitwise(kernel, dtype, d):
+@pytest.mark.parametrize("kernel,dtype,d,Hq", [("mfma", "bf16", 128, 16), ("generic", "f32", 64, 16),
+                                                ("valu", "f32", 64, 8), ("valu", "bf16", 128, 16)])
+def test_block_placement_invariance_bitwise(kernel, dtype, d, Hq):
     """Same logical content under a different physical permutation: identical bits."""
     need_gpu()
     print_case(test="placement", kernel=kernel)
-    L, N, Hq, Hkv, B = 1, 200, 16, 2, 16
+    L, N, Hkv, B = 1, 200, 2, 16
     lengths = [33, 250, 7, 129]
     a = make_batch(dtype, L, N, Hq, Hkv, d, B, lengths, seed=21)
     b = make_batch(dtype, L, N, Hq, Hkv, d, B, lengths, seed=22)
@@ -132,6 +147,11 @@ def test_split_count_invariance():
     one, _, _ = run_library(f, 0, kernel="generic", bps=1024)
     many, _, _ = run_library(f, 0, kernel="generic", bps=2)
     assert np.max(np.abs(one.astype(np.float64) - many.astype(np.float64))) <= 1e-6
+    one, _, _ = run_library(f, 0, kernel="valu", bps=64)     # 16 splits at most (1024 tokens)
+    many, _, _ = run_library(f, 0, kernel="valu", bps=2)
+    assert np.max(np.abs(one.astype(np.float64) - many.astype(np.float64))) <= 1e-6
+    _, _, expect = oracle_step(f, 0)
+    assert max_abs_err(many, expect, "f32") <= F32_TOL
     b = make_batch("bf16", 1, 300, 64, 8, 128, 16, lengths, seed=32)
     one, _, _ = run_library(b, 0, kernel="mfma", bps=1024)
     many, _, _ = run_library(b, 0, kernel="mfma", bps=2)
@@ -176,6 +196,11 @@ def test_unsupported_and_bad_arguments():
         pk.decode(geom, K, V, 0, q, out, tabs, lens, 16, kernel="mfma")    # fp32 has no MFMA path
     with pytest.raises(pk.PagedKVError):
         pk.decode(geom, K, V, 0, q, out, tabs, lens, 17)                    # table too short
+    g64 = pk.Geometry(1, 1, 64, 16, 8, "f32")                               # 8 heads at d = 64:
+    K64, V64 = pk.alloc_pools(g64)                                          # not a VALU shape
+    q64 = torch.zeros(1, 8, 64, device="cuda")
+    with pytest.raises(pk.PagedKVError):
+        pk.decode(g64, K64, V64, 0, q64, torch.empty_like(q64), tabs, lens, 16, kernel="valu")
     with pytest.raises(ValueError):
         pk.decode(geom, K, V, 0, q.to(torch.bfloat16), out, tabs, lens, 16)  # dtype mismatch
 
@@ -203,3 +228,68 @@ def test_kv_reuse_policy_same_result():
     assert np.array_equal(outs[0], outs[1])
     _, _, expect = oracle_step(batch, 0)
     assert max_abs_err(outs[0], expect, "bf16") <= BF16_TOL
+
+
+MERGE_CASES = [
+    # name, dtype, Hq, Hkv, d, bps, lengths
+    ("f32_d64_mha_bps2", "f32", 12, 12, 64, 2, RAGGED),
+    ("f32_d128_g4_bps4", "f32", 8, 2, 128, 4, RAGGED + [1000]),
+    ("bf16_d128_g8_bps2", "bf16", 64, 8, 128, 2, RAGGED),
+    ("bf16_d64_g2_auto", "bf16", 8, 4, 64, 0, RAGGED + [3000, 16 * 64 * 3 + 5]),
+]
+
+
+@pytest.mark.parametrize("case", MERGE_CASES, ids=[c[0] for c in MERGE_CASES])
+def test_in_kernel_merge(case):
+    """Splits merged inside the decode launch (the last split of each sequence and
+    KV head to finish merges, through a counter it resets) give the bits of the
+    separate combine launch; the same zeroed workspace serves later calls, so the
+    counters are back at zero after each one; one-split sequences are written
+    directly."""
+    need_gpu()
+    name, dtype, Hq, Hkv, d, bps, lengths = case
+    print_case(test="in_kernel_merge", case=name)
+    batch = make_batch(dtype, 1, 700, Hq, Hkv, d, 16, lengths, seed=zlib.crc32(name.encode()) % 10000)
+    sep, _, _ = run_library(batch, 0, kernel="valu", bps=bps)
+    geom = pk.Geometry(1, Hkv, d, 16, 700, dtype)
+    need = pk.decode_workspace_bytes(geom, len(lengths), Hq, int(max(lengths)), bps, "valu", True)
+    assert need >= pk.decode_workspace_bytes(geom, len(lengths), Hq, int(max(lengths)), bps, "valu")
+    ws = torch.zeros(max(1, need), dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        got, _, _ = run_library(batch, 0, kernel="valu", bps=bps, merge=True, ws=ws)
+        assert np.array_equal(got.view(np.uint8), sep.view(np.uint8)), (name, rep)
+    counters = ws[-((len(lengths) * Hkv * 4 + 15) // 16 * 16):].cpu().numpy()
+    assert not counters.any(), "counters not back at zero"
+    _, _, expect = oracle_step(batch, 0)
+    assert max_abs_err(got, expect, dtype) <= (BF16_TOL if dtype == "bf16" else F32_TOL)
+
+
+WG_CASES = [
+    # name, dtype, Hq, Hkv, d, bps (per wave), waves per workgroup, merge
+    ("f32_d64_mha_w16", "f32", 12, 12, 64, 2, 16, False),
+    ("f32_d64_mha_w4_merge", "f32", 12, 12, 64, 2, 4, True),
+    ("f32_d128_g4_w8", "f32", 8, 2, 128, 1, 8, True),
+    ("bf16_d128_g8_w8_merge", "bf16", 64, 8, 128, 2, 8, True),
+    ("bf16_d128_mha_w16", "bf16", 4, 4, 128, 2, 16, False),
+    ("bf16_d64_g2_w2", "bf16", 8, 4, 64, 4, 2, False),
+]
+
+
+@pytest.mark.parametrize("case", WG_CASES, ids=[c[0] for c in WG_CASES])
+def test_valu_workgroup_waves(case):
+    """Several waves per workgroup split its blocks and merge through LDS; the
+    workgroup's merged partial then goes to the combine launch or the in-kernel
+    merge. Against the oracle, and (fp32) within 1e-6 of one wave per item."""
+    need_gpu()
+    name, dtype, Hq, Hkv, d, bps, waves, merge = case
+    print_case(test="valu_workgroup_waves", case=name)
+    lengths = RAGGED + [1000, 16 * 40]
+    batch = make_batch(dtype, 1, 700, Hq, Hkv, d, 16, lengths, seed=zlib.crc32(name.encode()) % 10000)
+    got, _, _ = run_library(batch, 0, kernel="valu", bps=bps, merge=merge, waves=waves)
+    _, _, expect = oracle_step(batch, 0)
+    assert max_abs_err(got, expect, dtype) <= (BF16_TOL if dtype == "bf16" else F32_TOL), name
+    one, _, _ = run_library(batch, 0, kernel="valu", bps=bps, merge=merge)
+    if dtype == "f32":
+        assert np.max(np.abs(got.astype(np.float64) - one.astype(np.float64))) <= 1e-6, name
+    again, _, _ = run_library(batch, 0, kernel="valu", bps=bps, merge=merge, waves=waves)
+    assert np.array_equal(got.view(np.uint8), again.view(np.uint8)), name

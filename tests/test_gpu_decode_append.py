@@ -68,7 +68,8 @@ def test_fused_parity(case):
 def test_fused_zero_lengths_write_nothing():
     need_gpu()
     print_case(test="fused_zero_lengths")
-    for kernel, dtype, bps in (("mfma", "bf16", 0), ("mfma", "bf16", 2), ("generic", "f32", 2)):
+    for kernel, dtype, bps in (("mfma", "bf16", 0), ("mfma", "bf16", 2), ("generic", "f32", 2),
+                               ("valu", "f32", 2), ("valu", "bf16", 0)):
         batch = make_batch(dtype, 1, 64, 8, 2, 64 if dtype == "f32" else 128, 16, [0, 40, 0, 70],
                            seed=90)
         out, K, V = run_fused(batch, 0, kernel=kernel, bps=bps)
@@ -82,7 +83,8 @@ def test_fused_single_token_returns_its_value_bitwise():
     """A one-token context attends only to the token written in this call."""
     need_gpu()
     print_case(test="fused_single_token")
-    for kernel, dtype, d in (("mfma", "bf16", 128), ("generic", "f32", 64), ("generic", "bf16", 64)):
+    for kernel, dtype, d in (("mfma", "bf16", 128), ("generic", "f32", 64), ("generic", "bf16", 64),
+                             ("valu", "f32", 64), ("valu", "bf16", 64), ("valu", "f32", 128)):
         batch = make_batch(dtype, 1, 8, 8, 2, d, 16, [1, 1, 1], seed=95)
         out, _, _ = run_fused(batch, 0, kernel=kernel)
         for i in range(3):

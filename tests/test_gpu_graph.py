@@ -1,6 +1,7 @@
 """A whole decode step (every layer's fused append + decode, and the combine
-launches of split plans) captured in a HIP graph and replayed must give the
-same bits as the eager launches, on every replay; likewise one chunked-prefill
+launches of split plans, or the merge inside the decode launch with its
+counters) captured in a HIP graph and replayed must give the same bits as the
+eager launches, on every replay; likewise one chunked-prefill
 call (append through the tables, tile or short-chunk attention, split merge).
 
 Between replays the program does its own eager work on the same stream (an
@@ -18,10 +19,13 @@ from tests.gpu_helpers import make_batch, need_gpu, padded_tables, print_case, t
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # name, dtype, L, N, Hq, Hkv, d, B, lengths, bps, kernel
-    ("mfma_direct", "bf16", 3, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 0, "auto"),
-    ("mfma_split", "bf16", 2, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 4, "mfma"),
-    ("generic_f32_split", "f32", 2, 300, 12, 12, 64, 16, [5, 250, 900, 33], 2, "generic"),
+    # name, dtype, L, N, Hq, Hkv, d, B, lengths, bps, kernel, merge
+    ("mfma_direct", "bf16", 3, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 0, "auto", False),
+    ("mfma_split", "bf16", 2, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 4, "mfma", False),
+    ("generic_f32_split", "f32", 2, 300, 12, 12, 64, 16, [5, 250, 900, 33], 2, "generic", False),
+    ("valu_f32_split", "f32", 2, 300, 12, 12, 64, 16, [5, 250, 900, 33], 2, "valu", False),
+    ("valu_f32_merge", "f32", 2, 300, 12, 12, 64, 16, [5, 250, 900, 33], 2, "valu", True),
+    ("valu_bf16_merge", "bf16", 2, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 4, "valu", True),
 ]
 
 
@@ -32,7 +36,7 @@ def _bits(t):
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_graph_replay_matches_eager(case):
     need_gpu()
-    name, dtype, L, N, Hq, Hkv, d, B, lengths, bps, kernel = case
+    name, dtype, L, N, Hq, Hkv, d, B, lengths, bps, kernel, merge = case
     print_case(test="graph_replay", case=name)
     batch = make_batch(dtype, L, N, Hq, Hkv, d, B, lengths, seed=71, poison=False)
     geom = pk.Geometry(L, Hkv, d, B, N, dtype)
@@ -46,7 +50,7 @@ def test_graph_replay_matches_eager(case):
         tabs = torch.from_numpy(padded_tables(batch.tables, batch.max_blocks)).cuda()
         lens = torch.from_numpy(np.asarray(lengths, np.int32)).cuda()
         max_ctx = max(lengths)
-        ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, bps, kernel)),
+        ws = torch.zeros(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, bps, kernel, merge)),
                          dtype=torch.uint8, device="cuda")
         out_eager = torch.empty_like(q_all)
         out_graph = torch.full_like(q_all, float("nan"))
@@ -54,7 +58,7 @@ def test_graph_replay_matches_eager(case):
 
     def step(out):
         steps.decode_step(geom, K, V, q_all, kn, vn, None, tabs, lens, max_ctx, out, ws,
-                          blocks_per_split=bps, kernel=kernel, stream=s)
+                          blocks_per_split=bps, kernel=kernel, stream=s, merge=merge)
 
     step(out_eager)
     torch.cuda.synchronize()
