@@ -68,9 +68,11 @@ def parse():
                     help="append the step's tokens with a separate launch before each decode")
     ap.add_argument("--wg-waves", type=int, default=0,
                     help="streaming VALU kernel: waves per workgroup (0 = library default)")
-    ap.add_argument("--no-merge", action="store_true",
-                    help="merge decode splits with a separate launch even where the kernel can "
-                         "merge them in its own launch")
+    ap.add_argument("--merge", default="auto", choices=["auto", "on", "off"],
+                    help="merge decode splits inside the decode launch (auto: for the streaming "
+                         "VALU kernel, where it is faster; the MFMA kernels' last split would "
+                         "merge all eight heads serially, slower than the combine launch)")
+    ap.add_argument("--no-merge", action="store_true", help="same as --merge off")
     ap.add_argument("--chunk-blocks", type=int, default=-1,
                     help="offload_overlap: blocks per staging chunk (-1 = the workload's, 0 = library default)")
     ap.add_argument("--move-wgs", type=int, default=0,
@@ -298,7 +300,8 @@ def run_decode(args):
     lens = torch.from_numpy(np.ascontiguousarray(lens_np)).to(dev)
     max_ctx = int(lengths.max())
     out = torch.empty((L, n, Hq, d), dtype=io, device=dev)
-    merge = not args.no_merge
+    valu_path = args.kernel == "valu" or (args.kernel == "auto" and cfg.dtype == "f32")
+    merge = (not args.no_merge and args.merge != "off") and (args.merge == "on" or valu_path)
     ws_bytes = pk.decode_workspace_bytes(geom, n, Hq, max_ctx, args.bps, args.kernel, merge,
                                          args.wg_waves)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)   # merge counters start at 0
@@ -478,8 +481,8 @@ def run_decode(args):
                    "pool_blocks": cfg.num_blocks, "kv_bytes_per_step": kv_bytes_step,
                    "global_batch": n, "seq_len": int(lengths.max()), "parallelism": "none (1 GPU)",
                    "append": "separate launch" if args.unfused else "fused into decode",
-                   "split_merge": "separate launch" if (args.no_merge or "decode_combine" in kernel_ms)
-                   else "inside the decode launch (where splits exist)",
+                   "split_merge": "inside the decode launch (where splits exist)" if merge
+                   else "separate launch",
                    "launch": "hip graph replay" if args.graph else "eager"},
         "step_ms": step_ms,
         "tokens_per_s": round(n / (ms_per_step * 1e-3), 2),

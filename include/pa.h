@@ -151,8 +151,8 @@ typedef struct {
                                loads so repeats hit in L2 / Infinity Cache (MFMA kernel) */
   int32_t merge;            /* 0: split partials are merged by a second launch; 1: merged inside
                                the decode launch by the last split of each (sequence, KV head) to
-                               finish (streaming VALU kernel; other kernels keep the second
-                               launch). The workspace then ends with one int32 counter per
+                               finish (MFMA and streaming VALU kernels; the generic kernel keeps
+                               the second launch). The workspace then ends with one int32 counter per
                                (sequence, KV head), which must be zero before the workspace's
                                first such call (allocate it zeroed); every call leaves them zero.
                                Two calls sharing a workspace must not overlap. */

@@ -344,7 +344,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, int64_t layer_off, int N, int Hkv, int Hq, int G,
-    int max_blocks, int max_ctx, int bps, int S_max, float qk_scale) {
+    int max_blocks, int max_ctx, int bps, int S_max, float qk_scale, int* __restrict__ counters) {
   constexpr int KC = D / 32;
   constexpr int DT = D / 16;
 
@@ -363,7 +363,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const int h = g * G + c;
   const bool qvalid = c < G;
   if (b0 >= nblk) {
-    if (DIRECT && len == 0 && qvalid) {
+    // an empty sequence writes zeros (without a combine launch, by its split 0)
+    if ((DIRECT || counters) && len == 0 && s == 0 && qvalid) {
       uint16_t* o = out + ((int64_t)i * Hq + h) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -444,27 +445,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   }
 
   l_run = sum_over_groups(l_run);
-  if (!qvalid) return;
-  if (DIRECT) {
-    const float inv = 1.f / l_run;
-    uint16_t* o = out + ((int64_t)i * Hq + h) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) =
-          make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
-                     pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
-  } else {
-    const int64_t row = ((int64_t)i * Hq + h) * S_max + s;
-    float* po = part_o + row * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * gq) =
-          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (gq == 0) {
-      part_ml[row * 2 + 0] = m_run;
-      part_ml[row * 2 + 1] = l_run;
-    }
-  }
+  mfma_split_epilogue<D>(acc, m_run, l_run, lane, i, g, G, Hq, Hkv, s, S_max, (nblk + bps - 1) / bps,
+                         DIRECT, out, part_o, part_ml, counters);
 }
 
 }  // namespace pa_detail

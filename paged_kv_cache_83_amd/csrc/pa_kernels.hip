@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, int64_t layer_off, int N, int Hkv, int Hq, int G,
-    int max_blocks, int max_ctx, int bps, int S_max, float qk_scale) {
+    int max_blocks, int max_ctx, int bps, int S_max, float qk_scale, int* __restrict__ counters) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int DT = MfmaCfg<D>::DT;
 
@@ -188,7 +188,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
   const int h = g * G + c;
   const bool qvalid = c < G;
   if (b0 >= nblk) {
-    if (DIRECT && len == 0 && qvalid) {
+    // an empty sequence writes zeros (without a combine launch, by its split 0)
+    if ((DIRECT || counters) && len == 0 && s == 0 && qvalid) {
       uint16_t* o = out + ((int64_t)i * Hq + h) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -312,28 +313,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
   }
 
   l_run = sum_over_groups(l_run);
-  if (!qvalid) return;
   // acc[dt][e] = O^T[d = 16*dt + 4*gq + e][q = c]
-  if (DIRECT) {
-    const float inv = 1.f / l_run;
-    uint16_t* o = out + ((int64_t)i * Hq + h) * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) =
-          make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
-                     pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
-  } else {
-    const int64_t row = ((int64_t)i * Hq + h) * S_max + s;
-    float* po = part_o + row * D;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<float4*>(po + 16 * dt + 4 * gq) =
-          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    if (gq == 0) {
-      part_ml[row * 2 + 0] = m_run;
-      part_ml[row * 2 + 1] = l_run;
-    }
-  }
+  mfma_split_epilogue<D>(acc, m_run, l_run, lane, i, g, G, Hq, Hkv, s, S_max, (nblk + bps - 1) / bps,
+                         DIRECT, out, part_o, part_ml, counters);
 }
 
 // =============================================================================
@@ -653,7 +635,7 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
   plan->wg_waves = (int)W;
   plan->S_max = (int)S;
   plan->direct = S == 1;
-  plan->merge = !plan->direct && opts && opts->merge == 1 && k == 4;
+  plan->merge = !plan->direct && opts && opts->merge == 1 && k >= 2;   // not the generic kernel
   const size_t parts = plan->direct ? 0 : (size_t)n_seqs * Hq * S * (D + 2) * sizeof(float);
   plan->counters_off = parts;
   plan->ws = parts + (plan->merge ? ((size_t)n_seqs * g->num_kv_heads * sizeof(int32_t) + 15) / 16 * 16 : 0);
@@ -793,7 +775,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
                      (const uint8_t*)k_pool, (const uint8_t*)v_pool, (const uint16_t*)q,            \
                      (uint16_t*)out, part_o, part_ml, block_tables, context_lens, off8,           \
                      g->num_blocks, Hkv, n_q_heads, G, max_blocks_per_seq, max_context_len,       \
-                     plan.bps, plan.S_max, qk_scale)
+                     plan.bps, plan.S_max, qk_scale, counters)
 #define PA_FP8_LAUNCH(DD, DIR)                                   \
   do {                                                           \
     if (plan.stream_kv) PA_FP8_LAUNCH_X(DD, DIR, true);          \
@@ -813,7 +795,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
                      (const uint16_t*)knew, (const uint16_t*)vnew, (uint16_t*)out, part_o,         \
                      part_ml, block_tables, context_lens, layer_off, g->num_blocks, Hkv,          \
                      n_q_heads, G, max_blocks_per_seq, max_context_len, plan.bps, plan.S_max,      \
-                     qk_scale)
+                     qk_scale, counters)
 #define PA_MFMA_LAUNCH_NT(DD, DIR, NTV)                     \
   do {                                                      \
     if (append) PA_MFMA_LAUNCH_X(DD, DIR, NTV, true);       \

@@ -80,4 +80,74 @@ __device__ __forceinline__ void issue_pair(PairFrags<D>& f, const uint16_t* __re
   for (int dt = 0; dt < DT; ++dt) f.v[dt] = kv_load16<NT>(vrow + dt * 256 + v_off);
 }
 
+// End of a matrix-core decode work item (sequence i, KV head g, split s). Lane
+// (c = lane % 16, gq = lane / 16) holds O^T[d = 16*dt + 4*gq + e][query c] in
+// acc[dt][e] for query head h = g*G + c (valid for c < G), and the split's
+// (m, l) for that head (l already summed over the lane groups). A split that
+// covers the sequence (direct plan, or a one-split sequence when counters are
+// given) writes the normalised output; otherwise the split's partial row goes
+// to the workspace -- with counters as coherent stores, after which the last
+// split of (i, g) to finish merges every row of the group (the in-kernel merge
+// of "KV Cache Management", section "Chunked prefill mechanics"). Called by the
+// whole wave.
+template <int D>
+__device__ __forceinline__ void mfma_split_epilogue(const f32x4 (&acc)[D / 16], float m_run,
+                                                    float l_run, int lane, int i, int g, int G,
+                                                    int Hq, int Hkv, int s, int S_max, int ns,
+                                                    bool direct, uint16_t* __restrict__ out,
+                                                    float* __restrict__ part_o,
+                                                    float* __restrict__ part_ml,
+                                                    int* __restrict__ counters) {
+  constexpr int DT = D / 16;
+  const int c = lane & 15;
+  const int gq = lane >> 4;
+  const int h = g * G + c;
+  const bool qvalid = c < G;
+  if (direct || (counters && ns == 1)) {
+    if (!qvalid) return;
+    const float inv = 1.f / l_run;
+    uint16_t* o = out + ((int64_t)i * Hq + h) * D;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) =
+          make_uint2(pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv),
+                     pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv));
+    return;
+  }
+  const int64_t row = ((int64_t)i * Hq + (qvalid ? h : g * G)) * S_max + s;
+  float* po = part_o + row * D;
+  if (!counters) {
+    if (!qvalid) return;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<float4*>(po + 16 * dt + 4 * gq) =
+          make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
+    if (gq == 0) {
+      part_ml[row * 2 + 0] = m_run;
+      part_ml[row * 2 + 1] = l_run;
+    }
+    return;
+  }
+  if (qvalid) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) part_st_coherent(po + 16 * dt + 4 * gq + e, acc[dt][e]);
+    if (gq == 0) {
+      part_st_coherent(part_ml + row * 2 + 0, m_run);
+      part_st_coherent(part_ml + row * 2 + 1, l_run);
+    }
+  }
+  if (split_arrive_last(counters + (int64_t)i * Hkv + g, ns, lane)) {
+#pragma unroll 1
+    for (int t = 0; t < G; ++t) {
+      const int64_t row0 = ((int64_t)i * Hq + g * G + t) * S_max;
+      merge_split_row<uint16_t, true>(part_o + row0 * D, part_ml + row0 * 2, ns, D,
+                                      out + ((int64_t)i * Hq + g * G + t) * D, lane);
+    }
+    if (lane == 0) __hip_atomic_store(counters + (int64_t)i * Hkv + g, 0, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
 }  // namespace pa_detail

@@ -151,7 +151,8 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
   const int nblk = (len + 15) >> 4;
   const int B0 = s * bps;
   if (B0 >= nblk) {   // the whole workgroup (uniform)
-    if (direct && len == 0) {
+    // an empty sequence writes zeros (without a combine launch, by its split 0)
+    if ((direct || counters) && len == 0 && s == 0) {
       T* o = out + ((int64_t)i * Hq + (int64_t)g * G) * D;
       for (int e = threadIdx.x; e < G * D; e += blockDim.x) o[e] = from_f32<T>(0.f);
     }

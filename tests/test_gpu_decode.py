@@ -231,11 +231,17 @@ def test_kv_reuse_policy_same_result():
 
 
 MERGE_CASES = [
-    # name, dtype, Hq, Hkv, d, bps, lengths
-    ("f32_d64_mha_bps2", "f32", 12, 12, 64, 2, RAGGED),
-    ("f32_d128_g4_bps4", "f32", 8, 2, 128, 4, RAGGED + [1000]),
-    ("bf16_d128_g8_bps2", "bf16", 64, 8, 128, 2, RAGGED),
-    ("bf16_d64_g2_auto", "bf16", 8, 4, 64, 0, RAGGED + [3000, 16 * 64 * 3 + 5]),
+    # name, dtype, Hq, Hkv, d, bps, lengths, kernel
+    ("f32_d64_mha_bps2", "f32", 12, 12, 64, 2, RAGGED, "valu"),
+    ("f32_d128_g4_bps4", "f32", 8, 2, 128, 4, RAGGED + [1000], "valu"),
+    ("bf16_d128_g8_bps2", "bf16", 64, 8, 128, 2, RAGGED, "valu"),
+    ("bf16_d64_g2_auto", "bf16", 8, 4, 64, 0, RAGGED + [3000, 16 * 64 * 3 + 5], "valu"),
+    ("f32_d64_g2_empty", "f32", 6, 3, 64, 2, [0, 40, 0, 300, 1], "valu"),
+    ("mfma_d128_g4_empty", "bf16", 16, 4, 128, 2, [0, 40, 0, 300, 1], "mfma"),
+    ("mfma_d128_g8_bps2", "bf16", 64, 8, 128, 2, RAGGED, "mfma"),
+    ("mfma_d128_g4_auto", "bf16", 32, 8, 128, 0, RAGGED + [3000, 16 * 64 * 3 + 5], "mfma"),
+    ("mfma_d64_g16_bps4", "bf16", 32, 2, 64, 4, RAGGED + [1000], "mfma"),
+    ("mfma_d256_g2_bps6", "bf16", 4, 2, 256, 6, RAGGED, "mfma"),
 ]
 
 
@@ -247,16 +253,16 @@ def test_in_kernel_merge(case):
     counters are back at zero after each one; one-split sequences are written
     directly."""
     need_gpu()
-    name, dtype, Hq, Hkv, d, bps, lengths = case
+    name, dtype, Hq, Hkv, d, bps, lengths, kernel = case
     print_case(test="in_kernel_merge", case=name)
     batch = make_batch(dtype, 1, 700, Hq, Hkv, d, 16, lengths, seed=zlib.crc32(name.encode()) % 10000)
-    sep, _, _ = run_library(batch, 0, kernel="valu", bps=bps)
+    sep, _, _ = run_library(batch, 0, kernel=kernel, bps=bps)
     geom = pk.Geometry(1, Hkv, d, 16, 700, dtype)
-    need = pk.decode_workspace_bytes(geom, len(lengths), Hq, int(max(lengths)), bps, "valu", True)
-    assert need >= pk.decode_workspace_bytes(geom, len(lengths), Hq, int(max(lengths)), bps, "valu")
+    need = pk.decode_workspace_bytes(geom, len(lengths), Hq, int(max(lengths)), bps, kernel, True)
+    assert need >= pk.decode_workspace_bytes(geom, len(lengths), Hq, int(max(lengths)), bps, kernel)
     ws = torch.zeros(max(1, need), dtype=torch.uint8, device="cuda")
     for rep in range(3):
-        got, _, _ = run_library(batch, 0, kernel="valu", bps=bps, merge=True, ws=ws)
+        got, _, _ = run_library(batch, 0, kernel=kernel, bps=bps, merge=True, ws=ws)
         assert np.array_equal(got.view(np.uint8), sep.view(np.uint8)), (name, rep)
     counters = ws[-((len(lengths) * Hkv * 4 + 15) // 16 * 16):].cpu().numpy()
     assert not counters.any(), "counters not back at zero"

@@ -10,6 +10,8 @@ head): rows here carry magnitudes 10**U(-1, 1) (one case 10**U(-4, 4)), and a
 bf16 output keeps about 2**-9 of its magnitude. Unused slots hold NaN codes and scale
 byte 0xFF, which the kernels must never let into a result.
 """
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -122,7 +124,7 @@ def make_decode_case(Hq, Hkv, d, lengths, seed, N=None, L=2, decades=1.0):
                 kp=kp, vp=vp, q=q)
 
 
-def run_decode(c, layer, bps=0, kv_reuse=False, K=None, V=None, tables=None):
+def run_decode(c, layer, bps=0, kv_reuse=False, K=None, V=None, tables=None, merge=False, ws=None):
     geom = pk.Geometry(c["L"], c["Hkv"], c["d"], c["B"], c["N"], "fp8")
     K = to_dev(c["kp"], "fp8") if K is None else K
     V = to_dev(c["vp"], "fp8") if V is None else V
@@ -132,11 +134,12 @@ def run_decode(c, layer, bps=0, kv_reuse=False, K=None, V=None, tables=None):
     max_ctx = int(max(c["lengths"].max(), 1))
     q = to_dev(c["q"], "bf16")
     out = torch.full_like(q, float("nan"))
-    ws_bytes = pk.decode_workspace_bytes(geom, n, c["Hq"], max_ctx, bps)
-    ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws_bytes = pk.decode_workspace_bytes(geom, n, c["Hq"], max_ctx, bps, merge=merge)
+        ws = torch.zeros(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
     pk.decode(geom, K, V, layer, q, out, torch.from_numpy(padded_tables(tabs, mb)).cuda(),
               torch.from_numpy(c["lengths"].astype(np.int32)).cuda(), max_ctx, workspace=ws,
-              blocks_per_split=bps, kv_reuse=kv_reuse)
+              blocks_per_split=bps, kv_reuse=kv_reuse, merge=merge)
     torch.cuda.synchronize()
     return to_host(out, "bf16")
 
@@ -296,3 +299,22 @@ def test_fp8_unsupported_geometries():
         pk.prefill(geom8, K8, V8, 0, q, kn, kn, torch.empty_like(q),
                    torch.tensor([0, 1], dtype=torch.int32, device="cuda"), tab,
                    torch.zeros(1, dtype=torch.int32, device="cuda"), 1, 1)
+
+
+def test_fp8_in_kernel_merge_same_bits():
+    """FP8 decode with the splits merged inside the launch gives the bits of the
+    separate combine launch, call after call on one zeroed workspace."""
+    need_gpu()
+    print_case(test="fp8_in_kernel_merge")
+    for name, Hq, Hkv, d, lengths, bps, dec in DECODE_CASES:
+        if bps == 0:
+            continue
+        c = make_decode_case(Hq, Hkv, d, lengths, seed=zlib.crc32(name.encode()) % 10000, decades=dec)
+        sep = run_decode(c, 0, bps=bps)
+        geom = pk.Geometry(c["L"], Hkv, d, c["B"], c["N"], "fp8")
+        need = pk.decode_workspace_bytes(geom, len(lengths), Hq, int(max(max(lengths), 1)), bps,
+                                         merge=True)
+        ws = torch.zeros(max(1, need), dtype=torch.uint8, device="cuda")
+        for rep in range(2):
+            got = run_decode(c, 0, bps=bps, merge=True, ws=ws)
+            assert np.array_equal(got.view(np.uint8), sep.view(np.uint8)), (name, rep)

@@ -26,6 +26,7 @@ CASES = [
     ("valu_f32_split", "f32", 2, 300, 12, 12, 64, 16, [5, 250, 900, 33], 2, "valu", False),
     ("valu_f32_merge", "f32", 2, 300, 12, 12, 64, 16, [5, 250, 900, 33], 2, "valu", True),
     ("valu_bf16_merge", "bf16", 2, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 4, "valu", True),
+    ("mfma_merge", "bf16", 2, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 4, "mfma", True),
 ]
 
 
