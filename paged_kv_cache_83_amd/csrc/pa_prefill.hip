@@ -41,6 +41,7 @@
 
 #include "../../include/pa.h"
 #include "pa_append.h"
+#include "pa_addr.h"
 #include "pa_device.h"
 #include "pa_fp8.h"
 #include "pa_pairs.h"
@@ -225,12 +226,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       // The base is uniform; pinning it to scalar registers lets the load take
       // it as its scalar base with the lane's 16-byte offset, instead of a
       // 64-bit vector address computed per load.
-      // (readfirstlane returns a signed int: both halves are widened as
-      // unsigned 32-bit words, so the low word is not sign-extended.)
+      // (readfirstlane returns a signed int: join_address_words widens both
+      // halves as unsigned 32-bit words, so the low word is not sign-extended.)
       const uint64_t bu = reinterpret_cast<uint64_t>(base);
       const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32));
       const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu);
-      const uint64_t bs = ((uint64_t)bhi << 32) | (uint64_t)blo;
+      const uint64_t bs = join_address_words(bhi, blo);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(bs) + lane * 16,
                                        (__attribute__((address_space(3))) void*)(img + woff), 16,
                                        0, 0);

@@ -293,3 +293,62 @@ def test_prefill_random_batches(seed):
     assert np.isfinite(olayout.widen(out[:rows], "bf16")).all()
     err = max_abs_err(out, expect, "bf16")
     assert err <= BF16_TOL, (seed, err)
+
+
+def test_large_pool_high_address_tiles():
+    """Prefill tiles read from blocks of a pool larger than 4 GiB per array whose
+    addresses have bit 31 set in their low 32-bit word (and lie past the first
+    4 GiB): the tile kernel's scalar load bases are built from the two words of
+    such addresses. The blocks of a small batch are placed there; outputs and
+    written blocks equal the same batch on a small pool bit for bit, and the
+    oracle within the bf16 tolerance."""
+    need_gpu()
+    print_case(test="prefill_large_pool")
+    Hq, Hkv, d, B = 16, 2, 128, 16
+    b = make_prefill_batch(Hq, Hkv, d, [300, 0, 700], [40, 130, 33], seed=4242)
+    out_small, k_small, v_small = run_prefill(b)
+    tile = B * d * 2                       # bytes of one (block, head) tile, bf16
+    blk = Hkv * tile                       # bytes of one block of one pool array
+    N_big = (9 << 29) // blk               # 4.5 GiB per pool array
+    geom = pk.Geometry(1, Hkv, d, B, N_big, "bf16")
+    K = torch.empty(geom.k_pool_shape, dtype=torch.bfloat16, device="cuda")
+    V = torch.empty(geom.v_pool_shape, dtype=torch.bfloat16, device="cuda")
+    kb, vb = K.data_ptr(), V.data_ptr()
+    # physical ids: half whose K tiles start with bit 31 of the low word set, half
+    # whose V tiles do; all past the first 4 GiB of the array
+    first = (4 << 30) // blk + 1
+    hi_k = [p for p in range(first, N_big) if ((kb + p * blk) & 0xFFFFFFFF) >= 0x80000000
+            and ((kb + p * blk + blk - 1) & 0xFFFFFFFF) >= 0x80000000]
+    hi_v = [p for p in range(first, N_big) if ((vb + p * blk) & 0xFFFFFFFF) >= 0x80000000
+            and ((vb + p * blk + blk - 1) & 0xFFFFFFFF) >= 0x80000000]
+    rng = np.random.default_rng(77)
+    n_local = b["N"]
+    picks = list(rng.choice(hi_k, size=n_local // 2, replace=False))
+    rest = [p for p in hi_v if p not in set(picks)]
+    picks += list(rng.choice(rest, size=n_local - len(picks), replace=False))
+    phys = np.asarray(picks, np.int64)
+    assert len(set(phys.tolist())) == n_local
+    ids = torch.from_numpy(phys).cuda()
+    K[0].index_copy_(0, ids, to_dev(b["kp"], "bf16")[0])
+    V[0].index_copy_(0, ids, to_dev(b["vp"], "bf16")[0])
+    tabs = [[int(phys[x]) for x in t] for t in b["tables"]]
+    q = to_dev(b["q"], "bf16")
+    out = torch.full_like(q, float("nan"))
+    max_ctx = int(max(int(c) + int(ql) for c, ql in zip(b["ctx"], b["qlens"])))
+    pk.prefill(geom, K, V, 0, q, to_dev(b["kn"], "bf16"), to_dev(b["vn"], "bf16"), out,
+               torch.from_numpy(b["q_start"]).cuda(),
+               torch.from_numpy(padded_tables(tabs, max(len(t) for t in tabs))).cuda(),
+               torch.from_numpy(b["ctx"]).cuda(), int(max(b["qlens"])), max_ctx, splits=1)
+    torch.cuda.synchronize()
+    got = to_host(out, "bf16")
+    assert np.array_equal(got.view(np.uint8), out_small.view(np.uint8))
+    k_back = to_host(K[0].index_select(0, ids), "bf16")
+    v_back = to_host(V[0].index_select(0, ids), "bf16")
+    assert np.array_equal(k_back.view(np.uint8), k_small[0].view(np.uint8))
+    assert np.array_equal(v_back.view(np.uint8), v_small[0].view(np.uint8))
+    ek, ev, expect = oracle_prefill(b)
+    assert np.array_equal(k_back.view(np.uint8), ek[0].view(np.uint8))
+    assert np.array_equal(v_back.view(np.uint8), ev[0].view(np.uint8))
+    assert max_abs_err(got, expect, "bf16") <= BF16_TOL
+    del K, V
+    torch.cuda.empty_cache()
