@@ -203,6 +203,24 @@ pa_status pa_decode_append(const pa_geom* g, void* k_pool, void* v_pool, int32_t
                            int32_t max_context_len, float scale, const pa_decode_opts* opts,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the same
+ * decode step as pa_decode_append, with the split partials in a file-scope
+ * device array of the library (16 MiB = 16777216 bytes per GPU, held until the
+ * process ends) instead of a caller workspace. It allocates nothing and records
+ * no timing events; the partials are merged by the combine launch (opts->merge
+ * is ignored). A launch plan whose partials need more than 16 MiB (see
+ * pa_decode_workspace_bytes with merge = 0) returns PA_ERR_WORKSPACE before
+ * anything is launched. Every call on one GPU shares that GPU's array: calls
+ * that overlap on one GPU (other streams, other threads) race and must not be
+ * issued. */
+pa_status pa_decode_append_noalloc(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer,
+                                   const void* q, const void* k_new, const void* v_new, void* out,
+                                   int32_t n_seqs, int32_t n_q_heads, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t max_context_len, float scale,
+                                   const pa_decode_opts* opts, void* stream);
+
 /* Chunked-prefill (multi-query) paged attention, one layer. Source: "KV Cache
  * Management", section "Chunked prefill mechanics": the queries of a chunk
  * attend over every cached token of their sequence and, inside the chunk, over

@@ -56,6 +56,8 @@ SIGNATURES = {
                          _popts, _vp, _sz, _vp]),
     "pa_decode_append": (_i32, [_pg, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp, _i32,
                                 _vp, _i32, _f32, _popts, _vp, _sz, _vp]),
+    "pa_decode_append_noalloc": (_i32, [_pg, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
+                                        _i32, _vp, _i32, _f32, _popts, _vp]),
     "pa_prefill": (_i32, [_pg, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp,
                           _i32, _vp, _i32, _i32, _f32, _i32, _vp, _sz, _vp]),
     "pa_prefill_workspace_bytes": (_sz, [_pg, _i32, _i32, _i32, _i32, _i32, _i32]),

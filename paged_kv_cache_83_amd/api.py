@@ -172,7 +172,7 @@ def decode_workspace_bytes(geom: Geometry, n_seqs: int, n_q_heads: int, max_cont
 
 
 def _decode_args(geom: Geometry, k_pool, v_pool, q, out, block_tables, context_lens,
-                 max_context_len, workspace, o):
+                 max_context_len, workspace, o, need_workspace: bool = True):
     _dev(k_pool, "k_pool", geom.torch_dtype, geom.pool_numel)
     _dev(v_pool, "v_pool", geom.torch_dtype, geom.pool_numel)
     if q.dim() != 3 or q.shape[2] != geom.head_dim:
@@ -185,6 +185,8 @@ def _decode_args(geom: Geometry, k_pool, v_pool, q, out, block_tables, context_l
     _dev(block_tables, "block_tables", torch.int32)
     _dev(context_lens, "context_lens", torch.int32, n)
     g = geom.c()
+    if not need_workspace:
+        return g, n, hq, None, 0
     need = int(_L().pa_decode_workspace_bytes(C.byref(g), n, hq, max_context_len, C.byref(o)))
     ws_ptr, ws_bytes = None, 0
     if need:
@@ -232,6 +234,31 @@ def decode_append(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, o
                                 int(max_context_len), float(scale), C.byref(o), ws_ptr, ws_bytes,
                                 _stream(stream, q.device)),
           "pa_decode_append")
+
+
+# Bytes of the library's own partials array behind decode_append_noalloc.
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_append_noalloc(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out,
+                          block_tables, context_lens, max_context_len: int, scale: float = 0.0,
+                          blocks_per_split: int = 0, kernel: str = "auto", stream=None,
+                          kv_reuse: bool = False):
+    """decode_append with the split partials in the library's own device array
+    (NOALLOC_SCRATCH_BYTES per GPU) instead of a workspace: no allocation, for
+    callers that cannot allocate. Calls that overlap on one GPU race."""
+    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse)
+    g, n, hq, _, _ = _decode_args(geom, k_pool, v_pool, q, out, block_tables, context_lens,
+                                  max_context_len, None, o, need_workspace=False)
+    per = geom.num_kv_heads * geom.head_dim
+    _dev(k_new, "k_new", geom.io_dtype, n * per)
+    _dev(v_new, "v_new", geom.io_dtype, n * per)
+    check(_L().pa_decode_append_noalloc(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(q),
+                                        _ptr(k_new), _ptr(v_new), _ptr(out), n, hq,
+                                        _ptr(block_tables), int(block_tables.shape[1]),
+                                        _ptr(context_lens), int(max_context_len), float(scale),
+                                        C.byref(o), _stream(stream, q.device)),
+          "pa_decode_append_noalloc")
 
 
 def prefill_workspace_bytes(geom: Geometry, n_seqs: int, n_tokens: int, n_q_heads: int,

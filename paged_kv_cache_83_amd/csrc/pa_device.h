@@ -240,13 +240,14 @@ inline int64_t tile_bytes(const pa_geom* g) {
 
 inline pa_status launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
-// Records hipEvents around one launch when timing is on (pa_prof_enable).
+// Records hipEvents around one launch when timing is on (pa_prof_enable) and
+// `allowed` (the allocation-free entry point creates no events).
 struct ProfScope {
   const char* name;
   hipStream_t st;
   hipEvent_t a = nullptr, b = nullptr;
   bool on;
-  ProfScope(const char* n, hipStream_t s);
+  ProfScope(const char* n, hipStream_t s, bool allowed = true);
   ~ProfScope();
 };
 

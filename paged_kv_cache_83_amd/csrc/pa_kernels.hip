@@ -645,7 +645,8 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
 }  // namespace
 
 namespace pa_detail {
-ProfScope::ProfScope(const char* n, hipStream_t s) : name(n), st(s), on(false) {
+ProfScope::ProfScope(const char* n, hipStream_t s, bool allowed) : name(n), st(s), on(false) {
+  if (!allowed) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
   if (hipEventCreate(&a) != hipSuccess) return;
@@ -732,7 +733,8 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
                              int32_t n_seqs, int32_t n_q_heads, const int32_t* block_tables,
                              int32_t max_blocks_per_seq, const int32_t* context_lens,
                              int32_t max_context_len, float scale, const pa_decode_opts* opts,
-                             void* workspace, size_t workspace_bytes, void* stream) {
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             bool timing = true) {
   DecodePlan plan;
   pa_status st0 = make_plan(g, n_seqs, n_q_heads, max_context_len, opts, &plan);
   if (st0 != PA_OK) return st0;
@@ -755,7 +757,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   float* part_ml = plan.direct ? nullptr : part_o + (size_t)n_seqs * n_q_heads * plan.S_max * D;
   int* counters = plan.merge ? (int*)((char*)workspace + plan.counters_off) : nullptr;
   if (plan.kernel == 3 && append) {  // FP8: quantize the step's tokens into the pool first
-    ProfScope ps("append", st);
+    ProfScope ps("append", st, timing);
     if (!launch_append_fp8(st, (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)knew,
                            (const uint16_t*)vnew,
                            SlotsFromLens{block_tables, context_lens, max_blocks_per_seq,
@@ -766,7 +768,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   {
-    ProfScope ps("decode_partial", st);
+    ProfScope ps("decode_partial", st, timing);
     const dim3 grid((unsigned)items), block(64);
     if (plan.kernel == 3) {
       const int64_t off8 = (int64_t)layer * g->num_blocks * Hkv * tile_bytes(g);
@@ -877,7 +879,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   if (!plan.direct && !plan.merge) {
-    ProfScope ps("decode_combine", st);
+    ProfScope ps("decode_combine", st, timing);
     const dim3 grid((unsigned)((int64_t)n_seqs * n_q_heads)), block(64);
     if (g->dtype == PA_F32)  // bf16 output for bf16 and fp8 pools
       hipLaunchKernelGGL((decode_combine_kernel<float>), grid, block, 0, st, part_o, part_ml,
@@ -891,6 +893,36 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   }
   return PA_OK;
 }
+
+// Split partials of the allocation-free decode entry point: a file-scope
+// device array (one copy per GPU, kept until the process ends). Host code uses
+// the address hipGetSymbolAddress gives on each device, never the name.
+constexpr size_t kDecodeScratchBytes = 16u << 20;
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_dev;   // device id -> address of `scratch` there
+
+// Address of this device's copy of `scratch`, looked up on the first call made
+// with the device current.
+pa_status decode_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return PA_ERR_HIP;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_dev.size()) g_scratch_dev.resize(dev + 1, nullptr);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return PA_ERR_HIP;
+    }
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return PA_OK;
+}
+}  // namespace
 
 extern "C" {
 
@@ -915,6 +947,31 @@ pa_status pa_decode_append(const pa_geom* g, void* k_pool, void* v_pool, int32_t
   return decode_impl(g, k_pool, v_pool, layer, q, k_new, v_new, out, n_seqs, n_q_heads,
                      block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, opts,
                      workspace, workspace_bytes, stream);
+}
+
+pa_status pa_decode_append_noalloc(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer,
+                                   const void* q, const void* k_new, const void* v_new, void* out,
+                                   int32_t n_seqs, int32_t n_q_heads, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                   int32_t max_context_len, float scale,
+                                   const pa_decode_opts* opts, void* stream) {
+  if (n_seqs > 0 && (!k_new || !v_new)) return PA_ERR_INVALID_ARG;
+  // the combine launch merges the splits (the in-kernel merge's counters would
+  // have to start at zero), and no timing events are created
+  pa_decode_opts o = opts ? *opts : pa_decode_opts{};
+  o.merge = 0;
+  DecodePlan plan;
+  const pa_status st0 = make_plan(g, n_seqs, n_q_heads, max_context_len, &o, &plan);
+  if (st0 != PA_OK) return st0;
+  if (plan.ws > kDecodeScratchBytes) return PA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.ws > 0) {
+    const pa_status st1 = decode_scratch(&ws);
+    if (st1 != PA_OK) return st1;
+  }
+  return decode_impl(g, k_pool, v_pool, layer, q, k_new, v_new, out, n_seqs, n_q_heads,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, &o, ws,
+                     plan.ws > 0 ? kDecodeScratchBytes : 0, stream, /*timing=*/false);
 }
 
 static pa_status block_move(int mode, const char* name, const pa_geom* g, void* k_pool,
