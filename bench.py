@@ -73,6 +73,8 @@ def parse():
                          "VALU kernel, where it is faster; the MFMA kernels' last split would "
                          "merge all eight heads serially, slower than the combine launch)")
     ap.add_argument("--no-merge", action="store_true", help="same as --merge off")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="do not give the library the host copy of the lengths (no ragged plan)")
     ap.add_argument("--chunk-blocks", type=int, default=-1,
                     help="offload_overlap: blocks per staging chunk (-1 = the workload's, 0 = library default)")
     ap.add_argument("--move-wgs", type=int, default=0,
@@ -302,8 +304,9 @@ def run_decode(args):
     out = torch.empty((L, n, Hq, d), dtype=io, device=dev)
     valu_path = args.kernel == "valu" or (args.kernel == "auto" and cfg.dtype == "f32")
     merge = (not args.no_merge and args.merge != "off") and (args.merge == "on" or valu_path)
+    host_lens = None if args.no_ragged else np.asarray(lens_np, np.int32)
     ws_bytes = pk.decode_workspace_bytes(geom, n, Hq, max_ctx, args.bps, args.kernel, merge,
-                                         args.wg_waves)
+                                         args.wg_waves, host_lens)
     ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)   # merge counters start at 0
     torch.cuda.synchronize()
 
@@ -330,7 +333,7 @@ def run_decode(args):
         steps.decode_step(geom, k_pool, v_pool, q_all, k_new, v_new, slots, tables, lens, max_ctx, out,
                           ws, blocks_per_split=args.bps, kernel=args.kernel, stream=stream,
                           around_decode=around, fused=not args.unfused, merge=merge,
-                          waves_per_group=args.wg_waves)
+                          waves_per_group=args.wg_waves, host_lens=host_lens)
 
     for _ in range(args.warmup):
         step()
@@ -375,7 +378,7 @@ def run_decode(args):
             eb = geom.elem_bytes
             ib = 2 if fp8 else eb                                                # q / out element bytes
             splits = max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, args.bps, args.kernel,
-                                                      False, args.wg_waves)
+                                                      False, args.wg_waves, host_lens)
                          // (n * Hq * (d + 2) * 4)) if ws_bytes else 1
             per_launch = (int(lengths.sum()) * 2 * Hkv * (d * eb + (1 if fp8 else 0))  # K and V (+ scales)
                           + n * Hq * d * ib                                      # queries

@@ -156,6 +156,13 @@ typedef struct {
                                (sequence, KV head), which must be zero before the workspace's
                                first such call (allocate it zeroed); every call leaves them zero.
                                Two calls sharing a workspace must not overlap. */
+  const int32_t* host_context_lens; /* optional host copy of context_lens ([n_seqs], equal to
+                               the device array; NULL = not given). With it the MFMA bf16
+                               kernel takes a ragged plan when the lengths are uneven (the
+                               longest above 1.5x the mean): only sequences longer than an item
+                               size cut into items, the items listed longest first (with
+                               blocks_per_split > 0, that item size and the list always). A host
+                               copy shorter than the device lengths leaves outputs incomplete. */
   int32_t waves_per_group;  /* streaming VALU kernel: waves per workgroup, which split the
                                workgroup's blocks and merge in LDS (0 = choose; capped at 16 for
                                one query head per KV head with 256-byte rows, else 8) */

@@ -33,7 +33,8 @@ class pa_swap_opts(C.Structure):
 
 class pa_decode_opts(C.Structure):
     _fields_ = [("blocks_per_split", C.c_int32), ("kernel", C.c_int32), ("kv_reuse", C.c_int32),
-                ("merge", C.c_int32), ("waves_per_group", C.c_int32)]
+                ("merge", C.c_int32), ("host_context_lens", C.c_void_p),
+                ("waves_per_group", C.c_int32)]
 
 
 _i32, _i64, _f32, _f64 = C.c_int32, C.c_int64, C.c_float, C.c_double

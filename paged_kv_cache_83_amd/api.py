@@ -152,9 +152,22 @@ def append_kv(geom: Geometry, k_pool, v_pool, layer: int, k_new, v_new, slot_map
 
 
 def _opts(blocks_per_split: int, kernel: int, kv_reuse: bool = False,
-          merge: bool = False, waves_per_group: int = 0) -> _lib.pa_decode_opts:
+          merge: bool = False, waves_per_group: int = 0, host_lens=None) -> _lib.pa_decode_opts:
+    """pa_decode_opts; host_lens (a C-contiguous int32 numpy array, kept alive by
+    the caller for the call) is the host copy of context_lens."""
     return _lib.pa_decode_opts(int(blocks_per_split), int(kernel), 1 if kv_reuse else 0,
-                               1 if merge else 0, int(waves_per_group))
+                               1 if merge else 0,
+                               None if host_lens is None else host_lens.ctypes.data,
+                               int(waves_per_group))
+
+
+def _host_lens(host_lens, n=None):
+    if host_lens is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(host_lens), dtype=np.int32)
+    if a.ndim != 1 or (n is not None and a.size != n):
+        raise ValueError("host_lens must be [n_seqs] lengths")
+    return a
 
 
 KERNELS = {"auto": 0, "generic": 1, "mfma": 2, "valu": 3}
@@ -162,11 +175,12 @@ KERNELS = {"auto": 0, "generic": 1, "mfma": 2, "valu": 3}
 
 def decode_workspace_bytes(geom: Geometry, n_seqs: int, n_q_heads: int, max_context_len: int,
                            blocks_per_split: int = 0, kernel: str = "auto",
-                           merge: bool = False, waves_per_group: int = 0) -> int:
+                           merge: bool = False, waves_per_group: int = 0, host_lens=None) -> int:
     """Bytes of decode workspace for these sizes and options. With merge=True the
     workspace must be allocated zeroed (torch.zeros) before its first use."""
     g = geom.c()
-    o = _opts(blocks_per_split, KERNELS[kernel], False, merge, waves_per_group)
+    hl = _host_lens(host_lens, n_seqs)
+    o = _opts(blocks_per_split, KERNELS[kernel], False, merge, waves_per_group, hl)
     return int(_L().pa_decode_workspace_bytes(C.byref(g), n_seqs, n_q_heads, max_context_len,
                                               C.byref(o)))
 
@@ -200,12 +214,13 @@ def _decode_args(geom: Geometry, k_pool, v_pool, q, out, block_tables, context_l
 def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, context_lens,
            max_context_len: int, scale: float = 0.0, workspace=None, blocks_per_split: int = 0,
            kernel: str = "auto", stream=None, kv_reuse: bool = False, merge: bool = False,
-           waves_per_group: int = 0):
+           waves_per_group: int = 0, host_lens=None):
     """out[i, h] = softmax attention of q[i, h] over sequence i's first
     context_lens[i] tokens, read through block_tables[i]. kv_reuse=True when many
     sequences of the batch share blocks (keeps them cacheable). merge=True merges
     the splits inside the decode launch (the workspace must start zeroed)."""
-    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse, merge, waves_per_group)
+    hl = _host_lens(host_lens, q.shape[0])
+    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse, merge, waves_per_group, hl)
     g, n, hq, ws_ptr, ws_bytes = _decode_args(geom, k_pool, v_pool, q, out, block_tables,
                                               context_lens, max_context_len, workspace, o)
     check(_L().pa_decode(C.byref(g), _ptr(k_pool), _ptr(v_pool), layer, _ptr(q), _ptr(out), n, hq,
@@ -218,11 +233,13 @@ def decode(geom: Geometry, k_pool, v_pool, layer: int, q, out, block_tables, con
 def decode_append(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out, block_tables,
                   context_lens, max_context_len: int, scale: float = 0.0, workspace=None,
                   blocks_per_split: int = 0, kernel: str = "auto", stream=None,
-                  kv_reuse: bool = False, merge: bool = False, waves_per_group: int = 0):
+                  kv_reuse: bool = False, merge: bool = False, waves_per_group: int = 0,
+                  host_lens=None):
     """Write each sequence's new token (k_new[i], v_new[i]: [n_seqs, H_kv, d]) at
     position context_lens[i] - 1 through its block table, then decode as
     `decode` does, in one launch."""
-    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse, merge, waves_per_group)
+    hl = _host_lens(host_lens, q.shape[0])
+    o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse, merge, waves_per_group, hl)
     g, n, hq, ws_ptr, ws_bytes = _decode_args(geom, k_pool, v_pool, q, out, block_tables,
                                               context_lens, max_context_len, workspace, o)
     per = geom.num_kv_heads * geom.head_dim

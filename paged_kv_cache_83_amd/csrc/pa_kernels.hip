@@ -31,6 +31,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/pa.h"
@@ -160,14 +161,18 @@ __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)
 // APPEND: the step's new token of every sequence (position len-1) comes in
 // knew/vnew [n][H_kv][d]; the work item holding that position writes it into the
 // pool and uses it from registers (K by address, V by element) while attending.
-template <int D, bool DIRECT, bool NT, bool APPEND>
+// RAGGED: the work items come from a list in the arguments (ragged batches:
+// only long sequences split, longest items first) instead of the uniform grid
+// of every sequence's S_max splits.
+template <int D, bool DIRECT, bool NT, bool APPEND, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : PA_MFMA_WPE))) void decode_mfma_bf16_kernel(
     uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, int64_t layer_off, int N, int Hkv, int Hq, int G,
-    int max_blocks, int max_ctx, int bps, int S_max, float qk_scale, int* __restrict__ counters) {
+    int max_blocks, int max_ctx, int bps, int S_max, float qk_scale, int* __restrict__ counters,
+    std::conditional_t<RAGGED, RaggedItems, NoRaggedItems> items) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int DT = MfmaCfg<D>::DT;
 
@@ -176,8 +181,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
   const int w = blockIdx.x;
   const int g = w % Hkv;
   const int si = w / Hkv;
-  const int s = si % S_max;
-  const int i = si / S_max;
+  int s, i;
+  if constexpr (RAGGED) {
+    const uint32_t e = items.v[si];
+    i = (int)(e & 0xffffu);
+    s = (int)(e >> 16);
+  } else {
+    s = si % S_max;
+    i = si / S_max;
+  }
   const int lane = threadIdx.x;
   const int c = lane & 15;
   const int gq = lane >> 4;
@@ -552,7 +564,58 @@ struct DecodePlan {
   bool merge;       // splits merged inside the decode launch (counters after the partials)
   size_t ws;
   size_t counters_off;
+  bool ragged;      // MFMA bf16 kernel: work items from `items`
+  RaggedItems items;
 };
+
+// Ragged plan for the MFMA bf16 kernel from the host copy of the lengths: a
+// sequence longer than C blocks is cut into items of C blocks, the others stay
+// whole, and items go out longest first, so the long sequences no longer set
+// the launch's end while most waves sit idle. C spreads the batch's blocks over
+// about two waves per SIMD. Taken only when the lengths are uneven (longest
+// above 1.5x the mean) and the list fits the kernel arguments.
+bool plan_ragged(const int32_t* host_lens, int32_t n, int32_t max_ctx, int Hkv, int D,
+                 int64_t want_bps, DecodePlan* plan) {
+  if (n <= 0 || n > 65535) return false;
+  std::vector<int32_t> nb(n);
+  int64_t total = 0, longest = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t len = std::min(std::max(host_lens[i], 0), max_ctx);
+    nb[i] = (len + 15) / 16;
+    total += nb[i];
+    longest = std::max<int64_t>(longest, nb[i]);
+  }
+  if (want_bps <= 0 && (total == 0 || 2 * longest * n <= 3 * total)) return false;
+  const int64_t slots = D >= 256 ? 1024 : 2048;
+  int64_t C = want_bps > 0 ? want_bps : std::max<int64_t>(16, (total * Hkv + slots - 1) / slots);
+  C += C & 1;
+  C = std::min<int64_t>(C, kMfmaMaxBps);
+  auto count = [&](int64_t c) {
+    int64_t k = 0;
+    for (int32_t i = 0; i < n; ++i) k += std::max<int64_t>(1, (nb[i] + c - 1) / c);
+    return k;
+  };
+  while (count(C) > kMaxRaggedItems && C < kMfmaMaxBps) C = std::min<int64_t>(kMfmaMaxBps, 2 * C);
+  if (count(C) > kMaxRaggedItems) return false;
+  struct Item { int32_t size, seq, split; };
+  std::vector<Item> list;
+  int64_t S = 1;
+  for (int32_t i = 0; i < n; ++i) {
+    const int64_t c = std::max<int64_t>(1, (nb[i] + C - 1) / C);
+    S = std::max(S, c);
+    for (int64_t sp = 0; sp < c; ++sp)
+      list.push_back({(int32_t)std::min<int64_t>(C, nb[i] - sp * C), i, (int32_t)sp});
+  }
+  if (S > 65535) return false;
+  std::stable_sort(list.begin(), list.end(), [](const Item& a, const Item& b) { return a.size > b.size; });
+  plan->ragged = true;
+  plan->items.n = (int32_t)list.size();
+  for (size_t k = 0; k < list.size(); ++k)
+    plan->items.v[k] = (uint32_t)list[k].seq | ((uint32_t)list[k].split << 16);
+  plan->bps = (int)C;
+  plan->S_max = (int)S;
+  return true;
+}
 
 pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ctx,
                     const pa_decode_opts* opts, DecodePlan* plan) {
@@ -634,6 +697,12 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
   plan->bpw = (int)bpw;
   plan->wg_waves = (int)W;
   plan->S_max = (int)S;
+  plan->ragged = false;
+  plan->items.n = 0;
+  if (k == 2 && opts && opts->host_context_lens)
+    plan_ragged(opts->host_context_lens, n_seqs, max_ctx, g->num_kv_heads, D,
+                opts->blocks_per_split, plan);
+  S = plan->S_max;
   plan->direct = S == 1;
   plan->merge = !plan->direct && opts && opts->merge == 1 && k >= 2;   // not the generic kernel
   const size_t parts = plan->direct ? 0 : (size_t)n_seqs * Hq * S * (D + 2) * sizeof(float);
@@ -746,7 +815,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   const bool append = knew != nullptr;
   if (append != (vnew != nullptr)) return PA_ERR_INVALID_ARG;
   if (!plan.direct && (!workspace || workspace_bytes < plan.ws)) return PA_ERR_WORKSPACE;
-  const int64_t items = (int64_t)n_seqs * Hkv * plan.S_max;
+  const int64_t items = (int64_t)(plan.ragged ? plan.items.n : (int64_t)n_seqs * plan.S_max) * Hkv;
   if (items > INT32_MAX) return PA_ERR_UNSUPPORTED;
   hipStream_t st = (hipStream_t)stream;
   if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
@@ -791,13 +860,18 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
 #undef PA_FP8_LAUNCH
 #undef PA_FP8_LAUNCH_X
     } else if (plan.kernel == 2) {
-#define PA_MFMA_LAUNCH_X(DD, DIR, NTV, APP)                                                       \
-  hipLaunchKernelGGL((decode_mfma_bf16_kernel<DD, DIR, NTV, APP>), grid, block, 0, st,            \
+#define PA_MFMA_LAUNCH_RG(DD, DIR, NTV, APP, RG, ITEMS)                                           \
+  hipLaunchKernelGGL((decode_mfma_bf16_kernel<DD, DIR, NTV, APP, RG>), grid, block, 0, st,        \
                      (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)q,                     \
                      (const uint16_t*)knew, (const uint16_t*)vnew, (uint16_t*)out, part_o,         \
                      part_ml, block_tables, context_lens, layer_off, g->num_blocks, Hkv,          \
                      n_q_heads, G, max_blocks_per_seq, max_context_len, plan.bps, plan.S_max,      \
-                     qk_scale, counters)
+                     qk_scale, counters, ITEMS)
+#define PA_MFMA_LAUNCH_X(DD, DIR, NTV, APP)                                                       \
+  do {                                                                                           \
+    if (plan.ragged) PA_MFMA_LAUNCH_RG(DD, DIR, NTV, APP, true, plan.items);                      \
+    else PA_MFMA_LAUNCH_RG(DD, DIR, NTV, APP, false, NoRaggedItems{});                            \
+  } while (0)
 #define PA_MFMA_LAUNCH_NT(DD, DIR, NTV)                     \
   do {                                                      \
     if (append) PA_MFMA_LAUNCH_X(DD, DIR, NTV, true);       \
@@ -818,6 +892,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
 #undef PA_MFMA_LAUNCH
 #undef PA_MFMA_LAUNCH_NT
 #undef PA_MFMA_LAUNCH_X
+#undef PA_MFMA_LAUNCH_RG
     } else if (plan.kernel == 4) {
 #define PA_VALU_LAUNCH_X(T, DD, GG, NTV)                                                          \
   hipLaunchKernelGGL((decode_valu_kernel<T, DD, GG, NTV>), grid, dim3(64 * plan.wg_waves),         \

@@ -17,6 +17,17 @@ namespace pa_detail {
 
 constexpr int kMfmaMaxBps = 256;  // table entries of one split, held 64 per register
 
+// Work list of a ragged launch, passed by value in the kernel arguments (so a
+// captured graph keeps the list it was captured with): item k is (sequence,
+// split) packed as sequence | split << 16, longest items first. A launch with
+// more items than fit takes the uniform plan instead.
+constexpr int kMaxRaggedItems = 896;
+struct RaggedItems {
+  int32_t n;
+  uint32_t v[kMaxRaggedItems];
+};
+struct NoRaggedItems {};
+
 #ifndef PA_MFMA_STAGES
 #define PA_MFMA_STAGES 2
 #endif

@@ -33,7 +33,8 @@ def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slo
                 max_context_len: int, out_all, workspace, layers: Optional[Sequence[int]] = None,
                 blocks_per_split: int = 0, kernel: str = "auto", stream=None,
                 around_decode: Optional[Callable[[int, bool], None]] = None, kv_reuse: bool = False,
-                fused: bool = True, merge: bool = False, waves_per_group: int = 0):
+                fused: bool = True, merge: bool = False, waves_per_group: int = 0,
+                host_lens=None):
     """One decode step: for each layer, append the new tokens, then decode.
 
     q_all [L, n, H_q, d]; k_new_all / v_new_all [L, n_tok, H_kv, d]; slots int64
@@ -41,7 +42,8 @@ def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slo
     fused=True (one new token per sequence, at position lens[i] - 1 of its table,
     n_tok == n) does both in one launch per layer and ignores `slots`;
     fused=False issues the slot-mapped append and the decode separately.
-    merge=True merges the splits inside the decode launch (zeroed workspace).
+    merge=True merges the splits inside the decode launch (zeroed workspace);
+    host_lens (host copy of lens) lets the library plan ragged batches.
     around_decode(layer, before) is called just before and after each layer's
     decode call (host side, e.g. to switch per-kernel timing on and off).
     """
@@ -56,12 +58,12 @@ def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slo
                               v_new_all[layer], out_all[layer], tables, lens, max_context_len,
                               workspace=workspace, blocks_per_split=blocks_per_split,
                               kernel=kernel, stream=stream, kv_reuse=kv_reuse, merge=merge,
-                              waves_per_group=waves_per_group)
+                              waves_per_group=waves_per_group, host_lens=host_lens)
         else:
             api.decode(geom, k_pool, v_pool, layer, q_all[layer], out_all[layer], tables, lens,
                        max_context_len, workspace=workspace, blocks_per_split=blocks_per_split,
                        kernel=kernel, stream=stream, kv_reuse=kv_reuse, merge=merge,
-                              waves_per_group=waves_per_group)
+                              waves_per_group=waves_per_group, host_lens=host_lens)
         if around_decode is not None:
             around_decode(layer, False)
 

@@ -21,7 +21,7 @@ RAGGED = [1, 2, 15, 16, 17, 31, 32, 33, 47, 64, 100, 257]
 
 
 def run_library(batch, layer, kernel="auto", bps=0, scale=0.0, tables=None, lengths=None,
-                max_ctx=None, merge=False, ws=None, waves=0):
+                max_ctx=None, merge=False, ws=None, waves=0, host_lens=None):
     """Upload the batch, run the library's append + decode on one layer; returns
     (out, k_pool, v_pool) in storage form. merge=True merges the splits inside
     the decode launch (zeroed workspace, or the one passed in)."""
@@ -37,11 +37,12 @@ def run_library(batch, layer, kernel="auto", bps=0, scale=0.0, tables=None, leng
     out = torch.empty_like(q)
     if ws is None:
         ws_bytes = pk.decode_workspace_bytes(geom, q.shape[0], q.shape[1], max_ctx, bps, kernel,
-                                             merge, waves)
+                                             merge, waves, host_lens)
         ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
     pk.decode(geom, K, V, layer, q, out, torch.from_numpy(tabs).cuda(),
               torch.from_numpy(np.asarray(lens, np.int32)).cuda(), max_ctx, scale=scale,
-              workspace=ws, blocks_per_split=bps, kernel=kernel, merge=merge, waves_per_group=waves)
+              workspace=ws, blocks_per_split=bps, kernel=kernel, merge=merge, waves_per_group=waves,
+              host_lens=host_lens)
     torch.cuda.synchronize()
     return to_host(out, batch.dtype), to_host(K, batch.dtype), to_host(V, batch.dtype)
 
@@ -299,3 +300,52 @@ def test_valu_workgroup_waves(case):
         assert np.max(np.abs(got.astype(np.float64) - one.astype(np.float64))) <= 1e-6, name
     again, _, _ = run_library(batch, 0, kernel="valu", bps=bps, merge=merge, waves=waves)
     assert np.array_equal(got.view(np.uint8), again.view(np.uint8)), name
+
+
+RAGGED_PLAN_CASES = [
+    # name, Hq, Hkv, d, lengths, bps, merge
+    ("uneven_auto", 32, 8, 128, [1, 2000, 17, 300, 0, 1024, 64, 5000, 33], 0, False),
+    ("uneven_auto_merge", 32, 8, 128, [1, 2000, 17, 300, 0, 1024, 64, 5000, 33], 0, True),
+    ("items_of_6", 64, 8, 128, [300, 1, 900, 40, 0], 6, False),
+    ("items_of_4_merge_d64", 32, 2, 64, [129, 3000, 7, 640], 4, True),
+    ("items_of_2_g16_d64", 32, 2, 64, RAGGED, 2, False),
+]
+
+
+@pytest.mark.parametrize("case", RAGGED_PLAN_CASES, ids=[c[0] for c in RAGGED_PLAN_CASES])
+def test_ragged_plan(case):
+    """With the host copy of the lengths the MFMA kernel takes a list of work
+    items -- long sequences cut into items, longest first -- from its arguments:
+    outputs within the bf16 tolerance of the oracle (and of the uniform plan),
+    empty sequences zero, and the same bits on a second call."""
+    need_gpu()
+    name, Hq, Hkv, d, lengths, bps, merge = case
+    print_case(test="ragged_plan", case=name)
+    batch = make_batch("bf16", 1, 900, Hq, Hkv, d, 16, lengths, seed=zlib.crc32(name.encode()) % 10000)
+    hl = np.asarray(lengths, np.int32)
+    got, _, _ = run_library(batch, 0, kernel="mfma", bps=bps, merge=merge, host_lens=hl)
+    _, _, expect = oracle_step(batch, 0)
+    assert max_abs_err(got, expect, "bf16") <= BF16_TOL, name
+    for i, S in enumerate(lengths):
+        if S == 0:
+            assert not np.any(got[i].view(np.uint8)), (name, i)
+    uniform, _, _ = run_library(batch, 0, kernel="mfma", bps=bps, merge=merge)
+    assert np.max(np.abs(olayout_widen(got) - olayout_widen(uniform))) <= BF16_TOL
+    again, _, _ = run_library(batch, 0, kernel="mfma", bps=bps, merge=merge, host_lens=hl)
+    assert np.array_equal(got.view(np.uint8), again.view(np.uint8)), name
+
+
+def olayout_widen(a):
+    from oracle import layout
+    return layout.widen(a, "bf16")
+
+
+def test_uniform_lengths_keep_the_uniform_plan():
+    """Even lengths: the host copy changes nothing (same bits as without it)."""
+    need_gpu()
+    print_case(test="ragged_uniform")
+    lengths = [700] * 6
+    batch = make_batch("bf16", 1, 400, 32, 8, 128, 16, lengths, seed=808)
+    a, _, _ = run_library(batch, 0, kernel="mfma")
+    b, _, _ = run_library(batch, 0, kernel="mfma", host_lens=np.asarray(lengths, np.int32))
+    assert np.array_equal(a.view(np.uint8), b.view(np.uint8))

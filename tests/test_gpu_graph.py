@@ -27,6 +27,7 @@ CASES = [
     ("valu_f32_merge", "f32", 2, 300, 12, 12, 64, 16, [5, 250, 900, 33], 2, "valu", True),
     ("valu_bf16_merge", "bf16", 2, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 4, "valu", True),
     ("mfma_merge", "bf16", 2, 300, 32, 8, 128, 16, [1, 17, 300, 1024, 77], 4, "mfma", True),
+    ("mfma_ragged", "bf16", 2, 400, 32, 8, 128, 16, [1, 17, 3000, 1024, 77, 0], 0, "mfma", "ragged"),
 ]
 
 
@@ -51,7 +52,10 @@ def test_graph_replay_matches_eager(case):
         tabs = torch.from_numpy(padded_tables(batch.tables, batch.max_blocks)).cuda()
         lens = torch.from_numpy(np.asarray(lengths, np.int32)).cuda()
         max_ctx = max(lengths)
-        ws = torch.zeros(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, bps, kernel, merge)),
+        host_lens = np.asarray(lengths, np.int32) if merge == "ragged" else None
+        merge = merge is True
+        ws = torch.zeros(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, bps, kernel, merge,
+                                                          0, host_lens)),
                          dtype=torch.uint8, device="cuda")
         out_eager = torch.empty_like(q_all)
         out_graph = torch.full_like(q_all, float("nan"))
@@ -59,7 +63,8 @@ def test_graph_replay_matches_eager(case):
 
     def step(out):
         steps.decode_step(geom, K, V, q_all, kn, vn, None, tabs, lens, max_ctx, out, ws,
-                          blocks_per_split=bps, kernel=kernel, stream=s, merge=merge)
+                          blocks_per_split=bps, kernel=kernel, stream=s, merge=merge,
+                          host_lens=host_lens)
 
     step(out_eager)
     torch.cuda.synchronize()
