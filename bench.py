@@ -55,6 +55,8 @@ def parse():
                     help="record kernel events around the decode of every k-th layer")
     ap.add_argument("--cold", action="store_true",
                     help="also time steps after writing a 1 GiB buffer (flushes L2 and MALL)")
+    ap.add_argument("--cold-only", action="store_true",
+                    help="decode / fork workloads: run only the cold steps (for counter passes)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a 1 GiB device copy (for scaling HBM byte counters)")
     ap.add_argument("--parity-samples", type=int, default=4)
@@ -346,10 +348,13 @@ def run_decode(args):
     if not args.no_prof and not args.graph:
         pk.Profiler.reset()
         profiling[0] = True
-    t, step_ms = timed_steps(torch, stream, run, args.steps)
-    profiling[0] = False
-    ms_per_step = max(t.ms, t.wall_ms) / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step {step_ms}")
+    if args.cold_only:
+        args.cold = True
+    else:
+        t, step_ms = timed_steps(torch, stream, run, args.steps)
+        profiling[0] = False
+        ms_per_step = max(t.ms, t.wall_ms) / args.steps
+        log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step {step_ms}")
 
     cold = None
     if args.cold:
@@ -362,6 +367,9 @@ def run_decode(args):
             tot += tc.ms
         cold = tot / args.steps
         log(f"cold (1 GiB written before each step): {cold:.3f} ms/step")
+        if args.cold_only:
+            profiling[0] = False
+            ms_per_step, step_ms = cold, None
 
     kv_bytes_step = int(lengths.sum()) * m_token
     value = kv_bytes_step / (ms_per_step * 1e-3) / 1e9
@@ -560,10 +568,24 @@ def run_fork(args):
     if args.graph:
         run()
     pk.Profiler.reset()
-    pk.Profiler.enable(not args.graph)
-    t, step_ms = timed_steps(torch, stream, run, args.steps)
+    pk.Profiler.enable(not args.graph and not args.no_prof)
+    if not args.cold_only:
+        t, step_ms = timed_steps(torch, stream, run, args.steps)
+        ms = max(t.ms, t.wall_ms) / args.steps
+    cold = None
+    if args.cold or args.cold_only:
+        flush = torch.zeros(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        tot = 0.0
+        for _ in range(args.steps):
+            flush.add_(1.0)
+            with Timer(torch, stream) as tc:
+                run()
+            tot += tc.ms
+        cold = tot / args.steps
+        log(f"cold (1 GiB written before each step): {cold:.3f} ms/step")
+        if args.cold_only:
+            ms, step_ms = cold, None
     pk.Profiler.enable(False)
-    ms = max(t.ms, t.wall_ms) / args.steps
     m_token = pk.bytes_per_token(L, Hkv, d, geom.elem_bytes)
     logical = int(lengths.sum()) * m_token
     unique = (cfg.prefix_len + int(suffix.sum())) * m_token
@@ -588,6 +610,10 @@ def run_fork(args):
         "launch": "hip graph replay" if args.graph else "eager",
         "kernels": kern,
     }
+    if cold is not None:
+        result["cold_ms_per_step"] = round(cold, 4)
+        result["cold_logical_kv_GBps"] = round(logical / (cold * 1e-3) / 1e9, 1)
+        result["cold_unique_kv_GBps"] = round(unique / (cold * 1e-3) / 1e9, 1)
     print(json.dumps(result), flush=True)
 
 

@@ -80,7 +80,8 @@ __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)
                                              f32x4 (&acc)[MfmaCfg<D>::DT], float& m_run,
                                              float& l_run, int blk, int len, int gq,
                                              float qk_scale, int new_pos,
-                                             const uint32_t (&vnew)[MfmaCfg<D>::DT / 2]) {
+                                             const uint32_t (&vnew)[MfmaCfg<D>::DT / 2],
+                                             uint16_t* vt_new) {
   constexpr int KC = MfmaCfg<D>::KC;
   constexpr int DT = MfmaCfg<D>::DT;
   if (new_pos >= blk * 16 && new_pos < blk * 16 + 32) {  // wave-uniform
@@ -96,6 +97,17 @@ __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)
         for (int wv = 0; wv < 4; ++wv)
           f.v[dt][wv] = (wv == word) ? ((f.v[dt][wv] & keep) | ins) : f.v[dt][wv];
       }
+    }
+    // The new token's V goes into the pool as its whole tile: the lanes holding
+    // that block (every dimension, both halves of the slots) write their
+    // fragments -- as loaded, with the new slot patched -- as 16-byte stores,
+    // where storing the one new element per dimension row would touch 128
+    // separate 32-byte pieces of the tile with 2-byte writes.
+    if ((gq >> 1) == ((new_pos - blk * 16) >> 4)) {
+      const int c = threadIdx.x & 15;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<u32x4*>(vt_new + (16 * dt + c) * 16 + 8 * (gq & 1)) = f.v[dt];
     }
   }
   f32x4 sc[2];
@@ -247,6 +259,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
   // by address, V by element) wherever the pair loads would return its slot.
   int new_pos = -1;
   const uint16_t* knew_row = knew;
+  uint16_t* vt_new = nullptr;   // V tile of the appended token's block
   uint32_t vnw[DT / 2];
 #pragma unroll
   for (int k = 0; k < DT / 2; ++k) vnw[k] = 0;
@@ -257,12 +270,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
     const int pn = guard_block(trow[new_pos >> 4], N);
     const int on = new_pos & 15;
     uint16_t* kt = kpool + layer_off + ((int64_t)pn * Hkv + g) * (16 * D);
-    uint16_t* vt = vpool + layer_off + ((int64_t)pn * Hkv + g) * (16 * D);
     if (lane < D / 8) {  // K row: lane moves dims 8*lane .. +8 (a 32-dim chunk takes 4 lanes)
       const u32x4 kv8 = *reinterpret_cast<const u32x4*>(knew_row + 8 * lane);
       *reinterpret_cast<u32x4*>(kt + (lane >> 2) * 512 + on * 32 + 8 * (lane & 3)) = kv8;
     }
-    for (int d = lane; d < D; d += 64) vt[d * 16 + on] = vnew_row[d];  // V column
+    // the V tile is written whole by the pair that holds the token (compute_pair)
+    vt_new = vpool + layer_off + ((int64_t)pn * Hkv + g) * (16 * D);
 #pragma unroll
     for (int k = 0; k < DT / 2; ++k)
       vnw[k] = (uint32_t)vnew_row[32 * k + c] | ((uint32_t)vnew_row[32 * k + 16 + c] << 16);
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
       for (int st = 0; st < NS; ++st) {
         issue_at(f[(st + NS - 1) % NS], pj + st + NS - 1);
         compute_pair<D>(f[st], qf, acc, m_run, l_run, b0 + 2 * (pj + st), len, gq, qk_scale,
-                        new_pos, vnw);
+                        new_pos, vnw, vt_new);
       }
     }
   } else {
@@ -321,7 +334,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
     if (pj + k >= npairs) break;
     if (pj + k + NS - 1 < npairs) issue_at(f[(k + NS - 1) % NS], pj + k + NS - 1);
     compute_pair<D>(f[k % NS], qf, acc, m_run, l_run, b0 + 2 * (pj + k), len, gq, qk_scale, new_pos,
-                    vnw);
+                    vnw, vt_new);
   }
 
   l_run = sum_over_groups(l_run);

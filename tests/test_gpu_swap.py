@@ -268,6 +268,13 @@ def test_errors_change_nothing():
     su.ref.swap_out_begin(s, [1, 2])
     su.ref.swap_out_finish(s, [1, 2])
     su.same_state()
+    with pytest.raises(pk.PagedKVError):   # frames 0-1 hold the only copy of two blocks
+        su.sw.close()
+    su.bm.release(s)                        # releasing the sequence returns its frames
+    su.ref.release(s)
+    su.seqs.remove(s)
+    su.same_state()
+    assert su.bm.host_frames_free() == 6
     su.sw.close()
 
 
