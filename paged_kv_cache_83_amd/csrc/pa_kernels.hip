@@ -508,7 +508,8 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
                                                             T* __restrict__ out,
                                                             const int32_t* __restrict__ lens,
                                                             int Hq, int D, int B, int S_max,
-                                                            int bps, int max_ctx) {
+                                                            int bps, int max_ctx,
+                                                            int single_written) {
   const int w = blockIdx.x;
   const int h = w % Hq;
   const int i = w / Hq;
@@ -521,6 +522,7 @@ __global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restr
     for (int d = lane; d < D; d += 64) o[d] = from_f32<T>(0.f);
     return;
   }
+  if (ns == 1 && single_written) return;   // the decode launch wrote this row
   const int64_t row0 = ((int64_t)i * Hq + h) * S_max;
   merge_split_row<T>(part_o + row0 * D, part_ml + row0 * 2, ns, D, o, lane);
 }
@@ -969,14 +971,17 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   if (!plan.direct && !plan.merge) {
     ProfScope ps("decode_combine", st, timing);
     const dim3 grid((unsigned)((int64_t)n_seqs * n_q_heads)), block(64);
+    // the MFMA and streaming VALU kernels write a one-split sequence's output
+    // themselves; the generic kernel leaves every split to the combine
+    const int single_written = plan.kernel != 1;
     if (g->dtype == PA_F32)  // bf16 output for bf16 and fp8 pools
       hipLaunchKernelGGL((decode_combine_kernel<float>), grid, block, 0, st, part_o, part_ml,
                          (float*)out, context_lens, n_q_heads, D, B, plan.S_max, plan.bps,
-                         max_context_len);
+                         max_context_len, single_written);
     else
       hipLaunchKernelGGL((decode_combine_kernel<uint16_t>), grid, block, 0, st, part_o, part_ml,
                          (uint16_t*)out, context_lens, n_q_heads, D, B, plan.S_max, plan.bps,
-                         max_context_len);
+                         max_context_len, single_written);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   return PA_OK;

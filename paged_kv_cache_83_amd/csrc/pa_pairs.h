@@ -114,7 +114,7 @@ __device__ __forceinline__ void mfma_split_epilogue(const f32x4 (&acc)[D / 16], 
   const int gq = lane >> 4;
   const int h = g * G + c;
   const bool qvalid = c < G;
-  if (direct || (counters && ns == 1)) {
+  if (direct || ns == 1) {   // one split covers the sequence: the output itself
     if (!qvalid) return;
     const float inv = 1.f / l_run;
     uint16_t* o = out + ((int64_t)i * Hq + h) * D;

@@ -411,12 +411,12 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
   // The workgroup's result for head h -- maximum M, sum L, unnormalised o of
   // the lane's dims -- goes out as the output or as the split's partial.
   auto finish = [&](int h, float M, float L, const float (&o)[DPL]) {
-    if (whole && (direct || coherent)) {   // the output, normalised
+    if (whole) {   // the output, normalised
       const float inv = 1.f / L;
       T* op = out + ((int64_t)i * Hq + (int64_t)g * G + h) * D;
 #pragma unroll
       for (int r = 0; r < DPL; ++r) op[lane + 64 * r] = from_f32<T>(o[r] * inv);
-    } else {   // the split's partial (with the combine launch, also for a one-split sequence)
+    } else {   // the split's partial
       const int64_t row = ((int64_t)i * Hq + (int64_t)g * G + h) * S_max + s;
       if (coherent) {
 #pragma unroll
