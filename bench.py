@@ -90,28 +90,35 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def decode_kernel_source_sha() -> str:
-    """sha256 prefix of the bf16 matrix-core decode kernel's source: its section of
-    pa_kernels.hip (from its banner to the generic kernel's), the device helpers
-    and the pair-load helpers it includes. Edits elsewhere in the file leave it
-    unchanged."""
+def kernel_source_sha(kernel: str) -> str:
+    """sha256 prefix of a decode kernel's source: for the bf16 matrix-core kernel
+    its section of pa_kernels.hip (from its banner to the generic kernel's), for
+    the streaming VALU and FP8 kernels their headers, each with the device and
+    pair-load helpers. Edits elsewhere leave it unchanged."""
     here = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(here, "paged_kv_cache_83_amd", "csrc")
-    text = open(os.path.join(csrc, "pa_kernels.hip"), "rb").read()
-    a = text.index(b"// Decode, MFMA kernel:")
-    b = text.index(b"// Decode, generic kernel")
-    h = hashlib.sha256(text[a:b])
+    h = hashlib.sha256()
+    if kernel == "decode_mfma_bf16_kernel":
+        text = open(os.path.join(csrc, "pa_kernels.hip"), "rb").read()
+        h.update(text[text.index(b"// Decode, MFMA kernel:"):text.index(b"// Decode, generic kernel")])
+    elif kernel == "decode_valu_kernel":
+        h.update(open(os.path.join(csrc, "pa_valu.h"), "rb").read())
+    elif kernel == "decode_mfma_fp8_kernel":
+        h.update(open(os.path.join(csrc, "pa_fp8.h"), "rb").read())
+    else:
+        raise ValueError(kernel)
     h.update(open(os.path.join(csrc, "pa_device.h"), "rb").read())
     h.update(open(os.path.join(csrc, "pa_pairs.h"), "rb").read())
     return h.hexdigest()[:16]
 
 
-def profiled_traffic(workload: str):
+def profiled_traffic(kernel: str, workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 counter summary
-    (FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), or None when the kernel
-    source has changed since those counters were taken."""
+    of this kernel on this workload (FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB
+    copy), or None when there is none or the kernel source has changed since."""
     here = os.path.dirname(os.path.abspath(__file__))
-    path = os.path.join(here, "profiles", f"decode_mfma_bf16_{workload}_hbm_counters.md")
+    stem = kernel[:-len("_kernel")]
+    path = os.path.join(here, "profiles", f"{stem}_{workload}_hbm_counters.md")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -119,8 +126,8 @@ def profiled_traffic(workload: str):
         if ":" in line and line.split(":", 1)[0].strip() in ("source_sha256_prefix", "traffic_bytes_per_launch"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    sha = decode_kernel_source_sha()
-    if fields.get("source_sha256_prefix") != sha or "traffic_bytes_per_launch" not in fields:
+    if fields.get("source_sha256_prefix") != kernel_source_sha(kernel) or \
+            "traffic_bytes_per_launch" not in fields:
         return None
     return int(fields["traffic_bytes_per_launch"])
 
@@ -385,13 +392,11 @@ def run_decode(args):
         if cnt:
             eb = geom.elem_bytes
             ib = 2 if fp8 else eb                                                # q / out element bytes
-            splits = max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, args.bps, args.kernel,
-                                                      False, args.wg_waves, host_lens)
-                         // (n * Hq * (d + 2) * 4)) if ws_bytes else 1
+            # what the step must move; split partials (the launch plan's choice)
+            # are left out, so they show up only in the measured traffic
             per_launch = (int(lengths.sum()) * 2 * Hkv * (d * eb + (1 if fp8 else 0))  # K and V (+ scales)
-                          + n * Hq * d * ib                                      # queries
+                          + 2 * n * Hq * d * ib                                  # queries, outputs
                           + 4 * int(sum(math.ceil(S / B) for S in lengths))       # block-table entries
-                          + (n * Hq * splits * (d + 2) * 4 if ws_bytes else n * Hq * d * ib)
                           + (0 if (args.unfused or fp8) else 4 * n * Hkv * d * eb))  # fused new K/V
             avg_s = tot / cnt * 1e-3
             achieved = per_launch / avg_s / 1e9
@@ -402,8 +407,8 @@ def run_decode(args):
                      else "decode_valu_kernel" if valu else "decode_generic_kernel")
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / PEAK_GBS, 4),
-                        "traffic": profiled_traffic(cfg.name) if (mfma and not fp8 and args.bps == 0
-                                                                  and args.kernel == "auto") else None,
+                        "traffic": profiled_traffic(kname, cfg.name) if (args.bps == 0 and args.kernel == "auto"
+                                                                        and not args.unfused) else None,
                         "kernel": kname,
                         "bytes_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 2)}
 
