@@ -135,13 +135,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   constexpr int TW = kPfRowsPerWave / G;  // chunk tokens per wave
   extern __shared__ __align__(16) unsigned char pf_smem[];  // three pair images
 
-  const int64_t items = (int64_t)cb.n_seqs * Hkv * n_tiles * sp.n;
-  const int64_t per_xcd = (int64_t)gridDim.x / kXcds;
-  const int64_t item = (int64_t)(blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (item >= items) return;  // whole work group
-  const int split = (int)(item % sp.n);  // splits, then tiles, of one (chunk, head) are adjacent
-  const int tile = (int)((item / sp.n) % n_tiles);
-  const int64_t ig = item / sp.n / n_tiles;
+  // Work groups are dealt to the XCDs in turn (group b runs on XCD b % 8). XCD x
+  // takes the (chunk, KV head) groups x, x + 8, x + 16, ... (group = chunk * H_kv
+  // + head), each group's splits and tiles one after another, the last (longest)
+  // tiles first: a group's history is read into one L2, and every XCD gets the
+  // same mix of short and long chunks (with H_kv = 8, one head of every chunk).
+  const int64_t per_group = (int64_t)n_tiles * sp.n;
+  const int64_t u = blockIdx.x / kXcds;
+  const int64_t ig = (int64_t)(blockIdx.x % kXcds) + kXcds * (u / per_group);
+  if (ig >= (int64_t)cb.n_seqs * Hkv) return;  // whole work group
+  const int64_t rem = u % per_group;
+  const int split = (int)(rem % sp.n);
+  const int tile = n_tiles - 1 - (int)(rem / sp.n);
   const int g = (int)(ig % Hkv);
   const int i = (int)(ig / Hkv);
   int a, q_len, ctx;
@@ -1102,8 +1107,9 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
 #undef PA_PF_SHORT_D
 #undef PA_PF_SHORT
     } else {
-      const int64_t items = (int64_t)n_seqs * Hkv * plan.n_tiles * S;
-      const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
+      // each XCD gets ceil(groups / 8) (chunk, KV head) groups of n_tiles x S items
+      const int64_t groups = (int64_t)n_seqs * Hkv;
+      const int64_t wgs = kXcds * ((groups + kXcds - 1) / kXcds) * plan.n_tiles * S;
       if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
       const dim3 grid((unsigned)wgs);
       const size_t lds = 3 * (size_t)(D == 64 ? PfCfg<64>::PAIR_BYTES : PfCfg<128>::PAIR_BYTES);
