@@ -96,6 +96,28 @@ constexpr float kLazyLog2 = 8.0f;
 #define PA_PF_VALU_PER_MFMA 8
 #endif
 constexpr int kPfValuPerMfma = PA_PF_VALU_PER_MFMA;
+// ... and before the first of them, after the fragment reads.
+#ifndef PA_PF_LEAD_VALU
+#define PA_PF_LEAD_VALU 0
+#endif
+constexpr int kPfLeadValu = PA_PF_LEAD_VALU;
+
+// Maximum of three scores in one instruction. The scores reaching it are finite
+// or -inf (masked), so the quieting of signalling NaNs that fmaxf must do on the
+// products of the matrix cores (an extra instruction per operand) is not needed.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float d;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+  return d;
+}
+
+// acc + lo + hi of a packed pair of bf16 values, in one dot-product instruction
+// (against the pair (1, 1)).
+typedef __bf16 pf_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(pf_bf16x2, pair),
+                                         __builtin_bit_cast(pf_bf16x2, 0x3f803f80u), acc, false);
+}
 
 // This wave's LDS accesses have completed; then synchronise the work group
 // (no wait for global loads still in flight into registers).
@@ -217,10 +239,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const char* kg = kl + (int64_t)g * PTILE;  // head g's tile in block 0
   const char* vg = vl + (int64_t)g * PTILE;
   const int64_t blk_stride = (int64_t)Hkv * PTILE;
-  auto issue = [&](int pj, int buf) {
+
+  // The split's block ids, one per lane and register: a window of 256 blocks
+  // from wbase, read by readlane when a pair's loads are issued (no memory
+  // round trip per pair). Pairs are issued in increasing order; the window moves
+  // on when one falls past it (a wait for that load, once every 128 pairs).
+  int tb[4];
+  int wbase = 2 * pbeg;
+  auto load_window = [&]() {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)  // (lanes past the split's blocks repeat its last id)
+      tb[k] = guard_block(trow[min(wbase + 64 * k + lane, nblk - 1)], N);
+  };
+  load_window();
+  auto pair_ids = [&](int pj, int& p0, int& p1) {
     const int b0 = 2 * pj;
-    const int p0 = guard_block(trow[b0], N);
-    const int p1 = (b0 + 1 < nblk) ? guard_block(trow[b0 + 1], N) : p0;
+    if (b0 - wbase >= 256) {  // uniform
+      wbase = b0;
+      load_window();
+    }
+    p0 = table_at(tb, b0 - wbase);
+    p1 = (b0 + 1 < nblk) ? table_at(tb, b0 + 1 - wbase) : p0;
+  };
+  auto issue = [&](int pj, int buf) {
+    int p0, p1;
+    pair_ids(pj, p0, p1);
     unsigned char* img = pf_smem + buf;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
@@ -254,9 +297,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     u32x2 vs[KP];      // V: 8 bytes each, one per slot
   };
   auto load_raw = [&](int pj, Raw& r) {
-    const int b0 = 2 * pj;
-    const int p0 = guard_block(trow[b0], N);
-    const int p1 = (b0 + 1 < nblk) ? guard_block(trow[b0 + 1], N) : p0;
+    int p0, p1;
+    pair_ids(pj, p0, p1);
     r.ks = 0u;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
@@ -388,8 +430,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
           for (int e = 0; e < 4; ++e)
             if (key0 + 4 * t + e > qpos[ct]) sv[ct][4 * t + e] = -INFINITY;
       }
-      lmax[ct] = fmaxf(fmaxf(fmaxf(sv[ct][0], sv[ct][1]), fmaxf(sv[ct][2], sv[ct][3])),
-                       fmaxf(fmaxf(sv[ct][4], sv[ct][5]), fmaxf(sv[ct][6], sv[ct][7])));
+      lmax[ct] = max3f(max3f(sv[ct][0], sv[ct][1], sv[ct][2]), max3f(sv[ct][3], sv[ct][4], sv[ct][5]),
+                       max3f(sv[ct][6], sv[ct][7], sv[ct][7]));
       pass = pass || lmax[ct] > thr[ct];
     }
     auto probs = [&]() {
@@ -400,8 +442,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         for (int e = 0; e < 8; e += 2) {
           const float pa = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[ct][e], qk_scale, ms[ct]));
           const float pb = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[ct][e + 1], qk_scale, ms[ct]));
-          psum[ct] += pa + pb;
           pw[ct][e >> 1] = pack_bf16x2(pa, pb);
+          // the row sum takes the probabilities as the P.V products do (bf16)
+          psum[ct] = add_bf16x2(pw[ct][e >> 1], psum[ct]);
         }
       }
     };
@@ -418,6 +461,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         asm volatile("" : "+v"(psum[ct]), "+v"(pw[ct][0]), "+v"(pw[ct][1]), "+v"(pw[ct][2]),
                      "+v"(pw[ct][3]));
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * KC, 0);  // LDS reads
+      if constexpr (kPfLeadValu > 0)  // vector work while the reads are in flight
+        __builtin_amdgcn_sched_group_barrier(0x002, kPfLeadValu, 0);
 #pragma unroll
       for (int k = 0; k < 4 * KC; ++k) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
