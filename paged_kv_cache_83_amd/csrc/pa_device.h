@@ -144,6 +144,66 @@ template <typename T, bool COH = false>
 __device__ __forceinline__ void merge_split_row(const float* __restrict__ po,
                                                 const float* __restrict__ ml, int ns, int D,
                                                 T* __restrict__ o, int lane) {
+  const int C4 = D >> 2;  // float4 columns of one partial row
+  if ((D & 3) == 0 && C4 <= 64 && (64 % C4) == 0 && ns <= 64) {
+    // Lane s holds split s's (m, l); lane (grp, col) sums column col of every
+    // groups-th split, then the groups are summed across lanes. Every (m, l)
+    // and the first kU rows of each lane are requested together, so the merge
+    // waits for memory once; a split's weight 2^(m_s - M) is computed by lane s
+    // and fetched from it (every lane takes part: callers run the whole wave).
+    // The same arithmetic, in the same order, as the general form below.
+    constexpr int kU = 8;
+    const int groups = 64 / C4;
+    const int col = lane % C4;
+    const int grp = lane / C4;
+    float mv = -INFINITY, lv = 0.f;
+    if (lane < ns) {
+      mv = part_ld<COH>(ml + 2 * lane);
+      lv = part_ld<COH>(ml + 2 * lane + 1);
+    }
+    float4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int s = grp + u * groups;
+      v[u] = s < ns ? part_ld4<COH>(po + (int64_t)s * D + 4 * col) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    const float M = wave_max(mv);
+    const float w = lane < ns ? exp2f(mv - M) : 0.f;
+    const float inv = 1.f / wave_sum(w * lv);
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int s = grp + u * groups;   // < 64
+      const float ww = __shfl(w, s);
+      if (s < ns) {
+        a.x = fmaf(ww, v[u].x, a.x);
+        a.y = fmaf(ww, v[u].y, a.y);
+        a.z = fmaf(ww, v[u].z, a.z);
+        a.w = fmaf(ww, v[u].w, a.w);
+      }
+    }
+    for (int s = grp + kU * groups; s < ns; s += groups) {   // (lanes diverge: no fetch)
+      const float4 x = part_ld4<COH>(po + (int64_t)s * D + 4 * col);
+      const float ww = exp2f(part_ld<COH>(ml + 2 * s) - M);
+      a.x = fmaf(ww, x.x, a.x);
+      a.y = fmaf(ww, x.y, a.y);
+      a.z = fmaf(ww, x.z, a.z);
+      a.w = fmaf(ww, x.w, a.w);
+    }
+    for (int off = C4; off < 64; off <<= 1) {
+      a.x += __shfl_xor(a.x, off);
+      a.y += __shfl_xor(a.y, off);
+      a.z += __shfl_xor(a.z, off);
+      a.w += __shfl_xor(a.w, off);
+    }
+    if (grp == 0) {
+      o[4 * col + 0] = from_f32<T>(a.x * inv);
+      o[4 * col + 1] = from_f32<T>(a.y * inv);
+      o[4 * col + 2] = from_f32<T>(a.z * inv);
+      o[4 * col + 3] = from_f32<T>(a.w * inv);
+    }
+    return;
+  }
   float M = -INFINITY;
   for (int s = lane; s < ns; s += 64) M = fmaxf(M, part_ld<COH>(ml + 2 * s));
   M = wave_max(M);
@@ -152,40 +212,37 @@ __device__ __forceinline__ void merge_split_row(const float* __restrict__ po,
     Lsum += exp2f(part_ld<COH>(ml + 2 * s) - M) * part_ld<COH>(ml + 2 * s + 1);
   Lsum = wave_sum(Lsum);
   const float inv = 1.f / Lsum;
-
-  const int C4 = D >> 2;  // float4 columns of one partial row
   if ((D & 3) == 0 && C4 <= 64 && (64 % C4) == 0) {
-    // Lane (grp, col): column col of every groups-th split, independent loads
-    // unrolled four deep, then the groups are summed across lanes.
+    // more than 64 splits: the same lanes and order, loads four deep
     const int groups = 64 / C4;
     const int col = lane % C4;
     const int grp = lane / C4;
     float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
     int s = grp;
     for (; s + 3 * groups < ns; s += 4 * groups) {
-      float4 v[4];
+      float4 x[4];
       float wt[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        v[u] = part_ld4<COH>(po + (int64_t)(s + u * groups) * D + 4 * col);
+        x[u] = part_ld4<COH>(po + (int64_t)(s + u * groups) * D + 4 * col);
         wt[u] = part_ld<COH>(ml + 2 * (s + u * groups));
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float ww = exp2f(wt[u] - M);
-        a.x = fmaf(ww, v[u].x, a.x);
-        a.y = fmaf(ww, v[u].y, a.y);
-        a.z = fmaf(ww, v[u].z, a.z);
-        a.w = fmaf(ww, v[u].w, a.w);
+        a.x = fmaf(ww, x[u].x, a.x);
+        a.y = fmaf(ww, x[u].y, a.y);
+        a.z = fmaf(ww, x[u].z, a.z);
+        a.w = fmaf(ww, x[u].w, a.w);
       }
     }
     for (; s < ns; s += groups) {
-      const float4 v = part_ld4<COH>(po + (int64_t)s * D + 4 * col);
+      const float4 x = part_ld4<COH>(po + (int64_t)s * D + 4 * col);
       const float ww = exp2f(part_ld<COH>(ml + 2 * s) - M);
-      a.x = fmaf(ww, v.x, a.x);
-      a.y = fmaf(ww, v.y, a.y);
-      a.z = fmaf(ww, v.z, a.z);
-      a.w = fmaf(ww, v.w, a.w);
+      a.x = fmaf(ww, x.x, a.x);
+      a.y = fmaf(ww, x.y, a.y);
+      a.z = fmaf(ww, x.z, a.z);
+      a.w = fmaf(ww, x.w, a.w);
     }
     for (int off = C4; off < 64; off <<= 1) {
       a.x += __shfl_xor(a.x, off);

@@ -206,31 +206,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
   const int c = lane & 15;
   const int gq = lane >> 4;
 
-  const int len = clamp_len(lens, i, max_ctx);
-  const int nblk = (len + 15) >> 4;
   const int b0 = s * bps;
   const int h = g * G + c;
   const bool qvalid = c < G;
-  if (b0 >= nblk) {
-    // an empty sequence writes zeros (without a combine launch, by its split 0)
-    if ((DIRECT || counters) && len == 0 && s == 0 && qvalid) {
-      uint16_t* o = out + ((int64_t)i * Hq + h) * D;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) = make_uint2(0u, 0u);
-    }
-    return;
-  }
-  const int b1 = min(b0 + bps, nblk);
 
   // The split's block ids, one per lane and register, read once ("load the
   // physical block pointers on chip"); each pair takes its two ids by readlane.
+  // They and the queries are requested before the sequence's length is known
+  // (ids past its blocks are read but never used), so the three loads overlap.
   const int32_t* trow = tables + (int64_t)i * max_blocks;
   int tb[4];
+  {
+    const int lim = min(b0 + bps, max_blocks);
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int idx = b0 + 64 * k + lane;
-    tb[k] = (64 * k < b1 - b0 && idx < b1) ? guard_block(trow[idx], N) : 0;
+    for (int k = 0; k < 4; ++k) {
+      const int idx = b0 + 64 * k + lane;
+      tb[k] = (64 * k < bps && idx < lim) ? guard_block(trow[idx], N) : 0;
+    }
   }
 
   // Q fragments (B operand of QK): Q[h][32*kc + 8*gq .. +8]; zero for padded columns.
@@ -244,6 +236,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
       qf[kc] = __builtin_bit_cast(bf16x8, v);
     }
   }
+
+  const int len = clamp_len(lens, i, max_ctx);
+  const int nblk = (len + 15) >> 4;
+  if (b0 >= nblk) {
+    // an empty sequence writes zeros (without a combine launch, by its split 0)
+    if ((DIRECT || counters) && len == 0 && s == 0 && qvalid) {
+      uint16_t* o = out + ((int64_t)i * Hq + h) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *reinterpret_cast<uint2*>(o + 16 * dt + 4 * gq) = make_uint2(0u, 0u);
+    }
+    return;
+  }
+  const int b1 = min(b0 + bps, nblk);
 
   f32x4 acc[DT];
 #pragma unroll
@@ -267,7 +273,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
     new_pos = len - 1;
     knew_row = knew + ((int64_t)i * Hkv + g) * D;
     const uint16_t* vnew_row = vnew + ((int64_t)i * Hkv + g) * D;
-    const int pn = guard_block(trow[new_pos >> 4], N);
+    const int pn = table_at(tb, (new_pos >> 4) - b0);
     const int on = new_pos & 15;
     uint16_t* kt = kpool + layer_off + ((int64_t)pn * Hkv + g) * (16 * D);
     if (lane < D / 8) {  // K row: lane moves dims 8*lane .. +8 (a 32-dim chunk takes 4 lanes)

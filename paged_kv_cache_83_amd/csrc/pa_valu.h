@@ -147,9 +147,29 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
   const int part = lane / KPI;     // which KE-dim slice of it
 
   const int bps = W * bpw;         // blocks of one split (workgroup)
+  const int B0 = s * bps;
+
+  // The wave's block ids (at most 64), one per lane, read once, and the group's
+  // G query rows (contiguous in q), loaded into registers and put in LDS once
+  // the first K/V loads are on their way: both requested before the sequence's
+  // length is known (ids past its blocks are read but never used).
+  const int32_t* trow = tables + (int64_t)i * max_blocks;
+  const int tb_idx = B0 + wv * bpw + lane;
+  const int tb = (lane < bpw && tb_idx < max_blocks) ? guard_block(trow[tb_idx], N) : 0;
+  constexpr int QPIECES = G * D * ES / 16;
+  constexpr int QPT = (QPIECES + 63) / 64;   // pieces per thread of a one-wave workgroup
+  u32x4 qreg[QPT];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((int64_t)i * Hq + (int64_t)g * G) * D);
+#pragma unroll
+    for (int j = 0; j < QPT; ++j) {
+      const int e = threadIdx.x + j * (int)blockDim.x;
+      qreg[j] = e < QPIECES ? src[e] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
   const int len = clamp_len(lens, i, max_ctx);
   const int nblk = (len + 15) >> 4;
-  const int B0 = s * bps;
   if (B0 >= nblk) {   // the whole workgroup (uniform)
     // an empty sequence writes zeros (without a combine launch, by its split 0)
     if ((direct || counters) && len == 0 && s == 0) {
@@ -164,23 +184,6 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
   const int b1 = min(b0 + bpw, nblk);
   const int span = active ? b1 - b0 : 1;
   const int lim = min(len, b1 * 16);  // keys at or past lim belong to a later wave / split or past the length
-
-  // The wave's block ids (at most 64), one per lane, read once.
-  const int32_t* trow = tables + (int64_t)i * max_blocks;
-  const int tb = (active && lane < span) ? guard_block(trow[b0 + lane], N) : 0;
-  // The group's G query rows (contiguous in q): loaded now into registers, put
-  // in LDS once the first K/V loads are on their way.
-  constexpr int QPIECES = G * D * ES / 16;
-  constexpr int QPT = (QPIECES + 63) / 64;   // pieces per thread of a one-wave workgroup
-  u32x4 qreg[QPT];
-  {
-    const u32x4* src = reinterpret_cast<const u32x4*>(q + ((int64_t)i * Hq + (int64_t)g * G) * D);
-#pragma unroll
-    for (int j = 0; j < QPT; ++j) {
-      const int e = threadIdx.x + j * (int)blockDim.x;
-      qreg[j] = e < QPIECES ? src[e] : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
 
   const T* kl = kpool + layer_off + (int64_t)g * TILE;   // + block * Hkv * TILE
   const T* vl = vpool + layer_off + (int64_t)g * TILE;
