@@ -338,7 +338,7 @@ __device__ __forceinline__ void fp8_compute_pair(Fp8Frags<D>& f, const bf16x8 (&
     acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(f.v[dt]), pf, acc[dt], 0, 0, 0);
 }
 
-template <int D, bool DIRECT, bool NT, int NS>
+template <int D, int OUT, bool NT, int NS>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_fp8_kernel(
     const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool,
     const uint16_t* __restrict__ q, uint16_t* __restrict__ out, float* __restrict__ part_o,
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   const bool qvalid = c < G;
   if (b0 >= nblk) {
     // an empty sequence writes zeros (without a combine launch, by its split 0)
-    if ((DIRECT || counters) && len == 0 && s == 0 && qvalid) {
+    if (OUT != kOutPartial && len == 0 && s == 0 && qvalid) {
       uint16_t* o = out + ((int64_t)i * Hq + h) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -445,8 +445,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
   }
 
   l_run = sum_over_groups(l_run);
-  mfma_split_epilogue<D>(acc, m_run, l_run, lane, i, g, G, Hq, Hkv, s, S_max, (nblk + bps - 1) / bps,
-                         DIRECT, out, part_o, part_ml, counters);
+  mfma_split_epilogue<D, OUT>(acc, m_run, l_run, lane, i, g, G, Hq, Hkv, s, S_max, (nblk + bps - 1) / bps,
+                         out, part_o, part_ml, counters);
 }
 
 }  // namespace pa_detail

@@ -176,7 +176,7 @@ __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)
 // RAGGED: the work items come from a list in the arguments (ragged batches:
 // only long sequences split, longest items first) instead of the uniform grid
 // of every sequence's S_max splits.
-template <int D, bool DIRECT, bool NT, bool APPEND, bool RAGGED>
+template <int D, int OUT, bool NT, bool APPEND, bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : PA_MFMA_WPE))) void decode_mfma_bf16_kernel(
     uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ knew,
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
   const int nblk = (len + 15) >> 4;
   if (b0 >= nblk) {
     // an empty sequence writes zeros (without a combine launch, by its split 0)
-    if ((DIRECT || counters) && len == 0 && s == 0 && qvalid) {
+    if (OUT != kOutPartial && len == 0 && s == 0 && qvalid) {
       uint16_t* o = out + ((int64_t)i * Hq + h) * D;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
@@ -345,8 +345,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
 
   l_run = sum_over_groups(l_run);
   // acc[dt][e] = O^T[d = 16*dt + 4*gq + e][q = c]
-  mfma_split_epilogue<D>(acc, m_run, l_run, lane, i, g, G, Hq, Hkv, s, S_max, (nblk + bps - 1) / bps,
-                         DIRECT, out, part_o, part_ml, counters);
+  mfma_split_epilogue<D, OUT>(acc, m_run, l_run, lane, i, g, G, Hq, Hkv, s, S_max, (nblk + bps - 1) / bps,
+                         out, part_o, part_ml, counters);
 }
 
 // =============================================================================
@@ -860,6 +860,13 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   {
     ProfScope ps("decode_partial", st, timing);
     const dim3 grid((unsigned)items), block(64);
+    // the matrix-core kernels take the output mode as a template argument
+#define PA_OUT_MODE(LAUNCH, DD)                                    \
+  do {                                                             \
+    if (plan.direct) LAUNCH(DD, kOutDirect);                       \
+    else if (plan.merge) LAUNCH(DD, kOutMerge);                    \
+    else LAUNCH(DD, kOutPartial);                                  \
+  } while (0)
     if (plan.kernel == 3) {
       const int64_t off8 = (int64_t)layer * g->num_blocks * Hkv * tile_bytes(g);
 #define PA_FP8_LAUNCH_X(DD, DIR, NTV)                                                              \
@@ -873,11 +880,8 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
     if (plan.stream_kv) PA_FP8_LAUNCH_X(DD, DIR, true);          \
     else PA_FP8_LAUNCH_X(DD, DIR, false);                        \
   } while (0)
-      if (D == 64) {
-        if (plan.direct) PA_FP8_LAUNCH(64, true); else PA_FP8_LAUNCH(64, false);
-      } else {
-        if (plan.direct) PA_FP8_LAUNCH(128, true); else PA_FP8_LAUNCH(128, false);
-      }
+      if (D == 64) PA_OUT_MODE(PA_FP8_LAUNCH, 64);
+      else PA_OUT_MODE(PA_FP8_LAUNCH, 128);
 #undef PA_FP8_LAUNCH
 #undef PA_FP8_LAUNCH_X
     } else if (plan.kernel == 2) {
@@ -903,17 +907,14 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
     if (plan.stream_kv) PA_MFMA_LAUNCH_NT(DD, DIR, true);                \
     else PA_MFMA_LAUNCH_NT(DD, DIR, false);                              \
   } while (0)
-      if (D == 64) {
-        if (plan.direct) PA_MFMA_LAUNCH(64, true); else PA_MFMA_LAUNCH(64, false);
-      } else if (D == 128) {
-        if (plan.direct) PA_MFMA_LAUNCH(128, true); else PA_MFMA_LAUNCH(128, false);
-      } else {
-        if (plan.direct) PA_MFMA_LAUNCH(256, true); else PA_MFMA_LAUNCH(256, false);
-      }
+      if (D == 64) PA_OUT_MODE(PA_MFMA_LAUNCH, 64);
+      else if (D == 128) PA_OUT_MODE(PA_MFMA_LAUNCH, 128);
+      else PA_OUT_MODE(PA_MFMA_LAUNCH, 256);
 #undef PA_MFMA_LAUNCH
 #undef PA_MFMA_LAUNCH_NT
 #undef PA_MFMA_LAUNCH_X
 #undef PA_MFMA_LAUNCH_RG
+#undef PA_OUT_MODE
     } else if (plan.kernel == 4) {
 #define PA_VALU_LAUNCH_X(T, DD, GG, NTV)                                                          \
   hipLaunchKernelGGL((decode_valu_kernel<T, DD, GG, NTV>), grid, dim3(64 * plan.wg_waves),         \

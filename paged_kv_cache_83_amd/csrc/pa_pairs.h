@@ -91,21 +91,28 @@ __device__ __forceinline__ void issue_pair(PairFrags<D>& f, const uint16_t* __re
   for (int dt = 0; dt < DT; ++dt) f.v[dt] = kv_load16<NT>(vrow + dt * 256 + v_off);
 }
 
+// How a matrix-core decode launch hands out its results (a template argument
+// of the kernels, so that a launch carries only the code of its own mode): the
+// outputs themselves (one split covers every sequence), split partials for the
+// combine launch, or split partials merged inside the launch by each
+// sequence's last split.
+enum : int { kOutPartial = 0, kOutDirect = 1, kOutMerge = 2 };
+
 // End of a matrix-core decode work item (sequence i, KV head g, split s). Lane
 // (c = lane % 16, gq = lane / 16) holds O^T[d = 16*dt + 4*gq + e][query c] in
 // acc[dt][e] for query head h = g*G + c (valid for c < G), and the split's
 // (m, l) for that head (l already summed over the lane groups). A split that
-// covers the sequence (direct plan, or a one-split sequence when counters are
-// given) writes the normalised output; otherwise the split's partial row goes
-// to the workspace -- with counters as coherent stores, after which the last
-// split of (i, g) to finish merges every row of the group (the in-kernel merge
-// of "KV Cache Management", section "Chunked prefill mechanics"). Called by the
-// whole wave.
-template <int D>
+// covers the sequence (kOutDirect, or a one-split sequence) writes the
+// normalised output; otherwise the split's partial row goes to the workspace --
+// with kOutMerge as coherent stores, after which the last split of (i, g) to
+// finish (counted in counters) merges every row of the group (the in-kernel
+// merge of "KV Cache Management", section "Chunked prefill mechanics"). Called
+// by the whole wave.
+template <int D, int OUT>
 __device__ __forceinline__ void mfma_split_epilogue(const f32x4 (&acc)[D / 16], float m_run,
                                                     float l_run, int lane, int i, int g, int G,
                                                     int Hq, int Hkv, int s, int S_max, int ns,
-                                                    bool direct, uint16_t* __restrict__ out,
+                                                    uint16_t* __restrict__ out,
                                                     float* __restrict__ part_o,
                                                     float* __restrict__ part_ml,
                                                     int* __restrict__ counters) {
@@ -114,7 +121,7 @@ __device__ __forceinline__ void mfma_split_epilogue(const f32x4 (&acc)[D / 16], 
   const int gq = lane >> 4;
   const int h = g * G + c;
   const bool qvalid = c < G;
-  if (direct || ns == 1) {   // one split covers the sequence: the output itself
+  if (OUT == kOutDirect || ns == 1) {   // one split covers the sequence: the output itself
     if (!qvalid) return;
     const float inv = 1.f / l_run;
     uint16_t* o = out + ((int64_t)i * Hq + h) * D;
@@ -127,7 +134,7 @@ __device__ __forceinline__ void mfma_split_epilogue(const f32x4 (&acc)[D / 16], 
   }
   const int64_t row = ((int64_t)i * Hq + (qvalid ? h : g * G)) * S_max + s;
   float* po = part_o + row * D;
-  if (!counters) {
+  if constexpr (OUT == kOutPartial) {
     if (!qvalid) return;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -138,7 +145,7 @@ __device__ __forceinline__ void mfma_split_epilogue(const f32x4 (&acc)[D / 16], 
       part_ml[row * 2 + 1] = l_run;
     }
     return;
-  }
+  } else {
   if (qvalid) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
@@ -158,6 +165,7 @@ __device__ __forceinline__ void mfma_split_epilogue(const f32x4 (&acc)[D / 16], 
     }
     if (lane == 0) __hip_atomic_store(counters + (int64_t)i * Hkv + g, 0, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT);
+  }
   }
 }
 
