@@ -75,6 +75,8 @@ def parse():
                          "VALU kernel, where it is faster; the MFMA kernels' last split would "
                          "merge all eight heads serially, slower than the combine launch)")
     ap.add_argument("--no-merge", action="store_true", help="same as --merge off")
+    ap.add_argument("--kv-reuse", action="store_true",
+                    help="decode workloads: cached instead of non-temporal K/V loads")
     ap.add_argument("--no-ragged", action="store_true",
                     help="do not give the library the host copy of the lengths (no ragged plan)")
     ap.add_argument("--chunk-blocks", type=int, default=-1,
@@ -342,7 +344,8 @@ def run_decode(args):
         steps.decode_step(geom, k_pool, v_pool, q_all, k_new, v_new, slots, tables, lens, max_ctx, out,
                           ws, blocks_per_split=args.bps, kernel=args.kernel, stream=stream,
                           around_decode=around, fused=not args.unfused, merge=merge,
-                          waves_per_group=args.wg_waves, host_lens=host_lens)
+                          waves_per_group=args.wg_waves, host_lens=host_lens,
+                          kv_reuse=args.kv_reuse)
 
     for _ in range(args.warmup):
         step()

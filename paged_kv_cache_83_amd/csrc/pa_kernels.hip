@@ -100,14 +100,15 @@ __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)
     }
     // The new token's V goes into the pool as its whole tile: the lanes holding
     // that block (every dimension, both halves of the slots) write their
-    // fragments -- as loaded, with the new slot patched -- as 16-byte stores,
-    // where storing the one new element per dimension row would touch 128
-    // separate 32-byte pieces of the tile with 2-byte writes.
+    // fragments -- as loaded, with the new slot patched -- as 16-byte
+    // non-temporal stores, where storing the one new element per dimension row
+    // would touch 128 separate 32-byte pieces of the tile with 2-byte writes.
     if ((gq >> 1) == ((new_pos - blk * 16) >> 4)) {
       const int c = threadIdx.x & 15;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
-        *reinterpret_cast<u32x4*>(vt_new + (16 * dt + c) * 16 + 8 * (gq & 1)) = f.v[dt];
+        __builtin_nontemporal_store(f.v[dt],
+                                    reinterpret_cast<u32x4*>(vt_new + (16 * dt + c) * 16 + 8 * (gq & 1)));
     }
   }
   f32x4 sc[2];
@@ -297,6 +298,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
 
   const int span = b1 - b0;
   const int npairs = (span + 1) >> 1;
+  auto blk_of = [&](int pj) { return b0 + 2 * pj; };   // first block of pair pj
   auto ids = [&](int pj, int& p0, int& p1) {
     const int off = 2 * pj;
     p0 = table_at(tb, off);
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
     int p0, p1;
     ids(pj, p0, p1);
     issue_pair<D, NT>(fr, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, gq,
-                      new_pos >= 0 ? new_pos - 16 * (b0 + 2 * pj) : -1, knew_row);
+                      new_pos >= 0 ? new_pos - 16 * blk_of(pj) : -1, knew_row);
   };
   int pj = 0;
   if (npairs >= 2 * NS - 1) {
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
 #pragma unroll
       for (int st = 0; st < NS; ++st) {
         issue_at(f[(st + NS - 1) % NS], pj + st + NS - 1);
-        compute_pair<D>(f[st], qf, acc, m_run, l_run, b0 + 2 * (pj + st), len, gq, qk_scale,
+        compute_pair<D>(f[st], qf, acc, m_run, l_run, blk_of(pj + st), len, gq, qk_scale,
                         new_pos, vnw, vt_new);
       }
     }
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1
   for (int k = 0; k < 2 * NS - 2; ++k) {
     if (pj + k >= npairs) break;
     if (pj + k + NS - 1 < npairs) issue_at(f[(k + NS - 1) % NS], pj + k + NS - 1);
-    compute_pair<D>(f[k % NS], qf, acc, m_run, l_run, b0 + 2 * (pj + k), len, gq, qk_scale, new_pos,
+    compute_pair<D>(f[k % NS], qf, acc, m_run, l_run, blk_of(pj + k), len, gq, qk_scale, new_pos,
                     vnw, vt_new);
   }
 
