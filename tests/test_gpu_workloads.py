@@ -49,11 +49,14 @@ def _managers(cfg, histories):
     return ob, lb, oseqs, lseqs, otables, np.asarray(oslots, np.int64)
 
 
-def test_gpt2_fp32_all_outputs():
-    """GPT-2-small geometry, fp32: every layer, every sequence, every head."""
+@pytest.mark.parametrize("merge", [True, False], ids=["merge_in_launch", "combine_launch"])
+def test_gpt2_fp32_all_outputs(merge):
+    """GPT-2-small geometry, fp32: every layer, every sequence, every head; with
+    the splits merged inside the decode launch (the benchmark's configuration)
+    and by the combine launch."""
     need_gpu()
     cfg = get_config("gpt2_fp32")
-    print_case(test="workload", cfg=cfg.name)
+    print_case(test="workload", cfg=cfg.name, merge=merge)
     lengths = gen.context_lengths(cfg)
     batch = make_batch("f32", cfg.num_layers, cfg.num_blocks, cfg.num_q_heads, cfg.num_kv_heads,
                        cfg.head_dim, cfg.block_size, lengths, seed=cfg.seed)
@@ -66,10 +69,11 @@ def test_gpt2_fp32_all_outputs():
     tabs = torch.from_numpy(padded_tables(batch.tables, batch.max_blocks)).cuda()
     lens = torch.from_numpy(lengths.astype(np.int32)).cuda()
     out = torch.empty_like(q_all)
-    ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, n, cfg.num_q_heads, int(lengths.max()))),
-                     dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(1, pk.decode_workspace_bytes(geom, n, cfg.num_q_heads, int(lengths.max()),
+                                                      merge=merge)),
+                     dtype=torch.uint8, device="cuda")   # merge counters start at zero
     steps.decode_step(geom, K, V, q_all, kn, vn, torch.from_numpy(batch.slots_new).cuda(), tabs, lens,
-                      int(lengths.max()), out, ws)
+                      int(lengths.max()), out, ws, merge=merge)
     torch.cuda.synchronize()
     got_k, got_v, got = to_host(K, "f32"), to_host(V, "f32"), out.cpu().numpy()
     kp, vp = batch.k_pool, batch.v_pool
@@ -83,7 +87,7 @@ def test_gpt2_fp32_all_outputs():
         assert max_abs_err(got[layer], expect, "f32") <= F32_TOL, layer
 
 
-def _run_decode_workload(name, n_samples, seed_offset=0, bps=0):
+def _run_decode_workload(name, n_samples, seed_offset=0, bps=0, ragged=False):
     cfg = get_config(name)
     geom = _geom(cfg)
     lengths = gen.context_lengths(cfg)
@@ -108,10 +112,11 @@ def _run_decode_workload(name, n_samples, seed_offset=0, bps=0):
     lens_d = torch.from_numpy(np.ascontiguousarray(lens)).cuda()
     max_ctx = int(lengths.max())
     out = torch.empty_like(q_all)
-    ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, bps)), dtype=torch.uint8,
-                     device="cuda")
+    host_lens = np.ascontiguousarray(lens, np.int32) if ragged else None
+    ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, n, Hq, max_ctx, bps, host_lens=host_lens)),
+                     dtype=torch.uint8, device="cuda")
     steps.decode_step(geom, K, V, q_all, kn, vn, torch.from_numpy(oslots).cuda(), tabs, lens_d, max_ctx,
-                      out, ws, blocks_per_split=bps)
+                      out, ws, blocks_per_split=bps, host_lens=host_lens)
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all()
     errs = []
@@ -135,17 +140,21 @@ def _run_decode_workload(name, n_samples, seed_offset=0, bps=0):
     return errs
 
 
-def test_chat_ragged_full_geometry_sampled():
+@pytest.mark.parametrize("ragged", [True, False], ids=["ragged_plan", "uniform_plan"])
+def test_chat_ragged_full_geometry_sampled(ragged):
+    """The chat-like batch at full size, with the ragged launch plan the benchmark
+    uses (a host copy of the lengths) and with the uniform plan."""
     need_gpu()
-    print_case(test="workload", cfg="chat_ragged")
-    _run_decode_workload("chat_ragged", n_samples=24)
+    print_case(test="workload", cfg="chat_ragged", ragged=ragged)
+    _run_decode_workload("chat_ragged", n_samples=24, ragged=ragged)
 
 
 def test_gqa70b_32k_full_size_sampled():
-    """The benchmark workload at full size (171.8 GB pool), default launch plan."""
+    """The benchmark workload at full size (171.8 GB pool), default launch plan
+    (the benchmark's): 16 sampled (sequence, layer) outputs."""
     need_gpu()
     print_case(test="workload", cfg="gqa70b_32k")
-    _run_decode_workload("gqa70b_32k", n_samples=6)
+    _run_decode_workload("gqa70b_32k", n_samples=16)
 
 
 def test_fork_cow_full_geometry():
@@ -192,7 +201,7 @@ def test_fork_cow_full_geometry():
     kn = torch.randn((L, cfg.num_seqs, Hkv, d), generator=g, device="cuda").to(geom.torch_dtype)
     vn = torch.randn((L, cfg.num_seqs, Hkv, d), generator=g, device="cuda").to(geom.torch_dtype)
     rng = np.random.default_rng(cfg.seed)
-    samples = [(int(rng.integers(0, cfg.num_seqs)), int(rng.integers(0, L))) for _ in range(4)]
+    samples = [(int(rng.integers(0, cfg.num_seqs)), int(rng.integers(0, L))) for _ in range(12)]
     # snapshots for the oracle: the prefix tail and each sampled branch's blocks
     # before anything runs (copy and appends then happen on the oracle side too)
     pre = {}
