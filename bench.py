@@ -1557,8 +1557,9 @@ def run_prefix_reuse(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
-              "supported (see the sharding note in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: the decode path here runs on exactly one GPU; --gpus {args.gpus} is not "
+              "supported (across GPUs the path would shard by KV head or by sequence, with "
+              "no exchange inside it)", file=sys.stderr)
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
