@@ -309,6 +309,9 @@ RAGGED_PLAN_CASES = [
     ("items_of_6", 64, 8, 128, [300, 1, 900, 40, 0], 6, False),
     ("items_of_4_merge_d64", 32, 2, 64, [129, 3000, 7, 640], 4, True),
     ("items_of_2_g16_d64", 32, 2, 64, RAGGED, 2, False),
+    # longest sequence within three balanced items: one item each, outputs direct
+    ("unsplit_auto", 32, 8, 128, [1, 40, 300, 700, 17, 100, 0], 0, False),
+    ("unsplit_auto_merge", 32, 8, 128, [1, 40, 300, 700, 17, 100, 0], 0, True),
 ]
 
 
