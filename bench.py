@@ -500,8 +500,9 @@ def run_decode(args):
                    "pool_blocks": cfg.num_blocks, "kv_bytes_per_step": kv_bytes_step,
                    "global_batch": n, "seq_len": int(lengths.max()), "parallelism": "none (1 GPU)",
                    "append": "separate launch" if args.unfused else "fused into decode",
-                   "split_merge": "inside the decode launch (where splits exist)" if merge
-                   else "separate launch",
+                   "split_merge": ("none (every sequence in one split)" if ws_bytes == 0
+                                   else "inside the decode launch (where splits exist)" if merge
+                                   else "separate launch"),
                    "launch": "hip graph replay" if args.graph else "eager"},
         "step_ms": step_ms,
         "tokens_per_s": round(n / (ms_per_step * 1e-3), 2),
@@ -509,10 +510,10 @@ def run_decode(args):
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "kernels": kernel_ms,
-        "kernels_timing": ("hipEvent pairs the library records on the launch stream around every "
-                           f"{args.prof_every}th layer's launches; a pair adds about 2 us to a short "
-                           "kernel, so the rocprofv3 trace under profiles/ is the reference for short "
-                           "kernels (the combine above all)") if kernel_ms else None,
+        "kernels_timing": ("every {}th layer's launches, from a start event the library records "
+                           "on the launch stream before the kernel to a stop event the kernel's "
+                           "own launch takes at its end (hipExtLaunchKernelGGL)"
+                           .format(args.prof_every)) if kernel_ms else None,
         "parity": parity,
     }
     if cold is not None:

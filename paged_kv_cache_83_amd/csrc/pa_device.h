@@ -1,6 +1,7 @@
-// Pieces shared by the kernel translation units of libpa (gfx950): operand
-// vector types, bf16 conversion, 16-byte moves, the cross-lane-group
-// reductions the matrix-core kernels use, argument checks and launch timing.
+// Device pieces shared by the kernel translation units of libpa (gfx950):
+// operand vector types, bf16 conversion, 16-byte moves, the cross-lane-group
+// reductions the matrix-core kernels use, split partial loads, stores and
+// merges. The host side (argument checks, launch timing) is in pa_host.h.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -281,31 +282,5 @@ __device__ __forceinline__ bool split_arrive_last(int* counter, int ns, int lane
   asm volatile("" ::: "memory");
   return prev == ns - 1;
 }
-
-inline bool geom_ok(const pa_geom* g) {
-  return g && g->num_layers > 0 && g->num_kv_heads > 0 && g->head_dim > 0 && g->block_size > 0 &&
-         g->num_blocks > 0 && (g->dtype == PA_F32 || g->dtype == PA_BF16 || g->dtype == PA_FP8);
-}
-inline int64_t esize(const pa_geom* g) {
-  return g->dtype == PA_F32 ? 4 : g->dtype == PA_BF16 ? 2 : 1;
-}
-// Bytes of one (layer, block, head) tile of K or V: B*d elements, and for FP8
-// pools the B scale bytes that follow them.
-inline int64_t tile_bytes(const pa_geom* g) {
-  return (int64_t)g->block_size * g->head_dim * esize(g) + (g->dtype == PA_FP8 ? g->block_size : 0);
-}
-
-inline pa_status launch_status() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_HIP; }
-
-// Records hipEvents around one launch when timing is on (pa_prof_enable) and
-// `allowed` (the allocation-free entry point creates no events).
-struct ProfScope {
-  const char* name;
-  hipStream_t st;
-  hipEvent_t a = nullptr, b = nullptr;
-  bool on;
-  ProfScope(const char* n, hipStream_t s, bool allowed = true);
-  ~ProfScope();
-};
 
 }  // namespace pa_detail

@@ -36,6 +36,7 @@
 
 #include "../../include/pa.h"
 #include "pa_device.h"
+#include "pa_host.h"
 #include "pa_append.h"
 #include "pa_move.h"
 #include "pa_fp8.h"
@@ -744,20 +745,31 @@ pa_status make_plan(const pa_geom* g, int32_t n_seqs, int32_t Hq, int32_t max_ct
 }  // namespace
 
 namespace pa_detail {
-ProfScope::ProfScope(const char* n, hipStream_t s, bool allowed) : name(n), st(s), on(false) {
+ProfScope::ProfScope(const char* n, hipStream_t s, bool allowed, bool bind_kernel)
+    : name(n), st(s), on(false), bind(bind_kernel) {
   if (!allowed) return;
   std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
-  if (hipEventCreate(&a) != hipSuccess) return;
+  // the start marker carries no data: no system-scope fence when it completes
+  if (hipEventCreateWithFlags(&a, hipEventDisableSystemFence) != hipSuccess) return;
   if (hipEventCreate(&b) != hipSuccess) {
     (void)hipEventDestroy(a);
     return;
   }
   on = hipEventRecord(a, st) == hipSuccess;
+  if (!on) {
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+  }
 }
 ProfScope::~ProfScope() {
   if (!on) return;
-  (void)hipEventRecord(b, st);
+  if (bind && !bound) {  // the launch never took place (an argument error)
+    (void)hipEventDestroy(a);
+    (void)hipEventDestroy(b);
+    return;
+  }
+  if (!bind) (void)hipEventRecord(b, st);
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_pending.push_back({name, a, b});
 }
@@ -788,29 +800,29 @@ pa_status pa_append_kv(const pa_geom* g, void* k_pool, void* v_pool, int32_t lay
   }
   const size_t lds = g->dtype == PA_BF16 ? append_lds_bytes<uint16_t>(D) : append_lds_bytes<float>(D);
   if (lds > 65536) return PA_ERR_UNSUPPORTED;
-  ProfScope ps("append", st);
+  ProfScope ps("append", st, true, true);
   const int64_t items = ((int64_t)n_tokens + kAppendChunk - 1) / kAppendChunk * H;
   const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;  // a multiple of the XCD count
   if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)wgs);
   if (g->dtype == PA_BF16) {
     if (D % 8 == 0)
-      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 8, SlotsFromArray>), grid, dim3(256), lds, st,
+      PA_TIMED_LAUNCH(ps, (append_kv_kernel<uint16_t, 8, SlotsFromArray>), grid, dim3(256), lds, st,
                          (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_new,
                          (const uint16_t*)v_new, SlotsFromArray{slot_mapping}, n_tokens, H, D, B, nslots,
                          layer_off);
     else
-      hipLaunchKernelGGL((append_kv_kernel<uint16_t, 1, SlotsFromArray>), grid, dim3(256), lds, st,
+      PA_TIMED_LAUNCH(ps, (append_kv_kernel<uint16_t, 1, SlotsFromArray>), grid, dim3(256), lds, st,
                          (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)k_new,
                          (const uint16_t*)v_new, SlotsFromArray{slot_mapping}, n_tokens, H, D, B, nslots,
                          layer_off);
   } else {
     if (D % 4 == 0)
-      hipLaunchKernelGGL((append_kv_kernel<float, 4, SlotsFromArray>), grid, dim3(256), lds, st,
+      PA_TIMED_LAUNCH(ps, (append_kv_kernel<float, 4, SlotsFromArray>), grid, dim3(256), lds, st,
                          (float*)k_pool, (float*)v_pool, (const float*)k_new, (const float*)v_new,
                          SlotsFromArray{slot_mapping}, n_tokens, H, D, B, nslots, layer_off);
     else
-      hipLaunchKernelGGL((append_kv_kernel<float, 1, SlotsFromArray>), grid, dim3(256), lds, st,
+      PA_TIMED_LAUNCH(ps, (append_kv_kernel<float, 1, SlotsFromArray>), grid, dim3(256), lds, st,
                          (float*)k_pool, (float*)v_pool, (const float*)k_new, (const float*)v_new,
                          SlotsFromArray{slot_mapping}, n_tokens, H, D, B, nslots, layer_off);
   }
@@ -867,7 +879,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   {
-    ProfScope ps("decode_partial", st, timing);
+    ProfScope ps("decode_partial", st, timing, true);
     const dim3 grid((unsigned)items), block(64);
     // the matrix-core kernels take the output mode as a template argument
 #define PA_OUT_MODE(LAUNCH, DD)                                    \
@@ -879,7 +891,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
     if (plan.kernel == 3) {
       const int64_t off8 = (int64_t)layer * g->num_blocks * Hkv * tile_bytes(g);
 #define PA_FP8_LAUNCH_X(DD, DIR, NTV)                                                              \
-  hipLaunchKernelGGL((decode_mfma_fp8_kernel<DD, DIR, NTV, PA_FP8_STAGES>), grid, block, 0, st,     \
+  PA_TIMED_LAUNCH(ps, (decode_mfma_fp8_kernel<DD, DIR, NTV, PA_FP8_STAGES>), grid, block, 0, st,     \
                      (const uint8_t*)k_pool, (const uint8_t*)v_pool, (const uint16_t*)q,            \
                      (uint16_t*)out, part_o, part_ml, block_tables, context_lens, off8,           \
                      g->num_blocks, Hkv, n_q_heads, G, max_blocks_per_seq, max_context_len,       \
@@ -895,7 +907,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
 #undef PA_FP8_LAUNCH_X
     } else if (plan.kernel == 2) {
 #define PA_MFMA_LAUNCH_RG(DD, DIR, NTV, APP, RG, ITEMS)                                           \
-  hipLaunchKernelGGL((decode_mfma_bf16_kernel<DD, DIR, NTV, APP, RG>), grid, block, 0, st,        \
+  PA_TIMED_LAUNCH(ps, (decode_mfma_bf16_kernel<DD, DIR, NTV, APP, RG>), grid, block, 0, st,        \
                      (uint16_t*)k_pool, (uint16_t*)v_pool, (const uint16_t*)q,                     \
                      (const uint16_t*)knew, (const uint16_t*)vnew, (uint16_t*)out, part_o,         \
                      part_ml, block_tables, context_lens, layer_off, g->num_blocks, Hkv,          \
@@ -926,7 +938,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
 #undef PA_OUT_MODE
     } else if (plan.kernel == 4) {
 #define PA_VALU_LAUNCH_X(T, DD, GG, NTV)                                                          \
-  hipLaunchKernelGGL((decode_valu_kernel<T, DD, GG, NTV>), grid, dim3(64 * plan.wg_waves),         \
+  PA_TIMED_LAUNCH(ps, (decode_valu_kernel<T, DD, GG, NTV>), grid, dim3(64 * plan.wg_waves),         \
                      valu_lds_bytes(g, G, plan.wg_waves), st, (T*)k_pool,                          \
                      (T*)v_pool, (const T*)q, (const T*)knew, (const T*)vnew, (T*)out, part_o,     \
                      part_ml, block_tables, context_lens, layer_off, g->num_blocks, Hkv,          \
@@ -955,7 +967,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
     } else {
       const size_t lds = generic_lds_bytes(G, D, B);
 #define PA_GEN_LAUNCH_X(T, DIR, RR, APP)                                                          \
-  hipLaunchKernelGGL((decode_generic_kernel<T, DIR, RR, APP>), grid, block, lds, st, (T*)k_pool,  \
+  PA_TIMED_LAUNCH(ps, (decode_generic_kernel<T, DIR, RR, APP>), grid, block, lds, st, (T*)k_pool,  \
                      (T*)v_pool, (const T*)q, (const T*)knew, (const T*)vnew, (T*)out, part_o,     \
                      part_ml, block_tables, context_lens, layer_off, g->num_blocks, Hkv,          \
                      n_q_heads, G, D, B, max_blocks_per_seq, max_context_len, plan.bps,            \
@@ -985,17 +997,17 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   if (!plan.direct && !plan.merge) {
-    ProfScope ps("decode_combine", st, timing);
+    ProfScope ps("decode_combine", st, timing, true);
     const dim3 grid((unsigned)((int64_t)n_seqs * n_q_heads)), block(64);
     // the MFMA and streaming VALU kernels write a one-split sequence's output
     // themselves; the generic kernel leaves every split to the combine
     const int single_written = plan.kernel != 1;
     if (g->dtype == PA_F32)  // bf16 output for bf16 and fp8 pools
-      hipLaunchKernelGGL((decode_combine_kernel<float>), grid, block, 0, st, part_o, part_ml,
+      PA_TIMED_LAUNCH(ps, (decode_combine_kernel<float>), grid, block, 0, st, part_o, part_ml,
                          (float*)out, context_lens, n_q_heads, D, B, plan.S_max, plan.bps,
                          max_context_len, single_written);
     else
-      hipLaunchKernelGGL((decode_combine_kernel<uint16_t>), grid, block, 0, st, part_o, part_ml,
+      PA_TIMED_LAUNCH(ps, (decode_combine_kernel<uint16_t>), grid, block, 0, st, part_o, part_ml,
                          (uint16_t*)out, context_lens, n_q_heads, D, B, plan.S_max, plan.bps,
                          max_context_len, single_written);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;

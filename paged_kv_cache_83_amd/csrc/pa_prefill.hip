@@ -43,6 +43,7 @@
 #include "pa_append.h"
 #include "pa_addr.h"
 #include "pa_device.h"
+#include "pa_host.h"
 #include "pa_fp8.h"
 #include "pa_pairs.h"
 
@@ -933,22 +934,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((CT * D > 12
 }
 
 template <int D, int G, bool FP8>
-void launch_prefill(dim3 grid, size_t lds, hipStream_t st, const char* kp, const char* vp,
+void launch_prefill(dim3 grid, size_t lds, ProfScope& ps, const char* kp, const char* vp,
                     const uint16_t* q, uint16_t* out, ChunkBatch cb, const int32_t* tables,
                     int64_t layer_off, int N, int Hkv, int Hq, int max_blocks, int n_tiles,
                     float qk_scale, PfSplit sp) {
-  hipLaunchKernelGGL((prefill_mfma_kernel<D, G, FP8>), grid, dim3(256), lds, st, kp, vp, q, out, cb,
-                     tables, layer_off, N, Hkv, Hq, max_blocks, n_tiles, qk_scale, sp);
+  PA_TIMED_LAUNCH(ps, (prefill_mfma_kernel<D, G, FP8>), grid, dim3(256), lds, ps.st, kp, vp, q, out,
+                  cb, tables, layer_off, N, Hkv, Hq, max_blocks, n_tiles, qk_scale, sp);
 }
 
 template <int D, bool FP8>
-bool launch_prefill_g(int G, dim3 grid, size_t lds, hipStream_t st, const char* kp,
+bool launch_prefill_g(int G, dim3 grid, size_t lds, ProfScope& ps, const char* kp,
                       const char* vp, const uint16_t* q, uint16_t* out, ChunkBatch cb,
                       const int32_t* tables, int64_t layer_off, int N, int Hkv, int Hq,
                       int max_blocks, int n_tiles, float qk_scale, PfSplit sp) {
 #define PA_PF_CASE(GG)                                                                     \
   case GG:                                                                                \
-    launch_prefill<D, GG, FP8>(grid, lds, st, kp, vp, q, out, cb, tables, layer_off, N, Hkv,  \
+    launch_prefill<D, GG, FP8>(grid, lds, ps, kp, vp, q, out, cb, tables, layer_off, N, Hkv,  \
                                Hq, max_blocks, n_tiles, qk_scale, sp);                     \
     return true;
   switch (G) {
@@ -1109,15 +1110,15 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
       return PA_ERR_UNSUPPORTED;
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   } else {  // the chunks' keys and values go to their positions through the block tables
-    ProfScope ps("prefill_append", st);
+    ProfScope ps("prefill_append", st, true, true);
     const int64_t items = ((int64_t)n_tokens + kAppendChunk - 1) / kAppendChunk * Hkv;
     const int64_t wgs = (items + kXcds - 1) / kXcds * kXcds;
     if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
     const SlotsFromTables src{cb, block_tables, max_blocks_per_seq, B, g->num_blocks};
-    hipLaunchKernelGGL((append_kv_kernel<uint16_t, 8, SlotsFromTables>), dim3((unsigned)wgs),
-                       dim3(256), append_lds_bytes<uint16_t>(D), st, (uint16_t*)k_pool,
-                       (uint16_t*)v_pool, (const uint16_t*)k_new, (const uint16_t*)v_new, src,
-                       n_tokens, Hkv, D, B, (int64_t)g->num_blocks * B, layer_off / 2);
+    PA_TIMED_LAUNCH(ps, (append_kv_kernel<uint16_t, 8, SlotsFromTables>), dim3((unsigned)wgs),
+                    dim3(256), append_lds_bytes<uint16_t>(D), st, (uint16_t*)k_pool,
+                    (uint16_t*)v_pool, (const uint16_t*)k_new, (const uint16_t*)v_new, src,
+                    n_tokens, Hkv, D, B, (int64_t)g->num_blocks * B, layer_off / 2);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   PfSplit sp{S, nullptr, nullptr};
@@ -1126,7 +1127,7 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
     sp.part_ml = sp.part_o + (int64_t)n_tokens * n_q_heads * S * D;
   }
   {
-    ProfScope ps(plan.short_path ? "prefill_short" : "prefill_attention", st);
+    ProfScope ps(plan.short_path ? "prefill_short" : "prefill_attention", st, true, true);
     if (!(scale > 0.f)) scale = 1.f / std::sqrt((float)D);
     const float qk_scale = scale * kLog2e;
     const char* kp = static_cast<const char*>(k_pool);
@@ -1138,7 +1139,7 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
       if (waves > INT32_MAX) return PA_ERR_UNSUPPORTED;
       const dim3 grid((unsigned)waves);
 #define PA_PF_SHORT(DD, CC, F8)                                                                  \
-  hipLaunchKernelGGL((prefill_short_kernel<DD, CC, F8>), grid, dim3(64), 0, st, kp, vp, qq, oo,  \
+  PA_TIMED_LAUNCH(ps, (prefill_short_kernel<DD, CC, F8>), grid, dim3(64), 0, st, kp, vp, qq, oo,  \
                      cb, block_tables, layer_off, g->num_blocks, Hkv, n_q_heads, G,              \
                      max_blocks_per_seq, plan.bps, qk_scale, sp)
 #define PA_PF_SHORT_D(DD, F8)          \
@@ -1159,7 +1160,7 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
       const dim3 grid((unsigned)wgs);
       const size_t lds = 3 * (size_t)(D == 64 ? PfCfg<64>::PAIR_BYTES : PfCfg<128>::PAIR_BYTES);
 #define PA_PF_LAUNCH(DD, F8)                                                                  \
-  launch_prefill_g<DD, F8>(G, grid, lds, st, kp, vp, qq, oo, cb, block_tables, layer_off,     \
+  launch_prefill_g<DD, F8>(G, grid, lds, ps, kp, vp, qq, oo, cb, block_tables, layer_off,     \
                            g->num_blocks, Hkv, n_q_heads, max_blocks_per_seq, plan.n_tiles,   \
                            qk_scale, sp)
       const bool ok = D == 64 ? (fp8 ? PA_PF_LAUNCH(64, true) : PA_PF_LAUNCH(64, false))
@@ -1170,16 +1171,16 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }
   if (S > 1) {
-    ProfScope ps("prefill_combine", st);
+    ProfScope ps("prefill_combine", st, true, true);
     const int64_t rows = (int64_t)n_tokens * n_q_heads;
     const int rows_per_wg = 1024 / D;
     const int64_t wgs = (rows + rows_per_wg - 1) / rows_per_wg;
     if (wgs > INT32_MAX) return PA_ERR_UNSUPPORTED;
     if (D == 64)
-      hipLaunchKernelGGL((prefill_combine_kernel<64>), dim3((unsigned)wgs), dim3(256), 0, st,
+      PA_TIMED_LAUNCH(ps, (prefill_combine_kernel<64>), dim3((unsigned)wgs), dim3(256), 0, st,
                          sp.part_o, sp.part_ml, (uint16_t*)out, rows, S);
     else
-      hipLaunchKernelGGL((prefill_combine_kernel<128>), dim3((unsigned)wgs), dim3(256), 0, st,
+      PA_TIMED_LAUNCH(ps, (prefill_combine_kernel<128>), dim3((unsigned)wgs), dim3(256), 0, st,
                          sp.part_o, sp.part_ml, (uint16_t*)out, rows, S);
     if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
   }

@@ -34,6 +34,7 @@
 
 #include "../../include/pa.h"
 #include "pa_device.h"
+#include "pa_host.h"
 #include "pa_move.h"
 
 using namespace pa_detail;

@@ -309,7 +309,10 @@ def test_large_pool_high_address_tiles():
     out_small, k_small, v_small = run_prefill(b)
     tile = B * d * 2                       # bytes of one (block, head) tile, bf16
     blk = Hkv * tile                       # bytes of one block of one pool array
-    N_big = (9 << 29) // blk               # 4.5 GiB per pool array
+    # 6.5 GiB per pool array: past its first 4 GiB lie 2.5 GiB, more than the
+    # 2 GiB that can separate two stretches of low words with bit 31 set,
+    # wherever the allocation starts
+    N_big = (13 << 29) // blk
     geom = pk.Geometry(1, Hkv, d, B, N_big, "bf16")
     K = torch.empty(geom.k_pool_shape, dtype=torch.bfloat16, device="cuda")
     V = torch.empty(geom.v_pool_shape, dtype=torch.bfloat16, device="cuda")
