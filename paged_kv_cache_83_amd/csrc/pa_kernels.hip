@@ -177,9 +177,13 @@ __device__ __forceinline__ void compute_pair(PairFrags<D>& f, const bf16x8 (&qf)
 // pool and uses it from registers (K by address, V by element) while attending.
 // RAGGED: the work items come from a list in the arguments (ragged batches:
 // only long sequences split, longest items first) instead of the uniform grid
-// of every sequence's S_max splits.
+// of every sequence's S_max splits. A ragged launch runs one wave per SIMD:
+// its items (about two per SIMD) then go out in two waves of work, and the
+// short items of the second refill the SIMDs as the long items of the first
+// finish, instead of all starting at once and leaving SIMDs idle once the
+// short ones end (chat-like batch: 77 us per launch against 81).
 template <int D, int OUT, bool NT, bool APPEND, bool RAGGED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(D >= 256 ? 1 : PA_MFMA_WPE))) void decode_mfma_bf16_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((D >= 256 || RAGGED) ? 1 : PA_MFMA_WPE))) void decode_mfma_bf16_kernel(
     uint16_t* __restrict__ kpool, uint16_t* __restrict__ vpool,
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ knew,
     const uint16_t* __restrict__ vnew, uint16_t* __restrict__ out, float* __restrict__ part_o,
@@ -596,8 +600,9 @@ struct DecodePlan {
 // sequence longer than C blocks is cut into items of C blocks, the others stay
 // whole, and items go out longest first, so the long sequences no longer set
 // the launch's end while most waves sit idle. C spreads the batch's blocks over
-// about two waves per SIMD, or covers the longest sequence when that is at most
-// three such items. Taken only when the lengths are uneven (longest above 1.5x
+// about two items per SIMD (the ragged kernel runs one wave per SIMD, so the
+// second item of a SIMD starts when its first ends), or covers the longest
+// sequence when that is at most three such items. Taken only when the lengths are uneven (longest above 1.5x
 // the mean) and the list fits the kernel arguments.
 bool plan_ragged(const int32_t* host_lens, int32_t n, int32_t max_ctx, int Hkv, int D,
                  int64_t want_bps, DecodePlan* plan) {
