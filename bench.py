@@ -243,17 +243,39 @@ def setup(args):
     return torch, pk, cfg, dev, stream, geom, gen_, k_pool, v_pool
 
 
+def fp8_tile_order(B: int, d: int, is_k: bool) -> np.ndarray:
+    """For each code byte of a one-byte tile, the (slot * d + dim) it holds: the
+    tile order include/pa.h documents (B = 16: K rows of 64 codes in slot order
+    0-3, 8-11, 4-7, 12-15, a row's 8-dim groups in the order 0, 4, 1, 5, 2, 6, 3,
+    7; V [d/32][slot/8][dim%16][(dim/16)%2][slot%8]; else the bf16 orders)."""
+    o = np.arange(B)[:, None]
+    j = np.arange(d)[None, :]
+    if is_k and B == 16 and d % 64 == 0:
+        r = (o & ~12) | ((o >> 1) & 4) | ((o << 1) & 8)
+        pos = 1024 * (j // 64) + 64 * r + 16 * ((j // 8) % 4) + 8 * ((j // 32) % 2) + j % 8
+    elif is_k:
+        W = 32 if d % 32 == 0 else d
+        pos = (j // W) * B * W + o * W + j % W
+    elif B == 16 and d % 32 == 0:
+        pos = 512 * (j // 32) + 256 * (o // 8) + 16 * (j % 16) + 8 * ((j // 16) % 2) + o % 8
+    else:
+        pos = j * B + o
+    order = np.empty(B * d, np.int64)
+    order[np.broadcast_to(pos, (B, d)).reshape(-1)] = (o * d + j).reshape(-1)
+    return order
+
+
 def fill_fp8_pools(torch, pk, geom, gen_, k_pool, v_pool, dev, chunk_blocks=8192):
     """Every slot of an FP8 pool gets seeded N(0,1) K/V rows (rounded to bf16),
     quantized with plain torch operations on the device: per (token, head) the
     power-of-two scale 2^e with e the smallest integer such that max|x| <= 448 * 2^e,
     torch's float8_e4m3fn cast of x * 2^-e, the byte e + 127, laid out in the pool's
-    documented tile format (K codes [d/W][B][W], V codes [d][B], then the B scale
-    bytes). The pools are input data: neither the library nor the oracle writes
-    them."""
+    documented tile format (the codes in the order of fp8_tile_order, then the B
+    scale bytes). The pools are input data: neither the library nor the oracle
+    writes them."""
     L, N, H, B, d = (geom.num_layers, geom.num_blocks, geom.num_kv_heads, geom.block_size,
                      geom.head_dim)
-    W = geom.k_chunk
+    order = {is_k: torch.from_numpy(fp8_tile_order(B, d, is_k)).to(dev) for is_k in (True, False)}
     for layer in range(L):
         for b0 in range(0, N, chunk_blocks):
             nb = min(chunk_blocks, N - b0)
@@ -264,12 +286,8 @@ def fill_fp8_pools(torch, pk, geom, gen_, k_pool, v_pool, dev, chunk_blocks=8192
                 e = torch.where(m <= 0.875, ex - 9, ex - 8).clamp(-127, 127)
                 e = torch.where(amax == 0, torch.zeros_like(e), e)
                 codes = (x * torch.exp2(-e.float()).unsqueeze(-1)).to(torch.float8_e4m3fn)
-                codes = codes.view(torch.uint8)
-                if is_k:
-                    tile = codes.view(nb, B, H, d // W, W).permute(0, 2, 3, 1, 4).reshape(nb, H, B * d)
-                else:
-                    tile = codes.permute(0, 2, 3, 1).reshape(nb, H, d * B)
-                pool[layer, b0:b0 + nb, :, :B * d] = tile
+                codes = codes.view(torch.uint8).permute(0, 2, 1, 3).reshape(nb, H, B * d)
+                pool[layer, b0:b0 + nb, :, :B * d] = codes.index_select(2, order[is_k])
                 pool[layer, b0:b0 + nb, :, B * d:] = (e + 127).to(torch.uint8).permute(0, 2, 1)
     if k_pool.is_cuda:
         torch.cuda.synchronize()

@@ -42,8 +42,15 @@
  * laid out [L][2][run]: that layer's K run of the block, then its V run, each
  * exactly as stored in the pool.
  * FP8 pools (PA_FP8) are bytes [L][N][H_kv][B*d + B]: each (layer, block, head)
- * tile holds the B*d element codes in the same order as above (K: [d/W][B][W],
- * V: [d][B]) followed by B scale bytes, one per slot. A slot's d values x
+ * tile holds the B*d element codes followed by B scale bytes, one per slot in
+ * slot order. Code of slot o, dimension j: K, when B = 16 and 64 divides d, at
+ * 1024*(j/64) + 64*r(o) + 16*((j/8)%4) + 8*((j/32)%2) + j%8 with r(o) = o with
+ * bits 2 and 3 swapped (rows of 64 codes, slots 0-3, 8-11, 4-7, 12-15, a row's
+ * 8-dimension groups in the order 0, 4, 1, 5, 2, 6, 3, 7), else in the bf16 order above
+ * ((j/W)*B*W + o*W + j%W); V, when B = 16 and 32 divides d, at 512*(j/32) +
+ * 256*(o/8) + 16*(j%16) + 8*((j/16)%2) + o%8, else at j*B + o. (The decode
+ * kernel's lanes then read 16 contiguous bytes each, 512 per block and
+ * instruction.) A slot's d values x
  * (one token of one head) are stored as codes c_j = E4M3(x_j * 2^-e), rounded
  * to nearest with ties to the even code, and the byte e + 127, where e is the
  * smallest integer with max_j |x_j| <= 448 * 2^e (clamped to [-127, 127]; e = 0

@@ -20,10 +20,21 @@ Passages followed:
   - elements: x * 2**-e rounded to the nearest E4M3 value, ties to the even
     code (round-to-nearest-even of OFP8); the stored value is code * 2**e.
 
-* Pool layout (a property of the library's interface, restated): every
-  (layer, block, head) tile holds the B * d element codes in the bf16 layout
-  (K: [d/W][B][W] with W = 32 when 32 divides d, else W = d; V: [d][B]) followed
-  by the B scale bytes of its slots; a pool is uint8 [L][N][H_kv][B*d + B].
+* Pool layout (a property of the library's interface, restated; the pages give
+  no byte layout for a one-byte cache): every (layer, block, head) tile holds
+  the B * d element codes followed by the B scale bytes of its slots, one per
+  slot in slot order; a pool is uint8 [L][N][H_kv][B*d + B]. Code of slot o,
+  dimension j:
+
+  - K, when B = 16 and 64 divides d: at 1024 * (j // 64) + 64 * r(o)
+    + 16 * ((j // 8) % 4) + 8 * ((j // 32) % 2) + j % 8, where r(o) swaps bits 2
+    and 3 of o: rows of 64 codes, slots in row order 0-3, 8-11, 4-7, 12-15, a
+    row holding its 64 dimensions as 8-dimension groups 0, 4, 1, 5, 2, 6, 3, 7;
+    otherwise at (j // W) * B * W + o * W + j % W with W = 32 when 32 divides d,
+    else W = d (the bf16 K layout);
+  - V, when B = 16 and 32 divides d: at 512 * (j // 32) + 256 * (o // 8)
+    + 16 * (j % 16) + 8 * ((j // 16) % 2) + o % 8; otherwise at j * B + o (the
+    bf16 V layout).
 
 Everything here is plain and slow on purpose: the code table is the spec's
 formula evaluated for all 256 codes and encoding is a nearest-value search in it.
@@ -126,12 +137,23 @@ def pool_shape(num_layers, num_blocks, num_kv_heads, block_size, head_dim):
     return (num_layers, num_blocks, num_kv_heads, tile_bytes(block_size, head_dim))
 
 
-def _k_code_index(offset, j, block_size, head_dim):
+def _swap_bits_2_3(o):
+    return (o & ~12) | ((o >> 1) & 4) | ((o << 1) & 8)
+
+
+def k_code_index(offset, j, block_size, head_dim):
+    """Byte of slot `offset`'s dimension j in a K tile (ints or integer arrays)."""
+    if block_size == 16 and head_dim % 64 == 0:
+        return (1024 * (j // 64) + 64 * _swap_bits_2_3(offset) + 16 * ((j // 8) % 4)
+                + 8 * ((j // 32) % 2) + j % 8)
     W = layout.k_chunk(head_dim)
     return (j // W) * block_size * W + offset * W + (j % W)
 
 
-def _v_code_index(offset, j, block_size):
+def v_code_index(offset, j, block_size, head_dim):
+    """Byte of slot `offset`'s dimension j in a V tile (ints or integer arrays)."""
+    if block_size == 16 and head_dim % 32 == 0:
+        return 512 * (j // 32) + 256 * (offset // 8) + 16 * (j % 16) + 8 * ((j // 16) % 2) + offset % 8
     return j * block_size + offset
 
 
@@ -142,8 +164,8 @@ def write_token(k_pool, v_pool, layer, phys, head, offset, k_vals, v_vals, block
     kt = k_pool[layer, phys, head]
     vt = v_pool[layer, phys, head]
     for j in range(head_dim):
-        kt[_k_code_index(offset, j, block_size, head_dim)] = kc[j]
-        vt[_v_code_index(offset, j, block_size)] = vc[j]
+        kt[k_code_index(offset, j, block_size, head_dim)] = kc[j]
+        vt[v_code_index(offset, j, block_size, head_dim)] = vc[j]
     kt[block_size * head_dim + offset] = ks
     vt[block_size * head_dim + offset] = vs
 
@@ -151,13 +173,13 @@ def write_token(k_pool, v_pool, layer, phys, head, offset, k_vals, v_vals, block
 def read_k(k_pool, layer, phys, head, offset, block_size, head_dim) -> np.ndarray:
     """Dequantized K (float64 [d]) of one slot."""
     kt = k_pool[layer, phys, head]
-    codes = [kt[_k_code_index(offset, j, block_size, head_dim)] for j in range(head_dim)]
+    codes = [kt[k_code_index(offset, j, block_size, head_dim)] for j in range(head_dim)]
     return dequantize_vector(codes, kt[block_size * head_dim + offset])
 
 
 def read_v(v_pool, layer, phys, head, offset, block_size, head_dim) -> np.ndarray:
     vt = v_pool[layer, phys, head]
-    codes = [vt[_v_code_index(offset, j, block_size)] for j in range(head_dim)]
+    codes = [vt[v_code_index(offset, j, block_size, head_dim)] for j in range(head_dim)]
     return dequantize_vector(codes, vt[block_size * head_dim + offset])
 
 
@@ -176,12 +198,16 @@ def append_kv(k_pool, v_pool, layer, k_new, v_new, slots, block_size, dtype="bf1
     return kp, vp
 
 
+def _tile_offsets(index, block_size, head_dim):
+    o = np.arange(block_size)[:, None]
+    j = np.arange(head_dim)[None, :]
+    return index(o, j, block_size, head_dim)                                    # [B, d]
+
+
 def read_k_tile(k_pool, layer, phys, head, block_size, head_dim) -> np.ndarray:
     """Dequantized K of all B slots of one (layer, block, head), as [B, d]."""
-    W = layout.k_chunk(head_dim)
     kt = k_pool[layer, phys, head]
-    codes = kt[:block_size * head_dim].reshape(head_dim // W, block_size, W)
-    codes = np.concatenate([codes[c] for c in range(head_dim // W)], axis=1)   # [B, d]
+    codes = kt[_tile_offsets(k_code_index, block_size, head_dim)]
     scales = kt[block_size * head_dim:].astype(np.int64) - SCALE_BIAS
     return decode(codes) * np.ldexp(1.0, scales)[:, None]
 
@@ -189,7 +215,7 @@ def read_k_tile(k_pool, layer, phys, head, block_size, head_dim) -> np.ndarray:
 def read_v_tile(v_pool, layer, phys, head, block_size, head_dim) -> np.ndarray:
     """Dequantized V of all B slots of one (layer, block, head), as [B, d]."""
     vt = v_pool[layer, phys, head]
-    codes = vt[:block_size * head_dim].reshape(head_dim, block_size).T            # [B, d]
+    codes = vt[_tile_offsets(v_code_index, block_size, head_dim)]
     scales = vt[block_size * head_dim:].astype(np.int64) - SCALE_BIAS
     return decode(codes) * np.ldexp(1.0, scales)[:, None]
 

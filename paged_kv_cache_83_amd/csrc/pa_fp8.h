@@ -4,8 +4,10 @@
 // section "From Context Tokens to KV State", Eq. (1)): OCP FP8 E4M3 codes and,
 // per (token, KV head), one power-of-two scale 2^e stored as the byte e + 127,
 // with e the smallest integer such that max|x| <= 448 * 2^e. A (layer, block,
-// head) tile is the B*d codes in the bf16 element order (K [d/W][B][W], V
-// [d][B]) followed by the B scale bytes of its slots.
+// head) tile is the B*d codes followed by the B scale bytes of its slots; with
+// B = 16 the codes are ordered so that each lane of the decode kernel reads 16
+// contiguous bytes and each load instruction 512 bytes of a block
+// (fp8_k_index, fp8_v_index; other geometries keep the bf16 element order).
 //
 // Decode keeps the bf16 matrix-core path: E4M3 converts to bf16 exactly
 // (v_cvt_scalef32_pk_bf16_fp8 with scale 1), the K scale of each key multiplies
@@ -53,6 +55,28 @@ __device__ __forceinline__ int byte_of(u32x2 w, int k) {  // k compile-time afte
   return (int)((w[k >> 2] >> (8 * (k & 3))) & 0xffu);
 }
 
+// Byte of slot o's dimension j among a tile's codes. K, B = 16 and 64 | D:
+// rows of 64 codes, one chunk of 16 rows per 64 dimensions, the slots in row
+// order 0-3, 8-11, 4-7, 12-15 (o with bits 2 and 3 swapped), so the 8 keys that
+// one score tile's lanes read from a block are 512 contiguous bytes; a row's
+// 8-dimension groups in the order 0, 4, 1, 5, 2, 6, 3, 7, so the 16 bytes of
+// lane group gq are its fragments of two consecutive 32-dimension k-steps.
+// V, B = 16 and 32 | D: per 32 dimensions 512 bytes [slot half][dim % 16]
+// [(dim / 16) % 2][slot % 8], so a lane's 8 slots of two dimension tiles are 16
+// contiguous bytes. Other geometries: the bf16 orders (K [D/W][B][W], V [D][B]).
+__device__ __forceinline__ int fp8_k_index(int o, int j, int B, int D) {
+  if (B == 16 && (D & 63) == 0)
+    return 1024 * (j >> 6) + 64 * (o ^ ((((o >> 2) ^ (o >> 3)) & 1) * 12)) + 16 * ((j >> 3) & 3) +
+           8 * ((j >> 5) & 1) + (j & 7);
+  const int W = k_chunk(D);
+  return (j / W) * B * W + o * W + j % W;
+}
+__device__ __forceinline__ int fp8_v_index(int o, int j, int B, int D) {
+  if (B == 16 && (D & 31) == 0)
+    return 512 * (j >> 5) + 256 * (o >> 3) + 16 * (j & 15) + 8 * ((j >> 4) & 1) + (o & 7);
+  return j * B + o;
+}
+
 // ---------------------------------------------------------------------------
 // Quantizing append: one wave per (token, KV head). The wave reduces max|x|
 // over the head's d values, derives e, and writes the d codes and the scale
@@ -97,7 +121,6 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ k
   const int64_t p = slot / B;
   const int o = (int)(slot % B);
   const int64_t TB = (int64_t)B * D + B;
-  const int W = k_chunk(D);
 #pragma unroll
   for (int kv = 0; kv < 2; ++kv) {
     const uint16_t* row = (kv ? vnew : knew) + (j * H + h) * D;
@@ -109,8 +132,7 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ k
     for (int d = lane; d < D; d += 64) {
       const float x = __builtin_amdgcn_ldexpf(bf16_to_f32(row[d]), -e);
       const uint8_t code = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(x, 0.0f, 0, false) & 0xff);
-      const int64_t off = kv ? (int64_t)d * B + o : (int64_t)(d / W) * B * W + (int64_t)o * W + d % W;
-      t[off] = code;
+      t[kv ? fp8_v_index(o, d, B, D) : fp8_k_index(o, d, B, D)] = code;
     }
     if (lane == 0) t[(int64_t)B * D + o] = (uint8_t)(e + kFp8ScaleBias);
   }
@@ -119,9 +141,9 @@ __global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ k
 // Bulk form for d = 128, B = 16: a work group quantizes 16 consecutive rows of
 // one head. Thread t handles piece t % 16 (8 dimensions) of row t / 16, for K
 // and for V; the row's maximum comes from its 16 lanes. K pieces leave as
-// 8-byte stores into the chunked layout. V goes through LDS: when 8 rows land
-// in 8 consecutive slots of one block starting at a multiple of 8 (a chunk of
-// a prompt), each dimension's 8 codes leave as one 8-byte store; otherwise as
+// 8-byte stores into their row. V goes through LDS: when 8 rows land in 8
+// consecutive slots of one block starting at a multiple of 8 (a chunk of a
+// prompt), each dimension's 8 codes leave as one 8-byte store; otherwise as
 // single bytes. The codes are those of the general kernel (same scale rule,
 // same conversion instruction).
 template <typename SlotSrc>
@@ -131,7 +153,7 @@ __global__ __launch_bounds__(256) void append_fp8_rows16_kernel(uint8_t* __restr
                                                                const uint16_t* __restrict__ vnew,
                                                                SlotSrc slots, int64_t n_tok, int H,
                                                                int64_t nslots, int64_t layer_off) {
-  constexpr int D = 128, B = 16, W = 32;
+  constexpr int D = 128, B = 16;
   constexpr int64_t TB = (int64_t)B * D + B;
   __shared__ uint8_t vcodes[16][D];  // [row][dimension]
   __shared__ int64_t rslot[16];
@@ -176,7 +198,7 @@ __global__ __launch_bounds__(256) void append_fp8_rows16_kernel(uint8_t* __restr
     if (kv == 0) {
       if (slot >= 0) {
         const int d0 = 8 * piece;
-        *reinterpret_cast<u32x2*>(tile + (d0 / W) * B * W + o * W + d0 % W) = u32x2{c[0], c[1]};
+        *reinterpret_cast<u32x2*>(tile + fp8_k_index(o, d0, B, D)) = u32x2{c[0], c[1]};
       }
     } else {
       *reinterpret_cast<u32x2*>(&vcodes[r][8 * piece]) = u32x2{c[0], c[1]};
@@ -198,14 +220,14 @@ __global__ __launch_bounds__(256) void append_fp8_rows16_kernel(uint8_t* __restr
       hi |= (uint32_t)vcodes[8 * hf + 4 + k][d] << (8 * k);
     }
     uint8_t* tile = vpool + layer_off + ((s0 / B) * H + h) * TB;
-    *reinterpret_cast<u32x2*>(tile + (int64_t)d * B + s0 % B) = u32x2{lo, hi};
+    *reinterpret_cast<u32x2*>(tile + fp8_v_index((int)(s0 % B), d, B, D)) = u32x2{lo, hi};
   } else {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int64_t sk = rslot[8 * hf + k];
       if (sk < 0) continue;
       uint8_t* tile = vpool + layer_off + ((sk / B) * H + h) * TB;
-      tile[(int64_t)d * B + sk % B] = vcodes[8 * hf + k][d];
+      tile[fp8_v_index((int)(sk % B), d, B, D)] = vcodes[8 * hf + k][d];
     }
   }
 }
@@ -234,29 +256,48 @@ inline bool launch_append_fp8(hipStream_t st, uint8_t* kpool, uint8_t* vpool, co
 // Decode, FP8 pool, matrix cores: B = 16, d in {64, 128}, up to 16 query heads
 // per KV head. The work decomposition, the score-row / key assignment, the
 // split-K partials and the pipelining are those of the bf16 kernel; per pair
-// of blocks a lane loads 8-byte code fragments (K: 8 dims of one key; V: 8 keys
-// of one dim) and the 8 K and 8 V scale bytes of its 8 keys.
+// of blocks a lane loads 16-byte code pieces (K: 16 dims of one key; V: 8 keys
+// of two dims, from the tile orders of fp8_k_index / fp8_v_index) and the 8 K
+// and 8 V scale bytes of its 8 keys.
 // ---------------------------------------------------------------------------
 template <int D>
 struct Fp8Frags {
-  u32x2 k[2][D / 32];
-  u32x2 v[D / 16];
+  u32x4 k[2][D / 64];  // score tile t: dims 64 j + 8 gq .. + 8, then 64 j + 32 + 8 gq .. + 8
+  u32x4 v[D / 32];     // slots 8 (gq & 1) .. + 8 of dims 16 (2 u) + c, then 16 (2 u + 1) + c
   u32x2 ks, vs;
 };
 
+// The 8 codes that form K fragment kc of score tile t: dims 32 kc + 8 gq .. + 8.
+template <int D>
+__device__ __forceinline__ u32x2 fp8_k_frag(const Fp8Frags<D>& f, int t, int kc) {
+  const u32x4 w = f.k[t][kc >> 1];
+  return (kc & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+}
+// The 8 codes of the V^T fragment of dimension tile dt.
+template <int D>
+__device__ __forceinline__ u32x2 fp8_v_frag(const Fp8Frags<D>& f, int dt) {
+  const u32x4 w = f.v[dt >> 1];
+  return (dt & 1) ? u32x2{w[2], w[3]} : u32x2{w[0], w[1]};
+}
 template <bool NT>
 __device__ __forceinline__ u32x2 kv_load8(const uint8_t* p) {
   if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
   else return *reinterpret_cast<const u32x2*>(p);
 }
+template <bool NT>
+__device__ __forceinline__ u32x4 fp8_load16(const uint8_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  else return *reinterpret_cast<const u32x4*>(p);
+}
 
+// Lane (c, gq): k_lane = 64 * (c & 7) + 16 * gq (row 8 t + (c & 7) of the key's
+// block holds its key of score tile t), v_lane = 256 * (gq & 1) + 16 * c, s_off =
+// 8 * (gq & 1).
 template <int D, bool NT>
 __device__ __forceinline__ void fp8_issue_pair(Fp8Frags<D>& f, const uint8_t* __restrict__ kl,
                                                const uint8_t* __restrict__ vl, int p0, int p1,
-                                               int Hkv, int g, int k_sel, int k_off0, int v_sel,
-                                               int v_off, int s_off, int gq) {
-  constexpr int KC = D / 32;
-  constexpr int DT = D / 16;
+                                               int Hkv, int g, int k_sel, int k_lane, int v_sel,
+                                               int v_lane, int s_off) {
   constexpr int TB = 16 * D + 16;
   const uint8_t* kt = kl + ((int64_t)(k_sel ? p1 : p0) * Hkv + g) * TB;
   const uint8_t* ks = kl + ((int64_t)(v_sel ? p1 : p0) * Hkv + g) * TB;
@@ -264,12 +305,20 @@ __device__ __forceinline__ void fp8_issue_pair(Fp8Frags<D>& f, const uint8_t* __
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-      f.k[t][kc] = kv_load8<NT>(kt + kc * 512 + (k_off0 + 4 * t) * 32 + 8 * gq);
+    for (int j = 0; j < D / 64; ++j) f.k[t][j] = fp8_load16<NT>(kt + 1024 * j + 512 * t + k_lane);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) f.v[dt] = kv_load8<NT>(vt + dt * 256 + v_off);
+  for (int u = 0; u < D / 32; ++u) f.v[u] = fp8_load16<NT>(vt + 512 * u + v_lane);
   f.ks = kv_load8<NT>(ks + 16 * D + s_off);
   f.vs = kv_load8<NT>(vt + 16 * D + s_off);
+}
+
+// Zeroes the V codes of the lane's slots whose bit is clear in keep (8 slots,
+// one byte mask each).
+template <int D>
+__device__ __forceinline__ void fp8_mask_v(Fp8Frags<D>& f, u32x2 keep) {
+  const u32x4 k4 = {keep[0], keep[1], keep[0], keep[1]};
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) f.v[u] &= k4;
 }
 
 template <int D>
@@ -284,7 +333,8 @@ __device__ __forceinline__ void fp8_compute_pair(Fp8Frags<D>& f, const bf16x8 (&
     sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
-      sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(f.k[t][kc]), qf[kc], sc[t], 0, 0, 0);
+      sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(fp8_k_frag(f, t, kc)), qf[kc],
+                                                      sc[t], 0, 0, 0);
   }
   // Lane holds the scores of pair-local keys 8*gq + 4*t + e for query c; byte
   // 4*t + e of f.ks is that key's K scale.
@@ -330,12 +380,12 @@ __device__ __forceinline__ void fp8_compute_pair(Fp8Frags<D>& f, const bf16x8 (&
 #pragma unroll
     for (int k = 0; k < 8; ++k)
       if (pos0 + k < len) keep[k >> 2] |= 0xffu << (8 * (k & 3));
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) f.v[dt] &= keep;
+    fp8_mask_v(f, keep);
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
-    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(f.v[dt]), pf, acc[dt], 0, 0, 0);
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(fp8_v_frag(f, dt)), pf, acc[dt],
+                                                      0, 0, 0);
 }
 
 template <int D, int OUT, bool NT, int NS>
@@ -401,13 +451,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   const uint8_t* kl = kpool + layer_off;
   const uint8_t* vl = vpool + layer_off;
-  // Score row c of each tile holds pair-local key 8*(c>>2) + 4*t + (c&3).
+  // Score row c of each tile holds pair-local key 8*(c>>2) + 4*t + (c&3): block
+  // c >> 3, tile row 8*t + (c&7).
   const int k_sel = c >> 3;
-  const int k_off0 = 8 * ((c >> 2) & 1) + (c & 3);
+  const int k_lane = 64 * (c & 7) + 16 * gq;
   // V^T fragment: block (gq >> 1), dims 16*dt + c, slots 8*(gq&1) .. +8; the
   // lane's 8 keys are the same slots of the same block, whose scales it reads.
   const int v_sel = gq >> 1;
-  const int v_off = 16 * c + 8 * (gq & 1);
+  const int v_lane = 256 * (gq & 1) + 16 * c;
   const int s_off = 8 * (gq & 1);
 
   const int span = b1 - b0;
@@ -416,7 +467,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
     const int off = 2 * pj;
     const int p0 = table_at(tb, off);
     const int p1 = (off + 1 < span) ? table_at(tb, off + 1) : p0;
-    fp8_issue_pair<D, NT>(fr, kl, vl, p0, p1, Hkv, g, k_sel, k_off0, v_sel, v_off, s_off, gq);
+    fp8_issue_pair<D, NT>(fr, kl, vl, p0, p1, Hkv, g, k_sel, k_lane, v_sel, v_lane, s_off);
   };
   // NS pairs in flight; steady loop issues unconditionally, the tail drains
   // (the structure of the bf16 kernel).

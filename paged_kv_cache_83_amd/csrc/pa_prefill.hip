@@ -288,9 +288,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   };
 
   // FP8 staging. Piece u of a thread is the 8 elements whose bf16 form sits at
-  // image offset 16 * (256 u + tid): in the pool, 8 code bytes at element
-  // offset el of tile tl, plus the scale bytes of their keys (K: one key, the
-  // slot of the piece's row; V: 8 consecutive slots of one dimension).
+  // image offset 16 * (256 u + tid), element el of tile tl in the bf16 order
+  // (K: slot (el / 32) % 16, dims 32 (el / 512) + el % 32 .. + 8; V: dim el / 16,
+  // slots el % 16 .. + 8): in the pool, 8 contiguous code bytes of the one-byte
+  // tile order, plus the scale bytes of their keys (K: one key; V: 8 slots).
   constexpr int KP = LOADS / 2;  // pieces from K tiles (the first half); the rest from V
   struct Raw {
     u32x2 code[LOADS];
@@ -308,7 +309,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const int el = (woff - tl * TILE) / 2 + lane * 8;  // first element of the piece
       const int p = (tl & 1) ? p1 : p0;
       const char* t = (tl < 2 ? kg : vg) + p * blk_stride;
-      r.code[u] = *reinterpret_cast<const u32x2*>(t + el);
+      const int code_off = u < KP ? fp8_k_index((el >> 5) & 15, 32 * (el >> 9) + (el & 31), 16, D)
+                                  : fp8_v_index(el & 15, el >> 4, 16, D);
+      r.code[u] = *reinterpret_cast<const u32x2*>(t + code_off);
       if (u < KP)  // K: one key, the slot of the W-chunk row
         r.ks |= (uint32_t)(uint8_t)t[16 * D + ((el >> 5) & 15)] << (8 * u);
       else         // V: slots el % 16 .. + 7 of one dimension
@@ -659,7 +662,8 @@ __global__ __launch_bounds__(256) void prefill_combine_kernel(const float* __res
 //
 // FP8 pools (E4M3 codes with a power-of-two scale per token and head): the
 // pair's codes and scale bytes come in as the FP8 decode kernel loads them
-// (8-byte fragments), the codes are converted to bf16 exactly in registers,
+// (16-byte pieces of the one-byte tile order), the codes are converted to bf16
+// exactly in registers,
 // each key's K scale multiplies its score (ldexp, exact) and its V scale is
 // folded into its probability in the PV operand, as in the FP8 decode kernel.
 template <int D, int CT, bool FP8>
@@ -748,8 +752,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((CT * D > 12
       const int p1 = (off + 1 < span) ? table_at(tb, off + 1) : p0;
       if constexpr (FP8)
         fp8_issue_pair<D, true>(fr, reinterpret_cast<const uint8_t*>(kl),
-                                reinterpret_cast<const uint8_t*>(vl), p0, p1, Hkv, g, k_sel, k_off0,
-                                v_sel, v_off, 8 * (gq & 1), gq);
+                                reinterpret_cast<const uint8_t*>(vl), p0, p1, Hkv, g, k_sel,
+                                64 * (c & 7) + 16 * gq, v_sel, 256 * (gq & 1) + 16 * c, 8 * (gq & 1));
       else
         issue_pair<D, true>(fr, reinterpret_cast<const uint16_t*>(kl),
                             reinterpret_cast<const uint16_t*>(vl), p0, p1, Hkv, g, k_sel, k_off0,
@@ -769,7 +773,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((CT * D > 12
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          if constexpr (FP8) kb[t][kc] = fp8x8_to_bf16(f.k[t][kc]);
+          if constexpr (FP8) kb[t][kc] = fp8x8_to_bf16(fp8_k_frag(f, t, kc));
           else kb[t][kc] = __builtin_bit_cast(bf16x8, f.k[t][kc]);
         }
       f32x4 sc[CT][2];
@@ -790,8 +794,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((CT * D > 12
 #pragma unroll
           for (int k = 0; k < 8; ++k)
             if (key0 + k < total) keep[k >> 2] |= 0xffu << (8 * (k & 3));
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt) f.v[dt] &= keep;
+          fp8_mask_v(f, keep);
         } else {
           u32x4 keep;
 #pragma unroll
@@ -865,7 +868,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((CT * D > 12
       bf16x8 vb[DT];  // the V^T fragments as bf16, shared by the tiles
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        if constexpr (FP8) vb[dt] = fp8x8_to_bf16(f.v[dt]);
+        if constexpr (FP8) vb[dt] = fp8x8_to_bf16(fp8_v_frag(f, dt));
         else vb[dt] = __builtin_bit_cast(bf16x8, f.v[dt]);
       }
 #pragma unroll

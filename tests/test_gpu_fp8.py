@@ -38,7 +38,6 @@ def scaled_rows(seed, n, H, d, decades=4.0):
 def place_rows(kp, vp, layer, N, H, B, d, slots, K, V):
     """Quantize rows K, V [n, H, d] (float64) with the oracle into the listed slots
     of byte pools [L, N, H, B*d + B], through the documented offsets."""
-    W = olayout.k_chunk(d)
     TB = B * d + B
     n = len(slots)
     kc, ks = fp8.quantize_rows(K.reshape(n * H, d))
@@ -48,8 +47,8 @@ def place_rows(kp, vp, layer, N, H, B, d, slots, K, V):
     h = np.tile(np.arange(H), n)
     base = ((layer * N + p) * H + h) * TB
     j = np.arange(d)
-    kidx = base[:, None] + (j // W)[None] * B * W + o[:, None] * W + (j % W)[None]
-    vidx = base[:, None] + j[None] * B + o[:, None]
+    kidx = base[:, None] + fp8.k_code_index(o[:, None], j[None], B, d)
+    vidx = base[:, None] + fp8.v_code_index(o[:, None], j[None], B, d)
     kf, vf = kp.reshape(-1), vp.reshape(-1)
     kf[kidx] = kc
     vf[vidx] = vc

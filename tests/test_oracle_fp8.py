@@ -137,6 +137,57 @@ def test_pool_layout_flat_offsets():
     assert np.array_equal(fp8.read_v(vp, layer, p, h, o, B, d), fp8.dequantize_vector(vc, vs))
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_pool_layout_flat_offsets_b16(d):
+    """B = 16 with 64 | d: K rows of 64 codes in slot order 0-3, 8-11, 4-7, 12-15
+    per 64-dimension chunk, a row's dimensions in 8-wide groups 0, 4, 1, 5, 2, 6,
+    3, 7; V as [d/32][slot half][dim % 16][(dim / 16) % 2][slot % 8]. The
+    expected tiles are built row by row from that description."""
+    L, N, H, B = 1, 3, 2, 16
+    row_slots = [0, 1, 2, 3, 8, 9, 10, 11, 4, 5, 6, 7, 12, 13, 14, 15]
+    rng = np.random.default_rng(11)
+    kp = np.zeros(fp8.pool_shape(L, N, H, B, d), np.uint8)
+    vp = np.zeros_like(kp)
+    KC = np.zeros((B, d), np.uint8)
+    VC = np.zeros((B, d), np.uint8)
+    KS = np.zeros(B, np.uint8)
+    VS = np.zeros(B, np.uint8)
+    p, h = 2, 1
+    for o in range(B):
+        kv, vv = rng.standard_normal(d) * (o + 1), rng.standard_normal(d) / (o + 1)
+        fp8.write_token(kp, vp, 0, p, h, o, kv, vv, B, d)
+        KC[o], KS[o] = fp8.quantize_vector(kv)
+        VC[o], VS[o] = fp8.quantize_vector(vv)
+    group_order = [0, 4, 1, 5, 2, 6, 3, 7]
+    k_expect = b"".join(bytes(KC[row_slots[r], 64 * c + 8 * gr:64 * c + 8 * gr + 8])
+                        for c in range(d // 64) for r in range(16) for gr in group_order)
+    v_parts = []
+    for u in range(d // 32):
+        for half in range(2):
+            for dm in range(16):
+                for hi in range(2):
+                    dim = 32 * u + 16 * hi + dm
+                    v_parts.append(bytes(VC[8 * half:8 * half + 8, dim]))
+    v_expect = b"".join(v_parts)
+    assert bytes(kp[0, p, h, :B * d]) == k_expect
+    assert bytes(vp[0, p, h, :B * d]) == v_expect
+    assert bytes(kp[0, p, h, B * d:]) == bytes(KS) and bytes(vp[0, p, h, B * d:]) == bytes(VS)
+    assert np.array_equal(fp8.read_k_tile(kp, 0, p, h, B, d),
+                          np.stack([fp8.dequantize_vector(KC[o], KS[o]) for o in range(B)]))
+    assert np.array_equal(fp8.read_v_tile(vp, 0, p, h, B, d),
+                          np.stack([fp8.dequantize_vector(VC[o], VS[o]) for o in range(B)]))
+
+
+@pytest.mark.parametrize("B,d", [(16, 128), (16, 64), (16, 96), (16, 40), (4, 64), (3, 5), (8, 128)])
+def test_pool_layout_is_a_bijection(B, d):
+    """Every (slot, dimension) has its own byte of the tile's B*d code bytes."""
+    o = np.arange(B)[:, None]
+    j = np.arange(d)[None, :]
+    for index in (fp8.k_code_index, fp8.v_code_index):
+        offs = np.broadcast_to(index(o, j, B, d), (B, d)).reshape(-1)
+        assert np.array_equal(np.sort(offs), np.arange(B * d)), (index.__name__, B, d)
+
+
 def test_decode_equals_bf16_oracle_on_representable_values():
     """Values that E4M3 x 2**e represents exactly (and bf16 too): the FP8 pool
     decodes to exactly what the bf16 oracle gives for the same values."""
