@@ -262,16 +262,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     p0 = table_at(tb, b0 - wbase);
     p1 = (b0 + 1 < nblk) ? table_at(tb, b0 + 1 - wbase) : p0;
   };
+  // Load u of a thread fills the same tile (K or V of the pair's first or
+  // second block) at the same offset on every pair: fixed per wave, so only
+  // the two block products change from pair to pair.
+  const char* ld_base[LOADS];
+  bool ld_second[LOADS];
+#pragma unroll
+  for (int u = 0; u < LOADS; ++u) {
+    const int woff = (u * 256 + wave * 64) * 16;  // the wave's first byte in the image
+    const int tl = woff / TILE;                   // tile of the whole wave
+    ld_second[u] = (tl & 1) != 0;
+    ld_base[u] = (tl < 2 ? kg : vg) + (woff - tl * TILE);
+  }
+  // (d = 128: one load instruction of the work group fills exactly one tile,
+  // load u tile u, so the choice of block and array is known at compile time)
+  constexpr bool kLoadIsTile = TILE == 16 * 64 * kPfWaves;
   auto issue = [&](int pj, int buf) {
     int p0, p1;
     pair_ids(pj, p0, p1);
+    // block ids are in [0, N) and a block's stride fits 32 bits: unsigned products
+    const uint64_t off0 = (uint64_t)(uint32_t)p0 * (uint32_t)blk_stride;
+    const uint64_t off1 = (uint64_t)(uint32_t)p1 * (uint32_t)blk_stride;
     unsigned char* img = pf_smem + buf;
 #pragma unroll
     for (int u = 0; u < LOADS; ++u) {
-      const int woff = (u * 256 + wave * 64) * 16;  // the wave's first byte in the image
-      const int tl = woff / TILE;                   // tile of the whole wave
-      const int p = (tl & 1) ? p1 : p0;
-      const char* base = (tl < 2 ? kg : vg) + p * blk_stride + (woff - tl * TILE);
+      const int woff = (u * 256 + wave * 64) * 16;
+      const char* base;
+      if constexpr (kLoadIsTile)
+        base = (u < 2 ? kg : vg) + ((u & 1) ? off1 : off0) + wave * 64 * 16;
+      else
+        base = ld_base[u] + (ld_second[u] ? off1 : off0);
       // The base is uniform; pinning it to scalar registers lets the load take
       // it as its scalar base with the lane's 16-byte offset, instead of a
       // 64-bit vector address computed per load.
@@ -1102,6 +1122,7 @@ pa_status pa_prefill(const pa_geom* g, void* k_pool, void* v_pool, int32_t layer
   hipStream_t st = (hipStream_t)stream;
   const int64_t tile_b = fp8 ? (int64_t)B * D + B : (int64_t)B * D * 2;  // bytes per pool tile
   const int64_t layer_off = (int64_t)layer * g->num_blocks * Hkv * tile_b;   // bytes
+  if (Hkv * tile_b > UINT32_MAX) return PA_ERR_UNSUPPORTED;  // a block's stride: 32-bit products
   const ChunkBatch cb{q_start, ctx_lens, n_seqs, n_tokens, max_q_len, max_context_len};
 
   if (fp8) {  // the chunks' rows are quantized into their positions (one wave per row and head)
