@@ -317,3 +317,44 @@ def test_fp8_in_kernel_merge_same_bits():
         for rep in range(2):
             got = run_decode(c, 0, bps=bps, merge=True, ws=ws)
             assert np.array_equal(got.view(np.uint8), sep.view(np.uint8)), (name, rep)
+
+
+def test_fp8_gqa70b_32k_full_size_sampled():
+    """The 70B decode batch on one-byte pools at its full per-layer size (16 x
+    32,768 tokens, a 32,768-block pool of 8 heads, head dim 128), two layers, in
+    the launch plan the benchmark times (8 splits of 256 blocks and the combine):
+    sampled (sequence, layer) outputs against the oracle. The pools hold random
+    finite E4M3 codes with scale bytes 2^-3 .. 2^3 in seeded random placement."""
+    need_gpu()
+    print_case(test="fp8_full_size")
+    L, N, H, Hq, B, d, n, S = 2, 32768, 8, 64, 16, 128, 16, 32768
+    tb = fp8.tile_bytes(B, d)
+    g = torch.Generator(device="cuda").manual_seed(8311)
+    pools = []
+    for _ in range(2):
+        t = torch.randint(0, 0x7F, (L, N, H, tb), generator=g, device="cuda", dtype=torch.int32)
+        sign = torch.randint(0, 2, (L, N, H, tb), generator=g, device="cuda", dtype=torch.int32) << 7
+        t = (t | sign).to(torch.uint8)                     # codes 0x7F / 0xFF (NaN) never occur
+        t[..., B * d:] = torch.randint(124, 131, (L, N, H, B), generator=g, device="cuda",
+                                       dtype=torch.int32).to(torch.uint8)
+        pools.append(t)
+    K, V = pools
+    order = gen.permutation(8312, N)
+    nb = S // B
+    tables = [[int(x) for x in order[i * nb:(i + 1) * nb]] for i in range(n)]
+    q = gen.normal_values(8313, (n, Hq, d), "bf16")
+    c = dict(N=N, L=L, B=B, Hq=Hq, Hkv=H, d=d, tables=tables, lengths=np.full(n, S), q=q)
+    rng = np.random.default_rng(8314)
+    samples = [(int(rng.integers(0, n)), int(rng.integers(0, L))) for _ in range(3)]
+    kh, vh = K.cpu().numpy(), V.cpu().numpy()
+    for layer in sorted({s[1] for s in samples}):
+        got = run_decode(c, layer, K=K, V=V)
+        assert np.isfinite(olayout.widen(got, "bf16")).all()
+        for (i, lyr) in samples:
+            if lyr != layer:
+                continue
+            expect = fp8.paged_decode(q, kh, vh, layer, tables, c["lengths"], B, seqs=[i])
+            err = rel_err(got[i:i + 1], expect[i:i + 1])
+            assert err <= BF16_TOL, (i, layer, err)
+    del K, V, pools
+    torch.cuda.empty_cache()
