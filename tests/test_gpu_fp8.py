@@ -68,6 +68,8 @@ APPEND_CASES = [
     # name, L, N, H, d, B, n_tokens
     ("d128_b16", 2, 40, 8, 128, 16, 70),
     ("d64_b16", 1, 33, 2, 64, 16, 200),
+    ("d96_b16", 1, 20, 2, 96, 16, 50),      # K in the bf16 order (64 does not divide 96), V reordered
+    ("d32_b16", 1, 20, 2, 32, 16, 50),      # the same with one 32-dimension V group
     ("d40_b4", 2, 20, 3, 40, 4, 50),        # W = d = 40
     ("d5_b3", 1, 17, 1, 5, 3, 40),
 ]
