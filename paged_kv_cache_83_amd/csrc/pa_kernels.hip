@@ -575,7 +575,7 @@ size_t valu_lds_bytes(const pa_geom* g, int G, int W) {
   const size_t qs = (size_t)G * D * es / 4;
   const size_t ps = (size_t)G * kpi * (es == 2 ? 1 : 2) / 2 + 4;
   const size_t mg = (size_t)G * (D + 2);
-  return 4 * (qs + (size_t)W * (ps + mg));
+  return 4 * (qs + (size_t)W * ((ps + mg + 3) / 4 * 4));
 }
 int valu_wmax(const pa_geom* g, int G) {   // ValuWg::WMAX
   return (G == 1 && g->head_dim * esize(g) == 256) ? 16 : 8;

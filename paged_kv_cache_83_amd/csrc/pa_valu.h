@@ -11,22 +11,27 @@
 // exp(m_prev - m_new) as each tile of keys arrives.
 //
 // One wave = one work item (sequence i, KV head g, split s), no barrier other
-// than the wave's own LDS ordering. Per iteration it takes KPI keys (64 / LPK
-// keys, BPI = KPI / 16 blocks; LPK lanes share a key so that each holds 128
-// bytes of its row: 8 K loads and 8 V loads per lane and iteration):
-//   scores:  lane (key k, part p) holds the key's K row dims [p*KE, (p+1)*KE)
-//            in registers (the slot's row of every 32-wide chunk, KL 16-byte
-//            loads) and dots it with the group's queries, read from LDS as
-//            broadcasts; fp32 pools use FMAs, bf16 pools v_dot2_f32_bf16
-//            (two products per instruction, fp32 accumulation). Parts of one
-//            key are summed across lanes.
+// than the wave's own LDS ordering. Per iteration it takes KPI keys (BPI = KPI
+// / 16 blocks, 8 KB of K and 8 KB of V) in 8 K and 8 V loads per lane, each
+// load instruction reading 1 KB of one tile contiguously (lane l: bytes 16 l
+// .. 16 l + 15 of that KB), so that a wave's load touches 8 cache lines and
+// not 64:
+//   scores:  a K tile is rows of (32-dim chunk, slot), 32*b bytes each, PPR
+//            16-byte pieces: lane l holds piece l % PPR of KPL keys' rows
+//            (every chunk of them) and dots it with the matching pieces of
+//            the group's queries, read from LDS; fp32 pools use FMAs, bf16
+//            pools v_dot2_f32_bf16 (two products per instruction, fp32
+//            accumulation). The PPR lanes of a row group then sum their
+//            pieces (DPP lane swaps), and each key's score is taken by one
+//            lane of the group (its owner) and its duplicates.
 //   softmax: per query head a wave maximum, exp2 of the scaled scores, a
 //            rescale of the accumulators only when the head's maximum moved.
 //            Probabilities go to LDS (fp32, or bf16 for the bf16 dot).
-//   P.V:     lane l holds dims l + 64 r (r < D/64) of every key: the V tile is
-//            dimension-major, so each dim's 16 slots of a block are 16*b
-//            contiguous bytes (4 or 2 loads); products with the probabilities
-//            read back from LDS as broadcasts.
+//   P.V:     a V tile is dimension-major, each dim's 16 slots 16*b contiguous
+//            bytes (PPD pieces): lane l holds slots of piece l % PPD of DT
+//            dims per block and accumulates their products with those slots'
+//            probabilities (LDS). After the last iteration the PPD lanes of a
+//            dim sum their accumulators and each lane keeps D/64 dims.
 // The K registers of iteration it+1 are loaded as soon as the scores of it are
 // formed and the V registers of it+1 as soon as its P.V is done, so one
 // iteration of loads is always in flight; the last iteration is peeled so the
@@ -45,18 +50,45 @@ namespace pa_detail {
 template <typename T, int D>
 struct ValuCfg {
   static constexpr int ES = (int)sizeof(T);
-  // lanes per key: each lane holds 128 bytes of its key's row (8 loads), which
-  // keeps a wave's K and V registers at 64 VGPRs whatever the element size
-  static constexpr int LPK = (D * ES <= 128) ? 1 : (D * ES) / 128;
-  static constexpr int KPI = 64 / LPK;            // keys per iteration
+  // keys per iteration: 8 KB of K rows (and of V), which keeps a wave's K and V
+  // registers at 64 VGPRs whatever the element size
+  static constexpr int KPI = 8192 / (D * ES);
   static constexpr int BPI = KPI / 16;            // blocks per iteration
-  static constexpr int KE = D / LPK;              // K elements per lane
   static constexpr int EPL = 16 / ES;             // elements per 16-byte load
-  static constexpr int KL = KE / EPL;             // K loads per lane
-  static constexpr int DPL = D / 64;              // head dims per lane in P.V
-  static constexpr int VPB = 16 / EPL;            // loads per (block, dim): 16 slots
-  static_assert(D % 64 == 0 && KE % 32 == 0 && BPI >= 1, "head dim 64 or 128");
+  static constexpr int NL = 8;                    // K (and V) loads per lane and iteration
+  static constexpr int LPT = 16 * D * ES / 1024;  // loads per (block, head) tile
+  // K tile rows (chunk of 32 dims, slot): PPR pieces of 16 bytes; RPL rows per
+  // load; SPL loads per chunk (slot ranges of RPL); KPL keys per lane
+  static constexpr int PPR = 2 * ES;
+  static constexpr int RPL = 64 / PPR;
+  static constexpr int SPL = 16 / RPL;
+  static constexpr int KPL = KPI * PPR / 64;
+  // V tile rows (dim: 16 slots): PPD pieces of EPL slots; DPW dims per load;
+  // DT dims per lane and block; DPL dims per lane in the output
+  static constexpr int PPD = ES;
+  static constexpr int DPW = 64 / PPD;
+  static constexpr int DT = LPT;
+  static constexpr int DPL = D / 64;
+  static_assert(D % 64 == 0 && BPI >= 1 && BPI * LPT == NL && KPL <= PPR && DT == DPL * PPD,
+                "head dim 64 or 128");
 };
+
+// v + the value of another lane of its group of N consecutive lanes, repeated
+// until every lane of the group holds the group's sum (N = 1, 2, 4 or 8): DPP
+// lane swaps (lane ^ 1, lane ^ 2, then the other quad of eight lanes). Each
+// lane adds the same operands, so the group's lanes hold identical bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "group of 1, 2, 4 or 8 lanes");
+  if constexpr (N >= 2) v += dpp_mov<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v += dpp_mov<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v += dpp_mov<0x141>(v);   // row_half_mirror
+  return v;
+}
 
 template <bool NT>
 __device__ __forceinline__ u32x4 ld16(const void* p) {
@@ -101,7 +133,7 @@ struct ValuLds {
   static constexpr int QS = G * D * ES / 4;
   static constexpr int PS = G * ValuCfg<T, D>::KPI * (ES == 2 ? 1 : 2) / 2 + 4;
   static constexpr int MG = G * (D + 2);
-  static constexpr int PER_WAVE = PS + MG;
+  static constexpr int PER_WAVE = (PS + MG + 3) / 4 * 4;   // 16-byte aligned regions
 };
 
 // Work item = workgroup (sequence i, KV head g, split s) of W waves: wave wv
@@ -124,8 +156,9 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
     int* __restrict__ counters) {
   using C = ValuCfg<T, D>;
   using LW = ValuLds<T, D, G>;
-  constexpr int ES = C::ES, KPI = C::KPI, BPI = C::BPI, KE = C::KE, EPL = C::EPL, KL = C::KL;
-  constexpr int DPL = C::DPL, VPB = C::VPB;
+  constexpr int ES = C::ES, KPI = C::KPI, BPI = C::BPI, EPL = C::EPL, NL = C::NL, LPT = C::LPT;
+  constexpr int PPR = C::PPR, RPL = C::RPL, SPL = C::SPL, KPL = C::KPL;
+  constexpr int PPD = C::PPD, DPW = C::DPW, DT = C::DT, DPL = C::DPL;
   constexpr int TILE = 16 * D;                       // elements of one (block, head) tile
   constexpr bool BF = sizeof(T) == 2;
   extern __shared__ __attribute__((aligned(16))) uint32_t lds_valu[];
@@ -143,8 +176,15 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
   const int si = w / Hkv;
   const int s = si % S_max;
   const int i = si / S_max;
-  const int k = lane % KPI;        // key of the lane in the score phase
-  const int part = lane / KPI;     // which KE-dim slice of it
+  // K: piece of a chunk row and row within a load; the lane's own key (slot
+  // pc % KPL of its KPL keys; the lanes with pc < KPL own distinct keys)
+  const int pc = lane % PPR, rg = lane / PPR;
+  const int q_own = pc % KPL;
+  const int k_own = 16 * (q_own / SPL) + RPL * (q_own % SPL) + rg;
+  const bool owner = pc < KPL;
+  // V: slot piece and dim within a load; the lane's output dims
+  const int sg = lane % PPD, dg = lane / PPD;
+  auto dim_of = [&](int r) { return (sg * DPL + r) * DPW + dg; };
 
   const int bps = W * bpw;         // blocks of one split (workgroup)
   const int B0 = s * bps;
@@ -207,14 +247,17 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
     }
   }
 
-  float acc[G][DPL];
+  float acc[G][DT];    // the lane's DT dims, over its slot pieces
+  float o_own[G][DPL]; // the lane's output dims, summed over the slot pieces
   float m_run[G], l_part[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
     l_part[h] = 0.f;
 #pragma unroll
-    for (int r = 0; r < DPL; ++r) acc[h][r] = 0.f;
+    for (int t = 0; t < DT; ++t) acc[h][t] = 0.f;
+#pragma unroll
+    for (int r = 0; r < DPL; ++r) o_own[h][r] = 0.f;
   }
 
   // The queries to LDS. One wave: its own writes, ordered for its reads below
@@ -251,31 +294,30 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
       return v;
     };
 
-    u32x4 kr[KL];
-    u32x4 vr[BPI][DPL][VPB];
+    // Load j of an iteration reads KB j % LPT of the tile of block j / LPT.
+    // K: it holds rows RPL*(j % LPT) .. of that tile: chunk (j % LPT) / SPL,
+    // slots RPL*((j % LPT) % SPL) + rg; the lane's key slot of it is
+    // (j / LPT)*SPL + (j % LPT) % SPL.
+    u32x4 kr[NL];
+    u32x4 vr[NL];
     auto issue_k = [&](int it) {
-      // the lane's block: entry it*BPI + k/16 of the wave's range, fetched from its lane
-      const int idv = __shfl(tb, min(it * BPI + (k >> 4), span - 1));
-      const T* base = kl + (int64_t)idv * bstride + (k & 15) * 32 + (int64_t)part * (KE / 32) * 512;
-      const bool is_new = new_pos >= 0 && (b0 + it * BPI) * 16 + k == new_pos;
-      // one load per piece from a per-lane address: the new token's lanes read the input row
-      const T* nb = knew_row + part * KE;
+      // the appended token's key within the iteration (any value if not in it)
+      const int kk = new_pos - (b0 + it * BPI) * 16;
 #pragma unroll
-      for (int j = 0; j < KL; ++j) {
-        const int e0 = j * EPL;                       // element of the lane's slice
-        const T* pa = is_new ? nb + e0 : base + (e0 >> 5) * 512 + (e0 & 31);
-        kr[j] = ld16<NT>(pa);
+      for (int j = 0; j < NL; ++j) {
+        const int jj = j % LPT;
+        const int key0 = 16 * (j / LPT) + RPL * (jj % SPL);   // key of row group 0
+        const T* pool = kl + (int64_t)blk_id(it * BPI + j / LPT) * bstride + jj * (1024 / ES) + lane * EPL;
+        // the new token's lanes read the input row (the pool's copy is being written)
+        const T* fresh = knew_row + 32 * (jj / SPL) + pc * EPL;
+        kr[j] = ld16<NT>(new_pos >= 0 && rg == kk - key0 ? fresh : pool);
       }
     };
     auto issue_v = [&](int it) {
 #pragma unroll
-      for (int b = 0; b < BPI; ++b) {
-        const T* base = vl + (int64_t)blk_id(it * BPI + b) * bstride;
-#pragma unroll
-        for (int r = 0; r < DPL; ++r)
-#pragma unroll
-          for (int u = 0; u < VPB; ++u) vr[b][r][u] = ld16<NT>(base + (lane + 64 * r) * 16 + u * EPL);
-      }
+      for (int j = 0; j < NL; ++j)
+        vr[j] = ld16<NT>(vl + (int64_t)blk_id(it * BPI + j / LPT) * bstride + (j % LPT) * (1024 / ES) +
+                         lane * EPL);
     };
 
     auto scores_softmax = [&](int it) {
@@ -283,17 +325,29 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
       float sc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        float a = 0.f;
+        float a[KPL];
 #pragma unroll
-        for (int j = 0; j < KL; ++j) {
-          const u32x4 qv = *reinterpret_cast<const u32x4*>(qs + (h * D + part * KE + j * EPL) * ES / 4);
-          a = dot16<T>(kr[j], qv, a);
+        for (int q = 0; q < KPL; ++q) a[q] = 0.f;
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          const u32x4 qv = *reinterpret_cast<const u32x4*>(qs + (h * D + 32 * c + pc * EPL) * ES / 4);
+#pragma unroll
+          for (int b = 0; b < BPI; ++b)
+#pragma unroll
+            for (int u = 0; u < SPL; ++u) {
+              const int j = b * LPT + c * SPL + u;
+              a[b * SPL + u] = dot16<T>(kr[j], qv, a[b * SPL + u]);
+            }
         }
-        if constexpr (C::LPK >= 2) a += __shfl_xor(a, KPI);
-        if constexpr (C::LPK >= 4) a += __shfl_xor(a, 2 * KPI);
-        sc[h] = (pos0 + k < lim) ? a * qk_scale : -INFINITY;
+        float own = 0.f;
+#pragma unroll
+        for (int q = 0; q < KPL; ++q) {
+          const float v = group_sum<PPR>(a[q]);
+          own = q == 0 || q_own == q ? v : own;
+        }
+        sc[h] = (pos0 + k_own < lim) ? own * qk_scale : -INFINITY;
         // with 8 heads the scheduler would otherwise read every head's queries
-        // ahead (64 fragments, more registers than a wave has)
+        // ahead (more registers than a wave has)
         if constexpr (G >= 8) __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -304,13 +358,13 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
           const float alpha = __builtin_amdgcn_exp2f(m_run[h] - m_new);
           l_part[h] *= alpha;
 #pragma unroll
-          for (int r = 0; r < DPL; ++r) acc[h][r] *= alpha;
+          for (int t = 0; t < DT; ++t) acc[h][t] *= alpha;
         }
         m_run[h] = m_new;
-        if (part == 0) {
+        if (owner) {
           l_part[h] += p;
-          if constexpr (BF) reinterpret_cast<uint16_t*>(ps)[h * KPI + k] = f32_to_bf16(p);
-          else reinterpret_cast<float*>(ps)[h * KPI + k] = p;
+          if constexpr (BF) reinterpret_cast<uint16_t*>(ps)[h * KPI + k_own] = f32_to_bf16(p);
+          else reinterpret_cast<float*>(ps)[h * KPI + k_own] = p;
         }
       }
     };
@@ -321,46 +375,41 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
     // registers are fixed up here, outside the steady loop, so the loop's V
     // registers carry no conditional updates (which would make the compiler
     // copy them, and wait for every load in flight to do so).
+    // V load j: dim (j % LPT)*DPW + dg of block j / LPT, its slots sg*EPL ..
+    // sg*EPL + EPL-1; word c holds slots from sg*EPL + c*EPL/4.
     auto fix_last_v = [&](int it) {
       const int pos0 = (b0 + it * BPI) * 16;
       if (new_pos >= pos0 && new_pos < pos0 + KPI) {   // wave-uniform: the appended token's V
         const int kk = in_vgpr(new_pos - pos0);
+        const uint32_t keep = BF ? ((kk & 1) ? 0x0000ffffu : 0xffff0000u) : 0u;
 #pragma unroll
-        for (int r = 0; r < DPL; ++r) {
-          const uint32_t nv = BF ? (uint32_t)reinterpret_cast<const uint16_t*>(vnew_row)[lane + 64 * r]
-                                 : reinterpret_cast<const uint32_t*>(vnew_row)[lane + 64 * r];
+        for (int j = 0; j < NL; ++j) {
+          const int e = (j % LPT) * DPW + dg;
+          const uint32_t nv = BF ? (uint32_t)reinterpret_cast<const uint16_t*>(vnew_row)[e]
+                                 : reinterpret_cast<const uint32_t*>(vnew_row)[e];
           const uint32_t nw = BF ? ((kk & 1) ? (nv << 16) : nv) : nv;
-          const uint32_t keep = BF ? ((kk & 1) ? 0x0000ffffu : 0xffff0000u) : 0u;
 #pragma unroll
-          for (int b = 0; b < BPI; ++b)
-#pragma unroll
-            for (int u = 0; u < VPB; ++u)
-#pragma unroll
-              for (int c = 0; c < 4; ++c) {   // word c holds slots (u*EPL + c*EPL/4 ..)
-                const int key0 = b * 16 + u * EPL + c * (EPL / 4);
-                const uint32_t wd = vr[b][r][u][c];
-                const bool hit = BF ? ((kk >> 1) == (key0 >> 1)) : (kk == key0);
-                vr[b][r][u][c] = hit ? ((wd & keep) | nw) : wd;
-              }
+          for (int c = 0; c < 4; ++c) {
+            const int key0 = 16 * (j / LPT) + sg * EPL + c * (EPL / 4);
+            const uint32_t wd = vr[j][c];
+            const bool hit = BF ? ((kk >> 1) == (key0 >> 1)) : (kk == key0);
+            vr[j][c] = hit ? ((wd & keep) | nw) : wd;
+          }
         }
       }
       if (pos0 + KPI > lim) {   // wave-uniform: zero the V of masked keys (their data may be NaN)
         const int nval = in_vgpr(lim - pos0);   // keys 0 .. nval-1 of the iteration are attended
 #pragma unroll
-        for (int b = 0; b < BPI; ++b)
+        for (int j = 0; j < NL; ++j)
 #pragma unroll
-          for (int r = 0; r < DPL; ++r)
-#pragma unroll
-            for (int u = 0; u < VPB; ++u)
-#pragma unroll
-              for (int c = 0; c < 4; ++c) {
-                const int key0 = b * 16 + u * EPL + c * (EPL / 4);
-                const uint32_t wd = vr[b][r][u][c];
-                if constexpr (BF)
-                  vr[b][r][u][c] = key0 + 1 < nval ? wd : (key0 < nval ? (wd & 0x0000ffffu) : 0u);
-                else
-                  vr[b][r][u][c] = key0 < nval ? wd : 0u;
-              }
+          for (int c = 0; c < 4; ++c) {
+            const int key0 = 16 * (j / LPT) + sg * EPL + c * (EPL / 4);
+            const uint32_t wd = vr[j][c];
+            if constexpr (BF)
+              vr[j][c] = key0 + 1 < nval ? wd : (key0 < nval ? (wd & 0x0000ffffu) : 0u);
+            else
+              vr[j][c] = key0 < nval ? wd : 0u;
+          }
       }
     };
 
@@ -375,14 +424,11 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
 #pragma unroll
       for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int b = 0; b < BPI; ++b)
+        for (int b = 0; b < BPI; ++b) {
+          const u32x4 pv4 = *reinterpret_cast<const u32x4*>(ps + (h * KPI + b * 16 + sg * EPL) * ES / 4);
 #pragma unroll
-          for (int u = 0; u < VPB; ++u) {
-            const u32x4 pv4 = *reinterpret_cast<const u32x4*>(
-                ps + (h * KPI + b * 16 + u * EPL) * ES / 4);
-#pragma unroll
-            for (int r = 0; r < DPL; ++r) acc[h][r] = dot16<T>(vr[b][r][u], pv4, acc[h][r]);
-          }
+          for (int t = 0; t < DT; ++t) acc[h][t] = dot16<T>(vr[b * LPT + t], pv4, acc[h][t]);
+        }
         if constexpr (G >= 8) __builtin_amdgcn_sched_barrier(0);   // as in the score phase
       }
     };
@@ -403,9 +449,19 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
     fix_last_v(n_it - 1);
     pv();
 
-    // l: the sum over the wave of each lane's own keys
+    // l: the sum over the wave of each lane's own keys; o: each dim summed over
+    // its PPD slot pieces, the lane keeping dims dim_of(r)
 #pragma unroll
-    for (int h = 0; h < G; ++h) l_part[h] = wave_sum(l_part[h]);
+    for (int h = 0; h < G; ++h) {
+      l_part[h] = wave_sum(l_part[h]);
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const float v = group_sum<PPD>(acc[h][t]);
+#pragma unroll
+        for (int r = 0; r < DPL; ++r)
+          if (t % DPL == r) o_own[h][r] = t / DPL == 0 || sg == t / DPL ? v : o_own[h][r];
+      }
+    }
   }
 
   const int ns = (nblk + bps - 1) / bps;   // splits (workgroups) of this sequence
@@ -418,19 +474,19 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
       const float inv = 1.f / L;
       T* op = out + ((int64_t)i * Hq + (int64_t)g * G + h) * D;
 #pragma unroll
-      for (int r = 0; r < DPL; ++r) op[lane + 64 * r] = from_f32<T>(o[r] * inv);
+      for (int r = 0; r < DPL; ++r) op[dim_of(r)] = from_f32<T>(o[r] * inv);
     } else {   // the split's partial
       const int64_t row = ((int64_t)i * Hq + (int64_t)g * G + h) * S_max + s;
       if (coherent) {
 #pragma unroll
-        for (int r = 0; r < DPL; ++r) part_st_coherent(part_o + row * D + lane + 64 * r, o[r]);
+        for (int r = 0; r < DPL; ++r) part_st_coherent(part_o + row * D + dim_of(r), o[r]);
         if (lane == 0) {
           part_st_coherent(part_ml + row * 2 + 0, M);
           part_st_coherent(part_ml + row * 2 + 1, L);
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < DPL; ++r) part_o[row * D + lane + 64 * r] = o[r];
+        for (int r = 0; r < DPL; ++r) part_o[row * D + dim_of(r)] = o[r];
         if (lane == 0) {
           part_ml[row * 2 + 0] = M;
           part_ml[row * 2 + 1] = L;
@@ -441,14 +497,14 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
 
   if (W == 1) {   // one wave: its registers are the workgroup's result
 #pragma unroll
-    for (int h = 0; h < G; ++h) finish(h, m_run[h], l_part[h], acc[h]);
+    for (int h = 0; h < G; ++h) finish(h, m_run[h], l_part[h], o_own[h]);
   } else {
     if (active) {   // the wave's (o, m, l) to LDS
       float* mg = mg_base + (int64_t)wv * LW::PER_WAVE;
 #pragma unroll
       for (int h = 0; h < G; ++h) {
 #pragma unroll
-        for (int r = 0; r < DPL; ++r) mg[h * (D + 2) + lane + 64 * r] = acc[h][r];
+        for (int r = 0; r < DPL; ++r) mg[h * (D + 2) + dim_of(r)] = o_own[h][r];
         if (lane == 0) {
           mg[h * (D + 2) + D] = m_run[h];
           mg[h * (D + 2) + D + 1] = l_part[h];
@@ -471,7 +527,7 @@ __global__ __launch_bounds__((64 * ValuWg<T, D, G>::WMAX)) void decode_valu_kern
         const float wt = exp2f(mgx[D] - M);
         L = fmaf(wt, mgx[D + 1], L);
 #pragma unroll
-        for (int r = 0; r < DPL; ++r) o[r] = fmaf(wt, mgx[lane + 64 * r], o[r]);
+        for (int r = 0; r < DPL; ++r) o[r] = fmaf(wt, mgx[dim_of(r)], o[r]);
       }
       finish(h, M, L, o);
     }
