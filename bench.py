@@ -64,6 +64,9 @@ def parse():
                     help="prefill key splits (0 = library's choice, 1 = none)")
     ap.add_argument("--no-baseline-leg", action="store_true",
                     help="prefix_reuse: skip the no-reuse comparison leg")
+    ap.add_argument("--checked-calls", action="store_true",
+                    help="decode: check and marshal every layer's call (decode_step) instead of "
+                         "preparing each layer's call once (prepare_decode_step)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step in a HIP graph and time its replays")
     ap.add_argument("--unfused", action="store_true",
@@ -365,6 +368,14 @@ def run_decode(args):
                           waves_per_group=args.wg_waves, host_lens=host_lens,
                           kv_reuse=args.kv_reuse)
 
+    if not args.unfused and not args.checked_calls:
+        # the same fused step with each layer's call checked and marshalled once
+        step = steps.prepare_decode_step(geom, k_pool, v_pool, q_all, k_new, v_new, tables, lens,
+                                         max_ctx, out, ws, blocks_per_split=args.bps,
+                                         kernel=args.kernel, stream=stream, around_decode=around,
+                                         kv_reuse=args.kv_reuse, merge=merge,
+                                         waves_per_group=args.wg_waves, host_lens=host_lens)
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -521,7 +532,9 @@ def run_decode(args):
                    "split_merge": ("none (every sequence in one split)" if ws_bytes == 0
                                    else "inside the decode launch (where splits exist)" if merge
                                    else "separate launch"),
-                   "launch": "hip graph replay" if args.graph else "eager"},
+                   "launch": ("hip graph replay" if args.graph
+                              else "eager, calls checked per call" if args.unfused or args.checked_calls
+                              else "eager, calls prepared once")},
         "step_ms": step_ms,
         "tokens_per_s": round(n / (ms_per_step * 1e-3), 2),
         "pct_hbm_peak": round(100 * value / PEAK_GBS, 2),

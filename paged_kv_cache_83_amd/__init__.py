@@ -12,6 +12,7 @@ from ._lib import (DoubleFreeError, OutOfBlocksError, OutOfFramesError, PagedKVE
 from .api import (BlockManager, Geometry, Profiler, RadixCache, Swapper, alloc_pools, append_kv,  # noqa: F401
                   blocks_for_tokens, bytes_per_block, bytes_per_token, copy_blocks,
                   copy_to_device, copy_to_host, decode, decode_append, decode_append_noalloc,
+                  DecodeAppendCall,
                   decode_workspace_bytes, NOALLOC_SCRATCH_BYTES,
                   gather_blocks, pool_bytes, prefill, prefill_workspace_bytes, scatter_blocks)
 

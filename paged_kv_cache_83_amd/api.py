@@ -253,6 +253,48 @@ def decode_append(geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, o
           "pa_decode_append")
 
 
+class DecodeAppendCall:
+    """decode_append with its arguments checked and marshalled once: each call
+    is then one C call with the stored arguments. For a decode loop that reuses
+    the same buffers (static q / k_new / v_new / out / table / length tensors
+    whose contents change between calls), where the per-call checks would cost
+    more host time than a short launch runs. The tensors (and host_lens, which
+    may be updated in place) must stay alive and in place; max_context_len may
+    change per call."""
+
+    def __init__(self, geom: Geometry, k_pool, v_pool, layer: int, q, k_new, v_new, out,
+                 block_tables, context_lens, max_context_len: int, scale: float = 0.0,
+                 workspace=None, blocks_per_split: int = 0, kernel: str = "auto", stream=None,
+                 kv_reuse: bool = False, merge: bool = False, waves_per_group: int = 0,
+                 host_lens=None):
+        hl = _host_lens(host_lens, q.shape[0])
+        o = _opts(blocks_per_split, KERNELS[kernel], kv_reuse, merge, waves_per_group, hl)
+        g, n, hq, ws_ptr, ws_bytes = _decode_args(geom, k_pool, v_pool, q, out, block_tables,
+                                                  context_lens, max_context_len, workspace, o)
+        per = geom.num_kv_heads * geom.head_dim
+        _dev(k_new, "k_new", geom.io_dtype, n * per)
+        _dev(v_new, "v_new", geom.io_dtype, n * per)
+        self._keep = (hl, o, g, k_pool, v_pool, q, k_new, v_new, out, block_tables, context_lens,
+                      workspace)
+        self._fn = _L().pa_decode_append
+        self._n, self._hq, self._g, self._o, self._ws_bytes = n, hq, g, o, ws_bytes
+        self._head = (C.byref(g), _ptr(k_pool), _ptr(v_pool), int(layer), _ptr(q), _ptr(k_new),
+                      _ptr(v_new), _ptr(out), n, hq, _ptr(block_tables), int(block_tables.shape[1]),
+                      _ptr(context_lens))
+        self._tail = (float(scale), C.byref(o), ws_ptr, ws_bytes, _stream(stream, q.device))
+        self._max_ctx = int(max_context_len)
+
+    def __call__(self, max_context_len: Optional[int] = None) -> None:
+        if max_context_len is not None and int(max_context_len) != self._max_ctx:
+            m = int(max_context_len)
+            need = int(_L().pa_decode_workspace_bytes(C.byref(self._g), self._n, self._hq, m,
+                                                       C.byref(self._o)))
+            if need > self._ws_bytes:
+                raise ValueError(f"decode needs a workspace of {need} bytes")
+            self._max_ctx = m
+        check(self._fn(*self._head, self._max_ctx, *self._tail), "pa_decode_append")
+
+
 # Bytes of the library's own partials array behind decode_append_noalloc.
 NOALLOC_SCRATCH_BYTES = 16 << 20
 

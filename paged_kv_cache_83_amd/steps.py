@@ -68,6 +68,34 @@ def decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, slo
             around_decode(layer, False)
 
 
+def prepare_decode_step(geom: Geometry, k_pool, v_pool, q_all, k_new_all, v_new_all, tables, lens,
+                        max_context_len: int, out_all, workspace,
+                        layers: Optional[Sequence[int]] = None, blocks_per_split: int = 0,
+                        kernel: str = "auto", stream=None,
+                        around_decode: Optional[Callable[[int, bool], None]] = None,
+                        kv_reuse: bool = False, merge: bool = False, waves_per_group: int = 0,
+                        host_lens=None) -> Callable[[], None]:
+    """The fused decode step of decode_step (one new token per sequence, at
+    position lens[i] - 1) with each layer's call checked and marshalled once:
+    returns step(), which runs every layer's decode_append on the same buffers."""
+    calls = [(layer, api.DecodeAppendCall(geom, k_pool, v_pool, layer, q_all[layer],
+                                          k_new_all[layer], v_new_all[layer], out_all[layer],
+                                          tables, lens, max_context_len, workspace=workspace,
+                                          blocks_per_split=blocks_per_split, kernel=kernel,
+                                          stream=stream, kv_reuse=kv_reuse, merge=merge,
+                                          waves_per_group=waves_per_group, host_lens=host_lens))
+             for layer in (range(geom.num_layers) if layers is None else layers)]
+
+    def step():
+        for layer, call in calls:
+            if around_decode is not None:
+                around_decode(layer, True)
+            call()
+            if around_decode is not None:
+                around_decode(layer, False)
+    return step
+
+
 def cow_copy(geom: Geometry, k_pool, v_pool, pairs, device, stream=None):
     """Run the (src, dst) block copies a copy-on-write reservation returned."""
     if not pairs:

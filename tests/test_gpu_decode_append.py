@@ -122,3 +122,53 @@ def test_fused_missing_new_token_arrays():
                                       None, kn.data_ptr(), out.data_ptr(), 1, 4, tabs.data_ptr(),
                                       1, lens.data_ptr(), 16, 0.0, None, None, 0, None)
     assert st == -1  # PA_ERR_INVALID_ARG
+
+
+PREPARED_CASES = [
+    # name, dtype, Hq, Hkv, d, kernel, bps, merge
+    ("valu_f32_merge", "f32", 12, 12, 64, "valu", 0, True),
+    ("mfma_bf16_split", "bf16", 32, 8, 128, "mfma", 2, False),
+]
+
+
+@pytest.mark.parametrize("case", PREPARED_CASES, ids=[c[0] for c in PREPARED_CASES])
+def test_prepared_call_equals_checked_call(case):
+    """DecodeAppendCall (arguments checked and marshalled once) gives the same
+    bits as decode_append on the same inputs, on repeated calls (the pool state
+    and the merge counters carried from one call to the next), and accepts a
+    changed max_context_len."""
+    need_gpu()
+    name, dtype, Hq, Hkv, d, kernel, bps, merge = case
+    print_case(test="prepared_call", case=name)
+    batch = make_batch(dtype, 1, 400, Hq, Hkv, d, 16, RAGGED, seed=zlib.crc32(name.encode()) % 10000)
+    geom = pk.Geometry(batch.L, batch.Hkv, batch.d, batch.B, batch.N, batch.dtype)
+    # two spare table columns, so that a larger max_context_len is still valid
+    tabs = torch.from_numpy(padded_tables(batch.tables, batch.max_blocks + 2)).cuda()
+    lens = torch.from_numpy(np.asarray(batch.lengths, np.int32)).cuda()
+    max_ctx = int(max(batch.lengths))
+    q = to_dev(batch.q, batch.dtype)
+    kn, vn = to_dev(batch.k_new, batch.dtype), to_dev(batch.v_new, batch.dtype)
+    ws_bytes = pk.decode_workspace_bytes(geom, q.shape[0], q.shape[1], max_ctx + 16, bps, kernel, merge)
+    results = []
+    for prepared in (False, True):
+        K, V = to_dev(batch.k_pool, batch.dtype), to_dev(batch.v_pool, batch.dtype)
+        ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device="cuda")
+        outs = [torch.empty_like(q) for _ in range(3)]
+        if prepared:
+            calls = [pk.DecodeAppendCall(geom, K, V, 0, q, kn, vn, o, tabs, lens, max_ctx, workspace=ws,
+                                         blocks_per_split=bps, kernel=kernel, merge=merge)
+                     for o in outs]
+            calls[0]()
+            calls[1]()
+            calls[2](max_context_len=max_ctx + 16)
+        else:
+            for j, o in enumerate(outs):
+                pk.decode_append(geom, K, V, 0, q, kn, vn, o, tabs, lens, max_ctx + (16 if j == 2 else 0),
+                                 workspace=ws, blocks_per_split=bps, kernel=kernel, merge=merge)
+        torch.cuda.synchronize()
+        results.append([to_host(o, batch.dtype) for o in outs] + [to_host(K, batch.dtype), to_host(V, batch.dtype)])
+    for a, b in zip(*results):
+        assert _same_bits(a, b), name
+    tol = BF16_TOL if dtype == "bf16" else F32_TOL
+    _, _, expect = oracle_step(batch, 0)
+    assert max_abs_err(results[1][0], expect, dtype) <= tol
