@@ -171,8 +171,8 @@ typedef struct {
                                blocks_per_split > 0, that item size and the list always). A host
                                copy shorter than the device lengths leaves outputs incomplete. */
   int32_t waves_per_group;  /* streaming VALU kernel: waves per workgroup, which split the
-                               workgroup's blocks and merge in LDS (0 = choose; capped at 16 for
-                               one query head per KV head with 256-byte rows, else 8) */
+                               workgroup's blocks and merge in LDS (0 = choose: 2; capped at 16
+                               for one query head per KV head with 256-byte rows, else 8) */
 } pa_decode_opts;
 
 /* Workspace bytes pa_decode needs for these sizes and options (0 when the
