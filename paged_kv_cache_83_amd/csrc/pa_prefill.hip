@@ -15,8 +15,9 @@
 // keys in pairs of blocks (32 keys). Each pair's K and V tiles (4 per pair) are
 // loaded once for the 128 rows straight from global memory into LDS (16 bytes
 // per lane), two pairs ahead of use in three rotating images, then read as MFMA
-// operand fragments at the same offsets the decode kernel uses on the pool (the
-// LDS image has the pool's tile layout):
+// operand fragments at the offsets the decode kernel uses on the pool (the LDS
+// image has the pool's tile layout, but for a swap of 16-byte columns in the
+// K rows of slots 8-15 that keeps the fragment reads free of bank conflicts):
 //   S^T[32 keys][16 rows] = K[keys][d] . Q^T[d][rows]     (two tiles of rows)
 //   O^T[d][16 rows]      += V^T[d][keys] . P^T[keys][rows]
 // with the online-softmax update of the same section between them. The QK^T
@@ -229,7 +230,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   const char* kl = kpool + layer_off;  // layer_off in bytes
   const char* vl = vpool + layer_off;
 
-  // Pair image in LDS: [K blk0][K blk1][V blk0][V blk1], each tile as in the pool.
+  // Pair image in LDS: [K blk0][K blk1][V blk0][V blk1], each tile as in the
+  // pool except that in the K tiles' rows of slots 8-15 the 16-byte columns
+  // trade places in pairs (column j at j ^ 2): a K fragment read takes slots s
+  // and s + 8 of a chunk in one instruction, 512 bytes apart, which would
+  // otherwise fall in the same LDS banks (measured: 4 conflict cycles per read,
+  // none with the swap). The unit at 16-byte index x of a K chunk holds the
+  // pool's unit x ^ ((x >> 4) & 2).
   // Three images rotate: the pair whose softmax and PV are being done, the next
   // pair (its keys are read for QK^T one step early) and the pair after that
   // (its loads in flight). Loads go from global memory straight into LDS: lane
@@ -277,6 +284,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // (d = 128: one load instruction of the work group fills exactly one tile,
   // load u tile u, so the choice of block and array is known at compile time)
   constexpr bool kLoadIsTile = TILE == 16 * 64 * kPfWaves;
+  constexpr int KP = LOADS / 2;  // loads (pieces) of K tiles: the first half; the rest V
+  const int k_src = (lane ^ ((lane >> 4) & 2)) * 16;   // K: the pool unit of the lane's LDS unit
   auto issue = [&](int pj, int buf) {
     int p0, p1;
     pair_ids(pj, p0, p1);
@@ -301,7 +310,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
       const uint32_t bhi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bu >> 32));
       const uint32_t blo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bu);
       const uint64_t bs = join_address_words(bhi, blo);
-      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(bs) + lane * 16,
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const char*>(bs) + (u < KP ? k_src : lane * 16),
                                        (__attribute__((address_space(3))) void*)(img + woff), 16,
                                        0, 0);
     }
@@ -312,7 +321,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // (K: slot (el / 32) % 16, dims 32 (el / 512) + el % 32 .. + 8; V: dim el / 16,
   // slots el % 16 .. + 8): in the pool, 8 contiguous code bytes of the one-byte
   // tile order, plus the scale bytes of their keys (K: one key; V: 8 slots).
-  constexpr int KP = LOADS / 2;  // pieces from K tiles (the first half); the rest from V
   struct Raw {
     u32x2 code[LOADS];
     uint32_t ks;       // K: the scale byte of piece u in byte u
@@ -369,7 +377,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                   (cvt2(r.code[u][1], sv[4], lo_t{}) & m) | (cvt2(r.code[u][1], sv[5], lo_t{}) & ~m),
                   (cvt2(r.code[u][1], sv[6], hi_t{}) & m) | (cvt2(r.code[u][1], sv[7], hi_t{}) & ~m)};
       }
-      *reinterpret_cast<u32x4*>(pf_smem + buf + woff + lane * 16) = w;
+      // K pieces go to their swapped column (the LDS unit that holds this pool unit)
+      *reinterpret_cast<u32x4*>(pf_smem + buf + woff + (u < KP ? k_src : lane * 16)) = w;
     }
   };
 
@@ -378,6 +387,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
   // lane: block (gq >> 1), dims 16*dt + c, slots 8*(gq&1) .. +8.
   const int k_sel = c >> 3;
   const int k_off0 = 8 * ((c >> 2) & 1) + (c & 3);
+  const int k_col = 16 * (gq ^ (2 * ((c >> 2) & 1)));   // slot k_off0 + 4t >= 8 iff (c >> 2) & 1
   const int v_sel = gq >> 1;
   const int v_off = 32 * c + 16 * (gq & 1);  // bytes
 
@@ -391,7 +401,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
         kf[t][kc] = *reinterpret_cast<const u32x4*>(img + k_sel * TILE + kc * 1024 +
-                                                    (k_off0 + 4 * t) * 64 + 16 * gq);
+                                                    (k_off0 + 4 * t) * 64 + k_col);
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
