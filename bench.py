@@ -96,10 +96,11 @@ def log(msg):
 
 
 def kernel_source_sha(kernel: str) -> str:
-    """sha256 prefix of a decode kernel's source: for the bf16 matrix-core kernel
+    """sha256 prefix of a kernel's source: for the bf16 matrix-core decode kernel
     its section of pa_kernels.hip (from its banner to the generic kernel's), for
-    the streaming VALU and FP8 kernels their headers, each with the device and
-    pair-load helpers. Edits elsewhere leave it unchanged."""
+    the streaming VALU and FP8 decode kernels their headers, for the prefill tile
+    kernel pa_prefill.hip, each with the device and pair-load helpers. Edits
+    elsewhere leave it unchanged."""
     here = os.path.dirname(os.path.abspath(__file__))
     csrc = os.path.join(here, "paged_kv_cache_83_amd", "csrc")
     h = hashlib.sha256()
@@ -110,6 +111,8 @@ def kernel_source_sha(kernel: str) -> str:
         h.update(open(os.path.join(csrc, "pa_valu.h"), "rb").read())
     elif kernel == "decode_mfma_fp8_kernel":
         h.update(open(os.path.join(csrc, "pa_fp8.h"), "rb").read())
+    elif kernel == "prefill_mfma_kernel":
+        h.update(open(os.path.join(csrc, "pa_prefill.hip"), "rb").read())
     else:
         raise ValueError(kernel)
     h.update(open(os.path.join(csrc, "pa_device.h"), "rb").read())
@@ -118,13 +121,14 @@ def kernel_source_sha(kernel: str) -> str:
 
 
 def profiled_traffic(kernel: str, workload: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary
-    of this kernel on this workload (FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB
-    copy), or None when there is none or the kernel source has changed since."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary of this
+    kernel on this workload (FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy),
+    or None when there is none or the kernel source has changed since."""
     here = os.path.dirname(os.path.abspath(__file__))
     stem = kernel[:-len("_kernel")]
-    path = os.path.join(here, "profiles", f"{stem}_{workload}_hbm_counters.md")
-    if not os.path.exists(path):
+    path = next((p for p in (os.path.join(here, "profiles", f"{stem}_{workload}_{kind}.md")
+                             for kind in ("hbm_counters", "counters")) if os.path.exists(p)), None)
+    if path is None:
         return None
     fields = {}
     for line in open(path):
@@ -745,7 +749,8 @@ def run_prefill(args):
                 ach = flops_layer / avg_s / 1e12
                 roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                            "traffic": None, "kernel": kname,
+                            "traffic": profiled_traffic(kname, cfg.name) if args.pf_splits == 0
+                            else None, "kernel": kname,
                             "flops_per_launch": flops_layer, "avg_launch_us": round(avg_s * 1e6, 2)}
             else:
                 ach = bytes_layer / avg_s / 1e9
