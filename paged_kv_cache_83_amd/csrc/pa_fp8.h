@@ -83,27 +83,6 @@ __device__ __forceinline__ int fp8_v_index(int o, int j, int B, int D) {
 // byte of K and of V into the token's slot. k_new / v_new: bf16 [n][H][d].
 // ---------------------------------------------------------------------------
 
-// Slot of the token appended for sequence j of a decode step: position
-// lens[j] - 1 through row j of the block tables (-1 when there is none).
-struct SlotsFromLens {
-  const int32_t* tables;
-  const int32_t* lens;
-  int max_blocks;
-  int max_ctx;
-  int B;
-  int N;
-  __device__ int64_t operator()(int64_t j) const {
-    const int len = clamp_len(lens, (int)j, max_ctx);
-    if (len == 0) return -1;
-    const int pos = len - 1;
-    const int lb = pos / B;
-    if (lb >= max_blocks) return -1;
-    const int p = tables[j * max_blocks + lb];
-    if (p < 0 || p >= N) return -1;
-    return (int64_t)p * B + pos % B;
-  }
-};
-
 template <typename SlotSrc>
 __global__ __launch_bounds__(256) void append_fp8_kernel(uint8_t* __restrict__ kpool,
                                                         uint8_t* __restrict__ vpool,
@@ -388,10 +367,61 @@ __device__ __forceinline__ void fp8_compute_pair(Fp8Frags<D>& f, const bf16x8 (&
                                                       0, 0, 0);
 }
 
-template <int D, int OUT, bool NT, int NS>
+// One token's K and V rows (bf16, d values each) quantized into slot o of
+// their block's tiles by one wave, with the append kernels' rule and
+// instructions (one power-of-two scale per row from its largest magnitude,
+// E4M3 codes by the same pair conversion), so the pool bytes are theirs: lane
+// l < D/8 takes K dims 8 l .. + 7, lane D/8 + l the same V dims.
+template <int D>
+__device__ __forceinline__ void fp8_put_token(uint8_t* __restrict__ kt, uint8_t* __restrict__ vt,
+                                              const uint16_t* __restrict__ krow,
+                                              const uint16_t* __restrict__ vrow, int o, int lane) {
+  constexpr int P = D / 8;  // pieces of a row
+  const bool is_v = lane >= P;
+  const int piece = lane & (P - 1);
+  u32x4 raw = {0u, 0u, 0u, 0u};
+  if (lane < 2 * P) raw = *reinterpret_cast<const u32x4*>((is_v ? vrow : krow) + 8 * piece);
+  float x[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    x[2 * k] = __uint_as_float(raw[k] << 16);
+    x[2 * k + 1] = __uint_as_float(raw[k] & 0xffff0000u);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+  for (int m = P / 2; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, P));
+  const int e = fp8_scale_exp(amax);
+  uint32_t c[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x[4 * k], -e),
+                                            __builtin_amdgcn_ldexpf(x[4 * k + 1], -e), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_ldexpf(x[4 * k + 2], -e),
+                                        __builtin_amdgcn_ldexpf(x[4 * k + 3], -e), w, true);
+    c[k] = (uint32_t)w;
+  }
+  if (lane < P) {
+    *reinterpret_cast<u32x2*>(kt + fp8_k_index(o, 8 * piece, 16, D)) = u32x2{c[0], c[1]};
+    if (piece == 0) kt[16 * D + o] = (uint8_t)(e + kFp8ScaleBias);
+  } else if (lane < 2 * P) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      vt[fp8_v_index(o, 8 * piece + k, 16, D)] = (uint8_t)(c[k >> 2] >> (8 * (k & 3)));
+    if (piece == 0) vt[16 * D + o] = (uint8_t)(e + kFp8ScaleBias);
+  }
+}
+
+// APPEND: the step's new token of every sequence (position len-1) comes in
+// knew/vnew [n][H_kv][d] (bf16); the item whose range holds that position
+// quantizes it into the pool (fp8_put_token) and waits for those stores
+// before it loads any pair, so its loads of the block read the new codes.
+template <int D, int OUT, bool NT, int NS, bool APPEND>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_fp8_kernel(
-    const uint8_t* __restrict__ kpool, const uint8_t* __restrict__ vpool,
-    const uint16_t* __restrict__ q, uint16_t* __restrict__ out, float* __restrict__ part_o,
+    uint8_t* __restrict__ kpool, uint8_t* __restrict__ vpool,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ knew,
+    const uint16_t* __restrict__ vnew, uint16_t* __restrict__ out, float* __restrict__ part_o,
     float* __restrict__ part_ml, const int32_t* __restrict__ tables,
     const int32_t* __restrict__ lens, int64_t layer_off, int N, int Hkv, int Hq, int G,
     int max_blocks, int max_ctx, int bps, int S_max, float qk_scale, int* __restrict__ counters) {
@@ -451,6 +481,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void de
 
   const uint8_t* kl = kpool + layer_off;
   const uint8_t* vl = vpool + layer_off;
+  if constexpr (APPEND) {
+    if (len > 0 && b1 == nblk) {   // wave-uniform: the last block of the sequence is this item's
+      constexpr int TB = 16 * D + 16;
+      const int64_t tile = ((int64_t)table_at(tb, nblk - 1 - b0) * Hkv + g) * TB;
+      const int64_t row = ((int64_t)i * Hkv + g) * D;
+      fp8_put_token<D>(kpool + layer_off + tile, vpool + layer_off + tile, knew + row, vnew + row,
+                       (len - 1) & 15, lane);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the codes are in L2 before any pair load
+    }
+  }
   // Score row c of each tile holds pair-local key 8*(c>>2) + 4*t + (c&3): block
   // c >> 3, tile row 8*t + (c&7).
   const int k_sel = c >> 3;

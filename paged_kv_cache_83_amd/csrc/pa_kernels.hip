@@ -874,17 +874,6 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   float* part_o = (float*)workspace;
   float* part_ml = plan.direct ? nullptr : part_o + (size_t)n_seqs * n_q_heads * plan.S_max * D;
   int* counters = plan.merge ? (int*)((char*)workspace + plan.counters_off) : nullptr;
-  if (plan.kernel == 3 && append) {  // FP8: quantize the step's tokens into the pool first
-    ProfScope ps("append", st, timing);
-    if (!launch_append_fp8(st, (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)knew,
-                           (const uint16_t*)vnew,
-                           SlotsFromLens{block_tables, context_lens, max_blocks_per_seq,
-                                         max_context_len, B, g->num_blocks},
-                           (int64_t)n_seqs, Hkv, D, B, (int64_t)g->num_blocks * B,
-                           (int64_t)layer * g->num_blocks * Hkv * tile_bytes(g)))
-      return PA_ERR_UNSUPPORTED;
-    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
-  }
   {
     ProfScope ps("decode_partial", st, timing, true);
     const dim3 grid((unsigned)items), block(64);
@@ -897,12 +886,19 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
   } while (0)
     if (plan.kernel == 3) {
       const int64_t off8 = (int64_t)layer * g->num_blocks * Hkv * tile_bytes(g);
-#define PA_FP8_LAUNCH_X(DD, DIR, NTV)                                                              \
-  PA_TIMED_LAUNCH(ps, (decode_mfma_fp8_kernel<DD, DIR, NTV, PA_FP8_STAGES>), grid, block, 0, st,     \
-                     (const uint8_t*)k_pool, (const uint8_t*)v_pool, (const uint16_t*)q,            \
-                     (uint16_t*)out, part_o, part_ml, block_tables, context_lens, off8,           \
-                     g->num_blocks, Hkv, n_q_heads, G, max_blocks_per_seq, max_context_len,       \
-                     plan.bps, plan.S_max, qk_scale, counters)
+#define PA_FP8_LAUNCH_A(DD, DIR, NTV, APP)                                                         \
+  PA_TIMED_LAUNCH(ps, (decode_mfma_fp8_kernel<DD, DIR, NTV, PA_FP8_STAGES, APP>), grid, block, 0,    \
+                     st, (uint8_t*)k_pool, (uint8_t*)v_pool, (const uint16_t*)q,                    \
+                     (const uint16_t*)knew, (const uint16_t*)vnew, (uint16_t*)out, part_o, part_ml, \
+                     block_tables, context_lens, off8, g->num_blocks, Hkv, n_q_heads, G,           \
+                     max_blocks_per_seq, max_context_len, plan.bps, plan.S_max, qk_scale, counters)
+      // the step's tokens (decode_append) are quantized into the pool by the
+      // items that hold them, inside the decode launch
+#define PA_FP8_LAUNCH_X(DD, DIR, NTV)                            \
+  do {                                                           \
+    if (append) PA_FP8_LAUNCH_A(DD, DIR, NTV, true);             \
+    else PA_FP8_LAUNCH_A(DD, DIR, NTV, false);                   \
+  } while (0)
 #define PA_FP8_LAUNCH(DD, DIR)                                   \
   do {                                                           \
     if (plan.stream_kv) PA_FP8_LAUNCH_X(DD, DIR, true);          \
@@ -912,6 +908,7 @@ static pa_status decode_impl(const pa_geom* g, void* k_pool, void* v_pool, int32
       else PA_OUT_MODE(PA_FP8_LAUNCH, 128);
 #undef PA_FP8_LAUNCH
 #undef PA_FP8_LAUNCH_X
+#undef PA_FP8_LAUNCH_A
     } else if (plan.kernel == 2) {
 #define PA_MFMA_LAUNCH_RG(DD, DIR, NTV, APP, RG, ITEMS)                                           \
   PA_TIMED_LAUNCH(ps, (decode_mfma_bf16_kernel<DD, DIR, NTV, APP, RG>), grid, block, 0, st,        \

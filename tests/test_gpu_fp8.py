@@ -195,29 +195,42 @@ def test_fp8_placement_invariance_bitwise():
     assert np.array_equal(run_decode(a, 0), run_decode(b, 0))
 
 
-def test_fp8_decode_append_fused_api():
-    """pa_decode_append on an FP8 pool: the step's tokens are quantized into slot
-    len-1 (bit-exact) and attended."""
+FUSED_CASES = [
+    # name, d, lengths, blocks per split, merge inside the launch
+    ("d128", 128, [1, 40, 257, 16], 0, False),
+    ("d128_split2", 128, [1, 40, 257, 16, 0, 100], 2, False),
+    ("d128_split4_merge", 128, [300, 17, 64, 1], 4, True),
+    ("d64_split2", 64, [1, 40, 257, 16, 0, 33], 2, False),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_fp8_decode_append_fused_api(case):
+    """pa_decode_append on an FP8 pool: the item holding each sequence's last
+    block quantizes the step's token into slot len-1 inside the decode launch
+    (pool bytes equal the oracle's append) and attends over it."""
     need_gpu()
-    print_case(test="fp8_decode_append")
-    lengths = [1, 40, 257, 16]
-    c = make_decode_case(32, 4, 128, lengths, seed=71)
+    name, d, lengths, bps, merge = case
+    print_case(test="fp8_decode_append", case=name)
+    c = make_decode_case(32, 4, d, lengths, seed=71 + len(name))
     B, layer = c["B"], 1
     n = len(lengths)
-    kn, vn = scaled_rows(81, n, c["Hkv"], 128, 1.0), scaled_rows(82, n, c["Hkv"], 128, 1.0)
-    slots = [c["tables"][i][(S - 1) // B] * B + (S - 1) % B for i, S in enumerate(lengths)]
+    kn, vn = scaled_rows(81, n, c["Hkv"], d, 1.0), scaled_rows(82, n, c["Hkv"], d, 1.0)
+    slots = [c["tables"][i][(S - 1) // B] * B + (S - 1) % B if S > 0 else -1
+             for i, S in enumerate(lengths)]
     ek, ev = fp8.append_kv(c["kp"], c["vp"], layer, kn, vn, slots, B)
-    geom = pk.Geometry(c["L"], c["Hkv"], 128, B, c["N"], "fp8")
+    geom = pk.Geometry(c["L"], c["Hkv"], d, B, c["N"], "fp8")
     K, V = to_dev(c["kp"], "fp8"), to_dev(c["vp"], "fp8")
     mb = max(len(t) for t in c["tables"])
     q = to_dev(c["q"], "bf16")
     out = torch.full_like(q, float("nan"))
     max_ctx = max(lengths)
-    ws = torch.empty(max(1, pk.decode_workspace_bytes(geom, n, 32, max_ctx)), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.zeros(max(1, pk.decode_workspace_bytes(geom, n, 32, max_ctx, bps, "auto", merge)),
+                     dtype=torch.uint8, device="cuda")
     pk.decode_append(geom, K, V, layer, q, to_dev(kn, "bf16"), to_dev(vn, "bf16"), out,
                      torch.from_numpy(padded_tables(c["tables"], mb)).cuda(),
-                     torch.tensor(lengths, dtype=torch.int32, device="cuda"), max_ctx, workspace=ws)
+                     torch.tensor(lengths, dtype=torch.int32, device="cuda"), max_ctx, workspace=ws,
+                     blocks_per_split=bps, merge=merge)
     torch.cuda.synchronize()
     assert np.array_equal(to_host(K, "fp8"), ek) and np.array_equal(to_host(V, "fp8"), ev)
     expect = fp8.paged_decode(c["q"], ek, ev, layer, c["tables"], lengths, B)
