@@ -433,7 +433,9 @@ def run_decode(args):
             per_launch = (int(lengths.sum()) * 2 * Hkv * (d * eb + (1 if fp8 else 0))  # K and V (+ scales)
                           + 2 * n * Hq * d * ib                                  # queries, outputs
                           + 4 * int(sum(math.ceil(S / B) for S in lengths))       # block-table entries
-                          + (0 if (args.unfused or fp8) else 4 * n * Hkv * d * eb))  # fused new K/V
+                          + (0 if args.unfused                                   # fused new K/V:
+                             else 2 * n * Hkv * (2 * d + d + 1) if fp8           # bf16 rows in, codes + scale out
+                             else 4 * n * Hkv * d * eb))                          # rows in, rows out
             avg_s = tot / cnt * 1e-3
             achieved = per_launch / avg_s / 1e9
             mfma = cfg.dtype in ("bf16", "fp8") and B == 16 and args.kernel in ("auto", "mfma")
